@@ -1,0 +1,188 @@
+"""Seeded synthetic inputs for the KDA layer (host-side, numpy).
+
+This module is the one piece shared by the HIP path's callers and by the oracle's
+tests: it draws and shapes random inputs and holds none of the method's arithmetic
+(no decay, no delta update, no chunking).  It imports numpy only.
+
+Workloads (the five shapes the layer is measured and checked on):
+
+  0  tiny fp32 prefill      B=1,  H=2,  T=256,    d=64,  fp32 in/out, S0=0
+  1  training-shape prefill B=4,  H=16, T=4096,   d=128, bf16 in, S0=0
+  2  long-context prefill   B=1,  H=32, T=65536,  d=128, bf16 in, S0 ~ 0.02*N(0,1)
+  3  decode                 N=256 sequences, H=32, d=128, 1024 steps, bf16 in,
+                            S ~ 0.02*N(0,1)
+  4  packed varlen prefill  64 sequences, lengths U{512..16384}, H=32, d=128, bf16
+
+Distributions: q, k ~ N(0,1) then L2-normalised per (token, head); v ~ N(0,1);
+beta = sigmoid(N(0,1)); log_alpha = logsigmoid(N(0,1) + mu) / s per channel with
+(mu, s) = (4, 8) except workload 2 (6, 16); workload 4 draws each element from an
+even mixture of logsigmoid(N+4)/8 and logsigmoid(N)/2.  numpy PCG64
+``default_rng(seed)``; draws are float32 and happen in the order lengths (4 only),
+q, k, v, z_beta, z_alpha, z_alpha2 and mixture mask (4 only), S0.  Decode draws S0
+first and then each step's q, k, v, z_beta, z_alpha in step order, so steps can be
+streamed.  bf16 inputs are the round-to-nearest-even bf16 of the float32 value and
+are carried as uint16 bit patterns.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+D_DEFAULT = 128
+
+
+@dataclass(frozen=True)
+class Workload:
+    index: int
+    name: str
+    kind: str                 # "prefill" or "decode"
+    B: int = 1
+    T: int = 0
+    H: int = 32
+    D: int = 128
+    dtype: str = "bf16"       # input dtype: "bf16" or "f32"
+    mu: float = 4.0
+    s: float = 8.0
+    s0: bool = False
+    mix: bool = False
+    num_seqs: int = 0         # varlen sequences / decode sequences
+    len_range: tuple = ()     # varlen length bounds (inclusive)
+    steps: int = 0            # decode steps
+    chunk: int = 64
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def seed(self) -> int:
+        return self.index + 1
+
+
+WORKLOADS = {
+    0: Workload(0, "tiny_fp32_prefill", "prefill", B=1, T=256, H=2, D=64, dtype="f32"),
+    1: Workload(1, "train_prefill", "prefill", B=4, T=4096, H=16, D=128),
+    2: Workload(2, "long_context_prefill", "prefill", B=1, T=65536, H=32, D=128,
+                mu=6.0, s=16.0, s0=True),
+    3: Workload(3, "decode", "decode", H=32, D=128, s0=True, num_seqs=256, steps=1024),
+    4: Workload(4, "varlen_packed_prefill", "prefill", H=32, D=128, mix=True,
+                num_seqs=64, len_range=(512, 16384)),
+}
+
+
+# ---------------------------------------------------------------- bf16 bit helpers
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round-to-nearest-even float32 -> bf16, returned as uint16 bit patterns
+    (finite inputs only)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+    return (r >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def to_float(x: np.ndarray) -> np.ndarray:
+    """Exact float32 view of an input array (bf16 bits widen exactly)."""
+    return bf16_bits_to_f32(x) if x.dtype == np.uint16 else np.asarray(x, dtype=np.float32)
+
+
+def _cast(x: np.ndarray, dtype: str) -> np.ndarray:
+    return f32_to_bf16_bits(x) if dtype == "bf16" else np.ascontiguousarray(x, dtype=np.float32)
+
+
+# ---------------------------------------------------------------- transforms
+def _l2n(x: np.ndarray) -> np.ndarray:
+    return x / np.sqrt(np.sum(x.astype(np.float64) ** 2, axis=-1, keepdims=True)).astype(np.float32)
+
+
+def _sigmoid(x):
+    return (1.0 / (1.0 + np.exp(-x.astype(np.float64)))).astype(np.float32)
+
+
+def _logsigmoid(x):
+    x = x.astype(np.float64)
+    return (np.minimum(x, 0.0) - np.log1p(np.exp(-np.abs(x)))).astype(np.float32)
+
+
+def _normal(rng, shape):
+    return rng.standard_normal(shape, dtype=np.float32)
+
+
+# ---------------------------------------------------------------- prefill
+def make_prefill(w: Workload, seed: int | None = None, *, B=None, T=None, H=None, D=None,
+                 num_seqs=None, len_range=None, s0=None, dtype=None, mu=None, s=None,
+                 mix=None, lengths=None):
+    """Draw one prefill batch.  Keyword overrides shrink a workload for tests while
+    keeping its recipe.  Returns a dict with q, k, v, log_alpha, beta (float32 or
+    bf16 bits), S0 (float32 [N, H, D, D] or None), cu_seqlens (int32 [N+1] or None),
+    and the shape fields."""
+    seed = w.seed if seed is None else seed
+    rng = np.random.default_rng(seed)
+    H = w.H if H is None else H
+    D = w.D if D is None else D
+    dtype = w.dtype if dtype is None else dtype
+    mu = w.mu if mu is None else mu
+    s = w.s if s is None else s
+    mix = w.mix if mix is None else mix
+    s0 = w.s0 if s0 is None else s0
+    varlen = bool(w.len_range) or lengths is not None or num_seqs is not None and len_range is not None
+    if varlen:
+        if lengths is None:
+            lo, hi = len_range if len_range is not None else w.len_range
+            n = num_seqs if num_seqs is not None else w.num_seqs
+            lengths = rng.integers(lo, hi, endpoint=True, size=n)
+        lengths = np.asarray(lengths, dtype=np.int64)
+        cu = np.zeros(lengths.size + 1, dtype=np.int64)
+        np.cumsum(lengths, out=cu[1:])
+        B, T, N = 1, int(cu[-1]), int(lengths.size)
+    else:
+        B = w.B if B is None else B
+        T = w.T if T is None else T
+        N, cu = B, None
+    shp = (B, T, H, D)
+    q = _l2n(_normal(rng, shp))
+    k = _l2n(_normal(rng, shp))
+    v = _normal(rng, shp)
+    beta = _sigmoid(_normal(rng, (B, T, H)))
+    g = _logsigmoid(_normal(rng, shp) + np.float32(mu)) / np.float32(s)
+    if mix:
+        g_fast = _logsigmoid(_normal(rng, shp)) / np.float32(2.0)
+        pick = rng.random(shp, dtype=np.float32) < 0.5
+        g = np.where(pick, g_fast, g)
+    S0 = (np.float32(0.02) * _normal(rng, (N, H, D, D))) if s0 else None
+    return dict(q=_cast(q, dtype), k=_cast(k, dtype), v=_cast(v, dtype),
+                log_alpha=_cast(g, dtype), beta=_cast(beta, dtype), S0=S0,
+                cu_seqlens=None if cu is None else cu.astype(np.int32),
+                B=B, T=T, H=H, D=D, N=N, dtype=dtype)
+
+
+# ---------------------------------------------------------------- decode
+class DecodeStream:
+    """Seeded decode workload: ``state()`` gives the initial state, then ``step()``
+    returns each step's inputs in order (so 1024 steps never need to be resident
+    on the host at once)."""
+
+    def __init__(self, w: Workload, seed: int | None = None, *, num_seqs=None, H=None, D=None,
+                 dtype=None, mu=None, s=None):
+        self.rng = np.random.default_rng(w.seed if seed is None else seed)
+        self.N = w.num_seqs if num_seqs is None else num_seqs
+        self.H = w.H if H is None else H
+        self.D = w.D if D is None else D
+        self.dtype = w.dtype if dtype is None else dtype
+        self.mu = w.mu if mu is None else mu
+        self.s = w.s if s is None else s
+        self._S0 = np.float32(0.02) * _normal(self.rng, (self.N, self.H, self.D, self.D))
+
+    def state(self) -> np.ndarray:
+        return self._S0
+
+    def step(self):
+        shp = (self.N, self.H, self.D)
+        q = _l2n(_normal(self.rng, shp))
+        k = _l2n(_normal(self.rng, shp))
+        v = _normal(self.rng, shp)
+        beta = _sigmoid(_normal(self.rng, (self.N, self.H)))
+        g = _logsigmoid(_normal(self.rng, shp) + np.float32(self.mu)) / np.float32(self.s)
+        dt = self.dtype
+        return dict(q=_cast(q, dt), k=_cast(k, dt), v=_cast(v, dt), log_alpha=_cast(g, dt),
+                    beta=_cast(beta, dt))
