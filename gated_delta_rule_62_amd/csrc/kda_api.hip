@@ -1,0 +1,138 @@
+// kda_api.hip -- host side of libkda.so: argument checks, workspace carving and
+// kernel launches for the C ABI declared in include/kda.h.
+//
+// Every check that can be made from the arguments runs before the first HIP
+// call, so a rejected call touches no device state.  Nothing here allocates or
+// synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "kda.h"
+#include "kda_launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_size(kda_dtype d) { return d == KDA_BF16 ? 2 : 4; }
+
+bool dtype_ok(kda_dtype d) { return d == KDA_F32 || d == KDA_BF16; }
+
+bool head_ok(int Dk, int Dv) { return Dk == Dv && (Dk == 64 || Dk == 128); }
+
+// [a, a+na) and [b, b+nb) overlap?
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    auto x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+extern "C" const char* kda_status_string(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+        case KDA_ERR_WORKSPACE_TOO_SMALL: return "KDA_ERR_WORKSPACE_TOO_SMALL";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    }
+    return "KDA_ERR_UNKNOWN";
+}
+
+extern "C" size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int num_seqs,
+                                                int has_cu_seqlens, int chunk) {
+    if (B < 0 || T < 0 || H <= 0 || num_seqs < 0 || !head_ok(Dk, Dv)) return 0;
+    if (chunk != 0 && chunk != kda::kChunk) return 0;
+    kda::PrefillPlan plan = kda::plan_prefill(B, T, H, Dk, num_seqs, has_cu_seqlens != 0);
+    return plan.workspace_bytes;
+}
+
+extern "C" kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                                    const void* beta, const float* S0, const int32_t* cu_seqlens,
+                                    int B, int T, int H, int Dk, int Dv, int num_seqs, int chunk,
+                                    kda_dtype in_dtype, kda_dtype out_dtype, void* o, float* S_final,
+                                    void* workspace, size_t workspace_bytes, kda_stream_t stream) {
+    if (B < 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || num_seqs < 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_UNSUPPORTED;
+    if (!head_ok(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
+    if (chunk != 0 && chunk != kda::kChunk) return KDA_ERR_UNSUPPORTED;
+    if (cu_seqlens) {
+        if (B != 1) return KDA_ERR_INVALID_ARGUMENT;
+        if (!aligned16(cu_seqlens)) return KDA_ERR_INVALID_ARGUMENT;
+    } else if (num_seqs != B) {
+        return KDA_ERR_INVALID_ARGUMENT;
+    }
+    const size_t tokens = static_cast<size_t>(B) * static_cast<size_t>(T);
+    if (tokens > 0 && num_seqs > 0) {
+        if (!q || !k || !v || !log_alpha || !beta || !o) return KDA_ERR_INVALID_ARGUMENT;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) || !aligned16(o))
+            return KDA_ERR_INVALID_ARGUMENT;
+        // beta rows are [B, T, H]: 16-byte alignment of the base is enough for the
+        // kernels' scalar reads, but keep the documented contract uniform.
+        if (!aligned16(beta)) return KDA_ERR_INVALID_ARGUMENT;
+    }
+    if ((S0 && !aligned16(S0)) || (S_final && !aligned16(S_final))) return KDA_ERR_INVALID_ARGUMENT;
+
+    const size_t ein = elem_size(in_dtype), eout = elem_size(out_dtype);
+    const size_t n_qk = tokens * H * Dk * ein, n_v = tokens * H * Dv * ein, n_b = tokens * H * ein;
+    const size_t n_o = tokens * H * Dv * eout;
+    const size_t n_s = static_cast<size_t>(num_seqs) * H * Dk * Dv * sizeof(float);
+    if (tokens > 0) {
+        const void* ins[5] = {q, k, v, log_alpha, beta};
+        const size_t nin[5] = {n_qk, n_qk, n_v, n_qk, n_b};
+        for (int i = 0; i < 5; ++i)
+            if (overlap(ins[i], nin[i], o, n_o) || overlap(ins[i], nin[i], S_final, n_s))
+                return KDA_ERR_INVALID_ARGUMENT;
+    }
+    if (overlap(S0, n_s, S_final, n_s) || overlap(S0, n_s, o, n_o) || overlap(o, n_o, S_final, n_s))
+        return KDA_ERR_INVALID_ARGUMENT;
+
+    kda::PrefillPlan plan = kda::plan_prefill(B, T, H, Dk, num_seqs, cu_seqlens != nullptr);
+    if (workspace_bytes < plan.workspace_bytes) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    if (plan.workspace_bytes > 0 && (!workspace || !aligned16(workspace))) return KDA_ERR_INVALID_ARGUMENT;
+    if (num_seqs == 0) return KDA_OK;
+    if (overlap(workspace, plan.workspace_bytes, o, n_o) || overlap(workspace, plan.workspace_bytes, S_final, n_s))
+        return KDA_ERR_INVALID_ARGUMENT;
+
+    kda::PrefillArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = log_alpha; a.beta = beta;
+    a.S0 = S0; a.cu = cu_seqlens; a.o = o; a.S_final = S_final;
+    a.B = B; a.T = T; a.H = H; a.D = Dk; a.N = num_seqs;
+    a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = out_dtype == KDA_BF16;
+    a.workspace = workspace;
+    hipError_t err = kda::launch_prefill(a, plan, reinterpret_cast<hipStream_t>(stream));
+    return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+extern "C" kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const void* log_alpha,
+                                         const void* beta, const float* S_in, float* S_out,
+                                         int N, int H, int Dk, int Dv,
+                                         kda_dtype in_dtype, kda_dtype out_dtype,
+                                         void* o, kda_stream_t stream) {
+    if (N < 0 || H <= 0 || Dk <= 0 || Dv <= 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_UNSUPPORTED;
+    if (!head_ok(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
+    if (N == 0) return KDA_OK;
+    if (!q || !k || !v || !log_alpha || !beta || !S_in || !S_out || !o) return KDA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) || !aligned16(beta) ||
+        !aligned16(S_in) || !aligned16(S_out) || !aligned16(o))
+        return KDA_ERR_INVALID_ARGUMENT;
+    const size_t units = static_cast<size_t>(N) * H;
+    const size_t ein = elem_size(in_dtype), eout = elem_size(out_dtype);
+    const size_t n_s = units * Dk * Dv * sizeof(float), n_o = units * Dv * eout;
+    if (S_in != S_out && overlap(S_in, n_s, S_out, n_s)) return KDA_ERR_INVALID_ARGUMENT;
+    const void* ins[5] = {q, k, v, log_alpha, beta};
+    const size_t nin[5] = {units * Dk * ein, units * Dk * ein, units * Dv * ein, units * Dk * ein, units * ein};
+    for (int i = 0; i < 5; ++i)
+        if (overlap(ins[i], nin[i], S_out, n_s) || overlap(ins[i], nin[i], o, n_o)) return KDA_ERR_INVALID_ARGUMENT;
+    if (overlap(o, n_o, S_out, n_s) || overlap(o, n_o, S_in, n_s)) return KDA_ERR_INVALID_ARGUMENT;
+    if (units > 0x7fffffffu) return KDA_ERR_UNSUPPORTED;
+
+    hipError_t err = kda::launch_decode(Dk, in_dtype == KDA_BF16, out_dtype == KDA_BF16, q, k, v, log_alpha,
+                                        beta, S_in, S_out, o, static_cast<int>(units),
+                                        reinterpret_cast<hipStream_t>(stream));
+    return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}

@@ -1,0 +1,48 @@
+// kda_launch.h -- host-side launch plans and launchers shared by kda_api.hip and
+// the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int kChunk = 64;            // chunk length C (tokens)
+constexpr int kTargetWorkgroups = 256;  // one prefill workgroup per compute unit fills the chip
+constexpr int kMinChunksPerSegment = 4;
+
+// How a prefill call is split into kernels.
+//  G == 1: one pass, one workgroup per (sequence, head).
+//  G  > 1 (equal-length batches only): every sequence is cut into G segments of
+//         cps chunks.  Pass 1 runs segments 0..G-2 from a zero state and also
+//         carries the segment's transition matrix; a small combine kernel chains
+//         the segment entry states; pass 2 reruns every segment from its true
+//         entry state and writes o and S_final.
+struct PrefillPlan {
+    int G = 1;
+    int chunks = 0;        // chunks per sequence (equal-length case)
+    int cps = 0;           // chunks per segment
+    size_t off_phi = 0, off_sloc = 0, off_se = 0, off_order = 0;
+    size_t workspace_bytes = 0;
+};
+
+struct PrefillArgs {
+    const void *q, *k, *v, *g, *beta;
+    const float* S0;
+    const int32_t* cu;
+    void* o;
+    float* S_final;
+    void* workspace;
+    int B, T, H, D, N;
+    bool in_bf16, out_bf16;
+};
+
+PrefillPlan plan_prefill(int B, int T, int H, int D, int N, bool varlen);
+hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan, hipStream_t stream);
+
+hipError_t launch_decode(int D, bool in_bf16, bool out_bf16, const void* q, const void* k,
+                         const void* v, const void* g, const void* b, const float* S_in,
+                         float* S_out, void* o, int units, hipStream_t stream);
+
+}  // namespace kda

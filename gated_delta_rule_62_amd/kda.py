@@ -1,0 +1,133 @@
+"""Thin Python binding over libkda.so (argument marshalling only).
+
+The functions carry the C ABI's names (include/kda.h) and take torch tensors that
+live on the GPU; torch provides device memory and streams, every step of the
+computation runs in the library's HIP kernels.  There is no fallback: if the
+library is missing or a call fails, these raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkda.so")
+
+KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE_TOO_SMALL, KDA_ERR_HIP = range(5)
+KDA_F32, KDA_BF16 = 0, 1
+CHUNK = 64
+
+EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_step")
+
+_lib = None
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what} failed: {status_string(status)}")
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libkda.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m gated_delta_rule_62_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.kda_status_string.argtypes = [i32]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_chunk_fwd_workspace_bytes.argtypes = [i32] * 8
+    lib.kda_chunk_fwd_workspace_bytes.restype = sz
+    lib.kda_chunk_fwd.argtypes = [vp] * 7 + [i32] * 7 + [i32, i32] + [vp, vp] + [vp, sz, vp]
+    lib.kda_chunk_fwd.restype = i32
+    lib.kda_recurrent_step.argtypes = [vp] * 7 + [i32] * 4 + [i32, i32] + [vp, vp]
+    lib.kda_recurrent_step.restype = i32
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().kda_status_string(int(status)).decode()
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return KDA_F32
+    if t == torch.bfloat16:
+        return KDA_BF16
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_dev(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous and on the GPU")
+
+
+def kda_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, num_seqs, has_cu_seqlens, chunk=CHUNK) -> int:
+    return int(load_library().kda_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, num_seqs,
+                                                            int(bool(has_cu_seqlens)), chunk))
+
+
+def kda_chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, out_dtype=None, o=None,
+                  S_final=None, workspace=None, chunk=CHUNK, stream=None, want_final=True):
+    """Prefill.  q, k, log_alpha [B, T, H, Dk]; v [B, T, H, Dv]; beta [B, T, H]
+    (one dtype: float32 or bfloat16); S0 [N, H, Dk, Dv] float32 or None;
+    cu_seqlens int32 [N+1] on the GPU (B == 1) or None.  Returns (o, S_final)."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=out_dtype, device=q.device)
+    if S_final is None and want_final:
+        S_final = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    _check_dev(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_final, workspace)
+    ws_need = kda_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, N, cu_seqlens is not None, chunk)
+    if workspace is None and ws_need > 0:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().kda_chunk_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
+        B, T, H, Dk, Dv, N, chunk, _dtype_code(q.dtype), _dtype_code(o.dtype),
+        _ptr(o), _ptr(S_final), _ptr(workspace), ws_bytes, _stream_ptr(stream))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_chunk_fwd")
+    return o, S_final
+
+
+def kda_recurrent_step(q, k, v, log_alpha, beta, S_in, S_out=None, *, out_dtype=None, o=None,
+                       stream=None):
+    """Decode one token.  q, k, log_alpha [N, H, Dk]; v [N, H, Dv]; beta [N, H];
+    S_in [N, H, Dk, Dv] float32; S_out defaults to S_in (in place).  Returns (o, S_out)."""
+    N, H, Dk = q.shape
+    Dv = v.shape[-1]
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((N, H, Dv), dtype=out_dtype, device=q.device)
+    if S_out is None:
+        S_out = S_in
+    _check_dev(q, k, v, log_alpha, beta, S_in, S_out, o)
+    st = load_library().kda_recurrent_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S_in), _ptr(S_out),
+        N, H, Dk, Dv, _dtype_code(q.dtype), _dtype_code(o.dtype), _ptr(o), _stream_ptr(stream))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_recurrent_step")
+    return o, S_out

@@ -1,0 +1,124 @@
+/*
+ * kda.h -- C ABI of libkda.so: the KDA (fine-grained gated delta rule) layer on
+ * AMD Instinct MI355X (gfx950), chunkwise prefill and single-token decode.
+ *
+ * The operation.  Per sequence and head, over tokens t in order, with state
+ * S in R^{Dk x Dv}, keys/queries in R^{Dk}, values in R^{Dv}, a scalar write
+ * strength beta_t and a per-key-channel decay alpha_t = exp(log_alpha_t):
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t
+ *
+ * This is the fine-grained gated delta rule of "Decoding Hybrid Attention
+ * Architectures" (intl.cloud.baidu.com article 9569726), section 3.4 (and
+ * "Technical Analysis and Engineering Practices for Novel Hybrid Linear Attention
+ * Architectures", article 9578008, section 2 item 4), written with the state
+ * oriented d_k x d_v: decay acts on key channels, the write is k v^T, the read is
+ * S^T q, and token t's output reads the state after its own write.  There is no
+ * 1/sqrt(Dk) scaling of q; callers pre-scale q if they want one.
+ *
+ * Prefill evaluates the same result with the chunkwise algorithm of section 4 of
+ * article 9569726 (section 3 of article 9578008); decode applies the rule to one
+ * token (the constant-size recurrent state of section 1 of article 9569726).
+ *
+ * Conventions for every entry point:
+ *  - Tensor arguments are DEVICE pointers owned by the caller, contiguous,
+ *    row-major (last index fastest) and 16-byte aligned.
+ *  - Nothing allocates: scratch memory is a caller-provided workspace.
+ *  - Work is enqueued on `stream` (NULL = the default stream); no call
+ *    synchronises.  Errors detectable from the arguments are returned before any
+ *    HIP call; a failed launch returns KDA_ERR_HIP.  Faults inside kernels show
+ *    up at the caller's next synchronisation.
+ *  - Preconditions that live in device memory are documented, not checked:
+ *    cu_seqlens starts at 0, never decreases and ends at T; inputs are finite;
+ *    log_alpha <= 0; beta in [0, 1].  Per chunk of 64 tokens, the summed
+ *    log-decay of any channel must stay above -160 (the decay factors of a chunk
+ *    are formed around its midpoint in fp32).
+ *  - Outputs are bitwise deterministic for identical inputs (no atomics).
+ *  - Library functions keep no mutable global state and are thread-safe.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same object as hipStream_t. */
+typedef struct ihipStream_t* kda_stream_t;
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARGUMENT = 1,     /* null pointer, bad size, misalignment, aliasing */
+    KDA_ERR_UNSUPPORTED = 2,          /* head size, chunk size or dtype not built */
+    KDA_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes < kda_chunk_fwd_workspace_bytes() */
+    KDA_ERR_HIP = 4                   /* a HIP launch or API call failed */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* Human-readable name of a status code (static storage). */
+const char* kda_status_string(kda_status s);
+
+/*
+ * Workspace bytes kda_chunk_fwd needs for these sizes (same arguments, same
+ * meaning).  has_cu_seqlens is 0 or 1.  Returns 0 for unsupported sizes.
+ */
+size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int num_seqs,
+                                     int has_cu_seqlens, int chunk);
+
+/*
+ * kda_chunk_fwd -- prefill: o and the final state of every sequence.
+ *
+ *   q, k, log_alpha : [B, T, H, Dk]   in_dtype
+ *   v               : [B, T, H, Dv]   in_dtype
+ *   beta            : [B, T, H]       in_dtype
+ *   S0              : [N, H, Dk, Dv]  fp32 initial states, or NULL for zeros
+ *   cu_seqlens      : int32 [N+1] device offsets of N packed sequences (B must be
+ *                     1, sequence n owns tokens [cu[n], cu[n+1]), zero lengths
+ *                     allowed), or NULL: then N = B sequences of T tokens each
+ *   num_seqs        : N
+ *   chunk           : chunk size; 0 or 64 (the only size built)
+ *   o               : [B, T, H, Dv]   out_dtype (bf16 is round-to-nearest-even)
+ *   S_final         : [N, H, Dk, Dv]  fp32, or NULL to skip
+ *   workspace       : device scratch of workspace_bytes >= the query above
+ *                     (may be NULL when the query returns 0)
+ *
+ * Supported: Dk == Dv in {64, 128}; in_dtype, out_dtype in {KDA_F32, KDA_BF16}.
+ * A sequence of length 0 gets S_final = S0 (or zeros).  T == 0 or N == 0 only
+ * writes S_final.  Inputs must not overlap outputs.  The result does not depend
+ * on the chunk size beyond rounding.
+ */
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                         const void* beta, const float* S0, const int32_t* cu_seqlens,
+                         int B, int T, int H, int Dk, int Dv, int num_seqs, int chunk,
+                         kda_dtype in_dtype, kda_dtype out_dtype,
+                         void* o, float* S_final,
+                         void* workspace, size_t workspace_bytes, kda_stream_t stream);
+
+/*
+ * kda_recurrent_step -- decode: one token for each of N independent sequences.
+ *
+ *   q, k, log_alpha : [N, H, Dk]  in_dtype      v : [N, H, Dv] in_dtype
+ *   beta            : [N, H]      in_dtype
+ *   S_in            : [N, H, Dk, Dv] fp32 state before the token
+ *   S_out           : [N, H, Dk, Dv] fp32 state after the token; S_out == S_in
+ *                     (in place) is allowed, any other overlap is rejected
+ *   o               : [N, H, Dv]  out_dtype
+ *
+ * Supported: Dk == Dv in {64, 128}.  N == 0 is a no-op.
+ */
+kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const void* log_alpha,
+                              const void* beta, const float* S_in, float* S_out,
+                              int N, int H, int Dk, int Dv,
+                              kda_dtype in_dtype, kda_dtype out_dtype,
+                              void* o, kda_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */
