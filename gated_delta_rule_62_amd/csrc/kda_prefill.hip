@@ -1,17 +1,681 @@
-// kda_prefill.hip -- chunkwise KDA prefill (gfx950).  (kernels follow)
+// kda_prefill.hip -- chunkwise KDA prefill for gfx950 (MI355X).
+//
+// Method: the chunkwise parallel form of the fine-grained gated delta rule
+// ("Decoding Hybrid Attention Architectures", intl.cloud.baidu.com article 9569726,
+// section 4; "Technical Analysis and Engineering Practices for Novel Hybrid Linear
+// Attention Architectures", article 9578008, section 3).  Per chunk of C = 64
+// tokens with entry state S (d_k x d_v, fp32) and chunk-local cumulative log-decay
+// b_r = sum_{i<=r} g_i:
+//
+//   A    = StrictTril(Diag(beta) Kbar Ktil^T)           Kbar = K e^{b}, Ktil = K e^{-b}
+//   T    = (I + A)^{-1} Diag(beta)
+//   P    = Tril(Qbar Ktil^T)                             Qbar = Q e^{b}
+//   Unew = T (V - Kbar S)                                (= U - W S with U = T V, W = T Kbar)
+//   O    = Qbar S + P Unew
+//   S   <- Diag(gamma) S + Khat^T Unew                   gamma = e^{b_n}, Khat = K e^{b_n - b}
+//
+// The pages leave U and W undefined and print the state term with (Gamma.K)^T;
+// the reading used here (T as above, keys decayed to the chunk end) is the one
+// that reproduces the token recurrence exactly.
+//
+// MI355X design.
+//  * One workgroup runs the whole chunk loop of one (sequence, head[, segment]):
+//    intra-chunk operands live in LDS, the state lives in MFMA accumulator
+//    registers, and nothing but q, k, v, log_alpha, beta, o and the states
+//    touches HBM.  Wave w owns 32 state columns.
+//  * Every contraction runs on v_mfma_f32_16x16x32_bf16 with each fp32 operand
+//    split into hi + lo bf16 (three MFMAs per product, fp32 accumulation).  A
+//    single bf16 rounding of any computed operand would put the output error
+//    near 1e-2 relative; the split keeps it near 3e-5.
+//  * Accumulator tiles (S, Y, Unew) are fed straight back as MFMA B operands.
+//    A 16x16 accumulator holds rows 4*(lane/16)+e of its tile, so two stacked
+//    tiles form the 8 values a lane supplies for a 32-deep step once the
+//    reduction index is taken in the order kpos() below; the LDS-resident A
+//    operands are stored in that order, which costs nothing.
+//  * Decay factors are formed relative to the chunk midpoint for the C x C
+//    products (e^{b_r - b_m} and e^{b_m - b_i}), so their exponents stay within
+//    half a chunk's summed decay.
+//  * The (I + A)^{-1} solve is blocked 16 x 16 in fp32: one wave inverts the four
+//    diagonal blocks by substitution, the off-diagonal blocks follow in three
+//    block-row steps.
+//  * Few long sequences (the 64K-token workload has 32 heads): each sequence is
+//    cut into G segments.  Pass 1 runs segments 0..G-2 from a zero state and also
+//    carries the segment transition (the identity pushed through the same
+//    updates, which is linear in the state); a combine kernel chains
+//    S_entry(s+1) = Phi(s) S_entry(s) + S_loc(s); pass 2 reruns every segment from
+//    its entry state.  That fills the chip at the cost of a second pass.
+#include <algorithm>
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_launch.h"
 
 namespace kda {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16;
+
+constexpr int C = kChunk;
+
+// Position of reduction index L (0..31) inside a 32-deep MFMA step when the B
+// operand comes from two stacked accumulator tiles.
+__host__ __device__ constexpr int kpos(int L) {
+    return L < 16 ? 8 * (L >> 2) + (L & 3) : 8 * ((L - 16) >> 2) + 4 + ((L - 16) & 3);
+}
+__host__ __device__ constexpr int kperm(int x) { return (x & ~31) | kpos(x & 31); }
+
+__device__ __forceinline__ u16 bits(__bf16 h) { return __builtin_bit_cast(u16, h); }
+
+__device__ __forceinline__ void split2(float x, u16& hi, u16& lo) {
+    const __bf16 h = static_cast<__bf16>(x);
+    hi = bits(h);
+    lo = bits(static_cast<__bf16>(x - static_cast<float>(h)));
+}
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// (ah + al)(bh + bl) to fp32 accuracy, dropping only al*bl.
+__device__ __forceinline__ f32x4 mfma3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, f32x4 c) {
+    c = mfma(al, bh, c);
+    c = mfma(ah, bl, c);
+    return mfma(ah, bh, c);
+}
+
+__device__ __forceinline__ bf16x8 frag(const u16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+// Two stacked accumulator tiles -> hi/lo B operands of one 32-deep step.
+__device__ __forceinline__ void split_b(f32x4 t0, f32x4 t1, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const __bf16 h0 = static_cast<__bf16>(t0[e]);
+        const __bf16 h1 = static_cast<__bf16>(t1[e]);
+        hi[e] = h0;
+        hi[4 + e] = h1;
+        lo[e] = static_cast<__bf16>(t0[e] - static_cast<float>(h0));
+        lo[4 + e] = static_cast<__bf16>(t1[e] - static_cast<float>(h1));
+    }
+}
+
+__device__ __forceinline__ void store4(u16* p, const u16 (&x)[4]) {
+    uint2 w;
+    w.x = static_cast<uint32_t>(x[0]) | (static_cast<uint32_t>(x[1]) << 16);
+    w.y = static_cast<uint32_t>(x[2]) | (static_cast<uint32_t>(x[3]) << 16);
+    *reinterpret_cast<uint2*>(p) = w;
+}
+
+template <typename IN>
+__device__ __forceinline__ void load4(const typename IN::storage* p, size_t off, float (&out)[4]) {
+    if constexpr (std::is_same<IN, F32>::value) {
+        const float4 x = *reinterpret_cast<const float4*>(p + off);
+        out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
+    } else {
+        const uint2 x = *reinterpret_cast<const uint2*>(p + off);
+        out[0] = __uint_as_float(x.x << 16);
+        out[1] = __uint_as_float(x.x & 0xffff0000u);
+        out[2] = __uint_as_float(x.y << 16);
+        out[3] = __uint_as_float(x.y & 0xffff0000u);
+    }
+}
+
+// ------------------------------------------------------------------ LDS layout
+template <int D, int MODE>
+struct Smem {
+    static constexpr int PK = D + 8;   // pitch of [token][channel] planes (elements); 16-byte row skew
+    static constexpr int PT = C + 8;   // pitch of [row][token] planes
+    static constexpr int KT = (C * PK > D * PT) ? C * PK : D * PT;
+    static constexpr int NQ = MODE == 0 ? 2 : 1, QE = MODE == 0 ? C * PK : 8;
+    static constexpr int NP = MODE == 0 ? 2 : 1, PE = MODE == 0 ? C * PT : 8;
+    u16 kb[2][C * PK];       // Kbar_m = K e^{b - b_m}                 [token][kperm(channel)]
+    u16 qb[NQ][QE];          // Qbar_m = Q e^{b - b_m}                 [token][kperm(channel)]
+    u16 kt[2][KT];           // Ktil_m = K e^{b_m - b} [token][kperm(channel)], then
+                             // Khat^T = (K e^{b_n - b})^T               [channel][kperm(token)]
+    union {
+        float a[C * (C + 1)];     // A, then X = (I + A)^{-1} in place (fp32)
+        u16 t[2][C * PT];         // T = X Diag(beta)                    [token][kperm(token)]
+        float scan[16][D];        // per-thread-group decay sums
+    } at;
+    u16 p[NP][PE];           // P = Tril(Qbar Ktil^T)                   [token][kperm(token)]
+    float beta[C];
+    float em[D];             // e^{b_m}
+    float gam[D];            // gamma = e^{b_n}
+    float tmp[3][16][16];    // solve scratch
+};
+
+struct KernelArgs {
+    const void *q, *k, *v, *g, *beta;
+    const float* S0;
+    const int32_t* cu;
+    const int32_t* order;
+    void* o;
+    float* S_final;
+    float* phi;     // [G-1][N*H][D][D] segment transitions
+    float* sloc;    // [G-1][N*H][D][D] segment end states from a zero entry
+    float* se;      // [G-1][N*H][D][D] entry states of segments 1..G-1
+    int T, H, NH, G, cps, chunks;
+};
+
+template <int D, int MODE>
+constexpr int waves() { return MODE == 0 ? D / 32 : D / 16; }
+
+// MODE 0: outputs (o, S_final) from a known entry state.
+// MODE 1: segment summary (S_loc from a zero entry and the transition Phi).
+template <int D, typename IN, bool OUT_BF16, int MODE>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * waves<D, MODE>(), 64 * waves<D, MODE>()),
+                          amdgpu_waves_per_eu(1, 2)))
+void chunk_kernel(KernelArgs a) {
+    constexpr int NW = waves<D, MODE>();
+    constexpr int NT = 64 * NW;
+    constexpr int CQ = D / 4;          // channel quads
+    constexpr int TG = NT / CQ;        // token groups
+    constexpr int TPG = C / TG;        // tokens per thread
+    constexpr int RT = D / 16;         // state row tiles
+    constexpr int KS = D / 32;         // 32-deep steps over channels
+    constexpr int PK = Smem<D, MODE>::PK, PT = Smem<D, MODE>::PT;
+    static_assert(TPG % 4 == 0 && 32 % TPG == 0, "token grouping");
+    using ST = typename IN::storage;
+
+    __shared__ Smem<D, MODE> sm;
+
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, lr = l & 15;
+    const int H = a.H;
+
+    // ---------------------------------------------------------------- work unit
+    int n, h, s, c_begin, c_end;
+    long t0, t1;
+    if (a.cu) {
+        const int rank = blockIdx.x / H;
+        h = blockIdx.x % H;
+        n = a.order[rank];
+        t0 = a.cu[n];
+        t1 = a.cu[n + 1];
+        s = 0;
+        c_begin = 0;
+        c_end = static_cast<int>((t1 - t0 + C - 1) / C);
+    } else {
+        const int unit = blockIdx.x % a.NH;
+        s = blockIdx.x / a.NH;
+        n = unit / H;
+        h = unit % H;
+        t0 = static_cast<long>(n) * a.T;
+        t1 = t0 + a.T;
+        c_begin = s * a.cps;
+        c_end = min(c_begin + a.cps, a.chunks);
+    }
+    const int unit = n * H + h;
+    const size_t ubase = static_cast<size_t>(unit) * D * D;
+
+    const bool is_phi = MODE == 1 && w >= D / 32;
+    const int j0 = (MODE == 0 ? w : (w % (D / 32))) * 32;
+
+    // ---------------------------------------------------------------- entry state
+    f32x4 S[RT][2];
+    {
+        const float* src = nullptr;
+        if constexpr (MODE == 0) {
+            if (s == 0) src = a.S0 ? a.S0 + ubase : nullptr;
+            else src = a.se + (static_cast<size_t>(s - 1) * a.NH + unit) * D * D;
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = 16 * rt + 4 * g4 + e, col = j0 + 16 * ct + lr;
+                    S[rt][ct][e] = src ? src[row * D + col] : ((is_phi && row == col) ? 1.f : 0.f);
+                }
+    }
+    if constexpr (MODE == 0) {
+        // P's strictly-upper 16x16 tiles inside the 32-deep steps are read but never written.
+        for (int i = tid; i < 2 * C * PT; i += NT) sm.p[i / (C * PT)][i % (C * PT)] = 0;
+    }
+    __syncthreads();
+
+    const int cq = tid % CQ, tg = tid / CQ, c4 = 4 * cq;
+
+    for (int chunk = c_begin; chunk < c_end; ++chunk) {
+        const long ts = t0 + static_cast<long>(chunk) * C;
+        const int ntok = static_cast<int>(min(static_cast<long>(C), t1 - ts));
+
+        // ============================================================ phase A: loads, decay scan
+        float kr[TPG][4], qr[TPG][4], gr[TPG][4];
+#pragma unroll
+        for (int i = 0; i < TPG; ++i) {
+            const int r = tg * TPG + i;
+            if (r < ntok) {
+                const size_t off = (static_cast<size_t>(ts + r) * H + h) * D + c4;
+                load4<IN>(static_cast<const ST*>(a.k), off, kr[i]);
+                load4<IN>(static_cast<const ST*>(a.g), off, gr[i]);
+                if constexpr (MODE == 0) load4<IN>(static_cast<const ST*>(a.q), off, qr[i]);
+            } else {
+#pragma unroll
+                for (int ch = 0; ch < 4; ++ch) kr[i][ch] = gr[i][ch] = qr[i][ch] = 0.f;
+            }
+        }
+        // V in accumulator layout for this wave's columns
+        f32x4 V[4][2];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = 16 * rt + 4 * g4 + e;
+                    V[rt][ct][e] = (!is_phi && row < ntok)
+                        ? IN::to_f32(static_cast<const ST*>(a.v)[(static_cast<size_t>(ts + row) * H + h) * D + j0 + 16 * ct + lr])
+                        : 0.f;
+                }
+        if (tid < C)
+            sm.beta[tid] = tid < ntok ? IN::to_f32(static_cast<const ST*>(a.beta)[static_cast<size_t>(ts + tid) * H + h]) : 0.f;
+
+#pragma unroll
+        for (int i = 1; i < TPG; ++i)
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) gr[i][ch] += gr[i - 1][ch];
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch) sm.at.scan[tg][c4 + ch] = gr[TPG - 1][ch];
+        __syncthreads();
+
+        float off[4] = {0.f, 0.f, 0.f, 0.f}, bn[4] = {0.f, 0.f, 0.f, 0.f}, bm[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int gg = 0; gg < TG; ++gg)
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) {
+                const float x = sm.at.scan[gg][c4 + ch];
+                bn[ch] += x;
+                if (gg < tg) off[ch] += x;
+                if (gg < 32 / TPG) bm[ch] += x;
+            }
+
+        float ktk[TPG][4];   // Ktil_m kept for Khat^T after the C x C products
+        float enm[4];
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch) enm[ch] = fast_exp(bn[ch] - bm[ch]);
+#pragma unroll
+        for (int i = 0; i < TPG; ++i) {
+            const int r = tg * TPG + i;
+            u16 kh[4], kl[4], th[4], tl[4], qh[4], ql[4];
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) {
+                const float b = gr[i][ch] + off[ch];
+                const float em = fast_exp(b - bm[ch]);
+                const float ei = fast_exp(bm[ch] - b);
+                split2(kr[i][ch] * em, kh[ch], kl[ch]);
+                ktk[i][ch] = kr[i][ch] * ei;
+                split2(ktk[i][ch], th[ch], tl[ch]);
+                if constexpr (MODE == 0) split2(qr[i][ch] * em, qh[ch], ql[ch]);
+            }
+            const int idx = r * PK + kperm(c4);
+            store4(&sm.kb[0][idx], kh);
+            store4(&sm.kb[1][idx], kl);
+            store4(&sm.kt[0][idx], th);
+            store4(&sm.kt[1][idx], tl);
+            if constexpr (MODE == 0) {
+                store4(&sm.qb[0][idx], qh);
+                store4(&sm.qb[1][idx], ql);
+            }
+        }
+        if (tg == 0) {
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) {
+                sm.em[c4 + ch] = fast_exp(bm[ch]);
+                sm.gam[c4 + ch] = fast_exp(bn[ch]);
+            }
+        }
+        __syncthreads();
+
+        // ============================================================ phase B: A and P on MFMA
+        constexpr int NJOB = MODE == 0 ? 20 : 10;
+        for (int job = w; job < NJOB; job += NW) {
+            const bool isP = job >= 10;
+            const int tj = isP ? job - 10 : job;
+            const int rt = tj >= 6 ? 3 : tj >= 3 ? 2 : tj >= 1 ? 1 : 0;
+            const int ct = tj - rt * (rt + 1) / 2;
+            const u16* ah_base = &sm.kb[0][0];
+            const u16* al_base = &sm.kb[1][0];
+            if constexpr (MODE == 0) {
+                if (isP) { ah_base = &sm.qb[0][0]; al_base = &sm.qb[1][0]; }
+            }
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int ao = (16 * rt + lr) * PK + 32 * ks + 8 * g4;
+                const int bo = (16 * ct + lr) * PK + 32 * ks + 8 * g4;
+                acc = mfma3(frag(ah_base + ao), frag(al_base + ao), frag(&sm.kt[0][bo]), frag(&sm.kt[1][bo]), acc);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * rt + 4 * g4 + e, col = 16 * ct + lr;
+                if (!isP) {
+                    sm.at.a[row * (C + 1) + col] = col < row ? acc[e] * sm.beta[row] : 0.f;
+                } else if constexpr (MODE == 0) {
+                    u16 hi, lo;
+                    split2(col <= row ? acc[e] : 0.f, hi, lo);
+                    sm.p[0][row * PT + kperm(col)] = hi;
+                    sm.p[1][row * PT + kperm(col)] = lo;
+                }
+            }
+        }
+        __syncthreads();
+
+        // ============================================================ phase C: Khat^T (registers -> LDS)
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch) {
+            const int c = c4 + ch;
+#pragma unroll
+            for (int gq = 0; gq < TPG / 4; ++gq) {
+                u16 hi[4], lo[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) split2(ktk[4 * gq + j][ch] * enm[ch], hi[j], lo[j]);
+                const int idx = c * PT + kperm(tg * TPG + 4 * gq);
+                store4(&sm.kt[0][idx], hi);
+                store4(&sm.kt[1][idx], lo);
+            }
+        }
+
+        // ============================================================ phase D: T = (I + A)^{-1} Diag(beta)
+        if (w == 0) {
+            // one lane per column of each 16x16 diagonal block; forward substitution
+            const int blk = l >> 4, j = l & 15, o0 = 16 * blk;
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float acc = r == j ? 1.f : 0.f;
+#pragma unroll
+                for (int i = 0; i < r; ++i) acc -= sm.at.a[(o0 + r) * (C + 1) + o0 + i] * x[i];
+                x[r] = acc;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sm.at.a[(o0 + r) * (C + 1) + o0 + j] = x[r];
+        }
+        __syncthreads();
+        for (int bi = 1; bi < 4; ++bi) {
+            // Y_{bi,bj} = sum_{bk=bj}^{bi-1} A_{bi,bk} X_{bk,bj}
+            for (int idx = tid; idx < bi * 256; idx += NT) {
+                const int bj = idx >> 8, rr = (idx >> 4) & 15, cc = idx & 15;
+                float y = 0.f;
+                for (int bk = bj; bk < bi; ++bk)
+#pragma unroll
+                    for (int m = 0; m < 16; ++m)
+                        y += sm.at.a[(16 * bi + rr) * (C + 1) + 16 * bk + m] * sm.at.a[(16 * bk + m) * (C + 1) + 16 * bj + cc];
+                sm.tmp[bj][rr][cc] = y;
+            }
+            __syncthreads();
+            // X_{bi,bj} = -X_{bi,bi} Y_{bi,bj}, written over A_{bi,bj}
+            for (int idx = tid; idx < bi * 256; idx += NT) {
+                const int bj = idx >> 8, rr = (idx >> 4) & 15, cc = idx & 15;
+                float x = 0.f;
+#pragma unroll
+                for (int m = 0; m < 16; ++m) x -= sm.at.a[(16 * bi + rr) * (C + 1) + 16 * bi + m] * sm.tmp[bj][m][cc];
+                sm.at.a[(16 * bi + rr) * (C + 1) + 16 * bj + cc] = x;
+            }
+            __syncthreads();
+        }
+        {
+            constexpr int PER = C * C / NT;
+            float tv[PER];
+#pragma unroll
+            for (int u = 0; u < PER; ++u) {
+                const int idx = tid + u * NT, r = idx / C, i = idx % C;
+                tv[u] = i <= r ? sm.at.a[r * (C + 1) + i] * sm.beta[i] : 0.f;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < PER; ++u) {
+                const int idx = tid + u * NT, r = idx / C, i = idx % C;
+                u16 hi, lo;
+                split2(tv[u], hi, lo);
+                sm.at.t[0][r * PT + kperm(i)] = hi;
+                sm.at.t[1][r * PT + kperm(i)] = lo;
+            }
+        }
+        __syncthreads();
+
+        // ============================================================ phase E: state pass (per wave)
+        // B operands from Diag(e^{b_m}) S (the e^{b_m} completes Kbar_m / Qbar_m to Kbar / Qbar)
+        bf16x8 sbh[KS][2], sbl[KS][2];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                f32x4 x0 = S[2 * ks][ct], x1 = S[2 * ks + 1][ct];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x0[e] *= sm.em[32 * ks + 4 * g4 + e];
+                    x1[e] *= sm.em[32 * ks + 16 + 4 * g4 + e];
+                }
+                split_b(x0, x1, sbh[ks][ct], sbl[ks][ct]);
+            }
+        f32x4 Y[4][2], Z[4][2];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) Y[rt][ct] = Z[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int ao = (16 * rt + lr) * PK + 32 * ks + 8 * g4;
+                const bf16x8 kh = frag(&sm.kb[0][ao]), kl = frag(&sm.kb[1][ao]);
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) Y[rt][ct] = mfma3(kh, kl, sbh[ks][ct], sbl[ks][ct], Y[rt][ct]);
+                if constexpr (MODE == 0) {
+                    const bf16x8 qh = frag(&sm.qb[0][ao]), ql = frag(&sm.qb[1][ao]);
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct) Z[rt][ct] = mfma3(qh, ql, sbh[ks][ct], sbl[ks][ct], Z[rt][ct]);
+                }
+            }
+        // Unew = T (V - Kbar S)
+        bf16x8 dbh[2][2], dbl[2][2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+                split_b(V[2 * kt][ct] - Y[2 * kt][ct], V[2 * kt + 1][ct] - Y[2 * kt + 1][ct], dbh[kt][ct], dbl[kt][ct]);
+        f32x4 U[4][2];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) U[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int kt = 0; kt <= (rt >> 1); ++kt) {
+                const int ao = (16 * rt + lr) * PT + 32 * kt + 8 * g4;
+                const bf16x8 th = frag(&sm.at.t[0][ao]), tl = frag(&sm.at.t[1][ao]);
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) U[rt][ct] = mfma3(th, tl, dbh[kt][ct], dbl[kt][ct], U[rt][ct]);
+            }
+        bf16x8 ubh[2][2], ubl[2][2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) split_b(U[2 * kt][ct], U[2 * kt + 1][ct], ubh[kt][ct], ubl[kt][ct]);
+
+        if constexpr (MODE == 0) {
+            // O = Qbar S + P Unew
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int kt = 0; kt <= (rt >> 1); ++kt) {
+                    const int ao = (16 * rt + lr) * PT + 32 * kt + 8 * g4;
+                    const bf16x8 ph = frag(&sm.p[0][ao]), pl = frag(&sm.p[1][ao]);
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct) Z[rt][ct] = mfma3(ph, pl, ubh[kt][ct], ubl[kt][ct], Z[rt][ct]);
+                }
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int row = 16 * rt + 4 * g4 + e;
+                        if (row < ntok)
+                            store_out<OUT_BF16>(a.o, (static_cast<size_t>(ts + row) * H + h) * D + j0 + 16 * ct + lr,
+                                                Z[rt][ct][e]);
+                    }
+        }
+        // S <- Diag(gamma) S + Khat^T Unew
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) S[rt][ct][e] *= sm.gam[16 * rt + 4 * g4 + e];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                const int ao = (16 * rt + lr) * PT + 32 * kt + 8 * g4;
+                const bf16x8 kh = frag(&sm.kt[0][ao]), kl = frag(&sm.kt[1][ao]);
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) S[rt][ct] = mfma3(kh, kl, ubh[kt][ct], ubl[kt][ct], S[rt][ct]);
+            }
+        __syncthreads();
+    }
+
+    // ---------------------------------------------------------------- exit state
+    float* dst = nullptr;
+    if constexpr (MODE == 0) {
+        if ((a.cu || s == a.G - 1) && a.S_final) dst = a.S_final + ubase;
+    } else {
+        dst = (is_phi ? a.phi : a.sloc) + (static_cast<size_t>(s) * a.NH + unit) * D * D;
+    }
+    if (dst) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    dst[(16 * rt + 4 * g4 + e) * D + j0 + 16 * ct + lr] = S[rt][ct][e];
+    }
+}
+
+// Entry states of segments 1..G-1:  S_e(s) = Phi(s-1) S_e(s-1) + S_loc(s-1), S_e(0) = S0.
+// One workgroup per (unit, 16-column slice); fp32 on the vector ALUs.
+template <int D>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ S0, const float* __restrict__ phi,
+                                                      const float* __restrict__ sloc, float* __restrict__ se,
+                                                      int NH, int G) {
+    constexpr int CPT = 16 * D / 256;   // columns per thread
+    constexpr int TPR = 16 / CPT;       // threads per row
+    __shared__ float cur[D][16];
+    const int unit = blockIdx.x, c0 = blockIdx.y * 16, tid = threadIdx.x;
+    const int r = tid / TPR, cc = (tid % TPR) * CPT;
+    const size_t ub = static_cast<size_t>(unit) * D * D;
+    for (int j = 0; j < CPT; ++j) cur[r][cc + j] = S0 ? S0[ub + r * D + c0 + cc + j] : 0.f;
+    __syncthreads();
+    for (int s = 1; s < G; ++s) {
+        const size_t sb = (static_cast<size_t>(s - 1) * NH + unit) * D * D;
+        float acc[CPT];
+        for (int j = 0; j < CPT; ++j) acc[j] = sloc[sb + r * D + c0 + cc + j];
+        const float* prow = phi + sb + static_cast<size_t>(r) * D;
+        for (int m = 0; m < D; ++m) {
+            const float p = prow[m];
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) acc[j] += p * cur[m][cc + j];
+        }
+        __syncthreads();
+        for (int j = 0; j < CPT; ++j) {
+            cur[r][cc + j] = acc[j];
+            se[sb + r * D + c0 + cc + j] = acc[j];
+        }
+        __syncthreads();
+    }
+}
+
+// Longest-first order of packed sequences (ties by index); O(N^2), N is small.
+__global__ __launch_bounds__(256) void order_kernel(const int32_t* __restrict__ cu, int32_t* __restrict__ order, int N) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= N) return;
+    const int li = cu[i + 1] - cu[i];
+    int rank = 0;
+    for (int m = 0; m < N; ++m) {
+        const int lm = cu[m + 1] - cu[m];
+        rank += (lm > li) || (lm == li && m < i);
+    }
+    order[rank] = i;
+}
+
+template <int D, typename IN, bool OB>
+hipError_t launch_variant(const PrefillArgs& pa, const PrefillPlan& plan, hipStream_t stream) {
+    KernelArgs a;
+    a.q = pa.q; a.k = pa.k; a.v = pa.v; a.g = pa.g; a.beta = pa.beta;
+    a.S0 = pa.S0; a.cu = pa.cu; a.o = pa.o; a.S_final = pa.S_final;
+    a.T = pa.T; a.H = pa.H; a.NH = pa.N * pa.H; a.G = plan.G; a.cps = plan.cps; a.chunks = plan.chunks;
+    char* ws = static_cast<char*>(pa.workspace);
+    a.order = pa.cu ? reinterpret_cast<const int32_t*>(ws + plan.off_order) : nullptr;
+    a.phi = plan.G > 1 ? reinterpret_cast<float*>(ws + plan.off_phi) : nullptr;
+    a.sloc = plan.G > 1 ? reinterpret_cast<float*>(ws + plan.off_sloc) : nullptr;
+    a.se = plan.G > 1 ? reinterpret_cast<float*>(ws + plan.off_se) : nullptr;
+    const int NH = a.NH;
+    if (pa.cu) {
+        hipLaunchKernelGGL(order_kernel, dim3((pa.N + 255) / 256), dim3(256), 0, stream, pa.cu,
+                           reinterpret_cast<int32_t*>(ws + plan.off_order), pa.N);
+        hipLaunchKernelGGL((chunk_kernel<D, IN, OB, 0>), dim3(NH), dim3(64 * waves<D, 0>()), 0, stream, a);
+        return hipGetLastError();
+    }
+    if (plan.G > 1) {
+        hipLaunchKernelGGL((chunk_kernel<D, IN, OB, 1>), dim3(NH * (plan.G - 1)), dim3(64 * waves<D, 1>()), 0,
+                           stream, a);
+        hipLaunchKernelGGL(combine_kernel<D>, dim3(NH, D / 16), dim3(256), 0, stream, pa.S0, a.phi, a.sloc, a.se,
+                           NH, plan.G);
+    }
+    hipLaunchKernelGGL((chunk_kernel<D, IN, OB, 0>), dim3(NH * plan.G), dim3(64 * waves<D, 0>()), 0, stream, a);
+    return hipGetLastError();
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace
 
 PrefillPlan plan_prefill(int B, int T, int H, int D, int N, bool varlen) {
     PrefillPlan p;
-    (void)B; (void)T; (void)H; (void)D; (void)N; (void)varlen;
+    if (varlen) {
+        p.G = 1;
+        p.off_order = 0;
+        p.workspace_bytes = align256(static_cast<size_t>(N) * sizeof(int32_t));
+        return p;
+    }
+    (void)B;
+    p.chunks = (T + C - 1) / C;
+    const long units = static_cast<long>(N) * H;
+    int G = 1;
+    if (units > 0 && units < kTargetWorkgroups && p.chunks >= 2 * kMinChunksPerSegment) {
+        G = static_cast<int>((kTargetWorkgroups + units - 1) / units);
+        G = std::min(G, p.chunks / kMinChunksPerSegment);
+        G = std::max(G, 1);
+    }
+    p.cps = p.chunks > 0 ? (p.chunks + G - 1) / G : 0;
+    p.G = p.cps > 0 ? (p.chunks + p.cps - 1) / p.cps : 1;
+    if (p.G > 1) {
+        const size_t mat = static_cast<size_t>(units) * (p.G - 1) * D * D * sizeof(float);
+        p.off_phi = 0;
+        p.off_sloc = align256(mat);
+        p.off_se = 2 * align256(mat);
+        p.workspace_bytes = 3 * align256(mat);
+    }
     return p;
 }
 
-hipError_t launch_prefill(const PrefillArgs&, const PrefillPlan&, hipStream_t) {
-    return hipErrorNotSupported;
+hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan, hipStream_t stream) {
+#define KDA_PREFILL_CASE(DD, INT, OB)                                                     \
+    if (a.D == DD && a.in_bf16 == std::is_same<INT, BF16>::value && a.out_bf16 == OB)     \
+        return launch_variant<DD, INT, OB>(a, plan, stream);
+    KDA_PREFILL_CASE(128, BF16, true)
+    KDA_PREFILL_CASE(128, BF16, false)
+    KDA_PREFILL_CASE(128, F32, true)
+    KDA_PREFILL_CASE(128, F32, false)
+    KDA_PREFILL_CASE(64, BF16, true)
+    KDA_PREFILL_CASE(64, BF16, false)
+    KDA_PREFILL_CASE(64, F32, true)
+    KDA_PREFILL_CASE(64, F32, false)
+#undef KDA_PREFILL_CASE
+    return hipErrorInvalidValue;
 }
 
 }  // namespace kda

@@ -1,0 +1,159 @@
+"""Prefill parity on the GPU: kda_chunk_fwd (HIP, through the C ABI) vs the fp64
+CPU oracle on the same seeded inputs.
+
+Shapes span several chunks and a ragged tail, packed variable-length batches with
+empty sequences, the segmented (two-pass) path for few long sequences, fast-decay
+mixtures and both head sizes.  Pages: "Decoding Hybrid Attention Architectures"
+(intl.cloud.baidu.com article 9569726) sections 3.4 and 4.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+from gated_delta_rule_62_amd import inputs
+from gpu_util import TOL_BF16, TOL_F32, o_metric, state_metric, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+W = inputs.WORKLOADS
+
+
+def _kda():
+    from gated_delta_rule_62_amd import kda
+    kda.load_library()
+    return kda
+
+
+def gpu_fwd(d, out_dtype=torch.float32):
+    kda = _kda()
+    dev = {kk: to_dev(d[kk]) for kk in ("q", "k", "v", "log_alpha", "beta")}
+    S0 = to_dev(d["S0"]) if d["S0"] is not None else None
+    cu = to_dev(d["cu_seqlens"]) if d["cu_seqlens"] is not None else None
+    o, Sf = kda.kda_chunk_fwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], S0, cu,
+                              out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return to_host(o), to_host(Sf)
+
+
+def oracle_fwd(d, heads=None):
+    sel = slice(None) if heads is None else heads
+    args = [d[kk][:, :, sel] for kk in ("q", "k", "v", "log_alpha", "beta")]
+    S0 = None if d["S0"] is None else d["S0"][:, sel]
+    return oracle.kda_fwd(*args, S0=S0, cu_seqlens=d["cu_seqlens"], o_dtype=np.float64)
+
+
+def check(d, label, heads=None):
+    print(f"[prefill] {label}: B={d['B']} T={d['T']} H={d['H']} D={d['D']} N={d['N']} dtype={d['dtype']}",
+          flush=True)
+    o, Sf = gpu_fwd(d)
+    o_ref, S_ref = oracle_fwd(d, heads)
+    if heads is not None:
+        o, Sf = o[:, :, heads], Sf[:, heads]
+    eo = o_metric(o, o_ref, d["cu_seqlens"])
+    es = state_metric(Sf, S_ref)
+    tol = TOL_F32 if d["dtype"] == "f32" else TOL_BF16
+    print(f"[prefill]   worst o {eo:.3e}  S_final {es:.3e}  (tol {tol})", flush=True)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(Sf))
+    assert eo <= tol and es <= tol
+    return eo, es
+
+
+def test_tiny_fp32_workload():
+    """Workload 0 exactly: B=1, H=2, T=256, d=64, fp32."""
+    check(inputs.make_prefill(W[0]), "workload0")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_ragged_tail_with_initial_state(D):
+    d = inputs.make_prefill(W[1], seed=201, B=2, T=300, H=2, D=D, s0=True)
+    check(d, f"ragged D={D}")
+
+
+def test_fp32_inputs_d128():
+    d = inputs.make_prefill(W[1], seed=202, B=1, T=200, H=2, D=128, dtype="f32", s0=True)
+    check(d, "fp32 d128")
+
+
+def test_segmented_two_pass_path():
+    """Few (sequence, head) units and many chunks: the sequence is cut into
+    segments (segment summaries, combine, rerun)."""
+    kda = _kda()
+    plan_ws = kda.kda_chunk_fwd_workspace_bytes(1, 1000, 2, 128, 128, 1, False)
+    assert plan_ws > 0, "expected the segmented path for 2 units x 16 chunks"
+    d = inputs.make_prefill(W[2], seed=203, B=1, T=1000, H=2, s0=True)
+    check(d, "segmented slow-decay")
+    d = inputs.make_prefill(W[1], seed=204, B=2, T=777, H=3, s0=True)
+    check(d, "segmented ragged")
+
+
+def test_varlen_packed_with_empty_sequences():
+    d = inputs.make_prefill(W[4], seed=205, H=3, lengths=[70, 0, 1, 64, 200, 0, 129])
+    d["S0"] = (0.02 * np.random.default_rng(5).standard_normal((d["N"], 3, 128, 128))).astype(np.float32)
+    check(d, "varlen + S0")
+
+
+def test_fast_decay_mixture():
+    d = inputs.make_prefill(W[4], seed=206, H=2, lengths=[300, 190])
+    check(d, "mixture decay")
+
+
+def test_bf16_output_is_rne_of_fp32_output():
+    d = inputs.make_prefill(W[1], seed=207, B=1, T=130, H=2, s0=True)
+    o32, S32 = gpu_fwd(d, torch.float32)
+    o16, S16 = gpu_fwd(d, torch.bfloat16)
+    assert np.array_equal(S32, S16)
+    r = inputs.bf16_bits_to_f32(inputs.f32_to_bf16_bits(o32))
+    assert np.array_equal(r, o16)
+
+
+def test_run_to_run_bitwise_deterministic():
+    d = inputs.make_prefill(W[2], seed=208, B=1, T=900, H=2, s0=True)
+    a = gpu_fwd(d)
+    b = gpu_fwd(d)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_split_resume_matches_single_call():
+    """Prefill of [0, t) then [t, T) with S0 = S_final of the first equals one call."""
+    d = inputs.make_prefill(W[1], seed=209, B=1, T=400, H=2, s0=True)
+    o, Sf = gpu_fwd(d)
+    cut = 150
+    first = dict(d, T=cut, **{kk: d[kk][:, :cut] for kk in ("q", "k", "v", "log_alpha", "beta")})
+    o1, S1 = gpu_fwd(first)
+    second = dict(d, T=400 - cut, S0=S1, **{kk: d[kk][:, cut:] for kk in ("q", "k", "v", "log_alpha", "beta")})
+    o2, S2 = gpu_fwd(second)
+    # Exact in real arithmetic; the split moves chunk boundaries, so each side carries
+    # its own rounding (each within the parity error of ~5e-5): allow twice the fp32 bound.
+    assert o_metric(np.concatenate([o1, o2], axis=1), o) <= 2 * TOL_F32
+    assert state_metric(S2, Sf) <= 2 * TOL_F32
+
+
+def test_empty_inputs():
+    kda = _kda()
+    H, D = 2, 128
+    e = torch.empty((1, 0, H, D), dtype=torch.bfloat16, device="cuda")
+    eb = torch.empty((1, 0, H), dtype=torch.bfloat16, device="cuda")
+    S0 = torch.randn(1, H, D, D, device="cuda")
+    o, Sf = kda.kda_chunk_fwd(e, e, e, e, eb, S0)
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and torch.equal(Sf, S0)
+
+
+def test_rejects_bad_arguments():
+    kda = _kda()
+    d = inputs.make_prefill(W[1], seed=210, B=2, T=64, H=2)
+    dev = {kk: to_dev(d[kk]) for kk in ("q", "k", "v", "log_alpha", "beta")}
+    cu = torch.tensor([0, 64, 128], dtype=torch.int32, device="cuda")
+    with pytest.raises(kda.KDAError) as e:       # cu_seqlens needs B == 1
+        kda.kda_chunk_fwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], None, cu)
+    assert e.value.status == kda.KDA_ERR_INVALID_ARGUMENT
+    with pytest.raises(kda.KDAError) as e:       # chunk size not built
+        kda.kda_chunk_fwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], chunk=32)
+    assert e.value.status == kda.KDA_ERR_UNSUPPORTED
+    with pytest.raises(kda.KDAError) as e:       # o aliasing an input
+        kda.kda_chunk_fwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], o=dev["v"])
+    assert e.value.status == kda.KDA_ERR_INVALID_ARGUMENT
