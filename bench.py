@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA layer on one MI355X.
+
+A step is one prefill call (``kda_chunk_fwd``) on the long-context workload:
+B=1, H=32, T=65536, d_k=d_v=128, bf16 q/k/v/log_alpha/beta, fp32 initial state
+S0 ~ 0.02*N(0,1), bf16 o and fp32 S_final, chunk 64.  ``value`` is prefill
+tokens/s (sequence tokens, not token-heads) with the inputs resident in HBM.
+
+The same JSON line also reports the decode workload (256 sequences x 32 heads,
+d=128, 1024 sequential ``kda_recurrent_step`` calls on an fp32 state) as
+``decode``, the roofline of each path's dominant launch measured with HIP events
+on the launch stream, and the fp64 CPU oracle timed on a bounded sample of the
+same workloads on this host (``cpu_baseline``).
+
+Inputs are synthetic and seeded, drawn on the GPU with the workloads' recipe
+(q, k L2-normalised normals, v normal, beta = sigmoid(normal), log_alpha =
+logsigmoid(normal + mu)/s); the parity tests draw the same recipe on the host.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s (H32,d128,T64K) + decode steps/s and HBM GB/s"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+CHUNK = 64
+
+
+def prefill_alg_flops_per_token_head(d: int, C: int = CHUNK) -> int:
+    """Flops the chunkwise method needs per (token, head), counting only the
+    needed triangles: A (C-1)d, P (C+1)d, W and U 2(C+1)d, P*Unew (C+1)d,
+    and 6d^2 for K S, Q S and Khat^T Unew.  The (I+A)^-1 solve is excluded."""
+    return 6 * d * d + (C - 1) * d + 4 * (C + 1) * d
+
+
+def prefill_alg_bytes(T: int, H: int, d: int, n_seqs: int, has_s0: bool) -> int:
+    """q, k, v, log_alpha, beta read once, o written once (bf16), S0 read and
+    S_final written once (fp32)."""
+    per_token_head = 4 * d * 2 + 2 + d * 2
+    states = n_seqs * H * d * d * 4 * (2 if has_s0 else 1)
+    return T * H * per_token_head + states
+
+
+def decode_alg_bytes(N: int, H: int, d: int) -> int:
+    """State read and written once (fp32), q, k, v, log_alpha and o (bf16), beta."""
+    return 2 * N * H * d * d * 4 + 4 * N * H * d * 2 + N * H * 2 + N * H * d * 2
+
+
+def bf16_to_bits(torch, t):
+    from gated_delta_rule_62_amd.inputs import host_bits
+    return host_bits(t)
+
+
+def cpu_baseline_prefill(torch, q, k, v, la, beta, S0, target_s=10.0):
+    """Time the fp64 CPU oracle on the first T_s tokens (all heads) of the same
+    inputs; T_s is sized from a short calibration run to about target_s seconds."""
+    import oracle
+    T = q.shape[1]
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    H = q.shape[2]
+    threads = min(cores, oracle.max_threads(), H)
+
+    def run(Ts):
+        args = [bf16_to_bits(torch, x[:, :Ts]) for x in (q, k, v, la, beta)]
+        s0 = S0.detach().cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.kda_fwd(*args, S0=s0, num_threads=threads)
+        return time.perf_counter() - t0
+
+    cal = min(T, 1024)
+    dt = run(cal)
+    Ts = int(min(T, max(cal, cal * target_s / max(dt, 1e-6))))
+    Ts = max(CHUNK, (Ts // CHUNK) * CHUNK)
+    dt = run(Ts)
+    return {"value": Ts / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {Ts} of {T} tokens, all {H} heads (fp64 token recurrence, "
+                      f"OpenMP over heads), {dt:.1f} s"}
+
+
+def cpu_baseline_decode(torch, steps_inputs, S, target_s=8.0):
+    """Time the oracle's decode step on all sequences of the decode workload for
+    as many of the same steps as fit in about target_s seconds of oracle time."""
+    import numpy as np
+    import oracle
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    threads = min(cores, oracle.max_threads())
+    S64 = S.detach().cpu().numpy().astype(np.float64)
+    done, total = 0, 0.0
+    while total < target_s and done < len(steps_inputs):
+        x = [bf16_to_bits(torch, t) for t in steps_inputs[done]]
+        ts = time.perf_counter()
+        oracle.kda_step(*x, S64, num_threads=threads)
+        total += time.perf_counter() - ts
+        done += 1
+    return {"value": done / total, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"the first {done} steps of the decode workload, all {S.shape[0]}x{S.shape[1]} heads "
+                      f"(fp64, OpenMP over heads), {total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the KDA layer here is built and timed on a single MI355X; "
+              "--gpus must be 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_delta_rule_62_amd import kda
+    kda.load_library()
+    torch.cuda.init()
+    stream = torch.cuda.current_stream()
+
+    # ------------------------------------------------------------------ prefill (headline)
+    from gated_delta_rule_62_amd import inputs
+    w2 = inputs.WORKLOADS[2]
+    B, T, H, d = w2.B, w2.T, w2.H, w2.D
+    x = inputs.device_prefill(w2)
+    q, k, v, la, beta, S0 = x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"]
+    o = torch.empty((B, T, H, d), dtype=torch.bfloat16, device="cuda")
+    Sf = torch.empty((B, H, d, d), dtype=torch.float32, device="cuda")
+    ws_bytes = kda.kda_chunk_fwd_workspace_bytes(B, T, H, d, d, B, False)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+
+    def call():
+        kda.kda_chunk_fwd(q, k, v, la, beta, S0, None, o=o, S_final=Sf, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start = time.perf_counter()
+    torch.cuda.synchronize()
+    e_all0 = torch.cuda.Event(enable_timing=True)
+    e_all1 = torch.cuda.Event(enable_timing=True)
+    e_all0.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        call()
+        ev[i][1].record(stream)
+    e_all1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_total = e_all0.elapsed_time(e_all1)
+    ms_step = ms_total / args.steps
+    call_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    call_avg_ms = sum(call_ms) / len(call_ms)
+    tokens = B * T
+    value = tokens / (ms_step / 1e3)
+    flops = prefill_alg_flops_per_token_head(d) * tokens * H
+    byts = prefill_alg_bytes(tokens, H, d, B, True)
+    tflops = flops / (call_avg_ms / 1e3) / 1e12
+    gbs = byts / (call_avg_ms / 1e3) / 1e9
+
+    # ------------------------------------------------------------------ decode
+    w3 = inputs.WORKLOADS[3]
+    N, Hd = w3.num_seqs, w3.H
+    S_init, steps_in = inputs.device_decode_steps(w3, args.decode_steps)
+    S = torch.empty_like(S_init)
+    od = torch.empty((N, Hd, d), dtype=torch.bfloat16, device="cuda")
+    S.copy_(S_init)
+    for i in range(8):
+        kda.kda_recurrent_step(*steps_in[i], S, o=od, stream=stream)
+    dec_ms, step_ms = [], []
+    for rep in range(3):
+        S.copy_(S_init)
+        torch.cuda.synchronize()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.decode_steps + 1)]
+        evs[0].record(stream)
+        for i in range(args.decode_steps):
+            kda.kda_recurrent_step(*steps_in[i], S, o=od, stream=stream)
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        dec_ms.append(evs[0].elapsed_time(evs[-1]))
+        step_ms.extend(evs[i].elapsed_time(evs[i + 1]) for i in range(args.decode_steps))
+    dec_ms.sort()
+    dec_med = dec_ms[len(dec_ms) // 2]
+    step_avg = sum(step_ms) / len(step_ms)
+    dbytes = decode_alg_bytes(N, Hd, d)
+    decode = {
+        "value": args.decode_steps / (dec_med / 1e3), "unit": "steps/s",
+        "ms_per_step": dec_med / args.decode_steps,
+        "hbm_gbs": dbytes / (step_avg / 1e3) / 1e9,
+        "config": {"workload": "decode", "sequences": N, "H": Hd, "d_k": d, "d_v": d,
+                   "steps": args.decode_steps, "in_dtype": "bf16", "out_dtype": "bf16", "state": "fp32"},
+        "roofline": {"bound": "hbm", "achieved": dbytes / (step_avg / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": dbytes / (step_avg / 1e3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "decode_step_kernel<128,BF16,bf16 out>", "avg_launch_us": step_avg * 1e3,
+                     "bytes_per_launch": dbytes},
+    }
+
+    # ------------------------------------------------------------------ CPU baselines (oracle)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_prefill(torch, q, k, v, la, beta, S0)
+        S.copy_(S_init)
+        decode["cpu_baseline"] = cpu_baseline_decode(torch, steps_in, S_init)
+
+    plan_G = "segments" if ws_bytes > 0 else "single pass"
+    out = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "long_context_prefill", "B": B, "T": T, "H": H, "d_k": d, "d_v": d,
+                   "chunk": CHUNK, "in_dtype": "bf16", "out_dtype": "bf16", "state": "fp32", "S0": "0.02*N(0,1)",
+                   "log_alpha": "logsigmoid(N(0,1)+6)/16",
+                   "precision": "split-bf16 MFMA operands (hi+lo), fp32 accumulation and state",
+                   "schedule": plan_G},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None,
+                     "launch": "kda_chunk_fwd (all prefill kernels of one call)",
+                     "avg_launch_us": call_avg_ms * 1e3, "flops_per_launch": flops,
+                     "flop_convention": f"algorithmic, {prefill_alg_flops_per_token_head(d)} per token-head at C=64",
+                     "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS, "bytes_per_launch": byts},
+        "cpu_baseline": cpu,
+        "decode": decode,
+        "wall_s": wall,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

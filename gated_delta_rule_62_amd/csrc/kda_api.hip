@@ -45,8 +45,8 @@ extern "C" const char* kda_status_string(kda_status s) {
 extern "C" size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int num_seqs,
                                                 int has_cu_seqlens, int chunk) {
     if (B < 0 || T < 0 || H <= 0 || num_seqs < 0 || !head_ok(Dk, Dv)) return 0;
-    if (chunk != 0 && chunk != kda::kChunk) return 0;
-    kda::PrefillPlan plan = kda::plan_prefill(B, T, H, Dk, num_seqs, has_cu_seqlens != 0);
+    if (!kda::chunk_supported(chunk)) return 0;
+    kda::PrefillPlan plan = kda::plan_prefill(B, T, H, Dk, num_seqs, has_cu_seqlens != 0, chunk);
     return plan.workspace_bytes;
 }
 
@@ -58,7 +58,7 @@ extern "C" kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
     if (B < 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || num_seqs < 0) return KDA_ERR_INVALID_ARGUMENT;
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_UNSUPPORTED;
     if (!head_ok(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
-    if (chunk != 0 && chunk != kda::kChunk) return KDA_ERR_UNSUPPORTED;
+    if (!kda::chunk_supported(chunk)) return KDA_ERR_UNSUPPORTED;
     if (cu_seqlens) {
         if (B != 1) return KDA_ERR_INVALID_ARGUMENT;
         if (!aligned16(cu_seqlens)) return KDA_ERR_INVALID_ARGUMENT;
@@ -90,7 +90,7 @@ extern "C" kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
     if (overlap(S0, n_s, S_final, n_s) || overlap(S0, n_s, o, n_o) || overlap(o, n_o, S_final, n_s))
         return KDA_ERR_INVALID_ARGUMENT;
 
-    kda::PrefillPlan plan = kda::plan_prefill(B, T, H, Dk, num_seqs, cu_seqlens != nullptr);
+    kda::PrefillPlan plan = kda::plan_prefill(B, T, H, Dk, num_seqs, cu_seqlens != nullptr, chunk);
     if (workspace_bytes < plan.workspace_bytes) return KDA_ERR_WORKSPACE_TOO_SMALL;
     if (plan.workspace_bytes > 0 && (!workspace || !aligned16(workspace))) return KDA_ERR_INVALID_ARGUMENT;
     if (num_seqs == 0) return KDA_OK;

@@ -8,9 +8,11 @@
 
 namespace kda {
 
-constexpr int kChunk = 64;            // chunk length C (tokens)
-constexpr int kTargetWorkgroups = 256;  // one prefill workgroup per compute unit fills the chip
+constexpr int kDefaultChunk = 32;     // chunk length C (tokens) when the caller passes 0
+constexpr int kComputeUnits = 256;    // MI355X
 constexpr int kMinChunksPerSegment = 4;
+
+inline bool chunk_supported(int c) { return c == 0 || c == 32 || c == 64; }
 
 // How a prefill call is split into kernels.
 //  G == 1: one pass, one workgroup per (sequence, head).
@@ -20,6 +22,7 @@ constexpr int kMinChunksPerSegment = 4;
 //         the segment entry states; pass 2 reruns every segment from its true
 //         entry state and writes o and S_final.
 struct PrefillPlan {
+    int chunk = kDefaultChunk;
     int G = 1;
     int chunks = 0;        // chunks per sequence (equal-length case)
     int cps = 0;           // chunks per segment
@@ -38,7 +41,7 @@ struct PrefillArgs {
     bool in_bf16, out_bf16;
 };
 
-PrefillPlan plan_prefill(int B, int T, int H, int D, int N, bool varlen);
+PrefillPlan plan_prefill(int B, int T, int H, int D, int N, bool varlen, int chunk);
 hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan, hipStream_t stream);
 
 hipError_t launch_decode(int D, bool in_bf16, bool out_bf16, const void* q, const void* k,

@@ -57,8 +57,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16;
 
-constexpr int C = kChunk;
-
 // Position of reduction index L (0..31) inside a 32-deep MFMA step when the B
 // operand comes from two stacked accumulator tiles.
 __host__ __device__ constexpr int kpos(int L) {
@@ -121,28 +119,65 @@ __device__ __forceinline__ void load4(const typename IN::storage* p, size_t off,
     }
 }
 
-// ------------------------------------------------------------------ LDS layout
-template <int D, int MODE>
-struct Smem {
-    static constexpr int PK = D + 8;   // pitch of [token][channel] planes (elements); 16-byte row skew
-    static constexpr int PT = C + 8;   // pitch of [row][token] planes
+// ------------------------------------------------------------------ compile-time shape
+template <int D, int C, int MODE>
+struct Cfg {
+    static constexpr int NW = MODE == 0 ? D / 32 : D / 16;   // waves; each owns 32 state columns
+    static constexpr int NT = 64 * NW;
+    static constexpr int CQ = D / 4;                           // channel quads
+    static constexpr int TPG = (C * CQ / NT) > 4 ? (C * CQ / NT) : 4;   // tokens per loader thread
+    static constexpr int TGA = C / TPG;                        // token groups in the element phase
+    static constexpr int NA = TGA * CQ;                        // threads in the element phase
+    static constexpr int NRT = C / 16, NKT = C / 32;           // token row tiles, 32-deep token steps
+    static constexpr int RT = D / 16, KS = D / 32;             // state row tiles, 32-deep channel steps
+    static constexpr int PK = D + 8;                           // pitch of [token][channel] planes
+    static constexpr int PT = C + 8;                           // pitch of [row][token] planes
+    static constexpr int NB = C / 16;                          // 16x16 blocks of the solve
+    static constexpr int NTRI = NRT * (NRT + 1) / 2;           // lower 16x16 tiles of a C x C product
     static constexpr int KT = (C * PK > D * PT) ? C * PK : D * PT;
-    static constexpr int NQ = MODE == 0 ? 2 : 1, QE = MODE == 0 ? C * PK : 8;
-    static constexpr int NP = MODE == 0 ? 2 : 1, PE = MODE == 0 ? C * PT : 8;
-    u16 kb[2][C * PK];       // Kbar_m = K e^{b - b_m}                 [token][kperm(channel)]
+    // Two workgroups share a compute unit when the operands of a chunk fit in half the LDS.
+    static constexpr int WPE = (C == 32 && MODE == 0) ? 2 : 1;
+    static_assert(TPG % 4 == 0 && (C / 2) % TPG == 0 && NA <= NT && NA % 64 == 0, "element-phase tiling");
+};
+
+// ------------------------------------------------------------------ LDS layout
+template <int D, int C, int MODE>
+struct Smem {
+    using K = Cfg<D, C, MODE>;
+    static constexpr int NQ = MODE == 0 ? 2 : 1, QE = MODE == 0 ? C * K::PK : 8;
+    static constexpr int NP = MODE == 0 ? 2 : 1, PE = MODE == 0 ? C * K::PT : 8;
+    u16 kb[2][C * K::PK];    // Kbar_m = K e^{b - b_m}                 [token][kperm(channel)]
     u16 qb[NQ][QE];          // Qbar_m = Q e^{b - b_m}                 [token][kperm(channel)]
-    u16 kt[2][KT];           // Ktil_m = K e^{b_m - b} [token][kperm(channel)], then
+    u16 kt[2][K::KT];        // Ktil_m = K e^{b_m - b} [token][kperm(channel)], then
                              // Khat^T = (K e^{b_n - b})^T               [channel][kperm(token)]
     union {
         float a[C * (C + 1)];     // A, then X = (I + A)^{-1} in place (fp32)
-        u16 t[2][C * PT];         // T = X Diag(beta)                    [token][kperm(token)]
-        float scan[16][D];        // per-thread-group decay sums
+        u16 t[2][C * K::PT];      // T = X Diag(beta)                    [token][kperm(token)]
+        float scan[K::TGA][D];    // per-token-group decay sums
     } at;
     u16 p[NP][PE];           // P = Tril(Qbar Ktil^T)                   [token][kperm(token)]
     float beta[C];
     float em[D];             // e^{b_m}
     float gam[D];            // gamma = e^{b_n}
-    float tmp[3][16][16];    // solve scratch
+    float tmp[K::NB > 1 ? K::NB - 1 : 1][16][16];   // solve scratch
+};
+
+// Raw (undecoded) input registers: bf16 stays packed until it is used.
+template <typename IN> struct Raw;
+template <> struct Raw<BF16> {
+    using quad = uint2;
+    using elem = uint16_t;
+    static __device__ __forceinline__ float get(const uint2& x, int ch) {
+        const uint32_t w = ch < 2 ? x.x : x.y;
+        return __uint_as_float((ch & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+};
+template <> struct Raw<F32> {
+    using quad = float4;
+    using elem = float;
+    static __device__ __forceinline__ float get(const float4& x, int ch) {
+        return ch == 0 ? x.x : ch == 1 ? x.y : ch == 2 ? x.z : x.w;
+    }
 };
 
 struct KernelArgs {
@@ -158,27 +193,22 @@ struct KernelArgs {
     int T, H, NH, G, cps, chunks;
 };
 
-template <int D, int MODE>
-constexpr int waves() { return MODE == 0 ? D / 32 : D / 16; }
-
 // MODE 0: outputs (o, S_final) from a known entry state.
 // MODE 1: segment summary (S_loc from a zero entry and the transition Phi).
-template <int D, typename IN, bool OUT_BF16, int MODE>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * waves<D, MODE>(), 64 * waves<D, MODE>()),
-                          amdgpu_waves_per_eu(1, 2)))
+template <int D, int C, typename IN, bool OUT_BF16, int MODE>
+__global__ __attribute__((amdgpu_flat_work_group_size(Cfg<D, C, MODE>::NT, Cfg<D, C, MODE>::NT),
+                          amdgpu_waves_per_eu(Cfg<D, C, MODE>::NW * Cfg<D, C, MODE>::WPE / 4,
+                                              Cfg<D, C, MODE>::NW * Cfg<D, C, MODE>::WPE / 4)))
 void chunk_kernel(KernelArgs a) {
-    constexpr int NW = waves<D, MODE>();
-    constexpr int NT = 64 * NW;
-    constexpr int CQ = D / 4;          // channel quads
-    constexpr int TG = NT / CQ;        // token groups
-    constexpr int TPG = C / TG;        // tokens per thread
-    constexpr int RT = D / 16;         // state row tiles
-    constexpr int KS = D / 32;         // 32-deep steps over channels
-    constexpr int PK = Smem<D, MODE>::PK, PT = Smem<D, MODE>::PT;
-    static_assert(TPG % 4 == 0 && 32 % TPG == 0, "token grouping");
+    using K = Cfg<D, C, MODE>;
+    constexpr int NT = K::NT, NW = K::NW, CQ = K::CQ, TPG = K::TPG, NA = K::NA;
+    constexpr int NRT = K::NRT, NKT = K::NKT, RT = K::RT, KS = K::KS, PK = K::PK, PT = K::PT;
     using ST = typename IN::storage;
+    using R = Raw<IN>;
+    using quad = typename R::quad;
+    using elem = typename R::elem;
 
-    __shared__ Smem<D, MODE> sm;
+    __shared__ Smem<D, C, MODE> sm;
 
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g4 = l >> 4, lr = l & 15;
     const int H = a.H;
@@ -210,6 +240,8 @@ void chunk_kernel(KernelArgs a) {
 
     const bool is_phi = MODE == 1 && w >= D / 32;
     const int j0 = (MODE == 0 ? w : (w % (D / 32))) * 32;
+    const int cq = tid % CQ, tg = tid / CQ, c4 = 4 * cq;
+    const bool loader = tid < NA;
 
     // ---------------------------------------------------------------- entry state
     f32x4 S[RT][2];
@@ -219,167 +251,200 @@ void chunk_kernel(KernelArgs a) {
             if (s == 0) src = a.S0 ? a.S0 + ubase : nullptr;
             else src = a.se + (static_cast<size_t>(s - 1) * a.NH + unit) * D * D;
         }
+        if (src) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+            for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+                for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int row = 16 * rt + 4 * g4 + e, col = j0 + 16 * ct + lr;
-                    S[rt][ct][e] = src ? src[row * D + col] : ((is_phi && row == col) ? 1.f : 0.f);
-                }
+                    for (int e = 0; e < 4; ++e)
+                        S[rt][ct][e] = src[(16 * rt + 4 * g4 + e) * D + j0 + 16 * ct + lr];
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        S[rt][ct][e] = (is_phi && 16 * rt + 4 * g4 + e == j0 + 16 * ct + lr) ? 1.f : 0.f;
+        }
     }
     if constexpr (MODE == 0) {
         // P's strictly-upper 16x16 tiles inside the 32-deep steps are read but never written.
         for (int i = tid; i < 2 * C * PT; i += NT) sm.p[i / (C * PT)][i % (C * PT)] = 0;
     }
-    __syncthreads();
 
-    const int cq = tid % CQ, tg = tid / CQ, c4 = 4 * cq;
+    // ---------------------------------------------------------------- input prefetch
+    // Rows past the end of a ragged chunk load a valid row (clamped index) and are
+    // zeroed when used, so every load is unconditional.
+    quad pk[TPG], pq[TPG], pg[TPG];
+    elem pb = 0;
+    auto fetch = [&](int chunk) {
+        const long ts = t0 + static_cast<long>(chunk) * C;
+        const int last = static_cast<int>(min(static_cast<long>(C), t1 - ts)) - 1;
+        if (loader) {
+#pragma unroll
+            for (int i = 0; i < TPG; ++i) {
+                const int r = min(tg * TPG + i, last);
+                const size_t off = (static_cast<size_t>(ts + r) * H + h) * D + c4;
+                pk[i] = *reinterpret_cast<const quad*>(static_cast<const ST*>(a.k) + off);
+                pg[i] = *reinterpret_cast<const quad*>(static_cast<const ST*>(a.g) + off);
+                if constexpr (MODE == 0) pq[i] = *reinterpret_cast<const quad*>(static_cast<const ST*>(a.q) + off);
+            }
+        }
+        if (tid < C) pb = static_cast<const ST*>(a.beta)[static_cast<size_t>(ts + min(tid, last)) * H + h];
+    };
+    if (c_begin < c_end) fetch(c_begin);
+    __syncthreads();
 
     for (int chunk = c_begin; chunk < c_end; ++chunk) {
         const long ts = t0 + static_cast<long>(chunk) * C;
         const int ntok = static_cast<int>(min(static_cast<long>(C), t1 - ts));
 
-        // ============================================================ phase A: loads, decay scan
-        float kr[TPG][4], qr[TPG][4], gr[TPG][4];
+        // ============================================================ phase A: decay scan, decayed operands
+        float gr[TPG][4];
+        if (loader) {
 #pragma unroll
-        for (int i = 0; i < TPG; ++i) {
-            const int r = tg * TPG + i;
-            if (r < ntok) {
-                const size_t off = (static_cast<size_t>(ts + r) * H + h) * D + c4;
-                load4<IN>(static_cast<const ST*>(a.k), off, kr[i]);
-                load4<IN>(static_cast<const ST*>(a.g), off, gr[i]);
-                if constexpr (MODE == 0) load4<IN>(static_cast<const ST*>(a.q), off, qr[i]);
-            } else {
+            for (int i = 0; i < TPG; ++i)
 #pragma unroll
-                for (int ch = 0; ch < 4; ++ch) kr[i][ch] = gr[i][ch] = qr[i][ch] = 0.f;
-            }
+                for (int ch = 0; ch < 4; ++ch)
+                    gr[i][ch] = (tg * TPG + i < ntok ? R::get(pg[i], ch) : 0.f) + (i ? gr[i - 1][ch] : 0.f);
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) sm.at.scan[tg][c4 + ch] = gr[TPG - 1][ch];
         }
-        // V in accumulator layout for this wave's columns
-        f32x4 V[4][2];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int row = 16 * rt + 4 * g4 + e;
-                    V[rt][ct][e] = (!is_phi && row < ntok)
-                        ? IN::to_f32(static_cast<const ST*>(a.v)[(static_cast<size_t>(ts + row) * H + h) * D + j0 + 16 * ct + lr])
-                        : 0.f;
-                }
-        if (tid < C)
-            sm.beta[tid] = tid < ntok ? IN::to_f32(static_cast<const ST*>(a.beta)[static_cast<size_t>(ts + tid) * H + h]) : 0.f;
-
-#pragma unroll
-        for (int i = 1; i < TPG; ++i)
-#pragma unroll
-            for (int ch = 0; ch < 4; ++ch) gr[i][ch] += gr[i - 1][ch];
-#pragma unroll
-        for (int ch = 0; ch < 4; ++ch) sm.at.scan[tg][c4 + ch] = gr[TPG - 1][ch];
+        if (tid < C) sm.beta[tid] = tid < ntok ? IN::to_f32(pb) : 0.f;
         __syncthreads();
-
-        float off[4] = {0.f, 0.f, 0.f, 0.f}, bn[4] = {0.f, 0.f, 0.f, 0.f}, bm[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int gg = 0; gg < TG; ++gg)
-#pragma unroll
-            for (int ch = 0; ch < 4; ++ch) {
-                const float x = sm.at.scan[gg][c4 + ch];
-                bn[ch] += x;
-                if (gg < tg) off[ch] += x;
-                if (gg < 32 / TPG) bm[ch] += x;
-            }
 
         float ktk[TPG][4];   // Ktil_m kept for Khat^T after the C x C products
         float enm[4];
+        if (loader) {
+            float off[4] = {0.f, 0.f, 0.f, 0.f}, bn[4] = {0.f, 0.f, 0.f, 0.f}, bm[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ch = 0; ch < 4; ++ch) enm[ch] = fast_exp(bn[ch] - bm[ch]);
+            for (int gg = 0; gg < K::TGA; ++gg)
 #pragma unroll
-        for (int i = 0; i < TPG; ++i) {
-            const int r = tg * TPG + i;
-            u16 kh[4], kl[4], th[4], tl[4], qh[4], ql[4];
+                for (int ch = 0; ch < 4; ++ch) {
+                    const float x = sm.at.scan[gg][c4 + ch];
+                    bn[ch] += x;
+                    off[ch] += gg < tg ? x : 0.f;
+                    bm[ch] += gg < (C / 2) / TPG ? x : 0.f;
+                }
 #pragma unroll
-            for (int ch = 0; ch < 4; ++ch) {
-                const float b = gr[i][ch] + off[ch];
-                const float em = fast_exp(b - bm[ch]);
-                const float ei = fast_exp(bm[ch] - b);
-                split2(kr[i][ch] * em, kh[ch], kl[ch]);
-                ktk[i][ch] = kr[i][ch] * ei;
-                split2(ktk[i][ch], th[ch], tl[ch]);
-                if constexpr (MODE == 0) split2(qr[i][ch] * em, qh[ch], ql[ch]);
+            for (int ch = 0; ch < 4; ++ch) enm[ch] = fast_exp(bn[ch] - bm[ch]);
+#pragma unroll
+            for (int i = 0; i < TPG; ++i) {
+                const int r = tg * TPG + i;
+                const bool valid = r < ntok;
+                u16 kh[4], kl[4], th[4], tl[4], qh[4], ql[4];
+#pragma unroll
+                for (int ch = 0; ch < 4; ++ch) {
+                    const float b = gr[i][ch] + off[ch];
+                    const float em = fast_exp(b - bm[ch]);
+                    const float ei = fast_exp(bm[ch] - b);
+                    const float kv = valid ? R::get(pk[i], ch) : 0.f;
+                    split2(kv * em, kh[ch], kl[ch]);
+                    ktk[i][ch] = kv * ei;
+                    split2(ktk[i][ch], th[ch], tl[ch]);
+                    if constexpr (MODE == 0) split2((valid ? R::get(pq[i], ch) : 0.f) * em, qh[ch], ql[ch]);
+                }
+                const int idx = r * PK + kperm(c4);
+                store4(&sm.kb[0][idx], kh);
+                store4(&sm.kb[1][idx], kl);
+                store4(&sm.kt[0][idx], th);
+                store4(&sm.kt[1][idx], tl);
+                if constexpr (MODE == 0) {
+                    store4(&sm.qb[0][idx], qh);
+                    store4(&sm.qb[1][idx], ql);
+                }
             }
-            const int idx = r * PK + kperm(c4);
-            store4(&sm.kb[0][idx], kh);
-            store4(&sm.kb[1][idx], kl);
-            store4(&sm.kt[0][idx], th);
-            store4(&sm.kt[1][idx], tl);
-            if constexpr (MODE == 0) {
-                store4(&sm.qb[0][idx], qh);
-                store4(&sm.qb[1][idx], ql);
-            }
-        }
-        if (tg == 0) {
+            if (tg == 0) {
 #pragma unroll
-            for (int ch = 0; ch < 4; ++ch) {
-                sm.em[c4 + ch] = fast_exp(bm[ch]);
-                sm.gam[c4 + ch] = fast_exp(bn[ch]);
+                for (int ch = 0; ch < 4; ++ch) {
+                    sm.em[c4 + ch] = fast_exp(bm[ch]);
+                    sm.gam[c4 + ch] = fast_exp(bn[ch]);
+                }
             }
         }
         __syncthreads();
+        // V of this chunk (used by the state pass) and the next chunk's k, q, log_alpha,
+        // beta stream in while the C x C products and the solve run.
+        elem pv[NRT][2][4];
+        if (!is_phi) {
+            const int last = ntok - 1;
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = min(16 * rt + 4 * g4 + e, last);
+                        pv[rt][ct][e] = static_cast<const ST*>(a.v)[(static_cast<size_t>(ts + r) * H + h) * D + j0 + 16 * ct + lr];
+                    }
+        }
+        if (chunk + 1 < c_end) fetch(chunk + 1);
 
         // ============================================================ phase B: A and P on MFMA
-        constexpr int NJOB = MODE == 0 ? 20 : 10;
-        for (int job = w; job < NJOB; job += NW) {
-            const bool isP = job >= 10;
-            const int tj = isP ? job - 10 : job;
-            const int rt = tj >= 6 ? 3 : tj >= 3 ? 2 : tj >= 1 ? 1 : 0;
-            const int ct = tj - rt * (rt + 1) / 2;
-            const u16* ah_base = &sm.kb[0][0];
-            const u16* al_base = &sm.kb[1][0];
-            if constexpr (MODE == 0) {
-                if (isP) { ah_base = &sm.qb[0][0]; al_base = &sm.qb[1][0]; }
-            }
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        {
+            constexpr int NJOB = (MODE == 0 ? 2 : 1) * K::NTRI;
+            constexpr int JPW = (NJOB + NW - 1) / NW;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int ao = (16 * rt + lr) * PK + 32 * ks + 8 * g4;
-                const int bo = (16 * ct + lr) * PK + 32 * ks + 8 * g4;
-                acc = mfma3(frag(ah_base + ao), frag(al_base + ao), frag(&sm.kt[0][bo]), frag(&sm.kt[1][bo]), acc);
-            }
+            for (int jj = 0; jj < JPW; ++jj) {
+                const int job = w + jj * NW;
+                if (job < NJOB) {
+                    const bool isP = job >= K::NTRI;
+                    const int tj = isP ? job - K::NTRI : job;
+                    int rt = 0;
+                    while ((rt + 1) * (rt + 2) / 2 <= tj) ++rt;
+                    const int ct = tj - rt * (rt + 1) / 2;
+                    const u16* ah_base = &sm.kb[0][0];
+                    const u16* al_base = &sm.kb[1][0];
+                    if constexpr (MODE == 0) {
+                        if (isP) { ah_base = &sm.qb[0][0]; al_base = &sm.qb[1][0]; }
+                    }
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = 16 * rt + 4 * g4 + e, col = 16 * ct + lr;
-                if (!isP) {
-                    sm.at.a[row * (C + 1) + col] = col < row ? acc[e] * sm.beta[row] : 0.f;
-                } else if constexpr (MODE == 0) {
-                    u16 hi, lo;
-                    split2(col <= row ? acc[e] : 0.f, hi, lo);
-                    sm.p[0][row * PT + kperm(col)] = hi;
-                    sm.p[1][row * PT + kperm(col)] = lo;
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const int ao = (16 * rt + lr) * PK + 32 * ks + 8 * g4;
+                        const int bo = (16 * ct + lr) * PK + 32 * ks + 8 * g4;
+                        acc = mfma3(frag(ah_base + ao), frag(al_base + ao), frag(&sm.kt[0][bo]), frag(&sm.kt[1][bo]), acc);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int row = 16 * rt + 4 * g4 + e, col = 16 * ct + lr;
+                        if (!isP) {
+                            sm.at.a[row * (C + 1) + col] = col < row ? acc[e] * sm.beta[row] : 0.f;
+                        } else if constexpr (MODE == 0) {
+                            u16 hi, lo;
+                            split2(col <= row ? acc[e] : 0.f, hi, lo);
+                            sm.p[0][row * PT + kperm(col)] = hi;
+                            sm.p[1][row * PT + kperm(col)] = lo;
+                        }
+                    }
                 }
             }
         }
         __syncthreads();
 
         // ============================================================ phase C: Khat^T (registers -> LDS)
+        if (loader) {
 #pragma unroll
-        for (int ch = 0; ch < 4; ++ch) {
-            const int c = c4 + ch;
+            for (int ch = 0; ch < 4; ++ch) {
+                const int c = c4 + ch;
 #pragma unroll
-            for (int gq = 0; gq < TPG / 4; ++gq) {
-                u16 hi[4], lo[4];
+                for (int gq = 0; gq < TPG / 4; ++gq) {
+                    u16 hi[4], lo[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) split2(ktk[4 * gq + j][ch] * enm[ch], hi[j], lo[j]);
-                const int idx = c * PT + kperm(tg * TPG + 4 * gq);
-                store4(&sm.kt[0][idx], hi);
-                store4(&sm.kt[1][idx], lo);
+                    for (int j = 0; j < 4; ++j) split2(ktk[4 * gq + j][ch] * enm[ch], hi[j], lo[j]);
+                    const int idx = c * PT + kperm(tg * TPG + 4 * gq);
+                    store4(&sm.kt[0][idx], hi);
+                    store4(&sm.kt[1][idx], lo);
+                }
             }
         }
 
         // ============================================================ phase D: T = (I + A)^{-1} Diag(beta)
-        if (w == 0) {
+        if (w == 0 && l < 16 * K::NB) {
             // one lane per column of each 16x16 diagonal block; forward substitution
-            const int blk = l >> 4, j = l & 15, o0 = 16 * blk;
+            const int o0 = 16 * (l >> 4), j = l & 15;
             float x[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -392,25 +457,34 @@ void chunk_kernel(KernelArgs a) {
             for (int r = 0; r < 16; ++r) sm.at.a[(o0 + r) * (C + 1) + o0 + j] = x[r];
         }
         __syncthreads();
-        for (int bi = 1; bi < 4; ++bi) {
-            // Y_{bi,bj} = sum_{bk=bj}^{bi-1} A_{bi,bk} X_{bk,bj}
-            for (int idx = tid; idx < bi * 256; idx += NT) {
-                const int bj = idx >> 8, rr = (idx >> 4) & 15, cc = idx & 15;
-                float y = 0.f;
-                for (int bk = bj; bk < bi; ++bk)
 #pragma unroll
-                    for (int m = 0; m < 16; ++m)
-                        y += sm.at.a[(16 * bi + rr) * (C + 1) + 16 * bk + m] * sm.at.a[(16 * bk + m) * (C + 1) + 16 * bj + cc];
-                sm.tmp[bj][rr][cc] = y;
+        for (int bi = 1; bi < K::NB; ++bi) {
+            // Y_{bi,bj} = sum_{bk=bj}^{bi-1} A_{bi,bk} X_{bk,bj}
+#pragma unroll
+            for (int u = 0; u < (bi * 256 + NT - 1) / NT; ++u) {
+                const int idx = tid + u * NT;
+                if (idx < bi * 256) {
+                    const int bj = idx >> 8, rr = (idx >> 4) & 15, cc = idx & 15;
+                    float y = 0.f;
+                    for (int bk = bj; bk < bi; ++bk)
+#pragma unroll
+                        for (int m = 0; m < 16; ++m)
+                            y += sm.at.a[(16 * bi + rr) * (C + 1) + 16 * bk + m] * sm.at.a[(16 * bk + m) * (C + 1) + 16 * bj + cc];
+                    sm.tmp[bj][rr][cc] = y;
+                }
             }
             __syncthreads();
             // X_{bi,bj} = -X_{bi,bi} Y_{bi,bj}, written over A_{bi,bj}
-            for (int idx = tid; idx < bi * 256; idx += NT) {
-                const int bj = idx >> 8, rr = (idx >> 4) & 15, cc = idx & 15;
-                float x = 0.f;
 #pragma unroll
-                for (int m = 0; m < 16; ++m) x -= sm.at.a[(16 * bi + rr) * (C + 1) + 16 * bi + m] * sm.tmp[bj][m][cc];
-                sm.at.a[(16 * bi + rr) * (C + 1) + 16 * bj + cc] = x;
+            for (int u = 0; u < (bi * 256 + NT - 1) / NT; ++u) {
+                const int idx = tid + u * NT;
+                if (idx < bi * 256) {
+                    const int bj = idx >> 8, rr = (idx >> 4) & 15, cc = idx & 15;
+                    float x = 0.f;
+#pragma unroll
+                    for (int m = 0; m < 16; ++m) x -= sm.at.a[(16 * bi + rr) * (C + 1) + 16 * bi + m] * sm.tmp[bj][m][cc];
+                    sm.at.a[(16 * bi + rr) * (C + 1) + 16 * bj + cc] = x;
+                }
             }
             __syncthreads();
         }
@@ -435,10 +509,16 @@ void chunk_kernel(KernelArgs a) {
         __syncthreads();
 
         // ============================================================ phase E: state pass (per wave)
-        // B operands from Diag(e^{b_m}) S (the e^{b_m} completes Kbar_m / Qbar_m to Kbar / Qbar)
-        bf16x8 sbh[KS][2], sbl[KS][2];
+        // Y = Kbar S and Z = Qbar S.  The B operands are Diag(e^{b_m}) S (e^{b_m} completes
+        // Kbar_m / Qbar_m to Kbar / Qbar), split per 32-deep step to keep registers low.
+        f32x4 Y[NRT][2], Z[NRT][2];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) Y[rt][ct] = Z[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            bf16x8 sbh[2], sbl[2];
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) {
                 f32x4 x0 = S[2 * ks][ct], x1 = S[2 * ks + 1][ct];
@@ -447,41 +527,43 @@ void chunk_kernel(KernelArgs a) {
                     x0[e] *= sm.em[32 * ks + 4 * g4 + e];
                     x1[e] *= sm.em[32 * ks + 16 + 4 * g4 + e];
                 }
-                split_b(x0, x1, sbh[ks][ct], sbl[ks][ct]);
+                split_b(x0, x1, sbh[ct], sbl[ct]);
             }
-        f32x4 Y[4][2], Z[4][2];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) Y[rt][ct] = Z[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
+            for (int rt = 0; rt < NRT; ++rt) {
                 const int ao = (16 * rt + lr) * PK + 32 * ks + 8 * g4;
                 const bf16x8 kh = frag(&sm.kb[0][ao]), kl = frag(&sm.kb[1][ao]);
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) Y[rt][ct] = mfma3(kh, kl, sbh[ks][ct], sbl[ks][ct], Y[rt][ct]);
+                for (int ct = 0; ct < 2; ++ct) Y[rt][ct] = mfma3(kh, kl, sbh[ct], sbl[ct], Y[rt][ct]);
                 if constexpr (MODE == 0) {
                     const bf16x8 qh = frag(&sm.qb[0][ao]), ql = frag(&sm.qb[1][ao]);
 #pragma unroll
-                    for (int ct = 0; ct < 2; ++ct) Z[rt][ct] = mfma3(qh, ql, sbh[ks][ct], sbl[ks][ct], Z[rt][ct]);
+                    for (int ct = 0; ct < 2; ++ct) Z[rt][ct] = mfma3(qh, ql, sbh[ct], sbl[ct], Z[rt][ct]);
                 }
             }
+        }
         // Unew = T (V - Kbar S)
-        bf16x8 dbh[2][2], dbl[2][2];
+        f32x4 V[NRT][2];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    V[rt][ct][e] = (!is_phi && 16 * rt + 4 * g4 + e < ntok) ? IN::to_f32(pv[rt][ct][e]) : 0.f;
+        bf16x8 dbh[NKT][2], dbl[NKT][2];
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct)
                 split_b(V[2 * kt][ct] - Y[2 * kt][ct], V[2 * kt + 1][ct] - Y[2 * kt + 1][ct], dbh[kt][ct], dbl[kt][ct]);
-        f32x4 U[4][2];
+        f32x4 U[NRT][2];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
+        for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) U[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
+        for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
             for (int kt = 0; kt <= (rt >> 1); ++kt) {
                 const int ao = (16 * rt + lr) * PT + 32 * kt + 8 * g4;
@@ -489,16 +571,16 @@ void chunk_kernel(KernelArgs a) {
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct) U[rt][ct] = mfma3(th, tl, dbh[kt][ct], dbl[kt][ct], U[rt][ct]);
             }
-        bf16x8 ubh[2][2], ubl[2][2];
+        bf16x8 ubh[NKT][2], ubl[NKT][2];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) split_b(U[2 * kt][ct], U[2 * kt + 1][ct], ubh[kt][ct], ubl[kt][ct]);
 
         if constexpr (MODE == 0) {
             // O = Qbar S + P Unew
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
+            for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
                 for (int kt = 0; kt <= (rt >> 1); ++kt) {
                     const int ao = (16 * rt + lr) * PT + 32 * kt + 8 * g4;
@@ -506,14 +588,15 @@ void chunk_kernel(KernelArgs a) {
 #pragma unroll
                     for (int ct = 0; ct < 2; ++ct) Z[rt][ct] = mfma3(ph, pl, ubh[kt][ct], ubl[kt][ct], Z[rt][ct]);
                 }
+            const bool full = ntok == C;   // uniform: only a sequence's last chunk can be ragged
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
+            for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int row = 16 * rt + 4 * g4 + e;
-                        if (row < ntok)
+                        if (full || row < ntok)
                             store_out<OUT_BF16>(a.o, (static_cast<size_t>(ts + row) * H + h) * D + j0 + 16 * ct + lr,
                                                 Z[rt][ct][e]);
                     }
@@ -528,7 +611,7 @@ void chunk_kernel(KernelArgs a) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
+            for (int kt = 0; kt < NKT; ++kt) {
                 const int ao = (16 * rt + lr) * PT + 32 * kt + 8 * g4;
                 const bf16x8 kh = frag(&sm.kt[0][ao]), kl = frag(&sm.kt[1][ao]);
 #pragma unroll
@@ -601,7 +684,7 @@ __global__ __launch_bounds__(256) void order_kernel(const int32_t* __restrict__ 
     order[rank] = i;
 }
 
-template <int D, typename IN, bool OB>
+template <int D, int C, typename IN, bool OB>
 hipError_t launch_variant(const PrefillArgs& pa, const PrefillPlan& plan, hipStream_t stream) {
     KernelArgs a;
     a.q = pa.q; a.k = pa.k; a.v = pa.v; a.g = pa.g; a.beta = pa.beta;
@@ -616,16 +699,16 @@ hipError_t launch_variant(const PrefillArgs& pa, const PrefillPlan& plan, hipStr
     if (pa.cu) {
         hipLaunchKernelGGL(order_kernel, dim3((pa.N + 255) / 256), dim3(256), 0, stream, pa.cu,
                            reinterpret_cast<int32_t*>(ws + plan.off_order), pa.N);
-        hipLaunchKernelGGL((chunk_kernel<D, IN, OB, 0>), dim3(NH), dim3(64 * waves<D, 0>()), 0, stream, a);
+        hipLaunchKernelGGL((chunk_kernel<D, C, IN, OB, 0>), dim3(NH), dim3(Cfg<D, C, 0>::NT), 0, stream, a);
         return hipGetLastError();
     }
     if (plan.G > 1) {
-        hipLaunchKernelGGL((chunk_kernel<D, IN, OB, 1>), dim3(NH * (plan.G - 1)), dim3(64 * waves<D, 1>()), 0,
+        hipLaunchKernelGGL((chunk_kernel<D, C, IN, OB, 1>), dim3(NH * (plan.G - 1)), dim3(Cfg<D, C, 1>::NT), 0,
                            stream, a);
         hipLaunchKernelGGL(combine_kernel<D>, dim3(NH, D / 16), dim3(256), 0, stream, pa.S0, a.phi, a.sloc, a.se,
                            NH, plan.G);
     }
-    hipLaunchKernelGGL((chunk_kernel<D, IN, OB, 0>), dim3(NH * plan.G), dim3(64 * waves<D, 0>()), 0, stream, a);
+    hipLaunchKernelGGL((chunk_kernel<D, C, IN, OB, 0>), dim3(NH * plan.G), dim3(Cfg<D, C, 0>::NT), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -633,8 +716,9 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 }  // namespace
 
-PrefillPlan plan_prefill(int B, int T, int H, int D, int N, bool varlen) {
+PrefillPlan plan_prefill(int B, int T, int H, int D, int N, bool varlen, int chunk) {
     PrefillPlan p;
+    p.chunk = chunk == 0 ? kDefaultChunk : chunk;
     if (varlen) {
         p.G = 1;
         p.off_order = 0;
@@ -642,11 +726,13 @@ PrefillPlan plan_prefill(int B, int T, int H, int D, int N, bool varlen) {
         return p;
     }
     (void)B;
-    p.chunks = (T + C - 1) / C;
+    p.chunks = (T + p.chunk - 1) / p.chunk;
     const long units = static_cast<long>(N) * H;
+    // workgroups that fill the chip: one per compute unit, two at the 32-token chunk
+    const long target = static_cast<long>(kComputeUnits) * (p.chunk == 32 ? 2 : 1);
     int G = 1;
-    if (units > 0 && units < kTargetWorkgroups && p.chunks >= 2 * kMinChunksPerSegment) {
-        G = static_cast<int>((kTargetWorkgroups + units - 1) / units);
+    if (units > 0 && units < target && p.chunks >= 2 * kMinChunksPerSegment) {
+        G = static_cast<int>((target + units - 1) / units);
         G = std::min(G, p.chunks / kMinChunksPerSegment);
         G = std::max(G, 1);
     }
@@ -663,17 +749,19 @@ PrefillPlan plan_prefill(int B, int T, int H, int D, int N, bool varlen) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan, hipStream_t stream) {
-#define KDA_PREFILL_CASE(DD, INT, OB)                                                     \
-    if (a.D == DD && a.in_bf16 == std::is_same<INT, BF16>::value && a.out_bf16 == OB)     \
-        return launch_variant<DD, INT, OB>(a, plan, stream);
-    KDA_PREFILL_CASE(128, BF16, true)
-    KDA_PREFILL_CASE(128, BF16, false)
-    KDA_PREFILL_CASE(128, F32, true)
-    KDA_PREFILL_CASE(128, F32, false)
-    KDA_PREFILL_CASE(64, BF16, true)
-    KDA_PREFILL_CASE(64, BF16, false)
-    KDA_PREFILL_CASE(64, F32, true)
-    KDA_PREFILL_CASE(64, F32, false)
+#define KDA_PREFILL_CASE(DD, CC, INT, OB)                                                              \
+    if (a.D == DD && plan.chunk == CC && a.in_bf16 == std::is_same<INT, BF16>::value && a.out_bf16 == OB) \
+        return launch_variant<DD, CC, INT, OB>(a, plan, stream);
+#define KDA_PREFILL_D(DD, CC)              \
+    KDA_PREFILL_CASE(DD, CC, BF16, true)   \
+    KDA_PREFILL_CASE(DD, CC, BF16, false)  \
+    KDA_PREFILL_CASE(DD, CC, F32, true)    \
+    KDA_PREFILL_CASE(DD, CC, F32, false)
+    KDA_PREFILL_D(128, 32)
+    KDA_PREFILL_D(128, 64)
+    KDA_PREFILL_D(64, 32)
+    KDA_PREFILL_D(64, 64)
+#undef KDA_PREFILL_D
 #undef KDA_PREFILL_CASE
     return hipErrorInvalidValue;
 }

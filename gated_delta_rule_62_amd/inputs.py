@@ -2,7 +2,8 @@
 
 This module is the one piece shared by the HIP path's callers and by the oracle's
 tests: it draws and shapes random inputs and holds none of the method's arithmetic
-(no decay, no delta update, no chunking).  It imports numpy only.
+(no decay, no delta update, no chunking).  It imports numpy; the on-device draws
+for full-size workloads import torch lazily.
 
 Workloads (the five shapes the layer is measured and checked on):
 
@@ -186,3 +187,83 @@ class DecodeStream:
         dt = self.dtype
         return dict(q=_cast(q, dt), k=_cast(k, dt), v=_cast(v, dt), log_alpha=_cast(g, dt),
                     beta=_cast(beta, dt))
+
+
+# ---------------------------------------------------------------- on-device draws
+# The full-size workloads (up to 2^31 elements per tensor) are drawn directly on
+# the GPU with torch's seeded generator, same recipe, then the sampled slices a
+# test checks are copied to the host so both sides read identical bf16 values.
+
+def varlen_lengths(w: Workload, seed: int | None = None) -> np.ndarray:
+    """Sequence lengths of a packed workload: integers(lo, hi, endpoint=True) from
+    default_rng(seed) (seed 5 gives 525,197 tokens for workload 4)."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    lo, hi = w.len_range
+    return rng.integers(lo, hi, endpoint=True, size=w.num_seqs)
+
+
+def device_prefill(w: Workload, seed: int | None = None, device="cuda", *, lengths=None):
+    """Full-size prefill batch of workload w drawn on the device (bf16 inputs).
+    Returns a dict like make_prefill but with torch tensors; cu_seqlens is int32."""
+    import torch
+    F = torch.nn.functional
+    seed = w.seed if seed is None else seed
+    if w.len_range:
+        lengths = varlen_lengths(w, seed) if lengths is None else np.asarray(lengths)
+        cu = np.zeros(lengths.size + 1, dtype=np.int64)
+        np.cumsum(lengths, out=cu[1:])
+        B, T, N = 1, int(cu[-1]), int(lengths.size)
+    else:
+        B, T, N, cu = w.B, w.T, w.B, None
+    H, D = w.H, w.D
+    g = torch.Generator(device=device).manual_seed(seed)
+    shp = (B, T, H, D)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def normal(shape):
+        return torch.randn(shape, device=device, generator=g)
+
+    q = F.normalize(normal(shp), dim=-1).to(dt)
+    k = F.normalize(normal(shp), dim=-1).to(dt)
+    v = normal(shp).to(dt)
+    beta = torch.sigmoid(normal((B, T, H))).to(dt)
+    la = F.logsigmoid(normal(shp) + w.mu) / w.s
+    if w.mix:
+        fast = F.logsigmoid(normal(shp)) / 2.0
+        pick = torch.rand(shp, device=device, generator=g) < 0.5
+        la = torch.where(pick, fast, la)
+        del fast, pick
+    la = la.to(dt)
+    S0 = 0.02 * normal((N, H, D, D)) if w.s0 else None
+    return dict(q=q, k=k, v=v, log_alpha=la, beta=beta, S0=S0,
+                cu_seqlens=None if cu is None else torch.tensor(cu, dtype=torch.int32, device=device),
+                cu_host=cu, B=B, T=T, H=H, D=D, N=N, dtype=w.dtype)
+
+
+def device_decode_steps(w: Workload, steps: int, seed: int | None = None, device="cuda"):
+    """Initial state and `steps` per-step input tuples (q, k, v, log_alpha, beta) of
+    a decode workload, drawn on the device."""
+    import torch
+    F = torch.nn.functional
+    g = torch.Generator(device=device).manual_seed(w.seed if seed is None else seed)
+    N, H, D = w.num_seqs, w.H, w.D
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    S0 = 0.02 * torch.randn((N, H, D, D), device=device, generator=g)
+    out = []
+    for _ in range(steps):
+        q = F.normalize(torch.randn((N, H, D), device=device, generator=g), dim=-1).to(dt)
+        k = F.normalize(torch.randn((N, H, D), device=device, generator=g), dim=-1).to(dt)
+        v = torch.randn((N, H, D), device=device, generator=g).to(dt)
+        beta = torch.sigmoid(torch.randn((N, H), device=device, generator=g)).to(dt)
+        la = (F.logsigmoid(torch.randn((N, H, D), device=device, generator=g) + w.mu) / w.s).to(dt)
+        out.append((q, k, v, la, beta))
+    return S0, out
+
+
+def host_bits(t) -> np.ndarray:
+    """Device tensor -> host numpy array (bf16 as uint16 bit patterns, else float32)."""
+    import torch
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()

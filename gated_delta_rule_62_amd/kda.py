@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libkda.so")
 
 KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE_TOO_SMALL, KDA_ERR_HIP = range(5)
 KDA_F32, KDA_BF16 = 0, 1
-CHUNK = 64
+CHUNK = 0          # library default chunk length (32 tokens); 32 and 64 are built
 
 EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_step")
 

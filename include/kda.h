@@ -31,9 +31,9 @@
  *    up at the caller's next synchronisation.
  *  - Preconditions that live in device memory are documented, not checked:
  *    cu_seqlens starts at 0, never decreases and ends at T; inputs are finite;
- *    log_alpha <= 0; beta in [0, 1].  Per chunk of 64 tokens, the summed
- *    log-decay of any channel must stay above -160 (the decay factors of a chunk
- *    are formed around its midpoint in fp32).
+ *    log_alpha <= 0; beta in [0, 1].  Within one chunk, the summed log-decay of
+ *    any channel must stay above -160 (the decay factors of a chunk are formed
+ *    around its midpoint in fp32).
  *  - Outputs are bitwise deterministic for identical inputs (no atomics).
  *  - Library functions keep no mutable global state and are thread-safe.
  */
@@ -81,7 +81,7 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int nu
  *                     1, sequence n owns tokens [cu[n], cu[n+1]), zero lengths
  *                     allowed), or NULL: then N = B sequences of T tokens each
  *   num_seqs        : N
- *   chunk           : chunk size; 0 or 64 (the only size built)
+ *   chunk           : chunk length in tokens: 32 or 64, or 0 for the default (32)
  *   o               : [B, T, H, Dv]   out_dtype (bf16 is round-to-nearest-even)
  *   S_final         : [N, H, Dk, Dv]  fp32, or NULL to skip
  *   workspace       : device scratch of workspace_bytes >= the query above

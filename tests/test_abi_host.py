@@ -1,0 +1,103 @@
+"""CPU-side checks of the C ABI (no GPU needed): the library loads, exports every
+function include/kda.h declares, and rejects bad arguments before any HIP call.
+Pointer arguments here are fake addresses that the library must never touch."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+from gated_delta_rule_62_amd import kda  # noqa: E402
+
+FAKE = ctypes.c_void_p(1 << 40)          # 16-byte aligned, never dereferenced
+FAKE_MIS = ctypes.c_void_p((1 << 40) + 4)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.LIB_PATH):
+        pytest.skip("libkda.so is not built")
+    return kda.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(kda.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} missing from libkda.so"
+
+
+def test_status_strings(lib):
+    names = [kda.status_string(i) for i in range(5)]
+    assert names == ["KDA_OK", "KDA_ERR_INVALID_ARGUMENT", "KDA_ERR_UNSUPPORTED",
+                     "KDA_ERR_WORKSPACE_TOO_SMALL", "KDA_ERR_HIP"]
+
+
+def test_workspace_query_plans(lib):
+    q = kda.kda_chunk_fwd_workspace_bytes
+    # long context, 32 heads: 2048 chunks of 32 tokens cut into 16 segments (two workgroups
+    # per compute unit), or 1024 chunks of 64 cut into 8 -> 3 matrices per unit and segment gap
+    assert q(1, 65536, 32, 128, 128, 1, False) == 3 * 32 * 15 * 128 * 128 * 4
+    assert q(1, 65536, 32, 128, 128, 1, False, chunk=64) == 3 * 32 * 7 * 128 * 128 * 4
+    # enough units to fill the chip: single pass, no workspace
+    assert q(64, 4096, 32, 128, 128, 64, False) == 0
+    # packed sequences: an int32 order table (rounded to 256 bytes)
+    assert q(1, 1000, 32, 128, 128, 64, True) == 256
+    # unsupported sizes report 0
+    assert q(1, 64, 2, 96, 96, 1, False) == 0
+    assert q(1, 64, 2, 128, 128, 1, False, chunk=16) == 0
+
+
+def call_fwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, S0=None, cu=None, B=1, T=64, H=2, Dk=128, Dv=128,
+             N=1, chunk=64, in_dt=kda.KDA_BF16, out_dt=kda.KDA_BF16, o=ctypes.c_void_p(2 << 40),
+             Sf=None, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib.kda_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["cu"], a["B"], a["T"],
+                             a["H"], a["Dk"], a["Dv"], a["N"], a["chunk"], a["in_dt"], a["out_dt"], a["o"],
+                             a["Sf"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_prefill_argument_errors(lib):
+    assert call_fwd(lib, Dk=96, Dv=96) == kda.KDA_ERR_UNSUPPORTED
+    assert call_fwd(lib, Dk=128, Dv=64) == kda.KDA_ERR_UNSUPPORTED
+    assert call_fwd(lib, chunk=16) == kda.KDA_ERR_UNSUPPORTED
+    assert call_fwd(lib, in_dt=7) == kda.KDA_ERR_UNSUPPORTED
+    assert call_fwd(lib, q=None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call_fwd(lib, k=FAKE_MIS) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call_fwd(lib, B=2, N=2, cu=ctypes.c_void_p(3 << 40)) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call_fwd(lib, N=3) == kda.KDA_ERR_INVALID_ARGUMENT            # N != B without cu_seqlens
+    assert call_fwd(lib, o=FAKE) == kda.KDA_ERR_INVALID_ARGUMENT         # o aliases q
+    assert call_fwd(lib, T=-1) == kda.KDA_ERR_INVALID_ARGUMENT
+    # segmented plan needs a workspace
+    assert call_fwd(lib, T=65536, H=32) == kda.KDA_ERR_WORKSPACE_TOO_SMALL
+    # N == 0 sequences: nothing to do, no HIP call
+    assert call_fwd(lib, B=0, N=0, T=0) == kda.KDA_OK
+
+
+def test_decode_argument_errors(lib):
+    def step(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, b=FAKE, Si=ctypes.c_void_p(4 << 40), So=ctypes.c_void_p(4 << 40),
+                 N=2, H=2, Dk=128, Dv=128, i=kda.KDA_BF16, o_dt=kda.KDA_F32, o=ctypes.c_void_p(5 << 40))
+        a.update(kw)
+        return lib.kda_recurrent_step(a["q"], a["k"], a["v"], a["g"], a["b"], a["Si"], a["So"], a["N"], a["H"],
+                                      a["Dk"], a["Dv"], a["i"], a["o_dt"], a["o"], None)
+    assert step(N=0) == kda.KDA_OK
+    assert step(Dk=64, Dv=128) == kda.KDA_ERR_UNSUPPORTED
+    assert step(Si=None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert step(So=ctypes.c_void_p((4 << 40) + 256)) == kda.KDA_ERR_INVALID_ARGUMENT   # partial overlap
+    assert step(o=ctypes.c_void_p((4 << 40) + 512)) == kda.KDA_ERR_INVALID_ARGUMENT    # o inside the state
+    assert step(q=FAKE_MIS) == kda.KDA_ERR_INVALID_ARGUMENT

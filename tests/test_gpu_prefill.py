@@ -152,7 +152,7 @@ def test_rejects_bad_arguments():
         kda.kda_chunk_fwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], None, cu)
     assert e.value.status == kda.KDA_ERR_INVALID_ARGUMENT
     with pytest.raises(kda.KDAError) as e:       # chunk size not built
-        kda.kda_chunk_fwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], chunk=32)
+        kda.kda_chunk_fwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], chunk=48)
     assert e.value.status == kda.KDA_ERR_UNSUPPORTED
     with pytest.raises(kda.KDAError) as e:       # o aliasing an input
         kda.kda_chunk_fwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], o=dev["v"])
