@@ -55,6 +55,24 @@ def decode_alg_bytes(N: int, H: int, d: int) -> int:
     return 2 * N * H * d * d * 4 + 4 * N * H * d * 2 + N * H * 2 + N * H * d * 2
 
 
+def counted_traffic(kind: str):
+    """HBM bytes per launch recorded from rocprofv3 FETCH_SIZE/WRITE_SIZE runs
+    (profiles/traffic.json), or None once the kernel source has changed since."""
+    import hashlib
+    try:
+        rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))[kind]
+    except (OSError, KeyError, ValueError):
+        return None
+    files = {"decode": ["kda_decode.hip", "kda_device.h"], "prefill": ["kda_prefill.hip", "kda_device.h"]}[kind]
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "gated_delta_rule_62_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != rec.get("source_sha256"):
+        return None
+    return rec["read_bytes"] + rec["write_bytes"]
+
+
 def bf16_to_bits(torch, t):
     from gated_delta_rule_62_amd.inputs import host_bits
     return host_bits(t)
@@ -198,7 +216,7 @@ def main():
         "config": {"workload": "decode", "sequences": N, "H": Hd, "d_k": d, "d_v": d,
                    "steps": args.decode_steps, "in_dtype": "bf16", "out_dtype": "bf16", "state": "fp32"},
         "roofline": {"bound": "hbm", "achieved": dbytes / (step_avg / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": dbytes / (step_avg / 1e3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": dbytes / (step_avg / 1e3) / 1e9 / HBM_PEAK_GBS, "traffic": counted_traffic("decode"),
                      "kernel": "decode_step_kernel<128,BF16,bf16 out>", "avg_launch_us": step_avg * 1e3,
                      "bytes_per_launch": dbytes},
     }
@@ -221,7 +239,7 @@ def main():
                    "precision": "split-bf16 MFMA operands (hi+lo), fp32 accumulation and state",
                    "schedule": plan_G},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None,
+                     "frac": tflops / BF16_PEAK_TFLOPS, "traffic": counted_traffic("prefill"),
                      "launch": "kda_chunk_fwd (all prefill kernels of one call)",
                      "avg_launch_us": call_avg_ms * 1e3, "flops_per_launch": flops,
                      "flop_convention": f"algorithmic, {prefill_alg_flops_per_token_head(d)} per token-head at C=64",

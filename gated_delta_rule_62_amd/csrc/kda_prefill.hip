@@ -294,12 +294,12 @@ void chunk_kernel(KernelArgs a) {
         }
         if (tid < C) pb = static_cast<const ST*>(a.beta)[static_cast<size_t>(ts + min(tid, last)) * H + h];
     };
-    if (c_begin < c_end) fetch(c_begin);
     __syncthreads();
 
     for (int chunk = c_begin; chunk < c_end; ++chunk) {
         const long ts = t0 + static_cast<long>(chunk) * C;
         const int ntok = static_cast<int>(min(static_cast<long>(C), t1 - ts));
+        fetch(chunk);
 
         // ============================================================ phase A: decay scan, decayed operands
         float gr[TPG][4];
@@ -380,7 +380,6 @@ void chunk_kernel(KernelArgs a) {
                         pv[rt][ct][e] = static_cast<const ST*>(a.v)[(static_cast<size_t>(ts + r) * H + h) * D + j0 + 16 * ct + lr];
                     }
         }
-        if (chunk + 1 < c_end) fetch(chunk + 1);
 
         // ============================================================ phase B: A and P on MFMA
         {
