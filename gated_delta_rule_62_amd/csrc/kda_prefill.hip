@@ -85,6 +85,19 @@ __device__ __forceinline__ f32x4 mfma3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 b
 
 __device__ __forceinline__ bf16x8 frag(const u16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
+// Workgroup barrier for LDS traffic only.  The waves of a workgroup exchange data
+// through LDS alone, so the barrier waits for this wave's LDS operations and leaves
+// global loads (the next chunk's inputs) in flight; __syncthreads() would also wait
+// for every outstanding global load.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Order LDS accesses between lanes of one wave (no workgroup barrier involved).
+__device__ __forceinline__ void wave_lds_sync() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
 // Two stacked accumulator tiles -> hi/lo B operands of one 32-deep step.
 __device__ __forceinline__ void split_b(f32x4 t0, f32x4 t1, bf16x8& hi, bf16x8& lo) {
 #pragma unroll
@@ -125,19 +138,25 @@ struct Cfg {
     static constexpr int NW = MODE == 0 ? D / 32 : D / 16;   // waves; each owns 32 state columns
     static constexpr int NT = 64 * NW;
     static constexpr int CQ = D / 4;                           // channel quads
-    static constexpr int TPG = (C * CQ / NT) > 4 ? (C * CQ / NT) : 4;   // tokens per loader thread
-    static constexpr int TGA = C / TPG;                        // token groups in the element phase
-    static constexpr int NA = TGA * CQ;                        // threads in the element phase
+    // Element phase: each of the first NA threads owns one channel quad over TPG tokens; a
+    // wave holds 8 quads for all C tokens (8 token groups), so the decay prefix over tokens
+    // stays inside the wave.
+    static constexpr int TPG = C / 8;                          // tokens per element-phase thread
+    static constexpr int NA = 8 * CQ;                          // threads in the element phase
     static constexpr int NRT = C / 16, NKT = C / 32;           // token row tiles, 32-deep token steps
     static constexpr int RT = D / 16, KS = D / 32;             // state row tiles, 32-deep channel steps
     static constexpr int PK = D + 8;                           // pitch of [token][channel] planes
     static constexpr int PT = C + 8;                           // pitch of [row][token] planes
     static constexpr int NB = C / 16;                          // 16x16 blocks of the solve
     static constexpr int NTRI = NRT * (NRT + 1) / 2;           // lower 16x16 tiles of a C x C product
-    static constexpr int KT = (C * PK > D * PT) ? C * PK : D * PT;
-    // Two workgroups share a compute unit when the operands of a chunk fit in half the LDS.
+    // Khat^T gets its own LDS region when it fits; otherwise it overwrites Ktil_m after the
+    // C x C products that read it.
+    static constexpr bool KT_SEP = false;
+    static constexpr int KT = KT_SEP ? C * PK : ((C * PK > D * PT) ? C * PK : D * PT);
+    static constexpr int KH = KT_SEP ? D * PT : 8;
+    // Two workgroups share a compute unit when a chunk's operands fit in half the LDS.
     static constexpr int WPE = (C == 32 && MODE == 0) ? 2 : 1;
-    static_assert(TPG % 4 == 0 && (C / 2) % TPG == 0 && NA <= NT && NA % 64 == 0, "element-phase tiling");
+    static_assert(TPG % 4 == 0 && NA <= NT && NA % 64 == 0, "element-phase tiling");
 };
 
 // ------------------------------------------------------------------ LDS layout
@@ -148,18 +167,18 @@ struct Smem {
     static constexpr int NP = MODE == 0 ? 2 : 1, PE = MODE == 0 ? C * K::PT : 8;
     u16 kb[2][C * K::PK];    // Kbar_m = K e^{b - b_m}                 [token][kperm(channel)]
     u16 qb[NQ][QE];          // Qbar_m = Q e^{b - b_m}                 [token][kperm(channel)]
-    u16 kt[2][K::KT];        // Ktil_m = K e^{b_m - b} [token][kperm(channel)], then
-                             // Khat^T = (K e^{b_n - b})^T               [channel][kperm(token)]
+    u16 kt[2][K::KT];        // Ktil_m = K e^{b_m - b} [token][kperm(channel)]; without a
+                             // separate region, then Khat^T = (K e^{b_n - b})^T [channel][kperm(token)]
+    u16 kh[K::KT_SEP ? 2 : 1][K::KH];   // Khat^T when it has its own region
     union {
         float a[C * (C + 1)];     // A, then X = (I + A)^{-1} in place (fp32)
         u16 t[2][C * K::PT];      // T = X Diag(beta)                    [token][kperm(token)]
-        float scan[K::TGA][D];    // per-token-group decay sums
     } at;
     u16 p[NP][PE];           // P = Tril(Qbar Ktil^T)                   [token][kperm(token)]
     float beta[C];
     float em[D];             // e^{b_m}
     float gam[D];            // gamma = e^{b_n}
-    float tmp[K::NB > 1 ? K::NB - 1 : 1][16][16];   // solve scratch
+    float tmp[K::NB > 1 ? K::NB - 1 : 1][16][16];   // solve scratch (wave 0)
 };
 
 // Raw (undecoded) input registers: bf16 stays packed until it is used.
@@ -201,7 +220,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(Cfg<D, C, MODE>::NT, Cfg<D
                                               Cfg<D, C, MODE>::NW * Cfg<D, C, MODE>::WPE / 4)))
 void chunk_kernel(KernelArgs a) {
     using K = Cfg<D, C, MODE>;
-    constexpr int NT = K::NT, NW = K::NW, CQ = K::CQ, TPG = K::TPG, NA = K::NA;
+    constexpr int NT = K::NT, NW = K::NW, TPG = K::TPG, NA = K::NA;
     constexpr int NRT = K::NRT, NKT = K::NKT, RT = K::RT, KS = K::KS, PK = K::PK, PT = K::PT;
     using ST = typename IN::storage;
     using R = Raw<IN>;
@@ -240,7 +259,7 @@ void chunk_kernel(KernelArgs a) {
 
     const bool is_phi = MODE == 1 && w >= D / 32;
     const int j0 = (MODE == 0 ? w : (w % (D / 32))) * 32;
-    const int cq = tid % CQ, tg = tid / CQ, c4 = 4 * cq;
+    const int cq = 8 * w + (l & 7), tg = l >> 3, c4 = 4 * cq;
     const bool loader = tid < NA;
 
     // ---------------------------------------------------------------- entry state
@@ -294,42 +313,38 @@ void chunk_kernel(KernelArgs a) {
         }
         if (tid < C) pb = static_cast<const ST*>(a.beta)[static_cast<size_t>(ts + min(tid, last)) * H + h];
     };
-    __syncthreads();
+    if (c_begin < c_end) fetch(c_begin);
+    lds_barrier();
 
     for (int chunk = c_begin; chunk < c_end; ++chunk) {
         const long ts = t0 + static_cast<long>(chunk) * C;
         const int ntok = static_cast<int>(min(static_cast<long>(C), t1 - ts));
-        fetch(chunk);
 
-        // ============================================================ phase A: decay scan, decayed operands
-        float gr[TPG][4];
+        // ============================================================ phase A: decay prefix, decayed operands
+        float ktk[TPG][4];   // Ktil_m kept for Khat^T after the C x C products
+        float enm[4];
         if (loader) {
+            float gr[TPG][4];
 #pragma unroll
             for (int i = 0; i < TPG; ++i)
 #pragma unroll
                 for (int ch = 0; ch < 4; ++ch)
                     gr[i][ch] = (tg * TPG + i < ntok ? R::get(pg[i], ch) : 0.f) + (i ? gr[i - 1][ch] : 0.f);
+            float off[4], bm[4], bn[4];
 #pragma unroll
-            for (int ch = 0; ch < 4; ++ch) sm.at.scan[tg][c4 + ch] = gr[TPG - 1][ch];
-        }
-        if (tid < C) sm.beta[tid] = tid < ntok ? IN::to_f32(pb) : 0.f;
-        __syncthreads();
-
-        float ktk[TPG][4];   // Ktil_m kept for Khat^T after the C x C products
-        float enm[4];
-        if (loader) {
-            float off[4] = {0.f, 0.f, 0.f, 0.f}, bn[4] = {0.f, 0.f, 0.f, 0.f}, bm[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int ch = 0; ch < 4; ++ch) {
+                // inclusive prefix over the wave's 8 token groups (lanes 8 apart)
+                float incl = gr[TPG - 1][ch];
 #pragma unroll
-            for (int gg = 0; gg < K::TGA; ++gg)
-#pragma unroll
-                for (int ch = 0; ch < 4; ++ch) {
-                    const float x = sm.at.scan[gg][c4 + ch];
-                    bn[ch] += x;
-                    off[ch] += gg < tg ? x : 0.f;
-                    bm[ch] += gg < (C / 2) / TPG ? x : 0.f;
+                for (int dd = 8; dd < 64; dd <<= 1) {
+                    const float y = __shfl_up(incl, dd);
+                    incl += l >= dd ? y : 0.f;
                 }
-#pragma unroll
-            for (int ch = 0; ch < 4; ++ch) enm[ch] = fast_exp(bn[ch] - bm[ch]);
+                off[ch] = incl - gr[TPG - 1][ch];
+                bm[ch] = __shfl(incl, 24 + (l & 7));   // through token C/2 - 1
+                bn[ch] = __shfl(incl, 56 + (l & 7));   // through the chunk's last token
+                enm[ch] = fast_exp(bn[ch] - bm[ch]);
+            }
 #pragma unroll
             for (int i = 0; i < TPG; ++i) {
                 const int r = tg * TPG + i;
@@ -364,7 +379,9 @@ void chunk_kernel(KernelArgs a) {
                 }
             }
         }
-        __syncthreads();
+        if (tid < C) sm.beta[tid] = tid < ntok ? IN::to_f32(pb) : 0.f;
+        lds_barrier();
+
         // V of this chunk (used by the state pass) and the next chunk's k, q, log_alpha,
         // beta stream in while the C x C products and the solve run.
         elem pv[NRT][2][4];
@@ -380,85 +397,90 @@ void chunk_kernel(KernelArgs a) {
                         pv[rt][ct][e] = static_cast<const ST*>(a.v)[(static_cast<size_t>(ts + r) * H + h) * D + j0 + 16 * ct + lr];
                     }
         }
+        if (chunk + 1 < c_end) fetch(chunk + 1);
 
-        // ============================================================ phase B: A and P on MFMA
+        // ============================================================ phase B: C x C products on MFMA
+        // job < NTRI: tile of A = StrictTril(Diag(beta) Kbar_m Ktil_m^T); otherwise a tile of
+        // P = Tril(Qbar_m Ktil_m^T).  Tiles are the lower 16x16 tiles of the C x C product.
+        auto cxc_job = [&](int job) {
+            const bool isP = job >= K::NTRI;
+            const int tj = isP ? job - K::NTRI : job;
+            int rt = 0;
+            while ((rt + 1) * (rt + 2) / 2 <= tj) ++rt;
+            const int ct = tj - rt * (rt + 1) / 2;
+            const u16* ah_base = &sm.kb[0][0];
+            const u16* al_base = &sm.kb[1][0];
+            if constexpr (MODE == 0) {
+                if (isP) { ah_base = &sm.qb[0][0]; al_base = &sm.qb[1][0]; }
+            }
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int ao = (16 * rt + lr) * PK + 32 * ks + 8 * g4;
+                const int bo = (16 * ct + lr) * PK + 32 * ks + 8 * g4;
+                acc = mfma3(frag(ah_base + ao), frag(al_base + ao), frag(&sm.kt[0][bo]), frag(&sm.kt[1][bo]), acc);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * rt + 4 * g4 + e, col = 16 * ct + lr;
+                if (!isP) {
+                    sm.at.a[row * (C + 1) + col] = col < row ? acc[e] * sm.beta[row] : 0.f;
+                } else if constexpr (MODE == 0) {
+                    u16 hi, lo;
+                    split2(col <= row ? acc[e] : 0.f, hi, lo);
+                    sm.p[0][row * PT + kperm(col)] = hi;
+                    sm.p[1][row * PT + kperm(col)] = lo;
+                }
+            }
+        };
+        // Without a separate Khat^T region, P must finish before Khat^T overwrites Ktil_m.
+        constexpr int NJOB_B = (MODE == 0 && !K::KT_SEP) ? 2 * K::NTRI : K::NTRI;
+#pragma unroll
+        for (int jj = 0; jj < (NJOB_B + NW - 1) / NW; ++jj)
+            if (w + jj * NW < NJOB_B) cxc_job(w + jj * NW);
+        lds_barrier();
+
+        // ============================================================ phase C/D: Khat^T, P, and T
+        // Khat^T from registers (all element-phase threads)
         {
-            constexpr int NJOB = (MODE == 0 ? 2 : 1) * K::NTRI;
-            constexpr int JPW = (NJOB + NW - 1) / NW;
+            u16* khi = K::KT_SEP ? &sm.kh[0][0] : &sm.kt[0][0];
+            u16* klo = K::KT_SEP ? &sm.kh[K::KT_SEP ? 1 : 0][0] : &sm.kt[1][0];
+            if (loader) {
 #pragma unroll
-            for (int jj = 0; jj < JPW; ++jj) {
-                const int job = w + jj * NW;
-                if (job < NJOB) {
-                    const bool isP = job >= K::NTRI;
-                    const int tj = isP ? job - K::NTRI : job;
-                    int rt = 0;
-                    while ((rt + 1) * (rt + 2) / 2 <= tj) ++rt;
-                    const int ct = tj - rt * (rt + 1) / 2;
-                    const u16* ah_base = &sm.kb[0][0];
-                    const u16* al_base = &sm.kb[1][0];
-                    if constexpr (MODE == 0) {
-                        if (isP) { ah_base = &sm.qb[0][0]; al_base = &sm.qb[1][0]; }
-                    }
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                for (int ch = 0; ch < 4; ++ch) {
+                    const int c = c4 + ch;
 #pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) {
-                        const int ao = (16 * rt + lr) * PK + 32 * ks + 8 * g4;
-                        const int bo = (16 * ct + lr) * PK + 32 * ks + 8 * g4;
-                        acc = mfma3(frag(ah_base + ao), frag(al_base + ao), frag(&sm.kt[0][bo]), frag(&sm.kt[1][bo]), acc);
-                    }
+                    for (int gq = 0; gq < TPG / 4; ++gq) {
+                        u16 hi[4], lo[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int row = 16 * rt + 4 * g4 + e, col = 16 * ct + lr;
-                        if (!isP) {
-                            sm.at.a[row * (C + 1) + col] = col < row ? acc[e] * sm.beta[row] : 0.f;
-                        } else if constexpr (MODE == 0) {
-                            u16 hi, lo;
-                            split2(col <= row ? acc[e] : 0.f, hi, lo);
-                            sm.p[0][row * PT + kperm(col)] = hi;
-                            sm.p[1][row * PT + kperm(col)] = lo;
-                        }
+                        for (int j = 0; j < 4; ++j) split2(ktk[4 * gq + j][ch] * enm[ch], hi[j], lo[j]);
+                        const int idx = c * PT + kperm(tg * TPG + 4 * gq);
+                        store4(khi + idx, hi);
+                        store4(klo + idx, lo);
                     }
                 }
             }
         }
-        __syncthreads();
-
-        // ============================================================ phase C: Khat^T (registers -> LDS)
-        if (loader) {
-#pragma unroll
-            for (int ch = 0; ch < 4; ++ch) {
-                const int c = c4 + ch;
-#pragma unroll
-                for (int gq = 0; gq < TPG / 4; ++gq) {
-                    u16 hi[4], lo[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) split2(ktk[4 * gq + j][ch] * enm[ch], hi[j], lo[j]);
-                    const int idx = c * PT + kperm(tg * TPG + 4 * gq);
-                    store4(&sm.kt[0][idx], hi);
-                    store4(&sm.kt[1][idx], lo);
-                }
-            }
-        }
-
-        // ============================================================ phase D: T = (I + A)^{-1} Diag(beta)
         if (w == 0 && l < 16 * K::NB) {
-            // one lane per column of each 16x16 diagonal block; forward substitution
+            // Diagonal 16x16 blocks of X = (I + A)^{-1}: one lane per (block, column),
+            // right-looking substitution (the critical path is one FMA per column; the
+            // block entries do not depend on the chain, so their loads can run ahead).
             const int o0 = 16 * (l >> 4), j = l & 15;
             float x[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = r == j ? 1.f : 0.f;
+            for (int r = 0; r < 16; ++r) x[r] = r == j ? 1.f : 0.f;
 #pragma unroll
-                for (int i = 0; i < r; ++i) acc -= sm.at.a[(o0 + r) * (C + 1) + o0 + i] * x[i];
-                x[r] = acc;
-            }
+            for (int i = 0; i < 15; ++i)
+#pragma unroll
+                for (int r = i + 1; r < 16; ++r) x[r] -= sm.at.a[(o0 + r) * (C + 1) + o0 + i] * x[i];
 #pragma unroll
             for (int r = 0; r < 16; ++r) sm.at.a[(o0 + r) * (C + 1) + o0 + j] = x[r];
         }
-        __syncthreads();
+        lds_barrier();
+        // Off-diagonal blocks, one block row at a time:
+        //   X_{bi,bj} = -X_{bi,bi} sum_{bk=bj}^{bi-1} A_{bi,bk} X_{bk,bj}
 #pragma unroll
         for (int bi = 1; bi < K::NB; ++bi) {
-            // Y_{bi,bj} = sum_{bk=bj}^{bi-1} A_{bi,bk} X_{bk,bj}
 #pragma unroll
             for (int u = 0; u < (bi * 256 + NT - 1) / NT; ++u) {
                 const int idx = tid + u * NT;
@@ -472,8 +494,7 @@ void chunk_kernel(KernelArgs a) {
                     sm.tmp[bj][rr][cc] = y;
                 }
             }
-            __syncthreads();
-            // X_{bi,bj} = -X_{bi,bi} Y_{bi,bj}, written over A_{bi,bj}
+            lds_barrier();
 #pragma unroll
             for (int u = 0; u < (bi * 256 + NT - 1) / NT; ++u) {
                 const int idx = tid + u * NT;
@@ -485,9 +506,10 @@ void chunk_kernel(KernelArgs a) {
                     sm.at.a[(16 * bi + rr) * (C + 1) + 16 * bj + cc] = x;
                 }
             }
-            __syncthreads();
+            lds_barrier();
         }
         {
+            // T = X Diag(beta) over the same LDS bytes: stage in registers first.
             constexpr int PER = C * C / NT;
             float tv[PER];
 #pragma unroll
@@ -495,7 +517,7 @@ void chunk_kernel(KernelArgs a) {
                 const int idx = tid + u * NT, r = idx / C, i = idx % C;
                 tv[u] = i <= r ? sm.at.a[r * (C + 1) + i] * sm.beta[i] : 0.f;
             }
-            __syncthreads();
+            lds_barrier();
 #pragma unroll
             for (int u = 0; u < PER; ++u) {
                 const int idx = tid + u * NT, r = idx / C, i = idx % C;
@@ -505,7 +527,7 @@ void chunk_kernel(KernelArgs a) {
                 sm.at.t[1][r * PT + kperm(i)] = lo;
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ============================================================ phase E: state pass (per wave)
         // Y = Kbar S and Z = Qbar S.  The B operands are Diag(e^{b_m}) S (e^{b_m} completes
@@ -612,11 +634,13 @@ void chunk_kernel(KernelArgs a) {
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt) {
                 const int ao = (16 * rt + lr) * PT + 32 * kt + 8 * g4;
-                const bf16x8 kh = frag(&sm.kt[0][ao]), kl = frag(&sm.kt[1][ao]);
+                const u16* khi = K::KT_SEP ? &sm.kh[0][0] : &sm.kt[0][0];
+                const u16* klo = K::KT_SEP ? &sm.kh[K::KT_SEP ? 1 : 0][0] : &sm.kt[1][0];
+                const bf16x8 kh = frag(khi + ao), kl = frag(klo + ao);
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct) S[rt][ct] = mfma3(kh, kl, ubh[kt][ct], ubl[kt][ct], S[rt][ct]);
             }
-        __syncthreads();
+        lds_barrier();
     }
 
     // ---------------------------------------------------------------- exit state
