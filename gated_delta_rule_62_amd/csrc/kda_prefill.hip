@@ -54,6 +54,7 @@ namespace kda {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16;
 
@@ -84,6 +85,29 @@ __device__ __forceinline__ f32x4 mfma3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 b
 }
 
 __device__ __forceinline__ bf16x8 frag(const u16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ bf16x4 frag4(const u16* p) { return *reinterpret_cast<const bf16x4*>(p); }
+
+// 16x16x16 products: a 16x16 accumulator tile is, as it stands, the K = 16 B operand
+// (lane holds rows 4*(lane/16)+e of one column), so tiles chain with no reordering.
+__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma3_16(bf16x4 ah, bf16x4 al, bf16x4 bh, bf16x4 bl, f32x4 c) {
+    c = mfma16(al, bh, c);
+    c = mfma16(ah, bl, c);
+    return mfma16(ah, bh, c);
+}
+__device__ __forceinline__ void split4(f32x4 t, bf16x4& hi, bf16x4& lo) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const __bf16 h = static_cast<__bf16>(t[e]);
+        hi[e] = h;
+        lo[e] = static_cast<__bf16>(t[e] - static_cast<float>(h));
+    }
+}
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
 
 // Workgroup barrier for LDS traffic only.  The waves of a workgroup exchange data
 // through LDS alone, so the barrier waits for this wave's LDS operations and leaves
@@ -148,6 +172,8 @@ struct Cfg {
     static constexpr int PK = D + 8;                           // pitch of [token][channel] planes
     static constexpr int PT = C + 8;                           // pitch of [row][token] planes
     static constexpr int NB = C / 16;                          // 16x16 blocks of the solve
+    static constexpr int AP = C + 4;                           // pitch of the off-diagonal A planes
+    static constexpr int XP = 20;                              // pitch of the diagonal-inverse planes
     static constexpr int NTRI = NRT * (NRT + 1) / 2;           // lower 16x16 tiles of a C x C product
     // Khat^T gets its own LDS region when it fits; otherwise it overwrites Ktil_m after the
     // C x C products that read it.
@@ -170,15 +196,13 @@ struct Smem {
     u16 kt[2][K::KT];        // Ktil_m = K e^{b_m - b} [token][kperm(channel)]; without a
                              // separate region, then Khat^T = (K e^{b_n - b})^T [channel][kperm(token)]
     u16 kh[K::KT_SEP ? 2 : 1][K::KH];   // Khat^T when it has its own region
-    union {
-        float a[C * (C + 1)];     // A, then X = (I + A)^{-1} in place (fp32)
-        u16 t[2][C * K::PT];      // T = X Diag(beta)                    [token][kperm(token)]
-    } at;
+    float a[K::NB][16][17];  // diagonal 16x16 blocks of A (fp32)
+    u16 aoff[2][C * K::AP];  // -A off the diagonal blocks               [token][token]
+    u16 xd[2][C * K::XP];    // X_bb = (I + A_bb)^{-1} per diagonal block [16 b + r][c]
     u16 p[NP][PE];           // P = Tril(Qbar Ktil^T)                   [token][kperm(token)]
     float beta[C];
     float em[D];             // e^{b_m}
     float gam[D];            // gamma = e^{b_n}
-    float tmp[K::NB > 1 ? K::NB - 1 : 1][16][16];   // solve scratch (wave 0)
 };
 
 // Raw (undecoded) input registers: bf16 stays packed until it is used.
@@ -424,7 +448,14 @@ void chunk_kernel(KernelArgs a) {
             for (int e = 0; e < 4; ++e) {
                 const int row = 16 * rt + 4 * g4 + e, col = 16 * ct + lr;
                 if (!isP) {
-                    sm.at.a[row * (C + 1) + col] = col < row ? acc[e] * sm.beta[row] : 0.f;
+                    if (rt == ct) {
+                        sm.a[rt][4 * g4 + e][lr] = col < row ? acc[e] * sm.beta[row] : 0.f;
+                    } else {
+                        u16 hi, lo;
+                        split2(-acc[e] * sm.beta[row], hi, lo);
+                        sm.aoff[0][row * K::AP + col] = hi;
+                        sm.aoff[1][row * K::AP + col] = lo;
+                    }
                 } else if constexpr (MODE == 0) {
                     u16 hi, lo;
                     split2(col <= row ? acc[e] : 0.f, hi, lo);
@@ -462,9 +493,8 @@ void chunk_kernel(KernelArgs a) {
             }
         }
         if (w == 0 && l < 16 * K::NB) {
-            // Diagonal 16x16 blocks of X = (I + A)^{-1}: one lane per (block, column),
-            // right-looking substitution (the critical path is one FMA per column; the
-            // block entries do not depend on the chain, so their loads can run ahead).
+            // X_bb = (I + A_bb)^{-1} for each diagonal 16x16 block: one lane per (block,
+            // column), right-looking substitution (critical path: one FMA per column).
             const int o0 = 16 * (l >> 4), j = l & 15;
             float x[16];
 #pragma unroll
@@ -472,59 +502,13 @@ void chunk_kernel(KernelArgs a) {
 #pragma unroll
             for (int i = 0; i < 15; ++i)
 #pragma unroll
-                for (int r = i + 1; r < 16; ++r) x[r] -= sm.at.a[(o0 + r) * (C + 1) + o0 + i] * x[i];
+                for (int r = i + 1; r < 16; ++r) x[r] -= sm.a[l >> 4][r][i] * x[i];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sm.at.a[(o0 + r) * (C + 1) + o0 + j] = x[r];
-        }
-        lds_barrier();
-        // Off-diagonal blocks, one block row at a time:
-        //   X_{bi,bj} = -X_{bi,bi} sum_{bk=bj}^{bi-1} A_{bi,bk} X_{bk,bj}
-#pragma unroll
-        for (int bi = 1; bi < K::NB; ++bi) {
-#pragma unroll
-            for (int u = 0; u < (bi * 256 + NT - 1) / NT; ++u) {
-                const int idx = tid + u * NT;
-                if (idx < bi * 256) {
-                    const int bj = idx >> 8, rr = (idx >> 4) & 15, cc = idx & 15;
-                    float y = 0.f;
-                    for (int bk = bj; bk < bi; ++bk)
-#pragma unroll
-                        for (int m = 0; m < 16; ++m)
-                            y += sm.at.a[(16 * bi + rr) * (C + 1) + 16 * bk + m] * sm.at.a[(16 * bk + m) * (C + 1) + 16 * bj + cc];
-                    sm.tmp[bj][rr][cc] = y;
-                }
-            }
-            lds_barrier();
-#pragma unroll
-            for (int u = 0; u < (bi * 256 + NT - 1) / NT; ++u) {
-                const int idx = tid + u * NT;
-                if (idx < bi * 256) {
-                    const int bj = idx >> 8, rr = (idx >> 4) & 15, cc = idx & 15;
-                    float x = 0.f;
-#pragma unroll
-                    for (int m = 0; m < 16; ++m) x -= sm.at.a[(16 * bi + rr) * (C + 1) + 16 * bi + m] * sm.tmp[bj][m][cc];
-                    sm.at.a[(16 * bi + rr) * (C + 1) + 16 * bj + cc] = x;
-                }
-            }
-            lds_barrier();
-        }
-        {
-            // T = X Diag(beta) over the same LDS bytes: stage in registers first.
-            constexpr int PER = C * C / NT;
-            float tv[PER];
-#pragma unroll
-            for (int u = 0; u < PER; ++u) {
-                const int idx = tid + u * NT, r = idx / C, i = idx % C;
-                tv[u] = i <= r ? sm.at.a[r * (C + 1) + i] * sm.beta[i] : 0.f;
-            }
-            lds_barrier();
-#pragma unroll
-            for (int u = 0; u < PER; ++u) {
-                const int idx = tid + u * NT, r = idx / C, i = idx % C;
+            for (int r = 0; r < 16; ++r) {
                 u16 hi, lo;
-                split2(tv[u], hi, lo);
-                sm.at.t[0][r * PT + kperm(i)] = hi;
-                sm.at.t[1][r * PT + kperm(i)] = lo;
+                split2(x[r], hi, lo);
+                sm.xd[0][(o0 + r) * K::XP + j] = hi;
+                sm.xd[1][(o0 + r) * K::XP + j] = lo;
             }
         }
         lds_barrier();
@@ -563,7 +547,8 @@ void chunk_kernel(KernelArgs a) {
                 }
             }
         }
-        // Unew = T (V - Kbar S)
+        // Unew = (I + A)^{-1} Diag(beta) (V - Kbar S), one 16-token block at a time:
+        //   Unew_b = X_bb (beta_b (V - Kbar S)_b - sum_{k<b} A_bk Unew_k)
         f32x4 V[NRT][2];
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt)
@@ -572,31 +557,41 @@ void chunk_kernel(KernelArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     V[rt][ct][e] = (!is_phi && 16 * rt + 4 * g4 + e < ntok) ? IN::to_f32(pv[rt][ct][e]) : 0.f;
-        bf16x8 dbh[NKT][2], dbl[NKT][2];
+        f32x4 U[NRT][2];
+        bf16x4 uh[NRT][2], ul[NRT][2];
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
+        for (int b = 0; b < NRT; ++b) {
+            f32x4 acc[2];
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct)
-                split_b(V[2 * kt][ct] - Y[2 * kt][ct], V[2 * kt + 1][ct] - Y[2 * kt + 1][ct], dbh[kt][ct], dbl[kt][ct]);
-        f32x4 U[NRT][2];
 #pragma unroll
-        for (int rt = 0; rt < NRT; ++rt)
+                for (int e = 0; e < 4; ++e) acc[ct][e] = sm.beta[16 * b + 4 * g4 + e] * (V[b][ct][e] - Y[b][ct][e]);
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) U[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int k = 0; k < b; ++k) {
+                const int ao = (16 * b + lr) * K::AP + 16 * k + 4 * g4;
+                const bf16x4 ah = frag4(&sm.aoff[0][ao]), al = frag4(&sm.aoff[1][ao]);
 #pragma unroll
-        for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-            for (int kt = 0; kt <= (rt >> 1); ++kt) {
-                const int ao = (16 * rt + lr) * PT + 32 * kt + 8 * g4;
-                const bf16x8 th = frag(&sm.at.t[0][ao]), tl = frag(&sm.at.t[1][ao]);
-#pragma unroll
-                for (int ct = 0; ct < 2; ++ct) U[rt][ct] = mfma3(th, tl, dbh[kt][ct], dbl[kt][ct], U[rt][ct]);
+                for (int ct = 0; ct < 2; ++ct) acc[ct] = mfma3_16(ah, al, uh[k][ct], ul[k][ct], acc[ct]);
             }
+            const int xo = (16 * b + lr) * K::XP + 4 * g4;
+            const bf16x4 xh = frag4(&sm.xd[0][xo]), xl = frag4(&sm.xd[1][xo]);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                bf16x4 bh, bl;
+                split4(acc[ct], bh, bl);
+                U[b][ct] = mfma3_16(xh, xl, bh, bl, f32x4{0.f, 0.f, 0.f, 0.f});
+                split4(U[b][ct], uh[b][ct], ul[b][ct]);
+            }
+        }
+        // 32-deep B operands of Unew: two stacked tiles in kperm order
         bf16x8 ubh[NKT][2], ubl[NKT][2];
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) split_b(U[2 * kt][ct], U[2 * kt + 1][ct], ubh[kt][ct], ubl[kt][ct]);
+            for (int ct = 0; ct < 2; ++ct) {
+                ubh[kt][ct] = cat8(uh[2 * kt][ct], uh[2 * kt + 1][ct]);
+                ubl[kt][ct] = cat8(ul[2 * kt][ct], ul[2 * kt + 1][ct]);
+            }
 
         if constexpr (MODE == 0) {
             // O = Qbar S + P Unew
