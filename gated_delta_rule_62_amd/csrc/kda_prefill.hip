@@ -67,6 +67,10 @@ __host__ __device__ constexpr int kperm(int x) { return (x & ~31) | kpos(x & 31)
 
 __device__ __forceinline__ u16 bits(__bf16 h) { return __builtin_bit_cast(u16, h); }
 
+constexpr float kLog2e = 1.4426950408889634f;
+// 2^x on the hardware exp2 unit (v_exp_f32)
+__device__ __forceinline__ float exp2f_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ void split2(float x, u16& hi, u16& lo) {
     const __bf16 h = static_cast<__bf16>(x);
     hi = bits(h);
@@ -159,7 +163,12 @@ __device__ __forceinline__ void load4(const typename IN::storage* p, size_t off,
 // ------------------------------------------------------------------ compile-time shape
 template <int D, int C, int MODE>
 struct Cfg {
-    static constexpr int NW = MODE == 0 ? D / 32 : D / 16;   // waves; each owns 32 state columns
+    // The output pass at the 32-token chunk gives each of D/16 waves 16 state columns
+    // (one 16-wide tile); at the 64-token chunk, whose larger intra-chunk working set
+    // needs the full register file, D/32 waves of 32 columns.  The summary pass carries
+    // [S | Phi] (2D columns) on D/16 waves, 32 columns each.
+    static constexpr int CT = (MODE == 0 && C == 32) ? 1 : 2;  // 16-column tiles per wave
+    static constexpr int NW = (MODE == 0 ? D : 2 * D) / (16 * CT);
     static constexpr int NT = 64 * NW;
     static constexpr int CQ = D / 4;                           // channel quads
     // Element phase: each of the first NA threads owns one channel quad over TPG tokens; a
@@ -180,8 +189,7 @@ struct Cfg {
     static constexpr bool KT_SEP = false;
     static constexpr int KT = KT_SEP ? C * PK : ((C * PK > D * PT) ? C * PK : D * PT);
     static constexpr int KH = KT_SEP ? D * PT : 8;
-    // Two workgroups share a compute unit when a chunk's operands fit in half the LDS.
-    static constexpr int WPE = (C == 32 && MODE == 0) ? 2 : 1;
+    static constexpr int WPE = 1;   // one workgroup per compute unit (D/16 waves)
     static_assert(TPG % 4 == 0 && NA <= NT && NA % 64 == 0, "element-phase tiling");
 };
 
@@ -244,7 +252,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(Cfg<D, C, MODE>::NT, Cfg<D
                                               Cfg<D, C, MODE>::NW * Cfg<D, C, MODE>::WPE / 4)))
 void chunk_kernel(KernelArgs a) {
     using K = Cfg<D, C, MODE>;
-    constexpr int NT = K::NT, NW = K::NW, TPG = K::TPG, NA = K::NA;
+    constexpr int NT = K::NT, NW = K::NW, CT = K::CT, TPG = K::TPG, NA = K::NA;
     constexpr int NRT = K::NRT, NKT = K::NKT, RT = K::RT, KS = K::KS, PK = K::PK, PT = K::PT;
     using ST = typename IN::storage;
     using R = Raw<IN>;
@@ -282,12 +290,12 @@ void chunk_kernel(KernelArgs a) {
     const size_t ubase = static_cast<size_t>(unit) * D * D;
 
     const bool is_phi = MODE == 1 && w >= D / 32;
-    const int j0 = (MODE == 0 ? w : (w % (D / 32))) * 32;
+    const int j0 = MODE == 0 ? 16 * CT * w : 32 * (w % (NW / 2));
     const int cq = 8 * w + (l & 7), tg = l >> 3, c4 = 4 * cq;
     const bool loader = tid < NA;
 
     // ---------------------------------------------------------------- entry state
-    f32x4 S[RT][2];
+    f32x4 S[RT][CT];
     {
         const float* src = nullptr;
         if constexpr (MODE == 0) {
@@ -298,7 +306,7 @@ void chunk_kernel(KernelArgs a) {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct)
+                for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         S[rt][ct][e] = src[(16 * rt + 4 * g4 + e) * D + j0 + 16 * ct + lr];
@@ -306,7 +314,7 @@ void chunk_kernel(KernelArgs a) {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct)
+                for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         S[rt][ct][e] = (is_phi && 16 * rt + 4 * g4 + e == j0 + 16 * ct + lr) ? 1.f : 0.f;
@@ -322,20 +330,32 @@ void chunk_kernel(KernelArgs a) {
     // zeroed when used, so every load is unconditional.
     quad pk[TPG], pq[TPG], pg[TPG];
     elem pb = 0;
+    const int HD = H * D;   // elements between consecutive tokens of one head
     auto fetch = [&](int chunk) {
         const long ts = t0 + static_cast<long>(chunk) * C;
         const int last = static_cast<int>(min(static_cast<long>(C), t1 - ts)) - 1;
+        const size_t base = (static_cast<size_t>(ts) * H + h) * D;   // uniform
+        const ST* kp = static_cast<const ST*>(a.k) + base;
+        const ST* gp = static_cast<const ST*>(a.g) + base;
+        const ST* qp = static_cast<const ST*>(a.q) + base;
         if (loader) {
 #pragma unroll
             for (int i = 0; i < TPG; ++i) {
-                const int r = min(tg * TPG + i, last);
-                const size_t off = (static_cast<size_t>(ts + r) * H + h) * D + c4;
-                pk[i] = *reinterpret_cast<const quad*>(static_cast<const ST*>(a.k) + off);
-                pg[i] = *reinterpret_cast<const quad*>(static_cast<const ST*>(a.g) + off);
-                if constexpr (MODE == 0) pq[i] = *reinterpret_cast<const quad*>(static_cast<const ST*>(a.q) + off);
+                const unsigned off = static_cast<unsigned>(min(tg * TPG + i, last) * HD + c4);
+                pk[i] = *reinterpret_cast<const quad*>(kp + off);
+                pg[i] = *reinterpret_cast<const quad*>(gp + off);
+                if constexpr (MODE == 0) pq[i] = *reinterpret_cast<const quad*>(qp + off);
+            }
+            if (last < C - 1) {   // ragged last chunk: padded rows read as zero
+#pragma unroll
+                for (int i = 0; i < TPG; ++i)
+                    if (tg * TPG + i > last) pk[i] = pg[i] = pq[i] = quad{};
             }
         }
-        if (tid < C) pb = static_cast<const ST*>(a.beta)[static_cast<size_t>(ts + min(tid, last)) * H + h];
+        if (tid < C) {
+            pb = static_cast<const ST*>(a.beta)[static_cast<size_t>(ts + min(tid, last)) * H + h];
+            if (tid > last) pb = elem{};
+        }
     };
     if (c_begin < c_end) fetch(c_begin);
     lds_barrier();
@@ -353,7 +373,7 @@ void chunk_kernel(KernelArgs a) {
             for (int i = 0; i < TPG; ++i)
 #pragma unroll
                 for (int ch = 0; ch < 4; ++ch)
-                    gr[i][ch] = (tg * TPG + i < ntok ? R::get(pg[i], ch) : 0.f) + (i ? gr[i - 1][ch] : 0.f);
+                    gr[i][ch] = R::get(pg[i], ch) * kLog2e + (i ? gr[i - 1][ch] : 0.f);   // log2 units
             float off[4], bm[4], bn[4];
 #pragma unroll
             for (int ch = 0; ch < 4; ++ch) {
@@ -367,23 +387,22 @@ void chunk_kernel(KernelArgs a) {
                 off[ch] = incl - gr[TPG - 1][ch];
                 bm[ch] = __shfl(incl, 24 + (l & 7));   // through token C/2 - 1
                 bn[ch] = __shfl(incl, 56 + (l & 7));   // through the chunk's last token
-                enm[ch] = fast_exp(bn[ch] - bm[ch]);
+                enm[ch] = exp2f_hw(bn[ch] - bm[ch]);
             }
 #pragma unroll
             for (int i = 0; i < TPG; ++i) {
                 const int r = tg * TPG + i;
-                const bool valid = r < ntok;
                 u16 kh[4], kl[4], th[4], tl[4], qh[4], ql[4];
 #pragma unroll
                 for (int ch = 0; ch < 4; ++ch) {
-                    const float b = gr[i][ch] + off[ch];
-                    const float em = fast_exp(b - bm[ch]);
-                    const float ei = fast_exp(bm[ch] - b);
-                    const float kv = valid ? R::get(pk[i], ch) : 0.f;
+                    const float b = gr[i][ch] + off[ch] - bm[ch];   // b_r - b_m, log2 units
+                    const float em = exp2f_hw(b);
+                    const float ei = exp2f_hw(-b);
+                    const float kv = R::get(pk[i], ch);
                     split2(kv * em, kh[ch], kl[ch]);
                     ktk[i][ch] = kv * ei;
                     split2(ktk[i][ch], th[ch], tl[ch]);
-                    if constexpr (MODE == 0) split2((valid ? R::get(pq[i], ch) : 0.f) * em, qh[ch], ql[ch]);
+                    if constexpr (MODE == 0) split2(R::get(pq[i], ch) * em, qh[ch], ql[ch]);
                 }
                 const int idx = r * PK + kperm(c4);
                 store4(&sm.kb[0][idx], kh);
@@ -398,28 +417,36 @@ void chunk_kernel(KernelArgs a) {
             if (tg == 0) {
 #pragma unroll
                 for (int ch = 0; ch < 4; ++ch) {
-                    sm.em[c4 + ch] = fast_exp(bm[ch]);
-                    sm.gam[c4 + ch] = fast_exp(bn[ch]);
+                    sm.em[c4 + ch] = exp2f_hw(bm[ch]);
+                    sm.gam[c4 + ch] = exp2f_hw(bn[ch]);
                 }
             }
         }
-        if (tid < C) sm.beta[tid] = tid < ntok ? IN::to_f32(pb) : 0.f;
+        if (tid < C) sm.beta[tid] = IN::to_f32(pb);
         lds_barrier();
 
         // V of this chunk (used by the state pass) and the next chunk's k, q, log_alpha,
         // beta stream in while the C x C products and the solve run.
-        elem pv[NRT][2][4];
+        elem pv[NRT][CT][4];
         if (!is_phi) {
             const int last = ntok - 1;
+            const ST* vp = static_cast<const ST*>(a.v) + (static_cast<size_t>(ts) * H + h) * D + j0 + lr;
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct)
+                for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = min(16 * rt + 4 * g4 + e, last);
-                        pv[rt][ct][e] = static_cast<const ST*>(a.v)[(static_cast<size_t>(ts + r) * H + h) * D + j0 + 16 * ct + lr];
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        pv[rt][ct][e] = vp[static_cast<unsigned>(min(16 * rt + 4 * g4 + e, last) * HD + 16 * ct)];
+            if (last < C - 1) {
+#pragma unroll
+                for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (16 * rt + 4 * g4 + e > last) pv[rt][ct][e] = elem{};
+            }
         }
         if (chunk + 1 < c_end) fetch(chunk + 1);
 
@@ -516,16 +543,16 @@ void chunk_kernel(KernelArgs a) {
         // ============================================================ phase E: state pass (per wave)
         // Y = Kbar S and Z = Qbar S.  The B operands are Diag(e^{b_m}) S (e^{b_m} completes
         // Kbar_m / Qbar_m to Kbar / Qbar), split per 32-deep step to keep registers low.
-        f32x4 Y[NRT][2], Z[NRT][2];
+        f32x4 Y[NRT][CT], Z[NRT][CT];
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) Y[rt][ct] = Z[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int ct = 0; ct < CT; ++ct) Y[rt][ct] = Z[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            bf16x8 sbh[2], sbl[2];
+            bf16x8 sbh[CT], sbl[CT];
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
+            for (int ct = 0; ct < CT; ++ct) {
                 f32x4 x0 = S[2 * ks][ct], x1 = S[2 * ks + 1][ct];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -539,31 +566,31 @@ void chunk_kernel(KernelArgs a) {
                 const int ao = (16 * rt + lr) * PK + 32 * ks + 8 * g4;
                 const bf16x8 kh = frag(&sm.kb[0][ao]), kl = frag(&sm.kb[1][ao]);
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) Y[rt][ct] = mfma3(kh, kl, sbh[ct], sbl[ct], Y[rt][ct]);
+                for (int ct = 0; ct < CT; ++ct) Y[rt][ct] = mfma3(kh, kl, sbh[ct], sbl[ct], Y[rt][ct]);
                 if constexpr (MODE == 0) {
                     const bf16x8 qh = frag(&sm.qb[0][ao]), ql = frag(&sm.qb[1][ao]);
 #pragma unroll
-                    for (int ct = 0; ct < 2; ++ct) Z[rt][ct] = mfma3(qh, ql, sbh[ct], sbl[ct], Z[rt][ct]);
+                    for (int ct = 0; ct < CT; ++ct) Z[rt][ct] = mfma3(qh, ql, sbh[ct], sbl[ct], Z[rt][ct]);
                 }
             }
         }
         // Unew = (I + A)^{-1} Diag(beta) (V - Kbar S), one 16-token block at a time:
         //   Unew_b = X_bb (beta_b (V - Kbar S)_b - sum_{k<b} A_bk Unew_k)
-        f32x4 V[NRT][2];
+        f32x4 V[NRT][CT];
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    V[rt][ct][e] = (!is_phi && 16 * rt + 4 * g4 + e < ntok) ? IN::to_f32(pv[rt][ct][e]) : 0.f;
-        f32x4 U[NRT][2];
-        bf16x4 uh[NRT][2], ul[NRT][2];
+                    V[rt][ct][e] = is_phi ? 0.f : IN::to_f32(pv[rt][ct][e]);
+        f32x4 U[NRT][CT];
+        bf16x4 uh[NRT][CT], ul[NRT][CT];
 #pragma unroll
         for (int b = 0; b < NRT; ++b) {
-            f32x4 acc[2];
+            f32x4 acc[CT];
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[ct][e] = sm.beta[16 * b + 4 * g4 + e] * (V[b][ct][e] - Y[b][ct][e]);
 #pragma unroll
@@ -571,12 +598,12 @@ void chunk_kernel(KernelArgs a) {
                 const int ao = (16 * b + lr) * K::AP + 16 * k + 4 * g4;
                 const bf16x4 ah = frag4(&sm.aoff[0][ao]), al = frag4(&sm.aoff[1][ao]);
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) acc[ct] = mfma3_16(ah, al, uh[k][ct], ul[k][ct], acc[ct]);
+                for (int ct = 0; ct < CT; ++ct) acc[ct] = mfma3_16(ah, al, uh[k][ct], ul[k][ct], acc[ct]);
             }
             const int xo = (16 * b + lr) * K::XP + 4 * g4;
             const bf16x4 xh = frag4(&sm.xd[0][xo]), xl = frag4(&sm.xd[1][xo]);
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
+            for (int ct = 0; ct < CT; ++ct) {
                 bf16x4 bh, bl;
                 split4(acc[ct], bh, bl);
                 U[b][ct] = mfma3_16(xh, xl, bh, bl, f32x4{0.f, 0.f, 0.f, 0.f});
@@ -584,11 +611,11 @@ void chunk_kernel(KernelArgs a) {
             }
         }
         // 32-deep B operands of Unew: two stacked tiles in kperm order
-        bf16x8 ubh[NKT][2], ubl[NKT][2];
+        bf16x8 ubh[NKT][CT], ubl[NKT][CT];
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
+            for (int ct = 0; ct < CT; ++ct) {
                 ubh[kt][ct] = cat8(uh[2 * kt][ct], uh[2 * kt + 1][ct]);
                 ubl[kt][ct] = cat8(ul[2 * kt][ct], ul[2 * kt + 1][ct]);
             }
@@ -602,26 +629,26 @@ void chunk_kernel(KernelArgs a) {
                     const int ao = (16 * rt + lr) * PT + 32 * kt + 8 * g4;
                     const bf16x8 ph = frag(&sm.p[0][ao]), pl = frag(&sm.p[1][ao]);
 #pragma unroll
-                    for (int ct = 0; ct < 2; ++ct) Z[rt][ct] = mfma3(ph, pl, ubh[kt][ct], ubl[kt][ct], Z[rt][ct]);
+                    for (int ct = 0; ct < CT; ++ct) Z[rt][ct] = mfma3(ph, pl, ubh[kt][ct], ubl[kt][ct], Z[rt][ct]);
                 }
             const bool full = ntok == C;   // uniform: only a sequence's last chunk can be ragged
+            const size_t obase = (static_cast<size_t>(ts) * H + h) * D + j0 + lr;
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct)
+                for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int row = 16 * rt + 4 * g4 + e;
                         if (full || row < ntok)
-                            store_out<OUT_BF16>(a.o, (static_cast<size_t>(ts + row) * H + h) * D + j0 + 16 * ct + lr,
-                                                Z[rt][ct][e]);
+                            store_out<OUT_BF16>(a.o, obase + static_cast<unsigned>(row * HD + 16 * ct), Z[rt][ct][e]);
                     }
         }
         // S <- Diag(gamma) S + Khat^T Unew
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) S[rt][ct][e] *= sm.gam[16 * rt + 4 * g4 + e];
 #pragma unroll
@@ -633,7 +660,7 @@ void chunk_kernel(KernelArgs a) {
                 const u16* klo = K::KT_SEP ? &sm.kh[K::KT_SEP ? 1 : 0][0] : &sm.kt[1][0];
                 const bf16x8 kh = frag(khi + ao), kl = frag(klo + ao);
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) S[rt][ct] = mfma3(kh, kl, ubh[kt][ct], ubl[kt][ct], S[rt][ct]);
+                for (int ct = 0; ct < CT; ++ct) S[rt][ct] = mfma3(kh, kl, ubh[kt][ct], ubl[kt][ct], S[rt][ct]);
             }
         lds_barrier();
     }
@@ -649,7 +676,506 @@ void chunk_kernel(KernelArgs a) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    dst[(16 * rt + 4 * g4 + e) * D + j0 + 16 * ct + lr] = S[rt][ct][e];
+    }
+}
+
+// ------------------------------------------------------------------ pipelined kernel (C = 32)
+// The operands of a chunk depend only on that chunk's inputs, never on the state, so
+// they are built one chunk ahead.  Producer waves (one per SIMD) build chunk c+1's
+// decayed operands, the C x C products and the diagonal-block inverses into one LDS
+// buffer while consumer waves run chunk c's state pass out of the other.  Both sides
+// meet at three workgroup barriers per chunk, and the work between two barriers is
+// paired so that one side's vector-ALU work runs beside the other side's MFMA work:
+//
+//   interval   producer (chunk c+1)                 consumer (chunk c)
+//   1          decay prefix, decayed K/Q splits     Y = Kbar S, Z = Qbar S
+//   2          A and P tiles                        Unew block recurrence, O
+//   3          Khat^T, diagonal-block inverses      S <- Diag(gamma) S + Khat^T Unew
+template <int D, int MODE>
+struct PCfg {
+    static constexpr int C = 32;
+    static constexpr int NPW = D / 32;                             // producer waves
+    static constexpr int CT = 2;                                   // 16-column tiles per consumer wave
+    static constexpr int NCW = (MODE == 0 ? D : 2 * D) / (16 * CT);   // consumer waves
+    static constexpr int NW = NPW + NCW;
+    static constexpr int NT = 64 * NW;
+    static constexpr int WPE = (NW + 3) / 4;                       // waves per SIMD
+    static constexpr int TPG = C / 8;                              // tokens per producer thread
+    static constexpr int NRT = C / 16, RT = D / 16, KS = D / 32;
+    static constexpr int PK = D + 8;                               // pitch of [token][channel] planes
+    static constexpr int PT = C + 8;                               // pitch of [row][token] planes
+    static constexpr int AP = C + 4;                               // pitch of the off-diagonal A planes
+    static constexpr int XP = 24;                                  // pitch of the diagonal-inverse planes
+    static constexpr int KT = (C * PK > D * PT) ? C * PK : D * PT;
+    static constexpr int NJOB = 3;                                 // lower 16x16 tiles of a 32 x 32 product
+};
+
+template <int D, int MODE>
+struct alignas(16) PBuf {
+    using K = PCfg<D, MODE>;
+    static constexpr int NQ = MODE == 0 ? 2 : 1, QE = MODE == 0 ? K::C * K::PK : 8;
+    static constexpr int PE = MODE == 0 ? K::C * K::PT : 8;
+    u16 kb[2][K::C * K::PK];    // Kbar_m = K e^{b - b_m}     [token][kperm(channel)]
+    u16 qb[NQ][QE];             // Qbar_m = Q e^{b - b_m}     [token][kperm(channel)]
+    u16 kt[2][K::KT];           // Ktil_m = K e^{b_m - b} [token][kperm(channel)], then
+                                // Khat^T = (K e^{b_n - b})^T [channel][kperm(token)]
+    u16 aoff[2][K::C * K::AP];  // -A off the diagonal blocks  [token][token]
+    u16 xd[2][K::C * K::XP];    // X_bb = (I + A_bb)^{-1}      [16 b + r][c]
+    u16 p[NQ][PE];              // P = Tril(Qbar Ktil^T)       [token][kperm(token)]
+    float beta[K::C];
+    float em[D];                // e^{b_m}
+    float gam[D];               // gamma = e^{b_n}
+};
+
+template <int D, int MODE>
+struct PSmem {
+    PBuf<D, MODE> buf[2];
+    float a[2][16][20];         // diagonal 16x16 blocks of A (fp32), producer-private
+};
+
+template <int D, typename IN, bool OUT_BF16, int MODE>
+__global__ __attribute__((amdgpu_flat_work_group_size(PCfg<D, MODE>::NT, PCfg<D, MODE>::NT),
+                          amdgpu_waves_per_eu(PCfg<D, MODE>::WPE, PCfg<D, MODE>::WPE)))
+void pipe_kernel(KernelArgs a) {
+    using K = PCfg<D, MODE>;
+    constexpr int C = K::C, NPW = K::NPW, CT = K::CT, TPG = K::TPG;
+    constexpr int NRT = K::NRT, RT = K::RT, KS = K::KS, PK = K::PK, PT = K::PT;
+    using ST = typename IN::storage;
+    using R = Raw<IN>;
+    using quad = typename R::quad;
+    using elem = typename R::elem;
+    using Buf = PBuf<D, MODE>;
+
+    __shared__ PSmem<D, MODE> sm;
+
+    const int tid = threadIdx.x, l = tid & 63, g4 = l >> 4, lr = l & 15;
+    // wave index in a scalar register: the producer / consumer split below is a uniform
+    // branch, so each side runs its own loop with its own registers
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int H = a.H;
+    const bool producer = w < NPW;
+
+    // ---------------------------------------------------------------- work unit
+    int n, h, s, c_begin, c_end;
+    long t0, t1;
+    if (a.cu) {
+        const int rank = blockIdx.x / H;
+        h = blockIdx.x % H;
+        n = a.order[rank];
+        t0 = a.cu[n];
+        t1 = a.cu[n + 1];
+        s = 0;
+        c_begin = 0;
+        c_end = static_cast<int>((t1 - t0 + C - 1) / C);
+    } else {
+        const int unit = blockIdx.x % a.NH;
+        s = blockIdx.x / a.NH;
+        n = unit / H;
+        h = unit % H;
+        t0 = static_cast<long>(n) * a.T;
+        t1 = t0 + a.T;
+        c_begin = s * a.cps;
+        c_end = min(c_begin + a.cps, a.chunks);
+    }
+    const int unit = n * H + h;
+    const size_t ubase = static_cast<size_t>(unit) * D * D;
+    const int HD = H * D;   // elements between consecutive tokens of one head
+
+    // consumer identity: 32 state columns starting at j0 (of S, or of Phi in the summary pass)
+    const int ci = producer ? 0 : w - NPW;
+    const bool is_phi = MODE == 1 && ci >= D / 32;
+    const int j0 = 32 * (ci % (D / 32));
+    // producer identity: channel quad cq, token group tg (TPG tokens)
+    const int cq = 8 * w + (l & 7), tg = l >> 3, c4 = 4 * cq;
+
+    if constexpr (MODE == 0) {
+        // P's strictly-upper 16x16 tile inside the 32-deep step is read but never written.
+        for (int i = tid; i < 2 * 2 * C * PT; i += K::NT) {
+            const int b = i / (2 * C * PT), r = i % (2 * C * PT);
+            sm.buf[b].p[r / (C * PT)][r % (C * PT)] = 0;
+        }
+    }
+
+    // ================================================================ producer state
+    quad pk[TPG], pq[TPG], pg[TPG];
+    elem pb = 0;
+    float ktk[TPG][4];   // Ktil_m, kept from interval 1 for Khat^T in interval 3
+    float enm[4];        // e^{b_n - b_m}
+    auto fetch = [&](int chunk) {
+        const long ts = t0 + static_cast<long>(chunk) * C;
+        const int last = static_cast<int>(min(static_cast<long>(C), t1 - ts)) - 1;
+        const size_t base = (static_cast<size_t>(ts) * H + h) * D;   // uniform
+        const ST* kp = static_cast<const ST*>(a.k) + base;
+        const ST* gp = static_cast<const ST*>(a.g) + base;
+        const ST* qp = static_cast<const ST*>(a.q) + base;
+#pragma unroll
+        for (int i = 0; i < TPG; ++i) {
+            const unsigned off = static_cast<unsigned>(min(tg * TPG + i, last) * HD + c4);
+            pk[i] = *reinterpret_cast<const quad*>(kp + off);
+            pg[i] = *reinterpret_cast<const quad*>(gp + off);
+            if constexpr (MODE == 0) pq[i] = *reinterpret_cast<const quad*>(qp + off);
+        }
+        if (last < C - 1) {   // ragged last chunk: padded rows read as zero
+#pragma unroll
+            for (int i = 0; i < TPG; ++i)
+                if (tg * TPG + i > last) pk[i] = pg[i] = pq[i] = quad{};
+        }
+        if (tid < C) {
+            pb = static_cast<const ST*>(a.beta)[static_cast<size_t>(ts + min(tid, last)) * H + h];
+            if (tid > last) pb = elem{};
+        }
+    };
+
+    // interval 1: decay prefix (in log2 units) and the decayed, split K / Q planes
+    auto produce_decay = [&](Buf& B, int chunk) {
+        float gr[TPG][4];
+#pragma unroll
+        for (int i = 0; i < TPG; ++i)
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch)
+                gr[i][ch] = R::get(pg[i], ch) * kLog2e + (i ? gr[i - 1][ch] : 0.f);
+        float off[4], bm[4], bn[4];
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch) {
+            // inclusive prefix over the wave's 8 token groups (lanes 8 apart)
+            float incl = gr[TPG - 1][ch];
+#pragma unroll
+            for (int dd = 8; dd < 64; dd <<= 1) {
+                const float y = __shfl_up(incl, dd);
+                incl += l >= dd ? y : 0.f;
+            }
+            off[ch] = incl - gr[TPG - 1][ch];
+            bm[ch] = __shfl(incl, 24 + (l & 7));   // through token C/2 - 1
+            bn[ch] = __shfl(incl, 56 + (l & 7));   // through the chunk's last token
+            enm[ch] = exp2f_hw(bn[ch] - bm[ch]);
+        }
+#pragma unroll
+        for (int i = 0; i < TPG; ++i) {
+            const int r = tg * TPG + i;
+            u16 kh[4], kl[4], th[4], tl[4], qh[4], ql[4];
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) {
+                const float b = gr[i][ch] + off[ch] - bm[ch];   // b_r - b_m
+                const float em = exp2f_hw(b);
+                const float ei = exp2f_hw(-b);
+                const float kv = R::get(pk[i], ch);
+                split2(kv * em, kh[ch], kl[ch]);
+                ktk[i][ch] = kv * ei;
+                split2(ktk[i][ch], th[ch], tl[ch]);
+                if constexpr (MODE == 0) split2(R::get(pq[i], ch) * em, qh[ch], ql[ch]);
+            }
+            const int idx = r * PK + kperm(c4);
+            store4(&B.kb[0][idx], kh);
+            store4(&B.kb[1][idx], kl);
+            store4(&B.kt[0][idx], th);
+            store4(&B.kt[1][idx], tl);
+            if constexpr (MODE == 0) {
+                store4(&B.qb[0][idx], qh);
+                store4(&B.qb[1][idx], ql);
+            }
+        }
+        if (tg == 0) {
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) {
+                B.em[c4 + ch] = exp2f_hw(bm[ch]);
+                B.gam[c4 + ch] = exp2f_hw(bn[ch]);
+            }
+        }
+        if (tid < C) B.beta[tid] = IN::to_f32(pb);
+        if (chunk + 1 < c_end) fetch(chunk + 1);
+    };
+
+    // interval 2: tiles of A^T and P^T.  Job (rt, ct), ct <= rt, computes Ktil_m[ct] against
+    // Kbar_m[rt] (and Qbar_m[rt]): the accumulator of lane (g4, lr) then holds row 16 rt + lr,
+    // columns 16 ct + 4 g4 + e, so each lane stores 4 consecutive entries of one row.
+    auto produce_products = [&](Buf& B) {
+#pragma unroll
+      for (int job = w; job < K::NJOB; job += NPW) {
+        const int rt = job == 0 ? 0 : 1, ct = job == 2 ? 1 : 0;
+        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int ao = (16 * ct + lr) * PK + 32 * ks + 8 * g4;
+            const int bo = (16 * rt + lr) * PK + 32 * ks + 8 * g4;
+            const bf16x8 th = frag(&B.kt[0][ao]), tl = frag(&B.kt[1][ao]);
+            accA = mfma3(th, tl, frag(&B.kb[0][bo]), frag(&B.kb[1][bo]), accA);
+            if constexpr (MODE == 0) accP = mfma3(th, tl, frag(&B.qb[0][bo]), frag(&B.qb[1][bo]), accP);
+        }
+        const int row = 16 * rt + lr;
+        const float br = B.beta[row];
+        if (rt == ct) {
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = 4 * g4 + e < lr ? accA[e] * br : 0.f;
+            *reinterpret_cast<f32x4*>(&sm.a[rt][lr][4 * g4]) = v;
+        } else {
+            u16 hi[4], lo[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) split2(-accA[e] * br, hi[e], lo[e]);
+            const int idx = row * K::AP + 16 * ct + 4 * g4;
+            store4(&B.aoff[0][idx], hi);
+            store4(&B.aoff[1][idx], lo);
+        }
+        if constexpr (MODE == 0) {
+            u16 hi[4], lo[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) split2((rt > ct || 4 * g4 + e <= lr) ? accP[e] : 0.f, hi[e], lo[e]);
+            const int idx = row * PT + 8 * g4 + 4 * ct;   // kperm(16 ct + 4 g4 + e) = 8 g4 + 4 ct + e
+            store4(&B.p[0][idx], hi);
+            store4(&B.p[1][idx], lo);
+        }
+      }
+    };
+
+    // interval 3: Khat^T over Ktil_m (read by the products) and X_bb = (I + A_bb)^{-1}
+    auto produce_inverse = [&](Buf& B) {
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch) {
+            const int c = c4 + ch;
+#pragma unroll
+            for (int gq = 0; gq < TPG / 4; ++gq) {
+                u16 hi[4], lo[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) split2(ktk[4 * gq + j][ch] * enm[ch], hi[j], lo[j]);
+                const int idx = c * PT + kperm(tg * TPG + 4 * gq);
+                store4(&B.kt[0][idx], hi);
+                store4(&B.kt[1][idx], lo);
+            }
+        }
+        if (w == NPW - 1 && l < 32) {
+            // Row i of X solves x^T (I + A) = e_i^T: with A strictly lower triangular,
+            // x_j = [j == i] - sum_{k > j} x_k A_kj, taken for k = 15 .. 1.
+            const int blk = l >> 4;
+            int i = l & 15;
+            asm volatile("" : "+v"(i));   // keep the unit-vector set-up inside the loop
+            float y[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) y[j] = j == i ? 1.f : 0.f;
+#pragma unroll
+            for (int k = 15; k >= 1; --k)
+#pragma unroll
+                for (int j = 0; j < k; ++j) y[j] -= y[k] * sm.a[blk][k][j];
+            uint32_t hw[8], lw[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                u16 h0, l0, h1, l1;
+                split2(y[2 * j], h0, l0);
+                split2(y[2 * j + 1], h1, l1);
+                hw[j] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
+                lw[j] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
+            }
+            uint4* dh = reinterpret_cast<uint4*>(&B.xd[0][(16 * blk + i) * K::XP]);
+            uint4* dl = reinterpret_cast<uint4*>(&B.xd[1][(16 * blk + i) * K::XP]);
+            dh[0] = uint4{hw[0], hw[1], hw[2], hw[3]};
+            dh[1] = uint4{hw[4], hw[5], hw[6], hw[7]};
+            dl[0] = uint4{lw[0], lw[1], lw[2], lw[3]};
+            dl[1] = uint4{lw[4], lw[5], lw[6], lw[7]};
+        }
+    };
+
+    // ================================================================ consumer state
+    f32x4 S[RT][CT];
+    if (!producer) {
+        const float* src = nullptr;
+        if constexpr (MODE == 0) {
+            if (s == 0) src = a.S0 ? a.S0 + ubase : nullptr;
+            else src = a.se + (static_cast<size_t>(s - 1) * a.NH + unit) * D * D;
+        }
+        if (src) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        S[rt][ct][e] = src[(16 * rt + 4 * g4 + e) * D + j0 + 16 * ct + lr];
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        S[rt][ct][e] = (is_phi && 16 * rt + 4 * g4 + e == j0 + 16 * ct + lr) ? 1.f : 0.f;
+        }
+    }
+    f32x4 Y[NRT][CT], Z[NRT][CT];
+    elem pv[NRT][CT][4];
+    bf16x8 ubh[CT], ubl[CT];
+
+    // interval 1: V loads, Y = Kbar S and Z = Qbar S.  The B operands are Diag(e^{b_m}) S
+    // (e^{b_m} completes Kbar_m / Qbar_m to Kbar / Qbar), split per 32-deep step.
+    auto consume_project = [&](const Buf& B, int chunk) {
+        const long ts = t0 + static_cast<long>(chunk) * C;
+        const int last = static_cast<int>(min(static_cast<long>(C), t1 - ts)) - 1;
+        if (!is_phi) {
+            const ST* vp = static_cast<const ST*>(a.v) + (static_cast<size_t>(ts) * H + h) * D + j0 + lr;
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        pv[rt][ct][e] = vp[static_cast<unsigned>(min(16 * rt + 4 * g4 + e, last) * HD + 16 * ct)];
+        }
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) Y[rt][ct] = Z[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const f32x4 e0 = *reinterpret_cast<const f32x4*>(&B.em[32 * ks + 4 * g4]);
+            const f32x4 e1 = *reinterpret_cast<const f32x4*>(&B.em[32 * ks + 16 + 4 * g4]);
+            bf16x8 sbh[CT], sbl[CT];
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) split_b(S[2 * ks][ct] * e0, S[2 * ks + 1][ct] * e1, sbh[ct], sbl[ct]);
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) {
+                const int ao = (16 * rt + lr) * PK + 32 * ks + 8 * g4;
+                const bf16x8 kh = frag(&B.kb[0][ao]), kl = frag(&B.kb[1][ao]);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) Y[rt][ct] = mfma3(kh, kl, sbh[ct], sbl[ct], Y[rt][ct]);
+                if constexpr (MODE == 0) {
+                    const bf16x8 qh = frag(&B.qb[0][ao]), ql = frag(&B.qb[1][ao]);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) Z[rt][ct] = mfma3(qh, ql, sbh[ct], sbl[ct], Z[rt][ct]);
+                }
+            }
+        }
+    };
+
+    // interval 2: Unew = (I + A)^{-1} Diag(beta) (V - Kbar S) one 16-token block at a time,
+    //   Unew_b = X_bb (beta_b (V - Kbar S)_b - sum_{k<b} A_bk Unew_k),
+    // then O = Z + P Unew.
+    auto consume_solve = [&](const Buf& B, int chunk) {
+        const long ts = t0 + static_cast<long>(chunk) * C;
+        const int ntok = static_cast<int>(min(static_cast<long>(C), t1 - ts));
+        bf16x4 uh[NRT][CT], ul[NRT][CT];
+#pragma unroll
+        for (int b = 0; b < NRT; ++b) {
+            const f32x4 bb = *reinterpret_cast<const f32x4*>(&B.beta[16 * b + 4 * g4]);
+            f32x4 acc[CT];
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float vv = is_phi ? 0.f : IN::to_f32(pv[b][ct][e]);
+                    acc[ct][e] = bb[e] * (vv - Y[b][ct][e]);
+                }
+#pragma unroll
+            for (int k = 0; k < b; ++k) {
+                const int ao = (16 * b + lr) * K::AP + 16 * k + 4 * g4;
+                const bf16x4 ah = frag4(&B.aoff[0][ao]), al = frag4(&B.aoff[1][ao]);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) acc[ct] = mfma3_16(ah, al, uh[k][ct], ul[k][ct], acc[ct]);
+            }
+            const int xo = (16 * b + lr) * K::XP + 4 * g4;
+            const bf16x4 xh = frag4(&B.xd[0][xo]), xl = frag4(&B.xd[1][xo]);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                bf16x4 bh, bl;
+                split4(acc[ct], bh, bl);
+                const f32x4 u = mfma3_16(xh, xl, bh, bl, f32x4{0.f, 0.f, 0.f, 0.f});
+                split4(u, uh[b][ct], ul[b][ct]);
+            }
+        }
+        // 32-deep B operands of Unew: two stacked tiles in kperm order
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            ubh[ct] = cat8(uh[0][ct], uh[1][ct]);
+            ubl[ct] = cat8(ul[0][ct], ul[1][ct]);
+        }
+        if constexpr (MODE == 0) {
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) {
+                const int ao = (16 * rt + lr) * PT + 8 * g4;
+                const bf16x8 ph = frag(&B.p[0][ao]), pl = frag(&B.p[1][ao]);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) Z[rt][ct] = mfma3(ph, pl, ubh[ct], ubl[ct], Z[rt][ct]);
+            }
+            const bool full = ntok == C;   // uniform: only a sequence's last chunk can be ragged
+            const size_t obase = (static_cast<size_t>(ts) * H + h) * D + j0 + lr;
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int row = 16 * rt + 4 * g4 + e;
+                        if (full || row < ntok)
+                            store_out<OUT_BF16>(a.o, obase + static_cast<unsigned>(row * HD + 16 * ct), Z[rt][ct][e]);
+                    }
+        }
+    };
+
+    // interval 3: S <- Diag(gamma) S + Khat^T Unew
+    auto consume_update = [&](const Buf& B) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const f32x4 gm = *reinterpret_cast<const f32x4*>(&B.gam[16 * rt + 4 * g4]);
+            const int ao = (16 * rt + lr) * PT + 8 * g4;
+            const bf16x8 kh = frag(&B.kt[0][ao]), kl = frag(&B.kt[1][ao]);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) S[rt][ct] = mfma3(kh, kl, ubh[ct], ubl[ct], S[rt][ct] * gm);
+        }
+    };
+
+    // ================================================================ chunk loops
+    // Producer and consumer waves run separate loops that pass the same number of
+    // workgroup barriers: three for the first chunk's operands, then three per chunk.
+    if (producer) {
+        if (c_begin < c_end) {
+            fetch(c_begin);
+            produce_decay(sm.buf[c_begin & 1], c_begin);
+            lds_barrier();
+            produce_products(sm.buf[c_begin & 1]);
+            lds_barrier();
+            produce_inverse(sm.buf[c_begin & 1]);
+            lds_barrier();
+        }
+        for (int chunk = c_begin; chunk < c_end; ++chunk) {
+            Buf& nxt = sm.buf[(chunk & 1) ^ 1];
+            const bool more = chunk + 1 < c_end;
+            if (more) produce_decay(nxt, chunk + 1);
+            lds_barrier();
+            if (more) produce_products(nxt);
+            lds_barrier();
+            if (more) produce_inverse(nxt);
+            lds_barrier();
+        }
+        return;
+    }
+    if (c_begin < c_end) {
+        lds_barrier();
+        lds_barrier();
+        lds_barrier();
+    }
+    for (int chunk = c_begin; chunk < c_end; ++chunk) {
+        const Buf& cur = sm.buf[chunk & 1];
+        consume_project(cur, chunk);
+        lds_barrier();
+        consume_solve(cur, chunk);
+        lds_barrier();
+        consume_update(cur);
+        lds_barrier();
+    }
+
+    // ---------------------------------------------------------------- exit state
+    float* dst = nullptr;
+    if constexpr (MODE == 0) {
+        if ((a.cu || s == a.G - 1) && a.S_final) dst = a.S_final + ubase;
+    } else {
+        dst = (is_phi ? a.phi : a.sloc) + (static_cast<size_t>(s) * a.NH + unit) * D * D;
+    }
+    if (dst) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     dst[(16 * rt + 4 * g4 + e) * D + j0 + 16 * ct + lr] = S[rt][ct][e];
@@ -714,19 +1240,33 @@ hipError_t launch_variant(const PrefillArgs& pa, const PrefillPlan& plan, hipStr
     a.sloc = plan.G > 1 ? reinterpret_cast<float*>(ws + plan.off_sloc) : nullptr;
     a.se = plan.G > 1 ? reinterpret_cast<float*>(ws + plan.off_se) : nullptr;
     const int NH = a.NH;
+    // The 32-token chunk runs the producer/consumer kernel; the 64-token chunk, whose
+    // operands do not fit twice in LDS, the single-buffered one.
+    auto pass = [&](int mode, int grid) {
+        if constexpr (C == 32) {
+            if (mode == 0)
+                hipLaunchKernelGGL((pipe_kernel<D, IN, OB, 0>), dim3(grid), dim3(PCfg<D, 0>::NT), 0, stream, a);
+            else
+                hipLaunchKernelGGL((pipe_kernel<D, IN, OB, 1>), dim3(grid), dim3(PCfg<D, 1>::NT), 0, stream, a);
+        } else {
+            if (mode == 0)
+                hipLaunchKernelGGL((chunk_kernel<D, C, IN, OB, 0>), dim3(grid), dim3(Cfg<D, C, 0>::NT), 0, stream, a);
+            else
+                hipLaunchKernelGGL((chunk_kernel<D, C, IN, OB, 1>), dim3(grid), dim3(Cfg<D, C, 1>::NT), 0, stream, a);
+        }
+    };
     if (pa.cu) {
         hipLaunchKernelGGL(order_kernel, dim3((pa.N + 255) / 256), dim3(256), 0, stream, pa.cu,
                            reinterpret_cast<int32_t*>(ws + plan.off_order), pa.N);
-        hipLaunchKernelGGL((chunk_kernel<D, C, IN, OB, 0>), dim3(NH), dim3(Cfg<D, C, 0>::NT), 0, stream, a);
+        pass(0, NH);
         return hipGetLastError();
     }
     if (plan.G > 1) {
-        hipLaunchKernelGGL((chunk_kernel<D, C, IN, OB, 1>), dim3(NH * (plan.G - 1)), dim3(Cfg<D, C, 1>::NT), 0,
-                           stream, a);
+        pass(1, NH * (plan.G - 1));
         hipLaunchKernelGGL(combine_kernel<D>, dim3(NH, D / 16), dim3(256), 0, stream, pa.S0, a.phi, a.sloc, a.se,
                            NH, plan.G);
     }
-    hipLaunchKernelGGL((chunk_kernel<D, C, IN, OB, 0>), dim3(NH * plan.G), dim3(Cfg<D, C, 0>::NT), 0, stream, a);
+    pass(0, NH * plan.G);
     return hipGetLastError();
 }
 
@@ -746,8 +1286,8 @@ PrefillPlan plan_prefill(int B, int T, int H, int D, int N, bool varlen, int chu
     (void)B;
     p.chunks = (T + p.chunk - 1) / p.chunk;
     const long units = static_cast<long>(N) * H;
-    // workgroups that fill the chip: one per compute unit, two at the 32-token chunk
-    const long target = static_cast<long>(kComputeUnits) * (p.chunk == 32 ? 2 : 1);
+    // workgroups that fill the chip: one per compute unit
+    const long target = static_cast<long>(kComputeUnits);
     int G = 1;
     if (units > 0 && units < target && p.chunks >= 2 * kMinChunksPerSegment) {
         G = static_cast<int>((target + units - 1) / units);

@@ -48,10 +48,9 @@ def test_status_strings(lib):
 
 def test_workspace_query_plans(lib):
     q = kda.kda_chunk_fwd_workspace_bytes
-    # long context, 32 heads: 2048 chunks of 32 tokens cut into 16 segments (two workgroups
-    # per compute unit at the 32-token chunk), or 1024 chunks of 64 cut into 8 (one per
-    # compute unit) -> 3 matrices per unit and segment gap
-    assert q(1, 65536, 32, 128, 128, 1, False) == 3 * 32 * 15 * 128 * 128 * 4
+    # long context, 32 heads: 2048 chunks of 32 tokens or 1024 chunks of 64, cut into 8
+    # segments (one workgroup per compute unit) -> 3 matrices per unit and segment gap
+    assert q(1, 65536, 32, 128, 128, 1, False) == 3 * 32 * 7 * 128 * 128 * 4
     assert q(1, 65536, 32, 128, 128, 1, False, chunk=64) == 3 * 32 * 7 * 128 * 128 * 4
     # enough units to fill the chip: single pass, no workspace
     assert q(64, 4096, 32, 128, 128, 64, False) == 0
