@@ -19,18 +19,10 @@ struct BF16 {
     }
 };
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return static_cast<uint16_t>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
-}
-
-// Output stores: fp32 or bf16 (RNE).
+// Output stores: fp32 or bf16 (round to nearest even, the hardware conversion of gfx950).
 template <bool OUT_BF16>
 __device__ __forceinline__ void store_out(void* base, size_t idx, float x) {
-    if constexpr (OUT_BF16) static_cast<uint16_t*>(base)[idx] = f32_to_bf16_rne(x);
+    if constexpr (OUT_BF16) static_cast<__bf16*>(base)[idx] = static_cast<__bf16>(x);
     else static_cast<float*>(base)[idx] = x;
 }
 

@@ -71,6 +71,27 @@ constexpr float kLog2e = 1.4426950408889634f;
 // 2^x on the hardware exp2 unit (v_exp_f32)
 __device__ __forceinline__ float exp2f_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Two values at once: hi = bf16(x) packed in one word, lo = bf16(x - hi) packed in another
+// (one v_cvt_pk_bf16_f32 per word).
+__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+    const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
+    const float r0 = x0 - __uint_as_float(h << 16);
+    const float r1 = x1 - __uint_as_float(h & 0xffff0000u);
+    hi = h;
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
+}
+
+// Four values -> packed hi and lo words (8 bytes each).
+__device__ __forceinline__ void split_quad(float x0, float x1, float x2, float x3, uint2& hi, uint2& lo) {
+    split_pair(x0, x1, hi.x, lo.x);
+    split_pair(x2, x3, hi.y, lo.y);
+}
+
 __device__ __forceinline__ void split2(float x, u16& hi, u16& lo) {
     const __bf16 h = static_cast<__bf16>(x);
     hi = bits(h);
@@ -102,15 +123,26 @@ __device__ __forceinline__ f32x4 mfma3_16(bf16x4 ah, bf16x4 al, bf16x4 bh, bf16x
     return mfma16(ah, bh, c);
 }
 __device__ __forceinline__ void split4(f32x4 t, bf16x4& hi, bf16x4& lo) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const __bf16 h = static_cast<__bf16>(t[e]);
-        hi[e] = h;
-        lo[e] = static_cast<__bf16>(t[e] - static_cast<float>(h));
-    }
+    uint32_t h0, h1, l0, l1;
+    split_pair(t[0], t[1], h0, l0);
+    split_pair(t[2], t[3], h1, l1);
+    hi = __builtin_bit_cast(bf16x4, u32x2{h0, h1});
+    lo = __builtin_bit_cast(bf16x4, u32x2{l0, l1});
 }
 __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
     return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Four consecutive outputs (16-byte fp32 or 8-byte bf16 store; bf16 rounds to nearest even).
+template <bool OUT_BF16>
+__device__ __forceinline__ void store_out4(void* base, size_t idx, f32x4 x) {
+    if constexpr (OUT_BF16) {
+        const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x[0], x[1]}, bf16x2));
+        const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x[2], x[3]}, bf16x2));
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + idx) = uint2{w0, w1};
+    } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(base) + idx) = x;
+    }
 }
 
 // Workgroup barrier for LDS traffic only.  The waves of a workgroup exchange data
@@ -128,15 +160,13 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // Two stacked accumulator tiles -> hi/lo B operands of one 32-deep step.
 __device__ __forceinline__ void split_b(f32x4 t0, f32x4 t1, bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const __bf16 h0 = static_cast<__bf16>(t0[e]);
-        const __bf16 h1 = static_cast<__bf16>(t1[e]);
-        hi[e] = h0;
-        hi[4 + e] = h1;
-        lo[e] = static_cast<__bf16>(t0[e] - static_cast<float>(h0));
-        lo[4 + e] = static_cast<__bf16>(t1[e] - static_cast<float>(h1));
-    }
+    uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+    split_pair(t0[0], t0[1], h0, l0);
+    split_pair(t0[2], t0[3], h1, l1);
+    split_pair(t1[0], t1[1], h2, l2);
+    split_pair(t1[2], t1[3], h3, l3);
+    hi = __builtin_bit_cast(bf16x8, u32x4{h0, h1, h2, h3});
+    lo = __builtin_bit_cast(bf16x8, u32x4{l0, l1, l2, l3});
 }
 
 __device__ __forceinline__ void store4(u16* p, const u16 (&x)[4]) {
@@ -683,6 +713,22 @@ void chunk_kernel(KernelArgs a) {
     }
 }
 
+// Value of lane K of this lane's 16-lane row (DPP row broadcast).
+template <int K>
+__device__ __forceinline__ float row_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + K, 0xf, 0xf, true));
+}
+
+// Right-looking elimination steps K, K-1, .., 1 of x^T (I + A) = e_i^T for a strictly lower
+// triangular 16 x 16 A whose row k sits in lane k of the 16-lane row (ar = this lane's row).
+template <int K>
+__device__ __forceinline__ void unit_lower_solve(float (&y)[16], const float (&ar)[16]) {
+    const float nk = -y[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) y[j] = __builtin_fmaf(row_bcast<K>(ar[j]), nk, y[j]);
+    if constexpr (K > 1) unit_lower_solve<K - 1>(y, ar);
+}
+
 // ------------------------------------------------------------------ pipelined kernel (C = 32)
 // The operands of a chunk depend only on that chunk's inputs, never on the state, so
 // they are built one chunk ahead.  Producer waves (one per SIMD) build chunk c+1's
@@ -785,10 +831,10 @@ void pipe_kernel(KernelArgs a) {
     const size_t ubase = static_cast<size_t>(unit) * D * D;
     const int HD = H * D;   // elements between consecutive tokens of one head
 
-    // consumer identity: 32 state columns starting at j0 (of S, or of Phi in the summary pass)
+    // consumer identity: 16 CT state columns starting at j0 (of S, or of Phi in the summary pass)
     const int ci = producer ? 0 : w - NPW;
-    const bool is_phi = MODE == 1 && ci >= D / 32;
-    const int j0 = 32 * (ci % (D / 32));
+    const bool is_phi = MODE == 1 && ci >= D / (16 * CT);
+    const int j0 = 16 * CT * (ci % (D / (16 * CT)));
     // producer identity: channel quad cq, token group tg (TPG tokens)
     const int cq = 8 * w + (l & 7), tg = l >> 3, c4 = 4 * cq;
 
@@ -812,6 +858,8 @@ void pipe_kernel(KernelArgs a) {
         const ST* kp = static_cast<const ST*>(a.k) + base;
         const ST* gp = static_cast<const ST*>(a.g) + base;
         const ST* qp = static_cast<const ST*>(a.q) + base;
+        // Rows past a ragged end load a valid row here and are zeroed where they are used:
+        // touching a loaded value now would make the wave wait for the loads.
 #pragma unroll
         for (int i = 0; i < TPG; ++i) {
             const unsigned off = static_cast<unsigned>(min(tg * TPG + i, last) * HD + c4);
@@ -819,19 +867,19 @@ void pipe_kernel(KernelArgs a) {
             pg[i] = *reinterpret_cast<const quad*>(gp + off);
             if constexpr (MODE == 0) pq[i] = *reinterpret_cast<const quad*>(qp + off);
         }
-        if (last < C - 1) {   // ragged last chunk: padded rows read as zero
-#pragma unroll
-            for (int i = 0; i < TPG; ++i)
-                if (tg * TPG + i > last) pk[i] = pg[i] = pq[i] = quad{};
-        }
-        if (tid < C) {
-            pb = static_cast<const ST*>(a.beta)[static_cast<size_t>(ts + min(tid, last)) * H + h];
-            if (tid > last) pb = elem{};
-        }
+        if (tid < C) pb = static_cast<const ST*>(a.beta)[static_cast<size_t>(ts + min(tid, last)) * H + h];
     };
 
     // interval 1: decay prefix (in log2 units) and the decayed, split K / Q planes
     auto produce_decay = [&](Buf& B, int chunk) {
+        const long ts = t0 + static_cast<long>(chunk) * C;
+        const int last = static_cast<int>(min(static_cast<long>(C), t1 - ts)) - 1;
+        if (last < C - 1) {   // ragged last chunk: padded rows read as zero
+#pragma unroll
+            for (int i = 0; i < TPG; ++i)
+                if (tg * TPG + i > last) pk[i] = pg[i] = pq[i] = quad{};
+            if (tid > last) pb = elem{};
+        }
         float gr[TPG][4];
 #pragma unroll
         for (int i = 0; i < TPG; ++i)
@@ -852,30 +900,34 @@ void pipe_kernel(KernelArgs a) {
             bm[ch] = __shfl(incl, 24 + (l & 7));   // through token C/2 - 1
             bn[ch] = __shfl(incl, 56 + (l & 7));   // through the chunk's last token
             enm[ch] = exp2f_hw(bn[ch] - bm[ch]);
+            off[ch] -= bm[ch];                     // b_r - b_m = gr + off
         }
 #pragma unroll
         for (int i = 0; i < TPG; ++i) {
             const int r = tg * TPG + i;
-            u16 kh[4], kl[4], th[4], tl[4], qh[4], ql[4];
+            float kb[4], qb[4];
 #pragma unroll
             for (int ch = 0; ch < 4; ++ch) {
-                const float b = gr[i][ch] + off[ch] - bm[ch];   // b_r - b_m
+                const float b = gr[i][ch] + off[ch];   // b_r - b_m
                 const float em = exp2f_hw(b);
                 const float ei = exp2f_hw(-b);
                 const float kv = R::get(pk[i], ch);
-                split2(kv * em, kh[ch], kl[ch]);
+                kb[ch] = kv * em;
                 ktk[i][ch] = kv * ei;
-                split2(ktk[i][ch], th[ch], tl[ch]);
-                if constexpr (MODE == 0) split2(R::get(pq[i], ch) * em, qh[ch], ql[ch]);
+                if constexpr (MODE == 0) qb[ch] = R::get(pq[i], ch) * em;
             }
             const int idx = r * PK + kperm(c4);
-            store4(&B.kb[0][idx], kh);
-            store4(&B.kb[1][idx], kl);
-            store4(&B.kt[0][idx], th);
-            store4(&B.kt[1][idx], tl);
+            uint2 hi, lo;
+            split_quad(kb[0], kb[1], kb[2], kb[3], hi, lo);
+            *reinterpret_cast<uint2*>(&B.kb[0][idx]) = hi;
+            *reinterpret_cast<uint2*>(&B.kb[1][idx]) = lo;
+            split_quad(ktk[i][0], ktk[i][1], ktk[i][2], ktk[i][3], hi, lo);
+            *reinterpret_cast<uint2*>(&B.kt[0][idx]) = hi;
+            *reinterpret_cast<uint2*>(&B.kt[1][idx]) = lo;
             if constexpr (MODE == 0) {
-                store4(&B.qb[0][idx], qh);
-                store4(&B.qb[1][idx], ql);
+                split_quad(qb[0], qb[1], qb[2], qb[3], hi, lo);
+                *reinterpret_cast<uint2*>(&B.qb[0][idx]) = hi;
+                *reinterpret_cast<uint2*>(&B.qb[1][idx]) = lo;
             }
         }
         if (tg == 0) {
@@ -893,7 +945,6 @@ void pipe_kernel(KernelArgs a) {
     // Kbar_m[rt] (and Qbar_m[rt]): the accumulator of lane (g4, lr) then holds row 16 rt + lr,
     // columns 16 ct + 4 g4 + e, so each lane stores 4 consecutive entries of one row.
     auto produce_products = [&](Buf& B) {
-#pragma unroll
       for (int job = w; job < K::NJOB; job += NPW) {
         const int rt = job == 0 ? 0 : 1, ct = job == 2 ? 1 : 0;
         f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
@@ -913,20 +964,21 @@ void pipe_kernel(KernelArgs a) {
             for (int e = 0; e < 4; ++e) v[e] = 4 * g4 + e < lr ? accA[e] * br : 0.f;
             *reinterpret_cast<f32x4*>(&sm.a[rt][lr][4 * g4]) = v;
         } else {
-            u16 hi[4], lo[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) split2(-accA[e] * br, hi[e], lo[e]);
+            uint2 hi, lo;
+            split_quad(-accA[0] * br, -accA[1] * br, -accA[2] * br, -accA[3] * br, hi, lo);
             const int idx = row * K::AP + 16 * ct + 4 * g4;
-            store4(&B.aoff[0][idx], hi);
-            store4(&B.aoff[1][idx], lo);
+            *reinterpret_cast<uint2*>(&B.aoff[0][idx]) = hi;
+            *reinterpret_cast<uint2*>(&B.aoff[1][idx]) = lo;
         }
         if constexpr (MODE == 0) {
-            u16 hi[4], lo[4];
+            f32x4 pv4;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) split2((rt > ct || 4 * g4 + e <= lr) ? accP[e] : 0.f, hi[e], lo[e]);
+            for (int e = 0; e < 4; ++e) pv4[e] = (rt > ct || 4 * g4 + e <= lr) ? accP[e] : 0.f;
+            uint2 hi, lo;
+            split_quad(pv4[0], pv4[1], pv4[2], pv4[3], hi, lo);
             const int idx = row * PT + 8 * g4 + 4 * ct;   // kperm(16 ct + 4 g4 + e) = 8 g4 + 4 ct + e
-            store4(&B.p[0][idx], hi);
-            store4(&B.p[1][idx], lo);
+            *reinterpret_cast<uint2*>(&B.p[0][idx]) = hi;
+            *reinterpret_cast<uint2*>(&B.p[1][idx]) = lo;
         }
       }
     };
@@ -938,36 +990,34 @@ void pipe_kernel(KernelArgs a) {
             const int c = c4 + ch;
 #pragma unroll
             for (int gq = 0; gq < TPG / 4; ++gq) {
-                u16 hi[4], lo[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) split2(ktk[4 * gq + j][ch] * enm[ch], hi[j], lo[j]);
+                uint2 hi, lo;
+                split_quad(ktk[4 * gq][ch] * enm[ch], ktk[4 * gq + 1][ch] * enm[ch], ktk[4 * gq + 2][ch] * enm[ch],
+                           ktk[4 * gq + 3][ch] * enm[ch], hi, lo);
                 const int idx = c * PT + kperm(tg * TPG + 4 * gq);
-                store4(&B.kt[0][idx], hi);
-                store4(&B.kt[1][idx], lo);
+                *reinterpret_cast<uint2*>(&B.kt[0][idx]) = hi;
+                *reinterpret_cast<uint2*>(&B.kt[1][idx]) = lo;
             }
         }
         if (w == NPW - 1 && l < 32) {
-            // Row i of X solves x^T (I + A) = e_i^T: with A strictly lower triangular,
-            // x_j = [j == i] - sum_{k > j} x_k A_kj, taken for k = 15 .. 1.
+            // Lane (blk, i) solves row i of X: x^T (I + A) = e_i^T, i.e. with A strictly lower
+            // triangular x_j = [j == i] - sum_{k > j} x_k A_kj, taken for k = 15 .. 1.  The lane
+            // keeps row i of A_bb in registers; A_kj comes from lane k of the same 16-lane row.
             const int blk = l >> 4;
             int i = l & 15;
             asm volatile("" : "+v"(i));   // keep the unit-vector set-up inside the loop
-            float y[16];
+            float ar[16], y[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(&sm.a[blk][i][4 * q]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ar[4 * q + e] = v[e];
+            }
 #pragma unroll
             for (int j = 0; j < 16; ++j) y[j] = j == i ? 1.f : 0.f;
-#pragma unroll
-            for (int k = 15; k >= 1; --k)
-#pragma unroll
-                for (int j = 0; j < k; ++j) y[j] -= y[k] * sm.a[blk][k][j];
+            unit_lower_solve<15>(y, ar);
             uint32_t hw[8], lw[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                u16 h0, l0, h1, l1;
-                split2(y[2 * j], h0, l0);
-                split2(y[2 * j + 1], h1, l1);
-                hw[j] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
-                lw[j] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
-            }
+            for (int j = 0; j < 8; ++j) split_pair(y[2 * j], y[2 * j + 1], hw[j], lw[j]);
             uint4* dh = reinterpret_cast<uint4*>(&B.xd[0][(16 * blk + i) * K::XP]);
             uint4* dl = reinterpret_cast<uint4*>(&B.xd[1][(16 * blk + i) * K::XP]);
             dh[0] = uint4{hw[0], hw[1], hw[2], hw[3]};
@@ -1040,9 +1090,11 @@ void pipe_kernel(KernelArgs a) {
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) Y[rt][ct] = mfma3(kh, kl, sbh[ct], sbl[ct], Y[rt][ct]);
                 if constexpr (MODE == 0) {
+                    // Z^T = (Diag(e^{b_m}) S)^T Qbar_m^T: the split state serves as the A operand,
+                    // so lane (g4, lr) ends up with token 16 rt + lr, columns 16 ct + 4 g4 + e
                     const bf16x8 qh = frag(&B.qb[0][ao]), ql = frag(&B.qb[1][ao]);
 #pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) Z[rt][ct] = mfma3(qh, ql, sbh[ct], sbl[ct], Z[rt][ct]);
+                    for (int ct = 0; ct < CT; ++ct) Z[rt][ct] = mfma3(sbh[ct], sbl[ct], qh, ql, Z[rt][ct]);
                 }
             }
         }
@@ -1050,10 +1102,8 @@ void pipe_kernel(KernelArgs a) {
 
     // interval 2: Unew = (I + A)^{-1} Diag(beta) (V - Kbar S) one 16-token block at a time,
     //   Unew_b = X_bb (beta_b (V - Kbar S)_b - sum_{k<b} A_bk Unew_k),
-    // then O = Z + P Unew.
-    auto consume_solve = [&](const Buf& B, int chunk) {
-        const long ts = t0 + static_cast<long>(chunk) * C;
-        const int ntok = static_cast<int>(min(static_cast<long>(C), t1 - ts));
+    // then O = Z + P Unew (stored in interval 3).
+    auto consume_solve = [&](const Buf& B) {
         bf16x4 uh[NRT][CT], ul[NRT][CT];
 #pragma unroll
         for (int b = 0; b < NRT; ++b) {
@@ -1090,30 +1140,19 @@ void pipe_kernel(KernelArgs a) {
             ubl[ct] = cat8(ul[0][ct], ul[1][ct]);
         }
         if constexpr (MODE == 0) {
+            // O^T = Z^T + Unew^T P^T
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt) {
                 const int ao = (16 * rt + lr) * PT + 8 * g4;
                 const bf16x8 ph = frag(&B.p[0][ao]), pl = frag(&B.p[1][ao]);
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct) Z[rt][ct] = mfma3(ph, pl, ubh[ct], ubl[ct], Z[rt][ct]);
+                for (int ct = 0; ct < CT; ++ct) Z[rt][ct] = mfma3(ubh[ct], ubl[ct], ph, pl, Z[rt][ct]);
             }
-            const bool full = ntok == C;   // uniform: only a sequence's last chunk can be ragged
-            const size_t obase = (static_cast<size_t>(ts) * H + h) * D + j0 + lr;
-#pragma unroll
-            for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int row = 16 * rt + 4 * g4 + e;
-                        if (full || row < ntok)
-                            store_out<OUT_BF16>(a.o, obase + static_cast<unsigned>(row * HD + 16 * ct), Z[rt][ct][e]);
-                    }
         }
     };
 
-    // interval 3: S <- Diag(gamma) S + Khat^T Unew
-    auto consume_update = [&](const Buf& B) {
+    // interval 3: S <- Diag(gamma) S + Khat^T Unew, and the output rows of the chunk
+    auto consume_update = [&](const Buf& B, int chunk) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             const f32x4 gm = *reinterpret_cast<const f32x4*>(&B.gam[16 * rt + 4 * g4]);
@@ -1121,6 +1160,21 @@ void pipe_kernel(KernelArgs a) {
             const bf16x8 kh = frag(&B.kt[0][ao]), kl = frag(&B.kt[1][ao]);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) S[rt][ct] = mfma3(kh, kl, ubh[ct], ubl[ct], S[rt][ct] * gm);
+        }
+        if constexpr (MODE == 0) {
+            const long ts = t0 + static_cast<long>(chunk) * C;
+            const int ntok = static_cast<int>(min(static_cast<long>(C), t1 - ts));
+            // lane (g4, lr) holds 4 consecutive columns of token 16 rt + lr
+            const size_t obase = (static_cast<size_t>(ts) * H + h) * D + j0 + 4 * g4;
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) {
+                const int row = 16 * rt + lr;
+                if (row < ntok) {
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct)
+                        store_out4<OUT_BF16>(a.o, obase + static_cast<unsigned>(row * HD + 16 * ct), Z[rt][ct]);
+                }
+            }
         }
     };
 
@@ -1158,9 +1212,9 @@ void pipe_kernel(KernelArgs a) {
         const Buf& cur = sm.buf[chunk & 1];
         consume_project(cur, chunk);
         lds_barrier();
-        consume_solve(cur, chunk);
+        consume_solve(cur);
         lds_barrier();
-        consume_update(cur);
+        consume_update(cur, chunk);
         lds_barrier();
     }
 
