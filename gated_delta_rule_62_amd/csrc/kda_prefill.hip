@@ -740,7 +740,7 @@ __device__ __forceinline__ void unit_lower_solve(float (&y)[16], const float (&a
 //   interval   producer (chunk c+1)                 consumer (chunk c)
 //   1          decay prefix, decayed K/Q splits     Y = Kbar S, Z = Qbar S
 //   2          A and P tiles                        Unew block recurrence, O
-//   3          Khat^T, diagonal-block inverses      S <- Diag(gamma) S + Khat^T Unew
+//   3          Ktil_m^T, diagonal-block inverses    state update, O stores, state split
 template <int D, int MODE>
 struct PCfg {
     static constexpr int C = 32;
@@ -768,13 +768,13 @@ struct alignas(16) PBuf {
     u16 kb[2][K::C * K::PK];    // Kbar_m = K e^{b - b_m}     [token][kperm(channel)]
     u16 qb[NQ][QE];             // Qbar_m = Q e^{b - b_m}     [token][kperm(channel)]
     u16 kt[2][K::KT];           // Ktil_m = K e^{b_m - b} [token][kperm(channel)], then
-                                // Khat^T = (K e^{b_n - b})^T [channel][kperm(token)]
+                                // Ktil_m^T                   [channel][kperm(token)]
     u16 aoff[2][K::C * K::AP];  // -A off the diagonal blocks  [token][token]
     u16 xd[2][K::C * K::XP];    // X_bb = (I + A_bb)^{-1}      [16 b + r][c]
     u16 p[NQ][PE];              // P = Tril(Qbar Ktil^T)       [token][kperm(token)]
     float beta[K::C];
     float em[D];                // e^{b_m}
-    float gam[D];               // gamma = e^{b_n}
+    float rho[D];               // e^{b_m} of the next chunk times e^{b_n - b_m} (1 after the last)
 };
 
 template <int D, int MODE>
@@ -849,8 +849,8 @@ void pipe_kernel(KernelArgs a) {
     // ================================================================ producer state
     quad pk[TPG], pq[TPG], pg[TPG];
     elem pb = 0;
-    float ktk[TPG][4];   // Ktil_m, kept from interval 1 for Khat^T in interval 3
-    float enm[4];        // e^{b_n - b_m}
+    uint2 kth[TPG], ktl[TPG];   // split Ktil_m words, kept from interval 1 for Ktil_m^T in interval 3
+    float enm[4] = {1.f, 1.f, 1.f, 1.f};   // e^{b_n - b_m} of the chunk last produced
     auto fetch = [&](int chunk) {
         const long ts = t0 + static_cast<long>(chunk) * C;
         const int last = static_cast<int>(min(static_cast<long>(C), t1 - ts)) - 1;
@@ -870,8 +870,9 @@ void pipe_kernel(KernelArgs a) {
         if (tid < C) pb = static_cast<const ST*>(a.beta)[static_cast<size_t>(ts + min(tid, last)) * H + h];
     };
 
-    // interval 1: decay prefix (in log2 units) and the decayed, split K / Q planes
-    auto produce_decay = [&](Buf& B, int chunk) {
+    // interval 1: decay prefix (in log2 units) and the decayed, split K / Q planes.  With
+    // the previous chunk's buffer `prev`, also that chunk's state factor rho.
+    auto produce_decay = [&](Buf& B, int chunk, Buf* prev) {
         const long ts = t0 + static_cast<long>(chunk) * C;
         const int last = static_cast<int>(min(static_cast<long>(C), t1 - ts)) - 1;
         if (last < C - 1) {   // ragged last chunk: padded rows read as zero
@@ -899,13 +900,22 @@ void pipe_kernel(KernelArgs a) {
             off[ch] = incl - gr[TPG - 1][ch];
             bm[ch] = __shfl(incl, 24 + (l & 7));   // through token C/2 - 1
             bn[ch] = __shfl(incl, 56 + (l & 7));   // through the chunk's last token
-            enm[ch] = exp2f_hw(bn[ch] - bm[ch]);
             off[ch] -= bm[ch];                     // b_r - b_m = gr + off
         }
+        if (tg == 0) {
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) {
+                const float em = exp2f_hw(bm[ch]);
+                B.em[c4 + ch] = em;
+                if (prev) prev->rho[c4 + ch] = em * enm[ch];
+            }
+        }
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch) enm[ch] = exp2f_hw(bn[ch] - bm[ch]);
 #pragma unroll
         for (int i = 0; i < TPG; ++i) {
             const int r = tg * TPG + i;
-            float kb[4], qb[4];
+            float kb[4], kt[4], qb[4];
 #pragma unroll
             for (int ch = 0; ch < 4; ++ch) {
                 const float b = gr[i][ch] + off[ch];   // b_r - b_m
@@ -913,7 +923,7 @@ void pipe_kernel(KernelArgs a) {
                 const float ei = exp2f_hw(-b);
                 const float kv = R::get(pk[i], ch);
                 kb[ch] = kv * em;
-                ktk[i][ch] = kv * ei;
+                kt[ch] = kv * ei;
                 if constexpr (MODE == 0) qb[ch] = R::get(pq[i], ch) * em;
             }
             const int idx = r * PK + kperm(c4);
@@ -921,20 +931,13 @@ void pipe_kernel(KernelArgs a) {
             split_quad(kb[0], kb[1], kb[2], kb[3], hi, lo);
             *reinterpret_cast<uint2*>(&B.kb[0][idx]) = hi;
             *reinterpret_cast<uint2*>(&B.kb[1][idx]) = lo;
-            split_quad(ktk[i][0], ktk[i][1], ktk[i][2], ktk[i][3], hi, lo);
-            *reinterpret_cast<uint2*>(&B.kt[0][idx]) = hi;
-            *reinterpret_cast<uint2*>(&B.kt[1][idx]) = lo;
+            split_quad(kt[0], kt[1], kt[2], kt[3], kth[i], ktl[i]);
+            *reinterpret_cast<uint2*>(&B.kt[0][idx]) = kth[i];
+            *reinterpret_cast<uint2*>(&B.kt[1][idx]) = ktl[i];
             if constexpr (MODE == 0) {
                 split_quad(qb[0], qb[1], qb[2], qb[3], hi, lo);
                 *reinterpret_cast<uint2*>(&B.qb[0][idx]) = hi;
                 *reinterpret_cast<uint2*>(&B.qb[1][idx]) = lo;
-            }
-        }
-        if (tg == 0) {
-#pragma unroll
-            for (int ch = 0; ch < 4; ++ch) {
-                B.em[c4 + ch] = exp2f_hw(bm[ch]);
-                B.gam[c4 + ch] = exp2f_hw(bn[ch]);
             }
         }
         if (tid < C) B.beta[tid] = IN::to_f32(pb);
@@ -983,17 +986,27 @@ void pipe_kernel(KernelArgs a) {
       }
     };
 
-    // interval 3: Khat^T over Ktil_m (read by the products) and X_bb = (I + A_bb)^{-1}
+    // interval 3: Ktil_m^T over Ktil_m (read by the products), regrouped from the split words
+    // of interval 1, and X_bb = (I + A_bb)^{-1}
     auto produce_inverse = [&](Buf& B) {
 #pragma unroll
         for (int ch = 0; ch < 4; ++ch) {
             const int c = c4 + ch;
+            // channel ch of token i sits in the low (even ch) or high (odd ch) half of word ch / 2
+            const unsigned sel = (ch & 1) ? 0x07060302u : 0x05040100u;
 #pragma unroll
             for (int gq = 0; gq < TPG / 4; ++gq) {
                 uint2 hi, lo;
-                split_quad(ktk[4 * gq][ch] * enm[ch], ktk[4 * gq + 1][ch] * enm[ch], ktk[4 * gq + 2][ch] * enm[ch],
-                           ktk[4 * gq + 3][ch] * enm[ch], hi, lo);
-                const int idx = c * PT + kperm(tg * TPG + 4 * gq);
+                const int t = 4 * gq;
+                const uint32_t h0 = (ch < 2) ? kth[t].x : kth[t].y, h1 = (ch < 2) ? kth[t + 1].x : kth[t + 1].y;
+                const uint32_t h2 = (ch < 2) ? kth[t + 2].x : kth[t + 2].y, h3 = (ch < 2) ? kth[t + 3].x : kth[t + 3].y;
+                const uint32_t l0 = (ch < 2) ? ktl[t].x : ktl[t].y, l1 = (ch < 2) ? ktl[t + 1].x : ktl[t + 1].y;
+                const uint32_t l2 = (ch < 2) ? ktl[t + 2].x : ktl[t + 2].y, l3 = (ch < 2) ? ktl[t + 3].x : ktl[t + 3].y;
+                hi.x = __builtin_amdgcn_perm(h1, h0, sel);
+                hi.y = __builtin_amdgcn_perm(h3, h2, sel);
+                lo.x = __builtin_amdgcn_perm(l1, l0, sel);
+                lo.y = __builtin_amdgcn_perm(l3, l2, sel);
+                const int idx = c * PT + kperm(tg * TPG + t);
                 *reinterpret_cast<uint2*>(&B.kt[0][idx]) = hi;
                 *reinterpret_cast<uint2*>(&B.kt[1][idx]) = lo;
             }
@@ -1056,9 +1069,26 @@ void pipe_kernel(KernelArgs a) {
     f32x4 Y[NRT][CT], Z[NRT][CT];
     elem pv[NRT][CT][4];
     bf16x8 ubh[CT], ubl[CT];
+    // The consumers carry St = Diag(e^{b_m}) S, with b_m the midpoint decay of the chunk about to
+    // be processed: then Kbar S = Kbar_m St and Qbar S = Qbar_m St, and since
+    // gamma = e^{b_m} e^{b_n - b_m} and Khat = Ktil_m e^{b_n - b_m}, the chunk update is
+    //   St <- Diag(rho) (St + Ktil_m^T Unew),  rho = e^{b_m'} e^{b_n - b_m}
+    // with b_m' the next chunk's midpoint decay (rho = e^{b_n - b_m} after the last chunk, which
+    // leaves S itself).  The output pass splits St for the coming chunk at the end of
+    // interval 3, so interval 1 holds only MFMA work beside the producer's vector-ALU work; the
+    // summary pass, with twice the columns per compute unit, has no registers to spare for it.
+    constexpr bool PRESPLIT = MODE == 0;
+    bf16x8 sph[PRESPLIT ? KS : 1][CT], spl[PRESPLIT ? KS : 1][CT];
+    auto split_state = [&]() {
+        if constexpr (PRESPLIT) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) split_b(S[2 * ks][ct], S[2 * ks + 1][ct], sph[ks][ct], spl[ks][ct]);
+        }
+    };
 
-    // interval 1: V loads, Y = Kbar S and Z = Qbar S.  The B operands are Diag(e^{b_m}) S
-    // (e^{b_m} completes Kbar_m / Qbar_m to Kbar / Qbar), split per 32-deep step.
+    // interval 1: V loads, Y = Kbar_m St and Z = Qbar_m St, split per 32-deep step.
     auto consume_project = [&](const Buf& B, int chunk) {
         const long ts = t0 + static_cast<long>(chunk) * C;
         const int last = static_cast<int>(min(static_cast<long>(C), t1 - ts)) - 1;
@@ -1078,11 +1108,17 @@ void pipe_kernel(KernelArgs a) {
             for (int ct = 0; ct < CT; ++ct) Y[rt][ct] = Z[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const f32x4 e0 = *reinterpret_cast<const f32x4*>(&B.em[32 * ks + 4 * g4]);
-            const f32x4 e1 = *reinterpret_cast<const f32x4*>(&B.em[32 * ks + 16 + 4 * g4]);
             bf16x8 sbh[CT], sbl[CT];
+            if constexpr (PRESPLIT) {
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) split_b(S[2 * ks][ct] * e0, S[2 * ks + 1][ct] * e1, sbh[ct], sbl[ct]);
+                for (int ct = 0; ct < CT; ++ct) {
+                    sbh[ct] = sph[ks][ct];
+                    sbl[ct] = spl[ks][ct];
+                }
+            } else {
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) split_b(S[2 * ks][ct], S[2 * ks + 1][ct], sbh[ct], sbl[ct]);
+            }
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt) {
                 const int ao = (16 * rt + lr) * PK + 32 * ks + 8 * g4;
@@ -1090,7 +1126,7 @@ void pipe_kernel(KernelArgs a) {
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) Y[rt][ct] = mfma3(kh, kl, sbh[ct], sbl[ct], Y[rt][ct]);
                 if constexpr (MODE == 0) {
-                    // Z^T = (Diag(e^{b_m}) S)^T Qbar_m^T: the split state serves as the A operand,
+                    // Z^T = St^T Qbar_m^T: the split state serves as the A operand,
                     // so lane (g4, lr) ends up with token 16 rt + lr, columns 16 ct + 4 g4 + e
                     const bf16x8 qh = frag(&B.qb[0][ao]), ql = frag(&B.qb[1][ao]);
 #pragma unroll
@@ -1098,6 +1134,14 @@ void pipe_kernel(KernelArgs a) {
                 }
             }
         }
+        // Y <- V - Kbar S (frees the raw V registers before interval 2)
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    Y[rt][ct][e] = (is_phi ? 0.f : IN::to_f32(pv[rt][ct][e])) - Y[rt][ct][e];
     };
 
     // interval 2: Unew = (I + A)^{-1} Diag(beta) (V - Kbar S) one 16-token block at a time,
@@ -1112,10 +1156,7 @@ void pipe_kernel(KernelArgs a) {
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float vv = is_phi ? 0.f : IN::to_f32(pv[b][ct][e]);
-                    acc[ct][e] = bb[e] * (vv - Y[b][ct][e]);
-                }
+                for (int e = 0; e < 4; ++e) acc[ct][e] = bb[e] * Y[b][ct][e];
 #pragma unroll
             for (int k = 0; k < b; ++k) {
                 const int ao = (16 * b + lr) * K::AP + 16 * k + 4 * g4;
@@ -1151,15 +1192,15 @@ void pipe_kernel(KernelArgs a) {
         }
     };
 
-    // interval 3: S <- Diag(gamma) S + Khat^T Unew, and the output rows of the chunk
+    // interval 3: St <- Diag(rho) (St + Ktil_m^T Unew), and the output rows of the chunk
     auto consume_update = [&](const Buf& B, int chunk) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            const f32x4 gm = *reinterpret_cast<const f32x4*>(&B.gam[16 * rt + 4 * g4]);
+            const f32x4 rh = *reinterpret_cast<const f32x4*>(&B.rho[16 * rt + 4 * g4]);
             const int ao = (16 * rt + lr) * PT + 8 * g4;
             const bf16x8 kh = frag(&B.kt[0][ao]), kl = frag(&B.kt[1][ao]);
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) S[rt][ct] = mfma3(kh, kl, ubh[ct], ubl[ct], S[rt][ct] * gm);
+            for (int ct = 0; ct < CT; ++ct) S[rt][ct] = mfma3(kh, kl, ubh[ct], ubl[ct], S[rt][ct]) * rh;
         }
         if constexpr (MODE == 0) {
             const long ts = t0 + static_cast<long>(chunk) * C;
@@ -1184,7 +1225,7 @@ void pipe_kernel(KernelArgs a) {
     if (producer) {
         if (c_begin < c_end) {
             fetch(c_begin);
-            produce_decay(sm.buf[c_begin & 1], c_begin);
+            produce_decay(sm.buf[c_begin & 1], c_begin, nullptr);
             lds_barrier();
             produce_products(sm.buf[c_begin & 1]);
             lds_barrier();
@@ -1192,9 +1233,15 @@ void pipe_kernel(KernelArgs a) {
             lds_barrier();
         }
         for (int chunk = c_begin; chunk < c_end; ++chunk) {
+            Buf& cur = sm.buf[chunk & 1];
             Buf& nxt = sm.buf[(chunk & 1) ^ 1];
             const bool more = chunk + 1 < c_end;
-            if (more) produce_decay(nxt, chunk + 1);
+            if (more) {
+                produce_decay(nxt, chunk + 1, &cur);
+            } else if (tg == 0) {
+#pragma unroll
+                for (int ch = 0; ch < 4; ++ch) cur.rho[c4 + ch] = enm[ch];
+            }
             lds_barrier();
             if (more) produce_products(nxt);
             lds_barrier();
@@ -1207,6 +1254,14 @@ void pipe_kernel(KernelArgs a) {
         lds_barrier();
         lds_barrier();
         lds_barrier();
+        const Buf& first = sm.buf[c_begin & 1];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const f32x4 em = *reinterpret_cast<const f32x4*>(&first.em[16 * rt + 4 * g4]);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) S[rt][ct] *= em;
+        }
+        split_state();
     }
     for (int chunk = c_begin; chunk < c_end; ++chunk) {
         const Buf& cur = sm.buf[chunk & 1];
@@ -1215,6 +1270,7 @@ void pipe_kernel(KernelArgs a) {
         consume_solve(cur);
         lds_barrier();
         consume_update(cur, chunk);
+        if (chunk + 1 < c_end) split_state();
         lds_barrier();
     }
 
