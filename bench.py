@@ -3,8 +3,9 @@
 
 A step is one prefill call (``kda_chunk_fwd``) on the long-context workload:
 B=1, H=32, T=65536, d_k=d_v=128, bf16 q/k/v/log_alpha/beta, fp32 initial state
-S0 ~ 0.02*N(0,1), bf16 o and fp32 S_final, chunk 64.  ``value`` is prefill
-tokens/s (sequence tokens, not token-heads) with the inputs resident in HBM.
+S0 ~ 0.02*N(0,1), bf16 o and fp32 S_final, chunk 32 (the library default).
+``value`` is prefill tokens/s (sequence tokens, not token-heads) with the inputs
+resident in HBM.
 
 The same JSON line also reports the decode workload (256 sequences x 32 heads,
 d=128, 1024 sequential ``kda_recurrent_step`` calls on an fp32 state) as
@@ -32,7 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "KDA prefill tokens/s (H32,d128,T64K) + decode steps/s and HBM GB/s"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
-CHUNK = 64
+CHUNK = 32                       # chunk length passed to kda_chunk_fwd (the library default)
 
 
 def prefill_alg_flops_per_token_head(d: int, C: int = CHUNK) -> int:
@@ -40,6 +41,12 @@ def prefill_alg_flops_per_token_head(d: int, C: int = CHUNK) -> int:
     needed triangles: A (C-1)d, P (C+1)d, W and U 2(C+1)d, P*Unew (C+1)d,
     and 6d^2 for K S, Q S and Khat^T Unew.  The (I+A)^-1 solve is excluded."""
     return 6 * d * d + (C - 1) * d + 4 * (C + 1) * d
+
+
+def prefill_tile_flops_per_token_head(d: int, C: int = CHUNK) -> int:
+    """Flops the full C x C tiles would issue: 6d^2 + 6Cd (A, P, W, U, P*Unew
+    as dense products) + 4Cd."""
+    return 6 * d * d + 10 * C * d
 
 
 def prefill_alg_bytes(T: int, H: int, d: int, n_seqs: int, has_s0: bool) -> int:
@@ -127,8 +134,8 @@ def cpu_baseline_decode(torch, steps_inputs, S, target_s=8.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -151,11 +158,11 @@ def main():
     q, k, v, la, beta, S0 = x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"]
     o = torch.empty((B, T, H, d), dtype=torch.bfloat16, device="cuda")
     Sf = torch.empty((B, H, d, d), dtype=torch.float32, device="cuda")
-    ws_bytes = kda.kda_chunk_fwd_workspace_bytes(B, T, H, d, d, B, False)
+    ws_bytes = kda.kda_chunk_fwd_workspace_bytes(B, T, H, d, d, B, False, CHUNK)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
 
     def call():
-        kda.kda_chunk_fwd(q, k, v, la, beta, S0, None, o=o, S_final=Sf, workspace=ws, stream=stream)
+        kda.kda_chunk_fwd(q, k, v, la, beta, S0, None, o=o, S_final=Sf, workspace=ws, chunk=CHUNK, stream=stream)
 
     for _ in range(args.warmup):
         call()
@@ -180,8 +187,10 @@ def main():
     tokens = B * T
     value = tokens / (ms_step / 1e3)
     flops = prefill_alg_flops_per_token_head(d) * tokens * H
+    tile_flops = prefill_tile_flops_per_token_head(d) * tokens * H
     byts = prefill_alg_bytes(tokens, H, d, B, True)
     tflops = flops / (call_avg_ms / 1e3) / 1e12
+    tile_tflops = tile_flops / (call_avg_ms / 1e3) / 1e12
     gbs = byts / (call_avg_ms / 1e3) / 1e9
 
     # ------------------------------------------------------------------ decode
@@ -238,12 +247,17 @@ def main():
                    "log_alpha": "logsigmoid(N(0,1)+6)/16",
                    "precision": "split-bf16 MFMA operands (hi+lo), fp32 accumulation and state",
                    "schedule": plan_G},
-        "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / BF16_PEAK_TFLOPS, "traffic": counted_traffic("prefill"),
+        # Arithmetic intensity of the method (about 93 flop/B here) is below MI355X's ridge
+        # (2500 TFLOP/s / 8 TB/s = 312 flop/B), so HBM bounds it; the MFMA fractions follow.
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": counted_traffic("prefill"),
                      "launch": "kda_chunk_fwd (all prefill kernels of one call)",
-                     "avg_launch_us": call_avg_ms * 1e3, "flops_per_launch": flops,
-                     "flop_convention": f"algorithmic, {prefill_alg_flops_per_token_head(d)} per token-head at C=64",
-                     "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS, "bytes_per_launch": byts},
+                     "avg_launch_us": call_avg_ms * 1e3, "bytes_per_launch": byts,
+                     "mfma_tflops": tflops, "mfma_frac": tflops / BF16_PEAK_TFLOPS,
+                     "mfma_frac_dense_tile": tile_tflops / BF16_PEAK_TFLOPS,
+                     "flop_convention": f"algorithmic {prefill_alg_flops_per_token_head(d)} / dense-tile "
+                                        f"{prefill_tile_flops_per_token_head(d)} per token-head at C={CHUNK}",
+                     "flops_per_launch": flops},
         "cpu_baseline": cpu,
         "decode": decode,
         "wall_s": wall,
