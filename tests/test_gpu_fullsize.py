@@ -3,7 +3,7 @@ times: inputs are drawn on the GPU (seeded), the HIP path runs on the whole batc
 and the fp64 oracle recomputes sampled (sequence, head) units from the same bf16
 values copied back to the host.
 
-  workload 1  B=4, H=16, T=4096, d=128     all 64 units checked
+  workload 1  B=4, H=16, T=4096, d=128     all 64 units checked, chunk 32 and 64
   workload 2  B=1, H=32, T=65536, d=128    heads 0, 13, 31 checked (whole sequence)
   workload 4  64 packed sequences, 525,197 tokens, H=32, d=128
               the shortest, the longest and two other sequences, all heads
@@ -29,10 +29,10 @@ def _kda():
     return kda
 
 
-def run_full(x):
+def run_full(x, chunk=0):
     kda = _kda()
     o, Sf = kda.kda_chunk_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"], x["cu_seqlens"],
-                              out_dtype=torch.float32)
+                              out_dtype=torch.float32, chunk=chunk)
     torch.cuda.synchronize()
     return o, Sf
 
@@ -44,11 +44,12 @@ def sampled_oracle(x, heads):
     return oracle.kda_fwd(*args, S0=S0, o_dtype=np.float64)
 
 
-def test_workload1_full():
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_workload1_full(chunk):
     w = inputs.WORKLOADS[1]
-    print(f"[full] workload 1 {w}", flush=True)
+    print(f"[full] workload 1 {w} chunk {chunk}", flush=True)
     x = inputs.device_prefill(w)
-    o, Sf = run_full(x)
+    o, Sf = run_full(x, chunk)
     heads = list(range(w.H))
     o_ref, S_ref = sampled_oracle(x, heads)
     eo, es = o_metric(to_host(o), o_ref), state_metric(to_host(Sf), S_ref)

@@ -3,7 +3,8 @@ CPU oracle on the same seeded inputs.
 
 Shapes span several chunks and a ragged tail, packed variable-length batches with
 empty sequences, the segmented (two-pass) path for few long sequences, fast-decay
-mixtures and both head sizes.  Pages: "Decoding Hybrid Attention Architectures"
+mixtures, both head sizes and both chunk lengths (32: the pipelined kernel, 64: the
+single-buffered one).  Token-by-token decode steps must reproduce a prefill call.  Pages: "Decoding Hybrid Attention Architectures"
 (intl.cloud.baidu.com article 9569726) sections 3.4 and 4.
 """
 from __future__ import annotations
@@ -28,13 +29,16 @@ def _kda():
     return kda
 
 
-def gpu_fwd(d, out_dtype=torch.float32):
+CHUNKS = [32, 64]
+
+
+def gpu_fwd(d, out_dtype=torch.float32, chunk=0):
     kda = _kda()
     dev = {kk: to_dev(d[kk]) for kk in ("q", "k", "v", "log_alpha", "beta")}
     S0 = to_dev(d["S0"]) if d["S0"] is not None else None
     cu = to_dev(d["cu_seqlens"]) if d["cu_seqlens"] is not None else None
     o, Sf = kda.kda_chunk_fwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], S0, cu,
-                              out_dtype=out_dtype)
+                              out_dtype=out_dtype, chunk=chunk)
     torch.cuda.synchronize()
     return to_host(o), to_host(Sf)
 
@@ -46,10 +50,10 @@ def oracle_fwd(d, heads=None):
     return oracle.kda_fwd(*args, S0=S0, cu_seqlens=d["cu_seqlens"], o_dtype=np.float64)
 
 
-def check(d, label, heads=None):
-    print(f"[prefill] {label}: B={d['B']} T={d['T']} H={d['H']} D={d['D']} N={d['N']} dtype={d['dtype']}",
-          flush=True)
-    o, Sf = gpu_fwd(d)
+def check(d, label, heads=None, chunk=0):
+    print(f"[prefill] {label}: B={d['B']} T={d['T']} H={d['H']} D={d['D']} N={d['N']} dtype={d['dtype']} "
+          f"chunk={chunk or 'default'}", flush=True)
+    o, Sf = gpu_fwd(d, chunk=chunk)
     o_ref, S_ref = oracle_fwd(d, heads)
     if heads is not None:
         o, Sf = o[:, :, heads], Sf[:, heads]
@@ -62,59 +66,97 @@ def check(d, label, heads=None):
     return eo, es
 
 
-def test_tiny_fp32_workload():
+@pytest.mark.parametrize("chunk", CHUNKS)
+def test_tiny_fp32_workload(chunk):
     """Workload 0 exactly: B=1, H=2, T=256, d=64, fp32."""
-    check(inputs.make_prefill(W[0]), "workload0")
+    check(inputs.make_prefill(W[0]), "workload0", chunk=chunk)
 
 
+@pytest.mark.parametrize("chunk", CHUNKS)
 @pytest.mark.parametrize("D", [64, 128])
-def test_ragged_tail_with_initial_state(D):
+def test_ragged_tail_with_initial_state(D, chunk):
     d = inputs.make_prefill(W[1], seed=201, B=2, T=300, H=2, D=D, s0=True)
-    check(d, f"ragged D={D}")
+    check(d, f"ragged D={D}", chunk=chunk)
 
 
-def test_fp32_inputs_d128():
+@pytest.mark.parametrize("chunk", CHUNKS)
+def test_fp32_inputs_d128(chunk):
     d = inputs.make_prefill(W[1], seed=202, B=1, T=200, H=2, D=128, dtype="f32", s0=True)
-    check(d, "fp32 d128")
+    check(d, "fp32 d128", chunk=chunk)
 
 
-def test_segmented_two_pass_path():
+@pytest.mark.parametrize("chunk", CHUNKS)
+def test_segmented_two_pass_path(chunk):
     """Few (sequence, head) units and many chunks: the sequence is cut into
     segments (segment summaries, combine, rerun)."""
     kda = _kda()
-    plan_ws = kda.kda_chunk_fwd_workspace_bytes(1, 1000, 2, 128, 128, 1, False)
-    assert plan_ws > 0, "expected the segmented path for 2 units x 16 chunks"
+    plan_ws = kda.kda_chunk_fwd_workspace_bytes(1, 1000, 2, 128, 128, 1, False, chunk)
+    assert plan_ws > 0, "expected the segmented path for 2 units and 16 or more chunks"
     d = inputs.make_prefill(W[2], seed=203, B=1, T=1000, H=2, s0=True)
-    check(d, "segmented slow-decay")
+    check(d, "segmented slow-decay", chunk=chunk)
     d = inputs.make_prefill(W[1], seed=204, B=2, T=777, H=3, s0=True)
-    check(d, "segmented ragged")
+    check(d, "segmented ragged", chunk=chunk)
 
 
-def test_varlen_packed_with_empty_sequences():
+@pytest.mark.parametrize("chunk", CHUNKS)
+def test_varlen_packed_with_empty_sequences(chunk):
     d = inputs.make_prefill(W[4], seed=205, H=3, lengths=[70, 0, 1, 64, 200, 0, 129])
     d["S0"] = (0.02 * np.random.default_rng(5).standard_normal((d["N"], 3, 128, 128))).astype(np.float32)
-    check(d, "varlen + S0")
+    check(d, "varlen + S0", chunk=chunk)
 
 
-def test_fast_decay_mixture():
+@pytest.mark.parametrize("chunk", CHUNKS)
+def test_fast_decay_mixture(chunk):
     d = inputs.make_prefill(W[4], seed=206, H=2, lengths=[300, 190])
-    check(d, "mixture decay")
+    check(d, "mixture decay", chunk=chunk)
 
 
-def test_bf16_output_is_rne_of_fp32_output():
+@pytest.mark.parametrize("chunk", CHUNKS)
+def test_bf16_output_is_rne_of_fp32_output(chunk):
     d = inputs.make_prefill(W[1], seed=207, B=1, T=130, H=2, s0=True)
-    o32, S32 = gpu_fwd(d, torch.float32)
-    o16, S16 = gpu_fwd(d, torch.bfloat16)
+    o32, S32 = gpu_fwd(d, torch.float32, chunk)
+    o16, S16 = gpu_fwd(d, torch.bfloat16, chunk)
     assert np.array_equal(S32, S16)
     r = inputs.bf16_bits_to_f32(inputs.f32_to_bf16_bits(o32))
     assert np.array_equal(r, o16)
 
 
-def test_run_to_run_bitwise_deterministic():
+@pytest.mark.parametrize("chunk", CHUNKS)
+def test_run_to_run_bitwise_deterministic(chunk):
     d = inputs.make_prefill(W[2], seed=208, B=1, T=900, H=2, s0=True)
-    a = gpu_fwd(d)
-    b = gpu_fwd(d)
+    a = gpu_fwd(d, chunk=chunk)
+    b = gpu_fwd(d, chunk=chunk)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_chunk_lengths_agree():
+    """The result does not depend on the chunk length beyond rounding (fp32 inputs)."""
+    d = inputs.make_prefill(W[1], seed=211, B=2, T=333, H=2, D=128, dtype="f32", s0=True)
+    o32, S32 = gpu_fwd(d, chunk=32)
+    o64, S64 = gpu_fwd(d, chunk=64)
+    # each within the fp32 parity bound of the exact result
+    assert o_metric(o32, o64) <= 2 * TOL_F32
+    assert state_metric(S32, S64) <= 2 * TOL_F32
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_steps_reproduce_prefill(D):
+    """T single-token kda_recurrent_step calls from S0 give the prefill's o and S_final:
+    two independent GPU paths (the chunkwise form and the token recurrence)."""
+    kda = _kda()
+    d = inputs.make_prefill(W[1], seed=212, B=2, T=45, H=3, D=D, dtype="f32", s0=True)
+    o_p, S_p = gpu_fwd(d)
+    dev = {kk: to_dev(d[kk]) for kk in ("q", "k", "v", "log_alpha", "beta")}
+    S = to_dev(d["S0"]).clone()
+    outs = []
+    for t in range(d["T"]):
+        step = [dev[kk][:, t].contiguous() for kk in ("q", "k", "v", "log_alpha", "beta")]
+        o_t, _ = kda.kda_recurrent_step(*step, S, out_dtype=torch.float32)
+        outs.append(o_t)
+    o_d = torch.stack(outs, dim=1)
+    torch.cuda.synchronize()
+    assert o_metric(to_host(o_d), o_p) <= 2 * TOL_F32
+    assert state_metric(to_host(S), S_p) <= 2 * TOL_F32
 
 
 def test_split_resume_matches_single_call():
