@@ -760,7 +760,8 @@ struct PCfg {
     static constexpr int NJOB = 3;                                 // lower 16x16 tiles of a 32 x 32 product
 };
 
-template <int D, int MODE>
+// VLDS: bf16 inputs, whose V tiles the producer stages in LDS for the consumers.
+template <int D, int MODE, bool VLDS>
 struct alignas(16) PBuf {
     using K = PCfg<D, MODE>;
     static constexpr int NQ = MODE == 0 ? 2 : 1, QE = MODE == 0 ? K::C * K::PK : 8;
@@ -772,14 +773,15 @@ struct alignas(16) PBuf {
     u16 aoff[2][K::C * K::AP];  // -A off the diagonal blocks  [token][token]
     u16 xd[2][K::C * K::XP];    // X_bb = (I + A_bb)^{-1}      [16 b + r][c]
     u16 p[NQ][PE];              // P = Tril(Qbar Ktil^T)       [token][kperm(token)]
+    u16 vt[VLDS ? D * K::PT : 8];   // V^T (bf16)              [column][token]
     float beta[K::C];
     float em[D];                // e^{b_m}
     float rho[D];               // e^{b_m} of the next chunk times e^{b_n - b_m} (1 after the last)
 };
 
-template <int D, int MODE>
+template <int D, int MODE, bool VLDS>
 struct PSmem {
-    PBuf<D, MODE> buf[2];
+    PBuf<D, MODE, VLDS> buf[2];
     float a[2][16][20];         // diagonal 16x16 blocks of A (fp32), producer-private
 };
 
@@ -794,9 +796,10 @@ void pipe_kernel(KernelArgs a) {
     using R = Raw<IN>;
     using quad = typename R::quad;
     using elem = typename R::elem;
-    using Buf = PBuf<D, MODE>;
+    constexpr bool VLDS = std::is_same<IN, BF16>::value;
+    using Buf = PBuf<D, MODE, VLDS>;
 
-    __shared__ PSmem<D, MODE> sm;
+    __shared__ PSmem<D, MODE, VLDS> sm;
 
     const int tid = threadIdx.x, l = tid & 63, g4 = l >> 4, lr = l & 15;
     // wave index in a scalar register: the producer / consumer split below is a uniform
@@ -847,7 +850,7 @@ void pipe_kernel(KernelArgs a) {
     }
 
     // ================================================================ producer state
-    quad pk[TPG], pq[TPG], pg[TPG];
+    quad pk[TPG], pq[TPG], pg[TPG], pvq[TPG];
     elem pb = 0;
     uint2 kth[TPG], ktl[TPG];   // split Ktil_m words, kept from interval 1 for Ktil_m^T in interval 3
     float enm[4] = {1.f, 1.f, 1.f, 1.f};   // e^{b_n - b_m} of the chunk last produced
@@ -858,6 +861,7 @@ void pipe_kernel(KernelArgs a) {
         const ST* kp = static_cast<const ST*>(a.k) + base;
         const ST* gp = static_cast<const ST*>(a.g) + base;
         const ST* qp = static_cast<const ST*>(a.q) + base;
+        const ST* vp = static_cast<const ST*>(a.v) + base;
         // Rows past a ragged end load a valid row here and are zeroed where they are used:
         // touching a loaded value now would make the wave wait for the loads.
 #pragma unroll
@@ -866,6 +870,7 @@ void pipe_kernel(KernelArgs a) {
             pk[i] = *reinterpret_cast<const quad*>(kp + off);
             pg[i] = *reinterpret_cast<const quad*>(gp + off);
             if constexpr (MODE == 0) pq[i] = *reinterpret_cast<const quad*>(qp + off);
+            if constexpr (VLDS) pvq[i] = *reinterpret_cast<const quad*>(vp + off);
         }
         if (tid < C) pb = static_cast<const ST*>(a.beta)[static_cast<size_t>(ts + min(tid, last)) * H + h];
     };
@@ -940,8 +945,22 @@ void pipe_kernel(KernelArgs a) {
                 *reinterpret_cast<uint2*>(&B.qb[1][idx]) = lo;
             }
         }
+        if constexpr (VLDS) {
+            // V^T: channel ch of token i is the low (even ch) or high (odd ch) half of word ch / 2
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) {
+                const unsigned sel = (ch & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+                for (int gq = 0; gq < TPG / 4; ++gq) {
+                    const int t = 4 * gq;
+                    const uint32_t w0 = ch < 2 ? pvq[t].x : pvq[t].y, w1 = ch < 2 ? pvq[t + 1].x : pvq[t + 1].y;
+                    const uint32_t w2 = ch < 2 ? pvq[t + 2].x : pvq[t + 2].y, w3 = ch < 2 ? pvq[t + 3].x : pvq[t + 3].y;
+                    *reinterpret_cast<uint2*>(&B.vt[(c4 + ch) * PT + tg * TPG + t]) =
+                        uint2{__builtin_amdgcn_perm(w1, w0, sel), __builtin_amdgcn_perm(w3, w2, sel)};
+                }
+            }
+        }
         if (tid < C) B.beta[tid] = IN::to_f32(pb);
-        if (chunk + 1 < c_end) fetch(chunk + 1);
     };
 
     // interval 2: tiles of A^T and P^T.  Job (rt, ct), ct <= rt, computes Ktil_m[ct] against
@@ -1092,7 +1111,7 @@ void pipe_kernel(KernelArgs a) {
     auto consume_project = [&](const Buf& B, int chunk) {
         const long ts = t0 + static_cast<long>(chunk) * C;
         const int last = static_cast<int>(min(static_cast<long>(C), t1 - ts)) - 1;
-        if (!is_phi) {
+        if (!VLDS && !is_phi) {
             const ST* vp = static_cast<const ST*>(a.v) + (static_cast<size_t>(ts) * H + h) * D + j0 + lr;
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt)
@@ -1138,10 +1157,20 @@ void pipe_kernel(KernelArgs a) {
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
+            for (int ct = 0; ct < CT; ++ct) {
+                f32x4 vv = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (VLDS) {
+                    if (!is_phi) {
+                        const uint2 w = *reinterpret_cast<const uint2*>(&B.vt[(j0 + 16 * ct + lr) * PT + 16 * rt + 4 * g4]);
+                        vv = f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                                   __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+                    }
+                } else if (!is_phi) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    Y[rt][ct][e] = (is_phi ? 0.f : IN::to_f32(pv[rt][ct][e])) - Y[rt][ct][e];
+                    for (int e = 0; e < 4; ++e) vv[e] = IN::to_f32(pv[rt][ct][e]);
+                }
+                Y[rt][ct] = vv - Y[rt][ct];
+            }
     };
 
     // interval 2: Unew = (I + A)^{-1} Diag(beta) (V - Kbar S) one 16-token block at a time,
@@ -1227,6 +1256,7 @@ void pipe_kernel(KernelArgs a) {
             fetch(c_begin);
             produce_decay(sm.buf[c_begin & 1], c_begin, nullptr);
             lds_barrier();
+            if (c_begin + 1 < c_end) fetch(c_begin + 1);
             produce_products(sm.buf[c_begin & 1]);
             lds_barrier();
             produce_inverse(sm.buf[c_begin & 1]);
@@ -1243,6 +1273,9 @@ void pipe_kernel(KernelArgs a) {
                 for (int ch = 0; ch < 4; ++ch) cur.rho[c4 + ch] = enm[ch];
             }
             lds_barrier();
+            // The inputs of chunk c+2 are requested here, outside the decay phase that bounds
+            // interval 1; they have intervals 2 and 3 to arrive.
+            if (chunk + 2 < c_end) fetch(chunk + 2);
             if (more) produce_products(nxt);
             lds_barrier();
             if (more) produce_inverse(nxt);
