@@ -739,7 +739,7 @@ __device__ __forceinline__ void unit_lower_solve(float (&y)[16], const float (&a
 //
 //   interval   producer (chunk c+1)                 consumer (chunk c)
 //   1          decay prefix, decayed K/Q splits     Y = Kbar S, Z = Qbar S
-//   2          A and P tiles                        Unew block recurrence, O
+//   2          A tiles, next inputs requested       Unew block recurrence, O; P tiles of c+1
 //   3          Ktil_m^T, diagonal-block inverses    state update, O stores, state split
 template <int D, int MODE>
 struct PCfg {
@@ -854,7 +854,9 @@ void pipe_kernel(KernelArgs a) {
     elem pb = 0;
     uint2 kth[TPG], ktl[TPG];   // split Ktil_m words, kept from interval 1 for Ktil_m^T in interval 3
     float enm[4] = {1.f, 1.f, 1.f, 1.f};   // e^{b_n - b_m} of the chunk last produced
-    auto fetch = [&](int chunk) {
+    // part 0: k and log_alpha; part 1: q, v and beta; -1: everything.  The two parts are requested
+    // in different intervals so the chip's memory requests are spread over the chunk loop.
+    auto fetch = [&](int chunk, int part) {
         const long ts = t0 + static_cast<long>(chunk) * C;
         const int last = static_cast<int>(min(static_cast<long>(C), t1 - ts)) - 1;
         const size_t base = (static_cast<size_t>(ts) * H + h) * D;   // uniform
@@ -867,12 +869,16 @@ void pipe_kernel(KernelArgs a) {
 #pragma unroll
         for (int i = 0; i < TPG; ++i) {
             const unsigned off = static_cast<unsigned>(min(tg * TPG + i, last) * HD + c4);
-            pk[i] = *reinterpret_cast<const quad*>(kp + off);
-            pg[i] = *reinterpret_cast<const quad*>(gp + off);
-            if constexpr (MODE == 0) pq[i] = *reinterpret_cast<const quad*>(qp + off);
-            if constexpr (VLDS) pvq[i] = *reinterpret_cast<const quad*>(vp + off);
+            if (part != 1) {
+                pg[i] = *reinterpret_cast<const quad*>(gp + off);
+                pk[i] = *reinterpret_cast<const quad*>(kp + off);
+            }
+            if (part != 0) {
+                if constexpr (MODE == 0) pq[i] = *reinterpret_cast<const quad*>(qp + off);
+                if constexpr (VLDS) pvq[i] = *reinterpret_cast<const quad*>(vp + off);
+            }
         }
-        if (tid < C) pb = static_cast<const ST*>(a.beta)[static_cast<size_t>(ts + min(tid, last)) * H + h];
+        if (part != 0 && tid < C) pb = static_cast<const ST*>(a.beta)[static_cast<size_t>(ts + min(tid, last)) * H + h];
     };
 
     // interval 1: decay prefix (in log2 units) and the decayed, split K / Q planes.  With
@@ -963,46 +969,65 @@ void pipe_kernel(KernelArgs a) {
         if (tid < C) B.beta[tid] = IN::to_f32(pb);
     };
 
-    // interval 2: tiles of A^T and P^T.  Job (rt, ct), ct <= rt, computes Ktil_m[ct] against
-    // Kbar_m[rt] (and Qbar_m[rt]): the accumulator of lane (g4, lr) then holds row 16 rt + lr,
-    // columns 16 ct + 4 g4 + e, so each lane stores 4 consecutive entries of one row.
+    // Tiles of A^T and P^T: tile (rt, ct), ct <= rt, is Ktil_m[ct] against Kbar_m[rt] (or
+    // Qbar_m[rt]); the accumulator of lane (g4, lr) then holds row 16 rt + lr, columns
+    // 16 ct + 4 g4 + e, so each lane stores 4 consecutive entries of one row.  Tile index
+    // job: 0 -> (1, 0), 1 -> (0, 0), 2 -> (1, 1).
+    auto tile_of = [](int job, int& rt, int& ct) {
+        rt = job == 1 ? 0 : 1;
+        ct = job == 2 ? 1 : 0;
+    };
+    // interval 2 (producer): the three A tiles
     auto produce_products = [&](Buf& B) {
-      for (int job = w; job < K::NJOB; job += NPW) {
-        const int rt = job == 0 ? 0 : 1, ct = job == 2 ? 1 : 0;
-        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+        for (int job = w; job < 3; job += NPW) {
+            int rt, ct;
+            tile_of(job, rt, ct);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int ao = (16 * ct + lr) * PK + 32 * ks + 8 * g4;
-            const int bo = (16 * rt + lr) * PK + 32 * ks + 8 * g4;
-            const bf16x8 th = frag(&B.kt[0][ao]), tl = frag(&B.kt[1][ao]);
-            accA = mfma3(th, tl, frag(&B.kb[0][bo]), frag(&B.kb[1][bo]), accA);
-            if constexpr (MODE == 0) accP = mfma3(th, tl, frag(&B.qb[0][bo]), frag(&B.qb[1][bo]), accP);
-        }
-        const int row = 16 * rt + lr;
-        const float br = B.beta[row];
-        if (rt == ct) {
-            f32x4 v;
+            for (int ks = 0; ks < KS; ++ks) {
+                const int ao = (16 * ct + lr) * PK + 32 * ks + 8 * g4;
+                const int bo = (16 * rt + lr) * PK + 32 * ks + 8 * g4;
+                acc = mfma3(frag(&B.kt[0][ao]), frag(&B.kt[1][ao]), frag(&B.kb[0][bo]), frag(&B.kb[1][bo]), acc);
+            }
+            const int row = 16 * rt + lr;
+            const float br = B.beta[row];
+            if (rt == ct) {
+                f32x4 v;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = 4 * g4 + e < lr ? accA[e] * br : 0.f;
-            *reinterpret_cast<f32x4*>(&sm.a[rt][lr][4 * g4]) = v;
-        } else {
-            uint2 hi, lo;
-            split_quad(-accA[0] * br, -accA[1] * br, -accA[2] * br, -accA[3] * br, hi, lo);
-            const int idx = row * K::AP + 16 * ct + 4 * g4;
-            *reinterpret_cast<uint2*>(&B.aoff[0][idx]) = hi;
-            *reinterpret_cast<uint2*>(&B.aoff[1][idx]) = lo;
+                for (int e = 0; e < 4; ++e) v[e] = 4 * g4 + e < lr ? acc[e] * br : 0.f;
+                *reinterpret_cast<f32x4*>(&sm.a[rt][lr][4 * g4]) = v;
+            } else {
+                uint2 hi, lo;
+                split_quad(-acc[0] * br, -acc[1] * br, -acc[2] * br, -acc[3] * br, hi, lo);
+                const int idx = row * K::AP + 16 * ct + 4 * g4;
+                *reinterpret_cast<uint2*>(&B.aoff[0][idx]) = hi;
+                *reinterpret_cast<uint2*>(&B.aoff[1][idx]) = lo;
+            }
         }
+    };
+    // interval 2 (consumers, output pass): the three P tiles of the chunk the producer is building
+    auto consume_ptiles = [&](Buf& B) {
         if constexpr (MODE == 0) {
-            f32x4 pv4;
+            for (int job = ci; job < 3; job += K::NCW) {
+                int rt, ct;
+                tile_of(job, rt, ct);
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pv4[e] = (rt > ct || 4 * g4 + e <= lr) ? accP[e] : 0.f;
-            uint2 hi, lo;
-            split_quad(pv4[0], pv4[1], pv4[2], pv4[3], hi, lo);
-            const int idx = row * PT + 8 * g4 + 4 * ct;   // kperm(16 ct + 4 g4 + e) = 8 g4 + 4 ct + e
-            *reinterpret_cast<uint2*>(&B.p[0][idx]) = hi;
-            *reinterpret_cast<uint2*>(&B.p[1][idx]) = lo;
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int ao = (16 * ct + lr) * PK + 32 * ks + 8 * g4;
+                    const int bo = (16 * rt + lr) * PK + 32 * ks + 8 * g4;
+                    acc = mfma3(frag(&B.kt[0][ao]), frag(&B.kt[1][ao]), frag(&B.qb[0][bo]), frag(&B.qb[1][bo]), acc);
+                }
+                f32x4 pv4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pv4[e] = (rt > ct || 4 * g4 + e <= lr) ? acc[e] : 0.f;
+                uint2 hi, lo;
+                split_quad(pv4[0], pv4[1], pv4[2], pv4[3], hi, lo);
+                const int idx = (16 * rt + lr) * PT + 8 * g4 + 4 * ct;   // kperm(16 ct + 4 g4 + e) = 8 g4 + 4 ct + e
+                *reinterpret_cast<uint2*>(&B.p[0][idx]) = hi;
+                *reinterpret_cast<uint2*>(&B.p[1][idx]) = lo;
+            }
         }
-      }
     };
 
     // interval 3: Ktil_m^T over Ktil_m (read by the products), regrouped from the split words
@@ -1253,12 +1278,13 @@ void pipe_kernel(KernelArgs a) {
     // workgroup barriers: three for the first chunk's operands, then three per chunk.
     if (producer) {
         if (c_begin < c_end) {
-            fetch(c_begin);
+            fetch(c_begin, -1);
             produce_decay(sm.buf[c_begin & 1], c_begin, nullptr);
             lds_barrier();
-            if (c_begin + 1 < c_end) fetch(c_begin + 1);
+            if (c_begin + 1 < c_end) fetch(c_begin + 1, 0);
             produce_products(sm.buf[c_begin & 1]);
             lds_barrier();
+            if (c_begin + 1 < c_end) fetch(c_begin + 1, 1);
             produce_inverse(sm.buf[c_begin & 1]);
             lds_barrier();
         }
@@ -1273,11 +1299,12 @@ void pipe_kernel(KernelArgs a) {
                 for (int ch = 0; ch < 4; ++ch) cur.rho[c4 + ch] = enm[ch];
             }
             lds_barrier();
-            // The inputs of chunk c+2 are requested here, outside the decay phase that bounds
-            // interval 1; they have intervals 2 and 3 to arrive.
-            if (chunk + 2 < c_end) fetch(chunk + 2);
+            // The inputs of chunk c+2 are requested outside the decay phase that bounds interval 1,
+            // k and log_alpha (used first) here, q, v and beta at the start of interval 3.
+            if (chunk + 2 < c_end) fetch(chunk + 2, 0);
             if (more) produce_products(nxt);
             lds_barrier();
+            if (chunk + 2 < c_end) fetch(chunk + 2, 1);
             if (more) produce_inverse(nxt);
             lds_barrier();
         }
@@ -1285,6 +1312,7 @@ void pipe_kernel(KernelArgs a) {
     }
     if (c_begin < c_end) {
         lds_barrier();
+        consume_ptiles(sm.buf[c_begin & 1]);
         lds_barrier();
         lds_barrier();
         const Buf& first = sm.buf[c_begin & 1];
@@ -1301,6 +1329,7 @@ void pipe_kernel(KernelArgs a) {
         consume_project(cur, chunk);
         lds_barrier();
         consume_solve(cur);
+        if (chunk + 1 < c_end) consume_ptiles(sm.buf[(chunk & 1) ^ 1]);
         lds_barrier();
         consume_update(cur, chunk);
         if (chunk + 1 < c_end) split_state();
