@@ -807,6 +807,7 @@ void pipe_kernel(KernelArgs a) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = a.H;
     const bool producer = w < NPW;
+    const bool solver = w == NPW - 1;   // the producer wave that inverts the diagonal blocks
 
     // ---------------------------------------------------------------- work unit
     int n, h, s, c_begin, c_end;
@@ -1055,7 +1056,7 @@ void pipe_kernel(KernelArgs a) {
                 *reinterpret_cast<uint2*>(&B.kt[1][idx]) = lo;
             }
         }
-        if (w == NPW - 1 && l < 32) {
+        if (solver && l < 32) {
             // Lane (blk, i) solves row i of X: x^T (I + A) = e_i^T, i.e. with A strictly lower
             // triangular x_j = [j == i] - sum_{k > j} x_k A_kj, taken for k = 15 .. 1.  The lane
             // keeps row i of A_bb in registers; A_kj comes from lane k of the same 16-lane row.
@@ -1281,10 +1282,10 @@ void pipe_kernel(KernelArgs a) {
             fetch(c_begin, -1);
             produce_decay(sm.buf[c_begin & 1], c_begin, nullptr);
             lds_barrier();
-            if (c_begin + 1 < c_end) fetch(c_begin + 1, 0);
+            if (c_begin + 1 < c_end) fetch(c_begin + 1, solver ? -1 : 0);
             produce_products(sm.buf[c_begin & 1]);
             lds_barrier();
-            if (c_begin + 1 < c_end) fetch(c_begin + 1, 1);
+            if (!solver && c_begin + 1 < c_end) fetch(c_begin + 1, 1);
             produce_inverse(sm.buf[c_begin & 1]);
             lds_barrier();
         }
@@ -1299,12 +1300,13 @@ void pipe_kernel(KernelArgs a) {
                 for (int ch = 0; ch < 4; ++ch) cur.rho[c4 + ch] = enm[ch];
             }
             lds_barrier();
-            // The inputs of chunk c+2 are requested outside the decay phase that bounds interval 1,
-            // k and log_alpha (used first) here, q, v and beta at the start of interval 3.
-            if (chunk + 2 < c_end) fetch(chunk + 2, 0);
+            // The inputs of chunk c+2 are requested outside the decay phase that bounds interval 1:
+            // k and log_alpha (used first) here, q, v and beta at the start of interval 3, except
+            // on the wave that solves the diagonal blocks in interval 3, which requests all here.
+            if (chunk + 2 < c_end) fetch(chunk + 2, solver ? -1 : 0);
             if (more) produce_products(nxt);
             lds_barrier();
-            if (chunk + 2 < c_end) fetch(chunk + 2, 1);
+            if (!solver && chunk + 2 < c_end) fetch(chunk + 2, 1);
             if (more) produce_inverse(nxt);
             lds_barrier();
         }
