@@ -713,20 +713,22 @@ void chunk_kernel(KernelArgs a) {
     }
 }
 
-// Value of lane K of this lane's 16-lane row (DPP row broadcast).
-template <int K>
-__device__ __forceinline__ float row_bcast(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + K, 0xf, 0xf, true));
+// Value of lane S of this lane's group of 4 lanes (DPP quad_perm broadcast).
+template <int S>
+__device__ __forceinline__ float quad_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), S * 0x55, 0xf, 0xf, true));
 }
 
 // Right-looking elimination steps K, K-1, .., 1 of x^T (I + A) = e_i^T for a strictly lower
-// triangular 16 x 16 A whose row k sits in lane k of the 16-lane row (ar = this lane's row).
+// triangular 16 x 16 A, with row i of x spread over the 4 lanes of a quad: this lane holds
+// x_{4 jg + c}, c = 0..3, and col[k][c] = A_{k, 4 jg + c}.  x_K lives in lane K / 4 of the quad.
+// A_{k j} = 0 for j >= k, so every lane updates its 4 entries at every step.
 template <int K>
-__device__ __forceinline__ void unit_lower_solve(float (&y)[16], const float (&ar)[16]) {
-    const float nk = -y[K];
+__device__ __forceinline__ void quad_lower_solve(float (&y)[4], const f32x4 (&col)[16]) {
+    const float nk = -quad_bcast<K / 4>(y[K % 4]);
 #pragma unroll
-    for (int j = 0; j < K; ++j) y[j] = __builtin_fmaf(row_bcast<K>(ar[j]), nk, y[j]);
-    if constexpr (K > 1) unit_lower_solve<K - 1>(y, ar);
+    for (int c = 0; c < 4; ++c) y[c] = __builtin_fmaf(col[K][c], nk, y[c]);
+    if constexpr (K > 1) quad_lower_solve<K - 1>(y, col);
 }
 
 // ------------------------------------------------------------------ pipelined kernel (C = 32)
@@ -807,7 +809,8 @@ void pipe_kernel(KernelArgs a) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = a.H;
     const bool producer = w < NPW;
-    const bool solver = w == NPW - 1;   // the producer wave that inverts the diagonal blocks
+    // The last two producer waves invert the two diagonal blocks (one each) in interval 3.
+    const bool solver = w >= NPW - 2;
 
     // ---------------------------------------------------------------- work unit
     int n, h, s, c_begin, c_end;
@@ -1056,32 +1059,24 @@ void pipe_kernel(KernelArgs a) {
                 *reinterpret_cast<uint2*>(&B.kt[1][idx]) = lo;
             }
         }
-        if (solver && l < 32) {
-            // Lane (blk, i) solves row i of X: x^T (I + A) = e_i^T, i.e. with A strictly lower
-            // triangular x_j = [j == i] - sum_{k > j} x_k A_kj, taken for k = 15 .. 1.  The lane
-            // keeps row i of A_bb in registers; A_kj comes from lane k of the same 16-lane row.
-            const int blk = l >> 4;
-            int i = l & 15;
+        if (solver) {
+            // Block blk: lane (i, jg) = (l / 4, l % 4) solves columns 4 jg .. 4 jg + 3 of row i
+            // of X_bb = (I + A_bb)^{-1} (x^T (I + A) = e_i^T).
+            const int blk = w - (NPW - 2), jg = l & 3;
+            int i = l >> 2;
             asm volatile("" : "+v"(i));   // keep the unit-vector set-up inside the loop
-            float ar[16], y[16];
+            f32x4 col[16];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f32x4 v = *reinterpret_cast<const f32x4*>(&sm.a[blk][i][4 * q]);
+            for (int kk = 0; kk < 16; ++kk) col[kk] = *reinterpret_cast<const f32x4*>(&sm.a[blk][kk][4 * jg]);
+            float y[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) ar[4 * q + e] = v[e];
-            }
-#pragma unroll
-            for (int j = 0; j < 16; ++j) y[j] = j == i ? 1.f : 0.f;
-            unit_lower_solve<15>(y, ar);
-            uint32_t hw[8], lw[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) split_pair(y[2 * j], y[2 * j + 1], hw[j], lw[j]);
-            uint4* dh = reinterpret_cast<uint4*>(&B.xd[0][(16 * blk + i) * K::XP]);
-            uint4* dl = reinterpret_cast<uint4*>(&B.xd[1][(16 * blk + i) * K::XP]);
-            dh[0] = uint4{hw[0], hw[1], hw[2], hw[3]};
-            dh[1] = uint4{hw[4], hw[5], hw[6], hw[7]};
-            dl[0] = uint4{lw[0], lw[1], lw[2], lw[3]};
-            dl[1] = uint4{lw[4], lw[5], lw[6], lw[7]};
+            for (int c = 0; c < 4; ++c) y[c] = 4 * jg + c == i ? 1.f : 0.f;
+            quad_lower_solve<15>(y, col);
+            uint2 hi, lo;
+            split_quad(y[0], y[1], y[2], y[3], hi, lo);
+            const int idx = (16 * blk + i) * K::XP + 4 * jg;
+            *reinterpret_cast<uint2*>(&B.xd[0][idx]) = hi;
+            *reinterpret_cast<uint2*>(&B.xd[1][idx]) = lo;
         }
     };
 
