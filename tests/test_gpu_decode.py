@@ -67,6 +67,33 @@ def test_decode_full_shape_sampled():
     run_steps(N=256, H=32, D=128, dtype="bf16", steps=48, seed=4, sample=[0, 1, 2, 3, 100, 200, 254, 255])
 
 
+def test_decode_1024_steps_all_heads():
+    """1024 sequential steps (the decode workload's step count) on 32 sequences x 32 heads,
+    d=128, bf16: o checked at every step for sequences 0-7 and at the last step for all,
+    the final state for every head, all against the fp64 oracle run on every head."""
+    kda = _kda()
+    N, H, D, steps = 32, 32, 128, 1024
+    ds = inputs.DecodeStream(inputs.WORKLOADS[3], seed=4, num_seqs=N, H=H, D=D, dtype="bf16")
+    S_gpu = to_dev(ds.state())
+    S_ref = np.ascontiguousarray(ds.state().astype(np.float64))
+    worst_o = 0.0
+    for s in range(steps):
+        x = ds.step()
+        dev = {kk: to_dev(vv) for kk, vv in x.items()}
+        o, _ = kda.kda_recurrent_step(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"],
+                                      S_gpu, out_dtype=torch.float32)
+        o_ref = oracle.kda_step(*(x[kk] for kk in ("q", "k", "v", "log_alpha", "beta")), S_ref,
+                                o_dtype=np.float64)
+        rows = slice(None) if s == steps - 1 else slice(0, 8)
+        worst_o = max(worst_o, slice_metric(to_host(o)[rows], o_ref[rows], axes=(2,)))
+        if s % 256 == 0:
+            print(f"[decode] step {s}: worst o so far {worst_o:.3e}", flush=True)
+    torch.cuda.synchronize()
+    worst_s = slice_metric(to_host(S_gpu), S_ref, axes=(2, 3))
+    print(f"[decode]   1024 steps: worst o {worst_o:.3e}  S {worst_s:.3e}  tol {TOL_BF16}", flush=True)
+    assert worst_o <= TOL_BF16 and worst_s <= TOL_BF16
+
+
 def test_decode_inplace_and_out_of_place_agree_and_bf16_output_is_rne():
     kda = _kda()
     ds = inputs.DecodeStream(inputs.WORKLOADS[3], seed=7, num_seqs=3, H=2, D=128)
