@@ -76,12 +76,23 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Two values at once: hi = bf16(x) packed in one word, lo = bf16(x - hi) packed in another
-// (one v_cvt_pk_bf16_f32 per word).
+// A 32-bit constant in a scalar register.  The bf16 pairs (-1, 0) and (0, -1) below must not
+// become inline constants: an inline constant names a 32-bit float, not a bf16 pair.
+__device__ __forceinline__ uint32_t sreg_const(uint32_t v) {
+    uint32_t r;
+    asm("s_mov_b32 %0, %1" : "=s"(r) : "i"(v));
+    return r;
+}
+
+// Two values at once: hi = bf16(x) packed in one word, lo = bf16(x - hi) packed in another.
+// x_i - hi_i is exact in fp32; v_dot2_f32_bf16 forms it in one instruction as
+// hi . (-e_i) + x_i (the other product is hi_j * 0), so a pair costs two conversions and two
+// dot products.
 __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
     const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
-    const float r0 = x0 - __uint_as_float(h << 16);
-    const float r1 = x1 - __uint_as_float(h & 0xffff0000u);
+    const bf16x2 hb = __builtin_bit_cast(bf16x2, h);
+    const float r0 = __builtin_amdgcn_fdot2_f32_bf16(hb, __builtin_bit_cast(bf16x2, sreg_const(0x0000bf80u)), x0, false);
+    const float r1 = __builtin_amdgcn_fdot2_f32_bf16(hb, __builtin_bit_cast(bf16x2, sreg_const(0xbf800000u)), x1, false);
     hi = h;
     lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
 }
@@ -754,11 +765,17 @@ struct PCfg {
     static constexpr int WPE = (NW + 3) / 4;                       // waves per SIMD
     static constexpr int TPG = C / 8;                              // tokens per producer thread
     static constexpr int NRT = C / 16, RT = D / 16, KS = D / 32;
-    static constexpr int PK = D + 8;                               // pitch of [token][channel] planes
-    static constexpr int PT = C + 8;                               // pitch of [row][token] planes
+    // LDS planes carry no padding; 16-byte slots are XOR-swizzled per row instead, so that the
+    // MFMA fragment reads (16 rows x 4 slots per instruction) and the producers' 8-byte writes
+    // both avoid bank conflicts.  [token][channel] planes: rows of D channels, slot ^= row.
+    __device__ static int tok(int row, int col) {
+        return row * D + ((((col >> 3) ^ row) & (D / 8 - 1)) << 3) + (col & 7);
+    }
+    // [row][token] planes (C = 32 tokens, four 16-byte slots per row)
+    __device__ static int swz(int row) { return (((row >> 2) ^ (row >> 4)) & 3) ^ ((row >> 1) & 2); }
+    __device__ static int chm(int row, int col) { return row * C + ((((col >> 3) ^ swz(row)) & 3) << 3) + (col & 7); }
     static constexpr int AP = C + 4;                               // pitch of the off-diagonal A planes
     static constexpr int XP = 24;                                  // pitch of the diagonal-inverse planes
-    static constexpr int KT = (C * PK > D * PT) ? C * PK : D * PT;
     static constexpr int NJOB = 3;                                 // lower 16x16 tiles of a 32 x 32 product
 };
 
@@ -766,16 +783,16 @@ struct PCfg {
 template <int D, int MODE, bool VLDS>
 struct alignas(16) PBuf {
     using K = PCfg<D, MODE>;
-    static constexpr int NQ = MODE == 0 ? 2 : 1, QE = MODE == 0 ? K::C * K::PK : 8;
-    static constexpr int PE = MODE == 0 ? K::C * K::PT : 8;
-    u16 kb[2][K::C * K::PK];    // Kbar_m = K e^{b - b_m}     [token][kperm(channel)]
+    static constexpr int NQ = MODE == 0 ? 2 : 1, QE = MODE == 0 ? K::C * D : 8;
+    static constexpr int PE = MODE == 0 ? K::C * K::C : 8;
+    u16 kb[2][K::C * D];        // Kbar_m = K e^{b - b_m}     [token][kperm(channel)]
     u16 qb[NQ][QE];             // Qbar_m = Q e^{b - b_m}     [token][kperm(channel)]
-    u16 kt[2][K::KT];           // Ktil_m = K e^{b_m - b} [token][kperm(channel)], then
+    u16 kt[2][K::C * D];        // Ktil_m = K e^{b_m - b} [token][kperm(channel)], then
                                 // Ktil_m^T                   [channel][kperm(token)]
     u16 aoff[2][K::C * K::AP];  // -A off the diagonal blocks  [token][token]
     u16 xd[2][K::C * K::XP];    // X_bb = (I + A_bb)^{-1}      [16 b + r][c]
     u16 p[NQ][PE];              // P = Tril(Qbar Ktil^T)       [token][kperm(token)]
-    u16 vt[VLDS ? D * K::PT : 8];   // V^T (bf16)              [column][token]
+    u16 vt[VLDS ? D * K::C : 8];    // V^T (bf16)              [column][token]
     float beta[K::C];
     float em[D];                // e^{b_m}
     float rho[D];               // e^{b_m} of the next chunk times e^{b_n - b_m} (1 after the last)
@@ -793,7 +810,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(PCfg<D, MODE>::NT, PCfg<D,
 void pipe_kernel(KernelArgs a) {
     using K = PCfg<D, MODE>;
     constexpr int C = K::C, NPW = K::NPW, CT = K::CT, TPG = K::TPG;
-    constexpr int NRT = K::NRT, RT = K::RT, KS = K::KS, PK = K::PK, PT = K::PT;
+    constexpr int NRT = K::NRT, RT = K::RT, KS = K::KS;
     using ST = typename IN::storage;
     using R = Raw<IN>;
     using quad = typename R::quad;
@@ -847,9 +864,9 @@ void pipe_kernel(KernelArgs a) {
 
     if constexpr (MODE == 0) {
         // P's strictly-upper 16x16 tile inside the 32-deep step is read but never written.
-        for (int i = tid; i < 2 * 2 * C * PT; i += K::NT) {
-            const int b = i / (2 * C * PT), r = i % (2 * C * PT);
-            sm.buf[b].p[r / (C * PT)][r % (C * PT)] = 0;
+        for (int i = tid; i < 2 * 2 * C * C; i += K::NT) {
+            const int b = i / (2 * C * C), r = i % (2 * C * C);
+            sm.buf[b].p[r / (C * C)][r % (C * C)] = 0;
         }
     }
 
@@ -864,15 +881,16 @@ void pipe_kernel(KernelArgs a) {
         const long ts = t0 + static_cast<long>(chunk) * C;
         const int last = static_cast<int>(min(static_cast<long>(C), t1 - ts)) - 1;
         const size_t base = (static_cast<size_t>(ts) * H + h) * D;   // uniform
-        const ST* kp = static_cast<const ST*>(a.k) + base;
-        const ST* gp = static_cast<const ST*>(a.g) + base;
-        const ST* qp = static_cast<const ST*>(a.q) + base;
-        const ST* vp = static_cast<const ST*>(a.v) + base;
+        // uniform bases plus a 32-bit byte offset per lane (scalar base + vector offset addressing)
+        const char* kp = reinterpret_cast<const char*>(static_cast<const ST*>(a.k) + base);
+        const char* gp = reinterpret_cast<const char*>(static_cast<const ST*>(a.g) + base);
+        const char* qp = reinterpret_cast<const char*>(static_cast<const ST*>(a.q) + base);
+        const char* vp = reinterpret_cast<const char*>(static_cast<const ST*>(a.v) + base);
         // Rows past a ragged end load a valid row here and are zeroed where they are used:
         // touching a loaded value now would make the wave wait for the loads.
 #pragma unroll
         for (int i = 0; i < TPG; ++i) {
-            const unsigned off = static_cast<unsigned>(min(tg * TPG + i, last) * HD + c4);
+            const unsigned off = static_cast<unsigned>(min(tg * TPG + i, last) * HD + c4) * sizeof(ST);
             if (part != 1) {
                 pg[i] = *reinterpret_cast<const quad*>(gp + off);
                 pk[i] = *reinterpret_cast<const quad*>(kp + off);
@@ -941,7 +959,7 @@ void pipe_kernel(KernelArgs a) {
                 kt[ch] = kv * ei;
                 if constexpr (MODE == 0) qb[ch] = R::get(pq[i], ch) * em;
             }
-            const int idx = r * PK + kperm(c4);
+            const int idx = K::tok(r, kperm(c4));
             uint2 hi, lo;
             split_quad(kb[0], kb[1], kb[2], kb[3], hi, lo);
             *reinterpret_cast<uint2*>(&B.kb[0][idx]) = hi;
@@ -965,7 +983,7 @@ void pipe_kernel(KernelArgs a) {
                     const int t = 4 * gq;
                     const uint32_t w0 = ch < 2 ? pvq[t].x : pvq[t].y, w1 = ch < 2 ? pvq[t + 1].x : pvq[t + 1].y;
                     const uint32_t w2 = ch < 2 ? pvq[t + 2].x : pvq[t + 2].y, w3 = ch < 2 ? pvq[t + 3].x : pvq[t + 3].y;
-                    *reinterpret_cast<uint2*>(&B.vt[(c4 + ch) * PT + tg * TPG + t]) =
+                    *reinterpret_cast<uint2*>(&B.vt[K::chm(c4 + ch, tg * TPG + t)]) =
                         uint2{__builtin_amdgcn_perm(w1, w0, sel), __builtin_amdgcn_perm(w3, w2, sel)};
                 }
             }
@@ -989,8 +1007,8 @@ void pipe_kernel(KernelArgs a) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const int ao = (16 * ct + lr) * PK + 32 * ks + 8 * g4;
-                const int bo = (16 * rt + lr) * PK + 32 * ks + 8 * g4;
+                const int ao = K::tok(16 * ct + lr, 32 * ks + 8 * g4);
+                const int bo = K::tok(16 * rt + lr, 32 * ks + 8 * g4);
                 acc = mfma3(frag(&B.kt[0][ao]), frag(&B.kt[1][ao]), frag(&B.kb[0][bo]), frag(&B.kb[1][bo]), acc);
             }
             const int row = 16 * rt + lr;
@@ -1018,8 +1036,8 @@ void pipe_kernel(KernelArgs a) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const int ao = (16 * ct + lr) * PK + 32 * ks + 8 * g4;
-                    const int bo = (16 * rt + lr) * PK + 32 * ks + 8 * g4;
+                    const int ao = K::tok(16 * ct + lr, 32 * ks + 8 * g4);
+                    const int bo = K::tok(16 * rt + lr, 32 * ks + 8 * g4);
                     acc = mfma3(frag(&B.kt[0][ao]), frag(&B.kt[1][ao]), frag(&B.qb[0][bo]), frag(&B.qb[1][bo]), acc);
                 }
                 f32x4 pv4;
@@ -1027,7 +1045,7 @@ void pipe_kernel(KernelArgs a) {
                 for (int e = 0; e < 4; ++e) pv4[e] = (rt > ct || 4 * g4 + e <= lr) ? acc[e] : 0.f;
                 uint2 hi, lo;
                 split_quad(pv4[0], pv4[1], pv4[2], pv4[3], hi, lo);
-                const int idx = (16 * rt + lr) * PT + 8 * g4 + 4 * ct;   // kperm(16 ct + 4 g4 + e) = 8 g4 + 4 ct + e
+                const int idx = K::chm(16 * rt + lr, 8 * g4 + 4 * ct);   // kperm(16 ct + 4 g4 + e) = 8 g4 + 4 ct + e
                 *reinterpret_cast<uint2*>(&B.p[0][idx]) = hi;
                 *reinterpret_cast<uint2*>(&B.p[1][idx]) = lo;
             }
@@ -1054,7 +1072,7 @@ void pipe_kernel(KernelArgs a) {
                 hi.y = __builtin_amdgcn_perm(h3, h2, sel);
                 lo.x = __builtin_amdgcn_perm(l1, l0, sel);
                 lo.y = __builtin_amdgcn_perm(l3, l2, sel);
-                const int idx = c * PT + kperm(tg * TPG + t);
+                const int idx = K::chm(c, kperm(tg * TPG + t));
                 *reinterpret_cast<uint2*>(&B.kt[0][idx]) = hi;
                 *reinterpret_cast<uint2*>(&B.kt[1][idx]) = lo;
             }
@@ -1161,7 +1179,7 @@ void pipe_kernel(KernelArgs a) {
             }
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt) {
-                const int ao = (16 * rt + lr) * PK + 32 * ks + 8 * g4;
+                const int ao = K::tok(16 * rt + lr, 32 * ks + 8 * g4);
                 const bf16x8 kh = frag(&B.kb[0][ao]), kl = frag(&B.kb[1][ao]);
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) Y[rt][ct] = mfma3(kh, kl, sbh[ct], sbl[ct], Y[rt][ct]);
@@ -1182,7 +1200,7 @@ void pipe_kernel(KernelArgs a) {
                 f32x4 vv = {0.f, 0.f, 0.f, 0.f};
                 if constexpr (VLDS) {
                     if (!is_phi) {
-                        const uint2 w = *reinterpret_cast<const uint2*>(&B.vt[(j0 + 16 * ct + lr) * PT + 16 * rt + 4 * g4]);
+                        const uint2 w = *reinterpret_cast<const uint2*>(&B.vt[K::chm(j0 + 16 * ct + lr, 16 * rt + 4 * g4)]);
                         vv = f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
                                    __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
                     }
@@ -1234,7 +1252,7 @@ void pipe_kernel(KernelArgs a) {
             // O^T = Z^T + Unew^T P^T
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt) {
-                const int ao = (16 * rt + lr) * PT + 8 * g4;
+                const int ao = K::chm(16 * rt + lr, 8 * g4);
                 const bf16x8 ph = frag(&B.p[0][ao]), pl = frag(&B.p[1][ao]);
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) Z[rt][ct] = mfma3(ubh[ct], ubl[ct], ph, pl, Z[rt][ct]);
@@ -1247,7 +1265,7 @@ void pipe_kernel(KernelArgs a) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             const f32x4 rh = *reinterpret_cast<const f32x4*>(&B.rho[16 * rt + 4 * g4]);
-            const int ao = (16 * rt + lr) * PT + 8 * g4;
+            const int ao = K::chm(16 * rt + lr, 8 * g4);
             const bf16x8 kh = frag(&B.kt[0][ao]), kl = frag(&B.kt[1][ao]);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) S[rt][ct] = mfma3(kh, kl, ubh[ct], ubl[ct], S[rt][ct]) * rh;
