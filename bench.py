@@ -9,7 +9,8 @@ resident in HBM.
 
 The same JSON line also reports the decode workload (256 sequences x 32 heads,
 d=128, 1024 sequential ``kda_recurrent_step`` calls on an fp32 state) as
-``decode``, the roofline of each path's dominant launch measured with HIP events
+``decode``, a few new tokens per sequence on top of a carried state as
+``continuation``, the roofline of each path's dominant launch measured with HIP events
 on the launch stream, and the fp64 CPU oracle timed on a bounded sample of the
 same workloads on this host (``cpu_baseline``).
 
@@ -230,6 +231,44 @@ def main():
                      "bytes_per_launch": dbytes},
     }
 
+    # ------------------------------------------------------------------ continuation (serving shapes)
+    # New tokens on top of a carried state: 256 sequences x 32 heads.  "verify4": 4 tokens each
+    # (speculative verification; equal lengths, so kda_chunk_fwd runs them token by token);
+    # "packed": workload 5, 1..32 tokens per sequence packed by cu_seqlens (chunked path).
+    import dataclasses
+
+    def cont_case(w, label):
+        xc = inputs.device_prefill(w)
+        Nc, Tc = xc["N"], xc["B"] * xc["T"]
+        oc = torch.empty((xc["B"], xc["T"], w.H, w.D), dtype=torch.bfloat16, device="cuda")
+        Sc = torch.empty_like(xc["S0"])
+
+        def run():
+            kda.kda_chunk_fwd(xc["q"], xc["k"], xc["v"], xc["log_alpha"], xc["beta"], xc["S0"], xc["cu_seqlens"],
+                              o=oc, S_final=Sc, stream=stream)
+        for _ in range(5):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 50
+        e0.record(stream)
+        for _ in range(reps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        cb = prefill_alg_bytes(Tc, w.H, w.D, Nc, True)
+        return {"workload": label, "sequences": Nc, "tokens": Tc, "H": w.H, "d": w.D, "us_per_call": us,
+                "tokens_per_s": Tc / (us / 1e6), "bytes_per_call": cb, "hbm_gbs": cb / (us / 1e6) / 1e9,
+                "frac_hbm": cb / (us / 1e6) / 1e9 / HBM_PEAK_GBS}
+
+    w5 = inputs.WORKLOADS[5]
+    continuation = {
+        "verify4": cont_case(dataclasses.replace(w5, B=256, T=4, len_range=()),
+                             "256 sequences x 4 new tokens (token-by-token kernel)"),
+        "packed": cont_case(w5, "256 sequences x U{1..32} new tokens, packed (chunked kernel)"),
+    }
+
     # ------------------------------------------------------------------ CPU baselines (oracle)
     cpu = None
     if not args.no_cpu_baseline:
@@ -260,6 +299,7 @@ def main():
                      "flops_per_launch": flops},
         "cpu_baseline": cpu,
         "decode": decode,
+        "continuation": continuation,
         "wall_s": wall,
     }
     print(json.dumps(out))

@@ -97,6 +97,16 @@ extern "C" kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
     if (overlap(workspace, plan.workspace_bytes, o, n_o) || overlap(workspace, plan.workspace_bytes, S_final, n_s))
         return KDA_ERR_INVALID_ARGUMENT;
 
+    // A batch of equal-length sequences of at most kRecurrentMaxT tokens (new tokens on top of a
+    // carried state) runs token by token with the state on chip: a chunk would be mostly padding.
+    if (!cu_seqlens && T > 0 && T <= kda::kRecurrentMaxT) {
+        const size_t units = static_cast<size_t>(B) * H;
+        if (units > 0x7fffffffu) return KDA_ERR_UNSUPPORTED;
+        hipError_t err = kda::launch_recurrent_fwd(Dk, in_dtype == KDA_BF16, out_dtype == KDA_BF16, q, k, v,
+                                                   log_alpha, beta, S0, nullptr, T, H, static_cast<int>(units), o,
+                                                   S_final, reinterpret_cast<hipStream_t>(stream));
+        return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    }
     kda::PrefillArgs a;
     a.q = q; a.k = k; a.v = v; a.g = log_alpha; a.beta = beta;
     a.S0 = S0; a.cu = cu_seqlens; a.o = o; a.S_final = S_final;
@@ -134,5 +144,50 @@ extern "C" kda_status kda_recurrent_step(const void* q, const void* k, const voi
     hipError_t err = kda::launch_decode(Dk, in_dtype == KDA_BF16, out_dtype == KDA_BF16, q, k, v, log_alpha,
                                         beta, S_in, S_out, o, static_cast<int>(units),
                                         reinterpret_cast<hipStream_t>(stream));
+    return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+extern "C" kda_status kda_recurrent_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                                        const void* beta, const float* S0, const int32_t* cu_seqlens,
+                                        int B, int T, int H, int Dk, int Dv, int num_seqs,
+                                        kda_dtype in_dtype, kda_dtype out_dtype, void* o, float* S_final,
+                                        kda_stream_t stream) {
+    if (B < 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || num_seqs < 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_UNSUPPORTED;
+    if (!head_ok(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
+    if (cu_seqlens) {
+        if (B != 1 || !aligned16(cu_seqlens)) return KDA_ERR_INVALID_ARGUMENT;
+    } else if (num_seqs != B) {
+        return KDA_ERR_INVALID_ARGUMENT;
+    }
+    const size_t tokens = static_cast<size_t>(B) * static_cast<size_t>(T);
+    if (tokens > 0 && num_seqs > 0) {
+        if (!q || !k || !v || !log_alpha || !beta || !o) return KDA_ERR_INVALID_ARGUMENT;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) || !aligned16(beta) ||
+            !aligned16(o))
+            return KDA_ERR_INVALID_ARGUMENT;
+    }
+    if ((S0 && !aligned16(S0)) || (S_final && !aligned16(S_final))) return KDA_ERR_INVALID_ARGUMENT;
+    const size_t ein = elem_size(in_dtype), eout = elem_size(out_dtype);
+    const size_t n_qk = tokens * H * Dk * ein, n_v = tokens * H * Dv * ein, n_b = tokens * H * ein;
+    const size_t n_o = tokens * H * Dv * eout;
+    const size_t n_s = static_cast<size_t>(num_seqs) * H * Dk * Dv * sizeof(float);
+    if (tokens > 0) {
+        const void* ins[5] = {q, k, v, log_alpha, beta};
+        const size_t nin[5] = {n_qk, n_qk, n_v, n_qk, n_b};
+        for (int i = 0; i < 5; ++i)
+            if (overlap(ins[i], nin[i], o, n_o) || overlap(ins[i], nin[i], S_final, n_s))
+                return KDA_ERR_INVALID_ARGUMENT;
+    }
+    // S_final == S0 (in place) is allowed; any other overlap is not
+    if ((S0 != S_final && overlap(S0, n_s, S_final, n_s)) || overlap(S0, n_s, o, n_o) ||
+        overlap(o, n_o, S_final, n_s))
+        return KDA_ERR_INVALID_ARGUMENT;
+    const size_t units = static_cast<size_t>(num_seqs) * H;
+    if (units == 0) return KDA_OK;
+    if (units > 0x7fffffffu) return KDA_ERR_UNSUPPORTED;
+    hipError_t err = kda::launch_recurrent_fwd(Dk, in_dtype == KDA_BF16, out_dtype == KDA_BF16, q, k, v, log_alpha,
+                                               beta, S0, cu_seqlens, T, H, static_cast<int>(units), o, S_final,
+                                               reinterpret_cast<hipStream_t>(stream));
     return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

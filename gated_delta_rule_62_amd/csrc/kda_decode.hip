@@ -1,4 +1,5 @@
-// kda_decode.hip -- single-token KDA decode step (gfx950).
+// kda_decode.hip -- token-by-token KDA kernels for gfx950: the single-token decode step and
+// the multi-token recurrent forward (a few new tokens per sequence on top of a carried state).
 //
 // One token of the fine-grained gated delta rule ("Decoding Hybrid Attention
 // Architectures", intl.cloud.baidu.com article 9569726, section 3.4) for N x H
@@ -128,6 +129,248 @@ void decode_step_kernel(const typename IN::storage* __restrict__ q,
         store_out<OUT_BF16>(o, vec + j0 + 2, p.z + kqs * e.z);
         store_out<OUT_BF16>(o, vec + j0 + 3, p.w + kqs * e.w);
     }
+}
+
+// ------------------------------------------------------------------ multi-token recurrent forward
+// The same rule applied to every token of each sequence in order, with the state held in
+// registers between tokens: per (sequence, head) the state is read once and written once,
+// whatever the number of tokens.  This is the serving shape of a few new tokens per
+// sequence on top of a long context (speculative verification, chunked continuation),
+// where a chunk's intra-chunk work would be mostly padding.
+//
+// Mapping: one workgroup of 2D threads per (sequence, head); the two lanes of a pair own the
+// upper and lower half of state column j, so the reductions r = S'^T k and p = S'^T q over
+// the key channels are private to the pair (one DPP exchange) and a token needs a single
+// workgroup barrier: thread c < D also stages row c's per-token factors in LDS for everyone.
+//
+// Lazy decay: a thread carries St = Diag(1/A) S with A the product of the decays since
+// the last renormalisation (per key channel).  With A' = alpha A,
+//     r = St^T (A' k),  p = St^T (A' q),  St <- St + (k / A') e^T,
+// three fused multiply-adds per state element and token.  When some A' falls below 2^-32
+// the whole workgroup folds A' back into St (St <- Diag(A') St, A <- 1).  A single token's
+// decay is taken no smaller than 2^-60 (log_alpha >= -41.59; below that the decayed state is
+// negligible against any write), so A' >= 2^-92 and every factor stays well inside fp32.
+struct RecArgs {
+    const void *q, *k, *v, *g, *beta;
+    const float* S0;
+    const int32_t* cu;
+    void* o;
+    float* S_final;
+    int T, H;
+};
+
+// x plus the value of the other lane of its pair (DPP quad_perm [1, 0, 3, 2])
+__device__ __forceinline__ float pair_sum(float x) {
+    return x + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xf, 0xf, true));
+}
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xf, false));
+}
+
+// Sum over the 64 lanes of a wave, valid in lane 63: butterflies inside quads, half-rows
+// and rows, then the row broadcasts (DPP only, no LDS round trip).
+__device__ __forceinline__ float wave_sum_lane63(float x) {
+    x += dpp_f<0xB1>(x);          // quad_perm [1, 0, 3, 2]
+    x += dpp_f<0x4E>(x);          // quad_perm [2, 3, 0, 1]
+    x += dpp_f<0x141>(x);         // row_half_mirror
+    x += dpp_f<0x140>(x);         // row_mirror
+    x += dpp_f<0x142, 0xa>(x);    // row_bcast:15 into rows 1 and 3
+    x += dpp_f<0x143, 0xc>(x);    // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
+template <int D, typename IN, bool OUT_BF16>
+__global__ __launch_bounds__(2 * D)
+void recurrent_fwd_kernel(RecArgs a) {
+    using ST = typename IN::storage;
+    constexpr int NT = 2 * D, NW = NT / 64, R = D / 2;   // R rows per lane
+    constexpr float kRenorm = 2.3283064365386963e-10f;  // 2^-32
+    constexpr float kMinLog2Decay = -60.f;
+
+    __shared__ float4 s_f[2][3][D / 4];   // per row c (4 at a time): A' k, A' q, k / A'
+    __shared__ float4 s_ren[2][D / 4];    // renormalisation factors A'
+    __shared__ float s_kq[2][NW];
+    __shared__ int s_flag[2][NW];
+
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int j = t >> 1, half = t & 1, r0 = half * R;
+    const int unit = blockIdx.x, H = a.H;
+    const int n = unit / H, h = unit % H;
+    long t0, t1;
+    if (a.cu) {
+        t0 = a.cu[n];
+        t1 = a.cu[n + 1];
+    } else {
+        t0 = static_cast<long>(n) * a.T;
+        t1 = t0 + a.T;
+    }
+    const size_t sbase = static_cast<size_t>(unit) * D * D;
+
+    float st[R];
+    if (a.S0) {
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+            st[i] = __builtin_nontemporal_load(a.S0 + sbase + static_cast<size_t>(r0 + i) * D + j);
+    } else {
+#pragma unroll
+        for (int i = 0; i < R; ++i) st[i] = 0.f;
+    }
+
+    const ST* qp = static_cast<const ST*>(a.q);
+    const ST* kp = static_cast<const ST*>(a.k);
+    const ST* vp = static_cast<const ST*>(a.v);
+    const ST* gp = static_cast<const ST*>(a.g);
+    const ST* bp = static_cast<const ST*>(a.beta);
+    // token inputs of this thread: channel c (threads t < D) of q, k, log_alpha; column j of v; beta
+    struct Tok { ST q, k, g, v, b; };
+    const int c = t < D ? t : t - D;
+    // (tokens past the end re-read the last one, so every load is unconditional and in bounds)
+    auto load_tok = [&](long tk) {
+        const long tc = tk < t1 ? tk : t1 - 1;
+        const size_t base = (static_cast<size_t>(tc) * H + h) * D;
+        Tok x;
+        x.q = qp[base + c];
+        x.k = kp[base + c];
+        x.g = gp[base + c];
+        x.v = vp[base + j];
+        x.b = bp[static_cast<size_t>(tc) * H + h];
+        return x;
+    };
+    float A = 1.f;   // running decay product of row c (threads t < D)
+    float ap = 1.f;  // A' of the token staged last
+    // Stage token x's factors of row c into buffer buf (threads t < D); returns A'.
+    auto stage = [&](const Tok& x, int buf) {
+        const float xq = IN::to_f32(x.q), xk = IN::to_f32(x.k);
+        const float ap = A * __builtin_amdgcn_exp2f(fmaxf(IN::to_f32(x.g) * 1.4426950408889634f, kMinLog2Decay));
+        float kq = 0.f;
+        bool low = false;
+        if (t < D) {
+            reinterpret_cast<float*>(&s_f[buf][0][c >> 2])[c & 3] = ap * xk;
+            reinterpret_cast<float*>(&s_f[buf][1][c >> 2])[c & 3] = ap * xq;
+            reinterpret_cast<float*>(&s_f[buf][2][c >> 2])[c & 3] = xk * __builtin_amdgcn_rcpf(ap);
+            reinterpret_cast<float*>(&s_ren[buf][c >> 2])[c & 3] = ap;
+            kq = xk * xq;
+            low = ap < kRenorm;
+        }
+        kq = wave_sum_lane63(kq);
+        const bool any_low = __builtin_amdgcn_ballot_w64(low) != 0;
+        if (lane == 63) {
+            s_kq[buf][w] = kq;
+            s_flag[buf][w] = any_low;
+        }
+        return ap;
+    };
+
+    if (t0 < t1) {
+        // One token: stage the next token's factors (from nxt) into the other buffer, then
+        // r, p, the output and the state update from buffer buf; cur (token tk's v and beta)
+        // is then refilled with token tk + 4.  Four token slots are in flight, so a token's
+        // inputs are requested three tokens before its factors are staged.
+        auto token = [&](long tk, int buf, Tok& cur, const Tok& nxt) {
+            __syncthreads();
+            bool ren = false;
+            float kq = 0.f;
+#pragma unroll
+            for (int i = 0; i < NW; ++i) {
+                ren |= s_flag[buf][i] != 0;
+                kq += s_kq[buf][i];
+            }
+            A = ren ? 1.f : ap;
+            const float xv = IN::to_f32(cur.v), xb = IN::to_f32(cur.b);
+            if (tk + 1 < t1) ap = stage(nxt, buf ^ 1);
+            cur = load_tok(tk + 4);
+            float rr[4] = {0.f, 0.f, 0.f, 0.f}, pp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i4 = 0; i4 < R / 4; ++i4) {
+                const float4 fk = s_f[buf][0][r0 / 4 + i4], fq = s_f[buf][1][r0 / 4 + i4];
+                const int m = i4 & 3;
+                rr[m] += fk.x * st[4 * i4] + fk.y * st[4 * i4 + 1] + fk.z * st[4 * i4 + 2] + fk.w * st[4 * i4 + 3];
+                pp[m] += fq.x * st[4 * i4] + fq.y * st[4 * i4 + 1] + fq.z * st[4 * i4 + 2] + fq.w * st[4 * i4 + 3];
+            }
+            const float r = pair_sum((rr[0] + rr[1]) + (rr[2] + rr[3]));
+            const float p = pair_sum((pp[0] + pp[1]) + (pp[2] + pp[3]));
+            const float e = xb * (xv - r);
+            if (half == 0) store_out<OUT_BF16>(a.o, (static_cast<size_t>(tk) * H + h) * D + j, p + kq * e);
+#pragma unroll
+            for (int i4 = 0; i4 < R / 4; ++i4) {
+                const float4 fu = s_f[buf][2][r0 / 4 + i4];
+                st[4 * i4] += fu.x * e;
+                st[4 * i4 + 1] += fu.y * e;
+                st[4 * i4 + 2] += fu.z * e;
+                st[4 * i4 + 3] += fu.w * e;
+            }
+            if (ren) {
+#pragma unroll
+                for (int i4 = 0; i4 < R / 4; ++i4) {
+                    const float4 f = s_ren[buf][r0 / 4 + i4];
+                    st[4 * i4] *= f.x;
+                    st[4 * i4 + 1] *= f.y;
+                    st[4 * i4 + 2] *= f.z;
+                    st[4 * i4 + 3] *= f.w;
+                }
+            }
+        };
+        Tok x0 = load_tok(t0), x1 = load_tok(t0 + 1), x2 = load_tok(t0 + 2), x3 = load_tok(t0 + 3);
+        ap = stage(x0, 0);
+        // four tokens per trip with fixed slot roles (no register rotation, which would make
+        // each trip wait for the newest loads)
+        for (long base = t0; base < t1; base += 4) {
+            token(base, 0, x0, x1);
+            if (base + 1 >= t1) break;
+            token(base + 1, 1, x1, x2);
+            if (base + 2 >= t1) break;
+            token(base + 2, 0, x2, x3);
+            if (base + 3 >= t1) break;
+            token(base + 3, 1, x3, x0);
+        }
+        // fold the remaining decay product into the state (row c's A lives in thread c)
+        __syncthreads();
+        if (t < D) reinterpret_cast<float*>(&s_ren[0][c >> 2])[c & 3] = A;
+        __syncthreads();
+#pragma unroll
+        for (int i4 = 0; i4 < R / 4; ++i4) {
+            const float4 f = s_ren[0][r0 / 4 + i4];
+            st[4 * i4] *= f.x;
+            st[4 * i4 + 1] *= f.y;
+            st[4 * i4 + 2] *= f.z;
+            st[4 * i4 + 3] *= f.w;
+        }
+    }
+    if (a.S_final) {
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+            __builtin_nontemporal_store(st[i], a.S_final + sbase + static_cast<size_t>(r0 + i) * D + j);
+    }
+}
+
+template <int D, typename IN, bool OUT_BF16>
+static hipError_t launch_recurrent_t(const RecArgs& a, int units, hipStream_t stream) {
+    hipLaunchKernelGGL((recurrent_fwd_kernel<D, IN, OUT_BF16>), dim3(units), dim3(2 * D), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_recurrent_fwd(int D, bool in_bf16, bool out_bf16, const void* q, const void* k,
+                                const void* v, const void* g, const void* b, const float* S0,
+                                const int32_t* cu, int T, int H, int units, void* o, float* S_final,
+                                hipStream_t stream) {
+    RecArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = b;
+    a.S0 = S0; a.cu = cu; a.o = o; a.S_final = S_final; a.T = T; a.H = H;
+#define KDA_REC_CASE(DD, INT, OB)                                                          \
+    if (D == DD && in_bf16 == std::is_same<INT, BF16>::value && out_bf16 == OB)              \
+        return launch_recurrent_t<DD, INT, OB>(a, units, stream);
+    KDA_REC_CASE(128, BF16, true)
+    KDA_REC_CASE(128, BF16, false)
+    KDA_REC_CASE(128, F32, true)
+    KDA_REC_CASE(128, F32, false)
+    KDA_REC_CASE(64, BF16, true)
+    KDA_REC_CASE(64, BF16, false)
+    KDA_REC_CASE(64, F32, true)
+    KDA_REC_CASE(64, F32, false)
+#undef KDA_REC_CASE
+    return hipErrorInvalidValue;
 }
 
 template <int D, typename IN, bool OUT_BF16>

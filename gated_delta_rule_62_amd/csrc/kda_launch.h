@@ -11,6 +11,10 @@ namespace kda {
 constexpr int kDefaultChunk = 32;     // chunk length C (tokens) when the caller passes 0
 constexpr int kComputeUnits = 256;    // MI355X
 constexpr int kMinChunksPerSegment = 4;
+// Equal-length batches of at most this many tokens per sequence take the token-by-token
+// kernel (on MI355X it beats a one-chunk pass up to about 7 tokens: the state traffic is the
+// same and the chunk's fixed intra-chunk work is skipped).
+constexpr int kRecurrentMaxT = 4;
 
 inline bool chunk_supported(int c) { return c == 0 || c == 32 || c == 64; }
 
@@ -47,5 +51,10 @@ hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan, hipStre
 hipError_t launch_decode(int D, bool in_bf16, bool out_bf16, const void* q, const void* k,
                          const void* v, const void* g, const void* b, const float* S_in,
                          float* S_out, void* o, int units, hipStream_t stream);
+
+hipError_t launch_recurrent_fwd(int D, bool in_bf16, bool out_bf16, const void* q, const void* k,
+                                const void* v, const void* g, const void* b, const float* S0,
+                                const int32_t* cu, int T, int H, int units, void* o, float* S_final,
+                                hipStream_t stream);
 
 }  // namespace kda

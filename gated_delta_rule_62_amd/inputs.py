@@ -13,6 +13,9 @@ Workloads (the five shapes the layer is measured and checked on):
   3  decode                 N=256 sequences, H=32, d=128, 1024 steps, bf16 in,
                             S ~ 0.02*N(0,1)
   4  packed varlen prefill  64 sequences, lengths U{512..16384}, H=32, d=128, bf16
+  5  continuation           256 sequences of U{1..32} new tokens each on top of a carried
+                            state (speculative verification / chunked continuation),
+                            packed, H=32, d=128, bf16, S0 ~ 0.02*N(0,1)
 
 Distributions: q, k ~ N(0,1) then L2-normalised per (token, head); v ~ N(0,1);
 beta = sigmoid(N(0,1)); log_alpha = logsigmoid(N(0,1) + mu) / s per channel with
@@ -66,6 +69,8 @@ WORKLOADS = {
     3: Workload(3, "decode", "decode", H=32, D=128, s0=True, num_seqs=256, steps=1024),
     4: Workload(4, "varlen_packed_prefill", "prefill", H=32, D=128, mix=True,
                 num_seqs=64, len_range=(512, 16384)),
+    5: Workload(5, "continuation", "prefill", H=32, D=128, s0=True,
+                num_seqs=256, len_range=(1, 32)),
 }
 
 

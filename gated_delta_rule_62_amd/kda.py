@@ -19,7 +19,8 @@ KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE_TOO_SMA
 KDA_F32, KDA_BF16 = 0, 1
 CHUNK = 0          # library default chunk length (32 tokens); 32 and 64 are built
 
-EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_step")
+EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_step",
+            "kda_recurrent_fwd")
 
 _lib = None
 
@@ -47,6 +48,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd.restype = i32
     lib.kda_recurrent_step.argtypes = [vp] * 7 + [i32] * 4 + [i32, i32] + [vp, vp]
     lib.kda_recurrent_step.restype = i32
+    lib.kda_recurrent_fwd.argtypes = [vp] * 7 + [i32] * 6 + [i32, i32] + [vp, vp, vp]
+    lib.kda_recurrent_fwd.restype = i32
     _lib = lib
     return lib
 
@@ -131,3 +134,27 @@ def kda_recurrent_step(q, k, v, log_alpha, beta, S_in, S_out=None, *, out_dtype=
     if st != KDA_OK:
         raise KDAError(st, "kda_recurrent_step")
     return o, S_out
+
+
+def kda_recurrent_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, out_dtype=None, o=None,
+                      S_final=None, stream=None, want_final=True):
+    """Token-by-token forward over each sequence (the multi-token continuation of decode).
+    Same tensors as kda_chunk_fwd; S_final may be S0 (in place).  Returns (o, S_final)."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=out_dtype, device=q.device)
+    if S_final is None and want_final:
+        S_final = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    _check_dev(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_final)
+    st = load_library().kda_recurrent_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
+        B, T, H, Dk, Dv, N, _dtype_code(q.dtype), _dtype_code(o.dtype), _ptr(o), _ptr(S_final),
+        _stream_ptr(stream))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_recurrent_fwd")
+    return o, S_final

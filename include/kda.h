@@ -90,7 +90,8 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int nu
  * Supported: Dk == Dv in {64, 128}; in_dtype, out_dtype in {KDA_F32, KDA_BF16}.
  * A sequence of length 0 gets S_final = S0 (or zeros).  T == 0 or N == 0 only
  * writes S_final.  Inputs must not overlap outputs.  The result does not depend
- * on the chunk size beyond rounding.
+ * on the chunk size beyond rounding.  Equal-length batches (cu_seqlens NULL) with
+ * T <= 4 are evaluated token by token, as kda_recurrent_fwd does.
  */
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
                          const void* beta, const float* S0, const int32_t* cu_seqlens,
@@ -116,6 +117,25 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const
                               int N, int H, int Dk, int Dv,
                               kda_dtype in_dtype, kda_dtype out_dtype,
                               void* o, kda_stream_t stream);
+
+/*
+ * kda_recurrent_fwd -- the same result as kda_chunk_fwd, computed token by token per
+ * sequence with the state held on chip: every (sequence, head) state is read once
+ * and written once.  It is the multi-token continuation of decode (the constant-size
+ * recurrent state of section 1 of article 9569726): a few new tokens per sequence on
+ * top of a carried state, as in speculative verification or chunked continuation,
+ * where the chunkwise form would be mostly padding.  Its cost grows with the longest
+ * sequence, so long prompts belong to kda_chunk_fwd.
+ *
+ * Arguments and layouts are those of kda_chunk_fwd (there is no chunk and no
+ * workspace).  S_final == S0 (in place) is allowed; any other overlap is rejected.
+ * A single token's decay is taken no smaller than 2^-60 (log_alpha >= -41.59).
+ */
+kda_status kda_recurrent_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                             const void* beta, const float* S0, const int32_t* cu_seqlens,
+                             int B, int T, int H, int Dk, int Dv, int num_seqs,
+                             kda_dtype in_dtype, kda_dtype out_dtype,
+                             void* o, float* S_final, kda_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -101,3 +101,24 @@ def test_decode_argument_errors(lib):
     assert step(So=ctypes.c_void_p((4 << 40) + 256)) == kda.KDA_ERR_INVALID_ARGUMENT   # partial overlap
     assert step(o=ctypes.c_void_p((4 << 40) + 512)) == kda.KDA_ERR_INVALID_ARGUMENT    # o inside the state
     assert step(q=FAKE_MIS) == kda.KDA_ERR_INVALID_ARGUMENT
+
+
+def test_recurrent_fwd_argument_errors(lib):
+    def rec(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, S0=ctypes.c_void_p(4 << 40), cu=None, B=2, T=8, H=2,
+                 Dk=128, Dv=128, N=2, in_dt=kda.KDA_BF16, out_dt=kda.KDA_F32, o=ctypes.c_void_p(5 << 40),
+                 Sf=ctypes.c_void_p(4 << 40))
+        a.update(kw)
+        return lib.kda_recurrent_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["cu"], a["B"], a["T"],
+                                     a["H"], a["Dk"], a["Dv"], a["N"], a["in_dt"], a["out_dt"], a["o"], a["Sf"],
+                                     None)
+    assert rec(B=0, N=0, T=0) == kda.KDA_OK                                   # nothing to do, no HIP call
+    assert rec(Dk=96, Dv=96) == kda.KDA_ERR_UNSUPPORTED
+    assert rec(out_dt=5) == kda.KDA_ERR_UNSUPPORTED
+    assert rec(q=None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert rec(v=FAKE_MIS) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert rec(N=3) == kda.KDA_ERR_INVALID_ARGUMENT                           # N != B without cu_seqlens
+    assert rec(cu=ctypes.c_void_p(3 << 40)) == kda.KDA_ERR_INVALID_ARGUMENT   # cu_seqlens needs B == 1
+    assert rec(Sf=ctypes.c_void_p((4 << 40) + 256)) == kda.KDA_ERR_INVALID_ARGUMENT   # partial overlap with S0
+    assert rec(o=FAKE) == kda.KDA_ERR_INVALID_ARGUMENT                        # o aliases the inputs
+    assert rec(o=ctypes.c_void_p((4 << 40) + 1024)) == kda.KDA_ERR_INVALID_ARGUMENT   # o inside the state

@@ -159,6 +159,14 @@ def test_decode_steps_reproduce_prefill(D):
     assert state_metric(to_host(S), S_p) <= 2 * TOL_F32
 
 
+@pytest.mark.parametrize("T", [1, 3, 4, 5])
+def test_short_equal_length_batches(T):
+    """A few new tokens per sequence on top of a carried state: T <= 4 runs token by
+    token, T = 5 one chunk; both match the oracle."""
+    d = inputs.make_prefill(W[1], seed=213 + T, B=5, T=T, H=3, D=128, s0=True)
+    check(d, f"short equal-length T={T}")
+
+
 def test_split_resume_matches_single_call():
     """Prefill of [0, t) then [t, T) with S0 = S_final of the first equals one call."""
     d = inputs.make_prefill(W[1], seed=209, B=1, T=400, H=2, s0=True)

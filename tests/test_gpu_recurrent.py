@@ -1,0 +1,166 @@
+"""Multi-token recurrent forward on the GPU: kda_recurrent_fwd (HIP, through the C ABI)
+vs the fp64 CPU oracle on the same seeded inputs.
+
+This is the serving shape of a few new tokens per sequence on top of a carried state
+(speculative verification, chunked continuation): "Decoding Hybrid Attention
+Architectures" (intl.cloud.baidu.com article 9569726) section 1 (constant-size state)
+and section 3.4 (the rule).  Cases: packed sequences with empty and one-token members,
+both head sizes and input dtypes, equal-length batches, in-place state update, long
+fast-decay sequences (the lazy-decay renormalisation path), decays below the kernel's
+floor, agreement with kda_chunk_fwd, and the continuation workload at full size.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+from gated_delta_rule_62_amd import inputs
+from gated_delta_rule_62_amd.inputs import host_bits
+from gpu_util import TOL_BF16, TOL_F32, o_metric, state_metric, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+W = inputs.WORKLOADS
+KEYS = ("q", "k", "v", "log_alpha", "beta")
+
+
+def _kda():
+    from gated_delta_rule_62_amd import kda
+    kda.load_library()
+    return kda
+
+
+def gpu_rec(d, out_dtype=torch.float32, inplace=False):
+    kda = _kda()
+    dev = {kk: to_dev(d[kk]) for kk in KEYS}
+    S0 = to_dev(d["S0"]) if d["S0"] is not None else None
+    cu = to_dev(d["cu_seqlens"]) if d["cu_seqlens"] is not None else None
+    Sf = S0 if inplace else None
+    o, Sf = kda.kda_recurrent_fwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], S0, cu,
+                                  out_dtype=out_dtype, S_final=Sf)
+    torch.cuda.synchronize()
+    return to_host(o), to_host(Sf)
+
+
+def check(d, label, inplace=False):
+    print(f"[recurrent] {label}: B={d['B']} T={d['T']} H={d['H']} D={d['D']} N={d['N']} dtype={d['dtype']}",
+          flush=True)
+    o, Sf = gpu_rec(d, inplace=inplace)
+    S0 = None if d["S0"] is None else d["S0"]
+    o_ref, S_ref = oracle.kda_fwd(*(d[kk] for kk in KEYS), S0=S0, cu_seqlens=d["cu_seqlens"],
+                                  o_dtype=np.float64)
+    eo, es = o_metric(o, o_ref, d["cu_seqlens"]), state_metric(Sf, S_ref)
+    tol = TOL_F32 if d["dtype"] == "f32" else TOL_BF16
+    print(f"[recurrent]   worst o {eo:.3e}  S_final {es:.3e}  (tol {tol})", flush=True)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(Sf))
+    assert eo <= tol and es <= tol
+    return o, Sf
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_packed_short_sequences(D, dtype):
+    d = inputs.make_prefill(W[5], seed=501, H=3, D=D, dtype=dtype, lengths=[5, 0, 1, 17, 40, 3, 32, 2])
+    check(d, f"packed D={D} {dtype}")
+
+
+def test_equal_length_batch():
+    d = inputs.make_prefill(W[1], seed=502, B=4, T=20, H=2, D=128, s0=True)
+    check(d, "equal length")
+
+
+def test_zero_initial_state():
+    d = inputs.make_prefill(W[0], seed=503, B=2, T=50, H=2, D=64)
+    check(d, "S0 = 0, fp32")
+
+
+def test_in_place_state_update():
+    d = inputs.make_prefill(W[5], seed=504, H=2, lengths=[9, 1, 0, 30])
+    o_a, S_a = gpu_rec(d)
+    o_b, S_b = gpu_rec(d, inplace=True)
+    assert np.array_equal(o_a, o_b) and np.array_equal(S_a, S_b)
+    check(d, "in place", inplace=True)
+
+
+def test_long_fast_decay_renormalises():
+    """Fast-forgetting channels (about -0.4 nats per token, half the channels) over
+    hundreds of tokens: the decay product crosses 2^-32 many times."""
+    d = inputs.make_prefill(W[4], seed=505, H=2, lengths=[700, 333])
+    d["S0"] = (0.02 * np.random.default_rng(55).standard_normal((2, 2, 128, 128))).astype(np.float32)
+    check(d, "fast decay, renormalisation")
+
+
+def test_decay_below_floor():
+    """Tokens whose decay is far below 2^-60 wipe the state; the kernel's floor on a
+    single token's decay changes the result by far less than the parity bound."""
+    d = inputs.make_prefill(W[5], seed=506, H=2, lengths=[12, 7], dtype="f32")
+    g = d["log_alpha"].copy()
+    g[:, 3, :, :16] = -60.0
+    g[:, 10, 1, :] = -200.0
+    d["log_alpha"] = g
+    check(d, "decay below the floor")
+
+
+def test_agrees_with_chunked_prefill():
+    """Two independent GPU paths for the same result: token recurrence vs chunkwise."""
+    kda = _kda()
+    d = inputs.make_prefill(W[5], seed=507, H=3, lengths=[64, 3, 100, 0, 31])
+    o_r, S_r = gpu_rec(d)
+    dev = {kk: to_dev(d[kk]) for kk in KEYS}
+    o_c, S_c = kda.kda_chunk_fwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], to_dev(d["S0"]),
+                                 to_dev(d["cu_seqlens"]), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert o_metric(o_r, to_host(o_c), d["cu_seqlens"]) <= 2 * TOL_BF16
+    assert state_metric(S_r, to_host(S_c)) <= 2 * TOL_BF16
+
+
+def test_bf16_output_is_rne_of_fp32_output():
+    d = inputs.make_prefill(W[5], seed=508, H=2, lengths=[13, 4])
+    o32, S32 = gpu_rec(d, torch.float32)
+    o16, S16 = gpu_rec(d, torch.bfloat16)
+    assert np.array_equal(S32, S16)
+    assert np.array_equal(inputs.bf16_bits_to_f32(inputs.f32_to_bf16_bits(o32)), o16)
+
+
+def test_continuation_workload_full_size():
+    """The continuation workload (256 sequences of 1..32 new tokens, 32 heads) in the
+    launch configuration the benchmark times; the oracle checks every head of a few
+    sequences from the same bf16 values."""
+    kda = _kda()
+    w = W[5]
+    x = inputs.device_prefill(w)
+    cu = x["cu_host"]
+    lens = np.diff(cu)
+    print(f"[recurrent] continuation: {len(lens)} sequences, {int(cu[-1])} tokens", flush=True)
+    o, Sf = kda.kda_recurrent_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"], x["cu_seqlens"],
+                                  out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    picks = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 100, 255})
+    worst_o = worst_s = 0.0
+    for n in picks:
+        tok = slice(int(cu[n]), int(cu[n + 1]))
+        args = [host_bits(x[kk][:, tok]) for kk in KEYS]
+        o_ref, S_ref = oracle.kda_fwd(*args, S0=x["S0"][n:n + 1].cpu().numpy(), o_dtype=np.float64)
+        eo = o_metric(to_host(o[:, tok]), o_ref)
+        es = state_metric(to_host(Sf[n:n + 1]), S_ref)
+        worst_o, worst_s = max(worst_o, eo), max(worst_s, es)
+    print(f"[recurrent]   sequences {picks}: worst o {worst_o:.3e} S_final {worst_s:.3e}", flush=True)
+    assert worst_o <= TOL_BF16 and worst_s <= TOL_BF16
+
+
+def test_rejects_bad_arguments():
+    kda = _kda()
+    d = inputs.make_prefill(W[5], seed=509, H=2, lengths=[4, 4])
+    dev = {kk: to_dev(d[kk]) for kk in KEYS}
+    S0 = to_dev(d["S0"])
+    cu = to_dev(d["cu_seqlens"])
+    with pytest.raises(kda.KDAError) as e:       # S_final overlapping S0 without being it
+        kda.kda_recurrent_fwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], S0, cu,
+                              S_final=S0.view(-1)[64:])
+    assert e.value.status == kda.KDA_ERR_INVALID_ARGUMENT
+    with pytest.raises(kda.KDAError) as e:       # o aliasing an input
+        kda.kda_recurrent_fwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], S0, cu, o=dev["v"])
+    assert e.value.status == kda.KDA_ERR_INVALID_ARGUMENT
