@@ -9,7 +9,8 @@ resident in HBM.
 
 The same JSON line also reports the decode workload (256 sequences x 32 heads,
 d=128, 1024 sequential ``kda_recurrent_step`` calls on an fp32 state) as
-``decode``, a few new tokens per sequence on top of a carried state as
+``decode``, the scalar-gated variant (Gated DeltaNet) at the long-context shape
+as ``gdn``, a few new tokens per sequence on top of a carried state as
 ``continuation``, the roofline of each path's dominant launch measured with HIP events
 on the launch stream, and the fp64 CPU oracle timed on a bounded sample of the
 same workloads on this host (``cpu_baseline``).
@@ -231,6 +232,36 @@ def main():
                      "bytes_per_launch": dbytes},
     }
 
+    # ------------------------------------------------------------------ scalar gate (Gated DeltaNet)
+    # Workload 2's shape with one decay per (token, head): gdn_chunk_fwd.
+    w6 = inputs.WORKLOADS[6]
+    xg = inputs.device_prefill(w6)
+    og = torch.empty((w6.B, w6.T, w6.H, d), dtype=torch.bfloat16, device="cuda")
+    Sg = torch.empty((w6.B, w6.H, d, d), dtype=torch.float32, device="cuda")
+
+    def call_gdn():
+        kda.gdn_chunk_fwd(xg["q"], xg["k"], xg["v"], xg["log_alpha"], xg["beta"], xg["S0"], None, o=og, S_final=Sg,
+                          workspace=ws, stream=stream)
+    for _ in range(args.warmup):
+        call_gdn()
+    torch.cuda.synchronize()
+    eg0, eg1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    eg0.record(stream)
+    for _ in range(args.steps):
+        call_gdn()
+    eg1.record(stream)
+    torch.cuda.synchronize()
+    gdn_ms = eg0.elapsed_time(eg1) / args.steps
+    # bytes: q, k, v and o (bf16 rows of d), one log_alpha and one beta per token-head, S0 and S_final
+    gdn_bytes = w6.B * w6.T * w6.H * (4 * d * 2 + 2 + 2) + 2 * w6.B * w6.H * d * d * 4
+    gdn = {"workload": "long_context_prefill, scalar gate: B=1, T=65536, H=32, d=128, bf16, "
+                       "log_alpha [B,T,H] = logsigmoid(N(0,1)+6)/16",
+           "value": w6.B * w6.T / (gdn_ms / 1e3), "unit": "tokens/s", "ms_per_call": gdn_ms,
+           "roofline": {"bound": "hbm", "achieved": gdn_bytes / (gdn_ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": gdn_bytes / (gdn_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                        "bytes_per_launch": gdn_bytes, "launch": "gdn_chunk_fwd (all prefill kernels of one call)"}}
+    del xg, og, Sg
+
     # ------------------------------------------------------------------ continuation (serving shapes)
     # New tokens on top of a carried state: 256 sequences x 32 heads.  "verify4": 4 tokens each
     # (speculative verification; equal lengths, so kda_chunk_fwd runs them token by token);
@@ -299,6 +330,7 @@ def main():
                      "flops_per_launch": flops},
         "cpu_baseline": cpu,
         "decode": decode,
+        "gdn": gdn,
         "continuation": continuation,
         "wall_s": wall,
     }

@@ -50,15 +50,19 @@ extern "C" size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int
     return plan.workspace_bytes;
 }
 
-extern "C" kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
-                                    const void* beta, const float* S0, const int32_t* cu_seqlens,
-                                    int B, int T, int H, int Dk, int Dv, int num_seqs, int chunk,
-                                    kda_dtype in_dtype, kda_dtype out_dtype, void* o, float* S_final,
-                                    void* workspace, size_t workspace_bytes, kda_stream_t stream) {
+namespace {
+
+// Prefill for either decay layout: per key channel (KDA, log_alpha [B, T, H, Dk]) or one value
+// per token and head (scalar gate, log_alpha [B, T, H]).
+kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const void* log_alpha, const void* beta,
+                          const float* S0, const int32_t* cu_seqlens, int B, int T, int H, int Dk, int Dv,
+                          int num_seqs, int chunk, kda_dtype in_dtype, kda_dtype out_dtype, void* o, float* S_final,
+                          void* workspace, size_t workspace_bytes, kda_stream_t stream, bool scalar_gate) {
     if (B < 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || num_seqs < 0) return KDA_ERR_INVALID_ARGUMENT;
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_UNSUPPORTED;
     if (!head_ok(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
     if (!kda::chunk_supported(chunk)) return KDA_ERR_UNSUPPORTED;
+    if (scalar_gate && chunk != 0 && chunk != 32) return KDA_ERR_UNSUPPORTED;
     if (cu_seqlens) {
         if (B != 1) return KDA_ERR_INVALID_ARGUMENT;
         if (!aligned16(cu_seqlens)) return KDA_ERR_INVALID_ARGUMENT;
@@ -78,11 +82,12 @@ extern "C" kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
 
     const size_t ein = elem_size(in_dtype), eout = elem_size(out_dtype);
     const size_t n_qk = tokens * H * Dk * ein, n_v = tokens * H * Dv * ein, n_b = tokens * H * ein;
+    const size_t n_g = scalar_gate ? n_b : n_qk;
     const size_t n_o = tokens * H * Dv * eout;
     const size_t n_s = static_cast<size_t>(num_seqs) * H * Dk * Dv * sizeof(float);
     if (tokens > 0) {
         const void* ins[5] = {q, k, v, log_alpha, beta};
-        const size_t nin[5] = {n_qk, n_qk, n_v, n_qk, n_b};
+        const size_t nin[5] = {n_qk, n_qk, n_v, n_g, n_b};
         for (int i = 0; i < 5; ++i)
             if (overlap(ins[i], nin[i], o, n_o) || overlap(ins[i], nin[i], S_final, n_s))
                 return KDA_ERR_INVALID_ARGUMENT;
@@ -104,7 +109,7 @@ extern "C" kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
         if (units > 0x7fffffffu) return KDA_ERR_UNSUPPORTED;
         hipError_t err = kda::launch_recurrent_fwd(Dk, in_dtype == KDA_BF16, out_dtype == KDA_BF16, q, k, v,
                                                    log_alpha, beta, S0, nullptr, T, H, static_cast<int>(units), o,
-                                                   S_final, reinterpret_cast<hipStream_t>(stream));
+                                                   S_final, reinterpret_cast<hipStream_t>(stream), scalar_gate);
         return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
     }
     kda::PrefillArgs a;
@@ -112,16 +117,16 @@ extern "C" kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
     a.S0 = S0; a.cu = cu_seqlens; a.o = o; a.S_final = S_final;
     a.B = B; a.T = T; a.H = H; a.D = Dk; a.N = num_seqs;
     a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = out_dtype == KDA_BF16;
+    a.scalar_gate = scalar_gate;
     a.workspace = workspace;
     hipError_t err = kda::launch_prefill(a, plan, reinterpret_cast<hipStream_t>(stream));
     return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
-extern "C" kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const void* log_alpha,
-                                         const void* beta, const float* S_in, float* S_out,
-                                         int N, int H, int Dk, int Dv,
-                                         kda_dtype in_dtype, kda_dtype out_dtype,
-                                         void* o, kda_stream_t stream) {
+kda_status recurrent_step_impl(const void* q, const void* k, const void* v, const void* log_alpha,
+                               const void* beta, const float* S_in, float* S_out, int N, int H, int Dk, int Dv,
+                               kda_dtype in_dtype, kda_dtype out_dtype, void* o, kda_stream_t stream,
+                               bool scalar_gate) {
     if (N < 0 || H <= 0 || Dk <= 0 || Dv <= 0) return KDA_ERR_INVALID_ARGUMENT;
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_UNSUPPORTED;
     if (!head_ok(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
@@ -135,7 +140,8 @@ extern "C" kda_status kda_recurrent_step(const void* q, const void* k, const voi
     const size_t n_s = units * Dk * Dv * sizeof(float), n_o = units * Dv * eout;
     if (S_in != S_out && overlap(S_in, n_s, S_out, n_s)) return KDA_ERR_INVALID_ARGUMENT;
     const void* ins[5] = {q, k, v, log_alpha, beta};
-    const size_t nin[5] = {units * Dk * ein, units * Dk * ein, units * Dv * ein, units * Dk * ein, units * ein};
+    const size_t nin[5] = {units * Dk * ein, units * Dk * ein, units * Dv * ein,
+                           scalar_gate ? units * ein : units * Dk * ein, units * ein};
     for (int i = 0; i < 5; ++i)
         if (overlap(ins[i], nin[i], S_out, n_s) || overlap(ins[i], nin[i], o, n_o)) return KDA_ERR_INVALID_ARGUMENT;
     if (overlap(o, n_o, S_out, n_s) || overlap(o, n_o, S_in, n_s)) return KDA_ERR_INVALID_ARGUMENT;
@@ -143,15 +149,14 @@ extern "C" kda_status kda_recurrent_step(const void* q, const void* k, const voi
 
     hipError_t err = kda::launch_decode(Dk, in_dtype == KDA_BF16, out_dtype == KDA_BF16, q, k, v, log_alpha,
                                         beta, S_in, S_out, o, static_cast<int>(units),
-                                        reinterpret_cast<hipStream_t>(stream));
+                                        reinterpret_cast<hipStream_t>(stream), scalar_gate);
     return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
-extern "C" kda_status kda_recurrent_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
-                                        const void* beta, const float* S0, const int32_t* cu_seqlens,
-                                        int B, int T, int H, int Dk, int Dv, int num_seqs,
-                                        kda_dtype in_dtype, kda_dtype out_dtype, void* o, float* S_final,
-                                        kda_stream_t stream) {
+kda_status recurrent_fwd_impl(const void* q, const void* k, const void* v, const void* log_alpha, const void* beta,
+                              const float* S0, const int32_t* cu_seqlens, int B, int T, int H, int Dk, int Dv,
+                              int num_seqs, kda_dtype in_dtype, kda_dtype out_dtype, void* o, float* S_final,
+                              kda_stream_t stream, bool scalar_gate) {
     if (B < 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || num_seqs < 0) return KDA_ERR_INVALID_ARGUMENT;
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_UNSUPPORTED;
     if (!head_ok(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
@@ -170,11 +175,12 @@ extern "C" kda_status kda_recurrent_fwd(const void* q, const void* k, const void
     if ((S0 && !aligned16(S0)) || (S_final && !aligned16(S_final))) return KDA_ERR_INVALID_ARGUMENT;
     const size_t ein = elem_size(in_dtype), eout = elem_size(out_dtype);
     const size_t n_qk = tokens * H * Dk * ein, n_v = tokens * H * Dv * ein, n_b = tokens * H * ein;
+    const size_t n_g = scalar_gate ? n_b : n_qk;
     const size_t n_o = tokens * H * Dv * eout;
     const size_t n_s = static_cast<size_t>(num_seqs) * H * Dk * Dv * sizeof(float);
     if (tokens > 0) {
         const void* ins[5] = {q, k, v, log_alpha, beta};
-        const size_t nin[5] = {n_qk, n_qk, n_v, n_qk, n_b};
+        const size_t nin[5] = {n_qk, n_qk, n_v, n_g, n_b};
         for (int i = 0; i < 5; ++i)
             if (overlap(ins[i], nin[i], o, n_o) || overlap(ins[i], nin[i], S_final, n_s))
                 return KDA_ERR_INVALID_ARGUMENT;
@@ -188,6 +194,62 @@ extern "C" kda_status kda_recurrent_fwd(const void* q, const void* k, const void
     if (units > 0x7fffffffu) return KDA_ERR_UNSUPPORTED;
     hipError_t err = kda::launch_recurrent_fwd(Dk, in_dtype == KDA_BF16, out_dtype == KDA_BF16, q, k, v, log_alpha,
                                                beta, S0, cu_seqlens, T, H, static_cast<int>(units), o, S_final,
-                                               reinterpret_cast<hipStream_t>(stream));
+                                               reinterpret_cast<hipStream_t>(stream), scalar_gate);
     return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                                    const void* beta, const float* S0, const int32_t* cu_seqlens,
+                                    int B, int T, int H, int Dk, int Dv, int num_seqs, int chunk,
+                                    kda_dtype in_dtype, kda_dtype out_dtype, void* o, float* S_final,
+                                    void* workspace, size_t workspace_bytes, kda_stream_t stream) {
+    return chunk_fwd_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, B, T, H, Dk, Dv, num_seqs, chunk, in_dtype,
+                          out_dtype, o, S_final, workspace, workspace_bytes, stream, false);
+}
+
+extern "C" kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const void* log_alpha,
+                                         const void* beta, const float* S_in, float* S_out,
+                                         int N, int H, int Dk, int Dv,
+                                         kda_dtype in_dtype, kda_dtype out_dtype,
+                                         void* o, kda_stream_t stream) {
+    return recurrent_step_impl(q, k, v, log_alpha, beta, S_in, S_out, N, H, Dk, Dv, in_dtype, out_dtype, o, stream,
+                               false);
+}
+
+extern "C" kda_status kda_recurrent_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                                        const void* beta, const float* S0, const int32_t* cu_seqlens,
+                                        int B, int T, int H, int Dk, int Dv, int num_seqs,
+                                        kda_dtype in_dtype, kda_dtype out_dtype, void* o, float* S_final,
+                                        kda_stream_t stream) {
+    return recurrent_fwd_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, B, T, H, Dk, Dv, num_seqs, in_dtype,
+                              out_dtype, o, S_final, stream, false);
+}
+
+extern "C" kda_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                                    const void* beta, const float* S0, const int32_t* cu_seqlens,
+                                    int B, int T, int H, int Dk, int Dv, int num_seqs, int chunk,
+                                    kda_dtype in_dtype, kda_dtype out_dtype, void* o, float* S_final,
+                                    void* workspace, size_t workspace_bytes, kda_stream_t stream) {
+    return chunk_fwd_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, B, T, H, Dk, Dv, num_seqs, chunk, in_dtype,
+                          out_dtype, o, S_final, workspace, workspace_bytes, stream, true);
+}
+
+extern "C" kda_status gdn_recurrent_step(const void* q, const void* k, const void* v, const void* log_alpha,
+                                         const void* beta, const float* S_in, float* S_out,
+                                         int N, int H, int Dk, int Dv,
+                                         kda_dtype in_dtype, kda_dtype out_dtype,
+                                         void* o, kda_stream_t stream) {
+    return recurrent_step_impl(q, k, v, log_alpha, beta, S_in, S_out, N, H, Dk, Dv, in_dtype, out_dtype, o, stream,
+                               true);
+}
+
+extern "C" kda_status gdn_recurrent_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                                        const void* beta, const float* S0, const int32_t* cu_seqlens,
+                                        int B, int T, int H, int Dk, int Dv, int num_seqs,
+                                        kda_dtype in_dtype, kda_dtype out_dtype, void* o, float* S_final,
+                                        kda_stream_t stream) {
+    return recurrent_fwd_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, B, T, H, Dk, Dv, num_seqs, in_dtype,
+                              out_dtype, o, S_final, stream, true);
 }

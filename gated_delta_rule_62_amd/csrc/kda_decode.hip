@@ -37,7 +37,8 @@ __device__ __forceinline__ void store_stream(float4* p, float4 x) {
     __builtin_nontemporal_store(vf4{x.x, x.y, x.z, x.w}, reinterpret_cast<vf4*>(p));
 }
 
-template <int D, typename IN, bool OUT_BF16>
+// SG: log_alpha is one value per (sequence, head) (the scalar gate of Gated DeltaNet).
+template <int D, typename IN, bool OUT_BF16, bool SG = false>
 __global__ __launch_bounds__(kDecodeThreads)
 void decode_step_kernel(const typename IN::storage* __restrict__ q,
                         const typename IN::storage* __restrict__ k,
@@ -71,7 +72,7 @@ void decode_step_kernel(const typename IN::storage* __restrict__ q,
     if (t < D) {
         float kk = IN::to_f32(k[vec + t]);
         float qq = IN::to_f32(q[vec + t]);
-        s_alpha[t] = fast_exp(IN::to_f32(log_alpha[vec + t]));
+        s_alpha[t] = fast_exp(IN::to_f32(SG ? log_alpha[unit] : log_alpha[vec + t]));
         s_k[t] = kk;
         s_q[t] = qq;
         kq = kk * qq;
@@ -181,7 +182,7 @@ __device__ __forceinline__ float wave_sum_lane63(float x) {
     return x;
 }
 
-template <int D, typename IN, bool OUT_BF16>
+template <int D, typename IN, bool OUT_BF16, bool SG = false>
 __global__ __launch_bounds__(2 * D)
 void recurrent_fwd_kernel(RecArgs a) {
     using ST = typename IN::storage;
@@ -233,7 +234,7 @@ void recurrent_fwd_kernel(RecArgs a) {
         Tok x;
         x.q = qp[base + c];
         x.k = kp[base + c];
-        x.g = gp[base + c];
+        x.g = SG ? gp[static_cast<size_t>(tc) * H + h] : gp[base + c];
         x.v = vp[base + j];
         x.b = bp[static_cast<size_t>(tc) * H + h];
         return x;
@@ -345,22 +346,23 @@ void recurrent_fwd_kernel(RecArgs a) {
     }
 }
 
-template <int D, typename IN, bool OUT_BF16>
+template <int D, typename IN, bool OUT_BF16, bool SG>
 static hipError_t launch_recurrent_t(const RecArgs& a, int units, hipStream_t stream) {
-    hipLaunchKernelGGL((recurrent_fwd_kernel<D, IN, OUT_BF16>), dim3(units), dim3(2 * D), 0, stream, a);
+    hipLaunchKernelGGL((recurrent_fwd_kernel<D, IN, OUT_BF16, SG>), dim3(units), dim3(2 * D), 0, stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_recurrent_fwd(int D, bool in_bf16, bool out_bf16, const void* q, const void* k,
                                 const void* v, const void* g, const void* b, const float* S0,
                                 const int32_t* cu, int T, int H, int units, void* o, float* S_final,
-                                hipStream_t stream) {
+                                hipStream_t stream, bool scalar_gate) {
     RecArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = b;
     a.S0 = S0; a.cu = cu; a.o = o; a.S_final = S_final; a.T = T; a.H = H;
 #define KDA_REC_CASE(DD, INT, OB)                                                          \
     if (D == DD && in_bf16 == std::is_same<INT, BF16>::value && out_bf16 == OB)              \
-        return launch_recurrent_t<DD, INT, OB>(a, units, stream);
+        return scalar_gate ? launch_recurrent_t<DD, INT, OB, true>(a, units, stream)               \
+                           : launch_recurrent_t<DD, INT, OB, false>(a, units, stream);
     KDA_REC_CASE(128, BF16, true)
     KDA_REC_CASE(128, BF16, false)
     KDA_REC_CASE(128, F32, true)
@@ -373,12 +375,12 @@ hipError_t launch_recurrent_fwd(int D, bool in_bf16, bool out_bf16, const void* 
     return hipErrorInvalidValue;
 }
 
-template <int D, typename IN, bool OUT_BF16>
+template <int D, typename IN, bool OUT_BF16, bool SG>
 static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const void* g,
                                   const void* b, const float* S_in, float* S_out, void* o,
                                   int units, hipStream_t stream) {
     using T = typename IN::storage;
-    hipLaunchKernelGGL((decode_step_kernel<D, IN, OUT_BF16>), dim3(units), dim3(kDecodeThreads), 0, stream,
+    hipLaunchKernelGGL((decode_step_kernel<D, IN, OUT_BF16, SG>), dim3(units), dim3(kDecodeThreads), 0, stream,
                        static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
                        static_cast<const T*>(g), static_cast<const T*>(b), S_in, S_out, o);
     return hipGetLastError();
@@ -387,10 +389,11 @@ static hipError_t launch_decode_t(const void* q, const void* k, const void* v, c
 // Host-side dispatch over the built variants; arguments already validated.
 hipError_t launch_decode(int D, bool in_bf16, bool out_bf16, const void* q, const void* k,
                          const void* v, const void* g, const void* b, const float* S_in,
-                         float* S_out, void* o, int units, hipStream_t stream) {
+                         float* S_out, void* o, int units, hipStream_t stream, bool scalar_gate) {
 #define KDA_DECODE_CASE(DD, INT, OB)                                                        \
     if (D == DD && in_bf16 == std::is_same<INT, BF16>::value && out_bf16 == OB)               \
-        return launch_decode_t<DD, INT, OB>(q, k, v, g, b, S_in, S_out, o, units, stream);
+        return scalar_gate ? launch_decode_t<DD, INT, OB, true>(q, k, v, g, b, S_in, S_out, o, units, stream) \
+                           : launch_decode_t<DD, INT, OB, false>(q, k, v, g, b, S_in, S_out, o, units, stream);
     KDA_DECODE_CASE(128, BF16, true)
     KDA_DECODE_CASE(128, BF16, false)
     KDA_DECODE_CASE(128, F32, true)

@@ -43,6 +43,7 @@ struct PrefillArgs {
     void* workspace;
     int B, T, H, D, N;
     bool in_bf16, out_bf16;
+    bool scalar_gate = false;   // log_alpha is [B, T, H] (one decay per token and head)
 };
 
 PrefillPlan plan_prefill(int B, int T, int H, int D, int N, bool varlen, int chunk);
@@ -50,11 +51,11 @@ hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan, hipStre
 
 hipError_t launch_decode(int D, bool in_bf16, bool out_bf16, const void* q, const void* k,
                          const void* v, const void* g, const void* b, const float* S_in,
-                         float* S_out, void* o, int units, hipStream_t stream);
+                         float* S_out, void* o, int units, hipStream_t stream, bool scalar_gate);
 
 hipError_t launch_recurrent_fwd(int D, bool in_bf16, bool out_bf16, const void* q, const void* k,
                                 const void* v, const void* g, const void* b, const float* S0,
                                 const int32_t* cu, int T, int H, int units, void* o, float* S_final,
-                                hipStream_t stream);
+                                hipStream_t stream, bool scalar_gate);
 
 }  // namespace kda

@@ -794,6 +794,8 @@ struct alignas(16) PBuf {
     u16 p[NQ][PE];              // P = Tril(Qbar Ktil^T)       [token][kperm(token)]
     u16 vt[VLDS ? D * K::C : 8];    // V^T (bf16)              [column][token]
     float beta[K::C];
+    float fv[K::C];             // scalar gate: e^{b_m - b_r} (scales V rows)
+    float fo[K::C];             // scalar gate: e^{b_r - b_m} (scales O rows)
     float em[D];                // e^{b_m}
     float rho[D];               // e^{b_m} of the next chunk times e^{b_n - b_m} (1 after the last)
 };
@@ -804,7 +806,15 @@ struct PSmem {
     float a[2][16][20];         // diagonal 16x16 blocks of A (fp32), producer-private
 };
 
-template <int D, typename IN, bool OUT_BF16, int MODE>
+// SG (scalar gate): log_alpha is one value per (token, head), [B, T, H] -- the gated delta
+// rule of Gated DeltaNet.  With f_r = e^{b_r - b_m} a scalar per token, the decay factors move
+// off the contractions: A = StrictTril(Diag(beta) K K^T) and P = Tril(Q K^T) carry no decay,
+// and with U' = Diag(1/f) Unew, S~ = e^{b_m} S,
+//     U' = (I + A)^{-1} Diag(beta) (Diag(1/f) V - K S~),   O = Diag(f) (Q S~ + P U'),
+//     S~ <- rho (S~ + K^T U'),   rho = e^{b_m'} e^{b_n - b_m} (a scalar).
+// With bf16 inputs K and Q are exact MFMA operands, so every product that has them on one side
+// needs two MFMAs (or one) instead of three, and the producer has no per-element decay.
+template <int D, typename IN, bool OUT_BF16, int MODE, bool SG = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(PCfg<D, MODE>::NT, PCfg<D, MODE>::NT),
                           amdgpu_waves_per_eu(PCfg<D, MODE>::WPE, PCfg<D, MODE>::WPE)))
 void pipe_kernel(KernelArgs a) {
@@ -816,6 +826,8 @@ void pipe_kernel(KernelArgs a) {
     using quad = typename R::quad;
     using elem = typename R::elem;
     constexpr bool VLDS = std::is_same<IN, BF16>::value;
+    // scalar gate with bf16 inputs: K and Q are exact bf16 MFMA operands (no low parts)
+    constexpr bool EXACT = SG && std::is_same<IN, BF16>::value;
     using Buf = PBuf<D, MODE, VLDS>;
 
     __shared__ PSmem<D, MODE, VLDS> sm;
@@ -872,6 +884,7 @@ void pipe_kernel(KernelArgs a) {
 
     // ================================================================ producer state
     quad pk[TPG], pq[TPG], pg[TPG], pvq[TPG];
+    elem pgs[TPG];   // scalar gate: log_alpha of this lane's tokens
     elem pb = 0;
     uint2 kth[TPG], ktl[TPG];   // split Ktil_m words, kept from interval 1 for Ktil_m^T in interval 3
     float enm[4] = {1.f, 1.f, 1.f, 1.f};   // e^{b_n - b_m} of the chunk last produced
@@ -892,7 +905,10 @@ void pipe_kernel(KernelArgs a) {
         for (int i = 0; i < TPG; ++i) {
             const unsigned off = static_cast<unsigned>(min(tg * TPG + i, last) * HD + c4) * sizeof(ST);
             if (part != 1) {
-                pg[i] = *reinterpret_cast<const quad*>(gp + off);
+                if constexpr (SG)
+                    pgs[i] = static_cast<const ST*>(a.g)[static_cast<size_t>(ts + min(tg * TPG + i, last)) * H + h];
+                else
+                    pg[i] = *reinterpret_cast<const quad*>(gp + off);
                 pk[i] = *reinterpret_cast<const quad*>(kp + off);
             }
             if (part != 0) {
@@ -903,11 +919,95 @@ void pipe_kernel(KernelArgs a) {
         if (part != 0 && tid < C) pb = static_cast<const ST*>(a.beta)[static_cast<size_t>(ts + min(tid, last)) * H + h];
     };
 
+    // V^T staged in LDS for the consumers (bf16 inputs)
+    auto stage_v = [&](Buf& B) {
+        if constexpr (VLDS) {
+            // V^T: channel ch of token i is the low (even ch) or high (odd ch) half of word ch / 2
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) {
+                const unsigned sel = (ch & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+                for (int gq = 0; gq < TPG / 4; ++gq) {
+                    const int t = 4 * gq;
+                    const uint32_t w0 = ch < 2 ? pvq[t].x : pvq[t].y, w1 = ch < 2 ? pvq[t + 1].x : pvq[t + 1].y;
+                    const uint32_t w2 = ch < 2 ? pvq[t + 2].x : pvq[t + 2].y, w3 = ch < 2 ? pvq[t + 3].x : pvq[t + 3].y;
+                    *reinterpret_cast<uint2*>(&B.vt[K::chm(c4 + ch, tg * TPG + t)]) =
+                        uint2{__builtin_amdgcn_perm(w1, w0, sel), __builtin_amdgcn_perm(w3, w2, sel)};
+                }
+            }
+        }
+    };
+
     // interval 1: decay prefix (in log2 units) and the decayed, split K / Q planes.  With
     // the previous chunk's buffer `prev`, also that chunk's state factor rho.
     auto produce_decay = [&](Buf& B, int chunk, Buf* prev) {
         const long ts = t0 + static_cast<long>(chunk) * C;
         const int last = static_cast<int>(min(static_cast<long>(C), t1 - ts)) - 1;
+        if constexpr (SG) {
+            // scalar gate: decay prefix of the chunk's tokens, the per-token factors f and 1/f,
+            // and K, Q as they are (split into hi / lo only for fp32 inputs)
+            if (last < C - 1) {
+#pragma unroll
+                for (int i = 0; i < TPG; ++i)
+                    if (tg * TPG + i > last) {
+                        pk[i] = pq[i] = quad{};
+                        pgs[i] = elem{};
+                    }
+                if (tid > last) pb = elem{};
+            }
+            float gs[TPG];
+#pragma unroll
+            for (int i = 0; i < TPG; ++i) gs[i] = IN::to_f32(pgs[i]) * kLog2e + (i ? gs[i - 1] : 0.f);
+            float incl = gs[TPG - 1];
+#pragma unroll
+            for (int dd = 8; dd < 64; dd <<= 1) {
+                const float y = __shfl_up(incl, dd);
+                incl += l >= dd ? y : 0.f;
+            }
+            const float bm = __shfl(incl, 24), bn = __shfl(incl, 56);
+            const float off = incl - gs[TPG - 1] - bm;   // b_r - b_m = gs + off
+            if (tg == 0) {
+                const float em = exp2f_hw(bm);
+#pragma unroll
+                for (int ch = 0; ch < 4; ++ch) {
+                    B.em[c4 + ch] = em;
+                    if (prev) prev->rho[c4 + ch] = em * enm[0];
+                }
+            }
+            const float en = exp2f_hw(bn - bm);
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) enm[ch] = en;
+            if (w == 0 && (l & 7) == 0) {
+#pragma unroll
+                for (int i = 0; i < TPG; ++i) {
+                    const float b = gs[i] + off;
+                    B.fo[tg * TPG + i] = exp2f_hw(b);
+                    B.fv[tg * TPG + i] = exp2f_hw(-b);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < TPG; ++i) {
+                const int idx = K::tok(tg * TPG + i, kperm(c4));
+                if constexpr (EXACT) {
+                    *reinterpret_cast<quad*>(&B.kb[0][idx]) = pk[i];
+                    kth[i] = pk[i];
+                    if constexpr (MODE == 0) *reinterpret_cast<quad*>(&B.qb[0][idx]) = pq[i];
+                } else {
+                    uint2 hi, lo;
+                    split_quad(R::get(pk[i], 0), R::get(pk[i], 1), R::get(pk[i], 2), R::get(pk[i], 3), kth[i], ktl[i]);
+                    *reinterpret_cast<uint2*>(&B.kb[0][idx]) = kth[i];
+                    *reinterpret_cast<uint2*>(&B.kb[1][idx]) = ktl[i];
+                    if constexpr (MODE == 0) {
+                        split_quad(R::get(pq[i], 0), R::get(pq[i], 1), R::get(pq[i], 2), R::get(pq[i], 3), hi, lo);
+                        *reinterpret_cast<uint2*>(&B.qb[0][idx]) = hi;
+                        *reinterpret_cast<uint2*>(&B.qb[1][idx]) = lo;
+                    }
+                }
+            }
+            stage_v(B);
+            if (tid < C) B.beta[tid] = IN::to_f32(pb);
+            return;
+        }
         if (last < C - 1) {   // ragged last chunk: padded rows read as zero
 #pragma unroll
             for (int i = 0; i < TPG; ++i)
@@ -973,21 +1073,7 @@ void pipe_kernel(KernelArgs a) {
                 *reinterpret_cast<uint2*>(&B.qb[1][idx]) = lo;
             }
         }
-        if constexpr (VLDS) {
-            // V^T: channel ch of token i is the low (even ch) or high (odd ch) half of word ch / 2
-#pragma unroll
-            for (int ch = 0; ch < 4; ++ch) {
-                const unsigned sel = (ch & 1) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-                for (int gq = 0; gq < TPG / 4; ++gq) {
-                    const int t = 4 * gq;
-                    const uint32_t w0 = ch < 2 ? pvq[t].x : pvq[t].y, w1 = ch < 2 ? pvq[t + 1].x : pvq[t + 1].y;
-                    const uint32_t w2 = ch < 2 ? pvq[t + 2].x : pvq[t + 2].y, w3 = ch < 2 ? pvq[t + 3].x : pvq[t + 3].y;
-                    *reinterpret_cast<uint2*>(&B.vt[K::chm(c4 + ch, tg * TPG + t)]) =
-                        uint2{__builtin_amdgcn_perm(w1, w0, sel), __builtin_amdgcn_perm(w3, w2, sel)};
-                }
-            }
-        }
+        stage_v(B);
         if (tid < C) B.beta[tid] = IN::to_f32(pb);
     };
 
@@ -1009,7 +1095,12 @@ void pipe_kernel(KernelArgs a) {
             for (int ks = 0; ks < KS; ++ks) {
                 const int ao = K::tok(16 * ct + lr, 32 * ks + 8 * g4);
                 const int bo = K::tok(16 * rt + lr, 32 * ks + 8 * g4);
-                acc = mfma3(frag(&B.kt[0][ao]), frag(&B.kt[1][ao]), frag(&B.kb[0][bo]), frag(&B.kb[1][bo]), acc);
+                if constexpr (EXACT)
+                    acc = mfma(frag(&B.kb[0][ao]), frag(&B.kb[0][bo]), acc);
+                else if constexpr (SG)
+                    acc = mfma3(frag(&B.kb[0][ao]), frag(&B.kb[1][ao]), frag(&B.kb[0][bo]), frag(&B.kb[1][bo]), acc);
+                else
+                    acc = mfma3(frag(&B.kt[0][ao]), frag(&B.kt[1][ao]), frag(&B.kb[0][bo]), frag(&B.kb[1][bo]), acc);
             }
             const int row = 16 * rt + lr;
             const float br = B.beta[row];
@@ -1038,7 +1129,12 @@ void pipe_kernel(KernelArgs a) {
                 for (int ks = 0; ks < KS; ++ks) {
                     const int ao = K::tok(16 * ct + lr, 32 * ks + 8 * g4);
                     const int bo = K::tok(16 * rt + lr, 32 * ks + 8 * g4);
-                    acc = mfma3(frag(&B.kt[0][ao]), frag(&B.kt[1][ao]), frag(&B.qb[0][bo]), frag(&B.qb[1][bo]), acc);
+                    if constexpr (EXACT)
+                        acc = mfma(frag(&B.kb[0][ao]), frag(&B.qb[0][bo]), acc);
+                    else if constexpr (SG)
+                        acc = mfma3(frag(&B.kb[0][ao]), frag(&B.kb[1][ao]), frag(&B.qb[0][bo]), frag(&B.qb[1][bo]), acc);
+                    else
+                        acc = mfma3(frag(&B.kt[0][ao]), frag(&B.kt[1][ao]), frag(&B.qb[0][bo]), frag(&B.qb[1][bo]), acc);
                 }
                 f32x4 pv4;
 #pragma unroll
@@ -1074,7 +1170,7 @@ void pipe_kernel(KernelArgs a) {
                 lo.y = __builtin_amdgcn_perm(l3, l2, sel);
                 const int idx = K::chm(c, kperm(tg * TPG + t));
                 *reinterpret_cast<uint2*>(&B.kt[0][idx]) = hi;
-                *reinterpret_cast<uint2*>(&B.kt[1][idx]) = lo;
+                if constexpr (!EXACT) *reinterpret_cast<uint2*>(&B.kt[1][idx]) = lo;
             }
         }
         if (solver) {
@@ -1180,15 +1276,27 @@ void pipe_kernel(KernelArgs a) {
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt) {
                 const int ao = K::tok(16 * rt + lr, 32 * ks + 8 * g4);
-                const bf16x8 kh = frag(&B.kb[0][ao]), kl = frag(&B.kb[1][ao]);
+                if constexpr (EXACT) {
+                    const bf16x8 kh = frag(&B.kb[0][ao]);
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct) Y[rt][ct] = mfma3(kh, kl, sbh[ct], sbl[ct], Y[rt][ct]);
+                    for (int ct = 0; ct < CT; ++ct) Y[rt][ct] = mfma(kh, sbh[ct], mfma(kh, sbl[ct], Y[rt][ct]));
+                } else {
+                    const bf16x8 kh = frag(&B.kb[0][ao]), kl = frag(&B.kb[1][ao]);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) Y[rt][ct] = mfma3(kh, kl, sbh[ct], sbl[ct], Y[rt][ct]);
+                }
                 if constexpr (MODE == 0) {
                     // Z^T = St^T Qbar_m^T: the split state serves as the A operand,
                     // so lane (g4, lr) ends up with token 16 rt + lr, columns 16 ct + 4 g4 + e
-                    const bf16x8 qh = frag(&B.qb[0][ao]), ql = frag(&B.qb[1][ao]);
+                    if constexpr (EXACT) {
+                        const bf16x8 qh = frag(&B.qb[0][ao]);
 #pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) Z[rt][ct] = mfma3(sbh[ct], sbl[ct], qh, ql, Z[rt][ct]);
+                        for (int ct = 0; ct < CT; ++ct) Z[rt][ct] = mfma(sbh[ct], qh, mfma(sbl[ct], qh, Z[rt][ct]));
+                    } else {
+                        const bf16x8 qh = frag(&B.qb[0][ao]), ql = frag(&B.qb[1][ao]);
+#pragma unroll
+                        for (int ct = 0; ct < CT; ++ct) Z[rt][ct] = mfma3(sbh[ct], sbl[ct], qh, ql, Z[rt][ct]);
+                    }
                 }
             }
         }
@@ -1207,6 +1315,9 @@ void pipe_kernel(KernelArgs a) {
                 } else if (!is_phi) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) vv[e] = IN::to_f32(pv[rt][ct][e]);
+                }
+                if constexpr (SG) {
+                    if (!is_phi) vv *= *reinterpret_cast<const f32x4*>(&B.fv[16 * rt + 4 * g4]);
                 }
                 Y[rt][ct] = vv - Y[rt][ct];
             }
@@ -1266,9 +1377,15 @@ void pipe_kernel(KernelArgs a) {
         for (int rt = 0; rt < RT; ++rt) {
             const f32x4 rh = *reinterpret_cast<const f32x4*>(&B.rho[16 * rt + 4 * g4]);
             const int ao = K::chm(16 * rt + lr, 8 * g4);
-            const bf16x8 kh = frag(&B.kt[0][ao]), kl = frag(&B.kt[1][ao]);
+            if constexpr (EXACT) {
+                const bf16x8 kh = frag(&B.kt[0][ao]);
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) S[rt][ct] = mfma3(kh, kl, ubh[ct], ubl[ct], S[rt][ct]) * rh;
+                for (int ct = 0; ct < CT; ++ct) S[rt][ct] = mfma(kh, ubh[ct], mfma(kh, ubl[ct], S[rt][ct])) * rh;
+            } else {
+                const bf16x8 kh = frag(&B.kt[0][ao]), kl = frag(&B.kt[1][ao]);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) S[rt][ct] = mfma3(kh, kl, ubh[ct], ubl[ct], S[rt][ct]) * rh;
+            }
         }
         if constexpr (MODE == 0) {
             const long ts = t0 + static_cast<long>(chunk) * C;
@@ -1279,9 +1396,11 @@ void pipe_kernel(KernelArgs a) {
             for (int rt = 0; rt < NRT; ++rt) {
                 const int row = 16 * rt + lr;
                 if (row < ntok) {
+                    float fo = 1.f;
+                    if constexpr (SG) fo = B.fo[row];
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct)
-                        store_out4<OUT_BF16>(a.o, obase + static_cast<unsigned>(row * HD + 16 * ct), Z[rt][ct]);
+                        store_out4<OUT_BF16>(a.o, obase + static_cast<unsigned>(row * HD + 16 * ct), Z[rt][ct] * fo);
                 }
             }
         }
@@ -1415,8 +1534,9 @@ __global__ __launch_bounds__(256) void order_kernel(const int32_t* __restrict__ 
     order[rank] = i;
 }
 
-template <int D, int C, typename IN, bool OB>
+template <int D, int C, typename IN, bool OB, bool SG = false>
 hipError_t launch_variant(const PrefillArgs& pa, const PrefillPlan& plan, hipStream_t stream) {
+    static_assert(!SG || C == 32, "the scalar gate runs on the pipelined 32-token kernel");
     KernelArgs a;
     a.q = pa.q; a.k = pa.k; a.v = pa.v; a.g = pa.g; a.beta = pa.beta;
     a.S0 = pa.S0; a.cu = pa.cu; a.o = pa.o; a.S_final = pa.S_final;
@@ -1432,9 +1552,9 @@ hipError_t launch_variant(const PrefillArgs& pa, const PrefillPlan& plan, hipStr
     auto pass = [&](int mode, int grid) {
         if constexpr (C == 32) {
             if (mode == 0)
-                hipLaunchKernelGGL((pipe_kernel<D, IN, OB, 0>), dim3(grid), dim3(PCfg<D, 0>::NT), 0, stream, a);
+                hipLaunchKernelGGL((pipe_kernel<D, IN, OB, 0, SG>), dim3(grid), dim3(PCfg<D, 0>::NT), 0, stream, a);
             else
-                hipLaunchKernelGGL((pipe_kernel<D, IN, OB, 1>), dim3(grid), dim3(PCfg<D, 1>::NT), 0, stream, a);
+                hipLaunchKernelGGL((pipe_kernel<D, IN, OB, 1, SG>), dim3(grid), dim3(PCfg<D, 1>::NT), 0, stream, a);
         } else {
             if (mode == 0)
                 hipLaunchKernelGGL((chunk_kernel<D, C, IN, OB, 0>), dim3(grid), dim3(Cfg<D, C, 0>::NT), 0, stream, a);
@@ -1495,8 +1615,13 @@ PrefillPlan plan_prefill(int B, int T, int H, int D, int N, bool varlen, int chu
 
 hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan, hipStream_t stream) {
 #define KDA_PREFILL_CASE(DD, CC, INT, OB)                                                              \
-    if (a.D == DD && plan.chunk == CC && a.in_bf16 == std::is_same<INT, BF16>::value && a.out_bf16 == OB) \
-        return launch_variant<DD, CC, INT, OB>(a, plan, stream);
+    if (a.D == DD && plan.chunk == CC && a.in_bf16 == std::is_same<INT, BF16>::value && a.out_bf16 == OB) { \
+        if (a.scalar_gate) {                                                                           \
+            if constexpr (CC == 32) return launch_variant<DD, CC, INT, OB, true>(a, plan, stream);      \
+            return hipErrorInvalidValue;                                                               \
+        }                                                                                              \
+        return launch_variant<DD, CC, INT, OB>(a, plan, stream);                                       \
+    }
 #define KDA_PREFILL_D(DD, CC)              \
     KDA_PREFILL_CASE(DD, CC, BF16, true)   \
     KDA_PREFILL_CASE(DD, CC, BF16, false)  \

@@ -16,6 +16,8 @@ Workloads (the five shapes the layer is measured and checked on):
   5  continuation           256 sequences of U{1..32} new tokens each on top of a carried
                             state (speculative verification / chunked continuation),
                             packed, H=32, d=128, bf16, S0 ~ 0.02*N(0,1)
+  6  scalar-gate prefill    workload 2's shape with one decay per (token, head) (Gated
+                            DeltaNet): log_alpha [B, T, H] = logsigmoid(N(0,1) + 6) / 16
 
 Distributions: q, k ~ N(0,1) then L2-normalised per (token, head); v ~ N(0,1);
 beta = sigmoid(N(0,1)); log_alpha = logsigmoid(N(0,1) + mu) / s per channel with
@@ -54,6 +56,7 @@ class Workload:
     len_range: tuple = ()     # varlen length bounds (inclusive)
     steps: int = 0            # decode steps
     chunk: int = 64
+    scalar_gate: bool = False # log_alpha drawn [B, T, H] (one decay per token and head)
     extra: dict = field(default_factory=dict)
 
     @property
@@ -71,6 +74,8 @@ WORKLOADS = {
                 num_seqs=64, len_range=(512, 16384)),
     5: Workload(5, "continuation", "prefill", H=32, D=128, s0=True,
                 num_seqs=256, len_range=(1, 32)),
+    6: Workload(6, "gdn_long_context_prefill", "prefill", B=1, T=65536, H=32, D=128,
+                mu=6.0, s=16.0, s0=True, scalar_gate=True),
 }
 
 
@@ -117,7 +122,7 @@ def _normal(rng, shape):
 # ---------------------------------------------------------------- prefill
 def make_prefill(w: Workload, seed: int | None = None, *, B=None, T=None, H=None, D=None,
                  num_seqs=None, len_range=None, s0=None, dtype=None, mu=None, s=None,
-                 mix=None, lengths=None):
+                 mix=None, lengths=None, scalar_gate=None):
     """Draw one prefill batch.  Keyword overrides shrink a workload for tests while
     keeping its recipe.  Returns a dict with q, k, v, log_alpha, beta (float32 or
     bf16 bits), S0 (float32 [N, H, D, D] or None), cu_seqlens (int32 [N+1] or None),
@@ -131,6 +136,7 @@ def make_prefill(w: Workload, seed: int | None = None, *, B=None, T=None, H=None
     s = w.s if s is None else s
     mix = w.mix if mix is None else mix
     s0 = w.s0 if s0 is None else s0
+    scalar_gate = w.scalar_gate if scalar_gate is None else scalar_gate
     varlen = bool(w.len_range) or lengths is not None or num_seqs is not None and len_range is not None
     if varlen:
         if lengths is None:
@@ -150,16 +156,17 @@ def make_prefill(w: Workload, seed: int | None = None, *, B=None, T=None, H=None
     k = _l2n(_normal(rng, shp))
     v = _normal(rng, shp)
     beta = _sigmoid(_normal(rng, (B, T, H)))
-    g = _logsigmoid(_normal(rng, shp) + np.float32(mu)) / np.float32(s)
+    gshp = (B, T, H) if scalar_gate else shp
+    g = _logsigmoid(_normal(rng, gshp) + np.float32(mu)) / np.float32(s)
     if mix:
-        g_fast = _logsigmoid(_normal(rng, shp)) / np.float32(2.0)
-        pick = rng.random(shp, dtype=np.float32) < 0.5
+        g_fast = _logsigmoid(_normal(rng, gshp)) / np.float32(2.0)
+        pick = rng.random(gshp, dtype=np.float32) < 0.5
         g = np.where(pick, g_fast, g)
     S0 = (np.float32(0.02) * _normal(rng, (N, H, D, D))) if s0 else None
     return dict(q=_cast(q, dtype), k=_cast(k, dtype), v=_cast(v, dtype),
                 log_alpha=_cast(g, dtype), beta=_cast(beta, dtype), S0=S0,
                 cu_seqlens=None if cu is None else cu.astype(np.int32),
-                B=B, T=T, H=H, D=D, N=N, dtype=dtype)
+                B=B, T=T, H=H, D=D, N=N, dtype=dtype, scalar_gate=scalar_gate)
 
 
 # ---------------------------------------------------------------- decode
@@ -169,7 +176,7 @@ class DecodeStream:
     on the host at once)."""
 
     def __init__(self, w: Workload, seed: int | None = None, *, num_seqs=None, H=None, D=None,
-                 dtype=None, mu=None, s=None):
+                 dtype=None, mu=None, s=None, scalar_gate=False):
         self.rng = np.random.default_rng(w.seed if seed is None else seed)
         self.N = w.num_seqs if num_seqs is None else num_seqs
         self.H = w.H if H is None else H
@@ -177,6 +184,7 @@ class DecodeStream:
         self.dtype = w.dtype if dtype is None else dtype
         self.mu = w.mu if mu is None else mu
         self.s = w.s if s is None else s
+        self.scalar_gate = scalar_gate
         self._S0 = np.float32(0.02) * _normal(self.rng, (self.N, self.H, self.D, self.D))
 
     def state(self) -> np.ndarray:
@@ -188,7 +196,8 @@ class DecodeStream:
         k = _l2n(_normal(self.rng, shp))
         v = _normal(self.rng, shp)
         beta = _sigmoid(_normal(self.rng, (self.N, self.H)))
-        g = _logsigmoid(_normal(self.rng, shp) + np.float32(self.mu)) / np.float32(self.s)
+        gshp = (self.N, self.H) if self.scalar_gate else shp
+        g = _logsigmoid(_normal(self.rng, gshp) + np.float32(self.mu)) / np.float32(self.s)
         dt = self.dtype
         return dict(q=_cast(q, dt), k=_cast(k, dt), v=_cast(v, dt), log_alpha=_cast(g, dt),
                     beta=_cast(beta, dt))
@@ -232,17 +241,18 @@ def device_prefill(w: Workload, seed: int | None = None, device="cuda", *, lengt
     k = F.normalize(normal(shp), dim=-1).to(dt)
     v = normal(shp).to(dt)
     beta = torch.sigmoid(normal((B, T, H))).to(dt)
-    la = F.logsigmoid(normal(shp) + w.mu) / w.s
+    gshp = (B, T, H) if w.scalar_gate else shp
+    la = F.logsigmoid(normal(gshp) + w.mu) / w.s
     if w.mix:
-        fast = F.logsigmoid(normal(shp)) / 2.0
-        pick = torch.rand(shp, device=device, generator=g) < 0.5
+        fast = F.logsigmoid(normal(gshp)) / 2.0
+        pick = torch.rand(gshp, device=device, generator=g) < 0.5
         la = torch.where(pick, fast, la)
         del fast, pick
     la = la.to(dt)
     S0 = 0.02 * normal((N, H, D, D)) if w.s0 else None
     return dict(q=q, k=k, v=v, log_alpha=la, beta=beta, S0=S0,
                 cu_seqlens=None if cu is None else torch.tensor(cu, dtype=torch.int32, device=device),
-                cu_host=cu, B=B, T=T, H=H, D=D, N=N, dtype=w.dtype)
+                cu_host=cu, B=B, T=T, H=H, D=D, N=N, dtype=w.dtype, scalar_gate=w.scalar_gate)
 
 
 def device_decode_steps(w: Workload, steps: int, seed: int | None = None, device="cuda"):

@@ -20,7 +20,7 @@ KDA_F32, KDA_BF16 = 0, 1
 CHUNK = 0          # library default chunk length (32 tokens); 32 and 64 are built
 
 EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_step",
-            "kda_recurrent_fwd")
+            "kda_recurrent_fwd", "gdn_chunk_fwd", "gdn_recurrent_step", "gdn_recurrent_fwd")
 
 _lib = None
 
@@ -50,6 +50,13 @@ def load_library(path: str = LIB_PATH):
     lib.kda_recurrent_step.restype = i32
     lib.kda_recurrent_fwd.argtypes = [vp] * 7 + [i32] * 6 + [i32, i32] + [vp, vp, vp]
     lib.kda_recurrent_fwd.restype = i32
+    for pre in ("kda", "gdn"):
+        getattr(lib, f"{pre}_chunk_fwd").argtypes = lib.kda_chunk_fwd.argtypes
+        getattr(lib, f"{pre}_chunk_fwd").restype = i32
+        getattr(lib, f"{pre}_recurrent_step").argtypes = lib.kda_recurrent_step.argtypes
+        getattr(lib, f"{pre}_recurrent_step").restype = i32
+        getattr(lib, f"{pre}_recurrent_fwd").argtypes = lib.kda_recurrent_fwd.argtypes
+        getattr(lib, f"{pre}_recurrent_fwd").restype = i32
     _lib = lib
     return lib
 
@@ -88,7 +95,7 @@ def kda_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, num_seqs, has_cu_seqlens, chu
 
 
 def kda_chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, out_dtype=None, o=None,
-                  S_final=None, workspace=None, chunk=CHUNK, stream=None, want_final=True):
+                  S_final=None, workspace=None, chunk=CHUNK, stream=None, want_final=True, _fn="kda_chunk_fwd"):
     """Prefill.  q, k, log_alpha [B, T, H, Dk]; v [B, T, H, Dv]; beta [B, T, H]
     (one dtype: float32 or bfloat16); S0 [N, H, Dk, Dv] float32 or None;
     cu_seqlens int32 [N+1] on the GPU (B == 1) or None.  Returns (o, S_final)."""
@@ -107,17 +114,17 @@ def kda_chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, out_dty
     if workspace is None and ws_need > 0:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = load_library().kda_chunk_fwd(
+    st = getattr(load_library(), _fn)(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
         B, T, H, Dk, Dv, N, chunk, _dtype_code(q.dtype), _dtype_code(o.dtype),
         _ptr(o), _ptr(S_final), _ptr(workspace), ws_bytes, _stream_ptr(stream))
     if st != KDA_OK:
-        raise KDAError(st, "kda_chunk_fwd")
+        raise KDAError(st, _fn)
     return o, S_final
 
 
 def kda_recurrent_step(q, k, v, log_alpha, beta, S_in, S_out=None, *, out_dtype=None, o=None,
-                       stream=None):
+                       stream=None, _fn="kda_recurrent_step"):
     """Decode one token.  q, k, log_alpha [N, H, Dk]; v [N, H, Dv]; beta [N, H];
     S_in [N, H, Dk, Dv] float32; S_out defaults to S_in (in place).  Returns (o, S_out)."""
     N, H, Dk = q.shape
@@ -128,16 +135,16 @@ def kda_recurrent_step(q, k, v, log_alpha, beta, S_in, S_out=None, *, out_dtype=
     if S_out is None:
         S_out = S_in
     _check_dev(q, k, v, log_alpha, beta, S_in, S_out, o)
-    st = load_library().kda_recurrent_step(
+    st = getattr(load_library(), _fn)(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S_in), _ptr(S_out),
         N, H, Dk, Dv, _dtype_code(q.dtype), _dtype_code(o.dtype), _ptr(o), _stream_ptr(stream))
     if st != KDA_OK:
-        raise KDAError(st, "kda_recurrent_step")
+        raise KDAError(st, _fn)
     return o, S_out
 
 
 def kda_recurrent_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, out_dtype=None, o=None,
-                      S_final=None, stream=None, want_final=True):
+                      S_final=None, stream=None, want_final=True, _fn="kda_recurrent_fwd"):
     """Token-by-token forward over each sequence (the multi-token continuation of decode).
     Same tensors as kda_chunk_fwd; S_final may be S0 (in place).  Returns (o, S_final)."""
     B, T, H, Dk = q.shape
@@ -151,10 +158,24 @@ def kda_recurrent_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, out
     if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
         raise TypeError("cu_seqlens must be int32")
     _check_dev(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_final)
-    st = load_library().kda_recurrent_fwd(
+    st = getattr(load_library(), _fn)(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
         B, T, H, Dk, Dv, N, _dtype_code(q.dtype), _dtype_code(o.dtype), _ptr(o), _ptr(S_final),
         _stream_ptr(stream))
     if st != KDA_OK:
-        raise KDAError(st, "kda_recurrent_fwd")
+        raise KDAError(st, _fn)
     return o, S_final
+
+
+# Scalar-gated variant (Gated DeltaNet): log_alpha is [B, T, H] ([N, H] for a decode step);
+# everything else as in the kda_ function of the same suffix.
+def gdn_chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, **kw):
+    return kda_chunk_fwd(q, k, v, log_alpha, beta, S0, cu_seqlens, _fn="gdn_chunk_fwd", **kw)
+
+
+def gdn_recurrent_step(q, k, v, log_alpha, beta, S_in, S_out=None, **kw):
+    return kda_recurrent_step(q, k, v, log_alpha, beta, S_in, S_out, _fn="gdn_recurrent_step", **kw)
+
+
+def gdn_recurrent_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, **kw):
+    return kda_recurrent_fwd(q, k, v, log_alpha, beta, S0, cu_seqlens, _fn="gdn_recurrent_fwd", **kw)

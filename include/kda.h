@@ -137,6 +137,42 @@ kda_status kda_recurrent_fwd(const void* q, const void* k, const void* v, const 
                              kda_dtype in_dtype, kda_dtype out_dtype,
                              void* o, float* S_final, kda_stream_t stream);
 
+/*
+ * Scalar-gated variant (Gated DeltaNet): the same rule with one decay per token and
+ * head, S_t = (I - beta_t k_t k_t^T) alpha_t S_{t-1} + beta_t k_t v_t^T, alpha_t a
+ * scalar in (0, 1] ("Decoding Hybrid Attention Architectures", section 3.3 and the
+ * variant table of section 3; "Technical Analysis ...", section 2).  It is KDA with
+ * every key channel given the same decay, so each function below returns what its
+ * kda_ counterpart returns for log_alpha broadcast over the key channels.
+ *
+ *   log_alpha : [B, T, H] (gdn_chunk_fwd, gdn_recurrent_fwd) or [N, H]
+ *               (gdn_recurrent_step), in_dtype; every other argument as in the
+ *               kda_ function of the same suffix.
+ *
+ * gdn_chunk_fwd supports chunk 0 or 32 and uses kda_chunk_fwd_workspace_bytes().
+ * With a scalar decay the chunk's decay factors leave the contractions, so with
+ * bf16 inputs the keys and queries are exact MFMA operands and the prefill does
+ * about a third less matrix work and almost no per-element decay work.
+ */
+kda_status gdn_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                         const void* beta, const float* S0, const int32_t* cu_seqlens,
+                         int B, int T, int H, int Dk, int Dv, int num_seqs, int chunk,
+                         kda_dtype in_dtype, kda_dtype out_dtype,
+                         void* o, float* S_final,
+                         void* workspace, size_t workspace_bytes, kda_stream_t stream);
+
+kda_status gdn_recurrent_step(const void* q, const void* k, const void* v, const void* log_alpha,
+                              const void* beta, const float* S_in, float* S_out,
+                              int N, int H, int Dk, int Dv,
+                              kda_dtype in_dtype, kda_dtype out_dtype,
+                              void* o, kda_stream_t stream);
+
+kda_status gdn_recurrent_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                             const void* beta, const float* S0, const int32_t* cu_seqlens,
+                             int B, int T, int H, int Dk, int Dv, int num_seqs,
+                             kda_dtype in_dtype, kda_dtype out_dtype,
+                             void* o, float* S_final, kda_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

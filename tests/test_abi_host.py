@@ -28,7 +28,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:kda|gdn)_[a-z_]+)\s*\(", text)))
 
 
 def test_header_declares_the_entry_points():
