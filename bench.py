@@ -9,7 +9,8 @@ resident in HBM.
 
 The same JSON line also reports the decode workload (256 sequences x 32 heads,
 d=128, 1024 sequential ``kda_recurrent_step`` calls on an fp32 state) as
-``decode``, the scalar-gated variant (Gated DeltaNet) at the long-context shape
+``decode``, the same prefill with the fused prologue / epilogue as
+``fused_prologue``, the scalar-gated variant (Gated DeltaNet) at the long-context shape
 as ``gdn``, a few new tokens per sequence on top of a carried state as
 ``continuation``, the roofline of each path's dominant launch measured with HIP events
 on the launch stream, and the fp64 CPU oracle timed on a bounded sample of the
@@ -232,6 +233,32 @@ def main():
                      "bytes_per_launch": dbytes},
     }
 
+    # ------------------------------------------------------------------ fused prologue / epilogue
+    # The headline call with every fused step on: q, k normalised in the kernels, beta and
+    # log_alpha taken as logits (sigmoid; logsigmoid(a + 6) / 16), an output gate of N(0,1)
+    # logits (one more bf16 tensor of o's shape to read).
+    gate = torch.randn((B, T, H, d), device="cuda").to(torch.bfloat16)
+
+    def call_fused():
+        kda.kda_chunk_fwd_fused(q, k, v, la, beta, S0, None, qk_l2norm=True, beta_logits=True,
+                                decay_logits=(6.0, 16.0), out_gate=gate, o=o, S_final=Sf, workspace=ws,
+                                stream=stream)
+    for _ in range(3):
+        call_fused()
+    torch.cuda.synchronize()
+    ef0, ef1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ef0.record(stream)
+    for _ in range(args.steps):
+        call_fused()
+    ef1.record(stream)
+    torch.cuda.synchronize()
+    fused_ms = ef0.elapsed_time(ef1) / args.steps
+    fused = {"workload": "long_context_prefill with q/k L2 norm, sigmoid beta, logsigmoid decay and an output "
+                         "gate inside the kernels (kda_chunk_fwd_fused)",
+             "ms_per_call": fused_ms, "vs_plain_call": fused_ms / ms_step,
+             "tokens_per_s": tokens / (fused_ms / 1e3)}
+    del gate
+
     # ------------------------------------------------------------------ scalar gate (Gated DeltaNet)
     # Workload 2's shape with one decay per (token, head): gdn_chunk_fwd.
     w6 = inputs.WORKLOADS[6]
@@ -330,6 +357,7 @@ def main():
                      "flops_per_launch": flops},
         "cpu_baseline": cpu,
         "decode": decode,
+        "fused_prologue": fused,
         "gdn": gdn,
         "continuation": continuation,
         "wall_s": wall,

@@ -54,15 +54,38 @@ namespace {
 
 // Prefill for either decay layout: per key channel (KDA, log_alpha [B, T, H, Dk]) or one value
 // per token and head (scalar gate, log_alpha [B, T, H]).
+// Validated fusion options (nullptr when none are requested).
+bool fusion_ok(const kda_fusion* f) {
+    if (!f) return true;
+    if (f->flags & ~(KDA_FUSE_QK_L2NORM | KDA_FUSE_BETA_SIGMOID | KDA_FUSE_DECAY_LOGSIGMOID)) return false;
+    if ((f->flags & KDA_FUSE_DECAY_LOGSIGMOID) && !(f->decay_scale > 0.f && f->decay_scale < 3.0e38f)) return false;
+    if ((f->flags & KDA_FUSE_DECAY_LOGSIGMOID) && !(f->decay_bias > -3.0e38f && f->decay_bias < 3.0e38f)) return false;
+    return f->out_gate == nullptr || aligned16(f->out_gate);
+}
+
+kda::Fusion to_fusion(const kda_fusion* f) {
+    kda::Fusion x;
+    if (f) {
+        x.flags = f->flags;
+        x.decay_bias = f->decay_bias;
+        x.decay_scale = (f->flags & KDA_FUSE_DECAY_LOGSIGMOID) ? f->decay_scale : 1.f;
+        x.out_gate = f->out_gate;
+    }
+    return x;
+}
+
 kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const void* log_alpha, const void* beta,
                           const float* S0, const int32_t* cu_seqlens, int B, int T, int H, int Dk, int Dv,
                           int num_seqs, int chunk, kda_dtype in_dtype, kda_dtype out_dtype, void* o, float* S_final,
-                          void* workspace, size_t workspace_bytes, kda_stream_t stream, bool scalar_gate) {
+                          void* workspace, size_t workspace_bytes, kda_stream_t stream, bool scalar_gate,
+                          const kda_fusion* fusion = nullptr) {
     if (B < 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || num_seqs < 0) return KDA_ERR_INVALID_ARGUMENT;
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_UNSUPPORTED;
     if (!head_ok(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
     if (!kda::chunk_supported(chunk)) return KDA_ERR_UNSUPPORTED;
-    if (scalar_gate && chunk != 0 && chunk != 32) return KDA_ERR_UNSUPPORTED;
+    if (!fusion_ok(fusion)) return KDA_ERR_INVALID_ARGUMENT;
+    const bool fused = fusion && (fusion->flags || fusion->out_gate);
+    if ((scalar_gate || fused) && chunk != 0 && chunk != 32) return KDA_ERR_UNSUPPORTED;
     if (cu_seqlens) {
         if (B != 1) return KDA_ERR_INVALID_ARGUMENT;
         if (!aligned16(cu_seqlens)) return KDA_ERR_INVALID_ARGUMENT;
@@ -91,6 +114,11 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
         for (int i = 0; i < 5; ++i)
             if (overlap(ins[i], nin[i], o, n_o) || overlap(ins[i], nin[i], S_final, n_s))
                 return KDA_ERR_INVALID_ARGUMENT;
+        if (fused && fusion->out_gate) {
+            const size_t n_gate = tokens * H * Dv * ein;
+            if (overlap(fusion->out_gate, n_gate, o, n_o) || overlap(fusion->out_gate, n_gate, S_final, n_s))
+                return KDA_ERR_INVALID_ARGUMENT;
+        }
     }
     if (overlap(S0, n_s, S_final, n_s) || overlap(S0, n_s, o, n_o) || overlap(o, n_o, S_final, n_s))
         return KDA_ERR_INVALID_ARGUMENT;
@@ -104,7 +132,7 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
 
     // A batch of equal-length sequences of at most kRecurrentMaxT tokens (new tokens on top of a
     // carried state) runs token by token with the state on chip: a chunk would be mostly padding.
-    if (!cu_seqlens && T > 0 && T <= kda::kRecurrentMaxT) {
+    if (!cu_seqlens && T > 0 && T <= kda::kRecurrentMaxT && !fused) {
         const size_t units = static_cast<size_t>(B) * H;
         if (units > 0x7fffffffu) return KDA_ERR_UNSUPPORTED;
         hipError_t err = kda::launch_recurrent_fwd(Dk, in_dtype == KDA_BF16, out_dtype == KDA_BF16, q, k, v,
@@ -118,6 +146,11 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
     a.B = B; a.T = T; a.H = H; a.D = Dk; a.N = num_seqs;
     a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = out_dtype == KDA_BF16;
     a.scalar_gate = scalar_gate;
+    const kda::Fusion fz = to_fusion(fused ? fusion : nullptr);
+    a.fuse_flags = fz.flags;
+    a.decay_bias = fz.decay_bias;
+    a.decay_scale = fz.decay_scale;
+    a.out_gate = fz.out_gate;
     a.workspace = workspace;
     hipError_t err = kda::launch_prefill(a, plan, reinterpret_cast<hipStream_t>(stream));
     return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
@@ -126,10 +159,12 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
 kda_status recurrent_step_impl(const void* q, const void* k, const void* v, const void* log_alpha,
                                const void* beta, const float* S_in, float* S_out, int N, int H, int Dk, int Dv,
                                kda_dtype in_dtype, kda_dtype out_dtype, void* o, kda_stream_t stream,
-                               bool scalar_gate) {
+                               bool scalar_gate, const kda_fusion* fusion = nullptr) {
     if (N < 0 || H <= 0 || Dk <= 0 || Dv <= 0) return KDA_ERR_INVALID_ARGUMENT;
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_UNSUPPORTED;
     if (!head_ok(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
+    if (!fusion_ok(fusion)) return KDA_ERR_INVALID_ARGUMENT;
+    const bool fused = fusion && (fusion->flags || fusion->out_gate);
     if (N == 0) return KDA_OK;
     if (!q || !k || !v || !log_alpha || !beta || !S_in || !S_out || !o) return KDA_ERR_INVALID_ARGUMENT;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) || !aligned16(beta) ||
@@ -145,11 +180,17 @@ kda_status recurrent_step_impl(const void* q, const void* k, const void* v, cons
     for (int i = 0; i < 5; ++i)
         if (overlap(ins[i], nin[i], S_out, n_s) || overlap(ins[i], nin[i], o, n_o)) return KDA_ERR_INVALID_ARGUMENT;
     if (overlap(o, n_o, S_out, n_s) || overlap(o, n_o, S_in, n_s)) return KDA_ERR_INVALID_ARGUMENT;
+    if (fused && fusion->out_gate) {
+        const size_t n_gate = units * Dv * ein;
+        if (overlap(fusion->out_gate, n_gate, o, n_o) || overlap(fusion->out_gate, n_gate, S_out, n_s))
+            return KDA_ERR_INVALID_ARGUMENT;
+    }
     if (units > 0x7fffffffu) return KDA_ERR_UNSUPPORTED;
 
+    const kda::Fusion fz = to_fusion(fused ? fusion : nullptr);
     hipError_t err = kda::launch_decode(Dk, in_dtype == KDA_BF16, out_dtype == KDA_BF16, q, k, v, log_alpha,
                                         beta, S_in, S_out, o, static_cast<int>(units),
-                                        reinterpret_cast<hipStream_t>(stream), scalar_gate);
+                                        reinterpret_cast<hipStream_t>(stream), scalar_gate, fused ? &fz : nullptr);
     return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -252,4 +293,23 @@ extern "C" kda_status gdn_recurrent_fwd(const void* q, const void* k, const void
                                         kda_stream_t stream) {
     return recurrent_fwd_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, B, T, H, Dk, Dv, num_seqs, in_dtype,
                               out_dtype, o, S_final, stream, true);
+}
+
+extern "C" kda_status kda_chunk_fwd_fused(const void* q, const void* k, const void* v, const void* log_alpha,
+                                          const void* beta, const float* S0, const int32_t* cu_seqlens,
+                                          int B, int T, int H, int Dk, int Dv, int num_seqs, int chunk,
+                                          kda_dtype in_dtype, kda_dtype out_dtype, void* o, float* S_final,
+                                          void* workspace, size_t workspace_bytes, const kda_fusion* fusion,
+                                          kda_stream_t stream) {
+    return chunk_fwd_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, B, T, H, Dk, Dv, num_seqs, chunk, in_dtype,
+                          out_dtype, o, S_final, workspace, workspace_bytes, stream, false, fusion);
+}
+
+extern "C" kda_status kda_recurrent_step_fused(const void* q, const void* k, const void* v, const void* log_alpha,
+                                               const void* beta, const float* S_in, float* S_out,
+                                               int N, int H, int Dk, int Dv,
+                                               kda_dtype in_dtype, kda_dtype out_dtype,
+                                               void* o, const kda_fusion* fusion, kda_stream_t stream) {
+    return recurrent_step_impl(q, k, v, log_alpha, beta, S_in, S_out, N, H, Dk, Dv, in_dtype, out_dtype, o, stream,
+                               false, fusion);
 }

@@ -22,6 +22,7 @@
 // stores are non-temporal (`nt`): on MI355X that lifts the step from about 5.1 to
 // 5.9 TB/s of state traffic.
 #include "kda_device.h"
+#include "kda_launch.h"
 
 namespace kda {
 
@@ -37,15 +38,27 @@ __device__ __forceinline__ void store_stream(float4* p, float4 x) {
     __builtin_nontemporal_store(vf4{x.x, x.y, x.z, x.w}, reinterpret_cast<vf4*>(p));
 }
 
+// Fused prologue / epilogue of a decode step (FUSE kernels).
+struct DecodeFusion {
+    int flags;                // 1: L2-normalise q and k; 2: beta holds logits; 4: log_alpha holds logits
+    float decay_bias, decay_scale;
+    const void* out_gate;     // [N, H, D] output-gate logits or nullptr
+};
+
+__device__ __forceinline__ float sigmoid_d(float x) { return __builtin_amdgcn_rcpf(1.f + fast_exp(-x)); }
+
 // SG: log_alpha is one value per (sequence, head) (the scalar gate of Gated DeltaNet).
-template <int D, typename IN, bool OUT_BF16, bool SG = false>
+// FUSE: q, k unnormalised, beta and log_alpha as logits, optional output gate.  With
+// nk = 1/|k|, nq = 1/|q|: r = nk S'^T k, p = nq S'^T q, e = beta (v - r),
+// S_out = S' + k (nk e)^T, o = p + (k . q) nk nq e.
+template <int D, typename IN, bool OUT_BF16, bool SG = false, bool FUSE = false>
 __global__ __launch_bounds__(kDecodeThreads)
 void decode_step_kernel(const typename IN::storage* __restrict__ q,
                         const typename IN::storage* __restrict__ k,
                         const typename IN::storage* __restrict__ v,
                         const typename IN::storage* __restrict__ log_alpha,
                         const typename IN::storage* __restrict__ beta,
-                        const float* S_in, float* S_out, void* __restrict__ o) {
+                        const float* S_in, float* S_out, void* __restrict__ o, DecodeFusion fu) {
     constexpr int CG = D / 4;                 // column groups of 4
     constexpr int RG = kDecodeThreads / CG;   // row groups
     constexpr int ROWS = D / RG;              // rows per thread
@@ -55,6 +68,7 @@ void decode_step_kernel(const typename IN::storage* __restrict__ q,
     __shared__ float4 s_r[RG][CG];
     __shared__ float4 s_p[RG][CG];
     __shared__ float s_kq[kDecodeThreads / 64];
+    __shared__ float s_kk[kDecodeThreads / 64], s_qq[kDecodeThreads / 64];
 
     const int unit = blockIdx.x;              // n * H + h
     const int t = threadIdx.x;
@@ -68,20 +82,46 @@ void decode_step_kernel(const typename IN::storage* __restrict__ q,
 #pragma unroll
     for (int i = 0; i < ROWS; ++i) s[i] = load_stream(&src[(rg * ROWS + i) * CG + cg]);
 
-    float kq = 0.f;
+    float kq = 0.f, k2 = 0.f, q2 = 0.f;
     if (t < D) {
         float kk = IN::to_f32(k[vec + t]);
         float qq = IN::to_f32(q[vec + t]);
-        s_alpha[t] = fast_exp(IN::to_f32(SG ? log_alpha[unit] : log_alpha[vec + t]));
+        float g = IN::to_f32(SG ? log_alpha[unit] : log_alpha[vec + t]);
+        if constexpr (FUSE) {
+            if (fu.flags & 4) {
+                // logsigmoid(g + bias) / scale, stable for any g
+                const float x = g + fu.decay_bias;
+                g = (fminf(x, 0.f) - __builtin_amdgcn_logf(1.f + fast_exp(-fabsf(x))) * 0.6931471805599453f) /
+                    fu.decay_scale;
+            }
+        }
+        s_alpha[t] = fast_exp(g);
         s_k[t] = kk;
         s_q[t] = qq;
         kq = kk * qq;
+        k2 = kk * kk;
+        q2 = qq * qq;
     }
-    // k . q: wave reduction, then across waves through LDS
+    // k . q (and |k|^2, |q|^2): wave reduction, then across waves through LDS
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) kq += __shfl_xor(kq, off, 64);
-    if ((t & 63) == 0) s_kq[t >> 6] = kq;
-    const float b = IN::to_f32(beta[unit]);
+    for (int off = 32; off > 0; off >>= 1) {
+        kq += __shfl_xor(kq, off, 64);
+        if constexpr (FUSE) {
+            k2 += __shfl_xor(k2, off, 64);
+            q2 += __shfl_xor(q2, off, 64);
+        }
+    }
+    if ((t & 63) == 0) {
+        s_kq[t >> 6] = kq;
+        if constexpr (FUSE) {
+            s_kk[t >> 6] = k2;
+            s_qq[t >> 6] = q2;
+        }
+    }
+    float b = IN::to_f32(beta[unit]);
+    if constexpr (FUSE) {
+        if (fu.flags & 2) b = sigmoid_d(b);
+    }
     __syncthreads();
 
     float4 r = make_float4(0.f, 0.f, 0.f, 0.f), p = r;
@@ -108,6 +148,22 @@ void decode_step_kernel(const typename IN::storage* __restrict__ q,
     float kqs = 0.f;
 #pragma unroll
     for (int w = 0; w < kDecodeThreads / 64; ++w) kqs += s_kq[w];
+    float nk = 1.f;   // 1/|k| and 1/|q| under the fused normalisation
+    if constexpr (FUSE) {
+        if (fu.flags & 1) {
+            float kks = 1e-12f, qqs = 1e-12f;
+#pragma unroll
+            for (int w = 0; w < kDecodeThreads / 64; ++w) {
+                kks += s_kk[w];
+                qqs += s_qq[w];
+            }
+            nk = __builtin_amdgcn_rsqf(kks);
+            const float nq = __builtin_amdgcn_rsqf(qqs);
+            r.x *= nk; r.y *= nk; r.z *= nk; r.w *= nk;
+            p.x *= nq; p.y *= nq; p.z *= nq; p.w *= nq;
+            kqs *= nk * nq;
+        }
+    }
 
     const int j0 = cg * 4;
     float4 e;
@@ -116,19 +172,26 @@ void decode_step_kernel(const typename IN::storage* __restrict__ q,
     e.z = b * (IN::to_f32(v[vec + j0 + 2]) - r.z);
     e.w = b * (IN::to_f32(v[vec + j0 + 3]) - r.w);
 
+    const float4 eu = make_float4(nk * e.x, nk * e.y, nk * e.z, nk * e.w);   // k_normalised e^T = k (nk e)^T
     float4* dst = reinterpret_cast<float4*>(S_out + sbase);
 #pragma unroll
     for (int i = 0; i < ROWS; ++i) {
         const float kc = s_k[rg * ROWS + i];
         float4 x = s[i];
-        x.x += kc * e.x; x.y += kc * e.y; x.z += kc * e.z; x.w += kc * e.w;
+        x.x += kc * eu.x; x.y += kc * eu.y; x.z += kc * eu.z; x.w += kc * eu.w;
         store_stream(&dst[(rg * ROWS + i) * CG + cg], x);
     }
     if (rg == 0) {
-        store_out<OUT_BF16>(o, vec + j0 + 0, p.x + kqs * e.x);
-        store_out<OUT_BF16>(o, vec + j0 + 1, p.y + kqs * e.y);
-        store_out<OUT_BF16>(o, vec + j0 + 2, p.z + kqs * e.z);
-        store_out<OUT_BF16>(o, vec + j0 + 3, p.w + kqs * e.w);
+        float ov[4] = {p.x + kqs * e.x, p.y + kqs * e.y, p.z + kqs * e.z, p.w + kqs * e.w};
+        if constexpr (FUSE) {
+            if (fu.out_gate) {
+                const typename IN::storage* gp = static_cast<const typename IN::storage*>(fu.out_gate);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) ov[c] *= sigmoid_d(IN::to_f32(gp[vec + j0 + c]));
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) store_out<OUT_BF16>(o, vec + j0 + c, ov[c]);
     }
 }
 
@@ -375,25 +438,33 @@ hipError_t launch_recurrent_fwd(int D, bool in_bf16, bool out_bf16, const void* 
     return hipErrorInvalidValue;
 }
 
-template <int D, typename IN, bool OUT_BF16, bool SG>
+template <int D, typename IN, bool OUT_BF16, bool SG, bool FUSE = false>
 static hipError_t launch_decode_t(const void* q, const void* k, const void* v, const void* g,
                                   const void* b, const float* S_in, float* S_out, void* o,
-                                  int units, hipStream_t stream) {
+                                  int units, hipStream_t stream, DecodeFusion fu = DecodeFusion{0, 0.f, 1.f, nullptr}) {
     using T = typename IN::storage;
-    hipLaunchKernelGGL((decode_step_kernel<D, IN, OUT_BF16, SG>), dim3(units), dim3(kDecodeThreads), 0, stream,
+    hipLaunchKernelGGL((decode_step_kernel<D, IN, OUT_BF16, SG, FUSE>), dim3(units), dim3(kDecodeThreads), 0, stream,
                        static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
-                       static_cast<const T*>(g), static_cast<const T*>(b), S_in, S_out, o);
+                       static_cast<const T*>(g), static_cast<const T*>(b), S_in, S_out, o, fu);
     return hipGetLastError();
 }
 
 // Host-side dispatch over the built variants; arguments already validated.
 hipError_t launch_decode(int D, bool in_bf16, bool out_bf16, const void* q, const void* k,
                          const void* v, const void* g, const void* b, const float* S_in,
-                         float* S_out, void* o, int units, hipStream_t stream, bool scalar_gate) {
+                         float* S_out, void* o, int units, hipStream_t stream, bool scalar_gate,
+                         const Fusion* fusion) {
+    const bool fused = fusion && (fusion->flags || fusion->out_gate);
+    const DecodeFusion fu = fused ? DecodeFusion{fusion->flags, fusion->decay_bias, fusion->decay_scale,
+                                                 fusion->out_gate}
+                                  : DecodeFusion{0, 0.f, 1.f, nullptr};
+    if (fused && scalar_gate) return hipErrorInvalidValue;
 #define KDA_DECODE_CASE(DD, INT, OB)                                                        \
-    if (D == DD && in_bf16 == std::is_same<INT, BF16>::value && out_bf16 == OB)               \
+    if (D == DD && in_bf16 == std::is_same<INT, BF16>::value && out_bf16 == OB) {             \
+        if (fused) return launch_decode_t<DD, INT, OB, false, true>(q, k, v, g, b, S_in, S_out, o, units, stream, fu); \
         return scalar_gate ? launch_decode_t<DD, INT, OB, true>(q, k, v, g, b, S_in, S_out, o, units, stream) \
-                           : launch_decode_t<DD, INT, OB, false>(q, k, v, g, b, S_in, S_out, o, units, stream);
+                           : launch_decode_t<DD, INT, OB, false>(q, k, v, g, b, S_in, S_out, o, units, stream); \
+    }
     KDA_DECODE_CASE(128, BF16, true)
     KDA_DECODE_CASE(128, BF16, false)
     KDA_DECODE_CASE(128, F32, true)

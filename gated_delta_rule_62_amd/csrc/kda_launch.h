@@ -25,6 +25,13 @@ inline bool chunk_supported(int c) { return c == 0 || c == 32 || c == 64; }
 //         carries the segment's transition matrix; a small combine kernel chains
 //         the segment entry states; pass 2 reruns every segment from its true
 //         entry state and writes o and S_final.
+// Fused prologue / epilogue of the _fused entry points (flags as in kda_fusion).
+struct Fusion {
+    int flags = 0;                     // 1: L2-normalise q, k; 2: beta logits; 4: log_alpha logits
+    float decay_bias = 0.f, decay_scale = 1.f;
+    const void* out_gate = nullptr;    // output-gate logits shaped like o (in dtype)
+};
+
 struct PrefillPlan {
     int chunk = kDefaultChunk;
     int G = 1;
@@ -44,6 +51,11 @@ struct PrefillArgs {
     int B, T, H, D, N;
     bool in_bf16, out_bf16;
     bool scalar_gate = false;   // log_alpha is [B, T, H] (one decay per token and head)
+    // fused prologue / epilogue: 1 = L2-normalise q and k, 2 = beta holds logits,
+    // 4 = log_alpha holds logits a (decay logsigmoid(a + decay_bias) / decay_scale)
+    int fuse_flags = 0;
+    float decay_bias = 0.f, decay_scale = 1.f;
+    const void* out_gate = nullptr;   // [B, T, H, D] output-gate logits (in dtype) or nullptr
 };
 
 PrefillPlan plan_prefill(int B, int T, int H, int D, int N, bool varlen, int chunk);
@@ -51,7 +63,8 @@ hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan, hipStre
 
 hipError_t launch_decode(int D, bool in_bf16, bool out_bf16, const void* q, const void* k,
                          const void* v, const void* g, const void* b, const float* S_in,
-                         float* S_out, void* o, int units, hipStream_t stream, bool scalar_gate);
+                         float* S_out, void* o, int units, hipStream_t stream, bool scalar_gate,
+                         const Fusion* fusion = nullptr);
 
 hipError_t launch_recurrent_fwd(int D, bool in_bf16, bool out_bf16, const void* q, const void* k,
                                 const void* v, const void* g, const void* b, const float* S0,

@@ -283,6 +283,10 @@ struct KernelArgs {
     float* sloc;    // [G-1][N*H][D][D] segment end states from a zero entry
     float* se;      // [G-1][N*H][D][D] entry states of segments 1..G-1
     int T, H, NH, G, cps, chunks;
+    // fused prologue / epilogue (FUSE kernels only)
+    int fuse_flags;           // kFuseQK | kFuseBeta | kFuseDecay
+    float decay_bias, decay_scale;
+    const void* out_gate;     // [B, T, H, D] gate logits or nullptr
 };
 
 // MODE 0: outputs (o, S_final) from a known entry state.
@@ -754,6 +758,37 @@ __device__ __forceinline__ void quad_lower_solve(float (&y)[4], const f32x4 (&co
 //   1          decay prefix, decayed K/Q splits     Y = Kbar S, Z = Qbar S
 //   2          A tiles, next inputs requested       Unew block recurrence, O; P tiles of c+1
 //   3          Ktil_m^T, diagonal-block inverses    state update, O stores, state split
+// ------------------------------------------------------------------ fused prologue helpers
+constexpr int kFuseQK = 1, kFuseBeta = 2, kFuseDecay = 4;
+
+__device__ __forceinline__ float sigmoid_f(float x) { return __builtin_amdgcn_rcpf(1.f + exp2f_hw(-x * kLog2e)); }
+
+// log2(sigmoid(x)) = min(x, 0) log2(e) - log2(1 + 2^{-|x| log2(e)}), without overflow for any x
+__device__ __forceinline__ float log2_sigmoid(float x) {
+    return fminf(x, 0.f) * kLog2e - __builtin_amdgcn_logf(1.f + exp2f_hw(-fabsf(x) * kLog2e));
+}
+
+// Sum over the 8 lanes of an aligned lane octet (DPP butterflies; every lane gets the sum).
+__device__ __forceinline__ float sum8(float x) {
+    auto dpp = [](float v, auto ctrl) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), decltype(ctrl)::value,
+                                                                   0xf, 0xf, true));
+    };
+    x += dpp(x, std::integral_constant<int, 0xB1>{});    // quad_perm [1, 0, 3, 2]
+    x += dpp(x, std::integral_constant<int, 0x4E>{});    // quad_perm [2, 3, 0, 1]
+    x += dpp(x, std::integral_constant<int, 0x141>{});   // row_half_mirror
+    return x;
+}
+
+// 1 / (sum over producer waves of the partial sums of squares of token r + 1e-12)
+template <int NPW, int C>
+__device__ __forceinline__ float inv_sumsq(const float (&part)[NPW][C], int r) {
+    float t = 1e-12f;
+#pragma unroll
+    for (int i = 0; i < NPW; ++i) t += part[i][r];
+    return __builtin_amdgcn_rcpf(t);
+}
+
 template <int D, int MODE>
 struct PCfg {
     static constexpr int C = 32;
@@ -794,6 +829,11 @@ struct alignas(16) PBuf {
     u16 p[NQ][PE];              // P = Tril(Qbar Ktil^T)       [token][kperm(token)]
     u16 vt[VLDS ? D * K::C : 8];    // V^T (bf16)              [column][token]
     float beta[K::C];
+    float betae[K::C];          // fused prologue: beta_r / |k_r|^2
+    float vs[K::C];             // fused prologue: |k_r| (scales V rows)
+    float os[K::C];             // fused prologue: 1 / |q_r| (scales O rows)
+    float nk[K::NPW][K::C];     // fused prologue: per producer wave, partial sums of k_r^2 and q_r^2
+    float nq[K::NPW][K::C];
     float fv[K::C];             // scalar gate: e^{b_m - b_r} (scales V rows)
     float fo[K::C];             // scalar gate: e^{b_r - b_m} (scales O rows)
     float em[D];                // e^{b_m}
@@ -814,7 +854,15 @@ struct PSmem {
 //     S~ <- rho (S~ + K^T U'),   rho = e^{b_m'} e^{b_n - b_m} (a scalar).
 // With bf16 inputs K and Q are exact MFMA operands, so every product that has them on one side
 // needs two MFMAs (or one) instead of three, and the producer has no per-element decay.
-template <int D, typename IN, bool OUT_BF16, int MODE, bool SG = false>
+//
+// FUSE (fused prologue / epilogue, flags in KernelArgs): q and k arrive unnormalised, beta and
+// log_alpha as logits, and o may be gated.  The L2 norms enter as per-token scalars only: with
+// n_r = |k_r| and m_r = |q_r| (over the key channels, plus 1e-12 under the root),
+//     A = Diag(beta / n^2) StrictTril(Kbar Ktil^T),  U' = T (Diag(n) V - Kbar S),
+//     O = Diag(1/m) (Qbar S + P U'),  S <- Diag(gamma) S + Khat^T U'
+// with the unnormalised Kbar, Ktil, Khat, Qbar, P (U' = Diag(1/n) Unew of the normalised keys),
+// so the producer only adds per-token sums of squares to its decay phase.
+template <int D, typename IN, bool OUT_BF16, int MODE, bool SG = false, bool FUSE = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(PCfg<D, MODE>::NT, PCfg<D, MODE>::NT),
                           amdgpu_waves_per_eu(PCfg<D, MODE>::WPE, PCfg<D, MODE>::WPE)))
 void pipe_kernel(KernelArgs a) {
@@ -1018,8 +1066,32 @@ void pipe_kernel(KernelArgs a) {
 #pragma unroll
         for (int i = 0; i < TPG; ++i)
 #pragma unroll
-            for (int ch = 0; ch < 4; ++ch)
-                gr[i][ch] = R::get(pg[i], ch) * kLog2e + (i ? gr[i - 1][ch] : 0.f);
+            for (int ch = 0; ch < 4; ++ch) {
+                float g2 = R::get(pg[i], ch) * kLog2e;   // log2 of this token's decay
+                if constexpr (FUSE) {
+                    if ((a.fuse_flags & kFuseDecay) && tg * TPG + i <= last)
+                        g2 = log2_sigmoid(R::get(pg[i], ch) + a.decay_bias) / a.decay_scale;
+                }
+                gr[i][ch] = g2 + (i ? gr[i - 1][ch] : 0.f);
+            }
+        if constexpr (FUSE) {
+            // per-token sums of squares of this wave's 32 channels (8 lanes share a token group)
+#pragma unroll
+            for (int i = 0; i < TPG; ++i) {
+                float sk = 0.f, sq = 0.f;
+#pragma unroll
+                for (int ch = 0; ch < 4; ++ch) {
+                    sk += R::get(pk[i], ch) * R::get(pk[i], ch);
+                    if constexpr (MODE == 0) sq += R::get(pq[i], ch) * R::get(pq[i], ch);
+                }
+                sk = sum8(sk);
+                if constexpr (MODE == 0) sq = sum8(sq);
+                if ((l & 7) == 0) {
+                    B.nk[w][tg * TPG + i] = sk;
+                    if constexpr (MODE == 0) B.nq[w][tg * TPG + i] = sq;
+                }
+            }
+        }
         float off[4], bm[4], bn[4];
 #pragma unroll
         for (int ch = 0; ch < 4; ++ch) {
@@ -1074,7 +1146,13 @@ void pipe_kernel(KernelArgs a) {
             }
         }
         stage_v(B);
-        if (tid < C) B.beta[tid] = IN::to_f32(pb);
+        if (tid < C) {
+            float bt = IN::to_f32(pb);
+            if constexpr (FUSE) {
+                if ((a.fuse_flags & kFuseBeta) && tid <= last) bt = sigmoid_f(bt);
+            }
+            B.beta[tid] = bt;
+        }
     };
 
     // Tiles of A^T and P^T: tile (rt, ct), ct <= rt, is Ktil_m[ct] against Kbar_m[rt] (or
@@ -1103,7 +1181,10 @@ void pipe_kernel(KernelArgs a) {
                     acc = mfma3(frag(&B.kt[0][ao]), frag(&B.kt[1][ao]), frag(&B.kb[0][bo]), frag(&B.kb[1][bo]), acc);
             }
             const int row = 16 * rt + lr;
-            const float br = B.beta[row];
+            float br = B.beta[row];
+            if constexpr (FUSE) {
+                if (a.fuse_flags & kFuseQK) br *= inv_sumsq(B.nk, row);
+            }
             if (rt == ct) {
                 f32x4 v;
 #pragma unroll
@@ -1115,6 +1196,18 @@ void pipe_kernel(KernelArgs a) {
                 const int idx = row * K::AP + 16 * ct + 4 * g4;
                 *reinterpret_cast<uint2*>(&B.aoff[0][idx]) = hi;
                 *reinterpret_cast<uint2*>(&B.aoff[1][idx]) = lo;
+            }
+        }
+    };
+    // interval 2 (producer, fused prologue): per-token scalars for the consumers
+    auto produce_token_scales = [&](Buf& B) {
+        if constexpr (FUSE) {
+            if (w == NPW - 1 && l < C) {
+                const bool qk = a.fuse_flags & kFuseQK;
+                const float ik = qk ? inv_sumsq(B.nk, l) : 1.f;
+                B.betae[l] = B.beta[l] * ik;
+                B.vs[l] = qk ? __builtin_amdgcn_rsqf(ik) : 1.f;
+                if constexpr (MODE == 0) B.os[l] = qk ? __builtin_amdgcn_sqrtf(inv_sumsq(B.nq, l)) : 1.f;
             }
         }
     };
@@ -1319,6 +1412,9 @@ void pipe_kernel(KernelArgs a) {
                 if constexpr (SG) {
                     if (!is_phi) vv *= *reinterpret_cast<const f32x4*>(&B.fv[16 * rt + 4 * g4]);
                 }
+                if constexpr (FUSE) {
+                    if (!is_phi) vv *= *reinterpret_cast<const f32x4*>(&B.vs[16 * rt + 4 * g4]);
+                }
                 Y[rt][ct] = vv - Y[rt][ct];
             }
     };
@@ -1330,7 +1426,7 @@ void pipe_kernel(KernelArgs a) {
         bf16x4 uh[NRT][CT], ul[NRT][CT];
 #pragma unroll
         for (int b = 0; b < NRT; ++b) {
-            const f32x4 bb = *reinterpret_cast<const f32x4*>(&B.beta[16 * b + 4 * g4]);
+            const f32x4 bb = *reinterpret_cast<const f32x4*>(FUSE ? &B.betae[16 * b + 4 * g4] : &B.beta[16 * b + 4 * g4]);
             f32x4 acc[CT];
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct)
@@ -1398,9 +1494,20 @@ void pipe_kernel(KernelArgs a) {
                 if (row < ntok) {
                     float fo = 1.f;
                     if constexpr (SG) fo = B.fo[row];
+                    if constexpr (FUSE) fo = B.os[row];
 #pragma unroll
-                    for (int ct = 0; ct < CT; ++ct)
-                        store_out4<OUT_BF16>(a.o, obase + static_cast<unsigned>(row * HD + 16 * ct), Z[rt][ct] * fo);
+                    for (int ct = 0; ct < CT; ++ct) {
+                        f32x4 ov = Z[rt][ct] * fo;
+                        if constexpr (FUSE) {
+                            if (a.out_gate) {
+                                float gv[4];
+                                load4<IN>(static_cast<const ST*>(a.out_gate), obase + static_cast<unsigned>(row * HD + 16 * ct), gv);
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) ov[e] *= sigmoid_f(gv[e]);
+                            }
+                        }
+                        store_out4<OUT_BF16>(a.o, obase + static_cast<unsigned>(row * HD + 16 * ct), ov);
+                    }
                 }
             }
         }
@@ -1416,6 +1523,7 @@ void pipe_kernel(KernelArgs a) {
             lds_barrier();
             if (c_begin + 1 < c_end) fetch(c_begin + 1, solver ? -1 : 0);
             produce_products(sm.buf[c_begin & 1]);
+            produce_token_scales(sm.buf[c_begin & 1]);
             lds_barrier();
             if (!solver && c_begin + 1 < c_end) fetch(c_begin + 1, 1);
             produce_inverse(sm.buf[c_begin & 1]);
@@ -1436,7 +1544,10 @@ void pipe_kernel(KernelArgs a) {
             // k and log_alpha (used first) here, q, v and beta at the start of interval 3, except
             // on the wave that solves the diagonal blocks in interval 3, which requests all here.
             if (chunk + 2 < c_end) fetch(chunk + 2, solver ? -1 : 0);
-            if (more) produce_products(nxt);
+            if (more) {
+                produce_products(nxt);
+                produce_token_scales(nxt);
+            }
             lds_barrier();
             if (!solver && chunk + 2 < c_end) fetch(chunk + 2, 1);
             if (more) produce_inverse(nxt);
@@ -1534,13 +1645,16 @@ __global__ __launch_bounds__(256) void order_kernel(const int32_t* __restrict__ 
     order[rank] = i;
 }
 
-template <int D, int C, typename IN, bool OB, bool SG = false>
+template <int D, int C, typename IN, bool OB, bool SG = false, bool FUSE = false>
 hipError_t launch_variant(const PrefillArgs& pa, const PrefillPlan& plan, hipStream_t stream) {
+    static_assert(!FUSE || (C == 32 && !SG), "the fused prologue runs on the pipelined 32-token KDA kernel");
     static_assert(!SG || C == 32, "the scalar gate runs on the pipelined 32-token kernel");
     KernelArgs a;
     a.q = pa.q; a.k = pa.k; a.v = pa.v; a.g = pa.g; a.beta = pa.beta;
     a.S0 = pa.S0; a.cu = pa.cu; a.o = pa.o; a.S_final = pa.S_final;
     a.T = pa.T; a.H = pa.H; a.NH = pa.N * pa.H; a.G = plan.G; a.cps = plan.cps; a.chunks = plan.chunks;
+    a.fuse_flags = pa.fuse_flags; a.decay_bias = pa.decay_bias; a.decay_scale = pa.decay_scale;
+    a.out_gate = pa.out_gate;
     char* ws = static_cast<char*>(pa.workspace);
     a.order = pa.cu ? reinterpret_cast<const int32_t*>(ws + plan.off_order) : nullptr;
     a.phi = plan.G > 1 ? reinterpret_cast<float*>(ws + plan.off_phi) : nullptr;
@@ -1552,9 +1666,9 @@ hipError_t launch_variant(const PrefillArgs& pa, const PrefillPlan& plan, hipStr
     auto pass = [&](int mode, int grid) {
         if constexpr (C == 32) {
             if (mode == 0)
-                hipLaunchKernelGGL((pipe_kernel<D, IN, OB, 0, SG>), dim3(grid), dim3(PCfg<D, 0>::NT), 0, stream, a);
+                hipLaunchKernelGGL((pipe_kernel<D, IN, OB, 0, SG, FUSE>), dim3(grid), dim3(PCfg<D, 0>::NT), 0, stream, a);
             else
-                hipLaunchKernelGGL((pipe_kernel<D, IN, OB, 1, SG>), dim3(grid), dim3(PCfg<D, 1>::NT), 0, stream, a);
+                hipLaunchKernelGGL((pipe_kernel<D, IN, OB, 1, SG, FUSE>), dim3(grid), dim3(PCfg<D, 1>::NT), 0, stream, a);
         } else {
             if (mode == 0)
                 hipLaunchKernelGGL((chunk_kernel<D, C, IN, OB, 0>), dim3(grid), dim3(Cfg<D, C, 0>::NT), 0, stream, a);
@@ -1616,8 +1730,12 @@ PrefillPlan plan_prefill(int B, int T, int H, int D, int N, bool varlen, int chu
 hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan, hipStream_t stream) {
 #define KDA_PREFILL_CASE(DD, CC, INT, OB)                                                              \
     if (a.D == DD && plan.chunk == CC && a.in_bf16 == std::is_same<INT, BF16>::value && a.out_bf16 == OB) { \
-        if (a.scalar_gate) {                                                                           \
-            if constexpr (CC == 32) return launch_variant<DD, CC, INT, OB, true>(a, plan, stream);      \
+        if (a.scalar_gate || a.fuse_flags || a.out_gate) {                                             \
+            if constexpr (CC == 32) {                                                                  \
+                if (a.scalar_gate && !a.fuse_flags && !a.out_gate)                                     \
+                    return launch_variant<DD, CC, INT, OB, true>(a, plan, stream);                      \
+                if (!a.scalar_gate) return launch_variant<DD, CC, INT, OB, false, true>(a, plan, stream); \
+            }                                                                                          \
             return hipErrorInvalidValue;                                                               \
         }                                                                                              \
         return launch_variant<DD, CC, INT, OB>(a, plan, stream);                                       \

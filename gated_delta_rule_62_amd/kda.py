@@ -20,7 +20,15 @@ KDA_F32, KDA_BF16 = 0, 1
 CHUNK = 0          # library default chunk length (32 tokens); 32 and 64 are built
 
 EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_step",
-            "kda_recurrent_fwd", "gdn_chunk_fwd", "gdn_recurrent_step", "gdn_recurrent_fwd")
+            "kda_recurrent_fwd", "gdn_chunk_fwd", "gdn_recurrent_step", "gdn_recurrent_fwd",
+            "kda_chunk_fwd_fused", "kda_recurrent_step_fused")
+KDA_FUSE_QK_L2NORM, KDA_FUSE_BETA_SIGMOID, KDA_FUSE_DECAY_LOGSIGMOID = 1, 2, 4
+
+
+class Fusion(ctypes.Structure):
+    """kda_fusion of include/kda.h."""
+    _fields_ = [("flags", ctypes.c_int), ("decay_bias", ctypes.c_float), ("decay_scale", ctypes.c_float),
+                ("out_gate", ctypes.c_void_p)]
 
 _lib = None
 
@@ -50,6 +58,11 @@ def load_library(path: str = LIB_PATH):
     lib.kda_recurrent_step.restype = i32
     lib.kda_recurrent_fwd.argtypes = [vp] * 7 + [i32] * 6 + [i32, i32] + [vp, vp, vp]
     lib.kda_recurrent_fwd.restype = i32
+    fp = ctypes.POINTER(Fusion)
+    lib.kda_chunk_fwd_fused.argtypes = [vp] * 7 + [i32] * 7 + [i32, i32] + [vp, vp] + [vp, sz, fp, vp]
+    lib.kda_chunk_fwd_fused.restype = i32
+    lib.kda_recurrent_step_fused.argtypes = [vp] * 7 + [i32] * 4 + [i32, i32] + [vp, fp, vp]
+    lib.kda_recurrent_step_fused.restype = i32
     for pre in ("kda", "gdn"):
         getattr(lib, f"{pre}_chunk_fwd").argtypes = lib.kda_chunk_fwd.argtypes
         getattr(lib, f"{pre}_chunk_fwd").restype = i32
@@ -179,3 +192,61 @@ def gdn_recurrent_step(q, k, v, log_alpha, beta, S_in, S_out=None, **kw):
 
 def gdn_recurrent_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, **kw):
     return kda_recurrent_fwd(q, k, v, log_alpha, beta, S0, cu_seqlens, _fn="gdn_recurrent_fwd", **kw)
+
+
+def _fusion(qk_l2norm=False, beta_logits=False, decay_logits=None, out_gate=None):
+    f = Fusion()
+    f.flags = (KDA_FUSE_QK_L2NORM if qk_l2norm else 0) | (KDA_FUSE_BETA_SIGMOID if beta_logits else 0) | \
+        (KDA_FUSE_DECAY_LOGSIGMOID if decay_logits is not None else 0)
+    f.decay_bias, f.decay_scale = (decay_logits if decay_logits is not None else (0.0, 1.0))
+    f.out_gate = None if out_gate is None else out_gate.data_ptr()
+    return f
+
+
+def kda_chunk_fwd_fused(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, qk_l2norm=False,
+                        beta_logits=False, decay_logits=None, out_gate=None, out_dtype=None, o=None,
+                        S_final=None, workspace=None, chunk=CHUNK, stream=None, want_final=True):
+    """Prefill with the fused prologue / epilogue: q, k unnormalised (qk_l2norm), beta as
+    logits (beta_logits), log_alpha as logits a with decay_logits = (bias, scale) giving
+    logsigmoid(a + bias) / scale, and an optional output gate (logits shaped like o)."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=out_dtype, device=q.device)
+    if S_final is None and want_final:
+        S_final = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    _check_dev(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_final, workspace, out_gate)
+    ws_need = kda_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, N, cu_seqlens is not None, chunk)
+    if workspace is None and ws_need > 0:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    f = _fusion(qk_l2norm, beta_logits, decay_logits, out_gate)
+    st = load_library().kda_chunk_fwd_fused(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
+        B, T, H, Dk, Dv, N, chunk, _dtype_code(q.dtype), _dtype_code(o.dtype),
+        _ptr(o), _ptr(S_final), _ptr(workspace), ws_bytes, ctypes.byref(f), _stream_ptr(stream))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_chunk_fwd_fused")
+    return o, S_final
+
+
+def kda_recurrent_step_fused(q, k, v, log_alpha, beta, S_in, S_out=None, *, qk_l2norm=False, beta_logits=False,
+                             decay_logits=None, out_gate=None, out_dtype=None, o=None, stream=None):
+    """Decode one token with the fused prologue / epilogue (see kda_chunk_fwd_fused)."""
+    N, H, Dk = q.shape
+    Dv = v.shape[-1]
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((N, H, Dv), dtype=out_dtype, device=q.device)
+    if S_out is None:
+        S_out = S_in
+    _check_dev(q, k, v, log_alpha, beta, S_in, S_out, o, out_gate)
+    f = _fusion(qk_l2norm, beta_logits, decay_logits, out_gate)
+    st = load_library().kda_recurrent_step_fused(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S_in), _ptr(S_out),
+        N, H, Dk, Dv, _dtype_code(q.dtype), _dtype_code(o.dtype), _ptr(o), ctypes.byref(f), _stream_ptr(stream))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_recurrent_step_fused")
+    return o, S_out

@@ -138,6 +138,52 @@ kda_status kda_recurrent_fwd(const void* q, const void* k, const void* v, const 
                              void* o, float* S_final, kda_stream_t stream);
 
 /*
+ * Fused prologue and epilogue: the elementwise steps on either side of the layer
+ * run inside its kernels instead of as separate passes over HBM.
+ *
+ *   KDA_FUSE_QK_L2NORM        q and k are L2-normalised per (token, head) over Dk:
+ *                             x / sqrt(sum x^2 + 1e-12) (the pages take the keys as
+ *                             normalised, "Decoding Hybrid Attention Architectures"
+ *                             section 3.2)
+ *   KDA_FUSE_BETA_SIGMOID     beta holds logits: beta = 1 / (1 + exp(-beta))
+ *   KDA_FUSE_DECAY_LOGSIGMOID log_alpha holds logits a: log_alpha = logsigmoid(a +
+ *                             decay_bias) / decay_scale (decay_scale > 0), so every
+ *                             decay lies in (0, 1)
+ *   out_gate                  NULL, or gate logits shaped like o in the input dtype:
+ *                             o <- o * sigmoid(gate), per value channel
+ *
+ * The _fused functions take the arguments of their plain counterparts plus a
+ * kda_fusion (NULL or all-zero = the plain function); kda_chunk_fwd_fused supports
+ * chunk 0 or 32 and uses kda_chunk_fwd_workspace_bytes().
+ */
+typedef enum {
+    KDA_FUSE_QK_L2NORM = 1,
+    KDA_FUSE_BETA_SIGMOID = 2,
+    KDA_FUSE_DECAY_LOGSIGMOID = 4
+} kda_fuse_flag;
+
+typedef struct {
+    int flags;               /* bitwise OR of kda_fuse_flag */
+    float decay_bias;        /* used with KDA_FUSE_DECAY_LOGSIGMOID */
+    float decay_scale;       /* used with KDA_FUSE_DECAY_LOGSIGMOID, > 0 */
+    const void* out_gate;    /* device pointer or NULL, 16-byte aligned */
+} kda_fusion;
+
+kda_status kda_chunk_fwd_fused(const void* q, const void* k, const void* v, const void* log_alpha,
+                               const void* beta, const float* S0, const int32_t* cu_seqlens,
+                               int B, int T, int H, int Dk, int Dv, int num_seqs, int chunk,
+                               kda_dtype in_dtype, kda_dtype out_dtype,
+                               void* o, float* S_final,
+                               void* workspace, size_t workspace_bytes,
+                               const kda_fusion* fusion, kda_stream_t stream);
+
+kda_status kda_recurrent_step_fused(const void* q, const void* k, const void* v, const void* log_alpha,
+                                    const void* beta, const float* S_in, float* S_out,
+                                    int N, int H, int Dk, int Dv,
+                                    kda_dtype in_dtype, kda_dtype out_dtype,
+                                    void* o, const kda_fusion* fusion, kda_stream_t stream);
+
+/*
  * Scalar-gated variant (Gated DeltaNet): the same rule with one decay per token and
  * head, S_t = (I - beta_t k_t k_t^T) alpha_t S_{t-1} + beta_t k_t v_t^T, alpha_t a
  * scalar in (0, 1] ("Decoding Hybrid Attention Architectures", section 3.3 and the

@@ -122,3 +122,34 @@ def test_recurrent_fwd_argument_errors(lib):
     assert rec(Sf=ctypes.c_void_p((4 << 40) + 256)) == kda.KDA_ERR_INVALID_ARGUMENT   # partial overlap with S0
     assert rec(o=FAKE) == kda.KDA_ERR_INVALID_ARGUMENT                        # o aliases the inputs
     assert rec(o=ctypes.c_void_p((4 << 40) + 1024)) == kda.KDA_ERR_INVALID_ARGUMENT   # o inside the state
+
+
+def test_fused_argument_errors(lib):
+    def fwd(fusion, **kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, S0=None, cu=None, B=1, T=64, H=2, Dk=128, Dv=128,
+                 N=1, chunk=0, in_dt=kda.KDA_BF16, out_dt=kda.KDA_BF16, o=ctypes.c_void_p(2 << 40),
+                 Sf=None, ws=None, ws_bytes=0)
+        a.update(kw)
+        return lib.kda_chunk_fwd_fused(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["cu"], a["B"],
+                                       a["T"], a["H"], a["Dk"], a["Dv"], a["N"], a["chunk"], a["in_dt"],
+                                       a["out_dt"], a["o"], a["Sf"], a["ws"], a["ws_bytes"],
+                                       ctypes.byref(fusion), None)
+
+    def fz(flags=0, bias=0.0, scale=1.0, gate=None):
+        f = kda.Fusion()
+        f.flags, f.decay_bias, f.decay_scale, f.out_gate = flags, bias, scale, gate
+        return f
+    assert fwd(fz(flags=8)) == kda.KDA_ERR_INVALID_ARGUMENT                        # unknown flag
+    assert fwd(fz(flags=kda.KDA_FUSE_DECAY_LOGSIGMOID, scale=0.0)) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert fwd(fz(flags=kda.KDA_FUSE_DECAY_LOGSIGMOID, scale=-2.0)) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert fwd(fz(gate=(3 << 40) + 4)) == kda.KDA_ERR_INVALID_ARGUMENT             # misaligned gate
+    assert fwd(fz(gate=(2 << 40) + 64)) == kda.KDA_ERR_INVALID_ARGUMENT            # gate overlaps o
+    assert fwd(fz(flags=kda.KDA_FUSE_QK_L2NORM), chunk=64) == kda.KDA_ERR_UNSUPPORTED
+    assert fwd(fz(flags=kda.KDA_FUSE_QK_L2NORM), B=0, N=0, T=0) == kda.KDA_OK       # nothing to do
+
+    def step(fusion):
+        return lib.kda_recurrent_step_fused(FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(4 << 40),
+                                            ctypes.c_void_p(4 << 40), 2, 2, 128, 128, kda.KDA_BF16, kda.KDA_F32,
+                                            ctypes.c_void_p(5 << 40), ctypes.byref(fusion), None)
+    assert step(fz(flags=16)) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert step(fz(gate=(4 << 40) + 1024)) == kda.KDA_ERR_INVALID_ARGUMENT          # gate inside the state
