@@ -73,7 +73,8 @@ def counted_traffic(kind: str):
         rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))[kind]
     except (OSError, KeyError, ValueError):
         return None
-    files = {"decode": ["kda_decode.hip", "kda_device.h"], "prefill": ["kda_prefill.hip", "kda_device.h"]}[kind]
+    files = {"decode": ["kda_decode.hip", "kda_device.h", "kda_launch.h"],
+             "prefill": ["kda_prefill.hip", "kda_device.h", "kda_launch.h"]}[kind]
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(ROOT, "gated_delta_rule_62_amd", "csrc", f), "rb") as fh:
