@@ -6,6 +6,8 @@ CPU-baseline leg may import this package; the product path
 
 * ``kda_fwd`` / ``kda_step`` call the C oracle (``kda_oracle.c``), a token-by-token
   fp64 recurrence, OpenMP-parallel over independent (sequence, head) units.
+* ``kda_bwd`` calls the C oracle's gradient: reverse mode of the same token
+  recurrence, the chain rule applied to each step of a token in reverse order.
 * ``twin`` is a second, independently written numpy implementation that uses the
   pages' matrix-product form instead of the delta form.
 
@@ -52,6 +54,10 @@ def load_library(path: str):
     lib.oracle_kda_fwd.restype = i32
     lib.oracle_kda_step.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, vp, i32, i32]
     lib.oracle_kda_step.restype = i32
+    lib.oracle_kda_bwd.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i64p,
+                                   i32, i32, i32, i32, i32, i32, vp, i32, vp, i32,
+                                   vp, vp, vp, vp, vp, vp, i32]
+    lib.oracle_kda_bwd.restype = i32
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = i32
     return lib
@@ -143,3 +149,50 @@ def kda_step(q, k, v, log_alpha, beta, S, o_dtype=np.float32, num_threads: int =
     if rc != 0:
         raise ValueError("oracle_kda_step rejected its arguments")
     return o
+
+
+def kda_bwd(q, k, v, log_alpha, beta, d_o, S0=None, cu_seqlens=None, dS_final=None,
+            num_threads: int = 0, lib=None):
+    """Gradient of ``kda_fwd``'s (o, S_final) against the upstream gradients d_o
+    [B, T, H, Dv] and dS_final [N, H, Dk, Dv] (None = zero).  Inputs as for
+    ``kda_fwd``; d_o and dS_final may be float64, float32 or bf16 bits.  Returns a
+    dict of float64 arrays dq, dk, dv, dlog_alpha, dbeta, dS0 shaped like q, k, v,
+    log_alpha, beta and S0 ([N, H, Dk, Dv])."""
+    arrs = [np.ascontiguousarray(x) for x in (q, k, v, log_alpha, beta)]
+    dt = _dtype_code(arrs[0])
+    if any(_dtype_code(a) != dt for a in arrs):
+        raise TypeError("q, k, v, log_alpha, beta must share one dtype")
+    q, k, v, log_alpha, beta = arrs
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if k.shape != q.shape or log_alpha.shape != q.shape or v.shape != (B, T, H, Dv) \
+            or beta.shape != (B, T, H):
+        raise ValueError("shape mismatch")
+    d_o = np.ascontiguousarray(d_o)
+    if d_o.shape != (B, T, H, Dv):
+        raise ValueError("d_o shape mismatch")
+    cu = None
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        N = cu.size - 1
+    else:
+        N = B
+    s0 = None if S0 is None else np.ascontiguousarray(S0)
+    dsf = None if dS_final is None else np.ascontiguousarray(dS_final)
+    for a in (s0, dsf):
+        if a is not None and a.shape != (N, H, Dk, Dv):
+            raise ValueError("state shape mismatch")
+    out = dict(dq=np.zeros((B, T, H, Dk)), dk=np.zeros((B, T, H, Dk)), dv=np.zeros((B, T, H, Dv)),
+               dlog_alpha=np.zeros((B, T, H, Dk)), dbeta=np.zeros((B, T, H)),
+               dS0=np.zeros((N, H, Dk, Dv)))
+    rc = (lib or _load()).oracle_kda_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), dt,
+        _ptr(s0), _dtype_code(s0) if s0 is not None else F64,
+        cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)) if cu is not None else None,
+        B, T, H, Dk, Dv, N, _ptr(d_o), _dtype_code(d_o),
+        _ptr(dsf), _dtype_code(dsf) if dsf is not None else F64,
+        _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlog_alpha"]),
+        _ptr(out["dbeta"]), _ptr(out["dS0"]), int(num_threads))
+    if rc != 0:
+        raise ValueError("oracle_kda_bwd rejected its arguments")
+    return out

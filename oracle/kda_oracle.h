@@ -58,6 +58,22 @@ int oracle_kda_step(const void* q, const void* k, const void* v, const void* log
                     double* S, int N, int H, int Dk, int Dv,
                     void* o, int o_dtype, int num_threads);
 
+/* Gradient of oracle_kda_fwd (exact reverse mode of the token recurrence, fp64).
+ * d_o [B, T, H, Dv] (element type do_dtype) is the gradient of the loss with
+ * respect to o; dS_final [N, H, Dk, Dv] (element type dsf_dtype) the gradient with
+ * respect to S_final, or NULL for zero.  Outputs, all fp64 and fully written for
+ * every token of every sequence: dq, dk, dlog_alpha [B, T, H, Dk], dv [B, T, H, Dv],
+ * dbeta [B, T, H], and dS0 [N, H, Dk, Dv] (may be NULL).  Other arguments as in
+ * oracle_kda_fwd.  Keeps every state of a (sequence, head) in memory. */
+int oracle_kda_bwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                   const void* beta, int in_dtype,
+                   const void* S0, int s0_dtype,
+                   const int64_t* cu_seqlens,
+                   int B, int T, int H, int Dk, int Dv, int num_seqs,
+                   const void* d_o, int do_dtype, const void* dS_final, int dsf_dtype,
+                   double* dq, double* dk, double* dv, double* dlog_alpha, double* dbeta,
+                   double* dS0, int num_threads);
+
 /* Threads the OpenMP runtime would use for num_threads <= 0. */
 int oracle_max_threads(void);
 
