@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_PATH = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_prefill.hip"]
+SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_prefill.hip", "kda_backward.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # gfx950 only.  Packed-fp32 VALU ops are disabled for all device code.

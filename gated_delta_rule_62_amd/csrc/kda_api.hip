@@ -313,3 +313,77 @@ extern "C" kda_status kda_recurrent_step_fused(const void* q, const void* k, con
     return recurrent_step_impl(q, k, v, log_alpha, beta, S_in, S_out, N, H, Dk, Dv, in_dtype, out_dtype, o, stream,
                                false, fusion);
 }
+
+extern "C" size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int num_seqs,
+                                                int has_cu_seqlens, int chunk) {
+    if (B < 0 || T < 0 || H <= 0 || num_seqs < 0 || !head_ok(Dk, Dv)) return 0;
+    if (chunk != 0 && chunk != 32) return 0;
+    return kda::plan_backward(B, T, H, Dk, num_seqs, has_cu_seqlens != 0).workspace_bytes;
+}
+
+extern "C" kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                                    const void* beta, const float* S0, const int32_t* cu_seqlens,
+                                    const void* d_o, const float* dS_final,
+                                    int B, int T, int H, int Dk, int Dv, int num_seqs, int chunk,
+                                    kda_dtype in_dtype, kda_dtype grad_dtype,
+                                    void* dq, void* dk, void* dv, void* dlog_alpha, void* dbeta, float* dS0,
+                                    void* workspace, size_t workspace_bytes, kda_stream_t stream) {
+    if (B < 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || num_seqs < 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (!dtype_ok(in_dtype) || !dtype_ok(grad_dtype)) return KDA_ERR_UNSUPPORTED;
+    if (!head_ok(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
+    if (chunk != 0 && chunk != 32) return KDA_ERR_UNSUPPORTED;
+    if (cu_seqlens) {
+        if (B != 1 || !aligned16(cu_seqlens)) return KDA_ERR_INVALID_ARGUMENT;
+    } else if (num_seqs != B) {
+        return KDA_ERR_INVALID_ARGUMENT;
+    }
+    const size_t tokens = static_cast<size_t>(B) * static_cast<size_t>(T);
+    const bool work = tokens > 0 && num_seqs > 0;
+    const void* ins[6] = {q, k, v, log_alpha, beta, d_o};
+    void* outs[5] = {dq, dk, dv, dlog_alpha, dbeta};
+    if (work) {
+        for (const void* x : ins)
+            if (!x || !aligned16(x)) return KDA_ERR_INVALID_ARGUMENT;
+        for (const void* x : outs)
+            if (!x || !aligned16(x)) return KDA_ERR_INVALID_ARGUMENT;
+    }
+    if ((S0 && !aligned16(S0)) || (dS_final && !aligned16(dS_final)) || (dS0 && !aligned16(dS0)))
+        return KDA_ERR_INVALID_ARGUMENT;
+
+    const size_t ein = elem_size(in_dtype), eg = elem_size(grad_dtype);
+    const size_t n_x = tokens * H * Dk, n_b = tokens * H;
+    const size_t n_s = static_cast<size_t>(num_seqs) * H * Dk * Dv * sizeof(float);
+    const size_t nin[6] = {n_x * ein, n_x * ein, n_x * ein, n_x * ein, n_b * ein, n_x * ein};
+    const size_t nout[5] = {n_x * eg, n_x * eg, n_x * eg, n_x * eg, n_b * eg};
+    kda::BackwardPlan plan = kda::plan_backward(B, T, H, Dk, num_seqs, cu_seqlens != nullptr);
+    // every output is disjoint from every input, from the other outputs and from the workspace
+    for (int o = 0; o < 6; ++o) {
+        const void* po = o < 5 ? outs[o] : dS0;
+        const size_t no = o < 5 ? (work ? nout[o] : 0) : n_s;
+        for (int i = 0; i < 6; ++i)
+            if (overlap(ins[i], work ? nin[i] : 0, po, no)) return KDA_ERR_INVALID_ARGUMENT;
+        if (overlap(S0, n_s, po, no) || overlap(dS_final, n_s, po, no)) return KDA_ERR_INVALID_ARGUMENT;
+        for (int o2 = o + 1; o2 < 6; ++o2) {
+            const void* p2 = o2 < 5 ? outs[o2] : dS0;
+            const size_t n2 = o2 < 5 ? (work ? nout[o2] : 0) : n_s;
+            if (overlap(po, no, p2, n2)) return KDA_ERR_INVALID_ARGUMENT;
+        }
+        if (overlap(workspace, plan.workspace_bytes, po, no)) return KDA_ERR_INVALID_ARGUMENT;
+    }
+    if (workspace_bytes < plan.workspace_bytes) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    if (plan.workspace_bytes > 0 && (!workspace || !aligned16(workspace))) return KDA_ERR_INVALID_ARGUMENT;
+    if (num_seqs == 0) return KDA_OK;
+    // grid sizes and token indices are 32-bit on the device
+    const size_t units = static_cast<size_t>(num_seqs) * H;
+    if (plan.nc_max * H > 0x7fffffffu || units * (Dk / 16) > 0x7fffffffu || tokens > 0x7fffffffu)
+        return KDA_ERR_UNSUPPORTED;
+
+    kda::BackwardArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = log_alpha; a.beta = beta; a.dO = d_o;
+    a.S0 = S0; a.dS_final = dS_final; a.cu = cu_seqlens;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dlog_alpha; a.dbeta = dbeta; a.dS0 = dS0;
+    a.B = B; a.T = T; a.H = H; a.D = Dk; a.N = num_seqs;
+    a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = grad_dtype == KDA_BF16;
+    hipError_t err = kda::launch_backward(a, plan, workspace, reinterpret_cast<hipStream_t>(stream));
+    return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}

@@ -1,0 +1,684 @@
+// kda_backward.hip -- gradient of the chunkwise KDA prefill on gfx950.
+//
+// The forward is the chunkwise form of "Decoding Hybrid Attention Architectures"
+// (intl.cloud.baidu.com article 9569726), section 4, for the fine-grained gated
+// delta rule of its section 3.4; the pages motivate the chunk form by training
+// throughput (section 4) but give no backward, so this is the chain rule through that
+// form.  Per chunk of C tokens (ragged tails are padded with zero q, k, v, beta and
+// zero log-decay, which changes nothing), entry state S, chunk-local cumulative
+// log-decay b and m = b at the chunk's midpoint row:
+//
+//   Q' = Q e^{b-m}, K' = K e^{b-m}, K'' = K e^{m-b}, e_m = e^m, e_n = e^{b_last-m}
+//   L = StrictTril(K' K''^T), M = (I + Diag(beta) L)^-1, P = Tril(Q' K''^T)
+//   S_m = Diag(e_m) S,  R = V - K' S_m,  E = M Diag(beta) R
+//   O = Q' S_m + P E,   S_next = Diag(e_n)(S_m + K''^T E)
+//
+// and with dS_n = Diag(e_n) dS_next (dS_next: gradient with respect to the exit state)
+//
+//   dE = P^T dO + K'' dS_n,  dY = M^T dE,  dV = Diag(beta) dY
+//   dS = Diag(e_m)(dS_n + Q'^T dO - K'^T dV)                       (entry-state gradient)
+//   dbeta = rowsum(dY R) + rowsum(dA L),  dA = -StrictTril(dY E^T),  dL = Diag(beta) dA
+//   dP = Tril(dO E^T)
+//   dQ' = dO S_m^T + dP K'',  dK' = -dV S_m^T + dL K'',  dK'' = dP^T Q' + dL^T K' + E dS_n^T
+//   dq = e^{b-m} dQ',  dk = e^{b-m} dK' + e^{m-b} dK''
+//   db = Q' dQ' + K' dK' - K'' dK'' (+ rowsum(dS_next S_next) on the last row)
+//   dlog_alpha = reverse cumulative sum of db over the chunk's rows.
+//
+// Kernels (all products on the fp32 matrix cores, v_mfma_f32_16x16x4_f32, operands
+// from LDS):
+//   seq_scan_kernel   packed batches: first chunk index of every sequence
+//   prep_kernel       per (chunk, head): Q', K', K'', M, P, L, e_m, e_n, beta -> record
+//   state_fwd_kernel  per (sequence, head, 16 value columns): every chunk's entry state
+//                     and the final state, chunks in order
+//   state_rev_kernel  same split: every chunk's dS_next, chunks in reverse order; dS0
+//   grad_kernel       per (chunk, head): dq, dk, dv, dlog_alpha, dbeta
+// The state passes are independent per value column because every operator of the
+// recurrence multiplies the state from the left.
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+namespace {
+
+constexpr int BC = 32;    // chunk length
+constexpr int BT = 256;   // threads per workgroup (4 waves)
+constexpr int TW = 16;    // value columns per state-pass workgroup
+constexpr int GW = 32;    // value columns per step of the gradient kernel
+
+using f4 = __attribute__((__vector_size__(4 * sizeof(float)))) float;
+
+// Offsets (in floats) inside the per-(chunk, head) record written by prep_kernel.
+template <int D>
+struct Rec {
+    static constexpr int QP = 0, KP = BC * D, KPP = 2 * BC * D, M = 3 * BC * D, P = M + BC * BC,
+                         L = P + BC * BC, EM = L + BC * BC, EN = EM + D, BETA = EN + D, SIZE = BETA + BC;
+    static_assert(SIZE % 4 == 0, "records must stay 16-byte aligned");
+};
+
+template <class IN>
+__device__ __forceinline__ float ld_in(const void* p, size_t i) {
+    return IN::to_f32(static_cast<const typename IN::storage*>(p)[i]);
+}
+
+// ---------------------------------------------------------------- chunk addressing
+// Sequence n owns chunks [chunk0(n), chunk0(n+1)) and state slots chunk0(n) + n + i,
+// i = 0..chunks(n) (the last one holds the final state).
+__device__ __forceinline__ int chunk0(const BackwardArgs& a, int n) {
+    return a.cu ? a.seq_chunk0[n] : n * ((a.T + BC - 1) / BC);
+}
+
+__device__ __forceinline__ int seq_first_token(const BackwardArgs& a, int n) {
+    return a.cu ? a.cu[n] : n * a.T;
+}
+
+__device__ __forceinline__ int seq_len(const BackwardArgs& a, int n) {
+    return a.cu ? max(a.cu[n + 1] - a.cu[n], 0) : a.T;
+}
+
+struct ChunkPos {
+    int n, i, t0, len;   // sequence, chunk within it, first token row of [B*T], valid rows
+};
+
+__device__ bool chunk_pos(const BackwardArgs& a, int j, ChunkPos& p) {
+    int n;
+    if (!a.cu) {
+        const int cps = (a.T + BC - 1) / BC;
+        if (cps == 0) return false;
+        n = j / cps;
+        if (n >= a.B) return false;
+    } else {
+        const int32_t* sc = a.seq_chunk0;
+        if (j >= sc[a.N]) return false;
+        int lo = 0, hi = a.N - 1;   // last n with sc[n] <= j; then sc[n + 1] > j
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (sc[mid] <= j) lo = mid;
+            else hi = mid - 1;
+        }
+        n = lo;
+    }
+    p.n = n;
+    p.i = j - chunk0(a, n);
+    p.t0 = seq_first_token(a, n) + p.i * BC;
+    p.len = min(BC, seq_len(a, n) - p.i * BC);
+    return true;
+}
+
+// ---------------------------------------------------------------- matrix-core helpers
+// acc (16 x 16) += A (16 x K) B (K x 16), A(i, k) = A[i*ai + k*ak], B(k, j) = B[k*bk + j*bj].
+// Lane l supplies A(l % 16, k0 + l / 16) and B(k0 + l / 16, l % 16) for each 4-deep step
+// and holds C(4 (l / 16) + v, l % 16) in acc[v].
+template <int K>
+__device__ __forceinline__ void mma(f4& acc, const float* A, int ai, int ak, const float* B, int bk, int bj) {
+    const int lane = threadIdx.x & 63, i = lane & 15, kq = lane >> 4;
+    const float* pa = A + i * ai + kq * ak;
+    const float* pb = B + kq * bk + i * bj;
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k0 * ak], pb[k0 * bk], acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ int acc_row(int v) { return 4 * ((threadIdx.x & 63) >> 4) + v; }
+__device__ __forceinline__ int acc_col() { return threadIdx.x & 15; }
+
+__device__ __forceinline__ f4 zero4() { return f4{0.f, 0.f, 0.f, 0.f}; }
+
+// rows x cols fp32 block between global memory (dense, row stride gs) and LDS (row stride ls)
+template <int ROWS, int COLS>
+__device__ __forceinline__ void g2s(float* s, int ls, const float* g, size_t gs) {
+    static_assert(COLS % 4 == 0, "");
+    for (int e = threadIdx.x; e < ROWS * COLS / 4; e += BT) {
+        const int r = e / (COLS / 4), c = 4 * (e % (COLS / 4));
+        const float4 x = *reinterpret_cast<const float4*>(g + r * gs + c);
+        *reinterpret_cast<float4*>(s + r * ls + c) = x;
+    }
+}
+
+template <int ROWS, int COLS>
+__device__ __forceinline__ void s2g(float* g, size_t gs, const float* s, int ls) {
+    static_assert(COLS % 4 == 0, "");
+    for (int e = threadIdx.x; e < ROWS * COLS / 4; e += BT) {
+        const int r = e / (COLS / 4), c = 4 * (e % (COLS / 4));
+        *reinterpret_cast<float4*>(g + r * gs + c) = *reinterpret_cast<const float4*>(s + r * ls + c);
+    }
+}
+
+// One chunk's rows of a [B*T, H, W] input (W columns starting at col0) into LDS as
+// fp32; rows past len are zero.
+template <class IN, int COLS>
+__device__ __forceinline__ void load_rows(float* s, int ls, const void* x, int t0, int len, int H, int h,
+                                          int W, int col0) {
+    for (int e = threadIdx.x; e < BC * COLS; e += BT) {
+        const int r = e / COLS, c = e % COLS;
+        s[r * ls + c] = r < len ? ld_in<IN>(x, ((size_t)(t0 + r) * H + h) * W + col0 + c) : 0.f;
+    }
+}
+
+// Maps a linear workgroup index to (unit, column tile) so that the tiles of one unit
+// land on one XCD (workgroups are dealt to the 8 XCDs round-robin) and share its L2.
+__device__ __forceinline__ void unit_tile(int b, int nwg, int ntile, int& unit, int& tile) {
+    int idx = b;
+    if (nwg % 8 == 0) idx = (b % 8) * (nwg / 8) + b / 8;
+    unit = idx / ntile;
+    tile = idx % ntile;
+}
+
+// ---------------------------------------------------------------- kernels
+__global__ __launch_bounds__(BT) void seq_scan_kernel(const int32_t* cu, int N, int32_t* sc) {
+    __shared__ int32_t buf[BT];
+    __shared__ int32_t carry;
+    if (threadIdx.x == 0) carry = 0;
+    __syncthreads();
+    for (int base = 0; base < N; base += BT) {
+        const int n = base + threadIdx.x;
+        const int c = n < N ? (max(cu[n + 1] - cu[n], 0) + BC - 1) / BC : 0;
+        buf[threadIdx.x] = c;
+        __syncthreads();
+        for (int off = 1; off < BT; off <<= 1) {
+            const int x = threadIdx.x >= off ? buf[threadIdx.x - off] : 0;
+            __syncthreads();
+            buf[threadIdx.x] += x;
+            __syncthreads();
+        }
+        const int incl = buf[threadIdx.x];
+        if (n < N) sc[n] = carry + incl - c;
+        __syncthreads();
+        if (threadIdx.x == BT - 1) carry += incl;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) sc[N] = carry;
+}
+
+template <int D, class IN>
+__global__ __launch_bounds__(BT) void prep_kernel(BackwardArgs a) {
+    constexpr int LD = D + 4, LC = BC + 4;
+    __shared__ __attribute__((aligned(16))) float sQ[BC * LD], sK[BC * LD], sKpp[BC * LD], sG[BC * LD];
+    __shared__ __attribute__((aligned(16))) float sL[BC * LC], sP[BC * LC];
+    __shared__ float sB[BC], sEm[D], sEn[D];
+    const int j = blockIdx.x / a.H, h = blockIdx.x % a.H;
+    ChunkPos p;
+    if (!chunk_pos(a, j, p)) return;
+    const int tid = threadIdx.x, w = tid >> 6;
+
+    load_rows<IN, D>(sQ, LD, a.q, p.t0, p.len, a.H, h, D, 0);
+    load_rows<IN, D>(sK, LD, a.k, p.t0, p.len, a.H, h, D, 0);
+    load_rows<IN, D>(sG, LD, a.g, p.t0, p.len, a.H, h, D, 0);
+    if (tid < BC) sB[tid] = tid < p.len ? ld_in<IN>(a.beta, (size_t)(p.t0 + tid) * a.H + h) : 0.f;
+    __syncthreads();
+
+    if (tid < D) {
+        float b = 0.f;
+        for (int r = 0; r < BC; ++r) {
+            b += sG[r * LD + tid];
+            sG[r * LD + tid] = b;
+        }
+        const float m = sG[(BC / 2 - 1) * LD + tid];
+        for (int r = 0; r < BC; ++r) {
+            const float x = sG[r * LD + tid] - m;
+            const float up = fast_exp(x), dn = fast_exp(-x);
+            const float kv = sK[r * LD + tid];
+            sQ[r * LD + tid] *= up;
+            sK[r * LD + tid] = kv * up;
+            sKpp[r * LD + tid] = kv * dn;
+        }
+        sEm[tid] = fast_exp(m);
+        sEn[tid] = fast_exp(b - m);
+    }
+    __syncthreads();
+
+    // L and P: the three lower 16x16 tiles of each (the upper-right tile is zero)
+    for (int t = w; t < 6; t += 4) {
+        const bool isP = t >= 3;
+        const int tt = t % 3, ti = tt == 0 ? 0 : 1, tj = tt == 2 ? 1 : 0;
+        f4 acc = zero4();
+        mma<D>(acc, (isP ? sQ : sK) + 16 * ti * LD, LD, 1, sKpp + 16 * tj * LD, 1, LD);
+        float* out = isP ? sP : sL;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int r = 16 * ti + acc_row(v), c = 16 * tj + acc_col();
+            out[r * LC + c] = (isP ? r >= c : r > c) ? acc[v] : 0.f;
+        }
+    }
+    {
+        const int r = tid / 16, c = 16 + tid % 16;
+        sL[r * LC + c] = 0.f;
+        sP[r * LC + c] = 0.f;
+    }
+    __syncthreads();
+
+    float* rec = a.prep + ((size_t)j * a.H + h) * Rec<D>::SIZE;
+    if (tid < BC) {
+        // M = (I + Diag(beta) L)^-1 by forward substitution; lane tid owns column tid
+        float col[BC];
+#pragma unroll
+        for (int r = 0; r < BC; ++r) {
+            float s = r == tid ? 1.f : 0.f;
+            const float br = sB[r];
+#pragma unroll
+            for (int i = 0; i < r; ++i) s -= br * sL[r * LC + i] * col[i];
+            col[r] = s;
+        }
+#pragma unroll
+        for (int r = 0; r < BC; ++r) rec[Rec<D>::M + r * BC + tid] = col[r];
+    }
+    s2g<BC, D>(rec + Rec<D>::QP, D, sQ, LD);
+    s2g<BC, D>(rec + Rec<D>::KP, D, sK, LD);
+    s2g<BC, D>(rec + Rec<D>::KPP, D, sKpp, LD);
+    s2g<BC, BC>(rec + Rec<D>::P, BC, sP, LC);
+    s2g<BC, BC>(rec + Rec<D>::L, BC, sL, LC);
+    if (tid < D) {
+        rec[Rec<D>::EM + tid] = sEm[tid];
+        rec[Rec<D>::EN + tid] = sEn[tid];
+    }
+    if (tid < BC) rec[Rec<D>::BETA + tid] = sB[tid];
+}
+
+template <int D, class IN>
+__global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
+    constexpr int LD = D + 4, LC = BC + 4, LT = TW + 4, NTILE = D / TW;
+    __shared__ __attribute__((aligned(16))) float sKp[BC * LD], sKpp[BC * LD], sM[BC * LC];
+    __shared__ __attribute__((aligned(16))) float sS[D * LT], sR[2 * BC * LT], sE[BC * LT], sV[BC * LT];
+    __shared__ float sB[BC], sEm[D], sEn[D];
+    int u, jt;
+    unit_tile(blockIdx.x, gridDim.x, NTILE, u, jt);
+    const int n = u / a.H, h = u % a.H, tid = threadIdx.x, w = tid >> 6;
+    const int c0 = chunk0(a, n), L = seq_len(a, n), nch = (L + BC - 1) / BC, tok0 = seq_first_token(a, n);
+    const size_t DD = (size_t)D * D;
+    for (int e = tid; e < D * TW; e += BT) {
+        const int r = e / TW, c = e % TW;
+        sS[r * LT + c] = a.S0 ? a.S0[(size_t)u * DD + (size_t)r * D + jt * TW + c] : 0.f;
+    }
+    for (int i = 0; i < nch; ++i) {
+        const int j = c0 + i, t0 = tok0 + i * BC, len = min(BC, L - i * BC);
+        const float* rec = a.prep + ((size_t)j * a.H + h) * Rec<D>::SIZE;
+        __syncthreads();
+        g2s<BC, D>(sKp, LD, rec + Rec<D>::KP, D);
+        g2s<BC, D>(sKpp, LD, rec + Rec<D>::KPP, D);
+        g2s<BC, BC>(sM, LC, rec + Rec<D>::M, BC);
+        if (tid < D) {
+            sEm[tid] = rec[Rec<D>::EM + tid];
+            sEn[tid] = rec[Rec<D>::EN + tid];
+        }
+        if (tid < BC) sB[tid] = rec[Rec<D>::BETA + tid];
+        load_rows<IN, TW>(sV, LT, a.v, t0, len, a.H, h, D, jt * TW);
+        __syncthreads();
+        // keep the entry state, then scale it to S_m
+        float* slot = a.states + ((size_t)(c0 + n + i) * a.H + h) * DD + jt * TW;
+        for (int e = tid; e < D * TW; e += BT) {
+            const int r = e / TW, c = e % TW;
+            const float x = sS[r * LT + c];
+            slot[(size_t)r * D + c] = x;
+            sS[r * LT + c] = x * sEm[r];
+        }
+        __syncthreads();
+        {   // K' S_m, the key-channel sum split in two halves over the waves
+            const int rt = w & 1, kh = w >> 1;
+            f4 acc = zero4();
+            mma<D / 2>(acc, sKp + 16 * rt * LD + kh * (D / 2), LD, 1, sS + kh * (D / 2) * LT, LT, 1);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sR[kh * BC * LT + (16 * rt + acc_row(v)) * LT + acc_col()] = acc[v];
+        }
+        __syncthreads();
+        for (int e = tid; e < BC * TW; e += BT) {
+            const int r = e / TW, c = e % TW;
+            sR[r * LT + c] = sB[r] * (sV[r * LT + c] - sR[r * LT + c] - sR[BC * LT + r * LT + c]);
+        }
+        __syncthreads();
+        if (w < 2) {   // E = M Y
+            f4 acc = zero4();
+            mma<BC>(acc, sM + 16 * w * LC, LC, 1, sR, LT, 1);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sE[(16 * w + acc_row(v)) * LT + acc_col()] = acc[v];
+        }
+        __syncthreads();
+        for (int rt = w; rt < D / 16; rt += 4) {   // S_next = Diag(e_n)(S_m + K''^T E)
+            f4 acc;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[v] = sS[(16 * rt + acc_row(v)) * LT + acc_col()];
+            mma<BC>(acc, sKpp + 16 * rt, 1, LD, sE, LT, 1);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int r = 16 * rt + acc_row(v);
+                sS[r * LT + acc_col()] = acc[v] * sEn[r];
+            }
+        }
+    }
+    __syncthreads();
+    float* slot = a.states + ((size_t)(c0 + n + nch) * a.H + h) * DD + jt * TW;
+    for (int e = tid; e < D * TW; e += BT) {
+        const int r = e / TW, c = e % TW;
+        slot[(size_t)r * D + c] = sS[r * LT + c];
+    }
+}
+
+template <int D, class IN>
+__global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
+    constexpr int LD = D + 4, LC = BC + 4, LT = TW + 4, NTILE = D / TW;
+    __shared__ __attribute__((aligned(16))) float sQp[BC * LD], sKp[BC * LD], sKpp[BC * LD];
+    __shared__ __attribute__((aligned(16))) float sM[BC * LC], sP[BC * LC];
+    __shared__ __attribute__((aligned(16))) float sS[D * LT], sO[BC * LT], sR[2 * BC * LT], sV[BC * LT];
+    __shared__ float sB[BC], sEm[D], sEn[D];
+    int u, jt;
+    unit_tile(blockIdx.x, gridDim.x, NTILE, u, jt);
+    const int n = u / a.H, h = u % a.H, tid = threadIdx.x, w = tid >> 6;
+    const int c0 = chunk0(a, n), L = seq_len(a, n), nch = (L + BC - 1) / BC, tok0 = seq_first_token(a, n);
+    const size_t DD = (size_t)D * D;
+    for (int e = tid; e < D * TW; e += BT) {
+        const int r = e / TW, c = e % TW;
+        sS[r * LT + c] = a.dS_final ? a.dS_final[(size_t)u * DD + (size_t)r * D + jt * TW + c] : 0.f;
+    }
+    for (int i = nch - 1; i >= 0; --i) {
+        const int j = c0 + i, t0 = tok0 + i * BC, len = min(BC, L - i * BC);
+        const float* rec = a.prep + ((size_t)j * a.H + h) * Rec<D>::SIZE;
+        __syncthreads();
+        g2s<BC, D>(sQp, LD, rec + Rec<D>::QP, D);
+        g2s<BC, D>(sKp, LD, rec + Rec<D>::KP, D);
+        g2s<BC, D>(sKpp, LD, rec + Rec<D>::KPP, D);
+        g2s<BC, BC>(sM, LC, rec + Rec<D>::M, BC);
+        g2s<BC, BC>(sP, LC, rec + Rec<D>::P, BC);
+        if (tid < D) {
+            sEm[tid] = rec[Rec<D>::EM + tid];
+            sEn[tid] = rec[Rec<D>::EN + tid];
+        }
+        if (tid < BC) sB[tid] = rec[Rec<D>::BETA + tid];
+        load_rows<IN, TW>(sO, LT, a.dO, t0, len, a.H, h, D, jt * TW);
+        __syncthreads();
+        // keep this chunk's dS_next, then scale it to dS_n
+        float* slot = a.dstates + ((size_t)j * a.H + h) * DD + jt * TW;
+        for (int e = tid; e < D * TW; e += BT) {
+            const int r = e / TW, c = e % TW;
+            const float x = sS[r * LT + c];
+            slot[(size_t)r * D + c] = x;
+            sS[r * LT + c] = x * sEn[r];
+        }
+        __syncthreads();
+        {   // dE = P^T dO + K'' dS_n, the key-channel sum split in two halves over the waves
+            const int rt = w & 1, kh = w >> 1;
+            f4 acc = zero4();
+            mma<D / 2>(acc, sKpp + 16 * rt * LD + kh * (D / 2), LD, 1, sS + kh * (D / 2) * LT, LT, 1);
+            if (kh == 0) mma<BC>(acc, sP + 16 * rt, 1, LC, sO, LT, 1);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sR[kh * BC * LT + (16 * rt + acc_row(v)) * LT + acc_col()] = acc[v];
+        }
+        __syncthreads();
+        for (int e = tid; e < BC * TW; e += BT) {
+            const int r = e / TW, c = e % TW;
+            sR[r * LT + c] += sR[BC * LT + r * LT + c];
+        }
+        __syncthreads();
+        if (w < 2) {   // -dV = -Diag(beta) M^T dE
+            f4 acc = zero4();
+            mma<BC>(acc, sM + 16 * w, 1, LC, sR, LT, 1);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int r = 16 * w + acc_row(v);
+                sV[r * LT + acc_col()] = -sB[r] * acc[v];
+            }
+        }
+        __syncthreads();
+        for (int rt = w; rt < D / 16; rt += 4) {   // dS = Diag(e_m)(dS_n + Q'^T dO - K'^T dV)
+            f4 acc;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[v] = sS[(16 * rt + acc_row(v)) * LT + acc_col()];
+            mma<BC>(acc, sQp + 16 * rt, 1, LD, sO, LT, 1);
+            mma<BC>(acc, sKp + 16 * rt, 1, LD, sV, LT, 1);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int r = 16 * rt + acc_row(v);
+                sS[r * LT + acc_col()] = acc[v] * sEm[r];
+            }
+        }
+    }
+    __syncthreads();
+    if (a.dS0) {
+        for (int e = tid; e < D * TW; e += BT) {
+            const int r = e / TW, c = e % TW;
+            a.dS0[(size_t)u * DD + (size_t)r * D + jt * TW + c] = sS[r * LT + c];
+        }
+    }
+}
+
+template <int D, class IN, bool OB>
+__global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
+    constexpr int LD = D + 4, LC = BC + 4, LT = GW + 4, NCT = D / GW;
+    constexpr int CT_PER_WAVE = D / 16 / 4;   // 16-column tiles of D owned by each wave
+    static_assert(LT == LC, "the C x C products reuse C x GW buffers");
+    static_assert(BC * LD <= D * LT, "the decay and db planes reuse the state tiles");
+    __shared__ __attribute__((aligned(16))) float sQp[BC * LD], sKp[BC * LD], sKpp[BC * LD];
+    __shared__ __attribute__((aligned(16))) float sM[BC * LC], sP[BC * LC], sL[BC * LC];
+    __shared__ __attribute__((aligned(16))) float sSm[D * LT], sdSn[D * LT];
+    __shared__ __attribute__((aligned(16))) float sV[BC * LT], sY[BC * LT], sO[BC * LT], sE[BC * LT];
+    __shared__ __attribute__((aligned(16))) float sdE[BC * LT], sdY[BC * LT], smdV[BC * LT];
+    __shared__ float sB[BC], sEm[D], sEn[D], sDbn[D];
+    const int j = blockIdx.x / a.H, h = blockIdx.x % a.H;
+    ChunkPos p;
+    if (!chunk_pos(a, j, p)) return;
+    const int tid = threadIdx.x, w = tid >> 6;
+    const size_t DD = (size_t)D * D;
+    const float* rec = a.prep + ((size_t)j * a.H + h) * Rec<D>::SIZE;
+    g2s<BC, D>(sQp, LD, rec + Rec<D>::QP, D);
+    g2s<BC, D>(sKp, LD, rec + Rec<D>::KP, D);
+    g2s<BC, D>(sKpp, LD, rec + Rec<D>::KPP, D);
+    g2s<BC, BC>(sM, LC, rec + Rec<D>::M, BC);
+    g2s<BC, BC>(sP, LC, rec + Rec<D>::P, BC);
+    g2s<BC, BC>(sL, LC, rec + Rec<D>::L, BC);
+    if (tid < D) {
+        sEm[tid] = rec[Rec<D>::EM + tid];
+        sEn[tid] = rec[Rec<D>::EN + tid];
+        sDbn[tid] = 0.f;
+    }
+    if (tid < BC) sB[tid] = rec[Rec<D>::BETA + tid];
+
+    const size_t slot = (size_t)(chunk0(a, p.n) + p.n + p.i);
+    const float* S = a.states + (slot * a.H + h) * DD;
+    const float* Snext = a.states + ((slot + 1) * a.H + h) * DD;
+    const float* dS = a.dstates + ((size_t)j * a.H + h) * DD;
+
+    f4 dQp[2][CT_PER_WAVE], dKp[2][CT_PER_WAVE], dKpp[2][CT_PER_WAVE];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int q = 0; q < CT_PER_WAVE; ++q) dQp[rt][q] = dKp[rt][q] = dKpp[rt][q] = zero4();
+    f4 dPacc = zero4(), dYE = zero4();
+    float dbeta = 0.f;
+    const int trt = w & 1, tct = w >> 1;   // this wave's C x GW tile (and C x C tile)
+
+    for (int ct = 0; ct < NCT; ++ct) {
+        __syncthreads();
+        load_rows<IN, GW>(sV, LT, a.v, p.t0, p.len, a.H, h, D, ct * GW);
+        load_rows<IN, GW>(sO, LT, a.dO, p.t0, p.len, a.H, h, D, ct * GW);
+        // S_m, dS_n tiles; rowsum(dS_next * S_next) for the last row's db
+        for (int e = tid; e < D * GW; e += BT) {
+            const int r = e / GW, c = e % GW;
+            const size_t gi = (size_t)r * D + ct * GW + c;
+            const float x = S[gi], y = dS[gi];
+            float t = y * Snext[gi];
+            sSm[r * LT + c] = x * sEm[r];
+            sdSn[r * LT + c] = y * sEn[r];
+            // the 32 columns of row r sit in 32 consecutive lanes
+#pragma unroll
+            for (int off = 16; off >= 1; off >>= 1) t += __shfl_xor(t, off, 64);
+            if (c == 0) sDbn[r] += t;
+        }
+        __syncthreads();
+        {
+            f4 acc = zero4();   // R = V - K' S_m;  Y = Diag(beta) R
+            mma<D>(acc, sKp + 16 * trt * LD, LD, 1, sSm + 16 * tct, LT, 1);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int r = 16 * trt + acc_row(v), c = 16 * tct + acc_col();
+                const float x = sV[r * LT + c] - acc[v];
+                sV[r * LT + c] = x;
+                sY[r * LT + c] = sB[r] * x;
+            }
+            f4 d = zero4();     // dE = P^T dO + K'' dS_n
+            mma<BC>(d, sP + 16 * trt, 1, LC, sO + 16 * tct, LT, 1);
+            mma<D>(d, sKpp + 16 * trt * LD, LD, 1, sdSn + 16 * tct, LT, 1);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sdE[(16 * trt + acc_row(v)) * LT + 16 * tct + acc_col()] = d[v];
+        }
+        __syncthreads();
+        {
+            f4 e = zero4();     // E = M Y
+            mma<BC>(e, sM + 16 * trt * LC, LC, 1, sY + 16 * tct, LT, 1);
+            f4 y = zero4();     // dY = M^T dE
+            mma<BC>(y, sM + 16 * trt, 1, LC, sdE + 16 * tct, LT, 1);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int r = 16 * trt + acc_row(v), c = 16 * tct + acc_col();
+                sE[r * LT + c] = e[v];
+                sdY[r * LT + c] = y[v];
+                const float dv = sB[r] * y[v];
+                smdV[r * LT + c] = -dv;
+                if (r < p.len) store_out<OB>(a.dv, ((size_t)(p.t0 + r) * a.H + h) * D + ct * GW + c, dv);
+            }
+        }
+        __syncthreads();
+        if (tid < BC) {
+            float s = 0.f;
+            for (int c = 0; c < GW; ++c) s += sdY[tid * LT + c] * sV[tid * LT + c];
+            dbeta += s;
+        }
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int q = 0; q < CT_PER_WAVE; ++q) {
+                const int dt = w * CT_PER_WAVE + q;   // 16-column tile of D
+                mma<GW>(dQp[rt][q], sO + 16 * rt * LT, LT, 1, sSm + 16 * dt * LT, 1, LT);
+                mma<GW>(dKp[rt][q], smdV + 16 * rt * LT, LT, 1, sSm + 16 * dt * LT, 1, LT);
+                mma<GW>(dKpp[rt][q], sE + 16 * rt * LT, LT, 1, sdSn + 16 * dt * LT, 1, LT);
+            }
+        // dP (+)= dO E^T, dY E^T on this wave's C x C tile
+        mma<GW>(dPacc, sO + 16 * trt * LT, LT, 1, sE + 16 * tct * LT, 1, LT);
+        mma<GW>(dYE, sdY + 16 * trt * LT, LT, 1, sE + 16 * tct * LT, 1, LT);
+    }
+    __syncthreads();
+    // dP = Tril(dO E^T) -> sdE;  dA = -StrictTril(dY E^T) -> sdY  (both C x C, row stride LC)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int r = 16 * trt + acc_row(v), c = 16 * tct + acc_col();
+        sdE[r * LC + c] = r >= c ? dPacc[v] : 0.f;
+        sdY[r * LC + c] = r > c ? -dYE[v] : 0.f;
+    }
+    __syncthreads();
+    if (tid < BC) {   // dbeta += rowsum(dA L); dL = Diag(beta) dA (in place)
+        float s = 0.f;
+        for (int c = 0; c < BC; ++c) {
+            const float x = sdY[tid * LC + c];
+            s += x * sL[tid * LC + c];
+            sdY[tid * LC + c] = sB[tid] * x;
+        }
+        dbeta += s;
+        if (tid < p.len) store_out<OB>(a.dbeta, (size_t)(p.t0 + tid) * a.H + h, dbeta);
+    }
+    // the decay exponents b - m of this chunk, into the S_m plane as [C][LD]
+    float* sX = sSm;
+    load_rows<IN, D>(sX, LD, a.g, p.t0, p.len, a.H, h, D, 0);
+    __syncthreads();
+    if (tid < D) {
+        float b = 0.f;
+        for (int r = 0; r < BC; ++r) {
+            b += sX[r * LD + tid];
+            sX[r * LD + tid] = b;
+        }
+        const float m = sX[(BC / 2 - 1) * LD + tid];
+        for (int r = 0; r < BC; ++r) sX[r * LD + tid] -= m;
+    }
+    __syncthreads();
+    float* sDb = sdSn;   // db as [C][LD]
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int q = 0; q < CT_PER_WAVE; ++q) {
+            const int dt = w * CT_PER_WAVE + q;
+            mma<BC>(dQp[rt][q], sdE + 16 * rt * LC, LC, 1, sKpp + 16 * dt, LD, 1);   // + dP K''
+            mma<BC>(dKp[rt][q], sdY + 16 * rt * LC, LC, 1, sKpp + 16 * dt, LD, 1);   // + dL K''
+            mma<BC>(dKpp[rt][q], sdE + 16 * rt, 1, LC, sQp + 16 * dt, LD, 1);        // + dP^T Q'
+            mma<BC>(dKpp[rt][q], sdY + 16 * rt, 1, LC, sKp + 16 * dt, LD, 1);        // + dL^T K'
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int r = 16 * rt + acc_row(v), c = 16 * dt + acc_col();
+                const float x = sX[r * LD + c], up = fast_exp(x), dn = fast_exp(-x);
+                const float gq = dQp[rt][q][v], gk = dKp[rt][q][v], gkk = dKpp[rt][q][v];
+                sDb[r * LD + c] = sQp[r * LD + c] * gq + sKp[r * LD + c] * gk - sKpp[r * LD + c] * gkk;
+                if (r < p.len) {
+                    const size_t gi = ((size_t)(p.t0 + r) * a.H + h) * D + c;
+                    store_out<OB>(a.dq, gi, up * gq);
+                    store_out<OB>(a.dk, gi, up * gk + dn * gkk);
+                }
+            }
+        }
+    __syncthreads();
+    if (tid < D) {   // dlog_alpha = reverse cumulative sum of db (last row: + rowsum(dS_next S_next))
+        float s = sDbn[tid];
+        for (int r = BC - 1; r >= 0; --r) {
+            s += sDb[r * LD + tid];
+            if (r < p.len) store_out<OB>(a.dg, ((size_t)(p.t0 + r) * a.H + h) * D + tid, s);
+        }
+    }
+}
+
+template <int D, class IN, bool OB>
+hipError_t launch_typed(const BackwardArgs& a, int nc_max, hipStream_t st) {
+    const int units = a.N * a.H;
+    if (a.cu) {
+        seq_scan_kernel<<<1, BT, 0, st>>>(a.cu, a.N, a.seq_chunk0);
+    }
+    if (nc_max > 0) prep_kernel<D, IN><<<nc_max * a.H, BT, 0, st>>>(a);
+    if (units > 0) {
+        state_fwd_kernel<D, IN><<<units * (D / TW), BT, 0, st>>>(a);
+        state_rev_kernel<D, IN><<<units * (D / TW), BT, 0, st>>>(a);
+    }
+    if (nc_max > 0) grad_kernel<D, IN, OB><<<nc_max * a.H, BT, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+BackwardPlan plan_backward(int B, int T, int H, int D, int N, bool varlen) {
+    BackwardPlan pl;
+    // sum over sequences of ceil(len / C) <= ceil(T / C) + N for a packed batch
+    const size_t nc = varlen ? (size_t)((T + BC - 1) / BC) + (size_t)N : (size_t)B * ((T + BC - 1) / BC);
+    const size_t rec = D == 64 ? Rec<64>::SIZE : Rec<128>::SIZE;
+    auto up256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    pl.nc_max = nc;
+    size_t off = 0;
+    pl.off_seq = off;
+    off += up256(varlen ? sizeof(int32_t) * (size_t)(N + 1) : 0);
+    pl.off_prep = off;
+    off += up256(sizeof(float) * nc * H * rec);
+    pl.off_states = off;
+    off += up256(sizeof(float) * (nc + (size_t)N) * H * D * D);
+    pl.off_dstates = off;
+    off += up256(sizeof(float) * nc * H * D * D);
+    pl.workspace_bytes = off;
+    return pl;
+}
+
+hipError_t launch_backward(BackwardArgs a, const BackwardPlan& pl, void* workspace, hipStream_t st) {
+    char* ws = static_cast<char*>(workspace);
+    a.seq_chunk0 = reinterpret_cast<int32_t*>(ws + pl.off_seq);
+    a.prep = reinterpret_cast<float*>(ws + pl.off_prep);
+    a.states = reinterpret_cast<float*>(ws + pl.off_states);
+    a.dstates = reinterpret_cast<float*>(ws + pl.off_dstates);
+    const int nc = static_cast<int>(pl.nc_max);
+#define KDA_BWD_CASE(DD, IN, OB)                                                              \
+    if (a.D == DD && a.in_bf16 == std::is_same<IN, BF16>::value && a.out_bf16 == OB)         \
+        return launch_typed<DD, IN, OB>(a, nc, st);
+    KDA_BWD_CASE(128, BF16, false)
+    KDA_BWD_CASE(128, BF16, true)
+    KDA_BWD_CASE(128, F32, false)
+    KDA_BWD_CASE(128, F32, true)
+    KDA_BWD_CASE(64, BF16, false)
+    KDA_BWD_CASE(64, BF16, true)
+    KDA_BWD_CASE(64, F32, false)
+    KDA_BWD_CASE(64, F32, true)
+#undef KDA_BWD_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kda

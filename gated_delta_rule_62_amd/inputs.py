@@ -169,6 +169,18 @@ def make_prefill(w: Workload, seed: int | None = None, *, B=None, T=None, H=None
                 B=B, T=T, H=H, D=D, N=N, dtype=dtype, scalar_gate=scalar_gate)
 
 
+def make_output_grads(d: dict, seed: int, *, dS_final: bool = True, scale: float = 1.0):
+    """Upstream gradients for a prefill batch ``d`` (from ``make_prefill``): d_o ~ N(0,1)
+    [B, T, H, D] in the batch's dtype and, if asked, dS_final ~ 0.02 N(0,1) [N, H, D, D]
+    float32 (the scale of the recipe's S0).  Drawn from their own stream (``seed``) so
+    the inputs of the batch stay as they are."""
+    rng = np.random.default_rng(seed)
+    shp = (d["B"], d["T"], d["H"], d["D"])
+    do = np.float32(scale) * _normal(rng, shp)
+    dsf = (np.float32(0.02) * _normal(rng, (d["N"], d["H"], d["D"], d["D"]))) if dS_final else None
+    return dict(d_o=_cast(do, d["dtype"]), dS_final=dsf)
+
+
 def make_raw_prefill(seed: int, *, B=1, T=64, H=2, D=128, dtype="bf16", num_seqs=None, lengths=None,
                      qk_scale=3.0, s0=True):
     """Unconstrained inputs for the fused prologue: q, k ~ qk_scale * N(0,1) (not normalised),

@@ -21,7 +21,8 @@ CHUNK = 0          # library default chunk length (32 tokens); 32 and 64 are bui
 
 EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_step",
             "kda_recurrent_fwd", "gdn_chunk_fwd", "gdn_recurrent_step", "gdn_recurrent_fwd",
-            "kda_chunk_fwd_fused", "kda_recurrent_step_fused")
+            "kda_chunk_fwd_fused", "kda_recurrent_step_fused", "kda_chunk_bwd_workspace_bytes",
+            "kda_chunk_bwd")
 KDA_FUSE_QK_L2NORM, KDA_FUSE_BETA_SIGMOID, KDA_FUSE_DECAY_LOGSIGMOID = 1, 2, 4
 
 
@@ -63,6 +64,10 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd_fused.restype = i32
     lib.kda_recurrent_step_fused.argtypes = [vp] * 7 + [i32] * 4 + [i32, i32] + [vp, fp, vp]
     lib.kda_recurrent_step_fused.restype = i32
+    lib.kda_chunk_bwd_workspace_bytes.argtypes = [i32] * 8
+    lib.kda_chunk_bwd_workspace_bytes.restype = sz
+    lib.kda_chunk_bwd.argtypes = [vp] * 9 + [i32] * 7 + [i32, i32] + [vp] * 6 + [vp, sz, vp]
+    lib.kda_chunk_bwd.restype = i32
     for pre in ("kda", "gdn"):
         getattr(lib, f"{pre}_chunk_fwd").argtypes = lib.kda_chunk_fwd.argtypes
         getattr(lib, f"{pre}_chunk_fwd").restype = i32
@@ -250,3 +255,45 @@ def kda_recurrent_step_fused(q, k, v, log_alpha, beta, S_in, S_out=None, *, qk_l
     if st != KDA_OK:
         raise KDAError(st, "kda_recurrent_step_fused")
     return o, S_out
+
+
+def kda_chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, num_seqs, has_cu_seqlens, chunk=CHUNK) -> int:
+    return int(load_library().kda_chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, num_seqs,
+                                                            int(bool(has_cu_seqlens)), chunk))
+
+
+def kda_chunk_bwd(q, k, v, log_alpha, beta, d_o, S0=None, cu_seqlens=None, dS_final=None, *,
+                  grad_dtype=torch.float32, grads=None, want_dS0=True, workspace=None, chunk=CHUNK,
+                  stream=None):
+    """Gradient of kda_chunk_fwd.  Inputs as for kda_chunk_fwd plus d_o [B, T, H, Dv]
+    (the inputs' dtype) and dS_final [N, H, Dk, Dv] float32 or None.  Returns a dict
+    dq, dk, dv, dlog_alpha, dbeta (grad_dtype) and dS0 (float32, or None when
+    want_dS0 is False); ``grads`` may supply preallocated outputs under those names."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if d_o.dtype != q.dtype:
+        raise TypeError("d_o must have the inputs' dtype")
+    g = dict(grads or {})
+    dev = q.device
+    for name, shape in (("dq", q.shape), ("dk", q.shape), ("dv", v.shape), ("dlog_alpha", q.shape),
+                        ("dbeta", beta.shape)):
+        if g.get(name) is None:
+            g[name] = torch.empty(shape, dtype=grad_dtype, device=dev)
+    if g.get("dS0") is None and want_dS0:
+        g["dS0"] = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev)
+    _check_dev(q, k, v, log_alpha, beta, d_o, S0, cu_seqlens, dS_final, workspace, *g.values())
+    ws_need = kda_chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, N, cu_seqlens is not None, chunk)
+    if workspace is None and ws_need > 0:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().kda_chunk_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
+        _ptr(d_o), _ptr(dS_final), B, T, H, Dk, Dv, N, chunk, _dtype_code(q.dtype), _dtype_code(g["dq"].dtype),
+        _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dlog_alpha"]), _ptr(g["dbeta"]), _ptr(g.get("dS0")),
+        _ptr(workspace), ws_bytes, _stream_ptr(stream))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_chunk_bwd")
+    return g

@@ -219,6 +219,49 @@ kda_status gdn_recurrent_fwd(const void* q, const void* k, const void* v, const 
                              kda_dtype in_dtype, kda_dtype out_dtype,
                              void* o, float* S_final, kda_stream_t stream);
 
+/*
+ * kda_chunk_bwd -- gradient of kda_chunk_fwd for training.
+ *
+ * The pages motivate the chunkwise form by training throughput ("Decoding Hybrid
+ * Attention Architectures", section 4) and give no backward; this is the exact
+ * gradient of the layer that kda_chunk_fwd computes (the recurrence of section 3.4),
+ * evaluated through the same chunkwise form: a forward pass over the chunks that
+ * keeps every chunk's entry state, a reverse pass that carries the state gradient
+ * from the last chunk to the first, and one parallel step per (chunk, head).
+ *
+ *   q, k, v, log_alpha, beta, S0, cu_seqlens, B, T, H, Dk, Dv, num_seqs, in_dtype:
+ *                     the arguments of the kda_chunk_fwd call being differentiated
+ *   d_o             : [B, T, H, Dv] in_dtype, gradient of the loss with respect to o
+ *   dS_final        : [N, H, Dk, Dv] fp32 gradient with respect to S_final, or NULL
+ *                     for zero
+ *   chunk           : 0 or 32
+ *   dq, dk          : [B, T, H, Dk]   grad_dtype
+ *   dv              : [B, T, H, Dv]   grad_dtype
+ *   dlog_alpha      : [B, T, H, Dk]   grad_dtype
+ *   dbeta           : [B, T, H]       grad_dtype
+ *   dS0             : [N, H, Dk, Dv]  fp32 gradient with respect to S0, or NULL to skip
+ *                     (written for every sequence, also when S0 is NULL)
+ *   workspace       : device scratch of kda_chunk_bwd_workspace_bytes() bytes; it holds
+ *                     every chunk's entry state and state gradient in fp32, about
+ *                     (2 Dk Dv + 3 chunk Dk + 3 chunk^2) * 4 bytes per chunk and head
+ *
+ * Supported: Dk == Dv in {64, 128}; in_dtype, grad_dtype in {KDA_F32, KDA_BF16}
+ * (bf16 gradients are the round-to-nearest-even bf16 of the fp32 result).  All
+ * arithmetic is fp32.  Outputs must not overlap inputs, each other or the workspace.
+ * With N == 0 nothing is written; with T == 0, dS0 = dS_final (or zeros).  Decays
+ * follow kda_chunk_fwd's domain: the decay of half a chunk stays within fp32 range.
+ */
+size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int num_seqs,
+                                     int has_cu_seqlens, int chunk);
+
+kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                         const void* beta, const float* S0, const int32_t* cu_seqlens,
+                         const void* d_o, const float* dS_final,
+                         int B, int T, int H, int Dk, int Dv, int num_seqs, int chunk,
+                         kda_dtype in_dtype, kda_dtype grad_dtype,
+                         void* dq, void* dk, void* dv, void* dlog_alpha, void* dbeta, float* dS0,
+                         void* workspace, size_t workspace_bytes, kda_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

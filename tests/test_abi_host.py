@@ -153,3 +153,50 @@ def test_fused_argument_errors(lib):
                                             ctypes.c_void_p(5 << 40), ctypes.byref(fusion), None)
     assert step(fz(flags=16)) == kda.KDA_ERR_INVALID_ARGUMENT
     assert step(fz(gate=(4 << 40) + 1024)) == kda.KDA_ERR_INVALID_ARGUMENT          # gate inside the state
+
+
+def test_backward_workspace_query(lib):
+    q = kda.kda_chunk_bwd_workspace_bytes
+    up = lambda x: (x + 255) // 256 * 256
+    rec = 3 * 32 * 128 + 3 * 32 * 32 + 2 * 128 + 32          # floats per (chunk, head) record
+    nc, H, D = 4 * 128, 16, 128                                # 4 sequences of 4096 tokens
+    want = up(4 * nc * H * rec) + up(4 * (nc + 4) * H * D * D) + up(4 * nc * H * D * D)
+    assert q(4, 4096, 16, 128, 128, 4, False) == want
+    # packed: a chunk-start table and room for ceil(T / 32) + N chunks
+    nc = 1000 // 32 + 1 + 3
+    want = up(4 * 4) + up(4 * nc * 2 * (3 * 32 * 64 + 3 * 32 * 32 + 2 * 64 + 32)) + \
+        up(4 * (nc + 3) * 2 * 64 * 64) + up(4 * nc * 2 * 64 * 64)
+    assert q(1, 1000, 2, 64, 64, 3, True) == want
+    assert q(1, 64, 2, 96, 96, 1, False) == 0
+    assert q(1, 64, 2, 128, 128, 1, False, chunk=64) == 0
+
+
+def test_backward_argument_errors(lib):
+    outs = {n: ctypes.c_void_p((10 + i) << 40) for i, n in enumerate(("dq", "dk", "dv", "dg", "db", "dS0"))}
+
+    def bwd(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, S0=None, cu=None, do=ctypes.c_void_p(2 << 40),
+                 dSf=None, B=2, T=64, H=2, Dk=128, Dv=128, N=2, chunk=0, in_dt=kda.KDA_BF16,
+                 g_dt=kda.KDA_F32, ws=ctypes.c_void_p(8 << 40), ws_bytes=1 << 40)
+        a.update(outs)
+        a.update(kw)
+        return lib.kda_chunk_bwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["cu"], a["do"], a["dSf"],
+                                 a["B"], a["T"], a["H"], a["Dk"], a["Dv"], a["N"], a["chunk"], a["in_dt"],
+                                 a["g_dt"], a["dq"], a["dk"], a["dv"], a["dg"], a["db"], a["dS0"], a["ws"],
+                                 a["ws_bytes"], None)
+    assert bwd(B=0, N=0, T=0) == kda.KDA_OK                                    # nothing to do, no HIP call
+    assert bwd(Dk=96, Dv=96) == kda.KDA_ERR_UNSUPPORTED
+    assert bwd(chunk=64) == kda.KDA_ERR_UNSUPPORTED
+    assert bwd(g_dt=3) == kda.KDA_ERR_UNSUPPORTED
+    assert bwd(do=None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert bwd(dk=None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert bwd(dv=FAKE_MIS) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert bwd(N=3) == kda.KDA_ERR_INVALID_ARGUMENT                            # N != B without cu_seqlens
+    assert bwd(cu=ctypes.c_void_p(3 << 40)) == kda.KDA_ERR_INVALID_ARGUMENT    # cu_seqlens needs B == 1
+    assert bwd(dq=FAKE) == kda.KDA_ERR_INVALID_ARGUMENT                        # output aliases an input
+    assert bwd(dk=ctypes.c_void_p((10 << 40) + 64)) == kda.KDA_ERR_INVALID_ARGUMENT   # outputs overlap
+    assert bwd(dS0=ctypes.c_void_p((8 << 40) + 4096)) == kda.KDA_ERR_INVALID_ARGUMENT  # inside the workspace
+    assert bwd(dSf=ctypes.c_void_p(15 << 40), dS0=ctypes.c_void_p((15 << 40) + 1024)) == \
+        kda.KDA_ERR_INVALID_ARGUMENT                                           # dS0 overlaps dS_final
+    assert bwd(ws_bytes=1024) == kda.KDA_ERR_WORKSPACE_TOO_SMALL
+    assert bwd(ws=None, ws_bytes=0) == kda.KDA_ERR_WORKSPACE_TOO_SMALL
