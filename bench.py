@@ -12,7 +12,8 @@ d=128, 1024 sequential ``kda_recurrent_step`` calls on an fp32 state) as
 ``decode``, the same prefill with the fused prologue / epilogue as
 ``fused_prologue``, the scalar-gated variant (Gated DeltaNet) at the long-context shape
 as ``gdn``, a few new tokens per sequence on top of a carried state as
-``continuation``, the roofline of each path's dominant launch measured with HIP events
+``continuation``, the gradient (``kda_chunk_bwd``) on the training-prefill
+workload as ``backward``, the roofline of each path's dominant launch measured with HIP events
 on the launch stream, and the fp64 CPU oracle timed on a bounded sample of the
 same workloads on this host (``cpu_baseline``).
 
@@ -36,6 +37,7 @@ sys.path.insert(0, ROOT)
 METRIC = "KDA prefill tokens/s (H32,d128,T64K) + decode steps/s and HBM GB/s"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3         # MI355X fp32 matrix cores
 CHUNK = 32                       # chunk length passed to kda_chunk_fwd (the library default)
 
 
@@ -58,6 +60,21 @@ def prefill_alg_bytes(T: int, H: int, d: int, n_seqs: int, has_s0: bool) -> int:
     per_token_head = 4 * d * 2 + 2 + d * 2
     states = n_seqs * H * d * d * 4 * (2 if has_s0 else 1)
     return T * H * per_token_head + states
+
+
+def backward_alg_flops_per_token_head(d: int, C: int = CHUNK) -> int:
+    """Flops of the chunkwise gradient per (token, head): ten d x d contractions per
+    token (the state pass K' S_m and K''^T E, the reverse pass K'' dS_n, Q'^T dO and
+    K'^T dV, then R, dE, dQ', dK', dK'' in the gradient step), 2 d^2 flops each, and
+    sixteen C-deep ones over d (L, P, M Y, M^T dE, P^T dO twice, dP, dA, dP K'',
+    dL K'', dP^T Q', dL^T K' and the C-sized parts of the state passes), 2 C d each."""
+    return 20 * d * d + 32 * C * d
+
+
+def backward_alg_bytes(T: int, H: int, d: int, n_seqs: int) -> int:
+    """q, k, v, log_alpha, d_o and beta read once, dq, dk, dv, dlog_alpha and dbeta
+    written once (bf16), dS_final read and dS0 written (fp32)."""
+    return T * H * (5 * d * 2 + 2 + 4 * d * 2 + 2) + 2 * n_seqs * H * d * d * 4
 
 
 def decode_alg_bytes(N: int, H: int, d: int) -> int:
@@ -328,6 +345,48 @@ def main():
         "packed": cont_case(w5, "256 sequences x U{1..32} new tokens, packed (chunked kernel)"),
     }
 
+    # ------------------------------------------------------------------ backward (training)
+    # kda_chunk_bwd on the training-prefill workload (4 x 4096 tokens, 16 heads, d=128, bf16
+    # inputs, bf16 gradients, fp32 dS0), upstream gradients d_o ~ N(0,1), dS_final ~ 0.02 N(0,1).
+    w1 = inputs.WORKLOADS[1]
+    xb = inputs.device_prefill(w1)
+    gb = inputs.device_output_grads(xb, seed=1001)
+    Bb, Tb, Hb = xb["B"], xb["T"], xb["H"]
+    grads = {nm: torch.empty((Bb, Tb, Hb, d), dtype=torch.bfloat16, device="cuda")
+             for nm in ("dq", "dk", "dv", "dlog_alpha")}
+    grads["dbeta"] = torch.empty((Bb, Tb, Hb), dtype=torch.bfloat16, device="cuda")
+    grads["dS0"] = torch.empty((Bb, Hb, d, d), dtype=torch.float32, device="cuda")
+    wsb = torch.empty(kda.kda_chunk_bwd_workspace_bytes(Bb, Tb, Hb, d, d, Bb, False), dtype=torch.uint8,
+                      device="cuda")
+
+    def call_bwd():
+        kda.kda_chunk_bwd(xb["q"], xb["k"], xb["v"], xb["log_alpha"], xb["beta"], gb["d_o"], None, None,
+                          gb["dS_final"], grads=grads, workspace=wsb, stream=stream)
+    for _ in range(3):
+        call_bwd()
+    torch.cuda.synchronize()
+    eb0, eb1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    eb0.record(stream)
+    for _ in range(args.steps):
+        call_bwd()
+    eb1.record(stream)
+    torch.cuda.synchronize()
+    bwd_ms = eb0.elapsed_time(eb1) / args.steps
+    bwd_flops = backward_alg_flops_per_token_head(d) * Bb * Tb * Hb
+    bwd_bytes = backward_alg_bytes(Bb * Tb, Hb, d, Bb)
+    backward = {
+        "workload": "train_prefill backward: B=4, T=4096, H=16, d=128, bf16 inputs and gradients, "
+                    "fp32 dS0, kda_chunk_bwd (all kernels of one call)",
+        "value": Bb * Tb / (bwd_ms / 1e3), "unit": "tokens/s", "ms_per_call": bwd_ms,
+        "roofline": {"bound": "mfma", "achieved": bwd_flops / (bwd_ms / 1e3) / 1e12, "peak": FP32_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": bwd_flops / (bwd_ms / 1e3) / 1e12 / FP32_PEAK_TFLOPS,
+                     "flops_per_call": bwd_flops, "bytes_per_call": bwd_bytes,
+                     "hbm_frac": bwd_bytes / (bwd_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                     "flop_convention": f"{backward_alg_flops_per_token_head(d)} per token-head "
+                                        "(20 d^2 + 16 C d, fp32 matrix-core products)"},
+    }
+    del xb, gb, grads, wsb
+
     # ------------------------------------------------------------------ CPU baselines (oracle)
     cpu = None
     if not args.no_cpu_baseline:
@@ -361,6 +420,7 @@ def main():
         "fused_prologue": fused,
         "gdn": gdn,
         "continuation": continuation,
+        "backward": backward,
         "wall_s": wall,
     }
     print(json.dumps(out))

@@ -112,14 +112,21 @@ __device__ bool chunk_pos(const BackwardArgs& a, int j, ChunkPos& p) {
 // acc (16 x 16) += A (16 x K) B (K x 16), A(i, k) = A[i*ai + k*ak], B(k, j) = B[k*bk + j*bj].
 // Lane l supplies A(l % 16, k0 + l / 16) and B(k0 + l / 16, l % 16) for each 4-deep step
 // and holds C(4 (l / 16) + v, l % 16) in acc[v].
+// All operands of the product are read from LDS before the first MFMA issues, so the
+// reads overlap each other instead of each step waiting on its own.
 template <int K>
 __device__ __forceinline__ void mma(f4& acc, const float* A, int ai, int ak, const float* B, int bk, int bj) {
     const int lane = threadIdx.x & 63, i = lane & 15, kq = lane >> 4;
     const float* pa = A + i * ai + kq * ak;
     const float* pb = B + kq * bk + i * bj;
+    float a[K / 4], b[K / 4];
 #pragma unroll
-    for (int k0 = 0; k0 < K; k0 += 4)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k0 * ak], pb[k0 * bk], acc, 0, 0, 0);
+    for (int s = 0; s < K / 4; ++s) {
+        a[s] = pa[4 * s * ak];
+        b[s] = pb[4 * s * bk];
+    }
+#pragma unroll
+    for (int s = 0; s < K / 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
 }
 
 __device__ __forceinline__ int acc_row(int v) { return 4 * ((threadIdx.x & 63) >> 4) + v; }
@@ -127,34 +134,109 @@ __device__ __forceinline__ int acc_col() { return threadIdx.x & 15; }
 
 __device__ __forceinline__ f4 zero4() { return f4{0.f, 0.f, 0.f, 0.f}; }
 
-// rows x cols fp32 block between global memory (dense, row stride gs) and LDS (row stride ls)
-template <int ROWS, int COLS>
-__device__ __forceinline__ void g2s(float* s, int ls, const float* g, size_t gs) {
-    static_assert(COLS % 4 == 0, "");
-    for (int e = threadIdx.x; e < ROWS * COLS / 4; e += BT) {
-        const int r = e / (COLS / 4), c = 4 * (e % (COLS / 4));
-        const float4 x = *reinterpret_cast<const float4*>(g + r * gs + c);
-        *reinterpret_cast<float4*>(s + r * ls + c) = x;
-    }
+// Workgroup barrier that orders LDS only: it waits for this wave's LDS operations, not
+// for global loads in flight (a prefetch may stay outstanding across it).  Every
+// exchange between waves in these kernels goes through LDS.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+
+// Native 4 x fp32 and 2 x u32 vectors: they stay in registers (HIP's v4f is a struct
+// whose copies can end up as memory copies through private memory).
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
+// A ROWS x COLS fp32 block of a dense global array (row stride gs) staged through
+// registers: load() issues every global load of the block and nothing waits on them
+// until store() writes the block to LDS (row stride ls), so a block can be fetched
+// while the previous one is being used.
+template <int ROWS, int COLS>
+struct Stage {
+    static constexpr int C4 = COLS / 4, N4 = ROWS * C4, IT = (N4 + BT - 1) / BT;
+    static_assert(COLS % 4 == 0, "");
+    v4f x[IT];
+    __device__ __forceinline__ static bool live(int e) { return N4 % BT == 0 || e < N4; }
+    __device__ __forceinline__ void load(const float* g, size_t gs) {
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int e = threadIdx.x + it * BT;
+            if (live(e)) x[it] = *reinterpret_cast<const v4f*>(g + (size_t)(e / C4) * gs + 4 * (e % C4));
+        }
+    }
+    __device__ __forceinline__ void store(float* s, int ls) const {
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int e = threadIdx.x + it * BT;
+            if (live(e)) *reinterpret_cast<v4f*>(s + (e / C4) * ls + 4 * (e % C4)) = x[it];
+        }
+    }
+};
 
 template <int ROWS, int COLS>
 __device__ __forceinline__ void s2g(float* g, size_t gs, const float* s, int ls) {
     static_assert(COLS % 4 == 0, "");
     for (int e = threadIdx.x; e < ROWS * COLS / 4; e += BT) {
         const int r = e / (COLS / 4), c = 4 * (e % (COLS / 4));
-        *reinterpret_cast<float4*>(g + r * gs + c) = *reinterpret_cast<const float4*>(s + r * ls + c);
+        *reinterpret_cast<v4f*>(g + r * gs + c) = *reinterpret_cast<const v4f*>(s + r * ls + c);
     }
 }
 
-// One chunk's rows of a [B*T, H, W] input (W columns starting at col0) into LDS as
-// fp32; rows past len are zero.
+// One chunk's rows [t0, t0 + len) of a [tokens, H, W] input, COLS columns from col0,
+// staged like Stage in the input's own type (converted to fp32 on the way to LDS);
+// rows past len are zero.
 template <class IN, int COLS>
-__device__ __forceinline__ void load_rows(float* s, int ls, const void* x, int t0, int len, int H, int h,
-                                          int W, int col0) {
-    for (int e = threadIdx.x; e < BC * COLS; e += BT) {
-        const int r = e / COLS, c = e % COLS;
-        s[r * ls + c] = r < len ? ld_in<IN>(x, ((size_t)(t0 + r) * H + h) * W + col0 + c) : 0.f;
+struct StageRows {
+    static constexpr bool B16 = std::is_same<IN, BF16>::value;
+    static constexpr int C4 = COLS / 4, N4 = BC * C4, IT = (N4 + BT - 1) / BT;
+    static_assert(COLS % 4 == 0, "");
+    using raw_t = typename std::conditional<B16, v2u, v4f>::type;
+    raw_t x[IT];
+    int len_ = 0;
+    __device__ __forceinline__ static bool live(int e) { return N4 % BT == 0 || e < N4; }
+    // Rows past len read row len - 1 (always in bounds for len >= 1) and are zeroed by
+    // store(), so no load sits behind a branch.
+    __device__ __forceinline__ void load(const void* p, int t0, int len, int H, int h, int W, int col0) {
+        len_ = len;
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int e = threadIdx.x + it * BT, r = min(e / C4, len - 1), c = 4 * (e % C4);
+            if (live(e)) {
+                const size_t idx = ((size_t)(t0 + r) * H + h) * W + col0 + c;
+                x[it] = *reinterpret_cast<const raw_t*>(static_cast<const typename IN::storage*>(p) + idx);
+            }
+        }
+    }
+    __device__ __forceinline__ static v4f widen(const raw_t& v) {
+        if constexpr (B16) {
+            return v4f{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                       __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
+        } else {
+            return v;
+        }
+    }
+    __device__ __forceinline__ void store(float* s, int ls) const {
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int e = threadIdx.x + it * BT;
+            const bool ok = e / C4 < len_;
+            v4f v = widen(x[it]);
+            v.x = ok ? v.x : 0.f;
+            v.y = ok ? v.y : 0.f;
+            v.z = ok ? v.z : 0.f;
+            v.w = ok ? v.w : 0.f;
+            if (live(e)) *reinterpret_cast<v4f*>(s + (e / C4) * ls + 4 * (e % C4)) = v;
+        }
+    }
+};
+
+// The D x TW column tile of a [D, D] state starting at g (or zeros when g is null) into LDS.
+template <int D>
+__device__ __forceinline__ void init_tile(float* s, int ls, const float* g) {
+    for (int e = threadIdx.x; e < D * TW / 4; e += BT) {
+        const int r = e / (TW / 4), c = 4 * (e % (TW / 4));
+        v4f x{0.f, 0.f, 0.f, 0.f};
+        if (g) x = *reinterpret_cast<const v4f*>(g + (size_t)r * D + c);
+        *reinterpret_cast<v4f*>(s + r * ls + c) = x;
     }
 }
 
@@ -204,10 +286,17 @@ __global__ __launch_bounds__(BT) void prep_kernel(BackwardArgs a) {
     if (!chunk_pos(a, j, p)) return;
     const int tid = threadIdx.x, w = tid >> 6;
 
-    load_rows<IN, D>(sQ, LD, a.q, p.t0, p.len, a.H, h, D, 0);
-    load_rows<IN, D>(sK, LD, a.k, p.t0, p.len, a.H, h, D, 0);
-    load_rows<IN, D>(sG, LD, a.g, p.t0, p.len, a.H, h, D, 0);
-    if (tid < BC) sB[tid] = tid < p.len ? ld_in<IN>(a.beta, (size_t)(p.t0 + tid) * a.H + h) : 0.f;
+    {
+        StageRows<IN, D> rq, rk, rg;
+        rq.load(a.q, p.t0, p.len, a.H, h, D, 0);
+        rk.load(a.k, p.t0, p.len, a.H, h, D, 0);
+        rg.load(a.g, p.t0, p.len, a.H, h, D, 0);
+        const float bt = tid < p.len ? ld_in<IN>(a.beta, (size_t)(p.t0 + tid) * a.H + h) : 0.f;
+        rq.store(sQ, LD);
+        rk.store(sK, LD);
+        rg.store(sG, LD);
+        if (tid < BC) sB[tid] = bt;
+    }
     __syncthreads();
 
     if (tid < D) {
@@ -288,33 +377,46 @@ __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
     const int n = u / a.H, h = u % a.H, tid = threadIdx.x, w = tid >> 6;
     const int c0 = chunk0(a, n), L = seq_len(a, n), nch = (L + BC - 1) / BC, tok0 = seq_first_token(a, n);
     const size_t DD = (size_t)D * D;
-    for (int e = tid; e < D * TW; e += BT) {
-        const int r = e / TW, c = e % TW;
-        sS[r * LT + c] = a.S0 ? a.S0[(size_t)u * DD + (size_t)r * D + jt * TW + c] : 0.f;
-    }
+    init_tile<D>(sS, LT, a.S0 ? a.S0 + (size_t)u * DD + jt * TW : nullptr);
+    // the next chunk's operands are fetched into registers while this chunk computes
+    Stage<BC, D> rKp, rKpp;
+    Stage<BC, BC> rM;
+    StageRows<IN, TW> rV;
+    float rEm = 0.f, rEn = 0.f, rB = 0.f;
+    auto fetch = [&](int i) __attribute__((always_inline)) {
+        const float* rec = a.prep + ((size_t)(c0 + i) * a.H + h) * Rec<D>::SIZE;
+        rKp.load(rec + Rec<D>::KP, D);
+        rKpp.load(rec + Rec<D>::KPP, D);
+        rM.load(rec + Rec<D>::M, BC);
+        rEm = rec[Rec<D>::EM + (tid & (D - 1))];
+        rEn = rec[Rec<D>::EN + (tid & (D - 1))];
+        rB = rec[Rec<D>::BETA + (tid & (BC - 1))];
+        rV.load(a.v, tok0 + i * BC, min(BC, L - i * BC), a.H, h, D, jt * TW);
+    };
+    if (nch > 0) fetch(0);
     for (int i = 0; i < nch; ++i) {
-        const int j = c0 + i, t0 = tok0 + i * BC, len = min(BC, L - i * BC);
-        const float* rec = a.prep + ((size_t)j * a.H + h) * Rec<D>::SIZE;
-        __syncthreads();
-        g2s<BC, D>(sKp, LD, rec + Rec<D>::KP, D);
-        g2s<BC, D>(sKpp, LD, rec + Rec<D>::KPP, D);
-        g2s<BC, BC>(sM, LC, rec + Rec<D>::M, BC);
+        lds_barrier();
+        rKp.store(sKp, LD);
+        rKpp.store(sKpp, LD);
+        rM.store(sM, LC);
+        rV.store(sV, LT);
         if (tid < D) {
-            sEm[tid] = rec[Rec<D>::EM + tid];
-            sEn[tid] = rec[Rec<D>::EN + tid];
+            sEm[tid] = rEm;
+            sEn[tid] = rEn;
         }
-        if (tid < BC) sB[tid] = rec[Rec<D>::BETA + tid];
-        load_rows<IN, TW>(sV, LT, a.v, t0, len, a.H, h, D, jt * TW);
-        __syncthreads();
+        if (tid < BC) sB[tid] = rB;
+        if (i + 1 < nch) fetch(i + 1);
+        lds_barrier();
         // keep the entry state, then scale it to S_m
         float* slot = a.states + ((size_t)(c0 + n + i) * a.H + h) * DD + jt * TW;
-        for (int e = tid; e < D * TW; e += BT) {
-            const int r = e / TW, c = e % TW;
-            const float x = sS[r * LT + c];
-            slot[(size_t)r * D + c] = x;
-            sS[r * LT + c] = x * sEm[r];
+        for (int e = tid; e < D * TW / 4; e += BT) {
+            const int r = e / (TW / 4), c = 4 * (e % (TW / 4));
+            const v4f x = *reinterpret_cast<const v4f*>(sS + r * LT + c);
+            const float m = sEm[r];
+            *reinterpret_cast<v4f*>(slot + (size_t)r * D + c) = x;
+            *reinterpret_cast<v4f*>(sS + r * LT + c) = v4f{x.x * m, x.y * m, x.z * m, x.w * m};
         }
-        __syncthreads();
+        lds_barrier();
         {   // K' S_m, the key-channel sum split in two halves over the waves
             const int rt = w & 1, kh = w >> 1;
             f4 acc = zero4();
@@ -322,19 +424,19 @@ __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) sR[kh * BC * LT + (16 * rt + acc_row(v)) * LT + acc_col()] = acc[v];
         }
-        __syncthreads();
+        lds_barrier();
         for (int e = tid; e < BC * TW; e += BT) {
             const int r = e / TW, c = e % TW;
             sR[r * LT + c] = sB[r] * (sV[r * LT + c] - sR[r * LT + c] - sR[BC * LT + r * LT + c]);
         }
-        __syncthreads();
+        lds_barrier();
         if (w < 2) {   // E = M Y
             f4 acc = zero4();
             mma<BC>(acc, sM + 16 * w * LC, LC, 1, sR, LT, 1);
 #pragma unroll
             for (int v = 0; v < 4; ++v) sE[(16 * w + acc_row(v)) * LT + acc_col()] = acc[v];
         }
-        __syncthreads();
+        lds_barrier();
         for (int rt = w; rt < D / 16; rt += 4) {   // S_next = Diag(e_n)(S_m + K''^T E)
             f4 acc;
 #pragma unroll
@@ -349,9 +451,9 @@ __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
     }
     __syncthreads();
     float* slot = a.states + ((size_t)(c0 + n + nch) * a.H + h) * DD + jt * TW;
-    for (int e = tid; e < D * TW; e += BT) {
-        const int r = e / TW, c = e % TW;
-        slot[(size_t)r * D + c] = sS[r * LT + c];
+    for (int e = tid; e < D * TW / 4; e += BT) {
+        const int r = e / (TW / 4), c = 4 * (e % (TW / 4));
+        *reinterpret_cast<v4f*>(slot + (size_t)r * D + c) = *reinterpret_cast<const v4f*>(sS + r * LT + c);
     }
 }
 
@@ -360,56 +462,74 @@ __global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
     constexpr int LD = D + 4, LC = BC + 4, LT = TW + 4, NTILE = D / TW;
     __shared__ __attribute__((aligned(16))) float sQp[BC * LD], sKp[BC * LD], sKpp[BC * LD];
     __shared__ __attribute__((aligned(16))) float sM[BC * LC], sP[BC * LC];
-    __shared__ __attribute__((aligned(16))) float sS[D * LT], sO[BC * LT], sR[2 * BC * LT], sV[BC * LT];
+    __shared__ __attribute__((aligned(16))) float sS[D * LT], sO[BC * LT], sR[BC * LT], sV[BC * LT];
     __shared__ float sB[BC], sEm[D], sEn[D];
     int u, jt;
     unit_tile(blockIdx.x, gridDim.x, NTILE, u, jt);
     const int n = u / a.H, h = u % a.H, tid = threadIdx.x, w = tid >> 6;
     const int c0 = chunk0(a, n), L = seq_len(a, n), nch = (L + BC - 1) / BC, tok0 = seq_first_token(a, n);
     const size_t DD = (size_t)D * D;
-    for (int e = tid; e < D * TW; e += BT) {
-        const int r = e / TW, c = e % TW;
-        sS[r * LT + c] = a.dS_final ? a.dS_final[(size_t)u * DD + (size_t)r * D + jt * TW + c] : 0.f;
-    }
+    init_tile<D>(sS, LT, a.dS_final ? a.dS_final + (size_t)u * DD + jt * TW : nullptr);
+    // the previous chunk's operands are fetched into registers while this chunk computes
+    Stage<BC, D> rQp, rKp, rKpp;
+    Stage<BC, BC> rM, rP;
+    StageRows<IN, TW> rO;
+    float rEm = 0.f, rEn = 0.f, rB = 0.f;
+    auto fetch = [&](int i) __attribute__((always_inline)) {
+        const float* rec = a.prep + ((size_t)(c0 + i) * a.H + h) * Rec<D>::SIZE;
+        rQp.load(rec + Rec<D>::QP, D);
+        rKp.load(rec + Rec<D>::KP, D);
+        rKpp.load(rec + Rec<D>::KPP, D);
+        rM.load(rec + Rec<D>::M, BC);
+        rP.load(rec + Rec<D>::P, BC);
+        rEm = rec[Rec<D>::EM + (tid & (D - 1))];
+        rEn = rec[Rec<D>::EN + (tid & (D - 1))];
+        rB = rec[Rec<D>::BETA + (tid & (BC - 1))];
+        rO.load(a.dO, tok0 + i * BC, min(BC, L - i * BC), a.H, h, D, jt * TW);
+    };
+    if (nch > 0) fetch(nch - 1);
     for (int i = nch - 1; i >= 0; --i) {
-        const int j = c0 + i, t0 = tok0 + i * BC, len = min(BC, L - i * BC);
-        const float* rec = a.prep + ((size_t)j * a.H + h) * Rec<D>::SIZE;
-        __syncthreads();
-        g2s<BC, D>(sQp, LD, rec + Rec<D>::QP, D);
-        g2s<BC, D>(sKp, LD, rec + Rec<D>::KP, D);
-        g2s<BC, D>(sKpp, LD, rec + Rec<D>::KPP, D);
-        g2s<BC, BC>(sM, LC, rec + Rec<D>::M, BC);
-        g2s<BC, BC>(sP, LC, rec + Rec<D>::P, BC);
+        const int j = c0 + i;
+        lds_barrier();
+        rQp.store(sQp, LD);
+        rKp.store(sKp, LD);
+        rKpp.store(sKpp, LD);
+        rM.store(sM, LC);
+        rP.store(sP, LC);
+        rO.store(sO, LT);
         if (tid < D) {
-            sEm[tid] = rec[Rec<D>::EM + tid];
-            sEn[tid] = rec[Rec<D>::EN + tid];
+            sEm[tid] = rEm;
+            sEn[tid] = rEn;
         }
-        if (tid < BC) sB[tid] = rec[Rec<D>::BETA + tid];
-        load_rows<IN, TW>(sO, LT, a.dO, t0, len, a.H, h, D, jt * TW);
-        __syncthreads();
+        if (tid < BC) sB[tid] = rB;
+        if (i > 0) fetch(i - 1);
+        lds_barrier();
         // keep this chunk's dS_next, then scale it to dS_n
         float* slot = a.dstates + ((size_t)j * a.H + h) * DD + jt * TW;
-        for (int e = tid; e < D * TW; e += BT) {
-            const int r = e / TW, c = e % TW;
-            const float x = sS[r * LT + c];
-            slot[(size_t)r * D + c] = x;
-            sS[r * LT + c] = x * sEn[r];
+        for (int e = tid; e < D * TW / 4; e += BT) {
+            const int r = e / (TW / 4), c = 4 * (e % (TW / 4));
+            const v4f x = *reinterpret_cast<const v4f*>(sS + r * LT + c);
+            const float m = sEn[r];
+            *reinterpret_cast<v4f*>(slot + (size_t)r * D + c) = x;
+            *reinterpret_cast<v4f*>(sS + r * LT + c) = v4f{x.x * m, x.y * m, x.z * m, x.w * m};
         }
-        __syncthreads();
+        lds_barrier();
         {   // dE = P^T dO + K'' dS_n, the key-channel sum split in two halves over the waves
+            // (the second half's partial goes to sV, which holds -dV only later)
             const int rt = w & 1, kh = w >> 1;
             f4 acc = zero4();
             mma<D / 2>(acc, sKpp + 16 * rt * LD + kh * (D / 2), LD, 1, sS + kh * (D / 2) * LT, LT, 1);
             if (kh == 0) mma<BC>(acc, sP + 16 * rt, 1, LC, sO, LT, 1);
+            float* part = kh == 0 ? sR : sV;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) sR[kh * BC * LT + (16 * rt + acc_row(v)) * LT + acc_col()] = acc[v];
+            for (int v = 0; v < 4; ++v) part[(16 * rt + acc_row(v)) * LT + acc_col()] = acc[v];
         }
-        __syncthreads();
+        lds_barrier();
         for (int e = tid; e < BC * TW; e += BT) {
             const int r = e / TW, c = e % TW;
-            sR[r * LT + c] += sR[BC * LT + r * LT + c];
+            sR[r * LT + c] += sV[r * LT + c];
         }
-        __syncthreads();
+        lds_barrier();
         if (w < 2) {   // -dV = -Diag(beta) M^T dE
             f4 acc = zero4();
             mma<BC>(acc, sM + 16 * w, 1, LC, sR, LT, 1);
@@ -419,7 +539,7 @@ __global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
                 sV[r * LT + acc_col()] = -sB[r] * acc[v];
             }
         }
-        __syncthreads();
+        lds_barrier();
         for (int rt = w; rt < D / 16; rt += 4) {   // dS = Diag(e_m)(dS_n + Q'^T dO - K'^T dV)
             f4 acc;
 #pragma unroll
@@ -435,9 +555,10 @@ __global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
     }
     __syncthreads();
     if (a.dS0) {
-        for (int e = tid; e < D * TW; e += BT) {
-            const int r = e / TW, c = e % TW;
-            a.dS0[(size_t)u * DD + (size_t)r * D + jt * TW + c] = sS[r * LT + c];
+        for (int e = tid; e < D * TW / 4; e += BT) {
+            const int r = e / (TW / 4), c = 4 * (e % (TW / 4));
+            *reinterpret_cast<v4f*>(a.dS0 + (size_t)u * DD + (size_t)r * D + jt * TW + c) =
+                *reinterpret_cast<const v4f*>(sS + r * LT + c);
         }
     }
 }
@@ -460,23 +581,48 @@ __global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
     const int tid = threadIdx.x, w = tid >> 6;
     const size_t DD = (size_t)D * D;
     const float* rec = a.prep + ((size_t)j * a.H + h) * Rec<D>::SIZE;
-    g2s<BC, D>(sQp, LD, rec + Rec<D>::QP, D);
-    g2s<BC, D>(sKp, LD, rec + Rec<D>::KP, D);
-    g2s<BC, D>(sKpp, LD, rec + Rec<D>::KPP, D);
-    g2s<BC, BC>(sM, LC, rec + Rec<D>::M, BC);
-    g2s<BC, BC>(sP, LC, rec + Rec<D>::P, BC);
-    g2s<BC, BC>(sL, LC, rec + Rec<D>::L, BC);
-    if (tid < D) {
-        sEm[tid] = rec[Rec<D>::EM + tid];
-        sEn[tid] = rec[Rec<D>::EN + tid];
-        sDbn[tid] = 0.f;
-    }
-    if (tid < BC) sB[tid] = rec[Rec<D>::BETA + tid];
-
     const size_t slot = (size_t)(chunk0(a, p.n) + p.n + p.i);
     const float* S = a.states + (slot * a.H + h) * DD;
     const float* Snext = a.states + ((slot + 1) * a.H + h) * DD;
     const float* dS = a.dstates + ((size_t)j * a.H + h) * DD;
+
+    // one column tile of S, dS_next, S_next, V and dO, fetched a tile ahead
+    Stage<D, GW> rS, rdS, rSn;
+    StageRows<IN, GW> rV, rO;
+    auto fetch = [&](int ct) __attribute__((always_inline)) {
+        rS.load(S + ct * GW, D);
+        rdS.load(dS + ct * GW, D);
+        rSn.load(Snext + ct * GW, D);
+        rV.load(a.v, p.t0, p.len, a.H, h, D, ct * GW);
+        rO.load(a.dO, p.t0, p.len, a.H, h, D, ct * GW);
+    };
+    StageRows<IN, D> rG;   // log-decays, used after the column loop
+    {
+        Stage<BC, D> r1, r2, r3;
+        Stage<BC, BC> r4, r5, r6;
+        r1.load(rec + Rec<D>::QP, D);
+        r2.load(rec + Rec<D>::KP, D);
+        r3.load(rec + Rec<D>::KPP, D);
+        r4.load(rec + Rec<D>::M, BC);
+        r5.load(rec + Rec<D>::P, BC);
+        r6.load(rec + Rec<D>::L, BC);
+        const float em = rec[Rec<D>::EM + (tid & (D - 1))], en = rec[Rec<D>::EN + (tid & (D - 1))];
+        const float bt = rec[Rec<D>::BETA + (tid & (BC - 1))];
+        fetch(0);
+        rG.load(a.g, p.t0, p.len, a.H, h, D, 0);
+        r1.store(sQp, LD);
+        r2.store(sKp, LD);
+        r3.store(sKpp, LD);
+        r4.store(sM, LC);
+        r5.store(sP, LC);
+        r6.store(sL, LC);
+        if (tid < D) {
+            sEm[tid] = em;
+            sEn[tid] = en;
+            sDbn[tid] = 0.f;
+        }
+        if (tid < BC) sB[tid] = bt;
+    }
 
     f4 dQp[2][CT_PER_WAVE], dKp[2][CT_PER_WAVE], dKpp[2][CT_PER_WAVE];
 #pragma unroll
@@ -488,23 +634,26 @@ __global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
     const int trt = w & 1, tct = w >> 1;   // this wave's C x GW tile (and C x C tile)
 
     for (int ct = 0; ct < NCT; ++ct) {
-        __syncthreads();
-        load_rows<IN, GW>(sV, LT, a.v, p.t0, p.len, a.H, h, D, ct * GW);
-        load_rows<IN, GW>(sO, LT, a.dO, p.t0, p.len, a.H, h, D, ct * GW);
+        lds_barrier();
+        rV.store(sV, LT);
+        rO.store(sO, LT);
         // S_m, dS_n tiles; rowsum(dS_next * S_next) for the last row's db
-        for (int e = tid; e < D * GW; e += BT) {
-            const int r = e / GW, c = e % GW;
-            const size_t gi = (size_t)r * D + ct * GW + c;
-            const float x = S[gi], y = dS[gi];
-            float t = y * Snext[gi];
-            sSm[r * LT + c] = x * sEm[r];
-            sdSn[r * LT + c] = y * sEn[r];
-            // the 32 columns of row r sit in 32 consecutive lanes
 #pragma unroll
-            for (int off = 16; off >= 1; off >>= 1) t += __shfl_xor(t, off, 64);
+        for (int it = 0; it < Stage<D, GW>::IT; ++it) {
+            constexpr int C4 = GW / 4;
+            const int e = tid + it * BT, r = e / C4, c = 4 * (e % C4);
+            const v4f x = rS.x[it], y = rdS.x[it], z = rSn.x[it];
+            const float em = sEm[r], en = sEn[r];
+            *reinterpret_cast<v4f*>(sSm + r * LT + c) = v4f{x.x * em, x.y * em, x.z * em, x.w * em};
+            *reinterpret_cast<v4f*>(sdSn + r * LT + c) = v4f{y.x * en, y.y * en, y.z * en, y.w * en};
+            float t = y.x * z.x + y.y * z.y + y.z * z.z + y.w * z.w;
+            // the GW / 4 v4f groups of row r sit in consecutive lanes
+#pragma unroll
+            for (int off = C4 / 2; off >= 1; off >>= 1) t += __shfl_xor(t, off, 64);
             if (c == 0) sDbn[r] += t;
         }
-        __syncthreads();
+        if (ct + 1 < NCT) fetch(ct + 1);
+        lds_barrier();
         {
             f4 acc = zero4();   // R = V - K' S_m;  Y = Diag(beta) R
             mma<D>(acc, sKp + 16 * trt * LD, LD, 1, sSm + 16 * tct, LT, 1);
@@ -521,7 +670,7 @@ __global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) sdE[(16 * trt + acc_row(v)) * LT + 16 * tct + acc_col()] = d[v];
         }
-        __syncthreads();
+        lds_barrier();
         {
             f4 e = zero4();     // E = M Y
             mma<BC>(e, sM + 16 * trt * LC, LC, 1, sY + 16 * tct, LT, 1);
@@ -537,7 +686,7 @@ __global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
                 if (r < p.len) store_out<OB>(a.dv, ((size_t)(p.t0 + r) * a.H + h) * D + ct * GW + c, dv);
             }
         }
-        __syncthreads();
+        lds_barrier();
         if (tid < BC) {
             float s = 0.f;
             for (int c = 0; c < GW; ++c) s += sdY[tid * LT + c] * sV[tid * LT + c];
@@ -556,7 +705,7 @@ __global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
         mma<GW>(dPacc, sO + 16 * trt * LT, LT, 1, sE + 16 * tct * LT, 1, LT);
         mma<GW>(dYE, sdY + 16 * trt * LT, LT, 1, sE + 16 * tct * LT, 1, LT);
     }
-    __syncthreads();
+    lds_barrier();
     // dP = Tril(dO E^T) -> sdE;  dA = -StrictTril(dY E^T) -> sdY  (both C x C, row stride LC)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -577,7 +726,7 @@ __global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
     }
     // the decay exponents b - m of this chunk, into the S_m plane as [C][LD]
     float* sX = sSm;
-    load_rows<IN, D>(sX, LD, a.g, p.t0, p.len, a.H, h, D, 0);
+    rG.store(sX, LD);
     __syncthreads();
     if (tid < D) {
         float b = 0.f;

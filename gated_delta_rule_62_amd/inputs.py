@@ -295,6 +295,17 @@ def device_prefill(w: Workload, seed: int | None = None, device="cuda", *, lengt
                 cu_host=cu, B=B, T=T, H=H, D=D, N=N, dtype=w.dtype, scalar_gate=w.scalar_gate)
 
 
+def device_output_grads(x: dict, seed: int, device="cuda", *, dS_final: bool = True):
+    """Upstream gradients for a device batch ``x`` (from ``device_prefill``), the recipe
+    of ``make_output_grads``: d_o ~ N(0,1) in the batch's dtype, dS_final ~ 0.02 N(0,1)."""
+    import torch
+    g = torch.Generator(device=device).manual_seed(seed)
+    dt = torch.bfloat16 if x["dtype"] == "bf16" else torch.float32
+    do = torch.randn((x["B"], x["T"], x["H"], x["D"]), device=device, generator=g).to(dt)
+    dsf = 0.02 * torch.randn((x["N"], x["H"], x["D"], x["D"]), device=device, generator=g) if dS_final else None
+    return dict(d_o=do, dS_final=dsf)
+
+
 def device_decode_steps(w: Workload, steps: int, seed: int | None = None, device="cuda"):
     """Initial state and `steps` per-step input tuples (q, k, v, log_alpha, beta) of
     a decode workload, drawn on the device."""
