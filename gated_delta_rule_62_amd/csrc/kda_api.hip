@@ -321,13 +321,14 @@ extern "C" size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int
     return kda::plan_backward(B, T, H, Dk, num_seqs, has_cu_seqlens != 0).workspace_bytes;
 }
 
-extern "C" kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* log_alpha,
-                                    const void* beta, const float* S0, const int32_t* cu_seqlens,
-                                    const void* d_o, const float* dS_final,
-                                    int B, int T, int H, int Dk, int Dv, int num_seqs, int chunk,
-                                    kda_dtype in_dtype, kda_dtype grad_dtype,
-                                    void* dq, void* dk, void* dv, void* dlog_alpha, void* dbeta, float* dS0,
-                                    void* workspace, size_t workspace_bytes, kda_stream_t stream) {
+namespace {
+
+kda_status chunk_bwd_impl(const void* q, const void* k, const void* v, const void* log_alpha, const void* beta,
+                          const float* S0, const int32_t* cu_seqlens, const void* d_o, const float* dS_final,
+                          int B, int T, int H, int Dk, int Dv, int num_seqs, int chunk, kda_dtype in_dtype,
+                          kda_dtype grad_dtype, void* dq, void* dk, void* dv, void* dlog_alpha, void* dbeta,
+                          float* dS0, void* workspace, size_t workspace_bytes, kda_stream_t stream,
+                          bool scalar_gate) {
     if (B < 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || num_seqs < 0) return KDA_ERR_INVALID_ARGUMENT;
     if (!dtype_ok(in_dtype) || !dtype_ok(grad_dtype)) return KDA_ERR_UNSUPPORTED;
     if (!head_ok(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
@@ -353,8 +354,9 @@ extern "C" kda_status kda_chunk_bwd(const void* q, const void* k, const void* v,
     const size_t ein = elem_size(in_dtype), eg = elem_size(grad_dtype);
     const size_t n_x = tokens * H * Dk, n_b = tokens * H;
     const size_t n_s = static_cast<size_t>(num_seqs) * H * Dk * Dv * sizeof(float);
-    const size_t nin[6] = {n_x * ein, n_x * ein, n_x * ein, n_x * ein, n_b * ein, n_x * ein};
-    const size_t nout[5] = {n_x * eg, n_x * eg, n_x * eg, n_x * eg, n_b * eg};
+    const size_t n_g = scalar_gate ? n_b : n_x;   // log_alpha and dlog_alpha
+    const size_t nin[6] = {n_x * ein, n_x * ein, n_x * ein, n_g * ein, n_b * ein, n_x * ein};
+    const size_t nout[5] = {n_x * eg, n_x * eg, n_x * eg, n_g * eg, n_b * eg};
     kda::BackwardPlan plan = kda::plan_backward(B, T, H, Dk, num_seqs, cu_seqlens != nullptr);
     // every output is disjoint from every input, from the other outputs and from the workspace
     for (int o = 0; o < 6; ++o) {
@@ -384,6 +386,33 @@ extern "C" kda_status kda_chunk_bwd(const void* q, const void* k, const void* v,
     a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dlog_alpha; a.dbeta = dbeta; a.dS0 = dS0;
     a.B = B; a.T = T; a.H = H; a.D = Dk; a.N = num_seqs;
     a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = grad_dtype == KDA_BF16;
+    a.scalar_gate = scalar_gate;
     hipError_t err = kda::launch_backward(a, plan, workspace, reinterpret_cast<hipStream_t>(stream));
     return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                                    const void* beta, const float* S0, const int32_t* cu_seqlens,
+                                    const void* d_o, const float* dS_final,
+                                    int B, int T, int H, int Dk, int Dv, int num_seqs, int chunk,
+                                    kda_dtype in_dtype, kda_dtype grad_dtype,
+                                    void* dq, void* dk, void* dv, void* dlog_alpha, void* dbeta, float* dS0,
+                                    void* workspace, size_t workspace_bytes, kda_stream_t stream) {
+    return chunk_bwd_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, dS_final, B, T, H, Dk, Dv, num_seqs,
+                          chunk, in_dtype, grad_dtype, dq, dk, dv, dlog_alpha, dbeta, dS0, workspace,
+                          workspace_bytes, stream, false);
+}
+
+extern "C" kda_status gdn_chunk_bwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                                    const void* beta, const float* S0, const int32_t* cu_seqlens,
+                                    const void* d_o, const float* dS_final,
+                                    int B, int T, int H, int Dk, int Dv, int num_seqs, int chunk,
+                                    kda_dtype in_dtype, kda_dtype grad_dtype,
+                                    void* dq, void* dk, void* dv, void* dlog_alpha, void* dbeta, float* dS0,
+                                    void* workspace, size_t workspace_bytes, kda_stream_t stream) {
+    return chunk_bwd_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, dS_final, B, T, H, Dk, Dv, num_seqs,
+                          chunk, in_dtype, grad_dtype, dq, dk, dv, dlog_alpha, dbeta, dS0, workspace,
+                          workspace_bytes, stream, true);
 }

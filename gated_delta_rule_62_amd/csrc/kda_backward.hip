@@ -27,11 +27,14 @@
 // Kernels (all products on the fp32 matrix cores, v_mfma_f32_16x16x4_f32, operands
 // from LDS):
 //   seq_scan_kernel   packed batches: first chunk index of every sequence
-//   prep_kernel       per (chunk, head): Q', K', K'', M, P, L, e_m, e_n, beta -> record
+//   prep_kernel       per (chunk, head): Q', K', K'', M, P, L, e_m, e_n, beta, b - m -> record
 //   state_fwd_kernel  per (sequence, head, 16 value columns): every chunk's entry state
 //                     and the final state, chunks in order
 //   state_rev_kernel  same split: every chunk's dS_next, chunks in reverse order; dS0
 //   grad_kernel       per (chunk, head): dq, dk, dv, dlog_alpha, dbeta
+// The scalar-gated variant (one log-decay per token and head, broadcast over the key
+// channels) runs the same kernels; its dlog_alpha is the per-channel one summed over the
+// key channels.
 // The state passes are independent per value column because every operator of the
 // recurrence multiplies the state from the left.
 #include <hip/hip_runtime.h>
@@ -55,7 +58,8 @@ using f4 = __attribute__((__vector_size__(4 * sizeof(float)))) float;
 template <int D>
 struct Rec {
     static constexpr int QP = 0, KP = BC * D, KPP = 2 * BC * D, M = 3 * BC * D, P = M + BC * BC,
-                         L = P + BC * BC, EM = L + BC * BC, EN = EM + D, BETA = EN + D, SIZE = BETA + BC;
+                         L = P + BC * BC, EM = L + BC * BC, EN = EM + D, BETA = EN + D, X = BETA + BC,
+                         SIZE = X + BC * D;
     static_assert(SIZE % 4 == 0, "records must stay 16-byte aligned");
 };
 
@@ -109,13 +113,18 @@ __device__ bool chunk_pos(const BackwardArgs& a, int j, ChunkPos& p) {
 }
 
 // ---------------------------------------------------------------- matrix-core helpers
+__device__ __forceinline__ f4 zero4() { return f4{0.f, 0.f, 0.f, 0.f}; }
+
 // acc (16 x 16) += A (16 x K) B (K x 16), A(i, k) = A[i*ai + k*ak], B(k, j) = B[k*bk + j*bj].
 // Lane l supplies A(l % 16, k0 + l / 16) and B(k0 + l / 16, l % 16) for each 4-deep step
 // and holds C(4 (l / 16) + v, l % 16) in acc[v].
-// All operands of the product are read from LDS before the first MFMA issues, so the
-// reads overlap each other instead of each step waiting on its own.
-template <int K>
+// The operands of all steps are requested before the MFMAs so the reads can overlap.
+// The 4-deep steps may be dealt round-robin to NACC independent accumulators (summed at
+// the end); a dependent fp32 MFMA issues 52 cycles after its predecessor, an
+// independent one every 32.
+template <int K, int NACC = 1>
 __device__ __forceinline__ void mma(f4& acc, const float* A, int ai, int ak, const float* B, int bk, int bj) {
+    static_assert((K / 4) % NACC == 0, "");
     const int lane = threadIdx.x & 63, i = lane & 15, kq = lane >> 4;
     const float* pa = A + i * ai + kq * ak;
     const float* pb = B + kq * bk + i * bj;
@@ -125,14 +134,20 @@ __device__ __forceinline__ void mma(f4& acc, const float* A, int ai, int ak, con
         a[s] = pa[4 * s * ak];
         b[s] = pb[4 * s * bk];
     }
+    f4 part[NACC];
+    part[0] = acc;
 #pragma unroll
-    for (int s = 0; s < K / 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
+    for (int c = 1; c < NACC; ++c) part[c] = zero4();
+#pragma unroll
+    for (int s = 0; s < K / 4; ++s)
+        part[s % NACC] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], part[s % NACC], 0, 0, 0);
+#pragma unroll
+    for (int c = 1; c < NACC; ++c) part[0] += part[c];
+    acc = part[0];
 }
 
 __device__ __forceinline__ int acc_row(int v) { return 4 * ((threadIdx.x & 63) >> 4) + v; }
 __device__ __forceinline__ int acc_col() { return threadIdx.x & 15; }
-
-__device__ __forceinline__ f4 zero4() { return f4{0.f, 0.f, 0.f, 0.f}; }
 
 // Workgroup barrier that orders LDS only: it waits for this wave's LDS operations, not
 // for global loads in flight (a prefetch may stay outstanding across it).  Every
@@ -275,7 +290,7 @@ __global__ __launch_bounds__(BT) void seq_scan_kernel(const int32_t* cu, int N, 
     if (threadIdx.x == 0) sc[N] = carry;
 }
 
-template <int D, class IN>
+template <int D, class IN, bool SG>
 __global__ __launch_bounds__(BT) void prep_kernel(BackwardArgs a) {
     constexpr int LD = D + 4, LC = BC + 4;
     __shared__ __attribute__((aligned(16))) float sQ[BC * LD], sK[BC * LD], sKpp[BC * LD], sG[BC * LD];
@@ -290,14 +305,23 @@ __global__ __launch_bounds__(BT) void prep_kernel(BackwardArgs a) {
         StageRows<IN, D> rq, rk, rg;
         rq.load(a.q, p.t0, p.len, a.H, h, D, 0);
         rk.load(a.k, p.t0, p.len, a.H, h, D, 0);
-        rg.load(a.g, p.t0, p.len, a.H, h, D, 0);
+        if constexpr (!SG) rg.load(a.g, p.t0, p.len, a.H, h, D, 0);
         const float bt = tid < p.len ? ld_in<IN>(a.beta, (size_t)(p.t0 + tid) * a.H + h) : 0.f;
+        // scalar gate: one log-decay per (token, head), the same for every key channel
+        const float gs = SG && tid < p.len ? ld_in<IN>(a.g, (size_t)(p.t0 + tid) * a.H + h) : 0.f;
         rq.store(sQ, LD);
         rk.store(sK, LD);
-        rg.store(sG, LD);
-        if (tid < BC) sB[tid] = bt;
+        if constexpr (!SG) rg.store(sG, LD);
+        if (tid < BC) {
+            sB[tid] = bt;
+            if (SG) sEm[tid] = gs;
+        }
     }
     __syncthreads();
+    if constexpr (SG) {
+        for (int e = tid; e < BC * D; e += BT) sG[(e / D) * LD + e % D] = sEm[e / D];
+        __syncthreads();
+    }
 
     if (tid < D) {
         float b = 0.f;
@@ -308,6 +332,7 @@ __global__ __launch_bounds__(BT) void prep_kernel(BackwardArgs a) {
         const float m = sG[(BC / 2 - 1) * LD + tid];
         for (int r = 0; r < BC; ++r) {
             const float x = sG[r * LD + tid] - m;
+            sG[r * LD + tid] = x;
             const float up = fast_exp(x), dn = fast_exp(-x);
             const float kv = sK[r * LD + tid];
             sQ[r * LD + tid] *= up;
@@ -359,6 +384,7 @@ __global__ __launch_bounds__(BT) void prep_kernel(BackwardArgs a) {
     s2g<BC, D>(rec + Rec<D>::KPP, D, sKpp, LD);
     s2g<BC, BC>(rec + Rec<D>::P, BC, sP, LC);
     s2g<BC, BC>(rec + Rec<D>::L, BC, sL, LC);
+    s2g<BC, D>(rec + Rec<D>::X, D, sG, LD);
     if (tid < D) {
         rec[Rec<D>::EM + tid] = sEm[tid];
         rec[Rec<D>::EN + tid] = sEn[tid];
@@ -563,7 +589,7 @@ __global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
     }
 }
 
-template <int D, class IN, bool OB>
+template <int D, class IN, bool OB, bool SG>
 __global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
     constexpr int LD = D + 4, LC = BC + 4, LT = GW + 4, NCT = D / GW;
     constexpr int CT_PER_WAVE = D / 16 / 4;   // 16-column tiles of D owned by each wave
@@ -596,7 +622,7 @@ __global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
         rV.load(a.v, p.t0, p.len, a.H, h, D, ct * GW);
         rO.load(a.dO, p.t0, p.len, a.H, h, D, ct * GW);
     };
-    StageRows<IN, D> rG;   // log-decays, used after the column loop
+    Stage<BC, D> rX;       // decay exponents b - m, used after the column loop
     {
         Stage<BC, D> r1, r2, r3;
         Stage<BC, BC> r4, r5, r6;
@@ -609,7 +635,7 @@ __global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
         const float em = rec[Rec<D>::EM + (tid & (D - 1))], en = rec[Rec<D>::EN + (tid & (D - 1))];
         const float bt = rec[Rec<D>::BETA + (tid & (BC - 1))];
         fetch(0);
-        rG.load(a.g, p.t0, p.len, a.H, h, D, 0);
+        rX.load(rec + Rec<D>::X, D);
         r1.store(sQp, LD);
         r2.store(sKp, LD);
         r3.store(sKpp, LD);
@@ -726,17 +752,7 @@ __global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
     }
     // the decay exponents b - m of this chunk, into the S_m plane as [C][LD]
     float* sX = sSm;
-    rG.store(sX, LD);
-    __syncthreads();
-    if (tid < D) {
-        float b = 0.f;
-        for (int r = 0; r < BC; ++r) {
-            b += sX[r * LD + tid];
-            sX[r * LD + tid] = b;
-        }
-        const float m = sX[(BC / 2 - 1) * LD + tid];
-        for (int r = 0; r < BC; ++r) sX[r * LD + tid] -= m;
-    }
+    rX.store(sX, LD);
     __syncthreads();
     float* sDb = sdSn;   // db as [C][LD]
 #pragma unroll
@@ -762,27 +778,60 @@ __global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
             }
         }
     __syncthreads();
-    if (tid < D) {   // dlog_alpha = reverse cumulative sum of db (last row: + rowsum(dS_next S_next))
-        float s = sDbn[tid];
-        for (int r = BC - 1; r >= 0; --r) {
-            s += sDb[r * LD + tid];
-            if (r < p.len) store_out<OB>(a.dg, ((size_t)(p.t0 + r) * a.H + h) * D + tid, s);
+    if constexpr (SG) {
+        // one log-decay per token: its gradient is the sum over key channels of the
+        // per-channel one, i.e. the reverse cumulative sum of the row sums of db
+        constexpr int TPR = BT / BC;   // threads per row
+        const int r = tid / TPR, part = tid % TPR, lane = tid & 63;
+        float t = 0.f;
+        for (int c = part; c < D; c += TPR) t += sDb[r * LD + c];
+#pragma unroll
+        for (int off = TPR / 2; off >= 1; off >>= 1) t += __shfl_xor(t, off, 64);
+        float* sRow = sY;   // [BC] row sums, then [BC] the channel sum of the last-row term
+        if (part == 0) sRow[r] = t;
+        if (w == 0) {
+            float v = 0.f;
+            for (int c = lane; c < D; c += 64) v += sDbn[c];
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+            if (lane == 0) sRow[BC] = v;
+        }
+        __syncthreads();
+        if (tid < p.len) {
+            float acc = sRow[BC];
+            for (int q = tid; q < BC; ++q) acc += sRow[q];
+            store_out<OB>(a.dg, (size_t)(p.t0 + tid) * a.H + h, acc);
+        }
+    } else {   // dlog_alpha = reverse cumulative sum of db (last row: + rowsum(dS_next S_next)); the
+        // rows are cut into BT / D parts, each part first sums its rows
+        constexpr int NP = BT / D, RP = BC / NP;
+        const int c = tid % D, part = tid / D;
+        float* sPart = sY;
+        float tot = 0.f;
+        for (int r = part * RP; r < (part + 1) * RP; ++r) tot += sDb[r * LD + c];
+        sPart[part * D + c] = tot;
+        __syncthreads();
+        float s = sDbn[c];
+        for (int q = part + 1; q < NP; ++q) s += sPart[q * D + c];
+        for (int r = (part + 1) * RP - 1; r >= part * RP; --r) {
+            s += sDb[r * LD + c];
+            if (r < p.len) store_out<OB>(a.dg, ((size_t)(p.t0 + r) * a.H + h) * D + c, s);
         }
     }
 }
 
-template <int D, class IN, bool OB>
+template <int D, class IN, bool OB, bool SG>
 hipError_t launch_typed(const BackwardArgs& a, int nc_max, hipStream_t st) {
     const int units = a.N * a.H;
     if (a.cu) {
         seq_scan_kernel<<<1, BT, 0, st>>>(a.cu, a.N, a.seq_chunk0);
     }
-    if (nc_max > 0) prep_kernel<D, IN><<<nc_max * a.H, BT, 0, st>>>(a);
+    if (nc_max > 0) prep_kernel<D, IN, SG><<<nc_max * a.H, BT, 0, st>>>(a);
     if (units > 0) {
         state_fwd_kernel<D, IN><<<units * (D / TW), BT, 0, st>>>(a);
         state_rev_kernel<D, IN><<<units * (D / TW), BT, 0, st>>>(a);
     }
-    if (nc_max > 0) grad_kernel<D, IN, OB><<<nc_max * a.H, BT, 0, st>>>(a);
+    if (nc_max > 0) grad_kernel<D, IN, OB, SG><<<nc_max * a.H, BT, 0, st>>>(a);
     return hipGetLastError();
 }
 
@@ -817,7 +866,7 @@ hipError_t launch_backward(BackwardArgs a, const BackwardPlan& pl, void* workspa
     const int nc = static_cast<int>(pl.nc_max);
 #define KDA_BWD_CASE(DD, IN, OB)                                                              \
     if (a.D == DD && a.in_bf16 == std::is_same<IN, BF16>::value && a.out_bf16 == OB)         \
-        return launch_typed<DD, IN, OB>(a, nc, st);
+        return a.scalar_gate ? launch_typed<DD, IN, OB, true>(a, nc, st) : launch_typed<DD, IN, OB, false>(a, nc, st);
     KDA_BWD_CASE(128, BF16, false)
     KDA_BWD_CASE(128, BF16, true)
     KDA_BWD_CASE(128, F32, false)

@@ -83,6 +83,7 @@ struct BackwardArgs {
     int32_t* seq_chunk0 = nullptr;
     int B, T, H, D, N;
     bool in_bf16, out_bf16;
+    bool scalar_gate = false;                // log_alpha and dlog_alpha are [B, T, H]
 };
 
 struct BackwardPlan {

@@ -22,7 +22,7 @@ CHUNK = 0          # library default chunk length (32 tokens); 32 and 64 are bui
 EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_step",
             "kda_recurrent_fwd", "gdn_chunk_fwd", "gdn_recurrent_step", "gdn_recurrent_fwd",
             "kda_chunk_fwd_fused", "kda_recurrent_step_fused", "kda_chunk_bwd_workspace_bytes",
-            "kda_chunk_bwd")
+            "kda_chunk_bwd", "gdn_chunk_bwd")
 KDA_FUSE_QK_L2NORM, KDA_FUSE_BETA_SIGMOID, KDA_FUSE_DECAY_LOGSIGMOID = 1, 2, 4
 
 
@@ -68,6 +68,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_bwd_workspace_bytes.restype = sz
     lib.kda_chunk_bwd.argtypes = [vp] * 9 + [i32] * 7 + [i32, i32] + [vp] * 6 + [vp, sz, vp]
     lib.kda_chunk_bwd.restype = i32
+    lib.gdn_chunk_bwd.argtypes = lib.kda_chunk_bwd.argtypes
+    lib.gdn_chunk_bwd.restype = i32
     for pre in ("kda", "gdn"):
         getattr(lib, f"{pre}_chunk_fwd").argtypes = lib.kda_chunk_fwd.argtypes
         getattr(lib, f"{pre}_chunk_fwd").restype = i32
@@ -264,7 +266,7 @@ def kda_chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, num_seqs, has_cu_seqlens, chu
 
 def kda_chunk_bwd(q, k, v, log_alpha, beta, d_o, S0=None, cu_seqlens=None, dS_final=None, *,
                   grad_dtype=torch.float32, grads=None, want_dS0=True, workspace=None, chunk=CHUNK,
-                  stream=None):
+                  stream=None, _fn="kda_chunk_bwd"):
     """Gradient of kda_chunk_fwd.  Inputs as for kda_chunk_fwd plus d_o [B, T, H, Dv]
     (the inputs' dtype) and dS_final [N, H, Dk, Dv] float32 or None.  Returns a dict
     dq, dk, dv, dlog_alpha, dbeta (grad_dtype) and dS0 (float32, or None when
@@ -278,7 +280,7 @@ def kda_chunk_bwd(q, k, v, log_alpha, beta, d_o, S0=None, cu_seqlens=None, dS_fi
         raise TypeError("d_o must have the inputs' dtype")
     g = dict(grads or {})
     dev = q.device
-    for name, shape in (("dq", q.shape), ("dk", q.shape), ("dv", v.shape), ("dlog_alpha", q.shape),
+    for name, shape in (("dq", q.shape), ("dk", q.shape), ("dv", v.shape), ("dlog_alpha", log_alpha.shape),
                         ("dbeta", beta.shape)):
         if g.get(name) is None:
             g[name] = torch.empty(shape, dtype=grad_dtype, device=dev)
@@ -289,11 +291,16 @@ def kda_chunk_bwd(q, k, v, log_alpha, beta, d_o, S0=None, cu_seqlens=None, dS_fi
     if workspace is None and ws_need > 0:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = load_library().kda_chunk_bwd(
+    st = getattr(load_library(), _fn)(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
         _ptr(d_o), _ptr(dS_final), B, T, H, Dk, Dv, N, chunk, _dtype_code(q.dtype), _dtype_code(g["dq"].dtype),
         _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dlog_alpha"]), _ptr(g["dbeta"]), _ptr(g.get("dS0")),
         _ptr(workspace), ws_bytes, _stream_ptr(stream))
     if st != KDA_OK:
-        raise KDAError(st, "kda_chunk_bwd")
+        raise KDAError(st, _fn)
     return g
+
+
+def gdn_chunk_bwd(q, k, v, log_alpha, beta, d_o, S0=None, cu_seqlens=None, dS_final=None, **kw):
+    """Gradient of gdn_chunk_fwd: log_alpha and the returned dlog_alpha are [B, T, H]."""
+    return kda_chunk_bwd(q, k, v, log_alpha, beta, d_o, S0, cu_seqlens, dS_final, _fn="gdn_chunk_bwd", **kw)

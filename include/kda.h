@@ -262,6 +262,21 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void
                          void* dq, void* dk, void* dv, void* dlog_alpha, void* dbeta, float* dS0,
                          void* workspace, size_t workspace_bytes, kda_stream_t stream);
 
+/*
+ * gdn_chunk_bwd -- gradient of gdn_chunk_fwd (scalar gate): the same arguments as
+ * kda_chunk_bwd except log_alpha [B, T, H] and dlog_alpha [B, T, H].  The scalar gate is
+ * the per-channel rule with one log-decay broadcast over the key channels, so its
+ * gradient is the per-channel dlog_alpha summed over the key channels.  Uses
+ * kda_chunk_bwd_workspace_bytes().
+ */
+kda_status gdn_chunk_bwd(const void* q, const void* k, const void* v, const void* log_alpha,
+                         const void* beta, const float* S0, const int32_t* cu_seqlens,
+                         const void* d_o, const float* dS_final,
+                         int B, int T, int H, int Dk, int Dv, int num_seqs, int chunk,
+                         kda_dtype in_dtype, kda_dtype grad_dtype,
+                         void* dq, void* dk, void* dv, void* dlog_alpha, void* dbeta, float* dS0,
+                         void* workspace, size_t workspace_bytes, kda_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,29 +33,47 @@ def _kda():
 
 def gpu_bwd(d, g, grad_dtype=torch.float32, want_dS0=True):
     kda = _kda()
+    fn = kda.gdn_chunk_bwd if d.get("scalar_gate") else kda.kda_chunk_bwd
     dev = {kk: to_dev(d[kk]) for kk in ("q", "k", "v", "log_alpha", "beta")}
     S0 = to_dev(d["S0"]) if d["S0"] is not None else None
     cu = to_dev(d["cu_seqlens"]) if d["cu_seqlens"] is not None else None
     dsf = to_dev(g["dS_final"]) if g["dS_final"] is not None else None
-    out = kda.kda_chunk_bwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], to_dev(g["d_o"]),
-                            S0, cu, dsf, grad_dtype=grad_dtype, want_dS0=want_dS0)
+    out = fn(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], to_dev(g["d_o"]),
+             S0, cu, dsf, grad_dtype=grad_dtype, want_dS0=want_dS0)
     torch.cuda.synchronize()
     return {kk: to_host(t) for kk, t in out.items() if t is not None}
 
 
 def oracle_bwd(d, g, heads=None):
+    """The oracle's gradient.  A scalar gate is the per-channel rule with the decay
+    broadcast over the key channels, so its dlog_alpha is the per-channel one summed over
+    them (the chain rule through the broadcast)."""
     sel = slice(None) if heads is None else heads
     args = [d[kk][:, :, sel] for kk in ("q", "k", "v", "log_alpha", "beta")]
+    if d.get("scalar_gate"):
+        la = inputs.to_float(args[3]).astype(np.float64)
+        args[3] = np.ascontiguousarray(np.broadcast_to(la[..., None], args[0].shape))
+        args = [inputs.to_float(x).astype(np.float64) for x in args[:3]] + [args[3]] + \
+            [inputs.to_float(args[4]).astype(np.float64)]
     S0 = None if d["S0"] is None else d["S0"][:, sel]
     dsf = None if g["dS_final"] is None else g["dS_final"][:, sel]
-    return oracle.kda_bwd(*args, g["d_o"][:, :, sel], S0=S0, cu_seqlens=d["cu_seqlens"], dS_final=dsf)
+    do = g["d_o"][:, :, sel]
+    if d.get("scalar_gate"):
+        do = inputs.to_float(do).astype(np.float64)
+    out = oracle.kda_bwd(*args, do, S0=S0, cu_seqlens=d["cu_seqlens"], dS_final=dsf)
+    if d.get("scalar_gate"):
+        out["dlog_alpha"] = out["dlog_alpha"].sum(axis=-1)
+    return out
 
 
 def metrics(got, ref, cu, heads=None):
     sel = slice(None) if heads is None else heads
     err = {}
     for name in ("dq", "dk", "dv", "dlog_alpha"):
-        err[name] = o_metric(got[name][:, :, sel], ref[name], cu)
+        x, y = got[name][:, :, sel], ref[name]
+        if x.ndim == 3:   # scalar-gate dlog_alpha [B, T, H]
+            x, y = x[..., None], y[..., None]
+        err[name] = o_metric(x, y, cu)
     err["dbeta"] = o_metric(got["dbeta"][:, :, sel, None], ref["dbeta"][..., None], cu)
     if "dS0" in got:
         err["dS0"] = state_metric(got["dS0"][:, sel], ref["dS0"])
@@ -175,3 +193,15 @@ def test_matches_forward_directional_derivative():
     print(f"[backward] directional derivative: grad {want:.6f}  central differences {fd1:.6f} {fd2:.6f} "
           f"extrapolated {fd:.6f}", flush=True)
     assert abs(want - fd) <= 1e-3 * max(1.0, abs(fd))
+
+
+# ------------------------------------------------------------------ scalar gate (gdn_chunk_bwd)
+@pytest.mark.parametrize("D", [64, 128])
+def test_scalar_gate_fp32_ragged(D):
+    d = inputs.make_prefill(W[0], seed=121, B=2, T=45, H=2, D=D, s0=True, mu=0.0, s=2.0, scalar_gate=True)
+    check(d, inputs.make_output_grads(d, seed=221), f"scalar gate fp32 ragged D={D}")
+
+
+def test_scalar_gate_packed_long_context_recipe():
+    d = inputs.make_prefill(W[6], seed=122, H=2, lengths=[300, 0, 41, 1, 96])
+    check(d, inputs.make_output_grads(d, seed=222), "scalar gate packed, long-context recipe")

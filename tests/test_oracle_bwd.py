@@ -225,3 +225,23 @@ def test_planted_mistakes_are_caught():
             assert failed, f"planted mistake '{name}' passed every pin"
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
+
+
+def test_scalar_gate_gradient_is_the_channel_sum():
+    """A scalar gate is the per-channel rule with one log-decay broadcast over the key
+    channels ("Decoding Hybrid Attention Architectures", section 3.3), so its gradient is
+    the per-channel dlog_alpha summed over the channels: checked against central
+    differences in the scalar log-decay."""
+    c = bcase(40, B=1, T=9, H=2, Dk=4, Dv=3)
+    gs = c["log_alpha"][..., 0].copy()                       # [B, T, H]
+    c["log_alpha"] = np.ascontiguousarray(np.broadcast_to(gs[..., None], c["q"].shape))
+    want = grads(c)["dlog_alpha"].sum(axis=-1)
+    num = np.zeros_like(gs)
+    h = 1e-6
+    for i in np.ndindex(gs.shape):
+        for sign in (1, -1):
+            x = gs.copy()
+            x[i] += sign * h
+            c["log_alpha"] = np.ascontiguousarray(np.broadcast_to(x[..., None], c["q"].shape))
+            num[i] += sign * loss(c) / (2 * h)
+    assert relerr(want, num) < 1e-7
