@@ -11,6 +11,7 @@
 
 #include "kda.h"
 #include "kda_launch.h"
+#include "kda_backward.h"
 
 namespace {
 

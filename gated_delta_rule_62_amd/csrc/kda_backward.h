@@ -1,0 +1,35 @@
+// kda_backward.h -- host-side plan and launcher of the chunkwise backward
+// (kda_backward.hip), shared with kda_api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Gradient of the chunkwise prefill (kda_backward.hip).  Chunk length 32.
+struct BackwardArgs {
+    const void *q, *k, *v, *g, *beta, *dO;   // inputs and the output gradient, in dtype
+    const float *S0, *dS_final;              // [N, H, D, D] or nullptr (zeros)
+    const int32_t* cu;                       // packed sequence offsets or nullptr
+    void *dq, *dk, *dv, *dg, *dbeta;         // gradients, out dtype
+    float* dS0;                              // [N, H, D, D] or nullptr
+    // workspace views (set by launch_backward)
+    float *prep = nullptr, *states = nullptr, *dstates = nullptr;
+    int32_t* seq_chunk0 = nullptr;
+    int B, T, H, D, N;
+    bool in_bf16, out_bf16;
+    bool scalar_gate = false;                // log_alpha and dlog_alpha are [B, T, H]
+};
+
+struct BackwardPlan {
+    size_t nc_max = 0;   // upper bound on the number of chunks
+    size_t off_seq = 0, off_prep = 0, off_states = 0, off_dstates = 0;
+    size_t workspace_bytes = 0;
+};
+
+BackwardPlan plan_backward(int B, int T, int H, int D, int N, bool varlen);
+hipError_t launch_backward(BackwardArgs a, const BackwardPlan& plan, void* workspace, hipStream_t stream);
+
+}  // namespace kda

@@ -43,6 +43,7 @@
 
 #include "kda_device.h"
 #include "kda_launch.h"
+#include "kda_backward.h"
 
 namespace kda {
 namespace {
