@@ -17,6 +17,7 @@ struct BackwardArgs {
     float* dS0;                              // [N, H, D, D] or nullptr
     // workspace views (set by launch_backward)
     float *prep = nullptr, *states = nullptr, *dstates = nullptr;
+    float *rbuf = nullptr, *debuf = nullptr;  // per (chunk, head): R = V - K S and dE, C x Dv
     int32_t* seq_chunk0 = nullptr;
     int B, T, H, D, N;
     bool in_bf16, out_bf16;
@@ -25,7 +26,7 @@ struct BackwardArgs {
 
 struct BackwardPlan {
     size_t nc_max = 0;   // upper bound on the number of chunks
-    size_t off_seq = 0, off_prep = 0, off_states = 0, off_dstates = 0;
+    size_t off_seq = 0, off_prep = 0, off_states = 0, off_dstates = 0, off_r = 0, off_de = 0;
     size_t workspace_bytes = 0;
 };
 

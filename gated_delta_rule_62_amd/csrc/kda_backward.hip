@@ -25,7 +25,8 @@
 //   dlog_alpha = reverse cumulative sum of db over the chunk's rows.
 //
 // Kernels (all products on the fp32 matrix cores, v_mfma_f32_16x16x4_f32, operands
-// from LDS):
+// from LDS; the state passes also keep R = V - K' S_m and dE of every chunk, which the
+// gradient step reads instead of recomputing):
 //   seq_scan_kernel   packed batches: first chunk index of every sequence
 //   prep_kernel       per (chunk, head): Q', K', K'', M, P, L, e_m, e_n, beta, b - m -> record
 //   state_fwd_kernel  per (sequence, head, 16 value columns): every chunk's entry state
@@ -452,9 +453,12 @@ __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
             for (int v = 0; v < 4; ++v) sR[kh * BC * LT + (16 * rt + acc_row(v)) * LT + acc_col()] = acc[v];
         }
         lds_barrier();
-        for (int e = tid; e < BC * TW; e += BT) {
+        float* rout = a.rbuf + ((size_t)(c0 + i) * a.H + h) * BC * D + jt * TW;
+        for (int e = tid; e < BC * TW; e += BT) {   // R = V - K' S_m (kept for the gradient step), Y = Diag(beta) R
             const int r = e / TW, c = e % TW;
-            sR[r * LT + c] = sB[r] * (sV[r * LT + c] - sR[r * LT + c] - sR[BC * LT + r * LT + c]);
+            const float rr = sV[r * LT + c] - sR[r * LT + c] - sR[BC * LT + r * LT + c];
+            rout[(size_t)r * D + c] = rr;
+            sR[r * LT + c] = sB[r] * rr;
         }
         lds_barrier();
         if (w < 2) {   // E = M Y
@@ -552,9 +556,12 @@ __global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
             for (int v = 0; v < 4; ++v) part[(16 * rt + acc_row(v)) * LT + acc_col()] = acc[v];
         }
         lds_barrier();
-        for (int e = tid; e < BC * TW; e += BT) {
+        float* deout = a.debuf + ((size_t)j * a.H + h) * BC * D + jt * TW;
+        for (int e = tid; e < BC * TW; e += BT) {   // dE (kept for the gradient step)
             const int r = e / TW, c = e % TW;
-            sR[r * LT + c] += sV[r * LT + c];
+            const float x = sR[r * LT + c] + sV[r * LT + c];
+            sR[r * LT + c] = x;
+            deout[(size_t)r * D + c] = x;
         }
         lds_barrier();
         if (w < 2) {   // -dV = -Diag(beta) M^T dE
@@ -597,7 +604,7 @@ __global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
     static_assert(LT == LC, "the C x C products reuse C x GW buffers");
     static_assert(BC * LD <= D * LT, "the decay and db planes reuse the state tiles");
     __shared__ __attribute__((aligned(16))) float sQp[BC * LD], sKp[BC * LD], sKpp[BC * LD];
-    __shared__ __attribute__((aligned(16))) float sM[BC * LC], sP[BC * LC], sL[BC * LC];
+    __shared__ __attribute__((aligned(16))) float sM[BC * LC], sL[BC * LC];
     __shared__ __attribute__((aligned(16))) float sSm[D * LT], sdSn[D * LT];
     __shared__ __attribute__((aligned(16))) float sV[BC * LT], sY[BC * LT], sO[BC * LT], sE[BC * LT];
     __shared__ __attribute__((aligned(16))) float sdE[BC * LT], sdY[BC * LT], smdV[BC * LT];
@@ -612,26 +619,29 @@ __global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
     const float* S = a.states + (slot * a.H + h) * DD;
     const float* Snext = a.states + ((slot + 1) * a.H + h) * DD;
     const float* dS = a.dstates + ((size_t)j * a.H + h) * DD;
+    const float* Rg = a.rbuf + ((size_t)j * a.H + h) * BC * D;    // R = V - K' S_m of the state pass
+    const float* dEg = a.debuf + ((size_t)j * a.H + h) * BC * D;  // dE of the reverse pass
 
-    // one column tile of S, dS_next, S_next, V and dO, fetched a tile ahead
+    // one column tile of S, dS_next, S_next, R, dE and dO, fetched a tile ahead
     Stage<D, GW> rS, rdS, rSn;
-    StageRows<IN, GW> rV, rO;
+    Stage<BC, GW> rR, rdE;
+    StageRows<IN, GW> rO;
     auto fetch = [&](int ct) __attribute__((always_inline)) {
         rS.load(S + ct * GW, D);
         rdS.load(dS + ct * GW, D);
         rSn.load(Snext + ct * GW, D);
-        rV.load(a.v, p.t0, p.len, a.H, h, D, ct * GW);
+        rR.load(Rg + ct * GW, D);
+        rdE.load(dEg + ct * GW, D);
         rO.load(a.dO, p.t0, p.len, a.H, h, D, ct * GW);
     };
     Stage<BC, D> rX;       // decay exponents b - m, used after the column loop
     {
         Stage<BC, D> r1, r2, r3;
-        Stage<BC, BC> r4, r5, r6;
+        Stage<BC, BC> r4, r6;
         r1.load(rec + Rec<D>::QP, D);
         r2.load(rec + Rec<D>::KP, D);
         r3.load(rec + Rec<D>::KPP, D);
         r4.load(rec + Rec<D>::M, BC);
-        r5.load(rec + Rec<D>::P, BC);
         r6.load(rec + Rec<D>::L, BC);
         const float em = rec[Rec<D>::EM + (tid & (D - 1))], en = rec[Rec<D>::EN + (tid & (D - 1))];
         const float bt = rec[Rec<D>::BETA + (tid & (BC - 1))];
@@ -641,7 +651,6 @@ __global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
         r2.store(sKp, LD);
         r3.store(sKpp, LD);
         r4.store(sM, LC);
-        r5.store(sP, LC);
         r6.store(sL, LC);
         if (tid < D) {
             sEm[tid] = em;
@@ -662,8 +671,19 @@ __global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
 
     for (int ct = 0; ct < NCT; ++ct) {
         lds_barrier();
-        rV.store(sV, LT);
+        rdE.store(sdE, LT);
         rO.store(sO, LT);
+#pragma unroll
+        for (int it = 0; it < Stage<BC, GW>::IT; ++it) {   // R, and Y = Diag(beta) R
+            constexpr int C4 = GW / 4;
+            const int e = tid + it * BT, r = e / C4, c = 4 * (e % C4);
+            if (Stage<BC, GW>::live(e)) {
+                const v4f x = rR.x[it];
+                const float b = sB[r];
+                *reinterpret_cast<v4f*>(sV + r * LT + c) = x;
+                *reinterpret_cast<v4f*>(sY + r * LT + c) = v4f{x.x * b, x.y * b, x.z * b, x.w * b};
+            }
+        }
         // S_m, dS_n tiles; rowsum(dS_next * S_next) for the last row's db
 #pragma unroll
         for (int it = 0; it < Stage<D, GW>::IT; ++it) {
@@ -680,23 +700,6 @@ __global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
             if (c == 0) sDbn[r] += t;
         }
         if (ct + 1 < NCT) fetch(ct + 1);
-        lds_barrier();
-        {
-            f4 acc = zero4();   // R = V - K' S_m;  Y = Diag(beta) R
-            mma<D>(acc, sKp + 16 * trt * LD, LD, 1, sSm + 16 * tct, LT, 1);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int r = 16 * trt + acc_row(v), c = 16 * tct + acc_col();
-                const float x = sV[r * LT + c] - acc[v];
-                sV[r * LT + c] = x;
-                sY[r * LT + c] = sB[r] * x;
-            }
-            f4 d = zero4();     // dE = P^T dO + K'' dS_n
-            mma<BC>(d, sP + 16 * trt, 1, LC, sO + 16 * tct, LT, 1);
-            mma<D>(d, sKpp + 16 * trt * LD, LD, 1, sdSn + 16 * tct, LT, 1);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) sdE[(16 * trt + acc_row(v)) * LT + 16 * tct + acc_col()] = d[v];
-        }
         lds_barrier();
         {
             f4 e = zero4();     // E = M Y
@@ -854,6 +857,10 @@ BackwardPlan plan_backward(int B, int T, int H, int D, int N, bool varlen) {
     off += up256(sizeof(float) * (nc + (size_t)N) * H * D * D);
     pl.off_dstates = off;
     off += up256(sizeof(float) * nc * H * D * D);
+    pl.off_r = off;
+    off += up256(sizeof(float) * nc * H * BC * D);
+    pl.off_de = off;
+    off += up256(sizeof(float) * nc * H * BC * D);
     pl.workspace_bytes = off;
     return pl;
 }
@@ -864,6 +871,8 @@ hipError_t launch_backward(BackwardArgs a, const BackwardPlan& pl, void* workspa
     a.prep = reinterpret_cast<float*>(ws + pl.off_prep);
     a.states = reinterpret_cast<float*>(ws + pl.off_states);
     a.dstates = reinterpret_cast<float*>(ws + pl.off_dstates);
+    a.rbuf = reinterpret_cast<float*>(ws + pl.off_r);
+    a.debuf = reinterpret_cast<float*>(ws + pl.off_de);
     const int nc = static_cast<int>(pl.nc_max);
 #define KDA_BWD_CASE(DD, IN, OB)                                                              \
     if (a.D == DD && a.in_bf16 == std::is_same<IN, BF16>::value && a.out_bf16 == OB)         \

@@ -160,12 +160,12 @@ def test_backward_workspace_query(lib):
     up = lambda x: (x + 255) // 256 * 256
     rec = 4 * 32 * 128 + 3 * 32 * 32 + 2 * 128 + 32          # floats per (chunk, head) record
     nc, H, D = 4 * 128, 16, 128                                # 4 sequences of 4096 tokens
-    want = up(4 * nc * H * rec) + up(4 * (nc + 4) * H * D * D) + up(4 * nc * H * D * D)
+    want = up(4 * nc * H * rec) + up(4 * (nc + 4) * H * D * D) + up(4 * nc * H * D * D) + 2 * up(4 * nc * H * 32 * D)
     assert q(4, 4096, 16, 128, 128, 4, False) == want
     # packed: a chunk-start table and room for ceil(T / 32) + N chunks
     nc = 1000 // 32 + 1 + 3
     want = up(4 * 4) + up(4 * nc * 2 * (4 * 32 * 64 + 3 * 32 * 32 + 2 * 64 + 32)) + \
-        up(4 * (nc + 3) * 2 * 64 * 64) + up(4 * nc * 2 * 64 * 64)
+        up(4 * (nc + 3) * 2 * 64 * 64) + up(4 * nc * 2 * 64 * 64) + 2 * up(4 * nc * 2 * 32 * 64)
     assert q(1, 1000, 2, 64, 64, 3, True) == want
     assert q(1, 64, 2, 96, 96, 1, False) == 0
     assert q(1, 64, 2, 128, 128, 1, False, chunk=64) == 0
