@@ -91,7 +91,8 @@ def counted_traffic(kind: str):
     except (OSError, KeyError, ValueError):
         return None
     files = {"decode": ["kda_decode.hip", "kda_device.h", "kda_launch.h"],
-             "prefill": ["kda_prefill.hip", "kda_device.h", "kda_launch.h"]}[kind]
+             "prefill": ["kda_prefill.hip", "kda_device.h", "kda_launch.h"],
+             "backward": ["kda_backward.hip", "kda_backward.h", "kda_device.h"]}[kind]
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(ROOT, "gated_delta_rule_62_amd", "csrc", f), "rb") as fh:
@@ -381,6 +382,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": bwd_flops / (bwd_ms / 1e3) / 1e12, "peak": FP32_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": bwd_flops / (bwd_ms / 1e3) / 1e12 / FP32_PEAK_TFLOPS,
                      "flops_per_call": bwd_flops, "bytes_per_call": bwd_bytes,
+                     "traffic": counted_traffic("backward"),
                      "hbm_frac": bwd_bytes / (bwd_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
                      "flop_convention": f"{backward_alg_flops_per_token_head(d)} per token-head "
                                         "(20 d^2 + 16 C d, fp32 matrix-core products)"},

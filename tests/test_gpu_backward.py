@@ -205,3 +205,34 @@ def test_scalar_gate_fp32_ragged(D):
 def test_scalar_gate_packed_long_context_recipe():
     d = inputs.make_prefill(W[6], seed=122, H=2, lengths=[300, 0, 41, 1, 96])
     check(d, inputs.make_output_grads(d, seed=222), "scalar gate packed, long-context recipe")
+
+
+def test_long_context_full_size_identities():
+    """Long-context workload at full size (B=1, T=65536, H=32, d=128, bf16, S0 != 0), where
+    the oracle would take hours: properties that hold at any size.  o is linear in q, and
+    (o, S_final) are jointly linear in (v, S0), so with this library's forward outputs
+    <dq, q> = <dO, o> and <dv, v> + <dS0, S0> = <dO, o> + <dS_final, S_final> (per head,
+    fp64 sums of the fp32 results)."""
+    kda = _kda()
+    x = inputs.device_prefill(W[2])
+    g = inputs.device_output_grads(x, seed=212)
+    print(f"[backward] long context full size: T={x['T']} H={x['H']}", flush=True)
+    o, Sf = kda.kda_chunk_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"], None,
+                              out_dtype=torch.float32)
+    gr = kda.kda_chunk_bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], g["d_o"], x["S0"], None,
+                           g["dS_final"])
+    torch.cuda.synchronize()
+    f64 = lambda t: t.double()
+    dims = (0, 1, 3)   # sum over batch, tokens, channels: one value per head
+    do_o = (f64(g["d_o"]) * f64(o)).sum(dim=dims)
+    lhs1 = (f64(gr["dq"]) * f64(x["q"])).sum(dim=dims)
+    lhs2 = (f64(gr["dv"]) * f64(x["v"])).sum(dim=dims) + (f64(gr["dS0"]) * f64(x["S0"])).sum(dim=(0, 2, 3))
+    rhs2 = do_o + (f64(g["dS_final"]) * f64(Sf)).sum(dim=(0, 2, 3))
+    scale1 = (f64(g["d_o"]).abs() * f64(o).abs()).sum(dim=dims)
+    scale2 = scale1 + (f64(g["dS_final"]).abs() * f64(Sf).abs()).sum(dim=(0, 2, 3))
+    e1 = ((lhs1 - do_o).abs() / scale1).max().item()
+    e2 = ((lhs2 - rhs2).abs() / scale2).max().item()
+    print(f"[backward]   identity errors (relative to the sum of |terms|): q {e1:.2e}  v,S0 {e2:.2e}", flush=True)
+    for t in gr.values():
+        assert torch.isfinite(t).all()
+    assert e1 < 1e-4 and e2 < 1e-4
