@@ -1469,6 +1469,26 @@ void pipe_kernel(KernelArgs a) {
 
     // interval 3: St <- Diag(rho) (St + Ktil_m^T Unew), and the output rows of the chunk
     auto consume_update = [&](const Buf& B, int chunk) {
+        // The output-gate logits of this chunk's rows are requested before the state update,
+        // so their latency overlaps it (fused output pass only; rows past the end of a
+        // ragged chunk read its last row and are not stored).
+        using GRaw = typename std::conditional<std::is_same<IN, F32>::value, f32x4, uint2>::type;
+        GRaw graw[NRT][CT];
+        if constexpr (MODE == 0 && FUSE) {
+            if (a.out_gate) {
+                const long ts = t0 + static_cast<long>(chunk) * C;
+                const int ntok = static_cast<int>(min(static_cast<long>(C), t1 - ts));
+                const size_t obase = (static_cast<size_t>(ts) * H + h) * D + j0 + 4 * g4;
+#pragma unroll
+                for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) {
+                        const int row = min(16 * rt + lr, ntok - 1);
+                        graw[rt][ct] = *reinterpret_cast<const GRaw*>(static_cast<const ST*>(a.out_gate) + obase +
+                                                                      static_cast<unsigned>(row * HD + 16 * ct));
+                    }
+            }
+        }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             const f32x4 rh = *reinterpret_cast<const f32x4*>(&B.rho[16 * rt + 4 * g4]);
@@ -1500,8 +1520,14 @@ void pipe_kernel(KernelArgs a) {
                         f32x4 ov = Z[rt][ct] * fo;
                         if constexpr (FUSE) {
                             if (a.out_gate) {
-                                float gv[4];
-                                load4<IN>(static_cast<const ST*>(a.out_gate), obase + static_cast<unsigned>(row * HD + 16 * ct), gv);
+                                f32x4 gv;
+                                if constexpr (std::is_same<IN, F32>::value) {
+                                    gv = graw[rt][ct];
+                                } else {
+                                    const uint2 x = graw[rt][ct];
+                                    gv = f32x4{__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u),
+                                               __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xffff0000u)};
+                                }
 #pragma unroll
                                 for (int e = 0; e < 4; ++e) ov[e] *= sigmoid_f(gv[e]);
                             }
