@@ -153,6 +153,14 @@ def test_zero_tokens_and_empty_sequences():
     g = inputs.make_output_grads(d, seed=209)
     got = gpu_bwd(d, g)
     np.testing.assert_array_equal(got["dS0"], g["dS_final"])
+    # equal-length batch with no tokens: dS0 = dS_final, and zeros without dS_final
+    d = inputs.make_prefill(W[1], seed=110, B=3, T=0, H=2, D=128, s0=True)
+    g = inputs.make_output_grads(d, seed=210)
+    got = gpu_bwd(d, g)
+    np.testing.assert_array_equal(got["dS0"], g["dS_final"])
+    g["dS_final"] = None
+    got = gpu_bwd(d, g)
+    assert not np.any(got["dS0"])
 
 
 def test_full_size_train_prefill_sampled_heads():
