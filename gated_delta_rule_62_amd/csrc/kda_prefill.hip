@@ -164,6 +164,44 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Counters in LDS that order the producer and consumer waves of a workgroup without a
+// workgroup barrier.  A wave publishes with signal_count once its earlier LDS accesses are
+// complete; a wave waits with wait_count until a counter reaches a target.  Global loads in
+// flight are not waited on by either.  A wait is bounded: after 2^16 polls (milliseconds) it
+// marks the workgroup broken and returns, every later wait returns at once, and the kernel
+// poisons the states it writes, so an ordering mistake shows as NaN results, not a stuck
+// workgroup.
+struct SyncCounters {
+    int p1, p2, ready;   // producer waves done with phase 1, phase 2, a whole chunk
+    int done[2];         // consumer waves done with a chunk, per LDS buffer
+    int broken;
+};
+
+__device__ __forceinline__ void signal_count(int* c) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Explicit LDS accesses (address space 3): a volatile access through a generic pointer
+// would become a flat access, whose completion wait also waits for global loads in flight.
+typedef __attribute__((address_space(3))) volatile int lds_vint;
+
+__device__ __forceinline__ int lds_read(const int* p) { return *(const lds_vint*)(p); }
+
+__device__ __forceinline__ void wait_count(const int* c, int target, int* broken) {
+    for (int polls = 0;; ++polls) {
+        const int v = __builtin_amdgcn_readfirstlane(lds_read(c));
+        const int b = __builtin_amdgcn_readfirstlane(lds_read(broken));
+        if (v >= target || b) break;
+        if (polls >= (1 << 16)) {
+            *(lds_vint*)(broken) = 1;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+}
+
 // Order LDS accesses between lanes of one wave (no workgroup barrier involved).
 __device__ __forceinline__ void wave_lds_sync() {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -844,6 +882,7 @@ template <int D, int MODE, bool VLDS>
 struct PSmem {
     PBuf<D, MODE, VLDS> buf[2];
     float a[2][16][20];         // diagonal 16x16 blocks of A (fp32), producer-private
+    SyncCounters sync;
 };
 
 // SG (scalar gate): log_alpha is one value per (token, head), [B, T, H] -- the gated delta
@@ -886,7 +925,7 @@ void pipe_kernel(KernelArgs a) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = a.H;
     const bool producer = w < NPW;
-    // The last two producer waves invert the two diagonal blocks (one each) in interval 3.
+    // The last two producer waves invert the two diagonal blocks (one each) in phase 3.
     const bool solver = w >= NPW - 2;
 
     // ---------------------------------------------------------------- work unit
@@ -929,15 +968,18 @@ void pipe_kernel(KernelArgs a) {
             sm.buf[b].p[r / (C * C)][r % (C * C)] = 0;
         }
     }
+    if (tid == 0) sm.sync = SyncCounters{0, 0, 0, {0, 0}, 0};
+    lds_barrier();
+    int* const broken = &sm.sync.broken;
 
     // ================================================================ producer state
     quad pk[TPG], pq[TPG], pg[TPG], pvq[TPG];
     elem pgs[TPG];   // scalar gate: log_alpha of this lane's tokens
     elem pb = 0;
-    uint2 kth[TPG], ktl[TPG];   // split Ktil_m words, kept from interval 1 for Ktil_m^T in interval 3
+    uint2 kth[TPG], ktl[TPG];   // split Ktil_m words, kept from phase 1 for Ktil_m^T in phase 3
     float enm[4] = {1.f, 1.f, 1.f, 1.f};   // e^{b_n - b_m} of the chunk last produced
     // part 0: k and log_alpha; part 1: q, v and beta; -1: everything.  The two parts are requested
-    // in different intervals so the chip's memory requests are spread over the chunk loop.
+    // in different phases so the chip's memory requests are spread over the chunk loop.
     auto fetch = [&](int chunk, int part) {
         const long ts = t0 + static_cast<long>(chunk) * C;
         const int last = static_cast<int>(min(static_cast<long>(C), t1 - ts)) - 1;
@@ -986,7 +1028,7 @@ void pipe_kernel(KernelArgs a) {
         }
     };
 
-    // interval 1: decay prefix (in log2 units) and the decayed, split K / Q planes.  With
+    // phase 1: decay prefix (in log2 units) and the decayed, split K / Q planes.  With
     // the previous chunk's buffer `prev`, also that chunk's state factor rho.
     auto produce_decay = [&](Buf& B, int chunk, Buf* prev) {
         const long ts = t0 + static_cast<long>(chunk) * C;
@@ -1163,9 +1205,41 @@ void pipe_kernel(KernelArgs a) {
         rt = job == 1 ? 0 : 1;
         ct = job == 2 ? 1 : 0;
     };
-    // interval 2 (producer): the three A tiles
+    // phase 2, output pass: the P tile `job` of the chunk being built
+    auto produce_ptile = [&](Buf& B, int job) {
+        if constexpr (MODE == 0) {
+            int rt, ct;
+            tile_of(job, rt, ct);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int ao = K::tok(16 * ct + lr, 32 * ks + 8 * g4);
+                const int bo = K::tok(16 * rt + lr, 32 * ks + 8 * g4);
+                if constexpr (EXACT)
+                    acc = mfma(frag(&B.kb[0][ao]), frag(&B.qb[0][bo]), acc);
+                else if constexpr (SG)
+                    acc = mfma3(frag(&B.kb[0][ao]), frag(&B.kb[1][ao]), frag(&B.qb[0][bo]), frag(&B.qb[1][bo]), acc);
+                else
+                    acc = mfma3(frag(&B.kt[0][ao]), frag(&B.kt[1][ao]), frag(&B.qb[0][bo]), frag(&B.qb[1][bo]), acc);
+            }
+            f32x4 pv4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pv4[e] = (rt > ct || 4 * g4 + e <= lr) ? acc[e] : 0.f;
+            uint2 hi, lo;
+            split_quad(pv4[0], pv4[1], pv4[2], pv4[3], hi, lo);
+            const int idx = K::chm(16 * rt + lr, 8 * g4 + 4 * ct);   // kperm(16 ct + 4 g4 + e) = 8 g4 + 4 ct + e
+            *reinterpret_cast<uint2*>(&B.p[0][idx]) = hi;
+            *reinterpret_cast<uint2*>(&B.p[1][idx]) = lo;
+        }
+    };
+    // phase 2 (producer): the three A tiles, then in the output pass the three P tiles
     auto produce_products = [&](Buf& B) {
-        for (int job = w; job < 3; job += NPW) {
+        constexpr int NJ = MODE == 0 ? 6 : 3;
+        for (int job = w; job < NJ; job += NPW) {
+            if (job >= 3) {
+                produce_ptile(B, job - 3);
+                continue;
+            }
             int rt, ct;
             tile_of(job, rt, ct);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -1199,7 +1273,7 @@ void pipe_kernel(KernelArgs a) {
             }
         }
     };
-    // interval 2 (producer, fused prologue): per-token scalars for the consumers
+    // phase 2 (producer, fused prologue): per-token scalars for the consumers
     auto produce_token_scales = [&](Buf& B) {
         if constexpr (FUSE) {
             if (w == NPW - 1 && l < C) {
@@ -1211,38 +1285,8 @@ void pipe_kernel(KernelArgs a) {
             }
         }
     };
-    // interval 2 (consumers, output pass): the three P tiles of the chunk the producer is building
-    auto consume_ptiles = [&](Buf& B) {
-        if constexpr (MODE == 0) {
-            for (int job = ci; job < 3; job += K::NCW) {
-                int rt, ct;
-                tile_of(job, rt, ct);
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const int ao = K::tok(16 * ct + lr, 32 * ks + 8 * g4);
-                    const int bo = K::tok(16 * rt + lr, 32 * ks + 8 * g4);
-                    if constexpr (EXACT)
-                        acc = mfma(frag(&B.kb[0][ao]), frag(&B.qb[0][bo]), acc);
-                    else if constexpr (SG)
-                        acc = mfma3(frag(&B.kb[0][ao]), frag(&B.kb[1][ao]), frag(&B.qb[0][bo]), frag(&B.qb[1][bo]), acc);
-                    else
-                        acc = mfma3(frag(&B.kt[0][ao]), frag(&B.kt[1][ao]), frag(&B.qb[0][bo]), frag(&B.qb[1][bo]), acc);
-                }
-                f32x4 pv4;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) pv4[e] = (rt > ct || 4 * g4 + e <= lr) ? acc[e] : 0.f;
-                uint2 hi, lo;
-                split_quad(pv4[0], pv4[1], pv4[2], pv4[3], hi, lo);
-                const int idx = K::chm(16 * rt + lr, 8 * g4 + 4 * ct);   // kperm(16 ct + 4 g4 + e) = 8 g4 + 4 ct + e
-                *reinterpret_cast<uint2*>(&B.p[0][idx]) = hi;
-                *reinterpret_cast<uint2*>(&B.p[1][idx]) = lo;
-            }
-        }
-    };
-
-    // interval 3: Ktil_m^T over Ktil_m (read by the products), regrouped from the split words
-    // of interval 1, and X_bb = (I + A_bb)^{-1}
+    // phase 3: Ktil_m^T over Ktil_m (read by the products), regrouped from the split words
+    // of phase 1, and X_bb = (I + A_bb)^{-1}
     auto produce_inverse = [&](Buf& B) {
 #pragma unroll
         for (int ch = 0; ch < 4; ++ch) {
@@ -1321,9 +1365,9 @@ void pipe_kernel(KernelArgs a) {
     // gamma = e^{b_m} e^{b_n - b_m} and Khat = Ktil_m e^{b_n - b_m}, the chunk update is
     //   St <- Diag(rho) (St + Ktil_m^T Unew),  rho = e^{b_m'} e^{b_n - b_m}
     // with b_m' the next chunk's midpoint decay (rho = e^{b_n - b_m} after the last chunk, which
-    // leaves S itself).  The output pass splits St for the coming chunk at the end of
-    // interval 3, so interval 1 holds only MFMA work beside the producer's vector-ALU work; the
-    // summary pass, with twice the columns per compute unit, has no registers to spare for it.
+    // leaves S itself).  The output pass splits St for the coming chunk right after the update,
+    // so step 1 holds only MFMA work beside the producer's vector-ALU work; the summary pass,
+    // with twice the columns per compute unit, has no registers to spare for it.
     constexpr bool PRESPLIT = MODE == 0;
     bf16x8 sph[PRESPLIT ? KS : 1][CT], spl[PRESPLIT ? KS : 1][CT];
     auto split_state = [&]() {
@@ -1335,7 +1379,7 @@ void pipe_kernel(KernelArgs a) {
         }
     };
 
-    // interval 1: V loads, Y = Kbar_m St and Z = Qbar_m St, split per 32-deep step.
+    // consumer step 1: V loads, Y = Kbar_m St and Z = Qbar_m St.
     auto consume_project = [&](const Buf& B, int chunk) {
         const long ts = t0 + static_cast<long>(chunk) * C;
         const int last = static_cast<int>(min(static_cast<long>(C), t1 - ts)) - 1;
@@ -1393,7 +1437,7 @@ void pipe_kernel(KernelArgs a) {
                 }
             }
         }
-        // Y <- V - Kbar S (frees the raw V registers before interval 2)
+        // Y <- V - Kbar S (frees the raw V registers before the solve)
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
@@ -1419,9 +1463,9 @@ void pipe_kernel(KernelArgs a) {
             }
     };
 
-    // interval 2: Unew = (I + A)^{-1} Diag(beta) (V - Kbar S) one 16-token block at a time,
+    // consumer step 2: Unew = (I + A)^{-1} Diag(beta) (V - Kbar S) one 16-token block at a time,
     //   Unew_b = X_bb (beta_b (V - Kbar S)_b - sum_{k<b} A_bk Unew_k),
-    // then O = Z + P Unew (stored in interval 3).
+    // then O = Z + P Unew (stored in step 3).
     auto consume_solve = [&](const Buf& B) {
         bf16x4 uh[NRT][CT], ul[NRT][CT];
 #pragma unroll
@@ -1467,7 +1511,7 @@ void pipe_kernel(KernelArgs a) {
         }
     };
 
-    // interval 3: St <- Diag(rho) (St + Ktil_m^T Unew), and the output rows of the chunk
+    // consumer step 3: St <- Diag(rho) (St + Ktil_m^T Unew), and the output rows of the chunk
     auto consume_update = [&](const Buf& B, int chunk) {
         // The output-gate logits of this chunk's rows are requested before the state update,
         // so their latency overlaps it (fused output pass only; rows past the end of a
@@ -1540,52 +1584,49 @@ void pipe_kernel(KernelArgs a) {
     };
 
     // ================================================================ chunk loops
-    // Producer and consumer waves run separate loops that pass the same number of
-    // workgroup barriers: three for the first chunk's operands, then three per chunk.
+    // Producer and consumer waves run separate loops, ordered by the LDS counters alone (no
+    // workgroup barrier).  The producers build chunk i in three phases, each closed by a
+    // count that the other producers wait for: phase 1 (decay, planes, and the previous
+    // chunk's rho), phase 2 (A and P tiles), phase 3 (Ktil_m^T, diagonal inverses; closes
+    // `ready`).  Before phase 1 of chunk i they wait until every consumer is done with chunk
+    // i - 2, the last user of the same buffer.  A consumer runs chunk i once it is `ready`,
+    // and waits for the producers' phase 1 of chunk i + 1 (which writes chunk i's rho) before
+    // the state update.  So the producers run up to one chunk ahead, and a chunk costs the
+    // longer of the two sides, not the sum of the longer side of every phase.
+    const int n_chunks = c_end - c_begin;
     if (producer) {
-        if (c_begin < c_end) {
-            fetch(c_begin, -1);
-            produce_decay(sm.buf[c_begin & 1], c_begin, nullptr);
-            lds_barrier();
-            if (c_begin + 1 < c_end) fetch(c_begin + 1, solver ? -1 : 0);
-            produce_products(sm.buf[c_begin & 1]);
-            produce_token_scales(sm.buf[c_begin & 1]);
-            lds_barrier();
-            if (!solver && c_begin + 1 < c_end) fetch(c_begin + 1, 1);
-            produce_inverse(sm.buf[c_begin & 1]);
-            lds_barrier();
+        if (n_chunks > 0) fetch(c_begin, -1);
+        for (int i = 0; i < n_chunks; ++i) {
+            const int chunk = c_begin + i;
+            Buf& B = sm.buf[chunk & 1];
+            if (i >= 2) wait_count(&sm.sync.done[chunk & 1], K::NCW * (i / 2), broken);
+            produce_decay(B, chunk, i > 0 ? &sm.buf[(chunk & 1) ^ 1] : nullptr);
+            signal_count(&sm.sync.p1);
+            wait_count(&sm.sync.p1, NPW * (i + 1), broken);
+            // The inputs of the next chunk are requested outside the decay phase: k and
+            // log_alpha (used first) here, q, v and beta before phase 3, except on the waves
+            // that solve the diagonal blocks in phase 3, which request all here.
+            if (chunk + 1 < c_end) fetch(chunk + 1, solver ? -1 : 0);
+            produce_products(B);
+            produce_token_scales(B);
+            signal_count(&sm.sync.p2);
+            wait_count(&sm.sync.p2, NPW * (i + 1), broken);
+            if (!solver && chunk + 1 < c_end) fetch(chunk + 1, 1);
+            produce_inverse(B);
+            signal_count(&sm.sync.ready);
         }
-        for (int chunk = c_begin; chunk < c_end; ++chunk) {
-            Buf& cur = sm.buf[chunk & 1];
-            Buf& nxt = sm.buf[(chunk & 1) ^ 1];
-            const bool more = chunk + 1 < c_end;
-            if (more) {
-                produce_decay(nxt, chunk + 1, &cur);
-            } else if (tg == 0) {
+        if (n_chunks > 0) {
+            // rho of the last chunk (no next midpoint): e^{b_n - b_m}, which leaves S itself
+            if (tg == 0) {
 #pragma unroll
-                for (int ch = 0; ch < 4; ++ch) cur.rho[c4 + ch] = enm[ch];
+                for (int ch = 0; ch < 4; ++ch) sm.buf[(c_end - 1) & 1].rho[c4 + ch] = enm[ch];
             }
-            lds_barrier();
-            // The inputs of chunk c+2 are requested outside the decay phase that bounds interval 1:
-            // k and log_alpha (used first) here, q, v and beta at the start of interval 3, except
-            // on the wave that solves the diagonal blocks in interval 3, which requests all here.
-            if (chunk + 2 < c_end) fetch(chunk + 2, solver ? -1 : 0);
-            if (more) {
-                produce_products(nxt);
-                produce_token_scales(nxt);
-            }
-            lds_barrier();
-            if (!solver && chunk + 2 < c_end) fetch(chunk + 2, 1);
-            if (more) produce_inverse(nxt);
-            lds_barrier();
+            signal_count(&sm.sync.p1);
         }
         return;
     }
-    if (c_begin < c_end) {
-        lds_barrier();
-        consume_ptiles(sm.buf[c_begin & 1]);
-        lds_barrier();
-        lds_barrier();
+    if (n_chunks > 0) {
+        wait_count(&sm.sync.ready, NPW, broken);
         const Buf& first = sm.buf[c_begin & 1];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -1595,16 +1636,16 @@ void pipe_kernel(KernelArgs a) {
         }
         split_state();
     }
-    for (int chunk = c_begin; chunk < c_end; ++chunk) {
+    for (int i = 0; i < n_chunks; ++i) {
+        const int chunk = c_begin + i;
         const Buf& cur = sm.buf[chunk & 1];
+        if (i > 0) wait_count(&sm.sync.ready, NPW * (i + 1), broken);
         consume_project(cur, chunk);
-        lds_barrier();
         consume_solve(cur);
-        if (chunk + 1 < c_end) consume_ptiles(sm.buf[(chunk & 1) ^ 1]);
-        lds_barrier();
+        wait_count(&sm.sync.p1, NPW * (i + 2), broken);
         consume_update(cur, chunk);
-        if (chunk + 1 < c_end) split_state();
-        lds_barrier();
+        signal_count(&sm.sync.done[chunk & 1]);
+        if (i + 1 < n_chunks) split_state();
     }
 
     // ---------------------------------------------------------------- exit state
@@ -1615,13 +1656,14 @@ void pipe_kernel(KernelArgs a) {
         dst = (is_phi ? a.phi : a.sloc) + (static_cast<size_t>(s) * a.NH + unit) * D * D;
     }
     if (dst) {
+        const bool poison = __builtin_amdgcn_readfirstlane(lds_read(broken)) != 0;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    dst[(16 * rt + 4 * g4 + e) * D + j0 + 16 * ct + lr] = S[rt][ct][e];
+                    dst[(16 * rt + 4 * g4 + e) * D + j0 + 16 * ct + lr] = poison ? __builtin_nanf("") : S[rt][ct][e];
     }
 }
 
