@@ -24,9 +24,10 @@
 //   db = Q' dQ' + K' dK' - K'' dK'' (+ rowsum(dS_next S_next) on the last row)
 //   dlog_alpha = reverse cumulative sum of db over the chunk's rows.
 //
-// Kernels (all products on the fp32 matrix cores, v_mfma_f32_16x16x4_f32, operands
-// from LDS; the state passes also keep R = V - K' S_m and dE of every chunk, which the
-// gradient step reads instead of recomputing):
+// Kernels (operands from LDS; products on the fp32 matrix cores for fp32 inputs, and as
+// split-bf16 products on the bf16 matrix cores for bf16 inputs, whose tolerance is wider;
+// the state passes also keep R = V - K' S_m and dE of every chunk, which the gradient step
+// reads instead of recomputing):
 //   seq_scan_kernel   packed batches: first chunk index of every sequence
 //   prep_kernel       per (chunk, head): Q', K', K'', M, P, L, e_m, e_n, beta, b - m -> record
 //   state_fwd_kernel  per (sequence, head, 16 value columns): every chunk's entry state
@@ -117,35 +118,84 @@ __device__ bool chunk_pos(const BackwardArgs& a, int j, ChunkPos& p) {
 // ---------------------------------------------------------------- matrix-core helpers
 __device__ __forceinline__ f4 zero4() { return f4{0.f, 0.f, 0.f, 0.f}; }
 
-// acc (16 x 16) += A (16 x K) B (K x 16), A(i, k) = A[i*ai + k*ak], B(k, j) = B[k*bk + j*bj].
-// Lane l supplies A(l % 16, k0 + l / 16) and B(k0 + l / 16, l % 16) for each 4-deep step
-// and holds C(4 (l / 16) + v, l % 16) in acc[v].
-// The operands of all steps are requested before the MFMAs so the reads can overlap.
-// The 4-deep steps may be dealt round-robin to NACC independent accumulators (summed at
-// the end); a dependent fp32 MFMA issues 52 cycles after its predecessor, an
-// independent one every 32.
-template <int K, int NACC = 1>
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// A 32-bit constant in a scalar register: the bf16 pairs (-1, 0) and (0, -1) below must not
+// become inline constants, which name a 32-bit float.
+__device__ __forceinline__ uint32_t sreg_const(uint32_t v) {
+    uint32_t r;
+    asm("s_mov_b32 %0, %1" : "=s"(r) : "i"(v));
+    return r;
+}
+
+// Two fp32 values -> packed bf16 hi = bf16(x) and lo = bf16(x - hi); x - hi is exact and
+// v_dot2_f32_bf16 forms it in one instruction as hi . (-e_i) + x_i.
+__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+    const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
+    const bf16x2 hb = __builtin_bit_cast(bf16x2, h);
+    const float r0 = __builtin_amdgcn_fdot2_f32_bf16(hb, __builtin_bit_cast(bf16x2, sreg_const(0x0000bf80u)), x0, false);
+    const float r1 = __builtin_amdgcn_fdot2_f32_bf16(hb, __builtin_bit_cast(bf16x2, sreg_const(0xbf800000u)), x1, false);
+    hi = h;
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
+}
+
+// Eight fp32 values -> hi and lo bf16x8 operands.
+__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) split_pair(x[2 * p], x[2 * p + 1], h[p], l[p]);
+    hi = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+    lo = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
+}
+
+// acc (16 x 16) += A (16 x K) B (K x 16), A(i, k) = A[i*ai + k*ak], B(k, j) = B[k*bk + j*bj],
+// K a multiple of 32.  Lane l holds C(4 (l / 16) + v, l % 16) in acc[v]; the operands of all
+// steps are requested before the products so the reads overlap.
+//  * SPLIT = false: fp32 matrix cores (v_mfma_f32_16x16x4_f32); lane l supplies A(l % 16,
+//    k0 + l / 16) and B(k0 + l / 16, l % 16) for each 4-deep step.
+//  * SPLIT = true: bf16 matrix cores.  Every fp32 operand is split into hi + lo bf16 and each
+//    32-deep step issues hi.hi + hi.lo + lo.hi (v_mfma_f32_16x16x32_bf16, fp32 accumulation):
+//    about 16 mantissa bits of each operand (relative error near 2^-16 per product) at 3/16 of
+//    the fp32 matrix-core time.  Lane l supplies A(l % 16, k0 + 8 (l / 16) + j) and
+//    B(k0 + 8 (l / 16) + j, l % 16), j = 0..7.
+template <int K, bool SPLIT>
 __device__ __forceinline__ void mma(f4& acc, const float* A, int ai, int ak, const float* B, int bk, int bj) {
-    static_assert((K / 4) % NACC == 0, "");
+    static_assert(K % 32 == 0, "");
     const int lane = threadIdx.x & 63, i = lane & 15, kq = lane >> 4;
-    const float* pa = A + i * ai + kq * ak;
-    const float* pb = B + kq * bk + i * bj;
     float a[K / 4], b[K / 4];
+    if constexpr (SPLIT) {
+        const float* pa = A + i * ai + 8 * kq * ak;
+        const float* pb = B + 8 * kq * bk + i * bj;
 #pragma unroll
-    for (int s = 0; s < K / 4; ++s) {
-        a[s] = pa[4 * s * ak];
-        b[s] = pb[4 * s * bk];
+        for (int s = 0; s < K / 32; ++s)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                a[8 * s + j] = pa[(32 * s + j) * ak];
+                b[8 * s + j] = pb[(32 * s + j) * bk];
+            }
+#pragma unroll
+        for (int s = 0; s < K / 32; ++s) {
+            bf16x8 ah, al, bh, bl;
+            split8(a + 8 * s, ah, al);
+            split8(b + 8 * s, bh, bl);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+        }
+    } else {
+        const float* pa = A + i * ai + kq * ak;
+        const float* pb = B + kq * bk + i * bj;
+#pragma unroll
+        for (int s = 0; s < K / 4; ++s) {
+            a[s] = pa[4 * s * ak];
+            b[s] = pb[4 * s * bk];
+        }
+#pragma unroll
+        for (int s = 0; s < K / 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
     }
-    f4 part[NACC];
-    part[0] = acc;
-#pragma unroll
-    for (int c = 1; c < NACC; ++c) part[c] = zero4();
-#pragma unroll
-    for (int s = 0; s < K / 4; ++s)
-        part[s % NACC] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], part[s % NACC], 0, 0, 0);
-#pragma unroll
-    for (int c = 1; c < NACC; ++c) part[0] += part[c];
-    acc = part[0];
 }
 
 __device__ __forceinline__ int acc_row(int v) { return 4 * ((threadIdx.x & 63) >> 4) + v; }
@@ -294,6 +344,7 @@ __global__ __launch_bounds__(BT) void seq_scan_kernel(const int32_t* cu, int N, 
 
 template <int D, class IN, bool SG>
 __global__ __launch_bounds__(BT) void prep_kernel(BackwardArgs a) {
+    constexpr bool SPLIT = std::is_same<IN, BF16>::value;   // split-bf16 products for bf16 inputs
     constexpr int LD = D + 4, LC = BC + 4;
     __shared__ __attribute__((aligned(16))) float sQ[BC * LD], sK[BC * LD], sKpp[BC * LD], sG[BC * LD];
     __shared__ __attribute__((aligned(16))) float sL[BC * LC], sP[BC * LC];
@@ -351,7 +402,7 @@ __global__ __launch_bounds__(BT) void prep_kernel(BackwardArgs a) {
         const bool isP = t >= 3;
         const int tt = t % 3, ti = tt == 0 ? 0 : 1, tj = tt == 2 ? 1 : 0;
         f4 acc = zero4();
-        mma<D>(acc, (isP ? sQ : sK) + 16 * ti * LD, LD, 1, sKpp + 16 * tj * LD, 1, LD);
+        mma<D, SPLIT>(acc, (isP ? sQ : sK) + 16 * ti * LD, LD, 1, sKpp + 16 * tj * LD, 1, LD);
         float* out = isP ? sP : sL;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
@@ -396,6 +447,7 @@ __global__ __launch_bounds__(BT) void prep_kernel(BackwardArgs a) {
 
 template <int D, class IN>
 __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
+    constexpr bool SPLIT = std::is_same<IN, BF16>::value;   // split-bf16 products for bf16 inputs
     constexpr int LD = D + 4, LC = BC + 4, LT = TW + 4, NTILE = D / TW;
     __shared__ __attribute__((aligned(16))) float sKp[BC * LD], sKpp[BC * LD], sM[BC * LC];
     __shared__ __attribute__((aligned(16))) float sS[D * LT], sR[2 * BC * LT], sE[BC * LT], sV[BC * LT];
@@ -448,7 +500,7 @@ __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
         {   // K' S_m, the key-channel sum split in two halves over the waves
             const int rt = w & 1, kh = w >> 1;
             f4 acc = zero4();
-            mma<D / 2>(acc, sKp + 16 * rt * LD + kh * (D / 2), LD, 1, sS + kh * (D / 2) * LT, LT, 1);
+            mma<D / 2, SPLIT>(acc, sKp + 16 * rt * LD + kh * (D / 2), LD, 1, sS + kh * (D / 2) * LT, LT, 1);
 #pragma unroll
             for (int v = 0; v < 4; ++v) sR[kh * BC * LT + (16 * rt + acc_row(v)) * LT + acc_col()] = acc[v];
         }
@@ -463,7 +515,7 @@ __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
         lds_barrier();
         if (w < 2) {   // E = M Y
             f4 acc = zero4();
-            mma<BC>(acc, sM + 16 * w * LC, LC, 1, sR, LT, 1);
+            mma<BC, SPLIT>(acc, sM + 16 * w * LC, LC, 1, sR, LT, 1);
 #pragma unroll
             for (int v = 0; v < 4; ++v) sE[(16 * w + acc_row(v)) * LT + acc_col()] = acc[v];
         }
@@ -472,7 +524,7 @@ __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
             f4 acc;
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[v] = sS[(16 * rt + acc_row(v)) * LT + acc_col()];
-            mma<BC>(acc, sKpp + 16 * rt, 1, LD, sE, LT, 1);
+            mma<BC, SPLIT>(acc, sKpp + 16 * rt, 1, LD, sE, LT, 1);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int r = 16 * rt + acc_row(v);
@@ -490,6 +542,7 @@ __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
 
 template <int D, class IN>
 __global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
+    constexpr bool SPLIT = std::is_same<IN, BF16>::value;   // split-bf16 products for bf16 inputs
     constexpr int LD = D + 4, LC = BC + 4, LT = TW + 4, NTILE = D / TW;
     __shared__ __attribute__((aligned(16))) float sQp[BC * LD], sKp[BC * LD], sKpp[BC * LD];
     __shared__ __attribute__((aligned(16))) float sM[BC * LC], sP[BC * LC];
@@ -549,8 +602,8 @@ __global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
             // (the second half's partial goes to sV, which holds -dV only later)
             const int rt = w & 1, kh = w >> 1;
             f4 acc = zero4();
-            mma<D / 2>(acc, sKpp + 16 * rt * LD + kh * (D / 2), LD, 1, sS + kh * (D / 2) * LT, LT, 1);
-            if (kh == 0) mma<BC>(acc, sP + 16 * rt, 1, LC, sO, LT, 1);
+            mma<D / 2, SPLIT>(acc, sKpp + 16 * rt * LD + kh * (D / 2), LD, 1, sS + kh * (D / 2) * LT, LT, 1);
+            if (kh == 0) mma<BC, SPLIT>(acc, sP + 16 * rt, 1, LC, sO, LT, 1);
             float* part = kh == 0 ? sR : sV;
 #pragma unroll
             for (int v = 0; v < 4; ++v) part[(16 * rt + acc_row(v)) * LT + acc_col()] = acc[v];
@@ -566,7 +619,7 @@ __global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
         lds_barrier();
         if (w < 2) {   // -dV = -Diag(beta) M^T dE
             f4 acc = zero4();
-            mma<BC>(acc, sM + 16 * w, 1, LC, sR, LT, 1);
+            mma<BC, SPLIT>(acc, sM + 16 * w, 1, LC, sR, LT, 1);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int r = 16 * w + acc_row(v);
@@ -578,8 +631,8 @@ __global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
             f4 acc;
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[v] = sS[(16 * rt + acc_row(v)) * LT + acc_col()];
-            mma<BC>(acc, sQp + 16 * rt, 1, LD, sO, LT, 1);
-            mma<BC>(acc, sKp + 16 * rt, 1, LD, sV, LT, 1);
+            mma<BC, SPLIT>(acc, sQp + 16 * rt, 1, LD, sO, LT, 1);
+            mma<BC, SPLIT>(acc, sKp + 16 * rt, 1, LD, sV, LT, 1);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int r = 16 * rt + acc_row(v);
@@ -599,6 +652,7 @@ __global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
 
 template <int D, class IN, bool OB, bool SG>
 __global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
+    constexpr bool SPLIT = std::is_same<IN, BF16>::value;   // split-bf16 products for bf16 inputs
     constexpr int LD = D + 4, LC = BC + 4, LT = GW + 4, NCT = D / GW;
     constexpr int CT_PER_WAVE = D / 16 / 4;   // 16-column tiles of D owned by each wave
     static_assert(LT == LC, "the C x C products reuse C x GW buffers");
@@ -703,9 +757,9 @@ __global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
         lds_barrier();
         {
             f4 e = zero4();     // E = M Y
-            mma<BC>(e, sM + 16 * trt * LC, LC, 1, sY + 16 * tct, LT, 1);
+            mma<BC, SPLIT>(e, sM + 16 * trt * LC, LC, 1, sY + 16 * tct, LT, 1);
             f4 y = zero4();     // dY = M^T dE
-            mma<BC>(y, sM + 16 * trt, 1, LC, sdE + 16 * tct, LT, 1);
+            mma<BC, SPLIT>(y, sM + 16 * trt, 1, LC, sdE + 16 * tct, LT, 1);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int r = 16 * trt + acc_row(v), c = 16 * tct + acc_col();
@@ -727,13 +781,13 @@ __global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
 #pragma unroll
             for (int q = 0; q < CT_PER_WAVE; ++q) {
                 const int dt = w * CT_PER_WAVE + q;   // 16-column tile of D
-                mma<GW>(dQp[rt][q], sO + 16 * rt * LT, LT, 1, sSm + 16 * dt * LT, 1, LT);
-                mma<GW>(dKp[rt][q], smdV + 16 * rt * LT, LT, 1, sSm + 16 * dt * LT, 1, LT);
-                mma<GW>(dKpp[rt][q], sE + 16 * rt * LT, LT, 1, sdSn + 16 * dt * LT, 1, LT);
+                mma<GW, SPLIT>(dQp[rt][q], sO + 16 * rt * LT, LT, 1, sSm + 16 * dt * LT, 1, LT);
+                mma<GW, SPLIT>(dKp[rt][q], smdV + 16 * rt * LT, LT, 1, sSm + 16 * dt * LT, 1, LT);
+                mma<GW, SPLIT>(dKpp[rt][q], sE + 16 * rt * LT, LT, 1, sdSn + 16 * dt * LT, 1, LT);
             }
         // dP (+)= dO E^T, dY E^T on this wave's C x C tile
-        mma<GW>(dPacc, sO + 16 * trt * LT, LT, 1, sE + 16 * tct * LT, 1, LT);
-        mma<GW>(dYE, sdY + 16 * trt * LT, LT, 1, sE + 16 * tct * LT, 1, LT);
+        mma<GW, SPLIT>(dPacc, sO + 16 * trt * LT, LT, 1, sE + 16 * tct * LT, 1, LT);
+        mma<GW, SPLIT>(dYE, sdY + 16 * trt * LT, LT, 1, sE + 16 * tct * LT, 1, LT);
     }
     lds_barrier();
     // dP = Tril(dO E^T) -> sdE;  dA = -StrictTril(dY E^T) -> sdY  (both C x C, row stride LC)
@@ -764,10 +818,10 @@ __global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
 #pragma unroll
         for (int q = 0; q < CT_PER_WAVE; ++q) {
             const int dt = w * CT_PER_WAVE + q;
-            mma<BC>(dQp[rt][q], sdE + 16 * rt * LC, LC, 1, sKpp + 16 * dt, LD, 1);   // + dP K''
-            mma<BC>(dKp[rt][q], sdY + 16 * rt * LC, LC, 1, sKpp + 16 * dt, LD, 1);   // + dL K''
-            mma<BC>(dKpp[rt][q], sdE + 16 * rt, 1, LC, sQp + 16 * dt, LD, 1);        // + dP^T Q'
-            mma<BC>(dKpp[rt][q], sdY + 16 * rt, 1, LC, sKp + 16 * dt, LD, 1);        // + dL^T K'
+            mma<BC, SPLIT>(dQp[rt][q], sdE + 16 * rt * LC, LC, 1, sKpp + 16 * dt, LD, 1);   // + dP K''
+            mma<BC, SPLIT>(dKp[rt][q], sdY + 16 * rt * LC, LC, 1, sKpp + 16 * dt, LD, 1);   // + dL K''
+            mma<BC, SPLIT>(dKpp[rt][q], sdE + 16 * rt, 1, LC, sQp + 16 * dt, LD, 1);        // + dP^T Q'
+            mma<BC, SPLIT>(dKpp[rt][q], sdY + 16 * rt, 1, LC, sKp + 16 * dt, LD, 1);        // + dL^T K'
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int r = 16 * rt + acc_row(v), c = 16 * dt + acc_col();
