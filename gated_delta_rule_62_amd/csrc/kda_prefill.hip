@@ -173,6 +173,7 @@ __device__ __forceinline__ void lds_barrier() {
 // workgroup.
 struct SyncCounters {
     int p1, p2, ready;   // producer waves done with phase 1, phase 2, a whole chunk
+    int pt;              // consumer waves done with the P tiles of the chunk being built
     int done[2];         // consumer waves done with a chunk, per LDS buffer
     int broken;
 };
@@ -190,14 +191,17 @@ __device__ __forceinline__ int lds_read(const int* p) { return *(const lds_vint*
 
 __device__ __forceinline__ void wait_count(const int* c, int target, int* broken) {
     for (int polls = 0;; ++polls) {
-        const int v = __builtin_amdgcn_readfirstlane(lds_read(c));
-        const int b = __builtin_amdgcn_readfirstlane(lds_read(broken));
-        if (v >= target || b) break;
-        if (polls >= (1 << 16)) {
-            *(lds_vint*)(broken) = 1;
-            break;
+        if (__builtin_amdgcn_readfirstlane(lds_read(c)) >= target) break;
+        // the first polls follow each other closely; later ones sleep between reads and
+        // look at the broken flag every 64 polls
+        if (polls >= 8) {
+            if ((polls & 63) == 0 && __builtin_amdgcn_readfirstlane(lds_read(broken))) break;
+            if (polls >= (1 << 16)) {
+                *(lds_vint*)(broken) = 1;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
         }
-        __builtin_amdgcn_s_sleep(1);
     }
     asm volatile("" ::: "memory");
 }
@@ -968,7 +972,7 @@ void pipe_kernel(KernelArgs a) {
             sm.buf[b].p[r / (C * C)][r % (C * C)] = 0;
         }
     }
-    if (tid == 0) sm.sync = SyncCounters{0, 0, 0, {0, 0}, 0};
+    if (tid == 0) sm.sync = SyncCounters{0, 0, 0, 0, {0, 0}, 0};
     lds_barrier();
     int* const broken = &sm.sync.broken;
 
@@ -1205,41 +1209,9 @@ void pipe_kernel(KernelArgs a) {
         rt = job == 1 ? 0 : 1;
         ct = job == 2 ? 1 : 0;
     };
-    // phase 2, output pass: the P tile `job` of the chunk being built
-    auto produce_ptile = [&](Buf& B, int job) {
-        if constexpr (MODE == 0) {
-            int rt, ct;
-            tile_of(job, rt, ct);
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int ao = K::tok(16 * ct + lr, 32 * ks + 8 * g4);
-                const int bo = K::tok(16 * rt + lr, 32 * ks + 8 * g4);
-                if constexpr (EXACT)
-                    acc = mfma(frag(&B.kb[0][ao]), frag(&B.qb[0][bo]), acc);
-                else if constexpr (SG)
-                    acc = mfma3(frag(&B.kb[0][ao]), frag(&B.kb[1][ao]), frag(&B.qb[0][bo]), frag(&B.qb[1][bo]), acc);
-                else
-                    acc = mfma3(frag(&B.kt[0][ao]), frag(&B.kt[1][ao]), frag(&B.qb[0][bo]), frag(&B.qb[1][bo]), acc);
-            }
-            f32x4 pv4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) pv4[e] = (rt > ct || 4 * g4 + e <= lr) ? acc[e] : 0.f;
-            uint2 hi, lo;
-            split_quad(pv4[0], pv4[1], pv4[2], pv4[3], hi, lo);
-            const int idx = K::chm(16 * rt + lr, 8 * g4 + 4 * ct);   // kperm(16 ct + 4 g4 + e) = 8 g4 + 4 ct + e
-            *reinterpret_cast<uint2*>(&B.p[0][idx]) = hi;
-            *reinterpret_cast<uint2*>(&B.p[1][idx]) = lo;
-        }
-    };
-    // phase 2 (producer): the three A tiles, then in the output pass the three P tiles
+    // phase 2 (producer): the three A tiles
     auto produce_products = [&](Buf& B) {
-        constexpr int NJ = MODE == 0 ? 6 : 3;
-        for (int job = w; job < NJ; job += NPW) {
-            if (job >= 3) {
-                produce_ptile(B, job - 3);
-                continue;
-            }
+        for (int job = w; job < 3; job += NPW) {
             int rt, ct;
             tile_of(job, rt, ct);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -1285,9 +1257,39 @@ void pipe_kernel(KernelArgs a) {
             }
         }
     };
+    // consumers, output pass: the three P tiles of the chunk the producers are building, once
+    // its planes are written (phase 1) and before phase 3 turns Ktil_m into Ktil_m^T
+    auto consume_ptiles = [&](Buf& B) {
+        if constexpr (MODE == 0) {
+            for (int job = ci; job < 3; job += K::NCW) {
+                int rt, ct;
+                tile_of(job, rt, ct);
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int ao = K::tok(16 * ct + lr, 32 * ks + 8 * g4);
+                    const int bo = K::tok(16 * rt + lr, 32 * ks + 8 * g4);
+                    if constexpr (EXACT)
+                        acc = mfma(frag(&B.kb[0][ao]), frag(&B.qb[0][bo]), acc);
+                    else if constexpr (SG)
+                        acc = mfma3(frag(&B.kb[0][ao]), frag(&B.kb[1][ao]), frag(&B.qb[0][bo]), frag(&B.qb[1][bo]), acc);
+                    else
+                        acc = mfma3(frag(&B.kt[0][ao]), frag(&B.kt[1][ao]), frag(&B.qb[0][bo]), frag(&B.qb[1][bo]), acc);
+                }
+                f32x4 pv4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pv4[e] = (rt > ct || 4 * g4 + e <= lr) ? acc[e] : 0.f;
+                uint2 hi, lo;
+                split_quad(pv4[0], pv4[1], pv4[2], pv4[3], hi, lo);
+                const int idx = K::chm(16 * rt + lr, 8 * g4 + 4 * ct);   // kperm(16 ct + 4 g4 + e) = 8 g4 + 4 ct + e
+                *reinterpret_cast<uint2*>(&B.p[0][idx]) = hi;
+                *reinterpret_cast<uint2*>(&B.p[1][idx]) = lo;
+            }
+        }
+    };
     // phase 3: Ktil_m^T over Ktil_m (read by the products), regrouped from the split words
-    // of phase 1, and X_bb = (I + A_bb)^{-1}
-    auto produce_inverse = [&](Buf& B) {
+    // of phase 1
+    auto produce_transpose = [&](Buf& B) {
 #pragma unroll
         for (int ch = 0; ch < 4; ++ch) {
             const int c = c4 + ch;
@@ -1310,6 +1312,9 @@ void pipe_kernel(KernelArgs a) {
                 if constexpr (!EXACT) *reinterpret_cast<uint2*>(&B.kt[1][idx]) = lo;
             }
         }
+    };
+    // phase 3: X_bb = (I + A_bb)^{-1} on the two solver waves
+    auto produce_inverse = [&](Buf& B) {
         if (solver) {
             // Block blk: lane (i, jg) = (l / 4, l % 4) solves columns 4 jg .. 4 jg + 3 of row i
             // of X_bb = (I + A_bb)^{-1} (x^T (I + A) = e_i^T).
@@ -1585,14 +1590,14 @@ void pipe_kernel(KernelArgs a) {
 
     // ================================================================ chunk loops
     // Producer and consumer waves run separate loops, ordered by the LDS counters alone (no
-    // workgroup barrier).  The producers build chunk i in three phases, each closed by a
-    // count that the other producers wait for: phase 1 (decay, planes, and the previous
-    // chunk's rho), phase 2 (A and P tiles), phase 3 (Ktil_m^T, diagonal inverses; closes
-    // `ready`).  Before phase 1 of chunk i they wait until every consumer is done with chunk
-    // i - 2, the last user of the same buffer.  A consumer runs chunk i once it is `ready`,
-    // and waits for the producers' phase 1 of chunk i + 1 (which writes chunk i's rho) before
-    // the state update.  So the producers run up to one chunk ahead, and a chunk costs the
-    // longer of the two sides, not the sum of the longer side of every phase.
+    // workgroup barrier).  The producers build chunk i in three phases, each closed by a count
+    // that the other producers wait for: phase 1 (decay, planes, and the previous chunk's rho),
+    // phase 2 (A tiles), phase 3 (diagonal inverses, then Ktil_m^T over Ktil_m once the
+    // consumers have taken the P tiles from it; closes `ready`).  Before phase 1 of chunk i they
+    // wait until every consumer is done with chunk i - 2, the last user of the same buffer.  A
+    // consumer runs chunk i once it is `ready`; after its solve it waits for the producers'
+    // phase 1 of chunk i + 1, forms that chunk's P tiles (closing `pt`), and then runs the
+    // state update, which needs chunk i's rho from that same phase.
     const int n_chunks = c_end - c_begin;
     if (producer) {
         if (n_chunks > 0) fetch(c_begin, -1);
@@ -1613,6 +1618,8 @@ void pipe_kernel(KernelArgs a) {
             wait_count(&sm.sync.p2, NPW * (i + 1), broken);
             if (!solver && chunk + 1 < c_end) fetch(chunk + 1, 1);
             produce_inverse(B);
+            wait_count(&sm.sync.pt, K::NCW * (i + 1), broken);
+            produce_transpose(B);
             signal_count(&sm.sync.ready);
         }
         if (n_chunks > 0) {
@@ -1626,6 +1633,9 @@ void pipe_kernel(KernelArgs a) {
         return;
     }
     if (n_chunks > 0) {
+        wait_count(&sm.sync.p1, NPW, broken);
+        consume_ptiles(sm.buf[c_begin & 1]);
+        signal_count(&sm.sync.pt);
         wait_count(&sm.sync.ready, NPW, broken);
         const Buf& first = sm.buf[c_begin & 1];
 #pragma unroll
@@ -1643,6 +1653,10 @@ void pipe_kernel(KernelArgs a) {
         consume_project(cur, chunk);
         consume_solve(cur);
         wait_count(&sm.sync.p1, NPW * (i + 2), broken);
+        if (i + 1 < n_chunks) {
+            consume_ptiles(sm.buf[(chunk & 1) ^ 1]);
+            signal_count(&sm.sync.pt);
+        }
         consume_update(cur, chunk);
         signal_count(&sm.sync.done[chunk & 1]);
         if (i + 1 < n_chunks) split_state();
