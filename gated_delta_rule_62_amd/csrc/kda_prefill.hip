@@ -791,15 +791,15 @@ __device__ __forceinline__ void quad_lower_solve(float (&y)[4], const f32x4 (&co
 // ------------------------------------------------------------------ pipelined kernel (C = 32)
 // The operands of a chunk depend only on that chunk's inputs, never on the state, so
 // they are built one chunk ahead.  Producer waves (one per SIMD) build chunk c+1's
-// decayed operands, the C x C products and the diagonal-block inverses into one LDS
-// buffer while consumer waves run chunk c's state pass out of the other.  Both sides
-// meet at three workgroup barriers per chunk, and the work between two barriers is
-// paired so that one side's vector-ALU work runs beside the other side's MFMA work:
+// decayed operands, the A tiles and the diagonal-block inverses into one LDS buffer
+// while consumer waves run chunk c's state pass out of the other.  The two sides are
+// ordered by counters in LDS (signal_count / wait_count), so that one side's vector-ALU
+// work runs beside the other side's MFMA work without workgroup barriers:
 //
-//   interval   producer (chunk c+1)                 consumer (chunk c)
-//   1          decay prefix, decayed K/Q splits     Y = Kbar S, Z = Qbar S
-//   2          A tiles, next inputs requested       Unew block recurrence, O; P tiles of c+1
-//   3          Ktil_m^T, diagonal-block inverses    state update, O stores, state split
+//   step   producer (chunk c+1)                      consumer (chunk c)
+//   1      decay prefix, decayed K/Q splits, rho     Y = Kbar S, Z = Qbar S
+//   2      A tiles, next inputs requested            Unew block recurrence, O; P tiles of c+1
+//   3      diagonal-block inverses, Ktil_m^T         state update, O stores, state split
 // ------------------------------------------------------------------ fused prologue helpers
 constexpr int kFuseQK = 1, kFuseBeta = 2, kFuseDecay = 4;
 
