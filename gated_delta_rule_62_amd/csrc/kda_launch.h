@@ -25,6 +25,10 @@ inline bool chunk_supported(int c) { return c == 0 || c == 32 || c == 64; }
 //         carries the segment's transition matrix; a small combine kernel chains
 //         the segment entry states; pass 2 reruns every segment from its true
 //         entry state and writes o and S_final.
+//         With split0, segment 0 needs no summary: its output pass runs on a second
+//         stream beside pass 1 (which then covers segments 1..G-2) and leaves its exit
+//         state as segment 1's entry, so pass 2 covers segments 1..G-1.  Both passes then
+//         fill the chip with one segment more than the plain schedule.
 // Fused prologue / epilogue of the _fused entry points (flags as in kda_fusion).
 struct Fusion {
     int flags = 0;                     // 1: L2-normalise q, k; 2: beta logits; 4: log_alpha logits
@@ -37,6 +41,7 @@ struct PrefillPlan {
     int G = 1;
     int chunks = 0;        // chunks per sequence (equal-length case)
     int cps = 0;           // chunks per segment
+    bool split0 = false;   // segment 0's output pass runs beside pass 1 (G >= 3)
     size_t off_phi = 0, off_sloc = 0, off_se = 0, off_order = 0;
     size_t workspace_bytes = 0;
 };

@@ -45,6 +45,7 @@
 //    S_entry(s+1) = Phi(s) S_entry(s) + S_loc(s); pass 2 reruns every segment from
 //    its entry state.  That fills the chip at the cost of a second pass.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "kda_device.h"
@@ -325,6 +326,8 @@ struct KernelArgs {
     float* sloc;    // [G-1][N*H][D][D] segment end states from a zero entry
     float* se;      // [G-1][N*H][D][D] entry states of segments 1..G-1
     int T, H, NH, G, cps, chunks;
+    int seg0;       // segment of the launch's first workgroup row (equal-length batches)
+    int split0;     // 1: segment 0's output pass writes its exit state as segment 1's entry
     // fused prologue / epilogue (FUSE kernels only)
     int fuse_flags;           // kFuseQK | kFuseBeta | kFuseDecay
     float decay_bias, decay_scale;
@@ -365,7 +368,7 @@ void chunk_kernel(KernelArgs a) {
         c_end = static_cast<int>((t1 - t0 + C - 1) / C);
     } else {
         const int unit = blockIdx.x % a.NH;
-        s = blockIdx.x / a.NH;
+        s = a.seg0 + blockIdx.x / a.NH;
         n = unit / H;
         h = unit % H;
         t0 = static_cast<long>(n) * a.T;
@@ -946,7 +949,7 @@ void pipe_kernel(KernelArgs a) {
         c_end = static_cast<int>((t1 - t0 + C - 1) / C);
     } else {
         const int unit = blockIdx.x % a.NH;
-        s = blockIdx.x / a.NH;
+        s = a.seg0 + blockIdx.x / a.NH;
         n = unit / H;
         h = unit % H;
         t0 = static_cast<long>(n) * a.T;
@@ -1666,6 +1669,7 @@ void pipe_kernel(KernelArgs a) {
     float* dst = nullptr;
     if constexpr (MODE == 0) {
         if ((a.cu || s == a.G - 1) && a.S_final) dst = a.S_final + ubase;
+        else if (!a.cu && s == 0 && a.split0) dst = a.se + ubase;   // segment 1's entry state
     } else {
         dst = (is_phi ? a.phi : a.sloc) + (static_cast<size_t>(s) * a.NH + unit) * D * D;
     }
@@ -1681,21 +1685,22 @@ void pipe_kernel(KernelArgs a) {
     }
 }
 
-// Entry states of segments 1..G-1:  S_e(s) = Phi(s-1) S_e(s-1) + S_loc(s-1), S_e(0) = S0.
-// One workgroup per (unit, 16-column slice); fp32 on the vector ALUs.
+// Entry states of segments s_first..G-1:  S_e(s) = Phi(s-1) S_e(s-1) + S_loc(s-1), starting from
+// S_e(s_first - 1) = init (S0, or segment 1's entry when segment 0 ran its output pass first;
+// null: zero).  One workgroup per (unit, 16-column slice); fp32 on the vector ALUs.
 template <int D>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ S0, const float* __restrict__ phi,
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ init, const float* __restrict__ phi,
                                                       const float* __restrict__ sloc, float* __restrict__ se,
-                                                      int NH, int G) {
+                                                      int NH, int G, int s_first) {
     constexpr int CPT = 16 * D / 256;   // columns per thread
     constexpr int TPR = 16 / CPT;       // threads per row
     __shared__ float cur[D][16];
     const int unit = blockIdx.x, c0 = blockIdx.y * 16, tid = threadIdx.x;
     const int r = tid / TPR, cc = (tid % TPR) * CPT;
     const size_t ub = static_cast<size_t>(unit) * D * D;
-    for (int j = 0; j < CPT; ++j) cur[r][cc + j] = S0 ? S0[ub + r * D + c0 + cc + j] : 0.f;
+    for (int j = 0; j < CPT; ++j) cur[r][cc + j] = init ? init[ub + r * D + c0 + cc + j] : 0.f;
     __syncthreads();
-    for (int s = 1; s < G; ++s) {
+    for (int s = s_first; s < G; ++s) {
         const size_t sb = (static_cast<size_t>(s - 1) * NH + unit) * D * D;
         float acc[CPT];
         for (int j = 0; j < CPT; ++j) acc[j] = sloc[sb + r * D + c0 + cc + j];
@@ -1727,6 +1732,44 @@ __global__ __launch_bounds__(256) void order_kernel(const int32_t* __restrict__ 
     order[rank] = i;
 }
 
+// A second stream per device (default priority) with two events, created on first use and
+// kept until the process ends: segment 0's output pass of the split schedule runs on it.
+struct SideStream {
+    std::mutex mu;
+    hipStream_t stream = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+
+hipError_t side_stream(SideStream*& out) {
+    constexpr int kMaxDevices = 64;
+    static SideStream side[kMaxDevices];
+    static std::mutex init_mu;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(init_mu);
+    SideStream& s = side[dev];
+    if (!s.stream) {
+        hipStream_t st = nullptr;
+        hipEvent_t f = nullptr, j = nullptr;
+        e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&f, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&j, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            if (j) (void)hipEventDestroy(j);
+            if (f) (void)hipEventDestroy(f);
+            if (st) (void)hipStreamDestroy(st);
+            return e;
+        }
+        s.fork = f;
+        s.join = j;
+        s.stream = st;
+    }
+    out = &s;
+    return hipSuccess;
+}
+
 template <int D, int C, typename IN, bool OB, bool SG = false, bool FUSE = false>
 hipError_t launch_variant(const PrefillArgs& pa, const PrefillPlan& plan, hipStream_t stream) {
     static_assert(!FUSE || (C == 32 && !SG), "the fused prologue runs on the pipelined 32-token KDA kernel");
@@ -1735,6 +1778,8 @@ hipError_t launch_variant(const PrefillArgs& pa, const PrefillPlan& plan, hipStr
     a.q = pa.q; a.k = pa.k; a.v = pa.v; a.g = pa.g; a.beta = pa.beta;
     a.S0 = pa.S0; a.cu = pa.cu; a.o = pa.o; a.S_final = pa.S_final;
     a.T = pa.T; a.H = pa.H; a.NH = pa.N * pa.H; a.G = plan.G; a.cps = plan.cps; a.chunks = plan.chunks;
+    a.seg0 = 0;
+    a.split0 = 0;
     a.fuse_flags = pa.fuse_flags; a.decay_bias = pa.decay_bias; a.decay_scale = pa.decay_scale;
     a.out_gate = pa.out_gate;
     char* ws = static_cast<char*>(pa.workspace);
@@ -1745,31 +1790,56 @@ hipError_t launch_variant(const PrefillArgs& pa, const PrefillPlan& plan, hipStr
     const int NH = a.NH;
     // The 32-token chunk runs the producer/consumer kernel; the 64-token chunk, whose
     // operands do not fit twice in LDS, the single-buffered one.
-    auto pass = [&](int mode, int grid) {
+    auto pass = [&](int mode, int grid, const KernelArgs& ka, hipStream_t st) {
         if constexpr (C == 32) {
             if (mode == 0)
-                hipLaunchKernelGGL((pipe_kernel<D, IN, OB, 0, SG, FUSE>), dim3(grid), dim3(PCfg<D, 0>::NT), 0, stream, a);
+                hipLaunchKernelGGL((pipe_kernel<D, IN, OB, 0, SG, FUSE>), dim3(grid), dim3(PCfg<D, 0>::NT), 0, st, ka);
             else
-                hipLaunchKernelGGL((pipe_kernel<D, IN, OB, 1, SG, FUSE>), dim3(grid), dim3(PCfg<D, 1>::NT), 0, stream, a);
+                hipLaunchKernelGGL((pipe_kernel<D, IN, OB, 1, SG, FUSE>), dim3(grid), dim3(PCfg<D, 1>::NT), 0, st, ka);
         } else {
             if (mode == 0)
-                hipLaunchKernelGGL((chunk_kernel<D, C, IN, OB, 0>), dim3(grid), dim3(Cfg<D, C, 0>::NT), 0, stream, a);
+                hipLaunchKernelGGL((chunk_kernel<D, C, IN, OB, 0>), dim3(grid), dim3(Cfg<D, C, 0>::NT), 0, st, ka);
             else
-                hipLaunchKernelGGL((chunk_kernel<D, C, IN, OB, 1>), dim3(grid), dim3(Cfg<D, C, 1>::NT), 0, stream, a);
+                hipLaunchKernelGGL((chunk_kernel<D, C, IN, OB, 1>), dim3(grid), dim3(Cfg<D, C, 1>::NT), 0, st, ka);
         }
     };
     if (pa.cu) {
         hipLaunchKernelGGL(order_kernel, dim3((pa.N + 255) / 256), dim3(256), 0, stream, pa.cu,
                            reinterpret_cast<int32_t*>(ws + plan.off_order), pa.N);
-        pass(0, NH);
+        pass(0, NH, a, stream);
         return hipGetLastError();
     }
-    if (plan.G > 1) {
-        pass(1, NH * (plan.G - 1));
-        hipLaunchKernelGGL(combine_kernel<D>, dim3(NH, D / 16), dim3(256), 0, stream, pa.S0, a.phi, a.sloc, a.se,
-                           NH, plan.G);
+    if (plan.G > 1 && plan.split0) {
+        SideStream* side = nullptr;
+        if (side_stream(side) == hipSuccess) {
+            // The fork / join events are shared by every call on this device: enqueue the
+            // schedule under the lock so that no other call records them in between.
+            std::lock_guard<std::mutex> lock(side->mu);
+            hipError_t e = hipEventRecord(side->fork, stream);
+            if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
+            if (e != hipSuccess) return e;
+            KernelArgs a0 = a;   // segment 0's output pass, exit state -> segment 1's entry
+            a0.split0 = 1;
+            pass(0, NH, a0, side->stream);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            if ((e = hipEventRecord(side->join, side->stream)) != hipSuccess) return e;
+            KernelArgs a1 = a;   // summaries of segments 1..G-2
+            a1.seg0 = 1;
+            if (plan.G > 2) pass(1, NH * (plan.G - 2), a1, stream);
+            if ((e = hipStreamWaitEvent(stream, side->join, 0)) != hipSuccess) return e;
+            if (plan.G > 2)
+                hipLaunchKernelGGL(combine_kernel<D>, dim3(NH, D / 16), dim3(256), 0, stream, a.se, a.phi, a.sloc,
+                                   a.se, NH, plan.G, 2);
+            pass(0, NH * (plan.G - 1), a1, stream);   // output passes of segments 1..G-1
+            return hipGetLastError();
+        }
     }
-    pass(0, NH * plan.G);
+    if (plan.G > 1) {
+        pass(1, NH * (plan.G - 1), a, stream);
+        hipLaunchKernelGGL(combine_kernel<D>, dim3(NH, D / 16), dim3(256), 0, stream, pa.S0, a.phi, a.sloc, a.se,
+                           NH, plan.G, 1);
+    }
+    pass(0, NH * plan.G, a, stream);
     return hipGetLastError();
 }
 
@@ -1792,13 +1862,25 @@ PrefillPlan plan_prefill(int B, int T, int H, int D, int N, bool varlen, int chu
     // workgroups that fill the chip: one per compute unit
     const long target = static_cast<long>(kComputeUnits);
     int G = 1;
+    bool split = false;
     if (units > 0 && units < target && p.chunks >= 2 * kMinChunksPerSegment) {
         G = static_cast<int>((target + units - 1) / units);
         G = std::min(G, p.chunks / kMinChunksPerSegment);
         G = std::max(G, 1);
+        // The pipelined kernel's split schedule: segment 0's output pass beside the summaries of
+        // segments 1..G-2, then the output passes of segments 1..G-1; each fills the chip with
+        // floor(target / units) segments, one more than the plain schedule's summary pass.
+        if (p.chunk == 32) {
+            const int gs = std::min(static_cast<int>(target / units) + 1, p.chunks / kMinChunksPerSegment);
+            if (gs >= 3) {
+                G = gs;
+                split = true;
+            }
+        }
     }
     p.cps = p.chunks > 0 ? (p.chunks + G - 1) / G : 0;
     p.G = p.cps > 0 ? (p.chunks + p.cps - 1) / p.cps : 1;
+    p.split0 = split && p.G >= 3;
     if (p.G > 1) {
         const size_t mat = static_cast<size_t>(units) * (p.G - 1) * D * D * sizeof(float);
         p.off_phi = 0;

@@ -48,10 +48,13 @@ def test_status_strings(lib):
 
 def test_workspace_query_plans(lib):
     q = kda.kda_chunk_fwd_workspace_bytes
-    # long context, 32 heads: 2048 chunks of 32 tokens or 1024 chunks of 64, cut into 8
-    # segments (one workgroup per compute unit) -> 3 matrices per unit and segment gap
-    assert q(1, 65536, 32, 128, 128, 1, False) == 3 * 32 * 7 * 128 * 128 * 4
+    # long context, 32 heads -> 3 matrices per unit and segment gap.  1024 chunks of 64 tokens
+    # are cut into 8 segments (one workgroup per compute unit in each pass); 2048 chunks of 32
+    # into 9, since segment 0's output pass runs beside the summaries of segments 1..7.
+    assert q(1, 65536, 32, 128, 128, 1, False) == 3 * 32 * 8 * 128 * 128 * 4
     assert q(1, 65536, 32, 128, 128, 1, False, chunk=64) == 3 * 32 * 7 * 128 * 128 * 4
+    # training shape, 64 units: 5 segments of 32-token chunks (summaries of 1..3 beside 0)
+    assert q(4, 4096, 16, 128, 128, 4, False) == 3 * 64 * 4 * 128 * 128 * 4
     # enough units to fill the chip: single pass, no workspace
     assert q(64, 4096, 32, 128, 128, 64, False) == 0
     # packed sequences: an int32 order table (rounded to 256 bytes)
