@@ -92,6 +92,12 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int nu
  * writes S_final.  Inputs must not overlap outputs.  The result does not depend
  * on the chunk size beyond rounding.  Equal-length batches (cu_seqlens NULL) with
  * T <= 4 are evaluated token by token, as kda_recurrent_fwd does.
+ * Streams: all work is ordered after what is already enqueued on `stream` and
+ * before what is enqueued on it after the call.  For few long sequences at chunk
+ * 32 part of it runs on a second stream that the library creates on the device
+ * on first use (default priority, kept until the process ends), joined back to
+ * `stream` by events; the enqueue is serialised by a lock, so calls from several
+ * host threads are safe.
  */
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
                          const void* beta, const float* S0, const int32_t* cu_seqlens,
