@@ -98,6 +98,18 @@ def test_segmented_two_pass_path(chunk):
     check(d, "segmented ragged", chunk=chunk)
 
 
+def test_segment_schedule_with_three_segments():
+    """128 units and 16 chunks of 32 tokens: the smallest split schedule (segment 0's output
+    pass beside the summary of segment 1, then the output passes of segments 1 and 2, with
+    a shorter last segment), and with 64-token chunks the plain two-segment schedule."""
+    kda = _kda()
+    assert kda.kda_chunk_fwd_workspace_bytes(2, 500, 64, 64, 64, 2, False, 32) == 3 * 128 * 2 * 64 * 64 * 4
+    assert kda.kda_chunk_fwd_workspace_bytes(2, 500, 64, 64, 64, 2, False, 64) == 3 * 128 * 1 * 64 * 64 * 4
+    d = inputs.make_prefill(W[1], seed=205, B=2, T=500, H=64, D=64, s0=True, mix=True)
+    check(d, "three segments", chunk=32)
+    check(d, "two segments, 64-token chunks", chunk=64)
+
+
 @pytest.mark.parametrize("chunk", CHUNKS)
 def test_varlen_packed_with_empty_sequences(chunk):
     d = inputs.make_prefill(W[4], seed=205, H=3, lengths=[70, 0, 1, 64, 200, 0, 129])
