@@ -19,6 +19,9 @@ struct BackwardArgs {
     float *prep = nullptr, *states = nullptr, *dstates = nullptr;
     float *rbuf = nullptr, *debuf = nullptr;  // per (chunk, head): R = V - K S and dE, C x Dv
     int32_t* seq_chunk0 = nullptr;
+    // Workspace slots are head-major, so the chunks of one (sequence, head) are adjacent:
+    // per-chunk data (records, dS_next, R, dE) at h * ncs + chunk, states at h * nss + slot.
+    int ncs = 0, nss = 0;
     int B, T, H, D, N;
     bool in_bf16, out_bf16;
     bool scalar_gate = false;                // log_alpha and dlog_alpha are [B, T, H]

@@ -78,6 +78,10 @@ __device__ __forceinline__ int chunk0(const BackwardArgs& a, int n) {
     return a.cu ? a.seq_chunk0[n] : n * ((a.T + BC - 1) / BC);
 }
 
+// Workspace slot of per-chunk data (record, dS_next, R, dE) and of a state, head-major.
+__device__ __forceinline__ size_t cslot(const BackwardArgs& a, int j, int h) { return (size_t)h * a.ncs + j; }
+__device__ __forceinline__ size_t sslot(const BackwardArgs& a, size_t j, int h) { return (size_t)h * a.nss + j; }
+
 __device__ __forceinline__ int seq_first_token(const BackwardArgs& a, int n) {
     return a.cu ? a.cu[n] : n * a.T;
 }
@@ -417,7 +421,7 @@ __global__ __launch_bounds__(BT) void prep_kernel(BackwardArgs a) {
     }
     __syncthreads();
 
-    float* rec = a.prep + ((size_t)j * a.H + h) * Rec<D>::SIZE;
+    float* rec = a.prep + cslot(a, j, h) * Rec<D>::SIZE;
     if (tid < BC) {
         // M = (I + Diag(beta) L)^-1 by forward substitution; lane tid owns column tid
         float col[BC];
@@ -464,7 +468,7 @@ __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
     StageRows<IN, TW> rV;
     float rEm = 0.f, rEn = 0.f, rB = 0.f;
     auto fetch = [&](int i) __attribute__((always_inline)) {
-        const float* rec = a.prep + ((size_t)(c0 + i) * a.H + h) * Rec<D>::SIZE;
+        const float* rec = a.prep + cslot(a, c0 + i, h) * Rec<D>::SIZE;
         rKp.load(rec + Rec<D>::KP, D);
         rKpp.load(rec + Rec<D>::KPP, D);
         rM.load(rec + Rec<D>::M, BC);
@@ -488,7 +492,7 @@ __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
         if (i + 1 < nch) fetch(i + 1);
         lds_barrier();
         // keep the entry state, then scale it to S_m
-        float* slot = a.states + ((size_t)(c0 + n + i) * a.H + h) * DD + jt * TW;
+        float* slot = a.states + sslot(a, c0 + n + i, h) * DD + jt * TW;
         for (int e = tid; e < D * TW / 4; e += BT) {
             const int r = e / (TW / 4), c = 4 * (e % (TW / 4));
             const v4f x = *reinterpret_cast<const v4f*>(sS + r * LT + c);
@@ -505,7 +509,7 @@ __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
             for (int v = 0; v < 4; ++v) sR[kh * BC * LT + (16 * rt + acc_row(v)) * LT + acc_col()] = acc[v];
         }
         lds_barrier();
-        float* rout = a.rbuf + ((size_t)(c0 + i) * a.H + h) * BC * D + jt * TW;
+        float* rout = a.rbuf + cslot(a, c0 + i, h) * BC * D + jt * TW;
         for (int e = tid; e < BC * TW; e += BT) {   // R = V - K' S_m (kept for the gradient step), Y = Diag(beta) R
             const int r = e / TW, c = e % TW;
             const float rr = sV[r * LT + c] - sR[r * LT + c] - sR[BC * LT + r * LT + c];
@@ -533,7 +537,7 @@ __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
         }
     }
     __syncthreads();
-    float* slot = a.states + ((size_t)(c0 + n + nch) * a.H + h) * DD + jt * TW;
+    float* slot = a.states + sslot(a, c0 + n + nch, h) * DD + jt * TW;
     for (int e = tid; e < D * TW / 4; e += BT) {
         const int r = e / (TW / 4), c = 4 * (e % (TW / 4));
         *reinterpret_cast<v4f*>(slot + (size_t)r * D + c) = *reinterpret_cast<const v4f*>(sS + r * LT + c);
@@ -560,7 +564,7 @@ __global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
     StageRows<IN, TW> rO;
     float rEm = 0.f, rEn = 0.f, rB = 0.f;
     auto fetch = [&](int i) __attribute__((always_inline)) {
-        const float* rec = a.prep + ((size_t)(c0 + i) * a.H + h) * Rec<D>::SIZE;
+        const float* rec = a.prep + cslot(a, c0 + i, h) * Rec<D>::SIZE;
         rQp.load(rec + Rec<D>::QP, D);
         rKp.load(rec + Rec<D>::KP, D);
         rKpp.load(rec + Rec<D>::KPP, D);
@@ -589,7 +593,7 @@ __global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
         if (i > 0) fetch(i - 1);
         lds_barrier();
         // keep this chunk's dS_next, then scale it to dS_n
-        float* slot = a.dstates + ((size_t)j * a.H + h) * DD + jt * TW;
+        float* slot = a.dstates + cslot(a, j, h) * DD + jt * TW;
         for (int e = tid; e < D * TW / 4; e += BT) {
             const int r = e / (TW / 4), c = 4 * (e % (TW / 4));
             const v4f x = *reinterpret_cast<const v4f*>(sS + r * LT + c);
@@ -609,7 +613,7 @@ __global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
             for (int v = 0; v < 4; ++v) part[(16 * rt + acc_row(v)) * LT + acc_col()] = acc[v];
         }
         lds_barrier();
-        float* deout = a.debuf + ((size_t)j * a.H + h) * BC * D + jt * TW;
+        float* deout = a.debuf + cslot(a, j, h) * BC * D + jt * TW;
         for (int e = tid; e < BC * TW; e += BT) {   // dE (kept for the gradient step)
             const int r = e / TW, c = e % TW;
             const float x = sR[r * LT + c] + sV[r * LT + c];
@@ -668,13 +672,13 @@ __global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
     if (!chunk_pos(a, j, p)) return;
     const int tid = threadIdx.x, w = tid >> 6;
     const size_t DD = (size_t)D * D;
-    const float* rec = a.prep + ((size_t)j * a.H + h) * Rec<D>::SIZE;
+    const float* rec = a.prep + cslot(a, j, h) * Rec<D>::SIZE;
     const size_t slot = (size_t)(chunk0(a, p.n) + p.n + p.i);
-    const float* S = a.states + (slot * a.H + h) * DD;
-    const float* Snext = a.states + ((slot + 1) * a.H + h) * DD;
-    const float* dS = a.dstates + ((size_t)j * a.H + h) * DD;
-    const float* Rg = a.rbuf + ((size_t)j * a.H + h) * BC * D;    // R = V - K' S_m of the state pass
-    const float* dEg = a.debuf + ((size_t)j * a.H + h) * BC * D;  // dE of the reverse pass
+    const float* S = a.states + sslot(a, slot, h) * DD;
+    const float* Snext = a.states + sslot(a, slot + 1, h) * DD;
+    const float* dS = a.dstates + cslot(a, j, h) * DD;
+    const float* Rg = a.rbuf + cslot(a, j, h) * BC * D;    // R = V - K' S_m of the state pass
+    const float* dEg = a.debuf + cslot(a, j, h) * BC * D;  // dE of the reverse pass
 
     // one column tile of S, dS_next, S_next, R, dE and dO, fetched a tile ahead
     Stage<D, GW> rS, rdS, rSn;
@@ -928,6 +932,8 @@ hipError_t launch_backward(BackwardArgs a, const BackwardPlan& pl, void* workspa
     a.rbuf = reinterpret_cast<float*>(ws + pl.off_r);
     a.debuf = reinterpret_cast<float*>(ws + pl.off_de);
     const int nc = static_cast<int>(pl.nc_max);
+    a.ncs = nc;
+    a.nss = nc + a.N;
 #define KDA_BWD_CASE(DD, IN, OB)                                                              \
     if (a.D == DD && a.in_bf16 == std::is_same<IN, BF16>::value && a.out_bf16 == OB)         \
         return a.scalar_gate ? launch_typed<DD, IN, OB, true>(a, nc, st) : launch_typed<DD, IN, OB, false>(a, nc, st);
