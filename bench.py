@@ -388,7 +388,7 @@ def main():
                      "traffic": counted_traffic("backward"),
                      "hbm_frac": bwd_bytes / (bwd_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
                      "flop_convention": f"{backward_alg_flops_per_token_head(d)} per token-head "
-                                        "(20 d^2 + 16 C d), each product as three bf16 MFMAs"},
+                                        "(20 d^2 + 32 C d), each product as three bf16 MFMAs"},
     }
     del xb, gb, grads, wsb
 
