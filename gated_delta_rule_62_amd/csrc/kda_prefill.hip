@@ -1519,13 +1519,12 @@ void pipe_kernel(KernelArgs a) {
         }
     };
 
-    // consumer step 3: St <- Diag(rho) (St + Ktil_m^T Unew), and the output rows of the chunk
-    auto consume_update = [&](const Buf& B, int chunk) {
-        // The output-gate logits of this chunk's rows are requested before the state update,
-        // so their latency overlaps it (fused output pass only; rows past the end of a
-        // ragged chunk read its last row and are not stored).
-        using GRaw = typename std::conditional<std::is_same<IN, F32>::value, f32x4, uint2>::type;
-        GRaw graw[NRT][CT];
+    // The output-gate logits of a chunk's rows (fused output pass only; rows past the end of a
+    // ragged chunk read its last row and are not stored), requested before the solve so that
+    // their latency overlaps the solve and the state update that precede the O store.
+    using GRaw = typename std::conditional<std::is_same<IN, F32>::value, f32x4, uint2>::type;
+    GRaw graw[NRT][CT];
+    auto request_gate = [&](int chunk) __attribute__((always_inline)) {
         if constexpr (MODE == 0 && FUSE) {
             if (a.out_gate) {
                 const long ts = t0 + static_cast<long>(chunk) * C;
@@ -1541,6 +1540,9 @@ void pipe_kernel(KernelArgs a) {
                     }
             }
         }
+    };
+    // consumer step 3: St <- Diag(rho) (St + Ktil_m^T Unew), and the output rows of the chunk
+    auto consume_update = [&](const Buf& B, int chunk) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             const f32x4 rh = *reinterpret_cast<const f32x4*>(&B.rho[16 * rt + 4 * g4]);
@@ -1654,6 +1656,7 @@ void pipe_kernel(KernelArgs a) {
         const Buf& cur = sm.buf[chunk & 1];
         if (i > 0) wait_count(&sm.sync.ready, NPW * (i + 1), broken);
         consume_project(cur, chunk);
+        request_gate(chunk);
         consume_solve(cur);
         wait_count(&sm.sync.p1, NPW * (i + 2), broken);
         if (i + 1 < n_chunks) {
