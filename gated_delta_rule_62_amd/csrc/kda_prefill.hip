@@ -39,11 +39,13 @@
 //    diagonal blocks by substitution, the off-diagonal blocks follow in three
 //    block-row steps.
 //  * Few long sequences (the 64K-token workload has 32 heads): each sequence is
-//    cut into G segments.  Pass 1 runs segments 0..G-2 from a zero state and also
-//    carries the segment transition (the identity pushed through the same
-//    updates, which is linear in the state); a combine kernel chains
-//    S_entry(s+1) = Phi(s) S_entry(s) + S_loc(s); pass 2 reruns every segment from
-//    its entry state.  That fills the chip at the cost of a second pass.
+//    cut into G segments.  Pass 1 runs segments from a zero state and also carries
+//    the segment transition (the identity pushed through the same updates, which is
+//    linear in the state); a combine kernel chains
+//    S_entry(s+1) = Phi(s) S_entry(s) + S_loc(s); pass 2 reruns the segments from
+//    their entry states.  Segment 0 needs no summary: with 32-token chunks its
+//    output pass runs on a second stream beside pass 1 (segments 1..G-2), and pass 2
+//    covers segments 1..G-1.  That fills the chip at the cost of a second pass.
 #include <algorithm>
 #include <mutex>
 #include <type_traits>
