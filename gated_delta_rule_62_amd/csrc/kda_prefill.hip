@@ -47,6 +47,7 @@
 //    output pass runs on a second stream beside pass 1 (segments 1..G-2), and pass 2
 //    covers segments 1..G-1.  That fills the chip at the cost of a second pass.
 #include <algorithm>
+#include <cmath>
 #include <mutex>
 #include <type_traits>
 
@@ -328,6 +329,7 @@ struct KernelArgs {
     float* sloc;    // [G-1][N*H][D][D] segment end states from a zero entry
     float* se;      // [G-1][N*H][D][D] entry states of segments 1..G-1
     int T, H, NH, G, cps, chunks;
+    int cps0;       // chunks in segment 0 (cps unless the split schedule lengthens or shortens it)
     int seg0;       // segment of the launch's first workgroup row (equal-length batches)
     int split0;     // 1: segment 0's output pass writes its exit state as segment 1's entry
     // fused prologue / epilogue (FUSE kernels only)
@@ -375,8 +377,8 @@ void chunk_kernel(KernelArgs a) {
         h = unit % H;
         t0 = static_cast<long>(n) * a.T;
         t1 = t0 + a.T;
-        c_begin = s * a.cps;
-        c_end = min(c_begin + a.cps, a.chunks);
+        c_begin = s == 0 ? 0 : a.cps0 + (s - 1) * a.cps;
+        c_end = min(s == 0 ? a.cps0 : c_begin + a.cps, a.chunks);
     }
     const int unit = n * H + h;
     const size_t ubase = static_cast<size_t>(unit) * D * D;
@@ -956,8 +958,8 @@ void pipe_kernel(KernelArgs a) {
         h = unit % H;
         t0 = static_cast<long>(n) * a.T;
         t1 = t0 + a.T;
-        c_begin = s * a.cps;
-        c_end = min(c_begin + a.cps, a.chunks);
+        c_begin = s == 0 ? 0 : a.cps0 + (s - 1) * a.cps;
+        c_end = min(s == 0 ? a.cps0 : c_begin + a.cps, a.chunks);
     }
     const int unit = n * H + h;
     const size_t ubase = static_cast<size_t>(unit) * D * D;
@@ -1783,6 +1785,7 @@ hipError_t launch_variant(const PrefillArgs& pa, const PrefillPlan& plan, hipStr
     a.q = pa.q; a.k = pa.k; a.v = pa.v; a.g = pa.g; a.beta = pa.beta;
     a.S0 = pa.S0; a.cu = pa.cu; a.o = pa.o; a.S_final = pa.S_final;
     a.T = pa.T; a.H = pa.H; a.NH = pa.N * pa.H; a.G = plan.G; a.cps = plan.cps; a.chunks = plan.chunks;
+    a.cps0 = plan.cps;
     a.seg0 = 0;
     a.split0 = 0;
     a.fuse_flags = pa.fuse_flags; a.decay_bias = pa.decay_bias; a.decay_scale = pa.decay_scale;
@@ -1815,6 +1818,19 @@ hipError_t launch_variant(const PrefillArgs& pa, const PrefillPlan& plan, hipStr
         return hipGetLastError();
     }
     if (plan.G > 1 && plan.split0) {
+        // Segment 0's output pass runs beside the summaries of segments 1..G-2, so it may be as long
+        // as the ratio of a summary chunk's cost to an output chunk's (measured on MI355X: plain
+        // 1.14, scalar gate 1.08, fused output pass with its gate 0.95); the other segments share
+        // the rest equally.  Only for segments of 64 chunks or more, where the per-chunk costs
+        // outweigh the fixed ones of a segment (state loads and stores, the pipeline's fill).
+        // G, and with it the workspace, is unchanged.
+        constexpr double kSeg0Ratio = FUSE ? 0.95 : (SG ? 1.08 : 1.14);
+        const int cps = static_cast<int>(std::ceil(plan.chunks / (plan.G - 1 + kSeg0Ratio)));
+        const int cps0 = plan.chunks - (plan.G - 1) * cps;
+        if (plan.cps >= 64 && cps0 >= 1) {
+            a.cps = cps;
+            a.cps0 = cps0;
+        }
         SideStream* side = nullptr;
         if (side_stream(side) == hipSuccess) {
             // The fork / join events are shared by every call on this device: enqueue the

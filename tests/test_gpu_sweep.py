@@ -1,7 +1,7 @@
 """Prefill parity over a sweep of shapes that reach every schedule the planner picks:
 one pass, the plain two-segment schedule, and split schedules of 3 to 26 segments
-(segment 0's output pass on a second stream beside the other summaries) with ragged
-last segments and chunks; both chunk lengths, both head sizes, fp32 and bf16 inputs,
+(segment 0's output pass on a second stream beside the other summaries, lengthened when
+segments are long) with ragged last segments and chunks; both chunk lengths, both head sizes, fp32 and bf16 inputs,
 the fast-decay mixture and packed batches.  Each case is compared with the fp64
 oracle on the same seeded inputs.  Pages: "Decoding Hybrid Attention Architectures"
 (intl.cloud.baidu.com article 9569726) sections 3.4 and 4.
@@ -34,6 +34,8 @@ CASES = [
     (3, 1000, 2, 128, 64, "bf16", True, True),     # 64-token chunks: plain schedule, 4 segments
     (1, 64, 2, 64, 32, "bf16", False, True),       # one pass
     (1, 4100, 1, 128, 32, "bf16", True, True),     # 1 unit, d = 128: 26 segments
+    (1, 10300, 64, 64, 32, "bf16", True, True),    # 64 units: 5 segments of 65 chunks; segment 0
+                                                   # lengthened to 70, the others 63, ragged chunk
 ]
 
 
