@@ -1694,35 +1694,80 @@ void pipe_kernel(KernelArgs a) {
 
 // Entry states of segments s_first..G-1:  S_e(s) = Phi(s-1) S_e(s-1) + S_loc(s-1), starting from
 // S_e(s_first - 1) = init (S0, or segment 1's entry when segment 0 ran its output pass first;
-// null: zero).  One workgroup per (unit, 16-column slice); fp32 on the vector ALUs.
+// null: zero).  One workgroup per (unit, 16-column slice).  Phi(s-1) is staged through LDS with
+// coalesced loads, and the next segment's Phi and S_loc are requested while this one is applied;
+// the products run on the fp32 matrix cores (v_mfma_f32_16x16x4_f32), D/64 16-row tiles per wave.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ init, const float* __restrict__ phi,
                                                       const float* __restrict__ sloc, float* __restrict__ se,
                                                       int NH, int G, int s_first) {
-    constexpr int CPT = 16 * D / 256;   // columns per thread
-    constexpr int TPR = 16 / CPT;       // threads per row
-    __shared__ float cur[D][16];
-    const int unit = blockIdx.x, c0 = blockIdx.y * 16, tid = threadIdx.x;
-    const int r = tid / TPR, cc = (tid % TPR) * CPT;
+    constexpr int LP = D + 4;              // row pitch of Phi in LDS
+    constexpr int LC = 20;                 // row pitch of the 16-column state slice
+    constexpr int RT = D / 64;             // row tiles per wave
+    constexpr int NF = D * D / 4 / 256;    // float4 of Phi per thread
+    using fx4 = __attribute__((__vector_size__(4 * sizeof(float)))) float;
+    __shared__ __attribute__((aligned(16))) float sphi[D * LP];
+    __shared__ __attribute__((aligned(16))) float cur[2][D * LC];
+    const int unit = blockIdx.x, c0 = blockIdx.y * 16, tid = threadIdx.x, w = tid >> 6;
+    const int i = tid & 15, kq = (tid & 63) >> 4;
     const size_t ub = static_cast<size_t>(unit) * D * D;
-    for (int j = 0; j < CPT; ++j) cur[r][cc + j] = init ? init[ub + r * D + c0 + cc + j] : 0.f;
-    __syncthreads();
-    for (int s = s_first; s < G; ++s) {
+    for (int e = tid; e < D * 16; e += 256) cur[0][(e >> 4) * LC + (e & 15)] = init ? init[ub + (e >> 4) * D + c0 + (e & 15)] : 0.f;
+    fx4 pf[NF];
+    float pl[RT][4];
+    auto fetch = [&](int s) __attribute__((always_inline)) {
         const size_t sb = (static_cast<size_t>(s - 1) * NH + unit) * D * D;
-        float acc[CPT];
-        for (int j = 0; j < CPT; ++j) acc[j] = sloc[sb + r * D + c0 + cc + j];
-        const float* prow = phi + sb + static_cast<size_t>(r) * D;
-        for (int m = 0; m < D; ++m) {
-            const float p = prow[m];
+        const fx4* src = reinterpret_cast<const fx4*>(phi + sb);
 #pragma unroll
-            for (int j = 0; j < CPT; ++j) acc[j] += p * cur[m][cc + j];
+        for (int f = 0; f < NF; ++f) pf[f] = src[tid + 256 * f];
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) pl[t][v] = sloc[sb + static_cast<size_t>(16 * (w * RT + t) + 4 * kq + v) * D + c0 + i];
+    };
+    if (s_first < G) fetch(s_first);
+    int b = 0;
+    for (int s = s_first; s < G; ++s) {
+        __syncthreads();   // the last step's reads of sphi are done and its slice is complete
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            const int e = tid + 256 * f;
+            *reinterpret_cast<fx4*>(sphi + (e / (D / 4)) * LP + 4 * (e % (D / 4))) = pf[f];
         }
+        fx4 acc[RT];
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[t][v] = pl[t][v];
         __syncthreads();
-        for (int j = 0; j < CPT; ++j) {
-            cur[r][cc + j] = acc[j];
-            se[sb + r * D + c0 + cc + j] = acc[j];
+        if (s + 1 < G) fetch(s + 1);
+        // lane (i, kq) supplies key index k = 16 s2 + 4 kq + e of row i and of column i in the
+        // e-th product of step s2, so its Phi values are four consecutive floats
+#pragma unroll 2
+        for (int s2 = 0; s2 < D / 16; ++s2) {
+            fx4 a4[RT];
+#pragma unroll
+            for (int t = 0; t < RT; ++t)
+                a4[t] = *reinterpret_cast<const fx4*>(sphi + (16 * (w * RT + t) + i) * LP + 16 * s2 + 4 * kq);
+            const float* bc = cur[b] + (16 * s2 + 4 * kq) * LC + i;
+            const float b0 = bc[0], b1 = bc[LC], b2 = bc[2 * LC], b3 = bc[3 * LC];
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[t][0], b0, acc[t], 0, 0, 0);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[t][1], b1, acc[t], 0, 0, 0);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[t][2], b2, acc[t], 0, 0, 0);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[t][3], b3, acc[t], 0, 0, 0);
+            }
         }
-        __syncthreads();
+        const size_t sb = (static_cast<size_t>(s - 1) * NH + unit) * D * D;
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int row = 16 * (w * RT + t) + 4 * kq + v;
+                cur[b ^ 1][row * LC + i] = acc[t][v];
+                se[sb + static_cast<size_t>(row) * D + c0 + i] = acc[t][v];
+            }
+        b ^= 1;
     }
 }
 
