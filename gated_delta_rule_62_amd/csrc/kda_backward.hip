@@ -221,23 +221,23 @@ typedef unsigned v2u __attribute__((ext_vector_type(2)));
 // registers: load() issues every global load of the block and nothing waits on them
 // until store() writes the block to LDS (row stride ls), so a block can be fetched
 // while the previous one is being used.
-template <int ROWS, int COLS>
+template <int ROWS, int COLS, int NT = BT>
 struct Stage {
-    static constexpr int C4 = COLS / 4, N4 = ROWS * C4, IT = (N4 + BT - 1) / BT;
+    static constexpr int C4 = COLS / 4, N4 = ROWS * C4, IT = (N4 + NT - 1) / NT;
     static_assert(COLS % 4 == 0, "");
     v4f x[IT];
-    __device__ __forceinline__ static bool live(int e) { return N4 % BT == 0 || e < N4; }
+    __device__ __forceinline__ static bool live(int e) { return N4 % NT == 0 || e < N4; }
     __device__ __forceinline__ void load(const float* g, size_t gs) {
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
-            const int e = threadIdx.x + it * BT;
+            const int e = threadIdx.x + it * NT;
             if (live(e)) x[it] = *reinterpret_cast<const v4f*>(g + (size_t)(e / C4) * gs + 4 * (e % C4));
         }
     }
     __device__ __forceinline__ void store(float* s, int ls) const {
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
-            const int e = threadIdx.x + it * BT;
+            const int e = threadIdx.x + it * NT;
             if (live(e)) *reinterpret_cast<v4f*>(s + (e / C4) * ls + 4 * (e % C4)) = x[it];
         }
     }
@@ -255,22 +255,22 @@ __device__ __forceinline__ void s2g(float* g, size_t gs, const float* s, int ls)
 // One chunk's rows [t0, t0 + len) of a [tokens, H, W] input, COLS columns from col0,
 // staged like Stage in the input's own type (converted to fp32 on the way to LDS);
 // rows past len are zero.
-template <class IN, int COLS>
+template <class IN, int COLS, int NT = BT>
 struct StageRows {
     static constexpr bool B16 = std::is_same<IN, BF16>::value;
-    static constexpr int C4 = COLS / 4, N4 = BC * C4, IT = (N4 + BT - 1) / BT;
+    static constexpr int C4 = COLS / 4, N4 = BC * C4, IT = (N4 + NT - 1) / NT;
     static_assert(COLS % 4 == 0, "");
     using raw_t = typename std::conditional<B16, v2u, v4f>::type;
     raw_t x[IT];
     int len_ = 0;
-    __device__ __forceinline__ static bool live(int e) { return N4 % BT == 0 || e < N4; }
+    __device__ __forceinline__ static bool live(int e) { return N4 % NT == 0 || e < N4; }
     // Rows past len read row len - 1 (always in bounds for len >= 1) and are zeroed by
     // store(), so no load sits behind a branch.
     __device__ __forceinline__ void load(const void* p, int t0, int len, int H, int h, int W, int col0) {
         len_ = len;
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
-            const int e = threadIdx.x + it * BT, r = min(e / C4, len - 1), c = 4 * (e % C4);
+            const int e = threadIdx.x + it * NT, r = min(e / C4, len - 1), c = 4 * (e % C4);
             if (live(e)) {
                 const size_t idx = ((size_t)(t0 + r) * H + h) * W + col0 + c;
                 x[it] = *reinterpret_cast<const raw_t*>(static_cast<const typename IN::storage*>(p) + idx);
@@ -288,7 +288,7 @@ struct StageRows {
     __device__ __forceinline__ void store(float* s, int ls) const {
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
-            const int e = threadIdx.x + it * BT;
+            const int e = threadIdx.x + it * NT;
             const bool ok = e / C4 < len_;
             v4f v = widen(x[it]);
             v.x = ok ? v.x : 0.f;
@@ -654,11 +654,18 @@ __global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
     }
 }
 
+// Each wave owns one 16-column tile of D in GRAD_RTW of the chunk's two 16-row tiles (so 8 D /
+// GRAD_RTW threads), and waves 0-3 also the four 16 x 16 tiles of the C x GW and C x C products.
+constexpr int GRAD_RTW = 2;
+template <int D>
+constexpr int grad_threads() { return 8 * D / GRAD_RTW; }
+
 template <int D, class IN, bool OB, bool SG>
-__global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
+__global__ __launch_bounds__(grad_threads<D>()) void grad_kernel(BackwardArgs a) {
     constexpr bool SPLIT = std::is_same<IN, BF16>::value;   // split-bf16 products for bf16 inputs
     constexpr int LD = D + 4, LC = BC + 4, LT = GW + 4, NCT = D / GW;
-    constexpr int CT_PER_WAVE = D / 16 / 4;   // 16-column tiles of D owned by each wave
+    constexpr int RTW = GRAD_RTW, GT = grad_threads<D>(), NW = GT / 64;   // threads and waves
+    static_assert(NW >= 4 && NW == (D / 16) * (2 / RTW), "");
     static_assert(LT == LC, "the C x C products reuse C x GW buffers");
     static_assert(BC * LD <= D * LT, "the decay and db planes reuse the state tiles");
     __shared__ __attribute__((aligned(16))) float sQp[BC * LD], sKp[BC * LD], sKpp[BC * LD];
@@ -681,9 +688,9 @@ __global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
     const float* dEg = a.debuf + cslot(a, j, h) * BC * D;  // dE of the reverse pass
 
     // one column tile of S, dS_next, S_next, R, dE and dO, fetched a tile ahead
-    Stage<D, GW> rS, rdS, rSn;
-    Stage<BC, GW> rR, rdE;
-    StageRows<IN, GW> rO;
+    Stage<D, GW, GT> rS, rdS, rSn;
+    Stage<BC, GW, GT> rR, rdE;
+    StageRows<IN, GW, GT> rO;
     auto fetch = [&](int ct) __attribute__((always_inline)) {
         rS.load(S + ct * GW, D);
         rdS.load(dS + ct * GW, D);
@@ -692,10 +699,10 @@ __global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
         rdE.load(dEg + ct * GW, D);
         rO.load(a.dO, p.t0, p.len, a.H, h, D, ct * GW);
     };
-    Stage<BC, D> rX;       // decay exponents b - m, used after the column loop
+    Stage<BC, D, GT> rX;   // decay exponents b - m, used after the column loop
     {
-        Stage<BC, D> r1, r2, r3;
-        Stage<BC, BC> r4, r6;
+        Stage<BC, D, GT> r1, r2, r3;
+        Stage<BC, BC, GT> r4, r6;
         r1.load(rec + Rec<D>::QP, D);
         r2.load(rec + Rec<D>::KP, D);
         r3.load(rec + Rec<D>::KPP, D);
@@ -718,24 +725,24 @@ __global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
         if (tid < BC) sB[tid] = bt;
     }
 
-    f4 dQp[2][CT_PER_WAVE], dKp[2][CT_PER_WAVE], dKpp[2][CT_PER_WAVE];
+    // this wave's 16-column tile dt of D and its row tiles rt0 .. rt0 + RTW - 1
+    const int dt = w * RTW / 2, rt0 = RTW == 2 ? 0 : (w & 1);
+    f4 dQp[RTW], dKp[RTW], dKpp[RTW];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int q = 0; q < CT_PER_WAVE; ++q) dQp[rt][q] = dKp[rt][q] = dKpp[rt][q] = zero4();
+    for (int q = 0; q < RTW; ++q) dQp[q] = dKp[q] = dKpp[q] = zero4();
     f4 dPacc = zero4(), dYE = zero4();
     float dbeta = 0.f;
-    const int trt = w & 1, tct = w >> 1;   // this wave's C x GW tile (and C x C tile)
+    const int trt = w & 1, tct = (w >> 1) & 1;   // the C x GW (and C x C) tile of waves 0-3
 
     for (int ct = 0; ct < NCT; ++ct) {
         lds_barrier();
         rdE.store(sdE, LT);
         rO.store(sO, LT);
 #pragma unroll
-        for (int it = 0; it < Stage<BC, GW>::IT; ++it) {   // R, and Y = Diag(beta) R
+        for (int it = 0; it < Stage<BC, GW, GT>::IT; ++it) {   // R, and Y = Diag(beta) R
             constexpr int C4 = GW / 4;
-            const int e = tid + it * BT, r = e / C4, c = 4 * (e % C4);
-            if (Stage<BC, GW>::live(e)) {
+            const int e = tid + it * GT, r = e / C4, c = 4 * (e % C4);
+            if (Stage<BC, GW, GT>::live(e)) {
                 const v4f x = rR.x[it];
                 const float b = sB[r];
                 *reinterpret_cast<v4f*>(sV + r * LT + c) = x;
@@ -744,9 +751,9 @@ __global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
         }
         // S_m, dS_n tiles; rowsum(dS_next * S_next) for the last row's db
 #pragma unroll
-        for (int it = 0; it < Stage<D, GW>::IT; ++it) {
+        for (int it = 0; it < Stage<D, GW, GT>::IT; ++it) {
             constexpr int C4 = GW / 4;
-            const int e = tid + it * BT, r = e / C4, c = 4 * (e % C4);
+            const int e = tid + it * GT, r = e / C4, c = 4 * (e % C4);
             const v4f x = rS.x[it], y = rdS.x[it], z = rSn.x[it];
             const float em = sEm[r], en = sEn[r];
             *reinterpret_cast<v4f*>(sSm + r * LT + c) = v4f{x.x * em, x.y * em, x.z * em, x.w * em};
@@ -759,7 +766,7 @@ __global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
         }
         if (ct + 1 < NCT) fetch(ct + 1);
         lds_barrier();
-        {
+        if (w < 4) {
             f4 e = zero4();     // E = M Y
             mma<BC, SPLIT>(e, sM + 16 * trt * LC, LC, 1, sY + 16 * tct, LT, 1);
             f4 y = zero4();     // dY = M^T dE
@@ -781,25 +788,27 @@ __global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
             dbeta += s;
         }
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int q = 0; q < CT_PER_WAVE; ++q) {
-                const int dt = w * CT_PER_WAVE + q;   // 16-column tile of D
-                mma<GW, SPLIT>(dQp[rt][q], sO + 16 * rt * LT, LT, 1, sSm + 16 * dt * LT, 1, LT);
-                mma<GW, SPLIT>(dKp[rt][q], smdV + 16 * rt * LT, LT, 1, sSm + 16 * dt * LT, 1, LT);
-                mma<GW, SPLIT>(dKpp[rt][q], sE + 16 * rt * LT, LT, 1, sdSn + 16 * dt * LT, 1, LT);
-            }
+        for (int q = 0; q < RTW; ++q) {
+            const int rt = rt0 + q;
+            mma<GW, SPLIT>(dQp[q], sO + 16 * rt * LT, LT, 1, sSm + 16 * dt * LT, 1, LT);
+            mma<GW, SPLIT>(dKp[q], smdV + 16 * rt * LT, LT, 1, sSm + 16 * dt * LT, 1, LT);
+            mma<GW, SPLIT>(dKpp[q], sE + 16 * rt * LT, LT, 1, sdSn + 16 * dt * LT, 1, LT);
+        }
         // dP (+)= dO E^T, dY E^T on this wave's C x C tile
-        mma<GW, SPLIT>(dPacc, sO + 16 * trt * LT, LT, 1, sE + 16 * tct * LT, 1, LT);
-        mma<GW, SPLIT>(dYE, sdY + 16 * trt * LT, LT, 1, sE + 16 * tct * LT, 1, LT);
+        if (w < 4) {
+            mma<GW, SPLIT>(dPacc, sO + 16 * trt * LT, LT, 1, sE + 16 * tct * LT, 1, LT);
+            mma<GW, SPLIT>(dYE, sdY + 16 * trt * LT, LT, 1, sE + 16 * tct * LT, 1, LT);
+        }
     }
     lds_barrier();
     // dP = Tril(dO E^T) -> sdE;  dA = -StrictTril(dY E^T) -> sdY  (both C x C, row stride LC)
+    if (w < 4) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int r = 16 * trt + acc_row(v), c = 16 * tct + acc_col();
-        sdE[r * LC + c] = r >= c ? dPacc[v] : 0.f;
-        sdY[r * LC + c] = r > c ? -dYE[v] : 0.f;
+        for (int v = 0; v < 4; ++v) {
+            const int r = 16 * trt + acc_row(v), c = 16 * tct + acc_col();
+            sdE[r * LC + c] = r >= c ? dPacc[v] : 0.f;
+            sdY[r * LC + c] = r > c ? -dYE[v] : 0.f;
+        }
     }
     __syncthreads();
     if (tid < BC) {   // dbeta += rowsum(dA L); dL = Diag(beta) dA (in place)
@@ -818,32 +827,30 @@ __global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
     __syncthreads();
     float* sDb = sdSn;   // db as [C][LD]
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int q = 0; q < RTW; ++q) {
+        const int rt = rt0 + q;
+        mma<BC, SPLIT>(dQp[q], sdE + 16 * rt * LC, LC, 1, sKpp + 16 * dt, LD, 1);   // + dP K''
+        mma<BC, SPLIT>(dKp[q], sdY + 16 * rt * LC, LC, 1, sKpp + 16 * dt, LD, 1);   // + dL K''
+        mma<BC, SPLIT>(dKpp[q], sdE + 16 * rt, 1, LC, sQp + 16 * dt, LD, 1);        // + dP^T Q'
+        mma<BC, SPLIT>(dKpp[q], sdY + 16 * rt, 1, LC, sKp + 16 * dt, LD, 1);        // + dL^T K'
 #pragma unroll
-        for (int q = 0; q < CT_PER_WAVE; ++q) {
-            const int dt = w * CT_PER_WAVE + q;
-            mma<BC, SPLIT>(dQp[rt][q], sdE + 16 * rt * LC, LC, 1, sKpp + 16 * dt, LD, 1);   // + dP K''
-            mma<BC, SPLIT>(dKp[rt][q], sdY + 16 * rt * LC, LC, 1, sKpp + 16 * dt, LD, 1);   // + dL K''
-            mma<BC, SPLIT>(dKpp[rt][q], sdE + 16 * rt, 1, LC, sQp + 16 * dt, LD, 1);        // + dP^T Q'
-            mma<BC, SPLIT>(dKpp[rt][q], sdY + 16 * rt, 1, LC, sKp + 16 * dt, LD, 1);        // + dL^T K'
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int r = 16 * rt + acc_row(v), c = 16 * dt + acc_col();
-                const float x = sX[r * LD + c], up = fast_exp(x), dn = fast_exp(-x);
-                const float gq = dQp[rt][q][v], gk = dKp[rt][q][v], gkk = dKpp[rt][q][v];
-                sDb[r * LD + c] = sQp[r * LD + c] * gq + sKp[r * LD + c] * gk - sKpp[r * LD + c] * gkk;
-                if (r < p.len) {
-                    const size_t gi = ((size_t)(p.t0 + r) * a.H + h) * D + c;
-                    store_out<OB>(a.dq, gi, up * gq);
-                    store_out<OB>(a.dk, gi, up * gk + dn * gkk);
-                }
+        for (int v = 0; v < 4; ++v) {
+            const int r = 16 * rt + acc_row(v), c = 16 * dt + acc_col();
+            const float x = sX[r * LD + c], up = fast_exp(x), dn = fast_exp(-x);
+            const float gq = dQp[q][v], gk = dKp[q][v], gkk = dKpp[q][v];
+            sDb[r * LD + c] = sQp[r * LD + c] * gq + sKp[r * LD + c] * gk - sKpp[r * LD + c] * gkk;
+            if (r < p.len) {
+                const size_t gi = ((size_t)(p.t0 + r) * a.H + h) * D + c;
+                store_out<OB>(a.dq, gi, up * gq);
+                store_out<OB>(a.dk, gi, up * gk + dn * gkk);
             }
         }
+    }
     __syncthreads();
     if constexpr (SG) {
         // one log-decay per token: its gradient is the sum over key channels of the
         // per-channel one, i.e. the reverse cumulative sum of the row sums of db
-        constexpr int TPR = BT / BC;   // threads per row
+        constexpr int TPR = GT / BC;   // threads per row
         const int r = tid / TPR, part = tid % TPR, lane = tid & 63;
         float t = 0.f;
         for (int c = part; c < D; c += TPR) t += sDb[r * LD + c];
@@ -865,8 +872,8 @@ __global__ __launch_bounds__(BT) void grad_kernel(BackwardArgs a) {
             store_out<OB>(a.dg, (size_t)(p.t0 + tid) * a.H + h, acc);
         }
     } else {   // dlog_alpha = reverse cumulative sum of db (last row: + rowsum(dS_next S_next)); the
-        // rows are cut into BT / D parts, each part first sums its rows
-        constexpr int NP = BT / D, RP = BC / NP;
+        // rows are cut into GT / D parts, each part first sums its rows
+        constexpr int NP = GT / D, RP = BC / NP;
         const int c = tid % D, part = tid / D;
         float* sPart = sY;
         float tot = 0.f;
@@ -893,7 +900,7 @@ hipError_t launch_typed(const BackwardArgs& a, int nc_max, hipStream_t st) {
         state_fwd_kernel<D, IN><<<units * (D / TW), BT, 0, st>>>(a);
         state_rev_kernel<D, IN><<<units * (D / TW), BT, 0, st>>>(a);
     }
-    if (nc_max > 0) grad_kernel<D, IN, OB, SG><<<nc_max * a.H, BT, 0, st>>>(a);
+    if (nc_max > 0) grad_kernel<D, IN, OB, SG><<<nc_max * a.H, grad_threads<D>(), 0, st>>>(a);
     return hipGetLastError();
 }
 
