@@ -1865,11 +1865,11 @@ hipError_t launch_variant(const PrefillArgs& pa, const PrefillPlan& plan, hipStr
     if (plan.G > 1 && plan.split0) {
         // Segment 0's output pass runs beside the summaries of segments 1..G-2, so it may be as long
         // as the ratio of a summary chunk's cost to an output chunk's (measured on MI355X: plain
-        // 1.14, scalar gate 1.08, fused output pass with its gate 0.95); the other segments share
+        // 1.18, scalar gate 1.08, fused output pass with its gate 0.95); the other segments share
         // the rest equally.  Only for segments of 64 chunks or more, where the per-chunk costs
         // outweigh the fixed ones of a segment (state loads and stores, the pipeline's fill).
         // G, and with it the workspace, is unchanged.
-        constexpr double kSeg0Ratio = FUSE ? 0.95 : (SG ? 1.08 : 1.14);
+        constexpr double kSeg0Ratio = FUSE ? 0.95 : (SG ? 1.08 : 1.18);
         const int cps = static_cast<int>(std::ceil(plan.chunks / (plan.G - 1 + kSeg0Ratio)));
         const int cps0 = plan.chunks - (plan.G - 1) * cps;
         if (plan.cps >= 64 && cps0 >= 1) {
