@@ -15,7 +15,12 @@ as ``gdn``, a few new tokens per sequence on top of a carried state as
 ``continuation``, the gradient (``kda_chunk_bwd``) on the training-prefill
 workload as ``backward``, the roofline of each path's dominant launch measured with HIP events
 on the launch stream, and the fp64 CPU oracle timed on a bounded sample of the
-same workloads on this host (``cpu_baseline``).
+same workloads on this host (``cpu_baseline``).  ``prefill_workloads`` gives the
+forward of the other prefill workloads the same way: the tiny fp32 one (B=1, H=2,
+T=256, d=64, chunk 64), the training shape (B=4, H=16, T=4096, d=128) at chunk 64
+as the workload names it and at the default chunk 32, and the packed varlen one
+(64 sequences, 525,197 tokens, H=32, d=128).  Every prefill line gives the median
+and the minimum of individually timed calls (HIP events around each call).
 
 Inputs are synthetic and seeded, drawn on the GPU with the workloads' recipe
 (q, k L2-normalised normals, v normal, beta = sigmoid(normal), log_alpha =
@@ -99,6 +104,89 @@ def counted_traffic(kind: str):
     if h.hexdigest() != rec.get("source_sha256"):
         return None
     return rec["read_bytes"] + rec["write_bytes"]
+
+
+def timed_calls(torch, fn, stream, warmup: int, n: int) -> dict:
+    """warmup untimed calls, then n calls each bracketed by HIP events on `stream`:
+    median, min and mean milliseconds per call."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    return {"median": ms[len(ms) // 2], "min": ms[0], "mean": sum(ms) / len(ms), "calls": n}
+
+
+def prefill_line(label, tokens, H, d, n_seqs, has_s0, C, t, in_bytes=2, out_bytes=2):
+    """Throughput and roofline fields of one prefill workload from its call times t (ms)."""
+    per_token_head = 4 * d * in_bytes + in_bytes + d * out_bytes
+    byts = tokens * H * per_token_head + n_seqs * H * d * d * 4 * (2 if has_s0 else 1)
+    flops = prefill_alg_flops_per_token_head(d, C) * tokens * H
+    tile = prefill_tile_flops_per_token_head(d, C) * tokens * H
+    sec = t["median"] / 1e3
+    return {"workload": label, "tokens": tokens, "value": tokens / sec, "unit": "tokens/s",
+            "ms_per_call_median": t["median"], "ms_per_call_min": t["min"], "ms_per_call_mean": t["mean"],
+            "roofline": {"bound": "hbm", "achieved": byts / sec / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": byts / sec / 1e9 / HBM_PEAK_GBS, "bytes_per_call": byts,
+                         "mfma_frac": flops / sec / 1e12 / BF16_PEAK_TFLOPS,
+                         "mfma_frac_dense_tile": tile / sec / 1e12 / BF16_PEAK_TFLOPS,
+                         "flop_convention": f"algorithmic {prefill_alg_flops_per_token_head(d, C)} / dense-tile "
+                                            f"{prefill_tile_flops_per_token_head(d, C)} per token-head at C={C}"}}
+
+
+def cpu_baseline_batch(torch, x, target_s=6.0):
+    """The fp64 oracle on a bounded sample of a device batch x (inputs.device_prefill layout):
+    equal-length batches run the first Ts tokens of every sequence, packed batches their first
+    sequences; the sample is sized from a calibration run to about target_s seconds."""
+    import numpy as np
+    import oracle
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    H = x["H"]
+    units_per_seq = H
+    keys = ("q", "k", "v", "log_alpha", "beta")
+    if x["cu_seqlens"] is None:
+        B, T = x["B"], x["T"]
+        threads = min(cores, oracle.max_threads(), B * H)
+
+        def run(Ts):
+            args = [bf16_to_bits(torch, x[kk][:, :Ts]) if x[kk].dtype == torch.bfloat16
+                    else x[kk][:, :Ts].contiguous().cpu().numpy() for kk in keys]
+            s0 = None if x["S0"] is None else x["S0"].cpu().numpy()
+            t0 = time.perf_counter()
+            oracle.kda_fwd(*args, S0=s0, num_threads=threads)
+            return time.perf_counter() - t0
+
+        cal = min(T, 512)
+        dt = run(cal)
+        Ts = int(min(T, max(cal, cal * target_s / max(dt, 1e-6))))
+        dt = run(Ts) if Ts != cal else dt
+        return {"value": B * Ts / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                "sample": f"first {Ts} of {T} tokens of all {B} sequences, all {H} heads (fp64 token "
+                          f"recurrence, OpenMP over (sequence, head)), {dt:.1f} s"}
+    cu = np.asarray(x["cu_host"], dtype=np.int64)
+    N = len(cu) - 1
+    threads = min(cores, oracle.max_threads())
+
+    def run(m):
+        sl = slice(0, int(cu[m]))
+        args = [bf16_to_bits(torch, x[kk][:, sl]) for kk in keys]
+        t0 = time.perf_counter()
+        oracle.kda_fwd(*args, cu_seqlens=cu[: m + 1].astype(np.int32), num_threads=threads)
+        return time.perf_counter() - t0
+
+    m = min(N, max(1, threads // units_per_seq))
+    dt = run(m)
+    while m < N and dt < target_s / 2:
+        m = min(N, 2 * m)
+        dt = run(m)
+    return {"value": int(cu[m]) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the first {m} of {N} packed sequences ({int(cu[m])} tokens), all {H} heads "
+                      f"(fp64 token recurrence, OpenMP over (sequence, head)), {dt:.1f} s"}
 
 
 def bf16_to_bits(torch, t):
@@ -205,6 +293,7 @@ def main():
     ms_step = ms_total / args.steps
     call_ms = sorted(a.elapsed_time(b) for a, b in ev)
     call_avg_ms = sum(call_ms) / len(call_ms)
+    call_med_ms, call_min_ms = call_ms[len(call_ms) // 2], call_ms[0]
     tokens = B * T
     value = tokens / (ms_step / 1e3)
     flops = prefill_alg_flops_per_token_head(d) * tokens * H
@@ -213,6 +302,45 @@ def main():
     tflops = flops / (call_avg_ms / 1e3) / 1e12
     tile_tflops = tile_flops / (call_avg_ms / 1e3) / 1e12
     gbs = byts / (call_avg_ms / 1e3) / 1e9
+
+    # ------------------------------------------------------------------ the other prefill workloads
+    # The forward of the remaining prefill workloads, each timed call by call (median and min of
+    # `steps` calls after `warmup`), with its own roofline and oracle sample.
+    del o
+    prefill_workloads = {}
+
+    def other_prefill(key, w, C, label, in_bytes=2, out_bytes=2):
+        xw = inputs.device_prefill(w)
+        Bw, Tw, Hw, dw, Nw = xw["B"], xw["T"], xw["H"], xw["D"], xw["N"]
+        odt = torch.bfloat16 if out_bytes == 2 else torch.float32
+        ow = torch.empty((Bw, Tw, Hw, dw), dtype=odt, device="cuda")
+        Sw = torch.empty((Nw, Hw, dw, dw), dtype=torch.float32, device="cuda")
+        wsw = torch.empty(kda.kda_chunk_fwd_workspace_bytes(Bw, Tw, Hw, dw, dw, Nw, xw["cu_seqlens"] is not None, C),
+                          dtype=torch.uint8, device="cuda")
+
+        def run():
+            kda.kda_chunk_fwd(xw["q"], xw["k"], xw["v"], xw["log_alpha"], xw["beta"], xw["S0"], xw["cu_seqlens"],
+                              o=ow, S_final=Sw, workspace=wsw, chunk=C, stream=stream)
+        t = timed_calls(torch, run, stream, max(3, args.warmup // 2), args.steps)
+        line = prefill_line(label, Bw * Tw, Hw, dw, Nw, xw["S0"] is not None, C, t, in_bytes, out_bytes)
+        line["config"] = {"workload": w.name, "B": Bw, "T": Tw, "H": Hw, "d_k": dw, "d_v": dw, "chunk": C,
+                          "sequences": Nw, "in_dtype": w.dtype, "out_dtype": "bf16" if out_bytes == 2 else "fp32"}
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = cpu_baseline_batch(torch, xw)
+        prefill_workloads[key] = line
+        del xw, ow, Sw, wsw
+        torch.cuda.empty_cache()
+
+    other_prefill("tiny_fp32", inputs.WORKLOADS[0], 64,
+                  "tiny fp32 prefill: B=1, T=256, H=2, d=64, fp32 in/out, chunk 64", in_bytes=4, out_bytes=4)
+    other_prefill("train_prefill_c64", inputs.WORKLOADS[1], 64,
+                  "training-shape prefill: B=4, T=4096, H=16, d=128, bf16, chunk 64 (as the workload states)")
+    other_prefill("train_prefill_c32", inputs.WORKLOADS[1], 32,
+                  "training-shape prefill: B=4, T=4096, H=16, d=128, bf16, chunk 32 (the library default)")
+    other_prefill("varlen_packed", inputs.WORKLOADS[4], 32,
+                  "packed varlen prefill: 64 sequences U{512..16384} (525,197 tokens), H=32, d=128, bf16, "
+                  "per-element decay mixture, chunk 32")
+    o = torch.empty((B, T, H, d), dtype=torch.bfloat16, device="cuda")
 
     # ------------------------------------------------------------------ decode
     w3 = inputs.WORKLOADS[3]
@@ -378,15 +506,16 @@ def main():
         "workload": "train_prefill backward: B=4, T=4096, H=16, d=128, bf16 inputs and gradients, "
                     "fp32 dS0, kda_chunk_bwd (all kernels of one call)",
         "value": Bb * Tb / (bwd_ms / 1e3), "unit": "tokens/s", "ms_per_call": bwd_ms,
-        # bf16 inputs: every product runs on the bf16 matrix cores as three split-bf16 MFMAs
-        # (hi.hi + hi.lo + lo.hi), so the dtype's peak is the bf16 one; frac_split_peak divides
-        # by a third of it, the rate those products can reach.
-        "roofline": {"bound": "mfma", "achieved": bwd_flops / (bwd_ms / 1e3) / 1e12, "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": bwd_flops / (bwd_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
-                     "frac_split_peak": bwd_flops / (bwd_ms / 1e3) / 1e12 / (BF16_PEAK_TFLOPS / 3),
-                     "flops_per_call": bwd_flops, "bytes_per_call": bwd_bytes,
-                     "traffic": counted_traffic("backward"),
-                     "hbm_frac": bwd_bytes / (bwd_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+        # The method's intensity (about 199 flop/B) is below MI355X's ridge (2500 TFLOP/s / 8 TB/s
+        # = 312 flop/B), so HBM bounds it.  The MFMA fractions are side figures: against the bf16
+        # peak, and against a third of it (each product here is three split-bf16 MFMAs).
+        "roofline": {"bound": "hbm", "achieved": bwd_bytes / (bwd_ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": bwd_bytes / (bwd_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                     "bytes_per_call": bwd_bytes, "traffic": counted_traffic("backward"),
+                     "mfma_tflops": bwd_flops / (bwd_ms / 1e3) / 1e12,
+                     "mfma_frac": bwd_flops / (bwd_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
+                     "mfma_frac_split_peak": bwd_flops / (bwd_ms / 1e3) / 1e12 / (BF16_PEAK_TFLOPS / 3),
+                     "flops_per_call": bwd_flops,
                      "flop_convention": f"{backward_alg_flops_per_token_head(d)} per token-head "
                                         "(20 d^2 + 32 C d), each product as three bf16 MFMAs"},
     }
@@ -414,13 +543,15 @@ def main():
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": counted_traffic("prefill"),
                      "launch": "kda_chunk_fwd (all prefill kernels of one call)",
-                     "avg_launch_us": call_avg_ms * 1e3, "bytes_per_launch": byts,
+                     "avg_launch_us": call_avg_ms * 1e3, "median_launch_us": call_med_ms * 1e3,
+                     "min_launch_us": call_min_ms * 1e3, "bytes_per_launch": byts,
                      "mfma_tflops": tflops, "mfma_frac": tflops / BF16_PEAK_TFLOPS,
                      "mfma_frac_dense_tile": tile_tflops / BF16_PEAK_TFLOPS,
                      "flop_convention": f"algorithmic {prefill_alg_flops_per_token_head(d)} / dense-tile "
                                         f"{prefill_tile_flops_per_token_head(d)} per token-head at C={CHUNK}",
                      "flops_per_launch": flops},
         "cpu_baseline": cpu,
+        "prefill_workloads": prefill_workloads,
         "decode": decode,
         "fused_prologue": fused,
         "gdn": gdn,

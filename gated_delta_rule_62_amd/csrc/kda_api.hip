@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 
 #include "kda.h"
@@ -22,6 +23,18 @@ size_t elem_size(kda_dtype d) { return d == KDA_BF16 ? 2 : 4; }
 bool dtype_ok(kda_dtype d) { return d == KDA_F32 || d == KDA_BF16; }
 
 bool head_ok(int Dk, int Dv) { return Dk == Dv && (Dk == 64 || Dk == 128); }
+
+// Polls before a kernel's ordering wait gives up.  KDA_DEBUG_WAIT_POLLS (a non-negative integer)
+// lowers it for tests of the failure path, which then see NaN outputs and a set status word
+// while every kernel still runs to its end.
+int wait_limit() {
+    const char* e = std::getenv("KDA_DEBUG_WAIT_POLLS");
+    if (!e || !*e) return kda::kWaitLimit;
+    char* end = nullptr;
+    const long v = std::strtol(e, &end, 10);
+    if (*end != '\0' || v < 0 || v > kda::kWaitLimit) return kda::kWaitLimit;
+    return static_cast<int>(v);
+}
 
 // [a, a+na) and [b, b+nb) overlap?
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
@@ -124,11 +137,22 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
     if (overlap(S0, n_s, S_final, n_s) || overlap(S0, n_s, o, n_o) || overlap(o, n_o, S_final, n_s))
         return KDA_ERR_INVALID_ARGUMENT;
 
+    if (num_seqs == 0) return KDA_OK;
     kda::PrefillPlan plan = kda::plan_prefill(B, T, H, Dk, num_seqs, cu_seqlens != nullptr, chunk);
     if (workspace_bytes < plan.workspace_bytes) return KDA_ERR_WORKSPACE_TOO_SMALL;
-    if (plan.workspace_bytes > 0 && (!workspace || !aligned16(workspace))) return KDA_ERR_INVALID_ARGUMENT;
-    if (num_seqs == 0) return KDA_OK;
+    if (!workspace || !aligned16(workspace)) return KDA_ERR_INVALID_ARGUMENT;
     if (overlap(workspace, plan.workspace_bytes, o, n_o) || overlap(workspace, plan.workspace_bytes, S_final, n_s))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (tokens > 0) {
+        const void* ins[5] = {q, k, v, log_alpha, beta};
+        const size_t nin[5] = {n_qk, n_qk, n_v, n_g, n_b};
+        for (int i = 0; i < 5; ++i)
+            if (overlap(ins[i], nin[i], workspace, plan.workspace_bytes)) return KDA_ERR_INVALID_ARGUMENT;
+    }
+    if (overlap(S0, n_s, workspace, plan.workspace_bytes) ||
+        overlap(cu_seqlens, (static_cast<size_t>(num_seqs) + 1) * sizeof(int32_t), workspace, plan.workspace_bytes))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (fused && fusion->out_gate && overlap(fusion->out_gate, tokens * H * Dv * ein, workspace, plan.workspace_bytes))
         return KDA_ERR_INVALID_ARGUMENT;
 
     // A batch of equal-length sequences of at most kRecurrentMaxT tokens (new tokens on top of a
@@ -136,9 +160,11 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
     if (!cu_seqlens && T > 0 && T <= kda::kRecurrentMaxT && !fused) {
         const size_t units = static_cast<size_t>(B) * H;
         if (units > 0x7fffffffu) return KDA_ERR_UNSUPPORTED;
-        hipError_t err = kda::launch_recurrent_fwd(Dk, in_dtype == KDA_BF16, out_dtype == KDA_BF16, q, k, v,
-                                                   log_alpha, beta, S0, nullptr, T, H, static_cast<int>(units), o,
-                                                   S_final, reinterpret_cast<hipStream_t>(stream), scalar_gate);
+        hipError_t err = kda::clear_prefill_status(workspace, plan, reinterpret_cast<hipStream_t>(stream));
+        if (err == hipSuccess)
+            err = kda::launch_recurrent_fwd(Dk, in_dtype == KDA_BF16, out_dtype == KDA_BF16, q, k, v, log_alpha, beta,
+                                            S0, nullptr, T, H, static_cast<int>(units), o, S_final,
+                                            reinterpret_cast<hipStream_t>(stream), scalar_gate);
         return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
     }
     kda::PrefillArgs a;
@@ -153,6 +179,7 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
     a.decay_scale = fz.decay_scale;
     a.out_gate = fz.out_gate;
     a.workspace = workspace;
+    a.wait_limit = wait_limit();
     hipError_t err = kda::launch_prefill(a, plan, reinterpret_cast<hipStream_t>(stream));
     return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

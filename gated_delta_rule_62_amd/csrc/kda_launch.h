@@ -11,6 +11,8 @@ namespace kda {
 constexpr int kDefaultChunk = 32;     // chunk length C (tokens) when the caller passes 0
 constexpr int kComputeUnits = 256;    // MI355X
 constexpr int kMinChunksPerSegment = 4;
+constexpr size_t kStatusBytes = 256;  // status word at the start of every prefill workspace
+constexpr int kWaitLimit = 1 << 16;   // polls before a kernel's ordering wait gives up
 // Equal-length batches of at most this many tokens per sequence take the token-by-token
 // kernel (on MI355X it beats a one-chunk pass up to about 7 tokens: the state traffic is the
 // same and the chunk's fixed intra-chunk work is skipped).
@@ -25,10 +27,13 @@ inline bool chunk_supported(int c) { return c == 0 || c == 32 || c == 64; }
 //         carries the segment's transition matrix; a small combine kernel chains
 //         the segment entry states; pass 2 reruns every segment from its true
 //         entry state and writes o and S_final.
-//         With split0, segment 0 needs no summary: its output pass runs on a second
-//         stream beside pass 1 (which then covers segments 1..G-2) and leaves its exit
-//         state as segment 1's entry, so pass 2 covers segments 1..G-1.  Both passes then
-//         fill the chip with one segment more than the plain schedule.
+//         With split0, segment 0 needs no summary: its output pass runs in the same
+//         launch as pass 1 (which then covers segments 1..G-2) and leaves its exit state
+//         as segment 1's entry, so pass 2 covers segments 1..G-1.  Both passes then fill
+//         the chip with one segment more than the plain schedule.
+// Every plan's workspace starts with the call's status word (kStatusBytes reserved): the
+// first kernel of the call clears it, and a workgroup whose bounded ordering wait gave up
+// sets it to 1 (and writes NaN to what it stores from then on).
 // Fused prologue / epilogue of the _fused entry points (flags as in kda_fusion).
 struct Fusion {
     int flags = 0;                     // 1: L2-normalise q, k; 2: beta logits; 4: log_alpha logits
@@ -42,7 +47,7 @@ struct PrefillPlan {
     int chunks = 0;        // chunks per sequence (equal-length case)
     int cps = 0;           // chunks per segment
     bool split0 = false;   // segment 0's output pass runs beside pass 1 (G >= 3)
-    size_t off_phi = 0, off_sloc = 0, off_se = 0, off_order = 0;
+    size_t off_status = 0, off_phi = 0, off_sloc = 0, off_se = 0, off_order = 0;
     size_t workspace_bytes = 0;
 };
 
@@ -61,10 +66,13 @@ struct PrefillArgs {
     int fuse_flags = 0;
     float decay_bias = 0.f, decay_scale = 1.f;
     const void* out_gate = nullptr;   // [B, T, H, D] output-gate logits (in dtype) or nullptr
+    int wait_limit = kWaitLimit;      // polls before an ordering wait gives up
 };
 
 PrefillPlan plan_prefill(int B, int T, int H, int D, int N, bool varlen, int chunk);
 hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan, hipStream_t stream);
+// Clears the status word of a prefill workspace (for calls that run no prefill kernel).
+hipError_t clear_prefill_status(void* workspace, const PrefillPlan& plan, hipStream_t stream);
 
 hipError_t launch_decode(int D, bool in_bf16, bool out_bf16, const void* q, const void* k,
                          const void* v, const void* g, const void* b, const float* S_in,

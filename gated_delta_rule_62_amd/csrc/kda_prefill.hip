@@ -3,9 +3,9 @@
 // Method: the chunkwise parallel form of the fine-grained gated delta rule
 // ("Decoding Hybrid Attention Architectures", intl.cloud.baidu.com article 9569726,
 // section 4; "Technical Analysis and Engineering Practices for Novel Hybrid Linear
-// Attention Architectures", article 9578008, section 3).  Per chunk of C = 64
-// tokens with entry state S (d_k x d_v, fp32) and chunk-local cumulative log-decay
-// b_r = sum_{i<=r} g_i:
+// Attention Architectures", article 9578008, section 3).  Per chunk of C tokens (32 by
+// default, 64 on request) with entry state S (d_k x d_v, fp32) and chunk-local
+// cumulative log-decay b_r = sum_{i<=r} g_i:
 //
 //   A    = StrictTril(Diag(beta) Kbar Ktil^T)           Kbar = K e^{b}, Ktil = K e^{-b}
 //   T    = (I + A)^{-1} Diag(beta)
@@ -35,20 +35,23 @@
 //  * Decay factors are formed relative to the chunk midpoint for the C x C
 //    products (e^{b_r - b_m} and e^{b_m - b_i}), so their exponents stay within
 //    half a chunk's summed decay.
-//  * The (I + A)^{-1} solve is blocked 16 x 16 in fp32: one wave inverts the four
-//    diagonal blocks by substitution, the off-diagonal blocks follow in three
-//    block-row steps.
+//  * The (I + A)^{-1} solve is blocked 16 x 16: the diagonal blocks are inverted by
+//    substitution in fp32 (X_bb = (I + A_bb)^{-1}), and Unew is formed block by block,
+//    Unew_b = X_bb (beta_b R_b - sum_{k<b} A_bk Unew_k), so T itself is never formed.
+//    The 32-token kernel inverts its two diagonal blocks on two producer waves (one
+//    block-row per lane quad); the 64-token kernel inverts its four on one wave.
 //  * Few long sequences (the 64K-token workload has 32 heads): each sequence is
 //    cut into G segments.  Pass 1 runs segments from a zero state and also carries
 //    the segment transition (the identity pushed through the same updates, which is
 //    linear in the state); a combine kernel chains
 //    S_entry(s+1) = Phi(s) S_entry(s) + S_loc(s); pass 2 reruns the segments from
 //    their entry states.  Segment 0 needs no summary: with 32-token chunks its
-//    output pass runs on a second stream beside pass 1 (segments 1..G-2), and pass 2
-//    covers segments 1..G-1.  That fills the chip at the cost of a second pass.
+//    output pass runs in the same launch as the summaries of segments 1..G-2 (its
+//    workgroups take the first compute units), and pass 2 covers segments 1..G-1.
+//    That fills the chip at the cost of a second pass; every kernel of a call runs
+//    on the caller's stream.
 #include <algorithm>
 #include <cmath>
-#include <mutex>
 #include <type_traits>
 
 #include "kda_device.h"
@@ -171,10 +174,11 @@ __device__ __forceinline__ void lds_barrier() {
 // Counters in LDS that order the producer and consumer waves of a workgroup without a
 // workgroup barrier.  A wave publishes with signal_count once its earlier LDS accesses are
 // complete; a wave waits with wait_count until a counter reaches a target.  Global loads in
-// flight are not waited on by either.  A wait is bounded: after 2^16 polls (milliseconds) it
-// marks the workgroup broken and returns, every later wait returns at once, and the kernel
-// poisons the states it writes, so an ordering mistake shows as NaN results, not a stuck
-// workgroup.
+// flight are not waited on by either.  A wait is bounded: after a poll limit (2^16 polls,
+// milliseconds, unless the host asks for fewer) it marks the workgroup broken and returns, and
+// every later wait returns at once.  A broken workgroup writes NaN to every output row and state
+// it stores from then on and sets the call's status word, so an ordering mistake shows as NaN
+// results and a nonzero status, never as a stuck workgroup.
 struct SyncCounters {
     int p1, p2, ready;   // producer waves done with phase 1, phase 2, a whole chunk
     int pt;              // consumer waves done with the P tiles of the chunk being built
@@ -193,14 +197,14 @@ typedef __attribute__((address_space(3))) volatile int lds_vint;
 
 __device__ __forceinline__ int lds_read(const int* p) { return *(const lds_vint*)(p); }
 
-__device__ __forceinline__ void wait_count(const int* c, int target, int* broken) {
+__device__ __forceinline__ void wait_count(const int* c, int target, int* broken, int limit) {
     for (int polls = 0;; ++polls) {
         if (__builtin_amdgcn_readfirstlane(lds_read(c)) >= target) break;
         // the first polls follow each other closely; later ones sleep between reads and
         // look at the broken flag every 64 polls
         if (polls >= 8) {
             if ((polls & 63) == 0 && __builtin_amdgcn_readfirstlane(lds_read(broken))) break;
-            if (polls >= (1 << 16)) {
+            if (polls >= limit) {
                 *(lds_vint*)(broken) = 1;
                 break;
             }
@@ -332,6 +336,8 @@ struct KernelArgs {
     int cps0;       // chunks in segment 0 (cps unless the split schedule lengthens or shortens it)
     int seg0;       // segment of the launch's first workgroup row (equal-length batches)
     int split0;     // 1: segment 0's output pass writes its exit state as segment 1's entry
+    int* status;    // call status word: set to 1 by a workgroup whose ordering wait gave up
+    int wait_limit; // polls before an ordering wait gives up (2^16 unless the host asks for fewer)
     // fused prologue / epilogue (FUSE kernels only)
     int fuse_flags;           // kFuseQK | kFuseBeta | kFuseDecay
     float decay_bias, decay_scale;
@@ -838,11 +844,15 @@ __device__ __forceinline__ float inv_sumsq(const float (&part)[NPW][C], int r) {
     return __builtin_amdgcn_rcpf(t);
 }
 
-template <int D, int MODE>
+// CT: 16-column tiles per consumer wave.  The output pass runs D/32 consumer waves of 32 state
+// columns (CT = 2) on its own, or D/16 waves of 16 (CT = 1) in the launch it shares with the
+// summary pass, which carries [S | Phi] (2D columns) on D/16 waves of 32: there both passes have
+// D/32 producer and D/16 consumer waves, so they fit one workgroup size and register budget.
+template <int D, int MODE, int CT_ = 2>
 struct PCfg {
     static constexpr int C = 32;
     static constexpr int NPW = D / 32;                             // producer waves
-    static constexpr int CT = 2;                                   // 16-column tiles per consumer wave
+    static constexpr int CT = CT_;
     static constexpr int NCW = (MODE == 0 ? D : 2 * D) / (16 * CT);   // consumer waves
     static constexpr int NW = NPW + NCW;
     static constexpr int NT = 64 * NW;
@@ -887,6 +897,9 @@ struct alignas(16) PBuf {
     float fo[K::C];             // scalar gate: e^{b_r - b_m} (scales O rows)
     float em[D];                // e^{b_m}
     float rho[D];               // e^{b_m} of the next chunk times e^{b_n - b_m} (1 after the last)
+    float rn[D];                // e^{b_n - b_m}
+    int tiny[K::NPW];           // per producer wave: some channel's rho is below 2^-100, so the
+                                // consumers apply its two factors one after the other
 };
 
 template <int D, int MODE, bool VLDS>
@@ -912,11 +925,10 @@ struct PSmem {
 //     O = Diag(1/m) (Qbar S + P U'),  S <- Diag(gamma) S + Khat^T U'
 // with the unnormalised Kbar, Ktil, Khat, Qbar, P (U' = Diag(1/n) Unew of the normalised keys),
 // so the producer only adds per-token sums of squares to its decay phase.
-template <int D, typename IN, bool OUT_BF16, int MODE, bool SG = false, bool FUSE = false>
-__global__ __attribute__((amdgpu_flat_work_group_size(PCfg<D, MODE>::NT, PCfg<D, MODE>::NT),
-                          amdgpu_waves_per_eu(PCfg<D, MODE>::WPE, PCfg<D, MODE>::WPE)))
-void pipe_kernel(KernelArgs a) {
-    using K = PCfg<D, MODE>;
+template <int D, typename IN, bool OUT_BF16, int MODE, bool SG, bool FUSE, int CT_>
+__device__ __forceinline__ void pipe_body(const KernelArgs& a, PSmem<D, MODE, std::is_same<IN, BF16>::value>& sm,
+                                          const int block) {
+    using K = PCfg<D, MODE, CT_>;
     constexpr int C = K::C, NPW = K::NPW, CT = K::CT, TPG = K::TPG;
     constexpr int NRT = K::NRT, RT = K::RT, KS = K::KS;
     using ST = typename IN::storage;
@@ -928,9 +940,8 @@ void pipe_kernel(KernelArgs a) {
     constexpr bool EXACT = SG && std::is_same<IN, BF16>::value;
     using Buf = PBuf<D, MODE, VLDS>;
 
-    __shared__ PSmem<D, MODE, VLDS> sm;
-
     const int tid = threadIdx.x, l = tid & 63, g4 = l >> 4, lr = l & 15;
+    const int wl = a.wait_limit;
     // wave index in a scalar register: the producer / consumer split below is a uniform
     // branch, so each side runs its own loop with its own registers
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -943,8 +954,8 @@ void pipe_kernel(KernelArgs a) {
     int n, h, s, c_begin, c_end;
     long t0, t1;
     if (a.cu) {
-        const int rank = blockIdx.x / H;
-        h = blockIdx.x % H;
+        const int rank = block / H;
+        h = block % H;
         n = a.order[rank];
         t0 = a.cu[n];
         t1 = a.cu[n + 1];
@@ -952,8 +963,8 @@ void pipe_kernel(KernelArgs a) {
         c_begin = 0;
         c_end = static_cast<int>((t1 - t0 + C - 1) / C);
     } else {
-        const int unit = blockIdx.x % a.NH;
-        s = a.seg0 + blockIdx.x / a.NH;
+        const int unit = block % a.NH;
+        s = a.seg0 + block / a.NH;
         n = unit / H;
         h = unit % H;
         t0 = static_cast<long>(n) * a.T;
@@ -1072,8 +1083,12 @@ void pipe_kernel(KernelArgs a) {
 #pragma unroll
                 for (int ch = 0; ch < 4; ++ch) {
                     B.em[c4 + ch] = em;
-                    if (prev) prev->rho[c4 + ch] = em * enm[0];
+                    if (prev) {
+                        prev->rho[c4 + ch] = em * enm[0];
+                        prev->rn[c4 + ch] = enm[0];
+                    }
                 }
+                if (prev && l == 0) prev->tiny[w] = em * enm[0] < 0x1p-100f;
             }
             const float en = exp2f_hw(bn - bm);
 #pragma unroll
@@ -1161,12 +1176,21 @@ void pipe_kernel(KernelArgs a) {
             off[ch] -= bm[ch];                     // b_r - b_m = gr + off
         }
         if (tg == 0) {
+            bool tiny = false;
 #pragma unroll
             for (int ch = 0; ch < 4; ++ch) {
                 const float em = exp2f_hw(bm[ch]);
                 B.em[c4 + ch] = em;
-                if (prev) prev->rho[c4 + ch] = em * enm[ch];
+                if (prev) {
+                    const float r = em * enm[ch];
+                    prev->rho[c4 + ch] = r;
+                    prev->rn[c4 + ch] = enm[ch];
+                    tiny |= r < 0x1p-100f;
+                }
             }
+            // lanes 0..7 hold the wave's 32 channels
+            const bool any_tiny = __builtin_amdgcn_ballot_w64(tiny) != 0;
+            if (prev && l == 0) prev->tiny[w] = any_tiny;
         }
 #pragma unroll
         for (int ch = 0; ch < 4; ++ch) enm[ch] = exp2f_hw(bn[ch] - bm[ch]);
@@ -1545,11 +1569,20 @@ void pipe_kernel(KernelArgs a) {
             }
         }
     };
-    // consumer step 3: St <- Diag(rho) (St + Ktil_m^T Unew), and the output rows of the chunk
-    auto consume_update = [&](const Buf& B, int chunk) {
+    // consumer step 3: St <- Diag(rho) (St + Ktil_m^T Unew), and the output rows of the chunk.
+    // rho = e^{b_m'} e^{b_n - b_m} can fall below fp32 range while St + Ktil_m^T Unew holds values
+    // up to e^{(b_m - b_n)}; when some channel's rho is that small (steep decays, a chunk's summed
+    // log-decay below about -87), the two factors are applied one after the other.
+    auto consume_update = [&](const Buf& B, const Buf& next, int chunk, bool last) {
+        int tiny = 0;
+#pragma unroll
+        for (int pw = 0; pw < NPW; ++pw) tiny |= B.tiny[pw];
+        tiny = __builtin_amdgcn_readfirstlane(tiny);
+        // the first factor: rho, or e^{b_n - b_m} when the two are applied one after the other
+        const float* r1 = tiny ? &B.rn[0] : &B.rho[0];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            const f32x4 rh = *reinterpret_cast<const f32x4*>(&B.rho[16 * rt + 4 * g4]);
+            const f32x4 rh = *reinterpret_cast<const f32x4*>(r1 + 16 * rt + 4 * g4);
             const int ao = K::chm(16 * rt + lr, 8 * g4);
             if constexpr (EXACT) {
                 const bf16x8 kh = frag(&B.kt[0][ao]);
@@ -1561,9 +1594,25 @@ void pipe_kernel(KernelArgs a) {
                 for (int ct = 0; ct < CT; ++ct) S[rt][ct] = mfma3(kh, kl, ubh[ct], ubl[ct], S[rt][ct]) * rh;
             }
         }
+        if (tiny && !last) {   // the second factor, e^{b_m} of the next chunk
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const f32x4 r2 = *reinterpret_cast<const f32x4*>(&next.em[16 * rt + 4 * g4]);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) S[rt][ct] *= r2;
+            }
+        }
         if constexpr (MODE == 0) {
             const long ts = t0 + static_cast<long>(chunk) * C;
             const int ntok = static_cast<int>(min(static_cast<long>(C), t1 - ts));
+            // a workgroup whose ordering broke stores NaN rows from here on
+            if (__builtin_amdgcn_readfirstlane(lds_read(broken)) != 0) {
+#pragma unroll
+                for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) Z[rt][ct] = f32x4{__builtin_nanf(""), __builtin_nanf(""),
+                                                                        __builtin_nanf(""), __builtin_nanf("")};
+            }
             // lane (g4, lr) holds 4 consecutive columns of token 16 rt + lr
             const size_t obase = (static_cast<size_t>(ts) * H + h) * D + j0 + 4 * g4;
 #pragma unroll
@@ -1613,10 +1662,10 @@ void pipe_kernel(KernelArgs a) {
         for (int i = 0; i < n_chunks; ++i) {
             const int chunk = c_begin + i;
             Buf& B = sm.buf[chunk & 1];
-            if (i >= 2) wait_count(&sm.sync.done[chunk & 1], K::NCW * (i / 2), broken);
+            if (i >= 2) wait_count(&sm.sync.done[chunk & 1], K::NCW * (i / 2), broken, wl);
             produce_decay(B, chunk, i > 0 ? &sm.buf[(chunk & 1) ^ 1] : nullptr);
             signal_count(&sm.sync.p1);
-            wait_count(&sm.sync.p1, NPW * (i + 1), broken);
+            wait_count(&sm.sync.p1, NPW * (i + 1), broken, wl);
             // The inputs of the next chunk are requested outside the decay phase: k and
             // log_alpha (used first) here, q, v and beta before phase 3, except on the waves
             // that solve the diagonal blocks in phase 3, which request all here.
@@ -1624,10 +1673,10 @@ void pipe_kernel(KernelArgs a) {
             produce_products(B);
             produce_token_scales(B);
             signal_count(&sm.sync.p2);
-            wait_count(&sm.sync.p2, NPW * (i + 1), broken);
+            wait_count(&sm.sync.p2, NPW * (i + 1), broken, wl);
             if (!solver && chunk + 1 < c_end) fetch(chunk + 1, 1);
             produce_inverse(B);
-            wait_count(&sm.sync.pt, K::NCW * (i + 1), broken);
+            wait_count(&sm.sync.pt, K::NCW * (i + 1), broken, wl);
             produce_transpose(B);
             signal_count(&sm.sync.ready);
         }
@@ -1636,16 +1685,17 @@ void pipe_kernel(KernelArgs a) {
             if (tg == 0) {
 #pragma unroll
                 for (int ch = 0; ch < 4; ++ch) sm.buf[(c_end - 1) & 1].rho[c4 + ch] = enm[ch];
+                if (l == 0) sm.buf[(c_end - 1) & 1].tiny[w] = 0;
             }
             signal_count(&sm.sync.p1);
         }
         return;
     }
     if (n_chunks > 0) {
-        wait_count(&sm.sync.p1, NPW, broken);
+        wait_count(&sm.sync.p1, NPW, broken, wl);
         consume_ptiles(sm.buf[c_begin & 1]);
         signal_count(&sm.sync.pt);
-        wait_count(&sm.sync.ready, NPW, broken);
+        wait_count(&sm.sync.ready, NPW, broken, wl);
         const Buf& first = sm.buf[c_begin & 1];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -1658,16 +1708,16 @@ void pipe_kernel(KernelArgs a) {
     for (int i = 0; i < n_chunks; ++i) {
         const int chunk = c_begin + i;
         const Buf& cur = sm.buf[chunk & 1];
-        if (i > 0) wait_count(&sm.sync.ready, NPW * (i + 1), broken);
+        if (i > 0) wait_count(&sm.sync.ready, NPW * (i + 1), broken, wl);
         consume_project(cur, chunk);
         request_gate(chunk);
         consume_solve(cur);
-        wait_count(&sm.sync.p1, NPW * (i + 2), broken);
+        wait_count(&sm.sync.p1, NPW * (i + 2), broken, wl);
         if (i + 1 < n_chunks) {
             consume_ptiles(sm.buf[(chunk & 1) ^ 1]);
             signal_count(&sm.sync.pt);
         }
-        consume_update(cur, chunk);
+        consume_update(cur, sm.buf[(chunk & 1) ^ 1], chunk, i + 1 == n_chunks);
         signal_count(&sm.sync.done[chunk & 1]);
         if (i + 1 < n_chunks) split_state();
     }
@@ -1680,8 +1730,9 @@ void pipe_kernel(KernelArgs a) {
     } else {
         dst = (is_phi ? a.phi : a.sloc) + (static_cast<size_t>(s) * a.NH + unit) * D * D;
     }
+    const bool poison = __builtin_amdgcn_readfirstlane(lds_read(broken)) != 0;
+    if (poison && l == 0 && a.status) *reinterpret_cast<volatile int*>(a.status) = 1;
     if (dst) {
-        const bool poison = __builtin_amdgcn_readfirstlane(lds_read(broken)) != 0;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -1689,6 +1740,41 @@ void pipe_kernel(KernelArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     dst[(16 * rt + 4 * g4 + e) * D + j0 + 16 * ct + lr] = poison ? __builtin_nanf("") : S[rt][ct][e];
+    }
+}
+
+template <int D, typename IN, bool OUT_BF16, int MODE, bool SG = false, bool FUSE = false>
+__global__ __attribute__((amdgpu_flat_work_group_size(PCfg<D, MODE>::NT, PCfg<D, MODE>::NT),
+                          amdgpu_waves_per_eu(PCfg<D, MODE>::WPE, PCfg<D, MODE>::WPE)))
+void pipe_kernel(KernelArgs a) {
+    __shared__ PSmem<D, MODE, std::is_same<IN, BF16>::value> sm;
+    pipe_body<D, IN, OUT_BF16, MODE, SG, FUSE, PCfg<D, MODE>::CT>(a, sm, blockIdx.x);
+}
+
+// Pass 1 of the split schedule in one launch: workgroups [0, NH) run segment 0's output pass
+// from S0 (writing o and, as segment 1's entry state, its exit state) with 16-column consumer
+// waves; the others run the summaries of segments 1..G-2.  Both have D/32 producer and D/16
+// consumer waves, and the launch order puts segment 0's workgroups first.
+template <int D, typename IN, bool OUT_BF16, bool SG = false, bool FUSE = false>
+__global__ __attribute__((amdgpu_flat_work_group_size(PCfg<D, 1>::NT, PCfg<D, 1>::NT),
+                          amdgpu_waves_per_eu(PCfg<D, 1>::WPE, PCfg<D, 1>::WPE)))
+void pipe_pass1_kernel(KernelArgs a) {
+    static_assert(PCfg<D, 0, 1>::NT == PCfg<D, 1>::NT, "both passes need the same workgroup size");
+    constexpr bool VLDS = std::is_same<IN, BF16>::value;
+    __shared__ union Both {
+        PSmem<D, 0, VLDS> out;
+        PSmem<D, 1, VLDS> sum;
+    } sm;
+    const int block = blockIdx.x;
+    if (block < a.NH) {
+        KernelArgs a0 = a;
+        a0.seg0 = 0;
+        a0.split0 = 1;
+        pipe_body<D, IN, OUT_BF16, 0, SG, FUSE, 1>(a0, sm.out, block);
+    } else {
+        KernelArgs a1 = a;
+        a1.seg0 = 1;
+        pipe_body<D, IN, OUT_BF16, 1, SG, FUSE, 2>(a1, sm.sum, block - a.NH);
     }
 }
 
@@ -1771,7 +1857,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     }
 }
 
-// Longest-first order of packed sequences (ties by index); O(N^2), N is small.
+// Longest-first order of packed sequences (ties by index).  Each thread ranks one sequence
+// against all others, O(N) per thread over a grid of N threads; the packed batches this
+// serves hold up to a few thousand sequences.
 __global__ __launch_bounds__(256) void order_kernel(const int32_t* __restrict__ cu, int32_t* __restrict__ order, int N) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= N) return;
@@ -1784,42 +1872,10 @@ __global__ __launch_bounds__(256) void order_kernel(const int32_t* __restrict__ 
     order[rank] = i;
 }
 
-// A second stream per device (default priority) with two events, created on first use and
-// kept until the process ends: segment 0's output pass of the split schedule runs on it.
-struct SideStream {
-    std::mutex mu;
-    hipStream_t stream = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-};
-
-hipError_t side_stream(SideStream*& out) {
-    constexpr int kMaxDevices = 64;
-    static SideStream side[kMaxDevices];
-    static std::mutex init_mu;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-    std::lock_guard<std::mutex> lock(init_mu);
-    SideStream& s = side[dev];
-    if (!s.stream) {
-        hipStream_t st = nullptr;
-        hipEvent_t f = nullptr, j = nullptr;
-        e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&f, hipEventDisableTiming);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&j, hipEventDisableTiming);
-        if (e != hipSuccess) {
-            if (j) (void)hipEventDestroy(j);
-            if (f) (void)hipEventDestroy(f);
-            if (st) (void)hipStreamDestroy(st);
-            return e;
-        }
-        s.fork = f;
-        s.join = j;
-        s.stream = st;
-    }
-    out = &s;
-    return hipSuccess;
+// Clears the call's status word before its kernels run (a fill kernel rather than a memset, so
+// that the call stays free of memset nodes under stream capture).
+__global__ void status_clear_kernel(int* status) {
+    if (threadIdx.x == 0) *status = 0;
 }
 
 template <int D, int C, typename IN, bool OB, bool SG = false, bool FUSE = false>
@@ -1835,77 +1891,70 @@ hipError_t launch_variant(const PrefillArgs& pa, const PrefillPlan& plan, hipStr
     a.split0 = 0;
     a.fuse_flags = pa.fuse_flags; a.decay_bias = pa.decay_bias; a.decay_scale = pa.decay_scale;
     a.out_gate = pa.out_gate;
+    a.wait_limit = pa.wait_limit;
     char* ws = static_cast<char*>(pa.workspace);
+    a.status = reinterpret_cast<int*>(ws + plan.off_status);
     a.order = pa.cu ? reinterpret_cast<const int32_t*>(ws + plan.off_order) : nullptr;
     a.phi = plan.G > 1 ? reinterpret_cast<float*>(ws + plan.off_phi) : nullptr;
     a.sloc = plan.G > 1 ? reinterpret_cast<float*>(ws + plan.off_sloc) : nullptr;
     a.se = plan.G > 1 ? reinterpret_cast<float*>(ws + plan.off_se) : nullptr;
     const int NH = a.NH;
+    hipLaunchKernelGGL(status_clear_kernel, dim3(1), dim3(64), 0, stream, a.status);
     // The 32-token chunk runs the producer/consumer kernel; the 64-token chunk, whose
     // operands do not fit twice in LDS, the single-buffered one.
-    auto pass = [&](int mode, int grid, const KernelArgs& ka, hipStream_t st) {
+    auto pass = [&](int mode, int grid, const KernelArgs& ka) {
         if constexpr (C == 32) {
             if (mode == 0)
-                hipLaunchKernelGGL((pipe_kernel<D, IN, OB, 0, SG, FUSE>), dim3(grid), dim3(PCfg<D, 0>::NT), 0, st, ka);
+                hipLaunchKernelGGL((pipe_kernel<D, IN, OB, 0, SG, FUSE>), dim3(grid), dim3(PCfg<D, 0>::NT), 0, stream, ka);
             else
-                hipLaunchKernelGGL((pipe_kernel<D, IN, OB, 1, SG, FUSE>), dim3(grid), dim3(PCfg<D, 1>::NT), 0, st, ka);
+                hipLaunchKernelGGL((pipe_kernel<D, IN, OB, 1, SG, FUSE>), dim3(grid), dim3(PCfg<D, 1>::NT), 0, stream, ka);
         } else {
             if (mode == 0)
-                hipLaunchKernelGGL((chunk_kernel<D, C, IN, OB, 0>), dim3(grid), dim3(Cfg<D, C, 0>::NT), 0, st, ka);
+                hipLaunchKernelGGL((chunk_kernel<D, C, IN, OB, 0>), dim3(grid), dim3(Cfg<D, C, 0>::NT), 0, stream, ka);
             else
-                hipLaunchKernelGGL((chunk_kernel<D, C, IN, OB, 1>), dim3(grid), dim3(Cfg<D, C, 1>::NT), 0, st, ka);
+                hipLaunchKernelGGL((chunk_kernel<D, C, IN, OB, 1>), dim3(grid), dim3(Cfg<D, C, 1>::NT), 0, stream, ka);
         }
     };
     if (pa.cu) {
         hipLaunchKernelGGL(order_kernel, dim3((pa.N + 255) / 256), dim3(256), 0, stream, pa.cu,
                            reinterpret_cast<int32_t*>(ws + plan.off_order), pa.N);
-        pass(0, NH, a, stream);
+        pass(0, NH, a);
         return hipGetLastError();
     }
-    if (plan.G > 1 && plan.split0) {
-        // Segment 0's output pass runs beside the summaries of segments 1..G-2, so it may be as long
-        // as the ratio of a summary chunk's cost to an output chunk's (measured on MI355X: plain
-        // 1.18, scalar gate 1.08, fused output pass with its gate 0.95); the other segments share
-        // the rest equally.  Only for segments of 64 chunks or more, where the per-chunk costs
-        // outweigh the fixed ones of a segment (state loads and stores, the pipeline's fill).
-        // G, and with it the workspace, is unchanged.
-        constexpr double kSeg0Ratio = FUSE ? 0.95 : (SG ? 1.08 : 1.18);
-        const int cps = static_cast<int>(std::ceil(plan.chunks / (plan.G - 1 + kSeg0Ratio)));
-        const int cps0 = plan.chunks - (plan.G - 1) * cps;
-        if (plan.cps >= 64 && cps0 >= 1) {
-            a.cps = cps;
-            a.cps0 = cps0;
-        }
-        SideStream* side = nullptr;
-        if (side_stream(side) == hipSuccess) {
-            // The fork / join events are shared by every call on this device: enqueue the
-            // schedule under the lock so that no other call records them in between.
-            std::lock_guard<std::mutex> lock(side->mu);
-            hipError_t e = hipEventRecord(side->fork, stream);
-            if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
-            if (e != hipSuccess) return e;
-            KernelArgs a0 = a;   // segment 0's output pass, exit state -> segment 1's entry
-            a0.split0 = 1;
-            pass(0, NH, a0, side->stream);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-            if ((e = hipEventRecord(side->join, side->stream)) != hipSuccess) return e;
-            KernelArgs a1 = a;   // summaries of segments 1..G-2
-            a1.seg0 = 1;
-            if (plan.G > 2) pass(1, NH * (plan.G - 2), a1, stream);
-            if ((e = hipStreamWaitEvent(stream, side->join, 0)) != hipSuccess) return e;
+    if constexpr (C == 32) {
+        if (plan.G > 1 && plan.split0) {
+            // Segment 0's output pass runs beside the summaries of segments 1..G-2, so it may be as
+            // long as the ratio of a summary chunk's cost to an output chunk's (measured on MI355X:
+            // plain 1.18, scalar gate 1.08, fused output pass with its gate 0.95); the other segments
+            // share the rest equally.  Only for segments of 64 chunks or more, where the per-chunk
+            // costs outweigh the fixed ones of a segment (state loads and stores, the pipeline's
+            // fill).  G, and with it the workspace, is unchanged.
+            constexpr double kSeg0Ratio = FUSE ? 0.95 : (SG ? 1.08 : 1.18);
+            const int cps = static_cast<int>(std::ceil(plan.chunks / (plan.G - 1 + kSeg0Ratio)));
+            const int cps0 = plan.chunks - (plan.G - 1) * cps;
+            if (plan.cps >= 64 && cps0 >= 1) {
+                a.cps = cps;
+                a.cps0 = cps0;
+            }
+            // one launch: segment 0's output pass (exit state -> segment 1's entry) and the
+            // summaries of segments 1..G-2
+            hipLaunchKernelGGL((pipe_pass1_kernel<D, IN, OB, SG, FUSE>), dim3(NH * (plan.G - 1)), dim3(PCfg<D, 1>::NT),
+                               0, stream, a);
             if (plan.G > 2)
                 hipLaunchKernelGGL(combine_kernel<D>, dim3(NH, D / 16), dim3(256), 0, stream, a.se, a.phi, a.sloc,
                                    a.se, NH, plan.G, 2);
-            pass(0, NH * (plan.G - 1), a1, stream);   // output passes of segments 1..G-1
+            KernelArgs a1 = a;   // output passes of segments 1..G-1
+            a1.seg0 = 1;
+            pass(0, NH * (plan.G - 1), a1);
             return hipGetLastError();
         }
     }
     if (plan.G > 1) {
-        pass(1, NH * (plan.G - 1), a, stream);
+        pass(1, NH * (plan.G - 1), a);
         hipLaunchKernelGGL(combine_kernel<D>, dim3(NH, D / 16), dim3(256), 0, stream, pa.S0, a.phi, a.sloc, a.se,
                            NH, plan.G, 1);
     }
-    pass(0, NH * plan.G, a, stream);
+    pass(0, NH * plan.G, a);
     return hipGetLastError();
 }
 
@@ -1916,10 +1965,12 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 PrefillPlan plan_prefill(int B, int T, int H, int D, int N, bool varlen, int chunk) {
     PrefillPlan p;
     p.chunk = chunk == 0 ? kDefaultChunk : chunk;
+    // Every plan starts with the call's status word (256 bytes reserved).
+    p.off_status = 0;
     if (varlen) {
         p.G = 1;
-        p.off_order = 0;
-        p.workspace_bytes = align256(static_cast<size_t>(N) * sizeof(int32_t));
+        p.off_order = kStatusBytes;
+        p.workspace_bytes = kStatusBytes + align256(static_cast<size_t>(N) * sizeof(int32_t));
         return p;
     }
     (void)B;
@@ -1947,14 +1998,21 @@ PrefillPlan plan_prefill(int B, int T, int H, int D, int N, bool varlen, int chu
     p.cps = p.chunks > 0 ? (p.chunks + G - 1) / G : 0;
     p.G = p.cps > 0 ? (p.chunks + p.cps - 1) / p.cps : 1;
     p.split0 = split && p.G >= 3;
+    p.workspace_bytes = kStatusBytes;
     if (p.G > 1) {
         const size_t mat = static_cast<size_t>(units) * (p.G - 1) * D * D * sizeof(float);
-        p.off_phi = 0;
-        p.off_sloc = align256(mat);
-        p.off_se = 2 * align256(mat);
-        p.workspace_bytes = 3 * align256(mat);
+        p.off_phi = kStatusBytes;
+        p.off_sloc = kStatusBytes + align256(mat);
+        p.off_se = kStatusBytes + 2 * align256(mat);
+        p.workspace_bytes = kStatusBytes + 3 * align256(mat);
     }
     return p;
+}
+
+hipError_t clear_prefill_status(void* workspace, const PrefillPlan& plan, hipStream_t stream) {
+    hipLaunchKernelGGL(status_clear_kernel, dim3(1), dim3(64), 0, stream,
+                       reinterpret_cast<int*>(static_cast<char*>(workspace) + plan.off_status));
+    return hipGetLastError();
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan, hipStream_t stream) {

@@ -103,6 +103,24 @@ def _stream_ptr(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _keep_for(stream, *ts):
+    """Tensors this wrapper allocated are used by work on ``stream``: when that is not the
+    current stream, tell the caching allocator, so that their memory is not handed to other
+    work before the library's kernels on ``stream`` are done with it."""
+    if stream is None or stream == torch.cuda.current_stream():
+        return
+    for t in ts:
+        if t is not None:
+            t.record_stream(stream)
+
+
+def workspace_status(workspace) -> int:
+    """The status word a prefill call left at the start of its workspace (waits for the device):
+    0 when every ordering wait inside the kernels completed, nonzero when some workgroup gave
+    up a wait and wrote NaN to what it stored from then on."""
+    return int(workspace[:4].view(torch.int32).item())
+
+
 def _check_dev(*ts):
     for t in ts:
         if t is not None and (not t.is_cuda or not t.is_contiguous()):
@@ -123,16 +141,19 @@ def kda_chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, out_dty
     Dv = v.shape[-1]
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
     out_dtype = q.dtype if out_dtype is None else out_dtype
-    if o is None:
+    o_new, sf_new = o is None, S_final is None and want_final
+    if o_new:
         o = torch.empty((B, T, H, Dv), dtype=out_dtype, device=q.device)
-    if S_final is None and want_final:
+    if sf_new:
         S_final = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
     if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
         raise TypeError("cu_seqlens must be int32")
     _check_dev(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_final, workspace)
     ws_need = kda_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, N, cu_seqlens is not None, chunk)
+    own = [o if o_new else None, S_final if sf_new else None]
     if workspace is None and ws_need > 0:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
+        own.append(workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = getattr(load_library(), _fn)(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
@@ -140,6 +161,7 @@ def kda_chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, out_dty
         _ptr(o), _ptr(S_final), _ptr(workspace), ws_bytes, _stream_ptr(stream))
     if st != KDA_OK:
         raise KDAError(st, _fn)
+    _keep_for(stream, *own)
     return o, S_final
 
 
@@ -150,7 +172,8 @@ def kda_recurrent_step(q, k, v, log_alpha, beta, S_in, S_out=None, *, out_dtype=
     N, H, Dk = q.shape
     Dv = v.shape[-1]
     out_dtype = q.dtype if out_dtype is None else out_dtype
-    if o is None:
+    o_new = o is None
+    if o_new:
         o = torch.empty((N, H, Dv), dtype=out_dtype, device=q.device)
     if S_out is None:
         S_out = S_in
@@ -160,6 +183,7 @@ def kda_recurrent_step(q, k, v, log_alpha, beta, S_in, S_out=None, *, out_dtype=
         N, H, Dk, Dv, _dtype_code(q.dtype), _dtype_code(o.dtype), _ptr(o), _stream_ptr(stream))
     if st != KDA_OK:
         raise KDAError(st, _fn)
+    _keep_for(stream, o if o_new else None)
     return o, S_out
 
 
@@ -171,9 +195,10 @@ def kda_recurrent_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, out
     Dv = v.shape[-1]
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
     out_dtype = q.dtype if out_dtype is None else out_dtype
-    if o is None:
+    o_new, sf_new = o is None, S_final is None and want_final
+    if o_new:
         o = torch.empty((B, T, H, Dv), dtype=out_dtype, device=q.device)
-    if S_final is None and want_final:
+    if sf_new:
         S_final = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
     if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
         raise TypeError("cu_seqlens must be int32")
@@ -184,6 +209,7 @@ def kda_recurrent_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, out
         _stream_ptr(stream))
     if st != KDA_OK:
         raise KDAError(st, _fn)
+    _keep_for(stream, o if o_new else None, S_final if sf_new else None)
     return o, S_final
 
 
@@ -220,14 +246,17 @@ def kda_chunk_fwd_fused(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, q
     Dv = v.shape[-1]
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
     out_dtype = q.dtype if out_dtype is None else out_dtype
-    if o is None:
+    o_new, sf_new = o is None, S_final is None and want_final
+    if o_new:
         o = torch.empty((B, T, H, Dv), dtype=out_dtype, device=q.device)
-    if S_final is None and want_final:
+    if sf_new:
         S_final = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
     _check_dev(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_final, workspace, out_gate)
     ws_need = kda_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, N, cu_seqlens is not None, chunk)
+    own = [o if o_new else None, S_final if sf_new else None]
     if workspace is None and ws_need > 0:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
+        own.append(workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     f = _fusion(qk_l2norm, beta_logits, decay_logits, out_gate)
     st = load_library().kda_chunk_fwd_fused(
@@ -236,6 +265,7 @@ def kda_chunk_fwd_fused(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, q
         _ptr(o), _ptr(S_final), _ptr(workspace), ws_bytes, ctypes.byref(f), _stream_ptr(stream))
     if st != KDA_OK:
         raise KDAError(st, "kda_chunk_fwd_fused")
+    _keep_for(stream, *own)
     return o, S_final
 
 
@@ -245,7 +275,8 @@ def kda_recurrent_step_fused(q, k, v, log_alpha, beta, S_in, S_out=None, *, qk_l
     N, H, Dk = q.shape
     Dv = v.shape[-1]
     out_dtype = q.dtype if out_dtype is None else out_dtype
-    if o is None:
+    o_new = o is None
+    if o_new:
         o = torch.empty((N, H, Dv), dtype=out_dtype, device=q.device)
     if S_out is None:
         S_out = S_in
@@ -256,6 +287,7 @@ def kda_recurrent_step_fused(q, k, v, log_alpha, beta, S_in, S_out=None, *, qk_l
         N, H, Dk, Dv, _dtype_code(q.dtype), _dtype_code(o.dtype), _ptr(o), ctypes.byref(f), _stream_ptr(stream))
     if st != KDA_OK:
         raise KDAError(st, "kda_recurrent_step_fused")
+    _keep_for(stream, o if o_new else None)
     return o, S_out
 
 
@@ -280,16 +312,20 @@ def kda_chunk_bwd(q, k, v, log_alpha, beta, d_o, S0=None, cu_seqlens=None, dS_fi
         raise TypeError("d_o must have the inputs' dtype")
     g = dict(grads or {})
     dev = q.device
+    own = []
     for name, shape in (("dq", q.shape), ("dk", q.shape), ("dv", v.shape), ("dlog_alpha", log_alpha.shape),
                         ("dbeta", beta.shape)):
         if g.get(name) is None:
             g[name] = torch.empty(shape, dtype=grad_dtype, device=dev)
+            own.append(g[name])
     if g.get("dS0") is None and want_dS0:
         g["dS0"] = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev)
+        own.append(g["dS0"])
     _check_dev(q, k, v, log_alpha, beta, d_o, S0, cu_seqlens, dS_final, workspace, *g.values())
     ws_need = kda_chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, N, cu_seqlens is not None, chunk)
     if workspace is None and ws_need > 0:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+        own.append(workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = getattr(load_library(), _fn)(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
@@ -298,6 +334,7 @@ def kda_chunk_bwd(q, k, v, log_alpha, beta, d_o, S0=None, cu_seqlens=None, dS_fi
         _ptr(workspace), ws_bytes, _stream_ptr(stream))
     if st != KDA_OK:
         raise KDAError(st, _fn)
+    _keep_for(stream, *own)
     return g
 
 

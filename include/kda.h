@@ -25,17 +25,19 @@
  *  - Tensor arguments are DEVICE pointers owned by the caller, contiguous,
  *    row-major (last index fastest) and 16-byte aligned.
  *  - Nothing allocates: scratch memory is a caller-provided workspace.
- *  - Work is enqueued on `stream` (NULL = the default stream); no call
- *    synchronises.  Errors detectable from the arguments are returned before any
- *    HIP call; a failed launch returns KDA_ERR_HIP.  Faults inside kernels show
- *    up at the caller's next synchronisation.
+ *  - All work is enqueued on `stream` (NULL = the default stream), and only there:
+ *    the library creates no stream or event of its own, and no call synchronises.
+ *    Errors detectable from the arguments are returned before any HIP call; a
+ *    failed launch returns KDA_ERR_HIP.  Faults inside kernels show up at the
+ *    caller's next synchronisation.
  *  - Preconditions that live in device memory are documented, not checked:
  *    cu_seqlens starts at 0, never decreases and ends at T; inputs are finite;
  *    log_alpha <= 0; beta in [0, 1].  Within one chunk, the summed log-decay of
  *    any channel must stay above -160 (the decay factors of a chunk are formed
  *    around its midpoint in fp32).
  *  - Outputs are bitwise deterministic for identical inputs (no atomics).
- *  - Library functions keep no mutable global state and are thread-safe.
+ *  - Library functions keep no mutable global state and are thread-safe; calls
+ *    that share a workspace must be ordered (one stream, or events).
  */
 #ifndef KDA_H
 #define KDA_H
@@ -65,7 +67,16 @@ const char* kda_status_string(kda_status s);
 
 /*
  * Workspace bytes kda_chunk_fwd needs for these sizes (same arguments, same
- * meaning).  has_cu_seqlens is 0 or 1.  Returns 0 for unsupported sizes.
+ * meaning).  has_cu_seqlens is 0 or 1.  Returns 0 for unsupported sizes, and at
+ * least 256 otherwise.
+ *
+ * Layout.  The first 4 bytes of every prefill workspace are the call's status
+ * word, an int32 on the device: the call's first kernel sets it to 0, and a
+ * workgroup whose bounded ordering wait inside the kernels gave up (a wait that
+ * polls an on-chip counter up to a fixed limit instead of forever) sets it to 1
+ * and writes NaN to every output row and state it stores from then on.  Read it
+ * after the call's work has completed: 0 means every wait completed.  The rest of
+ * the workspace is private scratch (segment summaries, the packed-sequence order).
  */
 size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int num_seqs,
                                      int has_cu_seqlens, int chunk);
@@ -84,20 +95,17 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int nu
  *   chunk           : chunk length in tokens: 32 or 64, or 0 for the default (32)
  *   o               : [B, T, H, Dv]   out_dtype (bf16 is round-to-nearest-even)
  *   S_final         : [N, H, Dk, Dv]  fp32, or NULL to skip
- *   workspace       : device scratch of workspace_bytes >= the query above
- *                     (may be NULL when the query returns 0)
+ *   workspace       : device scratch of workspace_bytes >= the query above, not
+ *                     overlapping any other argument; its first word receives the
+ *                     call's status (see the query)
  *
  * Supported: Dk == Dv in {64, 128}; in_dtype, out_dtype in {KDA_F32, KDA_BF16}.
  * A sequence of length 0 gets S_final = S0 (or zeros).  T == 0 or N == 0 only
  * writes S_final.  Inputs must not overlap outputs.  The result does not depend
  * on the chunk size beyond rounding.  Equal-length batches (cu_seqlens NULL) with
  * T <= 4 are evaluated token by token, as kda_recurrent_fwd does.
- * Streams: all work is ordered after what is already enqueued on `stream` and
- * before what is enqueued on it after the call.  For few long sequences at chunk
- * 32 part of it runs on a second stream that the library creates on the device
- * on first use (default priority, kept until the process ends), joined back to
- * `stream` by events; the enqueue is serialised by a lock, so calls from several
- * host threads are safe.
+ * Streams: every kernel runs on `stream`, ordered after what is already enqueued
+ * on it and before what is enqueued on it after the call.
  */
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
                          const void* beta, const float* S0, const int32_t* cu_seqlens,

@@ -8,8 +8,9 @@
  * Source of the recurrence: "Decoding Hybrid Attention Architectures"
  * (intl.cloud.baidu.com article 9569726), section 3.4, the fine-grained gated
  * delta rule S_t = (I - beta k k^T) Diag(a_t) S_{t-1} + beta (write), and section
- * 3.2 for the reading of the delta update as "proportional to the difference
- * between the new value and the stored value".  The same rule appears as item 4
+ * 3.2 for the delta form of the update: the write along key k is scaled by the
+ * error v - S^T k between the new value and what the state returns for k.  The
+ * same rule appears as item 4
  * of section 2 of "Technical Analysis and Engineering Practices for Novel Hybrid
  * Linear Attention Architectures" (article 9578008).
  *

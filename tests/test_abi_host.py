@@ -48,17 +48,18 @@ def test_status_strings(lib):
 
 def test_workspace_query_plans(lib):
     q = kda.kda_chunk_fwd_workspace_bytes
+    st = 256   # every plan starts with the call's 256-byte status block
     # long context, 32 heads -> 3 matrices per unit and segment gap.  1024 chunks of 64 tokens
     # are cut into 8 segments (one workgroup per compute unit in each pass); 2048 chunks of 32
     # into 9, since segment 0's output pass runs beside the summaries of segments 1..7.
-    assert q(1, 65536, 32, 128, 128, 1, False) == 3 * 32 * 8 * 128 * 128 * 4
-    assert q(1, 65536, 32, 128, 128, 1, False, chunk=64) == 3 * 32 * 7 * 128 * 128 * 4
+    assert q(1, 65536, 32, 128, 128, 1, False) == st + 3 * 32 * 8 * 128 * 128 * 4
+    assert q(1, 65536, 32, 128, 128, 1, False, chunk=64) == st + 3 * 32 * 7 * 128 * 128 * 4
     # training shape, 64 units: 5 segments of 32-token chunks (summaries of 1..3 beside 0)
-    assert q(4, 4096, 16, 128, 128, 4, False) == 3 * 64 * 4 * 128 * 128 * 4
-    # enough units to fill the chip: single pass, no workspace
-    assert q(64, 4096, 32, 128, 128, 64, False) == 0
-    # packed sequences: an int32 order table (rounded to 256 bytes)
-    assert q(1, 1000, 32, 128, 128, 64, True) == 256
+    assert q(4, 4096, 16, 128, 128, 4, False) == st + 3 * 64 * 4 * 128 * 128 * 4
+    # enough units to fill the chip: single pass, only the status block
+    assert q(64, 4096, 32, 128, 128, 64, False) == st
+    # packed sequences: the status block and an int32 order table (rounded to 256 bytes)
+    assert q(1, 1000, 32, 128, 128, 64, True) == st + 256
     # unsupported sizes report 0
     assert q(1, 64, 2, 96, 96, 1, False) == 0
     assert q(1, 64, 2, 128, 128, 1, False, chunk=16) == 0
@@ -87,6 +88,13 @@ def test_prefill_argument_errors(lib):
     assert call_fwd(lib, T=-1) == kda.KDA_ERR_INVALID_ARGUMENT
     # segmented plan needs a workspace
     assert call_fwd(lib, T=65536, H=32) == kda.KDA_ERR_WORKSPACE_TOO_SMALL
+    # every plan holds the call's status word: a workspace is always required
+    assert call_fwd(lib) == kda.KDA_ERR_WORKSPACE_TOO_SMALL
+    assert call_fwd(lib, ws=None, ws_bytes=256) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call_fwd(lib, ws=FAKE_MIS, ws_bytes=256) == kda.KDA_ERR_INVALID_ARGUMENT
+    # the workspace must not overlap an input or an output
+    assert call_fwd(lib, ws=FAKE, ws_bytes=256) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call_fwd(lib, ws=ctypes.c_void_p(2 << 40), ws_bytes=256) == kda.KDA_ERR_INVALID_ARGUMENT
     # N == 0 sequences: nothing to do, no HIP call
     assert call_fwd(lib, B=0, N=0, T=0) == kda.KDA_OK
 

@@ -91,7 +91,7 @@ def test_segmented_two_pass_path(chunk):
     segments (segment summaries, combine, rerun)."""
     kda = _kda()
     plan_ws = kda.kda_chunk_fwd_workspace_bytes(1, 1000, 2, 128, 128, 1, False, chunk)
-    assert plan_ws > 0, "expected the segmented path for 2 units and 16 or more chunks"
+    assert plan_ws > 256, "expected the segmented path for 2 units and 16 or more chunks"
     d = inputs.make_prefill(W[2], seed=203, B=1, T=1000, H=2, s0=True)
     check(d, "segmented slow-decay", chunk=chunk)
     d = inputs.make_prefill(W[1], seed=204, B=2, T=777, H=3, s0=True)
@@ -103,8 +103,8 @@ def test_segment_schedule_with_three_segments():
     pass beside the summary of segment 1, then the output passes of segments 1 and 2, with
     a shorter last segment), and with 64-token chunks the plain two-segment schedule."""
     kda = _kda()
-    assert kda.kda_chunk_fwd_workspace_bytes(2, 500, 64, 64, 64, 2, False, 32) == 3 * 128 * 2 * 64 * 64 * 4
-    assert kda.kda_chunk_fwd_workspace_bytes(2, 500, 64, 64, 64, 2, False, 64) == 3 * 128 * 1 * 64 * 64 * 4
+    assert kda.kda_chunk_fwd_workspace_bytes(2, 500, 64, 64, 64, 2, False, 32) == 256 + 3 * 128 * 2 * 64 * 64 * 4
+    assert kda.kda_chunk_fwd_workspace_bytes(2, 500, 64, 64, 64, 2, False, 64) == 256 + 3 * 128 * 1 * 64 * 64 * 4
     d = inputs.make_prefill(W[1], seed=205, B=2, T=500, H=64, D=64, s0=True, mix=True)
     check(d, "three segments", chunk=32)
     check(d, "two segments, 64-token chunks", chunk=64)

@@ -1,6 +1,6 @@
 """Prefill parity over a sweep of shapes that reach every schedule the planner picks:
 one pass, the plain two-segment schedule, and split schedules of 3 to 26 segments
-(segment 0's output pass on a second stream beside the other summaries, lengthened when
+(segment 0's output pass in the same launch as the other summaries, lengthened when
 segments are long) with ragged last segments and chunks; both chunk lengths, both head sizes, fp32 and bf16 inputs,
 the fast-decay mixture and packed batches.  Each case is compared with the fp64
 oracle on the same seeded inputs.  Pages: "Decoding Hybrid Attention Architectures"
@@ -68,8 +68,8 @@ def test_prefill_schedule_sweep(case):
 
 
 def test_two_calls_on_two_streams_interleave():
-    """Two segmented calls enqueued on two streams at once share the library's second stream
-    (its fork and join events are taken under a lock); both results must match one call alone."""
+    """Two segmented calls enqueued on two streams at once, each running all of its kernels on
+    its own stream; both results must match one call alone."""
     kda = _kda()
     d1 = inputs.make_prefill(W[1], seed=401, B=1, T=1500, H=3, D=64, s0=True)
     d2 = inputs.make_prefill(W[1], seed=402, B=1, T=1200, H=5, D=64, s0=True, mix=True)
