@@ -9,6 +9,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "kda.h"
 #include "kda_launch.h"
@@ -52,6 +53,7 @@ extern "C" const char* kda_status_string(kda_status s) {
         case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
         case KDA_ERR_WORKSPACE_TOO_SMALL: return "KDA_ERR_WORKSPACE_TOO_SMALL";
         case KDA_ERR_HIP: return "KDA_ERR_HIP";
+        case KDA_ERR_SCRATCH_LIMIT: return "KDA_ERR_SCRATCH_LIMIT";
     }
     return "KDA_ERR_UNKNOWN";
 }
@@ -92,7 +94,7 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
                           const float* S0, const int32_t* cu_seqlens, int B, int T, int H, int Dk, int Dv,
                           int num_seqs, int chunk, kda_dtype in_dtype, kda_dtype out_dtype, void* o, float* S_final,
                           void* workspace, size_t workspace_bytes, kda_stream_t stream, bool scalar_gate,
-                          const kda_fusion* fusion = nullptr) {
+                          const kda_fusion* fusion = nullptr, bool check_only = false) {
     if (B < 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || num_seqs < 0) return KDA_ERR_INVALID_ARGUMENT;
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_UNSUPPORTED;
     if (!head_ok(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
@@ -137,7 +139,7 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
     if (overlap(S0, n_s, S_final, n_s) || overlap(S0, n_s, o, n_o) || overlap(o, n_o, S_final, n_s))
         return KDA_ERR_INVALID_ARGUMENT;
 
-    if (num_seqs == 0) return KDA_OK;
+    if (num_seqs == 0 || check_only) return KDA_OK;
     kda::PrefillPlan plan = kda::plan_prefill(B, T, H, Dk, num_seqs, cu_seqlens != nullptr, chunk);
     if (workspace_bytes < plan.workspace_bytes) return KDA_ERR_WORKSPACE_TOO_SMALL;
     if (!workspace || !aligned16(workspace)) return KDA_ERR_INVALID_ARGUMENT;
@@ -276,6 +278,68 @@ extern "C" kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
                                     void* workspace, size_t workspace_bytes, kda_stream_t stream) {
     return chunk_fwd_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, B, T, H, Dk, Dv, num_seqs, chunk, in_dtype,
                           out_dtype, o, S_final, workspace, workspace_bytes, stream, false);
+}
+
+// ---------------------------------------------------------------- no-allocation prefill
+// The scratch of kda_chunk_fwd_noalloc: a file-scope device array, one instance per GPU the
+// library's code object is loaded on.  Host code never passes the array's name to a kernel (on
+// the host it is only a stand-in for the symbol); it passes the device address that
+// hipGetSymbolAddress returns for the GPU, looked up once per device and kept below.
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};   // device address of `scratch` on each GPU, once looked up
+
+// The device address of this GPU's scratch array (the GPU of `stream`, or the current one for
+// the null stream), looking it up with that GPU current on the first call for it.
+hipError_t scratch_address(hipStream_t stream, void** out) {
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* log_alpha,
+                                            const void* beta, const float* S0, const int32_t* cu_seqlens,
+                                            int B, int T, int H, int Dk, int Dv, int num_seqs, int chunk,
+                                            kda_dtype in_dtype, kda_dtype out_dtype, void* o, float* S_final,
+                                            kda_stream_t stream) {
+    // sizes the scratch cannot hold are rejected before any HIP call
+    if (B >= 0 && T >= 0 && H > 0 && num_seqs > 0 && head_ok(Dk, Dv) && kda::chunk_supported(chunk)) {
+        const kda::PrefillPlan plan = kda::plan_prefill(B, T, H, Dk, num_seqs, cu_seqlens != nullptr, chunk);
+        if (plan.workspace_bytes > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_SCRATCH_LIMIT;
+    }
+    // everything the arguments alone decide is checked before the scratch lookup
+    const kda_status pre = chunk_fwd_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, B, T, H, Dk, Dv, num_seqs,
+                                          chunk, in_dtype, out_dtype, o, S_final, nullptr, 0, stream, false,
+                                          nullptr, /*check_only=*/true);
+    if (pre != KDA_OK || num_seqs == 0) return pre;
+    void* ws = nullptr;
+    if (scratch_address(reinterpret_cast<hipStream_t>(stream), &ws) != hipSuccess) return KDA_ERR_HIP;
+    return chunk_fwd_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, B, T, H, Dk, Dv, num_seqs, chunk, in_dtype,
+                          out_dtype, o, S_final, ws, KDA_NOALLOC_SCRATCH_BYTES, stream, false);
 }
 
 extern "C" kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const void* log_alpha,

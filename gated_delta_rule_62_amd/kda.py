@@ -15,14 +15,16 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkda.so")
 
-KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE_TOO_SMALL, KDA_ERR_HIP = range(5)
+(KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE_TOO_SMALL, KDA_ERR_HIP,
+ KDA_ERR_SCRATCH_LIMIT) = range(6)
+NOALLOC_SCRATCH_BYTES = 64 << 20   # KDA_NOALLOC_SCRATCH_BYTES
 KDA_F32, KDA_BF16 = 0, 1
 CHUNK = 0          # library default chunk length (32 tokens); 32 and 64 are built
 
 EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_step",
             "kda_recurrent_fwd", "gdn_chunk_fwd", "gdn_recurrent_step", "gdn_recurrent_fwd",
             "kda_chunk_fwd_fused", "kda_recurrent_step_fused", "kda_chunk_bwd_workspace_bytes",
-            "kda_chunk_bwd", "gdn_chunk_bwd")
+            "kda_chunk_bwd", "gdn_chunk_bwd", "kda_chunk_fwd_noalloc")
 KDA_FUSE_QK_L2NORM, KDA_FUSE_BETA_SIGMOID, KDA_FUSE_DECAY_LOGSIGMOID = 1, 2, 4
 
 
@@ -55,6 +57,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd_workspace_bytes.restype = sz
     lib.kda_chunk_fwd.argtypes = [vp] * 7 + [i32] * 7 + [i32, i32] + [vp, vp] + [vp, sz, vp]
     lib.kda_chunk_fwd.restype = i32
+    lib.kda_chunk_fwd_noalloc.argtypes = [vp] * 7 + [i32] * 7 + [i32, i32] + [vp, vp] + [vp]
+    lib.kda_chunk_fwd_noalloc.restype = i32
     lib.kda_recurrent_step.argtypes = [vp] * 7 + [i32] * 4 + [i32, i32] + [vp, vp]
     lib.kda_recurrent_step.restype = i32
     lib.kda_recurrent_fwd.argtypes = [vp] * 7 + [i32] * 6 + [i32, i32] + [vp, vp, vp]
@@ -162,6 +166,25 @@ def kda_chunk_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, out_dty
     if st != KDA_OK:
         raise KDAError(st, _fn)
     _keep_for(stream, *own)
+    return o, S_final
+
+
+def kda_chunk_fwd_noalloc(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, o, S_final=None,
+                          chunk=CHUNK, stream=None):
+    """kda_chunk_fwd through the entry point that allocates nothing: the outputs are the
+    caller's (o required, S_final optional) and the scratch is the library's fixed array."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    _check_dev(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_final)
+    st = load_library().kda_chunk_fwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
+        B, T, H, Dk, Dv, N, chunk, _dtype_code(q.dtype), _dtype_code(o.dtype),
+        _ptr(o), _ptr(S_final), _stream_ptr(stream))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_chunk_fwd_noalloc")
     return o, S_final
 
 

@@ -57,7 +57,9 @@ typedef enum {
     KDA_ERR_INVALID_ARGUMENT = 1,     /* null pointer, bad size, misalignment, aliasing */
     KDA_ERR_UNSUPPORTED = 2,          /* head size, chunk size or dtype not built */
     KDA_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes < kda_chunk_fwd_workspace_bytes() */
-    KDA_ERR_HIP = 4                   /* a HIP launch or API call failed */
+    KDA_ERR_HIP = 4,                  /* a HIP launch or API call failed */
+    KDA_ERR_SCRATCH_LIMIT = 5         /* kda_chunk_fwd_noalloc: these sizes need more scratch
+                                         than the library's fixed array holds */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
@@ -113,6 +115,33 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
                          kda_dtype in_dtype, kda_dtype out_dtype,
                          void* o, float* S_final,
                          void* workspace, size_t workspace_bytes, kda_stream_t stream);
+
+/*
+ * kda_chunk_fwd_noalloc -- kda_chunk_fwd for callers that cannot allocate device
+ * memory: code being captured into a HIP graph, tight serving loops, and harnesses
+ * that forbid hipMalloc.  The arguments are kda_chunk_fwd's without the workspace;
+ * the call's scratch (status word, packed-sequence order, segment summaries) comes
+ * from a fixed array of KDA_NOALLOC_SCRATCH_BYTES in the library's own device memory,
+ * one per GPU, held until the process ends.  The call allocates nothing.
+ *
+ * Returns KDA_ERR_SCRATCH_LIMIT, before any HIP call, when
+ * kda_chunk_fwd_workspace_bytes() for these sizes exceeds KDA_NOALLOC_SCRATCH_BYTES
+ * (no equal-length plan at Dk = Dv <= 128 does: their segment summaries stay under
+ * 48 MiB; packed batches of more than about 16 million sequences do).  Every call on
+ * one GPU shares that GPU's array, which keeps the last call's contents (each call
+ * clears what must start at zero itself): calls that overlap in time on one GPU --
+ * on different streams, or from host threads whose streams are not ordered -- race
+ * and give wrong results.  Calls ordered on one stream are safe.  The status word of
+ * kda_chunk_fwd is kept in the array and is not readable here; a broken ordering
+ * still shows as NaN outputs.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* log_alpha,
+                                 const void* beta, const float* S0, const int32_t* cu_seqlens,
+                                 int B, int T, int H, int Dk, int Dv, int num_seqs, int chunk,
+                                 kda_dtype in_dtype, kda_dtype out_dtype,
+                                 void* o, float* S_final, kda_stream_t stream);
 
 /*
  * kda_recurrent_step -- decode: one token for each of N independent sequences.

@@ -41,9 +41,30 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    names = [kda.status_string(i) for i in range(5)]
+    names = [kda.status_string(i) for i in range(6)]
     assert names == ["KDA_OK", "KDA_ERR_INVALID_ARGUMENT", "KDA_ERR_UNSUPPORTED",
-                     "KDA_ERR_WORKSPACE_TOO_SMALL", "KDA_ERR_HIP"]
+                     "KDA_ERR_WORKSPACE_TOO_SMALL", "KDA_ERR_HIP", "KDA_ERR_SCRATCH_LIMIT"]
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
+    """The no-allocation prefill checks its fixed scratch limit (and the arguments) before any
+    HIP call: a packed batch whose order table alone exceeds the limit is rejected."""
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, S0=None, cu=ctypes.c_void_p(3 << 40), B=1, T=0,
+                 H=2, Dk=128, Dv=128, N=20_000_000, chunk=0, in_dt=kda.KDA_BF16, out_dt=kda.KDA_BF16,
+                 o=ctypes.c_void_p(2 << 40), Sf=None)
+        a.update(kw)
+        return lib.kda_chunk_fwd_noalloc(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["cu"], a["B"],
+                                         a["T"], a["H"], a["Dk"], a["Dv"], a["N"], a["chunk"], a["in_dt"],
+                                         a["out_dt"], a["o"], a["Sf"], None)
+    assert kda.kda_chunk_fwd_workspace_bytes(1, 0, 2, 128, 128, 20_000_000, True) > kda.NOALLOC_SCRATCH_BYTES
+    assert call() == kda.KDA_ERR_SCRATCH_LIMIT
+    # every equal-length plan fits: the segment summaries of the long-context shape are 48 MiB
+    assert kda.kda_chunk_fwd_workspace_bytes(1, 1 << 20, 32, 128, 128, 1, False) <= kda.NOALLOC_SCRATCH_BYTES
+    # argument errors are still reported first
+    assert call(N=1, cu=None, T=64, Dk=96, Dv=96) == kda.KDA_ERR_UNSUPPORTED
+    assert call(N=1, cu=None, T=64, q=None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call(N=0, cu=None, B=0, T=0) == kda.KDA_OK
 
 
 def test_workspace_query_plans(lib):
