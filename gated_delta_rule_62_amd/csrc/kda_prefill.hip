@@ -823,15 +823,17 @@ __device__ __forceinline__ float log2_sigmoid(float x) {
     return fminf(x, 0.f) * kLog2e - __builtin_amdgcn_logf(1.f + exp2f_hw(-fabsf(x) * kLog2e));
 }
 
-// Sum over the 8 lanes of an aligned lane octet (DPP butterflies; every lane gets the sum).
-__device__ __forceinline__ float sum8(float x) {
+// Sum over the N (4 or 8) lanes of an aligned lane group (DPP butterflies; every lane gets the sum).
+template <int N>
+__device__ __forceinline__ float sum_lanes(float x) {
+    static_assert(N == 4 || N == 8, "lane groups of 4 or 8");
     auto dpp = [](float v, auto ctrl) {
         return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), decltype(ctrl)::value,
                                                                    0xf, 0xf, true));
     };
     x += dpp(x, std::integral_constant<int, 0xB1>{});    // quad_perm [1, 0, 3, 2]
     x += dpp(x, std::integral_constant<int, 0x4E>{});    // quad_perm [2, 3, 0, 1]
-    x += dpp(x, std::integral_constant<int, 0x141>{});   // row_half_mirror
+    if constexpr (N == 8) x += dpp(x, std::integral_constant<int, 0x141>{});   // row_half_mirror
     return x;
 }
 
@@ -848,16 +850,23 @@ __device__ __forceinline__ float inv_sumsq(const float (&part)[NPW][C], int r) {
 // columns (CT = 2) on its own, or D/16 waves of 16 (CT = 1) in the launch it shares with the
 // summary pass, which carries [S | Phi] (2D columns) on D/16 waves of 32: there both passes have
 // D/32 producer and D/16 consumer waves, so they fit one workgroup size and register budget.
-template <int D, int MODE, int CT_ = 2>
+// NPW: producer waves.  Producer wave w owns QPW channel quads (4 QPW key channels) over all C
+// tokens: lane l takes quad QPW w + l % QPW and TPG consecutive tokens of token group l / QPW, so
+// the decay prefix over tokens stays inside the wave.  D/32 waves give 8 quads x 4 tokens per
+// lane; D/16 waves 4 quads x 2 tokens.
+template <int D, int MODE, int CT_ = 2, int NPW_ = D / 32>
 struct PCfg {
     static constexpr int C = 32;
-    static constexpr int NPW = D / 32;                             // producer waves
+    static constexpr int NPW = NPW_;                               // producer waves
+    static constexpr int QPW = D / (4 * NPW);                      // channel quads per producer wave
+    static constexpr int TGN = 64 / QPW;                           // token groups per producer wave
     static constexpr int CT = CT_;
     static constexpr int NCW = (MODE == 0 ? D : 2 * D) / (16 * CT);   // consumer waves
     static constexpr int NW = NPW + NCW;
     static constexpr int NT = 64 * NW;
     static constexpr int WPE = (NW + 3) / 4;                       // waves per SIMD
-    static constexpr int TPG = C / 8;                              // tokens per producer thread
+    static constexpr int TPG = C / TGN;                            // tokens per producer thread
+    static_assert(TPG == 2 || TPG == 4, "producer lanes hold 2 or 4 tokens");
     static constexpr int NRT = C / 16, RT = D / 16, KS = D / 32;
     // LDS planes carry no padding; 16-byte slots are XOR-swizzled per row instead, so that the
     // MFMA fragment reads (16 rows x 4 slots per instruction) and the producers' 8-byte writes
@@ -874,9 +883,9 @@ struct PCfg {
 };
 
 // VLDS: bf16 inputs, whose V tiles the producer stages in LDS for the consumers.
-template <int D, int MODE, bool VLDS>
+template <int D, int MODE, bool VLDS, int NPW_ = D / 32>
 struct alignas(16) PBuf {
-    using K = PCfg<D, MODE>;
+    using K = PCfg<D, MODE, 2, NPW_>;
     static constexpr int NQ = MODE == 0 ? 2 : 1, QE = MODE == 0 ? K::C * D : 8;
     static constexpr int PE = MODE == 0 ? K::C * K::C : 8;
     u16 kb[2][K::C * D];        // Kbar_m = K e^{b - b_m}     [token][kperm(channel)]
@@ -898,13 +907,20 @@ struct alignas(16) PBuf {
     float em[D];                // e^{b_m}
     float rho[D];               // e^{b_m} of the next chunk times e^{b_n - b_m} (1 after the last)
     float rn[D];                // e^{b_n - b_m}
-    int tiny[K::NPW];           // per producer wave: some channel's rho is below 2^-100, so the
-                                // consumers apply its two factors one after the other
+    int tiny[K::NPW];           // scalar gate, per producer wave: some channel's rho is below
+                                // 2^-100, so the consumers apply its two factors one after the other
+    // Per-channel decay: the carried state X holds S~ = Diag(F) X, and F is folded into the
+    // chunk's decayed operands instead of scaling the state every chunk.  When F would leave the
+    // range the operands need, the producer resets it to 1 and the consumers rescale X by
+    // f1 f2 f3 (three factors, each inside fp32 range) before this chunk.
+    float f1[D], f2[D], f3[D];
+    int renorm[K::NPW];         // per producer wave: some channel of the wave is rescaled
+    float fin1[D], fin2[D];     // after the last chunk: S = Diag(fin1 fin2) X
 };
 
-template <int D, int MODE, bool VLDS>
+template <int D, int MODE, bool VLDS, int NPW_ = D / 32>
 struct PSmem {
-    PBuf<D, MODE, VLDS> buf[2];
+    PBuf<D, MODE, VLDS, NPW_> buf[2];
     float a[2][16][20];         // diagonal 16x16 blocks of A (fp32), producer-private
     SyncCounters sync;
 };
@@ -925,11 +941,12 @@ struct PSmem {
 //     O = Diag(1/m) (Qbar S + P U'),  S <- Diag(gamma) S + Khat^T U'
 // with the unnormalised Kbar, Ktil, Khat, Qbar, P (U' = Diag(1/n) Unew of the normalised keys),
 // so the producer only adds per-token sums of squares to its decay phase.
-template <int D, typename IN, bool OUT_BF16, int MODE, bool SG, bool FUSE, int CT_>
-__device__ __forceinline__ void pipe_body(const KernelArgs& a, PSmem<D, MODE, std::is_same<IN, BF16>::value>& sm,
+template <int D, typename IN, bool OUT_BF16, int MODE, bool SG, bool FUSE, int CT_, int NPW_ = D / 32>
+__device__ __forceinline__ void pipe_body(const KernelArgs& a,
+                                          PSmem<D, MODE, std::is_same<IN, BF16>::value, NPW_>& sm,
                                           const int block) {
-    using K = PCfg<D, MODE, CT_>;
-    constexpr int C = K::C, NPW = K::NPW, CT = K::CT, TPG = K::TPG;
+    using K = PCfg<D, MODE, CT_, NPW_>;
+    constexpr int C = K::C, NPW = K::NPW, CT = K::CT, TPG = K::TPG, QPW = K::QPW, TGN = K::TGN;
     constexpr int NRT = K::NRT, RT = K::RT, KS = K::KS;
     using ST = typename IN::storage;
     using R = Raw<IN>;
@@ -938,7 +955,7 @@ __device__ __forceinline__ void pipe_body(const KernelArgs& a, PSmem<D, MODE, st
     constexpr bool VLDS = std::is_same<IN, BF16>::value;
     // scalar gate with bf16 inputs: K and Q are exact bf16 MFMA operands (no low parts)
     constexpr bool EXACT = SG && std::is_same<IN, BF16>::value;
-    using Buf = PBuf<D, MODE, VLDS>;
+    using Buf = PBuf<D, MODE, VLDS, NPW_>;
 
     const int tid = threadIdx.x, l = tid & 63, g4 = l >> 4, lr = l & 15;
     const int wl = a.wait_limit;
@@ -981,7 +998,7 @@ __device__ __forceinline__ void pipe_body(const KernelArgs& a, PSmem<D, MODE, st
     const bool is_phi = MODE == 1 && ci >= D / (16 * CT);
     const int j0 = 16 * CT * (ci % (D / (16 * CT)));
     // producer identity: channel quad cq, token group tg (TPG tokens)
-    const int cq = 8 * w + (l & 7), tg = l >> 3, c4 = 4 * cq;
+    const int cq = QPW * w + (l % QPW), tg = l / QPW, c4 = 4 * cq;
 
     if constexpr (MODE == 0) {
         // P's strictly-upper 16x16 tile inside the 32-deep step is read but never written.
@@ -1000,6 +1017,8 @@ __device__ __forceinline__ void pipe_body(const KernelArgs& a, PSmem<D, MODE, st
     elem pb = 0;
     uint2 kth[TPG], ktl[TPG];   // split Ktil_m words, kept from phase 1 for Ktil_m^T in phase 3
     float enm[4] = {1.f, 1.f, 1.f, 1.f};   // e^{b_n - b_m} of the chunk last produced
+    // per-channel decay: log2 F of the chunk last produced and log2 e^{b_n - b_m} of it
+    float lf[4] = {0.f, 0.f, 0.f, 0.f}, lrn[4] = {0.f, 0.f, 0.f, 0.f};
     // part 0: k and log_alpha; part 1: q, v and beta; -1: everything.  The two parts are requested
     // in different phases so the chip's memory requests are spread over the chunk loop.
     auto fetch = [&](int chunk, int part) {
@@ -1038,13 +1057,13 @@ __device__ __forceinline__ void pipe_body(const KernelArgs& a, PSmem<D, MODE, st
 #pragma unroll
             for (int ch = 0; ch < 4; ++ch) {
                 const unsigned sel = (ch & 1) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-                for (int gq = 0; gq < TPG / 4; ++gq) {
-                    const int t = 4 * gq;
-                    const uint32_t w0 = ch < 2 ? pvq[t].x : pvq[t].y, w1 = ch < 2 ? pvq[t + 1].x : pvq[t + 1].y;
-                    const uint32_t w2 = ch < 2 ? pvq[t + 2].x : pvq[t + 2].y, w3 = ch < 2 ? pvq[t + 3].x : pvq[t + 3].y;
-                    *reinterpret_cast<uint2*>(&B.vt[K::chm(c4 + ch, tg * TPG + t)]) =
-                        uint2{__builtin_amdgcn_perm(w1, w0, sel), __builtin_amdgcn_perm(w3, w2, sel)};
+                auto word = [&](int t) { return ch < 2 ? pvq[t].x : pvq[t].y; };
+                if constexpr (TPG == 4) {
+                    *reinterpret_cast<uint2*>(&B.vt[K::chm(c4 + ch, tg * TPG)]) =
+                        uint2{__builtin_amdgcn_perm(word(1), word(0), sel), __builtin_amdgcn_perm(word(3), word(2), sel)};
+                } else {
+                    *reinterpret_cast<uint32_t*>(&B.vt[K::chm(c4 + ch, tg * TPG)]) =
+                        __builtin_amdgcn_perm(word(1), word(0), sel);
                 }
             }
         }
@@ -1072,11 +1091,11 @@ __device__ __forceinline__ void pipe_body(const KernelArgs& a, PSmem<D, MODE, st
             for (int i = 0; i < TPG; ++i) gs[i] = IN::to_f32(pgs[i]) * kLog2e + (i ? gs[i - 1] : 0.f);
             float incl = gs[TPG - 1];
 #pragma unroll
-            for (int dd = 8; dd < 64; dd <<= 1) {
+            for (int dd = QPW; dd < 64; dd <<= 1) {
                 const float y = __shfl_up(incl, dd);
                 incl += l >= dd ? y : 0.f;
             }
-            const float bm = __shfl(incl, 24), bn = __shfl(incl, 56);
+            const float bm = __shfl(incl, (TGN / 2 - 1) * QPW), bn = __shfl(incl, (TGN - 1) * QPW);
             const float off = incl - gs[TPG - 1] - bm;   // b_r - b_m = gs + off
             if (tg == 0) {
                 const float em = exp2f_hw(bm);
@@ -1093,7 +1112,7 @@ __device__ __forceinline__ void pipe_body(const KernelArgs& a, PSmem<D, MODE, st
             const float en = exp2f_hw(bn - bm);
 #pragma unroll
             for (int ch = 0; ch < 4; ++ch) enm[ch] = en;
-            if (w == 0 && (l & 7) == 0) {
+            if (w == 0 && (l % QPW) == 0) {
 #pragma unroll
                 for (int i = 0; i < TPG; ++i) {
                     const float b = gs[i] + off;
@@ -1152,9 +1171,9 @@ __device__ __forceinline__ void pipe_body(const KernelArgs& a, PSmem<D, MODE, st
                     sk += R::get(pk[i], ch) * R::get(pk[i], ch);
                     if constexpr (MODE == 0) sq += R::get(pq[i], ch) * R::get(pq[i], ch);
                 }
-                sk = sum8(sk);
-                if constexpr (MODE == 0) sq = sum8(sq);
-                if ((l & 7) == 0) {
+                sk = sum_lanes<QPW>(sk);
+                if constexpr (MODE == 0) sq = sum_lanes<QPW>(sq);
+                if ((l % QPW) == 0) {
                     B.nk[w][tg * TPG + i] = sk;
                     if constexpr (MODE == 0) B.nq[w][tg * TPG + i] = sq;
                 }
@@ -1163,37 +1182,55 @@ __device__ __forceinline__ void pipe_body(const KernelArgs& a, PSmem<D, MODE, st
         float off[4], bm[4], bn[4];
 #pragma unroll
         for (int ch = 0; ch < 4; ++ch) {
-            // inclusive prefix over the wave's 8 token groups (lanes 8 apart)
+            // inclusive prefix over the wave's TGN token groups (lanes QPW apart)
             float incl = gr[TPG - 1][ch];
 #pragma unroll
-            for (int dd = 8; dd < 64; dd <<= 1) {
+            for (int dd = QPW; dd < 64; dd <<= 1) {
                 const float y = __shfl_up(incl, dd);
                 incl += l >= dd ? y : 0.f;
             }
             off[ch] = incl - gr[TPG - 1][ch];
-            bm[ch] = __shfl(incl, 24 + (l & 7));   // through token C/2 - 1
-            bn[ch] = __shfl(incl, 56 + (l & 7));   // through the chunk's last token
+            bm[ch] = __shfl(incl, (TGN / 2 - 1) * QPW + (l % QPW));   // through token C/2 - 1
+            bn[ch] = __shfl(incl, (TGN - 1) * QPW + (l % QPW));       // through the chunk's last token
             off[ch] -= bm[ch];                     // b_r - b_m = gr + off
         }
-        if (tg == 0) {
-            bool tiny = false;
+        // F of this chunk (log2): the previous chunk's F times its rho = e^{b_m} e^{b_n - b_m} of the
+        // previous chunk and this one.  The decayed operands take exponents (b_r - b_m) + log2 F
+        // (K, Q) and -(b_r - b_m) - log2 F (Ktil), kept within +-100 (the carried state X = S~ / F
+        // then stays below 2^100 |S~|); b_r - b_m spans [b_n - b_m, -b_m] and log2 F <= 0, so F is
+        // reset to 1 (and X rescaled) when log2 F < -100 + |b_n - b_m|.  The first chunk starts from
+        // F = 1 (the consumers scale the entry state by e^{b_m}).
+        bool rescale = false;
+        float f1v[4] = {1.f, 1.f, 1.f, 1.f}, f2v[4] = {1.f, 1.f, 1.f, 1.f}, f3v[4] = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
-            for (int ch = 0; ch < 4; ++ch) {
-                const float em = exp2f_hw(bm[ch]);
-                B.em[c4 + ch] = em;
-                if (prev) {
-                    const float r = em * enm[ch];
-                    prev->rho[c4 + ch] = r;
-                    prev->rn[c4 + ch] = enm[ch];
-                    tiny |= r < 0x1p-100f;
+        for (int ch = 0; ch < 4; ++ch) {
+            float lnew = 0.f;
+            if (prev) {
+                lnew = lf[ch] + lrn[ch] + bm[ch];
+                if (lnew < -100.f + fabsf(bn[ch] - bm[ch])) {
+                    f1v[ch] = exp2f_hw(lf[ch]);
+                    f2v[ch] = exp2f_hw(lrn[ch]);
+                    f3v[ch] = exp2f_hw(bm[ch]);
+                    rescale = true;
+                    lnew = 0.f;
                 }
             }
-            // lanes 0..7 hold the wave's 32 channels
-            const bool any_tiny = __builtin_amdgcn_ballot_w64(tiny) != 0;
-            if (prev && l == 0) prev->tiny[w] = any_tiny;
+            lf[ch] = lnew;
+            lrn[ch] = bn[ch] - bm[ch];
+            off[ch] += lnew;                       // (b_r - b_m) + log2 F = gr + off
         }
+        // every lane holds its channels' values; lanes with tg == 0 cover the wave's channels once
+        const bool any_rescale = __builtin_amdgcn_ballot_w64(rescale) != 0;
+        if (tg == 0) {   // every wave writes its factors (1 where unchanged): any wave's reset rescales all rows
 #pragma unroll
-        for (int ch = 0; ch < 4; ++ch) enm[ch] = exp2f_hw(bn[ch] - bm[ch]);
+            for (int ch = 0; ch < 4; ++ch) {
+                B.em[c4 + ch] = exp2f_hw(bm[ch]);
+                B.f1[c4 + ch] = f1v[ch];
+                B.f2[c4 + ch] = f2v[ch];
+                B.f3[c4 + ch] = f3v[ch];
+            }
+            if (l == 0) B.renorm[w] = any_rescale;
+        }
 #pragma unroll
         for (int i = 0; i < TPG; ++i) {
             const int r = tg * TPG + i;
@@ -1326,21 +1363,18 @@ __device__ __forceinline__ void pipe_body(const KernelArgs& a, PSmem<D, MODE, st
             const int c = c4 + ch;
             // channel ch of token i sits in the low (even ch) or high (odd ch) half of word ch / 2
             const unsigned sel = (ch & 1) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-            for (int gq = 0; gq < TPG / 4; ++gq) {
-                uint2 hi, lo;
-                const int t = 4 * gq;
-                const uint32_t h0 = (ch < 2) ? kth[t].x : kth[t].y, h1 = (ch < 2) ? kth[t + 1].x : kth[t + 1].y;
-                const uint32_t h2 = (ch < 2) ? kth[t + 2].x : kth[t + 2].y, h3 = (ch < 2) ? kth[t + 3].x : kth[t + 3].y;
-                const uint32_t l0 = (ch < 2) ? ktl[t].x : ktl[t].y, l1 = (ch < 2) ? ktl[t + 1].x : ktl[t + 1].y;
-                const uint32_t l2 = (ch < 2) ? ktl[t + 2].x : ktl[t + 2].y, l3 = (ch < 2) ? ktl[t + 3].x : ktl[t + 3].y;
-                hi.x = __builtin_amdgcn_perm(h1, h0, sel);
-                hi.y = __builtin_amdgcn_perm(h3, h2, sel);
-                lo.x = __builtin_amdgcn_perm(l1, l0, sel);
-                lo.y = __builtin_amdgcn_perm(l3, l2, sel);
-                const int idx = K::chm(c, kperm(tg * TPG + t));
-                *reinterpret_cast<uint2*>(&B.kt[0][idx]) = hi;
-                if constexpr (!EXACT) *reinterpret_cast<uint2*>(&B.kt[1][idx]) = lo;
+            auto hw = [&](int t) { return (ch < 2) ? kth[t].x : kth[t].y; };
+            auto lw = [&](int t) { return (ch < 2) ? ktl[t].x : ktl[t].y; };
+            const int idx = K::chm(c, kperm(tg * TPG));
+            if constexpr (TPG == 4) {
+                *reinterpret_cast<uint2*>(&B.kt[0][idx]) =
+                    uint2{__builtin_amdgcn_perm(hw(1), hw(0), sel), __builtin_amdgcn_perm(hw(3), hw(2), sel)};
+                if constexpr (!EXACT)
+                    *reinterpret_cast<uint2*>(&B.kt[1][idx]) =
+                        uint2{__builtin_amdgcn_perm(lw(1), lw(0), sel), __builtin_amdgcn_perm(lw(3), lw(2), sel)};
+            } else {
+                *reinterpret_cast<uint32_t*>(&B.kt[0][idx]) = __builtin_amdgcn_perm(hw(1), hw(0), sel);
+                if constexpr (!EXACT) *reinterpret_cast<uint32_t*>(&B.kt[1][idx]) = __builtin_amdgcn_perm(lw(1), lw(0), sel);
             }
         }
     };
@@ -1404,7 +1438,7 @@ __device__ __forceinline__ void pipe_body(const KernelArgs& a, PSmem<D, MODE, st
     // leaves S itself).  The output pass splits St for the coming chunk right after the update,
     // so step 1 holds only MFMA work beside the producer's vector-ALU work; the summary pass,
     // with twice the columns per compute unit, has no registers to spare for it.
-    constexpr bool PRESPLIT = MODE == 0;
+    constexpr bool PRESPLIT = MODE == 0 && NPW == D / 32;
     bf16x8 sph[PRESPLIT ? KS : 1][CT], spl[PRESPLIT ? KS : 1][CT];
     auto split_state = [&]() {
         if constexpr (PRESPLIT) {
@@ -1569,37 +1603,64 @@ __device__ __forceinline__ void pipe_body(const KernelArgs& a, PSmem<D, MODE, st
             }
         }
     };
-    // consumer step 3: St <- Diag(rho) (St + Ktil_m^T Unew), and the output rows of the chunk.
-    // rho = e^{b_m'} e^{b_n - b_m} can fall below fp32 range while St + Ktil_m^T Unew holds values
-    // up to e^{(b_m - b_n)}; when some channel's rho is that small (steep decays, a chunk's summed
-    // log-decay below about -87), the two factors are applied one after the other.
+    // consumer step 3: the state update and the output rows of the chunk.  Per-channel decay: the
+    // carried state takes X <- X + Ktil^T Unew with F folded into Ktil by the producer (no per-chunk
+    // scaling), and is rescaled only when the next chunk resets F.  Scalar gate: St <- rho (St +
+    // K^T U'), rho = e^{b_m'} e^{b_n - b_m}, applied as two factors when it falls below fp32 range
+    // (steep decays, a chunk's summed log-decay below about -87).
     auto consume_update = [&](const Buf& B, const Buf& next, int chunk, bool last) {
-        int tiny = 0;
+        if constexpr (SG) {
+            int tiny = 0;
 #pragma unroll
-        for (int pw = 0; pw < NPW; ++pw) tiny |= B.tiny[pw];
-        tiny = __builtin_amdgcn_readfirstlane(tiny);
-        // the first factor: rho, or e^{b_n - b_m} when the two are applied one after the other
-        const float* r1 = tiny ? &B.rn[0] : &B.rho[0];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const f32x4 rh = *reinterpret_cast<const f32x4*>(r1 + 16 * rt + 4 * g4);
-            const int ao = K::chm(16 * rt + lr, 8 * g4);
-            if constexpr (EXACT) {
-                const bf16x8 kh = frag(&B.kt[0][ao]);
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) S[rt][ct] = mfma(kh, ubh[ct], mfma(kh, ubl[ct], S[rt][ct])) * rh;
-            } else {
-                const bf16x8 kh = frag(&B.kt[0][ao]), kl = frag(&B.kt[1][ao]);
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) S[rt][ct] = mfma3(kh, kl, ubh[ct], ubl[ct], S[rt][ct]) * rh;
-            }
-        }
-        if (tiny && !last) {   // the second factor, e^{b_m} of the next chunk
+            for (int pw = 0; pw < NPW; ++pw) tiny |= B.tiny[pw];
+            tiny = __builtin_amdgcn_readfirstlane(tiny);
+            // the first factor: rho, or e^{b_n - b_m} when the two are applied one after the other
+            const float* r1 = tiny ? &B.rn[0] : &B.rho[0];
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
-                const f32x4 r2 = *reinterpret_cast<const f32x4*>(&next.em[16 * rt + 4 * g4]);
+                const f32x4 rh = *reinterpret_cast<const f32x4*>(r1 + 16 * rt + 4 * g4);
+                const int ao = K::chm(16 * rt + lr, 8 * g4);
+                if constexpr (EXACT) {
+                    const bf16x8 kh = frag(&B.kt[0][ao]);
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct) S[rt][ct] *= r2;
+                    for (int ct = 0; ct < CT; ++ct) S[rt][ct] = mfma(kh, ubh[ct], mfma(kh, ubl[ct], S[rt][ct])) * rh;
+                } else {
+                    const bf16x8 kh = frag(&B.kt[0][ao]), kl = frag(&B.kt[1][ao]);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) S[rt][ct] = mfma3(kh, kl, ubh[ct], ubl[ct], S[rt][ct]) * rh;
+                }
+            }
+            if (tiny && !last) {   // the second factor, e^{b_m} of the next chunk
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    const f32x4 r2 = *reinterpret_cast<const f32x4*>(&next.em[16 * rt + 4 * g4]);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) S[rt][ct] *= r2;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const int ao = K::chm(16 * rt + lr, 8 * g4);
+                const bf16x8 kh = frag(&B.kt[0][ao]), kl = frag(&B.kt[1][ao]);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) S[rt][ct] = mfma3(kh, kl, ubh[ct], ubl[ct], S[rt][ct]);
+            }
+            if (!last) {
+                int rs = 0;
+#pragma unroll
+                for (int pw = 0; pw < NPW; ++pw) rs |= next.renorm[pw];
+                if (__builtin_amdgcn_readfirstlane(rs)) {   // the next chunk resets F
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) {
+                        const int o = 16 * rt + 4 * g4;
+                        const f32x4 a1 = *reinterpret_cast<const f32x4*>(&next.f1[o]);
+                        const f32x4 a2 = *reinterpret_cast<const f32x4*>(&next.f2[o]);
+                        const f32x4 a3 = *reinterpret_cast<const f32x4*>(&next.f3[o]);
+#pragma unroll
+                        for (int ct = 0; ct < CT; ++ct) S[rt][ct] = ((S[rt][ct] * a1) * a2) * a3;
+                    }
+                }
             }
         }
         if constexpr (MODE == 0) {
@@ -1683,9 +1744,19 @@ __device__ __forceinline__ void pipe_body(const KernelArgs& a, PSmem<D, MODE, st
         if (n_chunks > 0) {
             // rho of the last chunk (no next midpoint): e^{b_n - b_m}, which leaves S itself
             if (tg == 0) {
+                Buf& lb = sm.buf[(c_end - 1) & 1];
+                if constexpr (SG) {
 #pragma unroll
-                for (int ch = 0; ch < 4; ++ch) sm.buf[(c_end - 1) & 1].rho[c4 + ch] = enm[ch];
-                if (l == 0) sm.buf[(c_end - 1) & 1].tiny[w] = 0;
+                    for (int ch = 0; ch < 4; ++ch) lb.rho[c4 + ch] = enm[ch];
+                    if (l == 0) lb.tiny[w] = 0;
+                } else {
+                    // S = Diag(F e^{b_n - b_m}) X after the last chunk
+#pragma unroll
+                    for (int ch = 0; ch < 4; ++ch) {
+                        lb.fin1[c4 + ch] = exp2f_hw(lf[ch]);
+                        lb.fin2[c4 + ch] = exp2f_hw(lrn[ch]);
+                    }
+                }
             }
             signal_count(&sm.sync.p1);
         }
@@ -1723,6 +1794,18 @@ __device__ __forceinline__ void pipe_body(const KernelArgs& a, PSmem<D, MODE, st
     }
 
     // ---------------------------------------------------------------- exit state
+    if constexpr (!SG) {
+        if (n_chunks > 0) {   // S = Diag(F e^{b_n - b_m}) X after the last chunk
+            const Buf& lb = sm.buf[(c_end - 1) & 1];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const f32x4 a1 = *reinterpret_cast<const f32x4*>(&lb.fin1[16 * rt + 4 * g4]);
+                const f32x4 a2 = *reinterpret_cast<const f32x4*>(&lb.fin2[16 * rt + 4 * g4]);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) S[rt][ct] = (S[rt][ct] * a1) * a2;
+            }
+        }
+    }
     float* dst = nullptr;
     if constexpr (MODE == 0) {
         if ((a.cu || s == a.G - 1) && a.S_final) dst = a.S_final + ubase;
