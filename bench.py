@@ -309,8 +309,10 @@ def main():
     del o
     prefill_workloads = {}
 
-    def other_prefill(key, w, C, label, in_bytes=2, out_bytes=2):
+    def other_prefill(key, w, C, label, in_bytes=2, out_bytes=2, as_packed=False):
         xw = inputs.device_prefill(w)
+        if as_packed:   # the equal-length batch passed as packed sequences (cu_seqlens)
+            xw["cu_seqlens"] = torch.arange(0, xw["B"] * xw["T"] + 1, xw["T"], dtype=torch.int32, device="cuda")
         Bw, Tw, Hw, dw, Nw = xw["B"], xw["T"], xw["H"], xw["D"], xw["N"]
         odt = torch.bfloat16 if out_bytes == 2 else torch.float32
         ow = torch.empty((Bw, Tw, Hw, dw), dtype=odt, device="cuda")
@@ -324,8 +326,11 @@ def main():
         t = timed_calls(torch, run, stream, max(3, args.warmup // 2), args.steps)
         line = prefill_line(label, Bw * Tw, Hw, dw, Nw, xw["S0"] is not None, C, t, in_bytes, out_bytes)
         line["config"] = {"workload": w.name, "B": Bw, "T": Tw, "H": Hw, "d_k": dw, "d_v": dw, "chunk": C,
-                          "sequences": Nw, "in_dtype": w.dtype, "out_dtype": "bf16" if out_bytes == 2 else "fp32"}
-        if not args.no_cpu_baseline:
+                          "sequences": Nw, "in_dtype": w.dtype, "out_dtype": "bf16" if out_bytes == 2 else "fp32",
+                          "packed": xw["cu_seqlens"] is not None}
+        if as_packed:
+            line["cpu_baseline"] = "the headline line's (same batch)"
+        elif not args.no_cpu_baseline:
             line["cpu_baseline"] = cpu_baseline_batch(torch, xw)
         prefill_workloads[key] = line
         del xw, ow, Sw, wsw
@@ -340,6 +345,9 @@ def main():
     other_prefill("varlen_packed", inputs.WORKLOADS[4], 32,
                   "packed varlen prefill: 64 sequences U{512..16384} (525,197 tokens), H=32, d=128, bf16, "
                   "per-element decay mixture, chunk 32")
+    other_prefill("long_context_packed", inputs.WORKLOADS[2], 32,
+                  "long-context prefill passed as one packed sequence (cu_seqlens = [0, 65536]): B=1, "
+                  "T=65536, H=32, d=128, bf16, S0 != 0, chunk 32", as_packed=True)
     o = torch.empty((B, T, H, d), dtype=torch.bfloat16, device="cuda")
 
     # ------------------------------------------------------------------ decode
@@ -399,11 +407,37 @@ def main():
     ef1.record(stream)
     torch.cuda.synchronize()
     fused_ms = ef0.elapsed_time(ef1) / args.steps
+
+    # The same work unfused: the prologue and the output gate as separate elementwise passes over
+    # HBM (torch's kernels, bf16 in and out) around the plain call.
+    F = torch.nn.functional
+    qn, kn, bn, lan = (torch.empty_like(t) for t in (q, k, beta, la))
+
+    def call_unfused():
+        qn.copy_(F.normalize(q, dim=-1))
+        kn.copy_(F.normalize(k, dim=-1))
+        torch.sigmoid(beta, out=bn)
+        lan.copy_(F.logsigmoid(la.float() + 6.0) / 16.0)
+        kda.kda_chunk_fwd(qn, kn, v, lan, bn, S0, None, o=o, S_final=Sf, workspace=ws, chunk=CHUNK, stream=stream)
+        o.mul_(torch.sigmoid(gate))
+    for _ in range(3):
+        call_unfused()
+    torch.cuda.synchronize()
+    eu0, eu1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    eu0.record(stream)
+    for _ in range(args.steps):
+        call_unfused()
+    eu1.record(stream)
+    torch.cuda.synchronize()
+    unfused_ms = eu0.elapsed_time(eu1) / args.steps
     fused = {"workload": "long_context_prefill with q/k L2 norm, sigmoid beta, logsigmoid decay and an output "
                          "gate inside the kernels (kda_chunk_fwd_fused)",
              "ms_per_call": fused_ms, "vs_plain_call": fused_ms / ms_step,
-             "tokens_per_s": tokens / (fused_ms / 1e3)}
-    del gate
+             "tokens_per_s": tokens / (fused_ms / 1e3),
+             "unfused_ms_per_call": unfused_ms,
+             "unfused": "the same maps as separate elementwise passes (torch, bf16) around kda_chunk_fwd",
+             "saving_ms": unfused_ms - fused_ms}
+    del gate, qn, kn, bn, lan
 
     # ------------------------------------------------------------------ scalar gate (Gated DeltaNet)
     # Workload 2's shape with one decay per (token, head): gdn_chunk_fwd.

@@ -31,6 +31,11 @@ inline bool chunk_supported(int c) { return c == 0 || c == 32 || c == 64; }
 //         launch as pass 1 (which then covers segments 1..G-2) and leaves its exit state
 //         as segment 1's entry, so pass 2 covers segments 1..G-1.  Both passes then fill
 //         the chip with one segment more than the plain schedule.
+//  seg_items > 0 (packed batches of fewer than kComputeUnits (sequence, head) pairs, 32-token
+//         chunks): the split schedule per sequence.  A first kernel reads cu_seqlens and writes
+//         a segment table (the segment length and, per sequence, its segments and the prefix
+//         sums that map workgroups to them); pass 1, the combine and pass 2 are launched with
+//         seg_items * H workgroups each (the table's upper bound), the surplus ones exiting.
 // Every plan's workspace starts with the call's status word (kStatusBytes reserved): the
 // first kernel of the call clears it, and a workgroup whose bounded ordering wait gave up
 // sets it to 1 (and writes NaN to what it stores from then on).
@@ -47,6 +52,7 @@ struct PrefillPlan {
     int chunks = 0;        // chunks per sequence (equal-length case)
     int cps = 0;           // chunks per segment
     bool split0 = false;   // segment 0's output pass runs beside pass 1 (G >= 3)
+    int seg_items = 0;     // packed batches cut into segments: pass-1 workgroups per head (0: one pass)
     size_t off_status = 0, off_phi = 0, off_sloc = 0, off_se = 0, off_order = 0;
     size_t workspace_bytes = 0;
 };

@@ -327,6 +327,7 @@ struct KernelArgs {
     const float* S0;
     const int32_t* cu;
     const int32_t* order;
+    const int32_t* seg;   // segment table of a packed batch (nullptr: one pass per sequence)
     void* o;
     float* S_final;
     float* phi;     // [G-1][N*H][D][D] segment transitions
@@ -925,6 +926,135 @@ struct PSmem {
     SyncCounters sync;
 };
 
+// One workgroup's share of a call: segment s, chunks [c_begin, c_end), of the (sequence n,
+// head h) pair whose tokens are [t0, t1), with where its entry state comes from and where its
+// result goes.  MODE 0 reads `entry` (nullptr: zero) and writes its exit state to `exit`
+// (nullptr: none); MODE 1 writes S_loc to `exit` and Phi to `phi`.
+struct Unit {
+    int n, h, s, c_begin, c_end;
+    long t0, t1;
+    const float* entry;
+    float* exit;
+    float* phi;
+};
+
+// Segment table of a packed batch (int32, in the workspace), ranks r = 0..N-1 longest first:
+//   [0]                 L, the segment length in chunks (segments 1.. of every sequence)
+//   [4 + r]             the sequence of rank r
+//   [4 + N + r]         chunks in its segment 0
+//   [4 + 2N + r]        its segments after segment 0 (G_n - 1)
+//   [4 + 3N + r], r<=N  exclusive prefix over ranks of its pass-1 workgroups, max(1, G_n - 1)
+//   [4 + 4N + 1 + r]    exclusive prefix over ranks of its pass-2 workgroups, G_n - 1; also its
+//                       first state slot (segment s >= 1 of rank r uses slot p2[r] + s - 1)
+constexpr int kSegHdr = 4;
+inline size_t seg_table_ints(int N) { return kSegHdr + 5 * static_cast<size_t>(N) + 2; }
+
+// Largest r in [0, N) with pre[r] <= j, for a non-decreasing prefix array with pre[0] = 0 <= j
+// < pre[N]: the rank whose range [pre[r], pre[r + 1]) holds item j.
+__device__ __forceinline__ int seg_rank(const int32_t* pre, int N, int j) {
+    int lo = 0, hi = N;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (pre[mid] <= j) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// Equal-length batches: workgroup `block` of a launch whose first workgroup row is segment
+// a.seg0; rows of N*H units.
+template <int D, int C, int MODE>
+__device__ __forceinline__ Unit unit_equal(const KernelArgs& a, int block) {
+    Unit u;
+    const int unit = block % a.NH;
+    u.s = a.seg0 + block / a.NH;
+    u.n = unit / a.H;
+    u.h = unit % a.H;
+    u.t0 = static_cast<long>(u.n) * a.T;
+    u.t1 = u.t0 + a.T;
+    u.c_begin = u.s == 0 ? 0 : a.cps0 + (u.s - 1) * a.cps;
+    u.c_end = min(u.s == 0 ? a.cps0 : u.c_begin + a.cps, a.chunks);
+    const size_t ub = static_cast<size_t>(unit) * D * D;
+    u.entry = nullptr;
+    u.exit = nullptr;
+    u.phi = nullptr;
+    if constexpr (MODE == 0) {
+        if (u.s == 0) u.entry = a.S0 ? a.S0 + ub : nullptr;
+        else u.entry = a.se + (static_cast<size_t>(u.s - 1) * a.NH + unit) * D * D;
+        if (u.s == a.G - 1 && a.S_final) u.exit = a.S_final + ub;
+        else if (u.s == 0 && a.split0) u.exit = a.se + ub;   // segment 1's entry state
+    } else {
+        const size_t sb = (static_cast<size_t>(u.s) * a.NH + unit) * D * D;
+        u.exit = a.sloc + sb;
+        u.phi = a.phi + sb;
+    }
+    return u;
+}
+
+// Packed sequences, one pass: workgroup `block` runs the whole of one (sequence, head), the
+// sequences taken longest first.
+template <int D, int C>
+__device__ __forceinline__ Unit unit_packed(const KernelArgs& a, int block) {
+    Unit u;
+    u.n = a.order[block / a.H];
+    u.h = block % a.H;
+    u.s = 0;
+    u.t0 = a.cu[u.n];
+    u.t1 = a.cu[u.n + 1];
+    u.c_begin = 0;
+    u.c_end = static_cast<int>((u.t1 - u.t0 + C - 1) / C);
+    const size_t ub = (static_cast<size_t>(u.n) * a.H + u.h) * D * D;
+    u.entry = a.S0 ? a.S0 + ub : nullptr;
+    u.exit = a.S_final ? a.S_final + ub : nullptr;
+    u.phi = nullptr;
+    return u;
+}
+
+// Packed sequences, segmented: item j = block / H of head h = block % H.  Pass 1 (pass2 false)
+// holds, per rank, segment 0's output pass and then the summaries of segments 1..G_n-2; pass 2
+// the output passes of segments 1..G_n-1.  Returns the item's mode (0 output, 1 summary), or -1
+// for a workgroup past the last item.
+template <int D, int C>
+__device__ __forceinline__ int unit_segmented(const KernelArgs& a, int block, bool pass2, Unit& u) {
+    const int32_t* tab = a.seg;
+    const int N = a.NH / a.H;
+    const int32_t* p1 = tab + kSegHdr + 3 * N;
+    const int32_t* p2 = p1 + N + 1;
+    const int32_t* pre = pass2 ? p2 : p1;
+    const int j = block / a.H;
+    if (j >= pre[N]) return -1;
+    const int r = seg_rank(pre, N, j);
+    const int L = tab[0], cps0 = tab[kSegHdr + N + r], more = tab[kSegHdr + 2 * N + r];
+    u.n = tab[kSegHdr + r];
+    u.h = block % a.H;
+    u.t0 = a.cu[u.n];
+    u.t1 = a.cu[u.n + 1];
+    const int nc = static_cast<int>((u.t1 - u.t0 + C - 1) / C);
+    u.s = j - pre[r] + (pass2 ? 1 : 0);
+    u.c_begin = u.s == 0 ? 0 : cps0 + (u.s - 1) * L;
+    u.c_end = u.s == 0 ? cps0 : min(u.c_begin + L, nc);
+    const size_t ub = (static_cast<size_t>(u.n) * a.H + u.h) * D * D;
+    // state slot of segment s (>= 1): the entry state of segment s, or the summary of segment s
+    const size_t slot = (static_cast<size_t>(p2[r] + u.s - 1) * a.H + u.h) * D * D;
+    u.entry = nullptr;
+    u.exit = nullptr;
+    u.phi = nullptr;
+    if (u.s == 0) {
+        u.entry = a.S0 ? a.S0 + ub : nullptr;
+        if (more == 0) u.exit = a.S_final ? a.S_final + ub : nullptr;
+        else u.exit = a.se + (static_cast<size_t>(p2[r]) * a.H + u.h) * D * D;   // segment 1's entry
+        return 0;
+    }
+    if (!pass2) {
+        u.exit = a.sloc + slot;
+        u.phi = a.phi + slot;
+        return 1;
+    }
+    u.entry = a.se + slot;
+    if (u.s == more) u.exit = a.S_final ? a.S_final + ub : nullptr;
+    return 0;
+}
+
 // SG (scalar gate): log_alpha is one value per (token, head), [B, T, H] -- the gated delta
 // rule of Gated DeltaNet.  With f_r = e^{b_r - b_m} a scalar per token, the decay factors move
 // off the contractions: A = StrictTril(Diag(beta) K K^T) and P = Tril(Q K^T) carry no decay,
@@ -944,7 +1074,7 @@ struct PSmem {
 template <int D, typename IN, bool OUT_BF16, int MODE, bool SG, bool FUSE, int CT_, int NPW_ = D / 32>
 __device__ __forceinline__ void pipe_body(const KernelArgs& a,
                                           PSmem<D, MODE, std::is_same<IN, BF16>::value, NPW_>& sm,
-                                          const int block) {
+                                          const Unit& u) {
     using K = PCfg<D, MODE, CT_, NPW_>;
     constexpr int C = K::C, NPW = K::NPW, CT = K::CT, TPG = K::TPG, QPW = K::QPW, TGN = K::TGN;
     constexpr int NRT = K::NRT, RT = K::RT, KS = K::KS;
@@ -968,29 +1098,8 @@ __device__ __forceinline__ void pipe_body(const KernelArgs& a,
     const bool solver = w >= NPW - 2;
 
     // ---------------------------------------------------------------- work unit
-    int n, h, s, c_begin, c_end;
-    long t0, t1;
-    if (a.cu) {
-        const int rank = block / H;
-        h = block % H;
-        n = a.order[rank];
-        t0 = a.cu[n];
-        t1 = a.cu[n + 1];
-        s = 0;
-        c_begin = 0;
-        c_end = static_cast<int>((t1 - t0 + C - 1) / C);
-    } else {
-        const int unit = block % a.NH;
-        s = a.seg0 + block / a.NH;
-        n = unit / H;
-        h = unit % H;
-        t0 = static_cast<long>(n) * a.T;
-        t1 = t0 + a.T;
-        c_begin = s == 0 ? 0 : a.cps0 + (s - 1) * a.cps;
-        c_end = min(s == 0 ? a.cps0 : c_begin + a.cps, a.chunks);
-    }
-    const int unit = n * H + h;
-    const size_t ubase = static_cast<size_t>(unit) * D * D;
+    const int h = u.h, c_begin = u.c_begin, c_end = u.c_end;
+    const long t0 = u.t0, t1 = u.t1;
     const int HD = H * D;   // elements between consecutive tokens of one head
 
     // consumer identity: 16 CT state columns starting at j0 (of S, or of Phi in the summary pass)
@@ -1404,11 +1513,7 @@ __device__ __forceinline__ void pipe_body(const KernelArgs& a,
     // ================================================================ consumer state
     f32x4 S[RT][CT];
     if (!producer) {
-        const float* src = nullptr;
-        if constexpr (MODE == 0) {
-            if (s == 0) src = a.S0 ? a.S0 + ubase : nullptr;
-            else src = a.se + (static_cast<size_t>(s - 1) * a.NH + unit) * D * D;
-        }
+        const float* src = MODE == 0 ? u.entry : nullptr;
         if (src) {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
@@ -1806,13 +1911,7 @@ __device__ __forceinline__ void pipe_body(const KernelArgs& a,
             }
         }
     }
-    float* dst = nullptr;
-    if constexpr (MODE == 0) {
-        if ((a.cu || s == a.G - 1) && a.S_final) dst = a.S_final + ubase;
-        else if (!a.cu && s == 0 && a.split0) dst = a.se + ubase;   // segment 1's entry state
-    } else {
-        dst = (is_phi ? a.phi : a.sloc) + (static_cast<size_t>(s) * a.NH + unit) * D * D;
-    }
+    float* const dst = MODE == 1 && is_phi ? u.phi : u.exit;
     const bool poison = __builtin_amdgcn_readfirstlane(lds_read(broken)) != 0;
     if (poison && l == 0 && a.status) *reinterpret_cast<volatile int*>(a.status) = 1;
     if (dst) {
@@ -1831,13 +1930,25 @@ __global__ __attribute__((amdgpu_flat_work_group_size(PCfg<D, MODE>::NT, PCfg<D,
                           amdgpu_waves_per_eu(PCfg<D, MODE>::WPE, PCfg<D, MODE>::WPE)))
 void pipe_kernel(KernelArgs a) {
     __shared__ PSmem<D, MODE, std::is_same<IN, BF16>::value> sm;
-    pipe_body<D, IN, OUT_BF16, MODE, SG, FUSE, PCfg<D, MODE>::CT>(a, sm, blockIdx.x);
+    constexpr int C = PCfg<D, MODE>::C;
+    Unit u;
+    if constexpr (MODE == 0) {
+        if (a.seg) {
+            if (unit_segmented<D, C>(a, blockIdx.x, true, u) < 0) return;
+        } else {
+            u = a.cu ? unit_packed<D, C>(a, blockIdx.x) : unit_equal<D, C, 0>(a, blockIdx.x);
+        }
+    } else {
+        u = unit_equal<D, C, 1>(a, blockIdx.x);
+    }
+    pipe_body<D, IN, OUT_BF16, MODE, SG, FUSE, PCfg<D, MODE>::CT>(a, sm, u);
 }
 
 // Pass 1 of the split schedule in one launch: workgroups [0, NH) run segment 0's output pass
 // from S0 (writing o and, as segment 1's entry state, its exit state) with 16-column consumer
 // waves; the others run the summaries of segments 1..G-2.  Both have D/32 producer and D/16
-// consumer waves, and the launch order puts segment 0's workgroups first.
+// consumer waves, and the launch order puts segment 0's workgroups first.  For a packed batch
+// the segment table assigns the two kinds of work per sequence.
 template <int D, typename IN, bool OUT_BF16, bool SG = false, bool FUSE = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(PCfg<D, 1>::NT, PCfg<D, 1>::NT),
                           amdgpu_waves_per_eu(PCfg<D, 1>::WPE, PCfg<D, 1>::WPE)))
@@ -1848,17 +1959,27 @@ void pipe_pass1_kernel(KernelArgs a) {
         PSmem<D, 0, VLDS> out;
         PSmem<D, 1, VLDS> sum;
     } sm;
+    constexpr int C = PCfg<D, 1>::C;
     const int block = blockIdx.x;
-    if (block < a.NH) {
+    Unit u;
+    int mode;
+    if (a.seg) {
+        mode = unit_segmented<D, C>(a, block, false, u);
+        if (mode < 0) return;
+    } else if (block < a.NH) {
         KernelArgs a0 = a;
         a0.seg0 = 0;
         a0.split0 = 1;
-        pipe_body<D, IN, OUT_BF16, 0, SG, FUSE, 1>(a0, sm.out, block);
+        u = unit_equal<D, C, 0>(a0, block);
+        mode = 0;
     } else {
         KernelArgs a1 = a;
         a1.seg0 = 1;
-        pipe_body<D, IN, OUT_BF16, 1, SG, FUSE, 2>(a1, sm.sum, block - a.NH);
+        u = unit_equal<D, C, 1>(a1, block - a.NH);
+        mode = 1;
     }
+    if (mode == 0) pipe_body<D, IN, OUT_BF16, 0, SG, FUSE, 1>(a, sm.out, u);
+    else pipe_body<D, IN, OUT_BF16, 1, SG, FUSE, 2>(a, sm.sum, u);
 }
 
 // Entry states of segments s_first..G-1:  S_e(s) = Phi(s-1) S_e(s-1) + S_loc(s-1), starting from
@@ -1866,10 +1987,13 @@ void pipe_pass1_kernel(KernelArgs a) {
 // null: zero).  One workgroup per (unit, 16-column slice).  Phi(s-1) is staged through LDS with
 // coalesced loads, and the next segment's Phi and S_loc are requested while this one is applied;
 // the products run on the fp32 matrix cores (v_mfma_f32_16x16x4_f32), D/64 16-row tiles per wave.
+// With a segment table (packed batches), unit r * H + h is rank r's sequence: its own G and
+// state slots, and s_first = 2 (segment 0's output pass left segment 1's entry state).
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ init, const float* __restrict__ phi,
                                                       const float* __restrict__ sloc, float* __restrict__ se,
-                                                      int NH, int G, int s_first) {
+                                                      int NH, int G, int s_first, const int32_t* __restrict__ seg,
+                                                      int H) {
     constexpr int LP = D + 4;              // row pitch of Phi in LDS
     constexpr int LC = 20;                 // row pitch of the 16-column state slice
     constexpr int RT = D / 64;             // row tiles per wave
@@ -1879,12 +2003,26 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     __shared__ __attribute__((aligned(16))) float cur[2][D * LC];
     const int unit = blockIdx.x, c0 = blockIdx.y * 16, tid = threadIdx.x, w = tid >> 6;
     const int i = tid & 15, kq = (tid & 63) >> 4;
-    const size_t ub = static_cast<size_t>(unit) * D * D;
-    for (int e = tid; e < D * 16; e += 256) cur[0][(e >> 4) * LC + (e & 15)] = init ? init[ub + (e >> 4) * D + c0 + (e & 15)] : 0.f;
+    // step s reads Phi and S_loc of segment s-1 at slot p0 + (s-1) st and writes segment s's
+    // entry state at slot e0 + (s-1) st (slots of D x D floats)
+    long p0 = unit, e0 = unit, st = NH;
+    const float* ini = init ? init + static_cast<size_t>(unit) * D * D : nullptr;
+    if (seg) {
+        const int N = NH / H, r = unit / H, h = unit % H;
+        G = 1 + seg[kSegHdr + 2 * N + r];
+        if (G < 3) return;
+        const long base = seg[kSegHdr + 4 * N + 1 + r];
+        s_first = 2;
+        p0 = (base - 1) * H + h;
+        e0 = base * H + h;
+        st = H;
+        ini = se + static_cast<size_t>(e0) * D * D;
+    }
+    for (int e = tid; e < D * 16; e += 256) cur[0][(e >> 4) * LC + (e & 15)] = ini ? ini[(e >> 4) * D + c0 + (e & 15)] : 0.f;
     fx4 pf[NF];
     float pl[RT][4];
     auto fetch = [&](int s) __attribute__((always_inline)) {
-        const size_t sb = (static_cast<size_t>(s - 1) * NH + unit) * D * D;
+        const size_t sb = static_cast<size_t>(p0 + (s - 1) * st) * D * D;
         const fx4* src = reinterpret_cast<const fx4*>(phi + sb);
 #pragma unroll
         for (int f = 0; f < NF; ++f) pf[f] = src[tid + 256 * f];
@@ -1927,7 +2065,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[t][3], b3, acc[t], 0, 0, 0);
             }
         }
-        const size_t sb = (static_cast<size_t>(s - 1) * NH + unit) * D * D;
+        const size_t sb = static_cast<size_t>(e0 + (s - 1) * st) * D * D;
 #pragma unroll
         for (int t = 0; t < RT; ++t)
 #pragma unroll
@@ -1955,6 +2093,80 @@ __global__ __launch_bounds__(256) void order_kernel(const int32_t* __restrict__ 
     order[rank] = i;
 }
 
+// Segment plan of a packed batch whose (sequence, head) pairs are too few to fill the chip, in
+// one workgroup (one thread per sequence, N <= 256).  A sequence of c chunks is cut into a
+// segment 0 of about t = round(ratio L) chunks (t = L for L < 64) and G - 1 = ceil((c - t) / L)
+// segments of L chunks after it (none when c <= t), segment 0 taking the remainder.  L is the
+// smallest length >= Lmin for which the pass-1 workgroups, the sum over sequences of
+// max(1, G - 1), fit `items` per head, raised to Lc, the smallest length with 25 Lc^2 >=
+// 9 c_max, when that fits too: the combine chains a sequence's segments one after another, at
+// about 0.8 of a chunk's time per segment on MI355X, so with segment 0 about L long the call
+// takes about 2.2 L + 0.8 c_max / L chunk-times, least near L = 0.6 sqrt(c_max).  When the
+// result leaves no gain over one pass per sequence (2 L + 8 >= c_max), no sequence is cut.
+// Ranks are longest first (ties by index), as in the one-pass order.
+__global__ __launch_bounds__(256) void seg_plan_kernel(const int32_t* __restrict__ cu, int N, int C, int items,
+                                                       int Lmin, float ratio, int32_t* __restrict__ tab) {
+    __shared__ int red[256];
+    __shared__ int more_r[256];
+    const int i = threadIdx.x;
+    const bool act = i < N;
+    const int len = act ? cu[i + 1] - cu[i] : 0;
+    const int c = (len + C - 1) / C;
+    auto reduce = [&](int x, bool take_max) {
+        red[i] = x;
+        __syncthreads();
+        for (int o = 128; o > 0; o >>= 1) {
+            if (i < o) red[i] = take_max ? max(red[i], red[i + o]) : red[i] + red[i + o];
+            __syncthreads();
+        }
+        const int r = red[0];
+        __syncthreads();
+        return r;
+    };
+    auto more_of = [&](int L) {
+        const int t = L >= 64 ? max(1, static_cast<int>(rintf(ratio * L))) : L;
+        int m = c > t ? (c - t + L - 1) / L : 0;
+        if (m > 0 && c - m * L < 1) --m;   // segment 0 keeps at least one chunk
+        return m;
+    };
+    const int maxc = reduce(c, true);
+    int lo = Lmin, hi = max(Lmin, maxc);   // at L = max(Lmin, maxc) every sequence needs one item
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (reduce(act ? max(1, more_of(mid)) : 0, false) <= items) hi = mid;
+        else lo = mid + 1;
+    }
+    int L = lo;
+    int Lc = static_cast<int>(sqrtf(0.36f * static_cast<float>(maxc)));
+    while (25LL * Lc * Lc < 9LL * maxc) ++Lc;
+    while (Lc > 1 && 25LL * (Lc - 1) * (Lc - 1) >= 9LL * maxc) --Lc;
+    if (Lc > L && reduce(act ? max(1, more_of(Lc)) : 0, false) <= items) L = Lc;
+    const bool cut = 2 * L + 8 < maxc;
+    if (act) {
+        int rank = 0;
+        for (int m = 0; m < N; ++m) {
+            const int lm = cu[m + 1] - cu[m];
+            rank += (lm > len) || (lm == len && m < i);
+        }
+        const int m = cut ? more_of(L) : 0;
+        tab[kSegHdr + rank] = i;
+        tab[kSegHdr + N + rank] = c - m * L;
+        tab[kSegHdr + 2 * N + rank] = m;
+        more_r[rank] = m;
+    }
+    __syncthreads();
+    if (i <= N) {
+        int s1 = 0, s2 = 0;
+        for (int r = 0; r < i; ++r) {
+            s1 += max(1, more_r[r]);
+            s2 += more_r[r];
+        }
+        tab[kSegHdr + 3 * N + i] = s1;
+        tab[kSegHdr + 4 * N + 1 + i] = s2;
+    }
+    if (i == 0) tab[0] = L;
+}
+
 // Clears the call's status word before its kernels run (a fill kernel rather than a memset, so
 // that the call stays free of memset nodes under stream capture).
 __global__ void status_clear_kernel(int* status) {
@@ -1978,9 +2190,11 @@ hipError_t launch_variant(const PrefillArgs& pa, const PrefillPlan& plan, hipStr
     char* ws = static_cast<char*>(pa.workspace);
     a.status = reinterpret_cast<int*>(ws + plan.off_status);
     a.order = pa.cu ? reinterpret_cast<const int32_t*>(ws + plan.off_order) : nullptr;
-    a.phi = plan.G > 1 ? reinterpret_cast<float*>(ws + plan.off_phi) : nullptr;
-    a.sloc = plan.G > 1 ? reinterpret_cast<float*>(ws + plan.off_sloc) : nullptr;
-    a.se = plan.G > 1 ? reinterpret_cast<float*>(ws + plan.off_se) : nullptr;
+    a.seg = nullptr;
+    const bool states = plan.G > 1 || plan.seg_items > 0;
+    a.phi = states ? reinterpret_cast<float*>(ws + plan.off_phi) : nullptr;
+    a.sloc = states ? reinterpret_cast<float*>(ws + plan.off_sloc) : nullptr;
+    a.se = states ? reinterpret_cast<float*>(ws + plan.off_se) : nullptr;
     const int NH = a.NH;
     hipLaunchKernelGGL(status_clear_kernel, dim3(1), dim3(64), 0, stream, a.status);
     // The 32-token chunk runs the producer/consumer kernel; the 64-token chunk, whose
@@ -1998,7 +2212,31 @@ hipError_t launch_variant(const PrefillArgs& pa, const PrefillPlan& plan, hipStr
                 hipLaunchKernelGGL((chunk_kernel<D, C, IN, OB, 1>), dim3(grid), dim3(Cfg<D, C, 1>::NT), 0, stream, ka);
         }
     };
+    // Segment 0's output pass runs beside the summaries of later segments, so it may be as long
+    // as the ratio of a summary chunk's cost to an output chunk's (measured on MI355X: plain
+    // 1.18, scalar gate 1.08, fused output pass with its gate 0.95); the other segments share
+    // the rest equally.  Only for segments of 64 chunks or more, where the per-chunk costs
+    // outweigh the fixed ones of a segment (state loads and stores, the pipeline's fill).
+    constexpr double kSeg0Ratio = FUSE ? 0.95 : (SG ? 1.08 : 1.18);
     if (pa.cu) {
+        if constexpr (C == 32) {
+            if (plan.seg_items > 0) {
+                // Packed batch with too few (sequence, head) pairs to fill the chip: the split
+                // schedule per sequence, from the segment table the first kernel writes.
+                int32_t* tab = reinterpret_cast<int32_t*>(ws + plan.off_order);
+                hipLaunchKernelGGL(seg_plan_kernel, dim3(1), dim3(256), 0, stream, pa.cu, pa.N, C,
+                                   plan.seg_items, kMinChunksPerSegment, static_cast<float>(kSeg0Ratio), tab);
+                a.seg = tab;
+                a.order = nullptr;
+                const int grid = plan.seg_items * pa.H;
+                hipLaunchKernelGGL((pipe_pass1_kernel<D, IN, OB, SG, FUSE>), dim3(grid), dim3(PCfg<D, 1>::NT), 0,
+                                   stream, a);
+                hipLaunchKernelGGL(combine_kernel<D>, dim3(NH, D / 16), dim3(256), 0, stream, nullptr, a.phi,
+                                   a.sloc, a.se, NH, 0, 2, a.seg, pa.H);
+                pass(0, grid, a);
+                return hipGetLastError();
+            }
+        }
         hipLaunchKernelGGL(order_kernel, dim3((pa.N + 255) / 256), dim3(256), 0, stream, pa.cu,
                            reinterpret_cast<int32_t*>(ws + plan.off_order), pa.N);
         pass(0, NH, a);
@@ -2006,13 +2244,7 @@ hipError_t launch_variant(const PrefillArgs& pa, const PrefillPlan& plan, hipStr
     }
     if constexpr (C == 32) {
         if (plan.G > 1 && plan.split0) {
-            // Segment 0's output pass runs beside the summaries of segments 1..G-2, so it may be as
-            // long as the ratio of a summary chunk's cost to an output chunk's (measured on MI355X:
-            // plain 1.18, scalar gate 1.08, fused output pass with its gate 0.95); the other segments
-            // share the rest equally.  Only for segments of 64 chunks or more, where the per-chunk
-            // costs outweigh the fixed ones of a segment (state loads and stores, the pipeline's
-            // fill).  G, and with it the workspace, is unchanged.
-            constexpr double kSeg0Ratio = FUSE ? 0.95 : (SG ? 1.08 : 1.18);
+            // G, and with it the workspace, is unchanged by the longer segment 0.
             const int cps = static_cast<int>(std::ceil(plan.chunks / (plan.G - 1 + kSeg0Ratio)));
             const int cps0 = plan.chunks - (plan.G - 1) * cps;
             if (plan.cps >= 64 && cps0 >= 1) {
@@ -2025,7 +2257,7 @@ hipError_t launch_variant(const PrefillArgs& pa, const PrefillPlan& plan, hipStr
                                0, stream, a);
             if (plan.G > 2)
                 hipLaunchKernelGGL(combine_kernel<D>, dim3(NH, D / 16), dim3(256), 0, stream, a.se, a.phi, a.sloc,
-                                   a.se, NH, plan.G, 2);
+                                   a.se, NH, plan.G, 2, nullptr, pa.H);
             KernelArgs a1 = a;   // output passes of segments 1..G-1
             a1.seg0 = 1;
             pass(0, NH * (plan.G - 1), a1);
@@ -2035,7 +2267,7 @@ hipError_t launch_variant(const PrefillArgs& pa, const PrefillPlan& plan, hipStr
     if (plan.G > 1) {
         pass(1, NH * (plan.G - 1), a);
         hipLaunchKernelGGL(combine_kernel<D>, dim3(NH, D / 16), dim3(256), 0, stream, pa.S0, a.phi, a.sloc, a.se,
-                           NH, plan.G, 1);
+                           NH, plan.G, 1, nullptr, pa.H);
     }
     pass(0, NH * plan.G, a);
     return hipGetLastError();
@@ -2053,6 +2285,21 @@ PrefillPlan plan_prefill(int B, int T, int H, int D, int N, bool varlen, int chu
     if (varlen) {
         p.G = 1;
         p.off_order = kStatusBytes;
+        const long pairs = static_cast<long>(N) * H;
+        const long tc = (static_cast<long>(T) + p.chunk - 1) / p.chunk;   // >= the longest sequence's chunks
+        if (p.chunk == 32 && pairs > 0 && pairs < kComputeUnits && tc >= 2 * kMinChunksPerSegment) {
+            // Too few (sequence, head) pairs to fill the chip: each sequence is cut into segments
+            // on the device, with at most kComputeUnits / H pass-1 workgroups per head (N of them
+            // at least, which N * H < kComputeUnits allows) and as many state slots.
+            p.seg_items = kComputeUnits / H;
+            const size_t mat = static_cast<size_t>(p.seg_items) * H * D * D * sizeof(float);
+            const size_t tab = align256(seg_table_ints(N) * sizeof(int32_t));
+            p.off_phi = kStatusBytes + tab;
+            p.off_sloc = p.off_phi + align256(mat);
+            p.off_se = p.off_sloc + align256(mat);
+            p.workspace_bytes = p.off_se + align256(mat);
+            return p;
+        }
         p.workspace_bytes = kStatusBytes + align256(static_cast<size_t>(N) * sizeof(int32_t));
         return p;
     }

@@ -79,6 +79,10 @@ const char* kda_status_string(kda_status s);
  * and writes NaN to every output row and state it stores from then on.  Read it
  * after the call's work has completed: 0 means every wait completed.  The rest of
  * the workspace is private scratch (segment summaries, the packed-sequence order).
+ * Packed batches with 32-token chunks and fewer than 256 (sequence, head) pairs
+ * reserve segment summaries for 256 / H segments per head: the call cuts its
+ * sequences into segments on the device, from cu_seqlens, so that one long
+ * sequence still spreads over the chip.
  */
 size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int num_seqs,
                                      int has_cu_seqlens, int chunk);
@@ -126,8 +130,9 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
  *
  * Returns KDA_ERR_SCRATCH_LIMIT, before any HIP call, when
  * kda_chunk_fwd_workspace_bytes() for these sizes exceeds KDA_NOALLOC_SCRATCH_BYTES
- * (no equal-length plan at Dk = Dv <= 128 does: their segment summaries stay under
- * 48 MiB; packed batches of more than about 16 million sequences do).  Every call on
+ * (no equal-length plan and no packed plan of fewer than 256 (sequence, head)
+ * pairs at Dk = Dv <= 128 does: their segment summaries stay under 48 MiB; packed
+ * batches of more than about 16 million sequences do).  Every call on
  * one GPU shares that GPU's array, which keeps the last call's contents (each call
  * clears what must start at zero itself): calls that overlap in time on one GPU --
  * on different streams, or from host threads whose streams are not ordered -- race

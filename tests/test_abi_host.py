@@ -81,6 +81,17 @@ def test_workspace_query_plans(lib):
     assert q(64, 4096, 32, 128, 128, 64, False) == st
     # packed sequences: the status block and an int32 order table (rounded to 256 bytes)
     assert q(1, 1000, 32, 128, 128, 64, True) == st + 256
+    assert q(1, 1000, 32, 128, 128, 8, True) == st + 256          # 256 pairs fill the chip
+    assert q(1, 200, 32, 128, 128, 1, True) == st + 256           # 7 chunks: too short to cut
+    assert q(1, 65536, 32, 128, 128, 1, True, chunk=64) == st + 256
+    # fewer than 256 (sequence, head) pairs, 32-token chunks: a segment table (4 + 5N + 2 int32,
+    # rounded to 256 bytes) and 3 matrices per head for each of 256 / H segment slots
+    mat = 128 * 128 * 4
+    assert q(1, 65536, 32, 128, 128, 1, True) == st + 256 + 3 * 32 * 8 * mat
+    assert q(1, 1000, 32, 128, 128, 7, True) == st + 256 + 3 * 32 * 8 * mat
+    assert q(1, 24740, 8, 128, 128, 5, True) == st + 256 + 3 * 8 * 32 * mat
+    assert q(1, 5000, 3, 64, 64, 60, True) == st + 1280 + 3 * 3 * 85 * 64 * 64 * 4   # 306 int32
+    assert q(1, 65536, 32, 128, 128, 1, True) <= kda.NOALLOC_SCRATCH_BYTES
     # unsupported sizes report 0
     assert q(1, 64, 2, 96, 96, 1, False) == 0
     assert q(1, 64, 2, 128, 128, 1, False, chunk=16) == 0
