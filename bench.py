@@ -106,6 +106,11 @@ def counted_traffic(kind: str):
     return rec["read_bytes"] + rec["write_bytes"]
 
 
+# floats per (chunk, head) record of the backward at d = 128: Q', K', K'', the decay exponents
+# (32 x 128 each), M, P, L (32 x 32 each), e_m, e_n (128 each), beta (32)
+Rec128 = 4 * 32 * 128 + 3 * 32 * 32 + 2 * 128 + 32
+
+
 def timed_calls(torch, fn, stream, warmup: int, n: int) -> dict:
     """warmup untimed calls, then n calls each bracketed by HIP events on `stream`:
     median, min and mean milliseconds per call."""
@@ -436,7 +441,11 @@ def main():
              "tokens_per_s": tokens / (fused_ms / 1e3),
              "unfused_ms_per_call": unfused_ms,
              "unfused": "the same maps as separate elementwise passes (torch, bf16) around kda_chunk_fwd",
-             "saving_ms": unfused_ms - fused_ms}
+             "saving_ms": unfused_ms - fused_ms,
+             # what separate passes cost at best: read and write q, k, log_alpha, beta once (bf16), and
+             # read o and the gate and write o once, at the HBM peak
+             "unfused_extra_hbm_floor_ms": tokens * H * ((3 * d + 1) * 2 * 2 + 3 * d * 2) / (HBM_PEAK_GBS * 1e9) * 1e3,
+             "fused_extra_ms": fused_ms - ms_step}
     del gate, qn, kn, bn, lan
 
     # ------------------------------------------------------------------ scalar gate (Gated DeltaNet)
@@ -552,8 +561,39 @@ def main():
                      "flops_per_call": bwd_flops,
                      "flop_convention": f"{backward_alg_flops_per_token_head(d)} per token-head "
                                         "(20 d^2 + 32 C d), each product as three bf16 MFMAs"},
+        "workspace_bytes": wsb.numel(),
     }
     del xb, gb, grads, wsb
+    torch.cuda.empty_cache()
+
+    # The long-context shape's backward (1 x 65,536 tokens, 32 heads): past the workspace limit
+    # it runs in windows of chunks (8 of 256 here), a forward sweep keeping each window's entry
+    # state and the windows from last to first; timed over a few calls.
+    x2 = inputs.device_prefill(inputs.WORKLOADS[2])
+    g2 = inputs.device_output_grads(x2, seed=1002)
+    B2, T2, H2 = x2["B"], x2["T"], x2["H"]
+    grads2 = {nm: torch.empty((B2, T2, H2, d), dtype=torch.bfloat16, device="cuda")
+              for nm in ("dq", "dk", "dv", "dlog_alpha")}
+    grads2["dbeta"] = torch.empty((B2, T2, H2), dtype=torch.bfloat16, device="cuda")
+    grads2["dS0"] = torch.empty((B2, H2, d, d), dtype=torch.float32, device="cuda")
+    ws2 = torch.empty(kda.kda_chunk_bwd_workspace_bytes(B2, T2, H2, d, d, B2, False), dtype=torch.uint8,
+                      device="cuda")
+
+    def call_bwd2():
+        kda.kda_chunk_bwd(x2["q"], x2["k"], x2["v"], x2["log_alpha"], x2["beta"], g2["d_o"], x2["S0"], None,
+                          g2["dS_final"], grads=grads2, workspace=ws2, stream=stream)
+    t2 = timed_calls(torch, call_bwd2, stream, 1, 3)
+    b2_bytes = backward_alg_bytes(B2 * T2, H2, d, B2)
+    backward["long_context"] = {
+        "workload": "long_context backward: B=1, T=65536, H=32, d=128, bf16 inputs and gradients, S0 != 0, "
+                    "kda_chunk_bwd", "value": B2 * T2 / (t2["median"] / 1e3), "unit": "tokens/s",
+        "ms_per_call_median": t2["median"], "ms_per_call_min": t2["min"],
+        "hbm_frac": b2_bytes / (t2["median"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "workspace_bytes": ws2.numel(),
+        "workspace_bytes_one_pass": 2048 * H2 * 4 * (Rec128 + 2 * d * d + 2 * 32 * d) + H2 * 4 * d * d,
+    }
+    del x2, g2, grads2, ws2
+    torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------ CPU baselines (oracle)
     cpu = None

@@ -41,6 +41,7 @@
 // recurrence multiplies the state from the left.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
 #include <type_traits>
 
 #include "kda_device.h"
@@ -90,12 +91,34 @@ __device__ __forceinline__ int seq_len(const BackwardArgs& a, int n) {
     return a.cu ? max(a.cu[n + 1] - a.cu[n], 0) : a.T;
 }
 
+__device__ __forceinline__ int seq_chunks(const BackwardArgs& a, int n) { return (seq_len(a, n) + BC - 1) / BC; }
+
+// Per-chunk slot of chunk i of sequence n, and the state slot of its entry state (i = the
+// chunk count: the final state), in the compact layout or in the current window's.
+__device__ __forceinline__ int chunk_slot(const BackwardArgs& a, int n, int i) {
+    return a.W ? n * a.W + (i - a.w0) : chunk0(a, n) + i;
+}
+__device__ __forceinline__ size_t state_slot(const BackwardArgs& a, int n, int i) {
+    return a.W ? (size_t)n * (a.W + 1) + (i - a.w0) : (size_t)chunk0(a, n) + n + i;
+}
+
 struct ChunkPos {
     int n, i, t0, len;   // sequence, chunk within it, first token row of [B*T], valid rows
 };
 
+// Chunk of per-chunk slot j (the compact layout, or the current window's).
 __device__ bool chunk_pos(const BackwardArgs& a, int j, ChunkPos& p) {
     int n;
+    if (a.W) {
+        n = j / a.W;
+        const int i = a.w0 + j % a.W;
+        if (n >= a.N || i >= seq_chunks(a, n)) return false;
+        p.n = n;
+        p.i = i;
+        p.t0 = seq_first_token(a, n) + i * BC;
+        p.len = min(BC, seq_len(a, n) - i * BC);
+        return true;
+    }
     if (!a.cu) {
         const int cps = (a.T + BC - 1) / BC;
         if (cps == 0) return false;
@@ -460,16 +483,20 @@ __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
     int u, jt;
     unit_tile(blockIdx.x, gridDim.x, NTILE, u, jt);
     const int n = u / a.H, h = u % a.H, tid = threadIdx.x, w = tid >> 6;
-    const int c0 = chunk0(a, n), L = seq_len(a, n), nch = (L + BC - 1) / BC, tok0 = seq_first_token(a, n);
+    const int L = seq_len(a, n), nch = (L + BC - 1) / BC, tok0 = seq_first_token(a, n);
     const size_t DD = (size_t)D * D;
-    init_tile<D>(sS, LT, a.S0 ? a.S0 + (size_t)u * DD + jt * TW : nullptr);
+    // chunks [i0, i1) of the sequence: all of them, or the window's
+    const int i0 = a.W ? a.w0 : 0, i1 = a.W ? min(nch, a.w0 + a.W) : nch;
+    if (a.W && a.w0 > 0 && nch <= a.w0) return;   // the sequence ended before this window
+    const float* init = a.W && a.w0 > 0 ? a.ckpt + ((size_t)(a.wi - 1) * a.N * a.H + u) * DD : a.S0 ? a.S0 + (size_t)u * DD : nullptr;
+    init_tile<D>(sS, LT, init ? init + jt * TW : nullptr);
     // the next chunk's operands are fetched into registers while this chunk computes
     Stage<BC, D> rKp, rKpp;
     Stage<BC, BC> rM;
     StageRows<IN, TW> rV;
     float rEm = 0.f, rEn = 0.f, rB = 0.f;
     auto fetch = [&](int i) __attribute__((always_inline)) {
-        const float* rec = a.prep + cslot(a, c0 + i, h) * Rec<D>::SIZE;
+        const float* rec = a.prep + cslot(a, chunk_slot(a, n, i), h) * Rec<D>::SIZE;
         rKp.load(rec + Rec<D>::KP, D);
         rKpp.load(rec + Rec<D>::KPP, D);
         rM.load(rec + Rec<D>::M, BC);
@@ -478,8 +505,8 @@ __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
         rB = rec[Rec<D>::BETA + (tid & (BC - 1))];
         rV.load(a.v, tok0 + i * BC, min(BC, L - i * BC), a.H, h, D, jt * TW);
     };
-    if (nch > 0) fetch(0);
-    for (int i = 0; i < nch; ++i) {
+    if (i1 > i0) fetch(i0);
+    for (int i = i0; i < i1; ++i) {
         lds_barrier();
         rKp.store(sKp, LD);
         rKpp.store(sKpp, LD);
@@ -490,15 +517,15 @@ __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
             sEn[tid] = rEn;
         }
         if (tid < BC) sB[tid] = rB;
-        if (i + 1 < nch) fetch(i + 1);
+        if (i + 1 < i1) fetch(i + 1);
         lds_barrier();
-        // keep the entry state, then scale it to S_m
-        float* slot = a.states + sslot(a, c0 + n + i, h) * DD + jt * TW;
+        // keep the entry state (not in the checkpoint sweep), then scale it to S_m
+        float* slot = a.states + sslot(a, state_slot(a, n, i), h) * DD + jt * TW;
         for (int e = tid; e < D * TW / 4; e += BT) {
             const int r = e / (TW / 4), c = 4 * (e % (TW / 4));
             const v4f x = *reinterpret_cast<const v4f*>(sS + r * LT + c);
             const float m = sEm[r];
-            *reinterpret_cast<v4f*>(slot + (size_t)r * D + c) = x;
+            if (!a.ckpt_only) *reinterpret_cast<v4f*>(slot + (size_t)r * D + c) = x;
             *reinterpret_cast<v4f*>(sS + r * LT + c) = v4f{x.x * m, x.y * m, x.z * m, x.w * m};
         }
         lds_barrier();
@@ -510,11 +537,11 @@ __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
             for (int v = 0; v < 4; ++v) sR[kh * BC * LT + (16 * rt + acc_row(v)) * LT + acc_col()] = acc[v];
         }
         lds_barrier();
-        float* rout = a.rbuf + cslot(a, c0 + i, h) * BC * D + jt * TW;
+        float* rout = a.rbuf + cslot(a, chunk_slot(a, n, i), h) * BC * D + jt * TW;
         for (int e = tid; e < BC * TW; e += BT) {   // R = V - K' S_m (kept for the gradient step), Y = Diag(beta) R
             const int r = e / TW, c = e % TW;
             const float rr = sV[r * LT + c] - sR[r * LT + c] - sR[BC * LT + r * LT + c];
-            rout[(size_t)r * D + c] = rr;
+            if (!a.ckpt_only) rout[(size_t)r * D + c] = rr;
             sR[r * LT + c] = sB[r] * rr;
         }
         lds_barrier();
@@ -538,7 +565,13 @@ __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
         }
     }
     __syncthreads();
-    float* slot = a.states + sslot(a, c0 + n + nch, h) * DD + jt * TW;
+    // the exit state: the final state or the window's last slot, or in the checkpoint sweep the
+    // next window's entry state (only for a sequence that goes on)
+    float* slot = a.states + sslot(a, state_slot(a, n, i1), h) * DD + jt * TW;
+    if (a.ckpt_only) {
+        if (i1 >= nch) return;
+        slot = a.ckpt + ((size_t)a.wi * a.N * a.H + u) * DD + jt * TW;
+    }
     for (int e = tid; e < D * TW / 4; e += BT) {
         const int r = e / (TW / 4), c = 4 * (e % (TW / 4));
         *reinterpret_cast<v4f*>(slot + (size_t)r * D + c) = *reinterpret_cast<const v4f*>(sS + r * LT + c);
@@ -556,16 +589,20 @@ __global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
     int u, jt;
     unit_tile(blockIdx.x, gridDim.x, NTILE, u, jt);
     const int n = u / a.H, h = u % a.H, tid = threadIdx.x, w = tid >> 6;
-    const int c0 = chunk0(a, n), L = seq_len(a, n), nch = (L + BC - 1) / BC, tok0 = seq_first_token(a, n);
+    const int L = seq_len(a, n), nch = (L + BC - 1) / BC, tok0 = seq_first_token(a, n);
     const size_t DD = (size_t)D * D;
-    init_tile<D>(sS, LT, a.dS_final ? a.dS_final + (size_t)u * DD + jt * TW : nullptr);
+    const int i0 = a.W ? a.w0 : 0, i1 = a.W ? min(nch, a.w0 + a.W) : nch;
+    if (a.W && a.w0 > 0 && nch <= a.w0) return;   // the sequence ended before this window
+    // dS_final where the sequence ends in this window, else the gradient the later window left
+    const float* init = a.W && nch > a.w0 + a.W ? a.dcarry + (size_t)u * DD : a.dS_final ? a.dS_final + (size_t)u * DD : nullptr;
+    init_tile<D>(sS, LT, init ? init + jt * TW : nullptr);
     // the previous chunk's operands are fetched into registers while this chunk computes
     Stage<BC, D> rQp, rKp, rKpp;
     Stage<BC, BC> rM, rP;
     StageRows<IN, TW> rO;
     float rEm = 0.f, rEn = 0.f, rB = 0.f;
     auto fetch = [&](int i) __attribute__((always_inline)) {
-        const float* rec = a.prep + cslot(a, c0 + i, h) * Rec<D>::SIZE;
+        const float* rec = a.prep + cslot(a, chunk_slot(a, n, i), h) * Rec<D>::SIZE;
         rQp.load(rec + Rec<D>::QP, D);
         rKp.load(rec + Rec<D>::KP, D);
         rKpp.load(rec + Rec<D>::KPP, D);
@@ -576,9 +613,9 @@ __global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
         rB = rec[Rec<D>::BETA + (tid & (BC - 1))];
         rO.load(a.dO, tok0 + i * BC, min(BC, L - i * BC), a.H, h, D, jt * TW);
     };
-    if (nch > 0) fetch(nch - 1);
-    for (int i = nch - 1; i >= 0; --i) {
-        const int j = c0 + i;
+    if (i1 > i0) fetch(i1 - 1);
+    for (int i = i1 - 1; i >= i0; --i) {
+        const int j = chunk_slot(a, n, i);
         lds_barrier();
         rQp.store(sQp, LD);
         rKp.store(sKp, LD);
@@ -591,7 +628,7 @@ __global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
             sEn[tid] = rEn;
         }
         if (tid < BC) sB[tid] = rB;
-        if (i > 0) fetch(i - 1);
+        if (i > i0) fetch(i - 1);
         lds_barrier();
         // keep this chunk's dS_next, then scale it to dS_n
         float* slot = a.dstates + cslot(a, j, h) * DD + jt * TW;
@@ -646,10 +683,12 @@ __global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
         }
     }
     __syncthreads();
-    if (a.dS0) {
+    // dS0 after the first window; before it, the gradient for the window before this one
+    float* out = a.W && a.w0 > 0 ? a.dcarry : a.dS0;
+    if (out) {
         for (int e = tid; e < D * TW / 4; e += BT) {
             const int r = e / (TW / 4), c = 4 * (e % (TW / 4));
-            *reinterpret_cast<v4f*>(a.dS0 + (size_t)u * DD + (size_t)r * D + jt * TW + c) =
+            *reinterpret_cast<v4f*>(out + (size_t)u * DD + (size_t)r * D + jt * TW + c) =
                 *reinterpret_cast<const v4f*>(sS + r * LT + c);
         }
     }
@@ -681,7 +720,7 @@ __global__ __launch_bounds__(grad_threads<D>()) void grad_kernel(BackwardArgs a)
     const int tid = threadIdx.x, w = tid >> 6;
     const size_t DD = (size_t)D * D;
     const float* rec = a.prep + cslot(a, j, h) * Rec<D>::SIZE;
-    const size_t slot = (size_t)(chunk0(a, p.n) + p.n + p.i);
+    const size_t slot = state_slot(a, p.n, p.i);
     const float* S = a.states + sslot(a, slot, h) * DD;
     const float* Snext = a.states + sslot(a, slot + 1, h) * DD;
     const float* dS = a.dstates + cslot(a, j, h) * DD;
@@ -891,17 +930,41 @@ __global__ __launch_bounds__(grad_threads<D>()) void grad_kernel(BackwardArgs a)
 }
 
 template <int D, class IN, bool OB, bool SG>
-hipError_t launch_typed(const BackwardArgs& a, int nc_max, hipStream_t st) {
+hipError_t launch_typed(BackwardArgs a, int nc_max, int n_win, hipStream_t st) {
     const int units = a.N * a.H;
     if (a.cu) {
         seq_scan_kernel<<<1, BT, 0, st>>>(a.cu, a.N, a.seq_chunk0);
     }
-    if (nc_max > 0) prep_kernel<D, IN, SG><<<nc_max * a.H, BT, 0, st>>>(a);
-    if (units > 0) {
+    if (!a.W) {
+        if (nc_max > 0) prep_kernel<D, IN, SG><<<nc_max * a.H, BT, 0, st>>>(a);
+        if (units > 0) {
+            state_fwd_kernel<D, IN><<<units * (D / TW), BT, 0, st>>>(a);
+            state_rev_kernel<D, IN><<<units * (D / TW), BT, 0, st>>>(a);
+        }
+        if (nc_max > 0) grad_kernel<D, IN, OB, SG><<<nc_max * a.H, grad_threads<D>(), 0, st>>>(a);
+        return hipGetLastError();
+    }
+    // Windows of W chunks per sequence.  A forward sweep over windows 0..n_win-2 keeps only the
+    // entry state of every later window; then, from the last window to the first, each window
+    // rebuilds its chunk records and entry states, runs the reverse pass from the state gradient
+    // the later window left, and takes its chunks' gradients.
+    const int grid = a.N * a.W * a.H;
+    for (int wi = 0; wi + 1 < n_win; ++wi) {
+        a.wi = wi;
+        a.w0 = wi * a.W;
+        a.ckpt_only = 1;
+        prep_kernel<D, IN, SG><<<grid, BT, 0, st>>>(a);
+        state_fwd_kernel<D, IN><<<units * (D / TW), BT, 0, st>>>(a);
+    }
+    a.ckpt_only = 0;
+    for (int wi = n_win - 1; wi >= 0; --wi) {
+        a.wi = wi;
+        a.w0 = wi * a.W;
+        prep_kernel<D, IN, SG><<<grid, BT, 0, st>>>(a);
         state_fwd_kernel<D, IN><<<units * (D / TW), BT, 0, st>>>(a);
         state_rev_kernel<D, IN><<<units * (D / TW), BT, 0, st>>>(a);
+        grad_kernel<D, IN, OB, SG><<<grid, grad_threads<D>(), 0, st>>>(a);
     }
-    if (nc_max > 0) grad_kernel<D, IN, OB, SG><<<nc_max * a.H, grad_threads<D>(), 0, st>>>(a);
     return hipGetLastError();
 }
 
@@ -914,6 +977,61 @@ BackwardPlan plan_backward(int B, int T, int H, int D, int N, bool varlen) {
     const size_t rec = D == 64 ? Rec<64>::SIZE : Rec<128>::SIZE;
     auto up256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
     pl.nc_max = nc;
+    // per (chunk, head): record, entry state, state gradient, R, dE
+    const size_t per_chunk = sizeof(float) * (rec + 2 * (size_t)D * D + 2 * (size_t)BC * D);
+    const size_t state = sizeof(float) * (size_t)D * D;
+    const size_t units = (size_t)N * H;
+    size_t limit = kBwdWorkspaceLimit;
+    if (const char* e = std::getenv("KDA_BWD_WORKSPACE_LIMIT")) limit = std::strtoull(e, nullptr, 10);
+    const size_t full = nc * H * per_chunk + units * state;
+    const int cmax = (T + BC - 1) / BC;
+    if (!varlen && full > limit && cmax > 1 && units > 0) {
+        // Windows of W chunks: the largest W whose data, W + 1 states per (sequence, head) and
+        // one checkpoint per later window plus the carried gradient, fit the limit; when none
+        // does, the W that needs the least.
+        auto need = [&](int w) {
+            const size_t nw = (size_t)((cmax + w - 1) / w);
+            return units * ((size_t)w * per_chunk + state + nw * state);
+        };
+        int best = 1;
+        size_t best_need = need(1);
+        int chosen = 0;
+        for (int k = 1; k <= cmax; ++k) {
+            const int w = (cmax + k - 1) / k;
+            if ((cmax + w - 1) / w != k) continue;   // the same W as a smaller k
+            const size_t x = need(w);
+            if (x <= limit) {
+                chosen = w;
+                break;
+            }
+            if (x < best_need) {
+                best_need = x;
+                best = w;
+            } else if ((size_t)k * k > 4 * (size_t)cmax) {
+                break;   // past the least
+            }
+        }
+        pl.W = chosen ? chosen : best;
+        pl.n_win = (cmax + pl.W - 1) / pl.W;
+        size_t off = 0;
+        pl.off_seq = 0;
+        pl.off_prep = off;
+        off += up256(sizeof(float) * units * pl.W * rec);
+        pl.off_states = off;
+        off += up256(state * units * (pl.W + 1));
+        pl.off_dstates = off;
+        off += up256(state * units * pl.W);
+        pl.off_r = off;
+        off += up256(sizeof(float) * units * pl.W * BC * D);
+        pl.off_de = off;
+        off += up256(sizeof(float) * units * pl.W * BC * D);
+        pl.off_ckpt = off;
+        off += up256(state * units * (pl.n_win - 1));
+        pl.off_dcarry = off;
+        off += up256(state * units);
+        pl.workspace_bytes = off;
+        return pl;
+    }
     size_t off = 0;
     pl.off_seq = off;
     off += up256(varlen ? sizeof(int32_t) * (size_t)(N + 1) : 0);
@@ -940,11 +1058,20 @@ hipError_t launch_backward(BackwardArgs a, const BackwardPlan& pl, void* workspa
     a.rbuf = reinterpret_cast<float*>(ws + pl.off_r);
     a.debuf = reinterpret_cast<float*>(ws + pl.off_de);
     const int nc = static_cast<int>(pl.nc_max);
-    a.ncs = nc;
-    a.nss = nc + a.N;
+    a.W = pl.W;
+    if (pl.W) {
+        a.ckpt = reinterpret_cast<float*>(ws + pl.off_ckpt);
+        a.dcarry = reinterpret_cast<float*>(ws + pl.off_dcarry);
+        a.ncs = a.N * pl.W;
+        a.nss = a.N * (pl.W + 1);
+    } else {
+        a.ncs = nc;
+        a.nss = nc + a.N;
+    }
+    const int nw = pl.n_win;
 #define KDA_BWD_CASE(DD, IN, OB)                                                              \
     if (a.D == DD && a.in_bf16 == std::is_same<IN, BF16>::value && a.out_bf16 == OB)         \
-        return a.scalar_gate ? launch_typed<DD, IN, OB, true>(a, nc, st) : launch_typed<DD, IN, OB, false>(a, nc, st);
+        return a.scalar_gate ? launch_typed<DD, IN, OB, true>(a, nc, nw, st) : launch_typed<DD, IN, OB, false>(a, nc, nw, st);
     KDA_BWD_CASE(128, BF16, false)
     KDA_BWD_CASE(128, BF16, true)
     KDA_BWD_CASE(128, F32, false)

@@ -214,6 +214,38 @@ def test_backward_workspace_query(lib):
     assert q(1, 64, 2, 128, 128, 1, False, chunk=64) == 0
 
 
+def test_backward_windowed_workspace(lib, monkeypatch):
+    """Past the workspace limit (2 GiB) an equal-length backward runs in windows of W chunks per
+    sequence: per (sequence, head) W chunks of data, W + 1 states, one checkpoint per later
+    window and the carried state gradient."""
+    q = kda.kda_chunk_bwd_workspace_bytes
+    up = lambda x: (x + 255) // 256 * 256
+    rec = 4 * 32 * 128 + 3 * 32 * 32 + 2 * 128 + 32
+    per_chunk = 4 * (rec + 2 * 128 * 128 + 2 * 32 * 128)
+    st = 4 * 128 * 128
+
+    def windowed(units, W, n_win):
+        return (up(4 * units * W * rec) + up(st * units * (W + 1)) + up(st * units * W) +
+                2 * up(4 * units * W * 32 * 128) + up(st * units * (n_win - 1)) + up(st * units))
+    # training shape: 1.99 GB, under the limit: one pass, unchanged
+    assert q(4, 4096, 16, 128, 128, 4, False) == up(4 * 512 * 16 * rec) + up(st * 516 * 16) + \
+        up(st * 512 * 16) + 2 * up(4 * 512 * 16 * 32 * 128)
+    # long context (2048 chunks, 32 heads): 8 windows of 256 chunks, 2.01 GB instead of 15.9 GB
+    lc = q(1, 65536, 32, 128, 128, 1, False)
+    assert lc == windowed(32, 256, 8) and lc <= 2 << 30
+    assert 2048 * 32 * per_chunk > 15.9e9
+    # a smaller limit (the environment override) gives smaller windows: 29 windows of 71 chunks
+    monkeypatch.setenv("KDA_BWD_WORKSPACE_LIMIT", str(600 << 20))
+    assert q(1, 65536, 32, 128, 128, 1, False) == windowed(32, 71, 29) <= 600 << 20
+    assert q(2, 1000, 2, 128, 128, 2, False) == up(4 * 64 * 2 * rec) + up(st * 66 * 2) + \
+        up(st * 64 * 2) + 2 * up(4 * 64 * 2 * 32 * 128)   # 2 x 32 chunks: one pass
+    # no window fits 4 MiB: the least, 11 windows of 3 chunks (6.06 MB)
+    monkeypatch.setenv("KDA_BWD_WORKSPACE_LIMIT", str(4 << 20))
+    assert q(2, 1000, 2, 128, 128, 2, False) == windowed(4, 3, 11)
+    # packed batches keep one pass
+    assert q(1, 1000, 2, 64, 64, 3, True) > 0
+
+
 def test_backward_argument_errors(lib):
     outs = {n: ctypes.c_void_p((10 + i) << 40) for i, n in enumerate(("dq", "dk", "dv", "dg", "db", "dS0"))}
 

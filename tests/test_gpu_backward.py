@@ -203,6 +203,71 @@ def test_matches_forward_directional_derivative():
     assert abs(want - fd) <= 1e-3 * max(1.0, abs(fd))
 
 
+# ------------------------------------------------------------------ windowed plan (memory control)
+WINDOW_CASES = [   # (label, make_prefill overrides, limit in bytes, expected windows of W chunks)
+    ("bf16 d128 ragged", dict(w=1, B=2, T=1000, H=2, s0=True), 4 << 20, (3, 11)),
+    ("fp32 d64 ragged", dict(w=0, B=2, T=1000, H=3, D=64, s0=True), 3 << 20, None),
+    ("bf16 d128 two windows", dict(w=2, B=1, T=2000, H=2, s0=True), 20 << 20, None),
+]
+
+
+@pytest.mark.parametrize("label,kw,limit,win", WINDOW_CASES, ids=[c[0] for c in WINDOW_CASES])
+def test_windowed_backward(label, kw, limit, win, monkeypatch):
+    """Past the workspace limit an equal-length backward runs window by window (a forward sweep
+    keeps each window's entry state, then the windows run from last to first, each carrying the
+    state gradient to the one before).  Every chunk's arithmetic is that of the one-pass plan, so
+    the gradients are bitwise equal to it, and within the parity bound of the oracle."""
+    kda = _kda()
+    kw = dict(kw)
+    w = W[kw.pop("w")]
+    d = inputs.make_prefill(w, seed=241, **kw)
+    g = inputs.make_output_grads(d, seed=242)
+    B, T, H, D = d["B"], d["T"], d["H"], d["D"]
+    one = kda.kda_chunk_bwd_workspace_bytes(B, T, H, D, D, B, False)
+    print(f"[backward] windowed {label}: B={B} T={T} H={H} D={D}, limit {limit}", flush=True)
+    ref_one = gpu_bwd(d, g)
+    monkeypatch.setenv("KDA_BWD_WORKSPACE_LIMIT", str(limit))
+    ws = kda.kda_chunk_bwd_workspace_bytes(B, T, H, D, D, B, False)
+    assert ws < one
+    if win is not None:   # W chunks per window, n windows: W + 1 states and n - 1 checkpoints
+        Wc, n = win
+        assert (T + 31) // 32 > Wc * (n - 1)
+    got = gpu_bwd(d, g)
+    for name in ref_one:
+        assert np.array_equal(got[name], ref_one[name]), f"{label}: {name} differs from the one-pass plan"
+    check(d, g, f"windowed {label}")
+    monkeypatch.delenv("KDA_BWD_WORKSPACE_LIMIT")
+
+
+def test_long_context_full_size_windowed_sampled_head():
+    """Long-context workload at full size (B=1, T=65536, H=32, d=128, bf16, S0 != 0): the
+    default plan runs 8 windows of 256 chunks in a 2.0 GB workspace (one pass would take 15.9
+    GB); head 9 against the oracle's gradient."""
+    kda = _kda()
+    x = inputs.device_prefill(W[2])
+    g = inputs.device_output_grads(x, seed=213)
+    B, T, H, D = x["B"], x["T"], x["H"], x["D"]
+    assert kda.kda_chunk_bwd_workspace_bytes(B, T, H, D, D, 1, False) <= 2 << 30
+    print(f"[backward] long context full size, windowed: T={T} H={H}", flush=True)
+    gr = kda.kda_chunk_bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], g["d_o"], x["S0"], None,
+                           g["dS_final"])
+    torch.cuda.synchronize()
+    h = [9]
+    from gated_delta_rule_62_amd.inputs import host_bits
+    args = [host_bits(x[kk][:, :, h]) for kk in ("q", "k", "v", "log_alpha", "beta")]
+    ref = oracle.kda_bwd(*args, host_bits(g["d_o"][:, :, h]), S0=x["S0"][:, h].cpu().numpy(), cu_seqlens=None,
+                         dS_final=g["dS_final"][:, h].cpu().numpy())
+    got = {kk: to_host(t[:, :, h]) if kk != "dS0" else to_host(t[:, h]) for kk, t in gr.items()}
+    err = {}
+    for name in ("dq", "dk", "dv", "dlog_alpha"):
+        err[name] = o_metric(got[name], ref[name])
+    err["dbeta"] = o_metric(got["dbeta"][..., None], ref["dbeta"][..., None])
+    err["dS0"] = state_metric(got["dS0"], ref["dS0"])
+    print("[backward]   head 9: " + "  ".join(f"{kk} {vv:.2e}" for kk, vv in err.items()), flush=True)
+    for name, e in err.items():
+        assert e <= TOL_BF16, f"{name} error {e:.3e}"
+
+
 # ------------------------------------------------------------------ scalar gate (gdn_chunk_bwd)
 @pytest.mark.parametrize("D", [64, 128])
 def test_scalar_gate_fp32_ragged(D):
