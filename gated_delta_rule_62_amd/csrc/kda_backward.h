@@ -27,7 +27,6 @@ struct BackwardArgs {
     // (i - w0).  ckpt holds the entry state of every window after the first, dcarry the state
     // gradient passed from a window to the one before it ([N * H, D, D] each).
     int W = 0, w0 = 0, wi = 0;
-    int ckpt_only = 0;                       // forward state pass: keep only the next checkpoint
     float *ckpt = nullptr, *dcarry = nullptr;
     int B, T, H, D, N;
     bool in_bf16, out_bf16;

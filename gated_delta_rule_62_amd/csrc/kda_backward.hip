@@ -93,13 +93,11 @@ __device__ __forceinline__ int seq_len(const BackwardArgs& a, int n) {
 
 __device__ __forceinline__ int seq_chunks(const BackwardArgs& a, int n) { return (seq_len(a, n) + BC - 1) / BC; }
 
-// Per-chunk slot of chunk i of sequence n, and the state slot of its entry state (i = the
-// chunk count: the final state), in the compact layout or in the current window's.
-__device__ __forceinline__ int chunk_slot(const BackwardArgs& a, int n, int i) {
-    return a.W ? n * a.W + (i - a.w0) : chunk0(a, n) + i;
-}
+// State slot of the entry state of chunk i of sequence n (i = the chunk count: the final state),
+// in the compact layout (WIN false) or in the current window's.
+template <bool WIN>
 __device__ __forceinline__ size_t state_slot(const BackwardArgs& a, int n, int i) {
-    return a.W ? (size_t)n * (a.W + 1) + (i - a.w0) : (size_t)chunk0(a, n) + n + i;
+    return WIN ? (size_t)n * (a.W + 1) + (i - a.w0) : (size_t)chunk0(a, n) + n + i;
 }
 
 struct ChunkPos {
@@ -473,8 +471,10 @@ __global__ __launch_bounds__(BT) void prep_kernel(BackwardArgs a) {
     if (tid < BC) rec[Rec<D>::BETA + tid] = sB[tid];
 }
 
-template <int D, class IN>
+// WM: 0 every chunk (compact layout), 1 the current window, 2 the current window's checkpoint only.
+template <int D, class IN, int WM>
 __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
+    constexpr bool WIN = WM != 0, CKPT = WM == 2;
     constexpr bool SPLIT = std::is_same<IN, BF16>::value;   // split-bf16 products for bf16 inputs
     constexpr int LD = D + 4, LC = BC + 4, LT = TW + 4, NTILE = D / TW;
     __shared__ __attribute__((aligned(16))) float sKp[BC * LD], sKpp[BC * LD], sM[BC * LC];
@@ -486,9 +486,12 @@ __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
     const int L = seq_len(a, n), nch = (L + BC - 1) / BC, tok0 = seq_first_token(a, n);
     const size_t DD = (size_t)D * D;
     // chunks [i0, i1) of the sequence: all of them, or the window's
-    const int i0 = a.W ? a.w0 : 0, i1 = a.W ? min(nch, a.w0 + a.W) : nch;
-    if (a.W && a.w0 > 0 && nch <= a.w0) return;   // the sequence ended before this window
-    const float* init = a.W && a.w0 > 0 ? a.ckpt + ((size_t)(a.wi - 1) * a.N * a.H + u) * DD : a.S0 ? a.S0 + (size_t)u * DD : nullptr;
+    const int i0 = WIN ? a.w0 : 0, i1 = WIN ? min(nch, a.w0 + a.W) : nch;
+    if (WIN && a.w0 > 0 && nch <= a.w0) return;   // the sequence ended before this window
+    // per-chunk and state slots of chunk i: c0 + i and s0 + i
+    const int c0 = WIN ? n * a.W - a.w0 : chunk0(a, n);
+    const size_t s0 = WIN ? (size_t)n * (a.W + 1) - a.w0 : (size_t)c0 + n;
+    const float* init = WIN && a.w0 > 0 ? a.ckpt + ((size_t)(a.wi - 1) * a.N * a.H + u) * DD : a.S0 ? a.S0 + (size_t)u * DD : nullptr;
     init_tile<D>(sS, LT, init ? init + jt * TW : nullptr);
     // the next chunk's operands are fetched into registers while this chunk computes
     Stage<BC, D> rKp, rKpp;
@@ -496,7 +499,7 @@ __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
     StageRows<IN, TW> rV;
     float rEm = 0.f, rEn = 0.f, rB = 0.f;
     auto fetch = [&](int i) __attribute__((always_inline)) {
-        const float* rec = a.prep + cslot(a, chunk_slot(a, n, i), h) * Rec<D>::SIZE;
+        const float* rec = a.prep + cslot(a, c0 + i, h) * Rec<D>::SIZE;
         rKp.load(rec + Rec<D>::KP, D);
         rKpp.load(rec + Rec<D>::KPP, D);
         rM.load(rec + Rec<D>::M, BC);
@@ -520,12 +523,12 @@ __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
         if (i + 1 < i1) fetch(i + 1);
         lds_barrier();
         // keep the entry state (not in the checkpoint sweep), then scale it to S_m
-        float* slot = a.states + sslot(a, state_slot(a, n, i), h) * DD + jt * TW;
+        float* slot = a.states + sslot(a, s0 + i, h) * DD + jt * TW;
         for (int e = tid; e < D * TW / 4; e += BT) {
             const int r = e / (TW / 4), c = 4 * (e % (TW / 4));
             const v4f x = *reinterpret_cast<const v4f*>(sS + r * LT + c);
             const float m = sEm[r];
-            if (!a.ckpt_only) *reinterpret_cast<v4f*>(slot + (size_t)r * D + c) = x;
+            if (!CKPT) *reinterpret_cast<v4f*>(slot + (size_t)r * D + c) = x;
             *reinterpret_cast<v4f*>(sS + r * LT + c) = v4f{x.x * m, x.y * m, x.z * m, x.w * m};
         }
         lds_barrier();
@@ -537,11 +540,11 @@ __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
             for (int v = 0; v < 4; ++v) sR[kh * BC * LT + (16 * rt + acc_row(v)) * LT + acc_col()] = acc[v];
         }
         lds_barrier();
-        float* rout = a.rbuf + cslot(a, chunk_slot(a, n, i), h) * BC * D + jt * TW;
+        float* rout = a.rbuf + cslot(a, c0 + i, h) * BC * D + jt * TW;
         for (int e = tid; e < BC * TW; e += BT) {   // R = V - K' S_m (kept for the gradient step), Y = Diag(beta) R
             const int r = e / TW, c = e % TW;
             const float rr = sV[r * LT + c] - sR[r * LT + c] - sR[BC * LT + r * LT + c];
-            if (!a.ckpt_only) rout[(size_t)r * D + c] = rr;
+            if (!CKPT) rout[(size_t)r * D + c] = rr;
             sR[r * LT + c] = sB[r] * rr;
         }
         lds_barrier();
@@ -567,8 +570,8 @@ __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
     __syncthreads();
     // the exit state: the final state or the window's last slot, or in the checkpoint sweep the
     // next window's entry state (only for a sequence that goes on)
-    float* slot = a.states + sslot(a, state_slot(a, n, i1), h) * DD + jt * TW;
-    if (a.ckpt_only) {
+    float* slot = a.states + sslot(a, s0 + i1, h) * DD + jt * TW;
+    if (CKPT) {
         if (i1 >= nch) return;
         slot = a.ckpt + ((size_t)a.wi * a.N * a.H + u) * DD + jt * TW;
     }
@@ -578,7 +581,7 @@ __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
     }
 }
 
-template <int D, class IN>
+template <int D, class IN, bool WIN>
 __global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
     constexpr bool SPLIT = std::is_same<IN, BF16>::value;   // split-bf16 products for bf16 inputs
     constexpr int LD = D + 4, LC = BC + 4, LT = TW + 4, NTILE = D / TW;
@@ -591,10 +594,11 @@ __global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
     const int n = u / a.H, h = u % a.H, tid = threadIdx.x, w = tid >> 6;
     const int L = seq_len(a, n), nch = (L + BC - 1) / BC, tok0 = seq_first_token(a, n);
     const size_t DD = (size_t)D * D;
-    const int i0 = a.W ? a.w0 : 0, i1 = a.W ? min(nch, a.w0 + a.W) : nch;
-    if (a.W && a.w0 > 0 && nch <= a.w0) return;   // the sequence ended before this window
+    const int i0 = WIN ? a.w0 : 0, i1 = WIN ? min(nch, a.w0 + a.W) : nch;
+    if (WIN && a.w0 > 0 && nch <= a.w0) return;   // the sequence ended before this window
+    const int c0 = WIN ? n * a.W - a.w0 : chunk0(a, n);   // per-chunk slot of chunk i: c0 + i
     // dS_final where the sequence ends in this window, else the gradient the later window left
-    const float* init = a.W && nch > a.w0 + a.W ? a.dcarry + (size_t)u * DD : a.dS_final ? a.dS_final + (size_t)u * DD : nullptr;
+    const float* init = WIN && nch > a.w0 + a.W ? a.dcarry + (size_t)u * DD : a.dS_final ? a.dS_final + (size_t)u * DD : nullptr;
     init_tile<D>(sS, LT, init ? init + jt * TW : nullptr);
     // the previous chunk's operands are fetched into registers while this chunk computes
     Stage<BC, D> rQp, rKp, rKpp;
@@ -602,7 +606,7 @@ __global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
     StageRows<IN, TW> rO;
     float rEm = 0.f, rEn = 0.f, rB = 0.f;
     auto fetch = [&](int i) __attribute__((always_inline)) {
-        const float* rec = a.prep + cslot(a, chunk_slot(a, n, i), h) * Rec<D>::SIZE;
+        const float* rec = a.prep + cslot(a, c0 + i, h) * Rec<D>::SIZE;
         rQp.load(rec + Rec<D>::QP, D);
         rKp.load(rec + Rec<D>::KP, D);
         rKpp.load(rec + Rec<D>::KPP, D);
@@ -615,7 +619,7 @@ __global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
     };
     if (i1 > i0) fetch(i1 - 1);
     for (int i = i1 - 1; i >= i0; --i) {
-        const int j = chunk_slot(a, n, i);
+        const int j = c0 + i;
         lds_barrier();
         rQp.store(sQp, LD);
         rKp.store(sKp, LD);
@@ -684,7 +688,7 @@ __global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
     }
     __syncthreads();
     // dS0 after the first window; before it, the gradient for the window before this one
-    float* out = a.W && a.w0 > 0 ? a.dcarry : a.dS0;
+    float* out = WIN && a.w0 > 0 ? a.dcarry : a.dS0;
     if (out) {
         for (int e = tid; e < D * TW / 4; e += BT) {
             const int r = e / (TW / 4), c = 4 * (e % (TW / 4));
@@ -720,7 +724,7 @@ __global__ __launch_bounds__(grad_threads<D>()) void grad_kernel(BackwardArgs a)
     const int tid = threadIdx.x, w = tid >> 6;
     const size_t DD = (size_t)D * D;
     const float* rec = a.prep + cslot(a, j, h) * Rec<D>::SIZE;
-    const size_t slot = state_slot(a, p.n, p.i);
+    const size_t slot = a.W ? state_slot<true>(a, p.n, p.i) : state_slot<false>(a, p.n, p.i);
     const float* S = a.states + sslot(a, slot, h) * DD;
     const float* Snext = a.states + sslot(a, slot + 1, h) * DD;
     const float* dS = a.dstates + cslot(a, j, h) * DD;
@@ -938,8 +942,8 @@ hipError_t launch_typed(BackwardArgs a, int nc_max, int n_win, hipStream_t st) {
     if (!a.W) {
         if (nc_max > 0) prep_kernel<D, IN, SG><<<nc_max * a.H, BT, 0, st>>>(a);
         if (units > 0) {
-            state_fwd_kernel<D, IN><<<units * (D / TW), BT, 0, st>>>(a);
-            state_rev_kernel<D, IN><<<units * (D / TW), BT, 0, st>>>(a);
+            state_fwd_kernel<D, IN, 0><<<units * (D / TW), BT, 0, st>>>(a);
+            state_rev_kernel<D, IN, false><<<units * (D / TW), BT, 0, st>>>(a);
         }
         if (nc_max > 0) grad_kernel<D, IN, OB, SG><<<nc_max * a.H, grad_threads<D>(), 0, st>>>(a);
         return hipGetLastError();
@@ -952,17 +956,15 @@ hipError_t launch_typed(BackwardArgs a, int nc_max, int n_win, hipStream_t st) {
     for (int wi = 0; wi + 1 < n_win; ++wi) {
         a.wi = wi;
         a.w0 = wi * a.W;
-        a.ckpt_only = 1;
         prep_kernel<D, IN, SG><<<grid, BT, 0, st>>>(a);
-        state_fwd_kernel<D, IN><<<units * (D / TW), BT, 0, st>>>(a);
+        state_fwd_kernel<D, IN, 2><<<units * (D / TW), BT, 0, st>>>(a);
     }
-    a.ckpt_only = 0;
     for (int wi = n_win - 1; wi >= 0; --wi) {
         a.wi = wi;
         a.w0 = wi * a.W;
         prep_kernel<D, IN, SG><<<grid, BT, 0, st>>>(a);
-        state_fwd_kernel<D, IN><<<units * (D / TW), BT, 0, st>>>(a);
-        state_rev_kernel<D, IN><<<units * (D / TW), BT, 0, st>>>(a);
+        state_fwd_kernel<D, IN, 1><<<units * (D / TW), BT, 0, st>>>(a);
+        state_rev_kernel<D, IN, true><<<units * (D / TW), BT, 0, st>>>(a);
         grad_kernel<D, IN, OB, SG><<<grid, grad_threads<D>(), 0, st>>>(a);
     }
     return hipGetLastError();
