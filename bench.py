@@ -476,7 +476,19 @@ def main():
            "roofline": {"bound": "hbm", "achieved": gdn_bytes / (gdn_ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
                         "unit": "GB/s", "frac": gdn_bytes / (gdn_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
                         "bytes_per_launch": gdn_bytes, "launch": "gdn_chunk_fwd (all prefill kernels of one call)"}}
-    del xg, og, Sg
+    # The same call with every fused step on (q, k normalised in the kernels, beta and the one
+    # log_alpha per token-head taken as logits, an output gate of N(0,1) logits).
+    gate_g = torch.randn((w6.B, w6.T, w6.H, d), device="cuda").to(torch.bfloat16)
+
+    def call_gdn_fused():
+        kda.gdn_chunk_fwd_fused(xg["q"], xg["k"], xg["v"], xg["log_alpha"], xg["beta"], xg["S0"], None,
+                                qk_l2norm=True, beta_logits=True, decay_logits=(6.0, 16.0), out_gate=gate_g,
+                                o=og, S_final=Sg, workspace=ws, stream=stream)
+    tgf = timed_calls(torch, call_gdn_fused, stream, 3, args.steps)
+    gdn["fused"] = {"workload": "the same with the fused prologue and an output gate (gdn_chunk_fwd_fused)",
+                    "ms_per_call_median": tgf["median"], "ms_per_call_min": tgf["min"],
+                    "vs_plain_call": tgf["median"] / gdn_ms}
+    del xg, og, Sg, gate_g
 
     # ------------------------------------------------------------------ continuation (serving shapes)
     # New tokens on top of a carried state: 256 sequences x 32 heads.  "verify4": 4 tokens each

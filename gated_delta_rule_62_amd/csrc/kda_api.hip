@@ -406,6 +406,25 @@ extern "C" kda_status kda_recurrent_step_fused(const void* q, const void* k, con
                                false, fusion);
 }
 
+extern "C" kda_status gdn_chunk_fwd_fused(const void* q, const void* k, const void* v, const void* log_alpha,
+                                          const void* beta, const float* S0, const int32_t* cu_seqlens,
+                                          int B, int T, int H, int Dk, int Dv, int num_seqs, int chunk,
+                                          kda_dtype in_dtype, kda_dtype out_dtype, void* o, float* S_final,
+                                          void* workspace, size_t workspace_bytes, const kda_fusion* fusion,
+                                          kda_stream_t stream) {
+    return chunk_fwd_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, B, T, H, Dk, Dv, num_seqs, chunk, in_dtype,
+                          out_dtype, o, S_final, workspace, workspace_bytes, stream, true, fusion);
+}
+
+extern "C" kda_status gdn_recurrent_step_fused(const void* q, const void* k, const void* v, const void* log_alpha,
+                                               const void* beta, const float* S_in, float* S_out,
+                                               int N, int H, int Dk, int Dv,
+                                               kda_dtype in_dtype, kda_dtype out_dtype,
+                                               void* o, const kda_fusion* fusion, kda_stream_t stream) {
+    return recurrent_step_impl(q, k, v, log_alpha, beta, S_in, S_out, N, H, Dk, Dv, in_dtype, out_dtype, o, stream,
+                               true, fusion);
+}
+
 extern "C" size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int num_seqs,
                                                 int has_cu_seqlens, int chunk) {
     if (B < 0 || T < 0 || H <= 0 || num_seqs < 0 || !head_ok(Dk, Dv)) return 0;

@@ -458,10 +458,10 @@ hipError_t launch_decode(int D, bool in_bf16, bool out_bf16, const void* q, cons
     const DecodeFusion fu = fused ? DecodeFusion{fusion->flags, fusion->decay_bias, fusion->decay_scale,
                                                  fusion->out_gate}
                                   : DecodeFusion{0, 0.f, 1.f, nullptr};
-    if (fused && scalar_gate) return hipErrorInvalidValue;
 #define KDA_DECODE_CASE(DD, INT, OB)                                                        \
     if (D == DD && in_bf16 == std::is_same<INT, BF16>::value && out_bf16 == OB) {             \
-        if (fused) return launch_decode_t<DD, INT, OB, false, true>(q, k, v, g, b, S_in, S_out, o, units, stream, fu); \
+        if (fused) return scalar_gate ? launch_decode_t<DD, INT, OB, true, true>(q, k, v, g, b, S_in, S_out, o, units, stream, fu) \
+                         : launch_decode_t<DD, INT, OB, false, true>(q, k, v, g, b, S_in, S_out, o, units, stream, fu); \
         return scalar_gate ? launch_decode_t<DD, INT, OB, true>(q, k, v, g, b, S_in, S_out, o, units, stream) \
                            : launch_decode_t<DD, INT, OB, false>(q, k, v, g, b, S_in, S_out, o, units, stream); \
     }

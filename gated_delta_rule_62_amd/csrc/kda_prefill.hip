@@ -1180,6 +1180,35 @@ __device__ __forceinline__ void pipe_body(const KernelArgs& a,
 
     // phase 1: decay prefix (in log2 units) and the decayed, split K / Q planes.  With
     // the previous chunk's buffer `prev`, also that chunk's state factor rho.
+    // fused prologue: per-token sums of squares of k and q over this wave's 32 channels (8 lanes
+    // share a token group), one partial per producer wave
+    auto fused_sumsq = [&](Buf& B) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < TPG; ++i) {
+            float sk = 0.f, sq = 0.f;
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) {
+                sk += R::get(pk[i], ch) * R::get(pk[i], ch);
+                if constexpr (MODE == 0) sq += R::get(pq[i], ch) * R::get(pq[i], ch);
+            }
+            sk = sum_lanes<QPW>(sk);
+            if constexpr (MODE == 0) sq = sum_lanes<QPW>(sq);
+            if ((l % QPW) == 0) {
+                B.nk[w][tg * TPG + i] = sk;
+                if constexpr (MODE == 0) B.nq[w][tg * TPG + i] = sq;
+            }
+        }
+    };
+    // beta of the chunk's tokens (sigmoid of the logits with the fused prologue; padded rows 0)
+    auto stage_beta = [&](Buf& B, int last) __attribute__((always_inline)) {
+        if (tid < C) {
+            float bt = IN::to_f32(pb);
+            if constexpr (FUSE) {
+                if ((a.fuse_flags & kFuseBeta) && tid <= last) bt = sigmoid_f(bt);
+            }
+            B.beta[tid] = bt;
+        }
+    };
     auto produce_decay = [&](Buf& B, int chunk, Buf* prev) {
         const long ts = t0 + static_cast<long>(chunk) * C;
         const int last = static_cast<int>(min(static_cast<long>(C), t1 - ts)) - 1;
@@ -1197,7 +1226,15 @@ __device__ __forceinline__ void pipe_body(const KernelArgs& a,
             }
             float gs[TPG];
 #pragma unroll
-            for (int i = 0; i < TPG; ++i) gs[i] = IN::to_f32(pgs[i]) * kLog2e + (i ? gs[i - 1] : 0.f);
+            for (int i = 0; i < TPG; ++i) {
+                float g2 = IN::to_f32(pgs[i]) * kLog2e;   // log2 of this token's decay
+                if constexpr (FUSE) {
+                    if ((a.fuse_flags & kFuseDecay) && tg * TPG + i <= last)
+                        g2 = log2_sigmoid(IN::to_f32(pgs[i]) + a.decay_bias) / a.decay_scale;
+                }
+                gs[i] = g2 + (i ? gs[i - 1] : 0.f);
+            }
+            if constexpr (FUSE) fused_sumsq(B);
             float incl = gs[TPG - 1];
 #pragma unroll
             for (int dd = QPW; dd < 64; dd <<= 1) {
@@ -1249,7 +1286,7 @@ __device__ __forceinline__ void pipe_body(const KernelArgs& a,
                 }
             }
             stage_v(B);
-            if (tid < C) B.beta[tid] = IN::to_f32(pb);
+            stage_beta(B, last);
             return;
         }
         if (last < C - 1) {   // ragged last chunk: padded rows read as zero
@@ -1270,24 +1307,7 @@ __device__ __forceinline__ void pipe_body(const KernelArgs& a,
                 }
                 gr[i][ch] = g2 + (i ? gr[i - 1][ch] : 0.f);
             }
-        if constexpr (FUSE) {
-            // per-token sums of squares of this wave's 32 channels (8 lanes share a token group)
-#pragma unroll
-            for (int i = 0; i < TPG; ++i) {
-                float sk = 0.f, sq = 0.f;
-#pragma unroll
-                for (int ch = 0; ch < 4; ++ch) {
-                    sk += R::get(pk[i], ch) * R::get(pk[i], ch);
-                    if constexpr (MODE == 0) sq += R::get(pq[i], ch) * R::get(pq[i], ch);
-                }
-                sk = sum_lanes<QPW>(sk);
-                if constexpr (MODE == 0) sq = sum_lanes<QPW>(sq);
-                if ((l % QPW) == 0) {
-                    B.nk[w][tg * TPG + i] = sk;
-                    if constexpr (MODE == 0) B.nq[w][tg * TPG + i] = sq;
-                }
-            }
-        }
+        if constexpr (FUSE) fused_sumsq(B);
         float off[4], bm[4], bn[4];
 #pragma unroll
         for (int ch = 0; ch < 4; ++ch) {
@@ -1369,13 +1389,7 @@ __device__ __forceinline__ void pipe_body(const KernelArgs& a,
             }
         }
         stage_v(B);
-        if (tid < C) {
-            float bt = IN::to_f32(pb);
-            if constexpr (FUSE) {
-                if ((a.fuse_flags & kFuseBeta) && tid <= last) bt = sigmoid_f(bt);
-            }
-            B.beta[tid] = bt;
-        }
+        stage_beta(B, last);
     };
 
     // Tiles of A^T and P^T: tile (rt, ct), ct <= rt, is Ktil_m[ct] against Kbar_m[rt] (or
@@ -1787,7 +1801,7 @@ __device__ __forceinline__ void pipe_body(const KernelArgs& a,
                 if (row < ntok) {
                     float fo = 1.f;
                     if constexpr (SG) fo = B.fo[row];
-                    if constexpr (FUSE) fo = B.os[row];
+                    if constexpr (FUSE) fo = SG ? fo * B.os[row] : B.os[row];
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct) {
                         f32x4 ov = Z[rt][ct] * fo;
@@ -2175,7 +2189,7 @@ __global__ void status_clear_kernel(int* status) {
 
 template <int D, int C, typename IN, bool OB, bool SG = false, bool FUSE = false>
 hipError_t launch_variant(const PrefillArgs& pa, const PrefillPlan& plan, hipStream_t stream) {
-    static_assert(!FUSE || (C == 32 && !SG), "the fused prologue runs on the pipelined 32-token KDA kernel");
+    static_assert(!FUSE || C == 32, "the fused prologue runs on the pipelined 32-token kernel");
     static_assert(!SG || C == 32, "the scalar gate runs on the pipelined 32-token kernel");
     KernelArgs a;
     a.q = pa.q; a.k = pa.k; a.v = pa.v; a.g = pa.g; a.beta = pa.beta;
@@ -2352,7 +2366,8 @@ hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan, hipStre
             if constexpr (CC == 32) {                                                                  \
                 if (a.scalar_gate && !a.fuse_flags && !a.out_gate)                                     \
                     return launch_variant<DD, CC, INT, OB, true>(a, plan, stream);                      \
-                if (!a.scalar_gate) return launch_variant<DD, CC, INT, OB, false, true>(a, plan, stream); \
+                if (a.scalar_gate) return launch_variant<DD, CC, INT, OB, true, true>(a, plan, stream);  \
+                return launch_variant<DD, CC, INT, OB, false, true>(a, plan, stream);                   \
             }                                                                                          \
             return hipErrorInvalidValue;                                                               \
         }                                                                                              \

@@ -182,11 +182,11 @@ def make_output_grads(d: dict, seed: int, *, dS_final: bool = True, scale: float
 
 
 def make_raw_prefill(seed: int, *, B=1, T=64, H=2, D=128, dtype="bf16", num_seqs=None, lengths=None,
-                     qk_scale=3.0, s0=True):
+                     qk_scale=3.0, s0=True, scalar_gate=False):
     """Unconstrained inputs for the fused prologue: q, k ~ qk_scale * N(0,1) (not normalised),
-    beta and log_alpha logits ~ N(0,1) (log_alpha [B, T, H, D]), output-gate logits ~ N(0,1),
-    v ~ N(0,1), S0 ~ 0.02 N(0,1); drawn in that order.  Same dict layout as make_prefill plus
-    ``gate``."""
+    beta and log_alpha logits ~ N(0,1) (log_alpha [B, T, H, D], or [B, T, H] with scalar_gate),
+    output-gate logits ~ N(0,1), v ~ N(0,1), S0 ~ 0.02 N(0,1); drawn in that order.  Same dict
+    layout as make_prefill plus ``gate``."""
     rng = np.random.default_rng(seed)
     if lengths is not None:
         lengths = np.asarray(lengths, dtype=np.int64)
@@ -200,13 +200,13 @@ def make_raw_prefill(seed: int, *, B=1, T=64, H=2, D=128, dtype="bf16", num_seqs
     k = np.float32(qk_scale) * _normal(rng, shp)
     v = _normal(rng, shp)
     beta = _normal(rng, (B, T, H))
-    g = _normal(rng, shp)
+    g = _normal(rng, (B, T, H) if scalar_gate else shp)
     gate = _normal(rng, shp)
     S0 = (np.float32(0.02) * _normal(rng, (N, H, D, D))) if s0 else None
     return dict(q=_cast(q, dtype), k=_cast(k, dtype), v=_cast(v, dtype), log_alpha=_cast(g, dtype),
                 beta=_cast(beta, dtype), gate=_cast(gate, dtype), S0=S0,
                 cu_seqlens=None if cu is None else cu.astype(np.int32),
-                B=B, T=T, H=H, D=D, N=N, dtype=dtype)
+                B=B, T=T, H=H, D=D, N=N, dtype=dtype, scalar_gate=scalar_gate)
 
 
 # ---------------------------------------------------------------- decode

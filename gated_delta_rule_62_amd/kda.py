@@ -24,7 +24,8 @@ CHUNK = 0          # library default chunk length (32 tokens); 32 and 64 are bui
 EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_step",
             "kda_recurrent_fwd", "gdn_chunk_fwd", "gdn_recurrent_step", "gdn_recurrent_fwd",
             "kda_chunk_fwd_fused", "kda_recurrent_step_fused", "kda_chunk_bwd_workspace_bytes",
-            "kda_chunk_bwd", "gdn_chunk_bwd", "kda_chunk_fwd_noalloc")
+            "kda_chunk_bwd", "gdn_chunk_bwd", "kda_chunk_fwd_noalloc", "gdn_chunk_fwd_fused",
+            "gdn_recurrent_step_fused")
 KDA_FUSE_QK_L2NORM, KDA_FUSE_BETA_SIGMOID, KDA_FUSE_DECAY_LOGSIGMOID = 1, 2, 4
 
 
@@ -68,6 +69,10 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd_fused.restype = i32
     lib.kda_recurrent_step_fused.argtypes = [vp] * 7 + [i32] * 4 + [i32, i32] + [vp, fp, vp]
     lib.kda_recurrent_step_fused.restype = i32
+    lib.gdn_chunk_fwd_fused.argtypes = lib.kda_chunk_fwd_fused.argtypes
+    lib.gdn_chunk_fwd_fused.restype = i32
+    lib.gdn_recurrent_step_fused.argtypes = lib.kda_recurrent_step_fused.argtypes
+    lib.gdn_recurrent_step_fused.restype = i32
     lib.kda_chunk_bwd_workspace_bytes.argtypes = [i32] * 8
     lib.kda_chunk_bwd_workspace_bytes.restype = sz
     lib.kda_chunk_bwd.argtypes = [vp] * 9 + [i32] * 7 + [i32, i32] + [vp] * 6 + [vp, sz, vp]
@@ -261,7 +266,8 @@ def _fusion(qk_l2norm=False, beta_logits=False, decay_logits=None, out_gate=None
 
 def kda_chunk_fwd_fused(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, qk_l2norm=False,
                         beta_logits=False, decay_logits=None, out_gate=None, out_dtype=None, o=None,
-                        S_final=None, workspace=None, chunk=CHUNK, stream=None, want_final=True):
+                        S_final=None, workspace=None, chunk=CHUNK, stream=None, want_final=True,
+                        _fn="kda_chunk_fwd_fused"):
     """Prefill with the fused prologue / epilogue: q, k unnormalised (qk_l2norm), beta as
     logits (beta_logits), log_alpha as logits a with decay_logits = (bias, scale) giving
     logsigmoid(a + bias) / scale, and an optional output gate (logits shaped like o)."""
@@ -282,18 +288,19 @@ def kda_chunk_fwd_fused(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, q
         own.append(workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     f = _fusion(qk_l2norm, beta_logits, decay_logits, out_gate)
-    st = load_library().kda_chunk_fwd_fused(
+    st = getattr(load_library(), _fn)(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
         B, T, H, Dk, Dv, N, chunk, _dtype_code(q.dtype), _dtype_code(o.dtype),
         _ptr(o), _ptr(S_final), _ptr(workspace), ws_bytes, ctypes.byref(f), _stream_ptr(stream))
     if st != KDA_OK:
-        raise KDAError(st, "kda_chunk_fwd_fused")
+        raise KDAError(st, _fn)
     _keep_for(stream, *own)
     return o, S_final
 
 
 def kda_recurrent_step_fused(q, k, v, log_alpha, beta, S_in, S_out=None, *, qk_l2norm=False, beta_logits=False,
-                             decay_logits=None, out_gate=None, out_dtype=None, o=None, stream=None):
+                             decay_logits=None, out_gate=None, out_dtype=None, o=None, stream=None,
+                             _fn="kda_recurrent_step_fused"):
     """Decode one token with the fused prologue / epilogue (see kda_chunk_fwd_fused)."""
     N, H, Dk = q.shape
     Dv = v.shape[-1]
@@ -305,13 +312,23 @@ def kda_recurrent_step_fused(q, k, v, log_alpha, beta, S_in, S_out=None, *, qk_l
         S_out = S_in
     _check_dev(q, k, v, log_alpha, beta, S_in, S_out, o, out_gate)
     f = _fusion(qk_l2norm, beta_logits, decay_logits, out_gate)
-    st = load_library().kda_recurrent_step_fused(
+    st = getattr(load_library(), _fn)(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S_in), _ptr(S_out),
         N, H, Dk, Dv, _dtype_code(q.dtype), _dtype_code(o.dtype), _ptr(o), ctypes.byref(f), _stream_ptr(stream))
     if st != KDA_OK:
-        raise KDAError(st, "kda_recurrent_step_fused")
+        raise KDAError(st, _fn)
     _keep_for(stream, o if o_new else None)
     return o, S_out
+
+
+def gdn_chunk_fwd_fused(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, **kw):
+    """gdn_chunk_fwd with the fused prologue / epilogue (log_alpha [B, T, H]; see kda_chunk_fwd_fused)."""
+    return kda_chunk_fwd_fused(q, k, v, log_alpha, beta, S0, cu_seqlens, _fn="gdn_chunk_fwd_fused", **kw)
+
+
+def gdn_recurrent_step_fused(q, k, v, log_alpha, beta, S_in, S_out=None, **kw):
+    """gdn_recurrent_step with the fused prologue / epilogue (log_alpha [N, H])."""
+    return kda_recurrent_step_fused(q, k, v, log_alpha, beta, S_in, S_out, _fn="gdn_recurrent_step_fused", **kw)
 
 
 def kda_chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, num_seqs, has_cu_seqlens, chunk=CHUNK) -> int:

@@ -261,6 +261,26 @@ kda_status gdn_recurrent_step(const void* q, const void* k, const void* v, const
                               kda_dtype in_dtype, kda_dtype out_dtype,
                               void* o, kda_stream_t stream);
 
+/*
+ * Scalar gate with the fused prologue / epilogue: gdn_chunk_fwd and gdn_recurrent_step
+ * plus a kda_fusion, with the maps of kda_chunk_fwd_fused applied to the scalar-gate
+ * inputs (KDA_FUSE_DECAY_LOGSIGMOID maps the one log_alpha logit per token and head).
+ * gdn_chunk_fwd_fused supports chunk 0 or 32 and uses kda_chunk_fwd_workspace_bytes().
+ */
+kda_status gdn_chunk_fwd_fused(const void* q, const void* k, const void* v, const void* log_alpha,
+                               const void* beta, const float* S0, const int32_t* cu_seqlens,
+                               int B, int T, int H, int Dk, int Dv, int num_seqs, int chunk,
+                               kda_dtype in_dtype, kda_dtype out_dtype,
+                               void* o, float* S_final,
+                               void* workspace, size_t workspace_bytes,
+                               const kda_fusion* fusion, kda_stream_t stream);
+
+kda_status gdn_recurrent_step_fused(const void* q, const void* k, const void* v, const void* log_alpha,
+                                    const void* beta, const float* S_in, float* S_out,
+                                    int N, int H, int Dk, int Dv,
+                                    kda_dtype in_dtype, kda_dtype out_dtype,
+                                    void* o, const kda_fusion* fusion, kda_stream_t stream);
+
 kda_status gdn_recurrent_fwd(const void* q, const void* k, const void* v, const void* log_alpha,
                              const void* beta, const float* S0, const int32_t* cu_seqlens,
                              int B, int T, int H, int Dk, int Dv, int num_seqs,
