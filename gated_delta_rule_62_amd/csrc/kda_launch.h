@@ -17,6 +17,11 @@ constexpr int kWaitLimit = 1 << 16;   // polls before a kernel's ordering wait g
 // kernel (on MI355X it beats a one-chunk pass up to about 7 tokens: the state traffic is the
 // same and the chunk's fixed intra-chunk work is skipped).
 constexpr int kRecurrentMaxT = 4;
+// Packed batches of at most this many sequences are ordered longest first exactly (one kernel,
+// O(N) per sequence); larger ones by length buckets of 32 tokens (four small kernels, O(1) per
+// sequence).
+constexpr int kOrderExactMax = 4096;
+constexpr int kOrderBuckets = 1024;
 
 inline bool chunk_supported(int c) { return c == 0 || c == 32 || c == 64; }
 
@@ -53,7 +58,7 @@ struct PrefillPlan {
     int cps = 0;           // chunks per segment
     bool split0 = false;   // segment 0's output pass runs beside pass 1 (G >= 3)
     int seg_items = 0;     // packed batches cut into segments: pass-1 workgroups per head (0: one pass)
-    size_t off_status = 0, off_phi = 0, off_sloc = 0, off_se = 0, off_order = 0;
+    size_t off_status = 0, off_phi = 0, off_sloc = 0, off_se = 0, off_order = 0, off_buckets = 0;
     size_t workspace_bytes = 0;
 };
 

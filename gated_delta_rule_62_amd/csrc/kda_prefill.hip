@@ -2093,8 +2093,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }
 
 // Longest-first order of packed sequences (ties by index).  Each thread ranks one sequence
-// against all others, O(N) per thread over a grid of N threads; the packed batches this
-// serves hold up to a few thousand sequences.
+// against all others, O(N) per thread over a grid of N threads: for batches of up to
+// kOrderExactMax sequences.  Larger batches take the bucketed order below.
 __global__ __launch_bounds__(256) void order_kernel(const int32_t* __restrict__ cu, int32_t* __restrict__ order, int N) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= N) return;
@@ -2105,6 +2105,50 @@ __global__ __launch_bounds__(256) void order_kernel(const int32_t* __restrict__ 
         rank += (lm > li) || (lm == li && m < i);
     }
     order[rank] = i;
+}
+
+// Bucketed longest-first order for large packed batches: sequences go to kOrderBuckets buckets
+// by length / 32 (the top bucket takes everything from 32 * (kOrderBuckets - 1) tokens on), in
+// decreasing bucket order; within a bucket the order is that of the atomic cursor.  The order
+// only decides which workgroup runs which (sequence, head) when, never what it computes, so the
+// outputs do not depend on it.  Four launches: clear the counters (a fill kernel, no memset),
+// count, exclusive scan, scatter.
+__device__ __forceinline__ int order_bucket(const int32_t* cu, int i) {
+    const int len = cu[i + 1] - cu[i];
+    return kOrderBuckets - 1 - min(max(len, 0) >> 5, kOrderBuckets - 1);   // longest first
+}
+
+__global__ __launch_bounds__(kOrderBuckets) void order_clear_kernel(int32_t* __restrict__ cnt) {
+    cnt[threadIdx.x] = 0;
+    cnt[kOrderBuckets + threadIdx.x] = 0;
+}
+
+__global__ __launch_bounds__(256) void order_count_kernel(const int32_t* __restrict__ cu, int32_t* __restrict__ cnt,
+                                                          int N) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < N) atomicAdd(&cnt[order_bucket(cu, i)], 1);
+}
+
+// cnt[kOrderBuckets + b] <- sum of cnt[b'] over b' < b (one workgroup)
+__global__ __launch_bounds__(kOrderBuckets) void order_scan_kernel(int32_t* __restrict__ cnt) {
+    __shared__ int32_t buf[kOrderBuckets];
+    const int t = threadIdx.x;
+    const int c = cnt[t];
+    buf[t] = c;
+    __syncthreads();
+    for (int off = 1; off < kOrderBuckets; off <<= 1) {
+        const int x = t >= off ? buf[t - off] : 0;
+        __syncthreads();
+        buf[t] += x;
+        __syncthreads();
+    }
+    cnt[kOrderBuckets + t] = buf[t] - c;
+}
+
+__global__ __launch_bounds__(256) void order_scatter_kernel(const int32_t* __restrict__ cu, int32_t* __restrict__ cnt,
+                                                            int32_t* __restrict__ order, int N) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < N) order[atomicAdd(&cnt[kOrderBuckets + order_bucket(cu, i)], 1)] = i;
 }
 
 // Segment plan of a packed batch whose (sequence, head) pairs are too few to fill the chip, in
@@ -2251,8 +2295,17 @@ hipError_t launch_variant(const PrefillArgs& pa, const PrefillPlan& plan, hipStr
                 return hipGetLastError();
             }
         }
-        hipLaunchKernelGGL(order_kernel, dim3((pa.N + 255) / 256), dim3(256), 0, stream, pa.cu,
-                           reinterpret_cast<int32_t*>(ws + plan.off_order), pa.N);
+        int32_t* order = reinterpret_cast<int32_t*>(ws + plan.off_order);
+        const dim3 grid((pa.N + 255) / 256);
+        if (pa.N <= kOrderExactMax) {
+            hipLaunchKernelGGL(order_kernel, grid, dim3(256), 0, stream, pa.cu, order, pa.N);
+        } else {
+            int32_t* cnt = reinterpret_cast<int32_t*>(ws + plan.off_buckets);
+            hipLaunchKernelGGL(order_clear_kernel, dim3(1), dim3(kOrderBuckets), 0, stream, cnt);
+            hipLaunchKernelGGL(order_count_kernel, grid, dim3(256), 0, stream, pa.cu, cnt, pa.N);
+            hipLaunchKernelGGL(order_scan_kernel, dim3(1), dim3(kOrderBuckets), 0, stream, cnt);
+            hipLaunchKernelGGL(order_scatter_kernel, grid, dim3(256), 0, stream, pa.cu, cnt, order, pa.N);
+        }
         pass(0, NH, a);
         return hipGetLastError();
     }
@@ -2315,6 +2368,10 @@ PrefillPlan plan_prefill(int B, int T, int H, int D, int N, bool varlen, int chu
             return p;
         }
         p.workspace_bytes = kStatusBytes + align256(static_cast<size_t>(N) * sizeof(int32_t));
+        if (N > kOrderExactMax) {   // bucket counters and cursors of the bucketed order
+            p.off_buckets = p.workspace_bytes;
+            p.workspace_bytes += align256(2 * kOrderBuckets * sizeof(int32_t));
+        }
         return p;
     }
     (void)B;

@@ -82,6 +82,9 @@ def test_workspace_query_plans(lib):
     # packed sequences: the status block and an int32 order table (rounded to 256 bytes)
     assert q(1, 1000, 32, 128, 128, 64, True) == st + 256
     assert q(1, 1000, 32, 128, 128, 8, True) == st + 256          # 256 pairs fill the chip
+    # more than 4096 sequences: the bucketed order's 2 x 1024 counters after the order table
+    assert q(1, 100000, 2, 128, 128, 4096, True) == st + 4096 * 4
+    assert q(1, 100000, 2, 128, 128, 5000, True) == st + 20224 + 8192
     assert q(1, 200, 32, 128, 128, 1, True) == st + 256           # 7 chunks: too short to cut
     assert q(1, 65536, 32, 128, 128, 1, True, chunk=64) == st + 256
     # fewer than 256 (sequence, head) pairs, 32-token chunks: a segment table (4 + 5N + 2 int32,

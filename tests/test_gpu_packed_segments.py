@@ -241,3 +241,29 @@ def test_single_long_packed_sequence_full_size():
         ss = refs.pow(2).mean().sqrt()
         errs = ((S_p[0, h].double() - refs).abs() / (refs.abs() + ss)).max().item()
         assert err <= TOL_BF16 and errs <= TOL_BF16, (h, err, errs)
+
+
+def test_large_packed_batch_bucketed_order():
+    """More than 4096 packed sequences take the bucketed longest-first order (length buckets of
+    32 tokens, the top one from 32,736 tokens on): the order table in the workspace is a
+    permutation of the sequences in non-increasing bucket order, and every output matches the
+    oracle.  5,000 sequences of 0..47 tokens plus two of 33,000 and 40,000 tokens, one head."""
+    kda = _kda()
+    rng = np.random.default_rng(901)
+    lengths = rng.integers(0, 48, size=5000)
+    lengths[[17, 4000]] = [33000, 40000]
+    d = inputs.make_prefill(W[4], seed=902, H=1, D=128, lengths=lengths.tolist())
+    d["S0"] = (0.02 * np.random.default_rng(903).standard_normal((d["N"], 1, 128, 128))).astype(np.float32)
+    n = kda.kda_chunk_fwd_workspace_bytes(1, d["T"], 1, 128, 128, d["N"], True, CHUNK)
+    ws = torch.zeros((n,), dtype=torch.uint8, device="cuda")
+    print(f"[packed] {d['N']} sequences, {d['T']} tokens", flush=True)
+    o, Sf = call(d, "kda", ws=ws)
+    order = ws[256:256 + 4 * d["N"]].cpu().numpy().view(np.int32)
+    assert np.array_equal(np.sort(order), np.arange(d["N"]))
+    bucket = np.minimum(lengths[order] >> 5, 1023)
+    assert np.all(np.diff(bucket) <= 0)
+    assert set(order[:2].tolist()) == {17, 4000}
+    o_ref, S_ref = reference(d)
+    eo, es = o_metric(o, o_ref, d["cu_seqlens"]), state_metric(Sf, S_ref)
+    print(f"[packed]   worst o {eo:.3e}  S_final {es:.3e}", flush=True)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
