@@ -1881,6 +1881,11 @@ __device__ __forceinline__ void pipe_body(const KernelArgs& a,
         }
         return;
     }
+    // With the scalar gate the producers have little vector work and the consumers' chain sets
+    // the pace: the consumer waves issue first when both sides are ready (2.6% faster on the
+    // long-context shape; the per-channel kernels gain nothing from either side's priority and
+    // lose 5% when the consumers go first).
+    if constexpr (SG) __builtin_amdgcn_s_setprio(2);
     if (n_chunks > 0) {
         wait_count(&sm.sync.p1, NPW, broken, wl);
         consume_ptiles(sm.buf[c_begin & 1]);
