@@ -159,14 +159,15 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
 
     // A batch of equal-length sequences of at most kRecurrentMaxT tokens (new tokens on top of a
     // carried state) runs token by token with the state on chip: a chunk would be mostly padding.
-    if (!cu_seqlens && T > 0 && T <= kda::kRecurrentMaxT && !fused) {
+    const kda::Fusion fz = to_fusion(fused ? fusion : nullptr);
+    if (!cu_seqlens && T > 0 && T <= kda::kRecurrentMaxT) {
         const size_t units = static_cast<size_t>(B) * H;
         if (units > 0x7fffffffu) return KDA_ERR_UNSUPPORTED;
         hipError_t err = kda::clear_prefill_status(workspace, plan, reinterpret_cast<hipStream_t>(stream));
         if (err == hipSuccess)
             err = kda::launch_recurrent_fwd(Dk, in_dtype == KDA_BF16, out_dtype == KDA_BF16, q, k, v, log_alpha, beta,
                                             S0, nullptr, T, H, static_cast<int>(units), o, S_final,
-                                            reinterpret_cast<hipStream_t>(stream), scalar_gate);
+                                            reinterpret_cast<hipStream_t>(stream), scalar_gate, fused ? &fz : nullptr);
         return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
     }
     kda::PrefillArgs a;
@@ -175,7 +176,6 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
     a.B = B; a.T = T; a.H = H; a.D = Dk; a.N = num_seqs;
     a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = out_dtype == KDA_BF16;
     a.scalar_gate = scalar_gate;
-    const kda::Fusion fz = to_fusion(fused ? fusion : nullptr);
     a.fuse_flags = fz.flags;
     a.decay_bias = fz.decay_bias;
     a.decay_scale = fz.decay_scale;
@@ -227,10 +227,12 @@ kda_status recurrent_step_impl(const void* q, const void* k, const void* v, cons
 kda_status recurrent_fwd_impl(const void* q, const void* k, const void* v, const void* log_alpha, const void* beta,
                               const float* S0, const int32_t* cu_seqlens, int B, int T, int H, int Dk, int Dv,
                               int num_seqs, kda_dtype in_dtype, kda_dtype out_dtype, void* o, float* S_final,
-                              kda_stream_t stream, bool scalar_gate) {
+                              kda_stream_t stream, bool scalar_gate, const kda_fusion* fusion = nullptr) {
     if (B < 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || num_seqs < 0) return KDA_ERR_INVALID_ARGUMENT;
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_UNSUPPORTED;
     if (!head_ok(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
+    if (!fusion_ok(fusion)) return KDA_ERR_INVALID_ARGUMENT;
+    const bool fused = fusion && (fusion->flags || fusion->out_gate);
     if (cu_seqlens) {
         if (B != 1 || !aligned16(cu_seqlens)) return KDA_ERR_INVALID_ARGUMENT;
     } else if (num_seqs != B) {
@@ -255,6 +257,11 @@ kda_status recurrent_fwd_impl(const void* q, const void* k, const void* v, const
         for (int i = 0; i < 5; ++i)
             if (overlap(ins[i], nin[i], o, n_o) || overlap(ins[i], nin[i], S_final, n_s))
                 return KDA_ERR_INVALID_ARGUMENT;
+        if (fused && fusion->out_gate) {
+            const size_t n_gate = tokens * H * Dv * ein;
+            if (overlap(fusion->out_gate, n_gate, o, n_o) || overlap(fusion->out_gate, n_gate, S_final, n_s))
+                return KDA_ERR_INVALID_ARGUMENT;
+        }
     }
     // S_final == S0 (in place) is allowed; any other overlap is not
     if ((S0 != S_final && overlap(S0, n_s, S_final, n_s)) || overlap(S0, n_s, o, n_o) ||
@@ -263,9 +270,11 @@ kda_status recurrent_fwd_impl(const void* q, const void* k, const void* v, const
     const size_t units = static_cast<size_t>(num_seqs) * H;
     if (units == 0) return KDA_OK;
     if (units > 0x7fffffffu) return KDA_ERR_UNSUPPORTED;
+    const kda::Fusion fz = to_fusion(fused ? fusion : nullptr);
     hipError_t err = kda::launch_recurrent_fwd(Dk, in_dtype == KDA_BF16, out_dtype == KDA_BF16, q, k, v, log_alpha,
                                                beta, S0, cu_seqlens, T, H, static_cast<int>(units), o, S_final,
-                                               reinterpret_cast<hipStream_t>(stream), scalar_gate);
+                                               reinterpret_cast<hipStream_t>(stream), scalar_gate,
+                                               fused ? &fz : nullptr);
     return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -423,6 +432,24 @@ extern "C" kda_status gdn_recurrent_step_fused(const void* q, const void* k, con
                                                void* o, const kda_fusion* fusion, kda_stream_t stream) {
     return recurrent_step_impl(q, k, v, log_alpha, beta, S_in, S_out, N, H, Dk, Dv, in_dtype, out_dtype, o, stream,
                                true, fusion);
+}
+
+extern "C" kda_status kda_recurrent_fwd_fused(const void* q, const void* k, const void* v, const void* log_alpha,
+                                              const void* beta, const float* S0, const int32_t* cu_seqlens,
+                                              int B, int T, int H, int Dk, int Dv, int num_seqs,
+                                              kda_dtype in_dtype, kda_dtype out_dtype, void* o, float* S_final,
+                                              const kda_fusion* fusion, kda_stream_t stream) {
+    return recurrent_fwd_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, B, T, H, Dk, Dv, num_seqs, in_dtype,
+                              out_dtype, o, S_final, stream, false, fusion);
+}
+
+extern "C" kda_status gdn_recurrent_fwd_fused(const void* q, const void* k, const void* v, const void* log_alpha,
+                                              const void* beta, const float* S0, const int32_t* cu_seqlens,
+                                              int B, int T, int H, int Dk, int Dv, int num_seqs,
+                                              kda_dtype in_dtype, kda_dtype out_dtype, void* o, float* S_final,
+                                              const kda_fusion* fusion, kda_stream_t stream) {
+    return recurrent_fwd_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, B, T, H, Dk, Dv, num_seqs, in_dtype,
+                              out_dtype, o, S_final, stream, true, fusion);
 }
 
 extern "C" size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int num_seqs,

@@ -221,6 +221,7 @@ struct RecArgs {
     void* o;
     float* S_final;
     int T, H;
+    DecodeFusion fu;   // fused prologue / epilogue (FUSE kernels only)
 };
 
 // x plus the value of the other lane of its pair (DPP quad_perm [1, 0, 3, 2])
@@ -245,7 +246,9 @@ __device__ __forceinline__ float wave_sum_lane63(float x) {
     return x;
 }
 
-template <int D, typename IN, bool OUT_BF16, bool SG = false>
+// FUSE: the maps of the fused decode step per token (nk = 1/|k|, nq = 1/|q| as per-token
+// scalars on the raw products, sigmoid beta, logsigmoid decay, the output gate at the store).
+template <int D, typename IN, bool OUT_BF16, bool SG = false, bool FUSE = false>
 __global__ __launch_bounds__(2 * D)
 void recurrent_fwd_kernel(RecArgs a) {
     using ST = typename IN::storage;
@@ -256,6 +259,7 @@ void recurrent_fwd_kernel(RecArgs a) {
     __shared__ float4 s_f[2][3][D / 4];   // per row c (4 at a time): A' k, A' q, k / A'
     __shared__ float4 s_ren[2][D / 4];    // renormalisation factors A'
     __shared__ float s_kq[2][NW];
+    __shared__ float s_kk[2][NW], s_qq[2][NW];   // fused prologue: partial |k|^2, |q|^2
     __shared__ int s_flag[2][NW];
 
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -287,8 +291,10 @@ void recurrent_fwd_kernel(RecArgs a) {
     const ST* vp = static_cast<const ST*>(a.v);
     const ST* gp = static_cast<const ST*>(a.g);
     const ST* bp = static_cast<const ST*>(a.beta);
-    // token inputs of this thread: channel c (threads t < D) of q, k, log_alpha; column j of v; beta
-    struct Tok { ST q, k, g, v, b; };
+    const ST* gtp = FUSE ? static_cast<const ST*>(a.fu.out_gate) : nullptr;
+    // token inputs of this thread: channel c (threads t < D) of q, k, log_alpha; column j of v
+    // (and of the output gate); beta
+    struct Tok { ST q, k, g, v, b, gt; };
     const int c = t < D ? t : t - D;
     // (tokens past the end re-read the last one, so every load is unconditional and in bounds)
     auto load_tok = [&](long tk) {
@@ -300,6 +306,9 @@ void recurrent_fwd_kernel(RecArgs a) {
         x.g = SG ? gp[static_cast<size_t>(tc) * H + h] : gp[base + c];
         x.v = vp[base + j];
         x.b = bp[static_cast<size_t>(tc) * H + h];
+        if constexpr (FUSE) {
+            if (gtp) x.gt = gtp[base + j];
+        }
         return x;
     };
     float A = 1.f;   // running decay product of row c (threads t < D)
@@ -307,8 +316,17 @@ void recurrent_fwd_kernel(RecArgs a) {
     // Stage token x's factors of row c into buffer buf (threads t < D); returns A'.
     auto stage = [&](const Tok& x, int buf) {
         const float xq = IN::to_f32(x.q), xk = IN::to_f32(x.k);
-        const float ap = A * __builtin_amdgcn_exp2f(fmaxf(IN::to_f32(x.g) * 1.4426950408889634f, kMinLog2Decay));
-        float kq = 0.f;
+        float lg = IN::to_f32(x.g) * 1.4426950408889634f;   // log2 of the token's decay
+        if constexpr (FUSE) {
+            if (a.fu.flags & 4) {   // log2 sigmoid(g + bias) / scale, stable for any g
+                const float y = IN::to_f32(x.g) + a.fu.decay_bias;
+                lg = (fminf(y, 0.f) * 1.4426950408889634f -
+                      __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-fabsf(y) * 1.4426950408889634f))) /
+                     a.fu.decay_scale;
+            }
+        }
+        const float ap = A * __builtin_amdgcn_exp2f(fmaxf(lg, kMinLog2Decay));
+        float kq = 0.f, kk = 0.f, qq = 0.f;
         bool low = false;
         if (t < D) {
             reinterpret_cast<float*>(&s_f[buf][0][c >> 2])[c & 3] = ap * xk;
@@ -316,13 +334,23 @@ void recurrent_fwd_kernel(RecArgs a) {
             reinterpret_cast<float*>(&s_f[buf][2][c >> 2])[c & 3] = xk * __builtin_amdgcn_rcpf(ap);
             reinterpret_cast<float*>(&s_ren[buf][c >> 2])[c & 3] = ap;
             kq = xk * xq;
+            kk = xk * xk;
+            qq = xq * xq;
             low = ap < kRenorm;
         }
         kq = wave_sum_lane63(kq);
+        if constexpr (FUSE) {
+            kk = wave_sum_lane63(kk);
+            qq = wave_sum_lane63(qq);
+        }
         const bool any_low = __builtin_amdgcn_ballot_w64(low) != 0;
         if (lane == 63) {
             s_kq[buf][w] = kq;
             s_flag[buf][w] = any_low;
+            if constexpr (FUSE) {
+                s_kk[buf][w] = kk;
+                s_qq[buf][w] = qq;
+            }
         }
         return ap;
     };
@@ -335,14 +363,28 @@ void recurrent_fwd_kernel(RecArgs a) {
         auto token = [&](long tk, int buf, Tok& cur, const Tok& nxt) {
             __syncthreads();
             bool ren = false;
-            float kq = 0.f;
+            float kq = 0.f, kk = 0.f, qq = 0.f;
 #pragma unroll
             for (int i = 0; i < NW; ++i) {
                 ren |= s_flag[buf][i] != 0;
                 kq += s_kq[buf][i];
+                if constexpr (FUSE) {
+                    kk += s_kk[buf][i];
+                    qq += s_qq[buf][i];
+                }
             }
             A = ren ? 1.f : ap;
-            const float xv = IN::to_f32(cur.v), xb = IN::to_f32(cur.b);
+            const float xv = IN::to_f32(cur.v);
+            float xb = IN::to_f32(cur.b);
+            float nk = 1.f, nq = 1.f, gt = 0.f;
+            if constexpr (FUSE) {
+                if (a.fu.flags & 1) {
+                    nk = __builtin_amdgcn_rsqf(kk + 1e-12f);
+                    nq = __builtin_amdgcn_rsqf(qq + 1e-12f);
+                }
+                if (a.fu.flags & 2) xb = sigmoid_d(xb);
+                if (gtp) gt = IN::to_f32(cur.gt);
+            }
             if (tk + 1 < t1) ap = stage(nxt, buf ^ 1);
             cur = load_tok(tk + 4);
             float rr[4] = {0.f, 0.f, 0.f, 0.f}, pp[4] = {0.f, 0.f, 0.f, 0.f};
@@ -353,17 +395,24 @@ void recurrent_fwd_kernel(RecArgs a) {
                 rr[m] += fk.x * st[4 * i4] + fk.y * st[4 * i4 + 1] + fk.z * st[4 * i4 + 2] + fk.w * st[4 * i4 + 3];
                 pp[m] += fq.x * st[4 * i4] + fq.y * st[4 * i4 + 1] + fq.z * st[4 * i4 + 2] + fq.w * st[4 * i4 + 3];
             }
-            const float r = pair_sum((rr[0] + rr[1]) + (rr[2] + rr[3]));
-            const float p = pair_sum((pp[0] + pp[1]) + (pp[2] + pp[3]));
+            const float r = nk * pair_sum((rr[0] + rr[1]) + (rr[2] + rr[3]));
+            const float p = nq * pair_sum((pp[0] + pp[1]) + (pp[2] + pp[3]));
             const float e = xb * (xv - r);
-            if (half == 0) store_out<OUT_BF16>(a.o, (static_cast<size_t>(tk) * H + h) * D + j, p + kq * e);
+            if (half == 0) {
+                float ov = p + (kq * (nk * nq)) * e;
+                if constexpr (FUSE) {
+                    if (gtp) ov *= sigmoid_d(gt);
+                }
+                store_out<OUT_BF16>(a.o, (static_cast<size_t>(tk) * H + h) * D + j, ov);
+            }
+            const float ek = nk * e;   // the update takes the normalised key: k (e / |k|)
 #pragma unroll
             for (int i4 = 0; i4 < R / 4; ++i4) {
                 const float4 fu = s_f[buf][2][r0 / 4 + i4];
-                st[4 * i4] += fu.x * e;
-                st[4 * i4 + 1] += fu.y * e;
-                st[4 * i4 + 2] += fu.z * e;
-                st[4 * i4 + 3] += fu.w * e;
+                st[4 * i4] += fu.x * ek;
+                st[4 * i4 + 1] += fu.y * ek;
+                st[4 * i4 + 2] += fu.z * ek;
+                st[4 * i4 + 3] += fu.w * ek;
             }
             if (ren) {
 #pragma unroll
@@ -409,23 +458,29 @@ void recurrent_fwd_kernel(RecArgs a) {
     }
 }
 
-template <int D, typename IN, bool OUT_BF16, bool SG>
+template <int D, typename IN, bool OUT_BF16, bool SG, bool FUSE = false>
 static hipError_t launch_recurrent_t(const RecArgs& a, int units, hipStream_t stream) {
-    hipLaunchKernelGGL((recurrent_fwd_kernel<D, IN, OUT_BF16, SG>), dim3(units), dim3(2 * D), 0, stream, a);
+    hipLaunchKernelGGL((recurrent_fwd_kernel<D, IN, OUT_BF16, SG, FUSE>), dim3(units), dim3(2 * D), 0, stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_recurrent_fwd(int D, bool in_bf16, bool out_bf16, const void* q, const void* k,
                                 const void* v, const void* g, const void* b, const float* S0,
                                 const int32_t* cu, int T, int H, int units, void* o, float* S_final,
-                                hipStream_t stream, bool scalar_gate) {
+                                hipStream_t stream, bool scalar_gate, const Fusion* fusion) {
     RecArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = b;
     a.S0 = S0; a.cu = cu; a.o = o; a.S_final = S_final; a.T = T; a.H = H;
+    const bool fused = fusion && (fusion->flags || fusion->out_gate);
+    a.fu = fused ? DecodeFusion{fusion->flags, fusion->decay_bias, fusion->decay_scale, fusion->out_gate}
+                 : DecodeFusion{0, 0.f, 1.f, nullptr};
 #define KDA_REC_CASE(DD, INT, OB)                                                          \
-    if (D == DD && in_bf16 == std::is_same<INT, BF16>::value && out_bf16 == OB)              \
+    if (D == DD && in_bf16 == std::is_same<INT, BF16>::value && out_bf16 == OB) {            \
+        if (fused) return scalar_gate ? launch_recurrent_t<DD, INT, OB, true, true>(a, units, stream) \
+                                      : launch_recurrent_t<DD, INT, OB, false, true>(a, units, stream); \
         return scalar_gate ? launch_recurrent_t<DD, INT, OB, true>(a, units, stream)               \
-                           : launch_recurrent_t<DD, INT, OB, false>(a, units, stream);
+                           : launch_recurrent_t<DD, INT, OB, false>(a, units, stream);             \
+    }
     KDA_REC_CASE(128, BF16, true)
     KDA_REC_CASE(128, BF16, false)
     KDA_REC_CASE(128, F32, true)

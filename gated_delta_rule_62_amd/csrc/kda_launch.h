@@ -93,6 +93,6 @@ hipError_t launch_decode(int D, bool in_bf16, bool out_bf16, const void* q, cons
 hipError_t launch_recurrent_fwd(int D, bool in_bf16, bool out_bf16, const void* q, const void* k,
                                 const void* v, const void* g, const void* b, const float* S0,
                                 const int32_t* cu, int T, int H, int units, void* o, float* S_final,
-                                hipStream_t stream, bool scalar_gate);
+                                hipStream_t stream, bool scalar_gate, const Fusion* fusion = nullptr);
 
 }  // namespace kda

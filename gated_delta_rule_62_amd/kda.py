@@ -25,7 +25,7 @@ EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd
             "kda_recurrent_fwd", "gdn_chunk_fwd", "gdn_recurrent_step", "gdn_recurrent_fwd",
             "kda_chunk_fwd_fused", "kda_recurrent_step_fused", "kda_chunk_bwd_workspace_bytes",
             "kda_chunk_bwd", "gdn_chunk_bwd", "kda_chunk_fwd_noalloc", "gdn_chunk_fwd_fused",
-            "gdn_recurrent_step_fused")
+            "gdn_recurrent_step_fused", "kda_recurrent_fwd_fused", "gdn_recurrent_fwd_fused")
 KDA_FUSE_QK_L2NORM, KDA_FUSE_BETA_SIGMOID, KDA_FUSE_DECAY_LOGSIGMOID = 1, 2, 4
 
 
@@ -73,6 +73,9 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_chunk_fwd_fused.restype = i32
     lib.gdn_recurrent_step_fused.argtypes = lib.kda_recurrent_step_fused.argtypes
     lib.gdn_recurrent_step_fused.restype = i32
+    for name in ("kda_recurrent_fwd_fused", "gdn_recurrent_fwd_fused"):
+        getattr(lib, name).argtypes = [vp] * 7 + [i32] * 6 + [i32, i32] + [vp, vp, fp, vp]
+        getattr(lib, name).restype = i32
     lib.kda_chunk_bwd_workspace_bytes.argtypes = [i32] * 8
     lib.kda_chunk_bwd_workspace_bytes.restype = sz
     lib.kda_chunk_bwd.argtypes = [vp] * 9 + [i32] * 7 + [i32, i32] + [vp] * 6 + [vp, sz, vp]
@@ -216,7 +219,7 @@ def kda_recurrent_step(q, k, v, log_alpha, beta, S_in, S_out=None, *, out_dtype=
 
 
 def kda_recurrent_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, out_dtype=None, o=None,
-                      S_final=None, stream=None, want_final=True, _fn="kda_recurrent_fwd"):
+                      S_final=None, stream=None, want_final=True, _fn="kda_recurrent_fwd", _fusion_arg=None):
     """Token-by-token forward over each sequence (the multi-token continuation of decode).
     Same tensors as kda_chunk_fwd; S_final may be S0 (in place).  Returns (o, S_final)."""
     B, T, H, Dk = q.shape
@@ -231,10 +234,11 @@ def kda_recurrent_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, out
     if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
         raise TypeError("cu_seqlens must be int32")
     _check_dev(q, k, v, log_alpha, beta, S0, cu_seqlens, o, S_final)
+    extra = () if _fusion_arg is None else (ctypes.byref(_fusion_arg),)
     st = getattr(load_library(), _fn)(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
         B, T, H, Dk, Dv, N, _dtype_code(q.dtype), _dtype_code(o.dtype), _ptr(o), _ptr(S_final),
-        _stream_ptr(stream))
+        *extra, _stream_ptr(stream))
     if st != KDA_OK:
         raise KDAError(st, _fn)
     _keep_for(stream, o if o_new else None, S_final if sf_new else None)
@@ -253,6 +257,21 @@ def gdn_recurrent_step(q, k, v, log_alpha, beta, S_in, S_out=None, **kw):
 
 def gdn_recurrent_fwd(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, **kw):
     return kda_recurrent_fwd(q, k, v, log_alpha, beta, S0, cu_seqlens, _fn="gdn_recurrent_fwd", **kw)
+
+
+def kda_recurrent_fwd_fused(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *, qk_l2norm=False,
+                            beta_logits=False, decay_logits=None, out_gate=None, _fn="kda_recurrent_fwd_fused", **kw):
+    """kda_recurrent_fwd with the fused prologue / epilogue (see kda_chunk_fwd_fused)."""
+    if out_gate is not None:
+        _check_dev(out_gate)
+    f = _fusion(qk_l2norm, beta_logits, decay_logits, out_gate)
+    o, Sf = kda_recurrent_fwd(q, k, v, log_alpha, beta, S0, cu_seqlens, _fn=_fn, _fusion_arg=f, **kw)
+    return o, Sf
+
+
+def gdn_recurrent_fwd_fused(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, **kw):
+    """gdn_recurrent_fwd with the fused prologue / epilogue (log_alpha [B, T, H])."""
+    return kda_recurrent_fwd_fused(q, k, v, log_alpha, beta, S0, cu_seqlens, _fn="gdn_recurrent_fwd_fused", **kw)
 
 
 def _fusion(qk_l2norm=False, beta_logits=False, decay_logits=None, out_gate=None):

@@ -288,6 +288,23 @@ kda_status gdn_recurrent_fwd(const void* q, const void* k, const void* v, const 
                              void* o, float* S_final, kda_stream_t stream);
 
 /*
+ * kda_recurrent_fwd and gdn_recurrent_fwd with the fused prologue / epilogue (the maps of
+ * kda_chunk_fwd_fused, per token).  kda_chunk_fwd_fused and gdn_chunk_fwd_fused take this
+ * path for equal-length batches of at most 4 tokens per sequence.
+ */
+kda_status kda_recurrent_fwd_fused(const void* q, const void* k, const void* v, const void* log_alpha,
+                                   const void* beta, const float* S0, const int32_t* cu_seqlens,
+                                   int B, int T, int H, int Dk, int Dv, int num_seqs,
+                                   kda_dtype in_dtype, kda_dtype out_dtype,
+                                   void* o, float* S_final, const kda_fusion* fusion, kda_stream_t stream);
+
+kda_status gdn_recurrent_fwd_fused(const void* q, const void* k, const void* v, const void* log_alpha,
+                                   const void* beta, const float* S0, const int32_t* cu_seqlens,
+                                   int B, int T, int H, int Dk, int Dv, int num_seqs,
+                                   kda_dtype in_dtype, kda_dtype out_dtype,
+                                   void* o, float* S_final, const kda_fusion* fusion, kda_stream_t stream);
+
+/*
  * kda_chunk_bwd -- gradient of kda_chunk_fwd for training.
  *
  * The pages motivate the chunkwise form by training throughput ("Decoding Hybrid

@@ -36,7 +36,7 @@ def flags_of(qk, beta, decay):
     return (P.QK_L2NORM if qk else 0) | (P.BETA_SIGMOID if beta else 0) | (P.DECAY_LOGSIGMOID if decay else 0)
 
 
-def run(d, flags, gate, chunk=0):
+def run(d, flags, gate, chunk=0, recurrent=False):
     """GPU call; inputs a flag does not transform are given already transformed (fp32/bf16 of
     the same map), so every case exercises exactly its flags."""
     kda = _kda()
@@ -52,21 +52,25 @@ def run(d, flags, gate, chunk=0):
     dev = {kk: to_dev(cast(f[kk])) for kk in KEYS}
     S0 = to_dev(d["S0"]) if d["S0"] is not None else None
     cu = to_dev(d["cu_seqlens"]) if d["cu_seqlens"] is not None else None
-    fn = kda.gdn_chunk_fwd_fused if d.get("scalar_gate") else kda.kda_chunk_fwd_fused
-    o, Sf = fn(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], S0, cu,
-               qk_l2norm=bool(flags & P.QK_L2NORM), beta_logits=bool(flags & P.BETA_SIGMOID),
-               decay_logits=(BIAS, SCALE) if flags & P.DECAY_LOGSIGMOID else None,
-               out_gate=to_dev(d["gate"]) if gate else None, out_dtype=torch.float32, chunk=chunk)
+    kw = dict(qk_l2norm=bool(flags & P.QK_L2NORM), beta_logits=bool(flags & P.BETA_SIGMOID),
+              decay_logits=(BIAS, SCALE) if flags & P.DECAY_LOGSIGMOID else None,
+              out_gate=to_dev(d["gate"]) if gate else None, out_dtype=torch.float32)
+    if recurrent:
+        fn = kda.gdn_recurrent_fwd_fused if d.get("scalar_gate") else kda.kda_recurrent_fwd_fused
+    else:
+        fn = kda.gdn_chunk_fwd_fused if d.get("scalar_gate") else kda.kda_chunk_fwd_fused
+        kw["chunk"] = chunk
+    o, Sf = fn(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], S0, cu, **kw)
     torch.cuda.synchronize()
     # the reference must see the same (rounded) inputs the GPU saw
     d2 = dict(d, **{kk: cast(f[kk]) for kk in KEYS})
     return to_host(o), to_host(Sf), d2
 
 
-def check(d, flags, gate, label):
+def check(d, flags, gate, label, recurrent=False):
     print(f"[fused] {label}: flags={flags} gate={gate} B={d['B']} T={d['T']} H={d['H']} D={d['D']} "
-          f"dtype={d['dtype']} scalar_gate={bool(d.get('scalar_gate'))}", flush=True)
-    o, Sf, d2 = run(d, flags, gate)
+          f"dtype={d['dtype']} scalar_gate={bool(d.get('scalar_gate'))} recurrent={recurrent}", flush=True)
+    o, Sf, d2 = run(d, flags, gate, recurrent=recurrent)
     # the reference reads the raw values of the transformed inputs, the transformed values of the rest
     o_ref, S_ref = reference_seen(d2, flags, gate)
     eo, es = o_metric(o, o_ref, d["cu_seqlens"]), state_metric(Sf, S_ref)
@@ -222,3 +226,20 @@ def test_scalar_gate_decode_steps(D):
     es = state_metric(to_host(S_dev), S_ref)
     print(f"[fused] scalar gate decode D={D}: worst o {worst:.3e} S {es:.3e}", flush=True)
     assert worst <= TOL_BF16 and es <= TOL_BF16
+
+
+# ------------------------------------------------------------------ token by token (kda/gdn_recurrent_fwd_fused)
+@pytest.mark.parametrize("sg", [False, True], ids=["kda", "gdn"])
+def test_token_by_token_fused(sg):
+    """The fused maps in the token-by-token forward: packed sequences with empty and one-token
+    members and fp32 inputs through kda/gdn_recurrent_fwd_fused, and equal-length batches of at
+    most 4 tokens through kda/gdn_chunk_fwd_fused (which take this kernel for them)."""
+    d = inputs.make_raw_prefill(721, H=3, D=128, lengths=[70, 0, 1, 64, 129], scalar_gate=sg)
+    check(d, ALL, True, "token by token, packed", recurrent=True)
+    for flags, gate in [(flags_of(True, False, False), False), (flags_of(False, True, True), True)]:
+        check(d, flags, gate, "token by token, packed", recurrent=True)
+    d = inputs.make_raw_prefill(722, B=2, T=40, H=2, D=64, dtype="f32", scalar_gate=sg)
+    check(d, ALL, True, "token by token, fp32 d64", recurrent=True)
+    for T in (1, 4):
+        d = inputs.make_raw_prefill(723 + T, B=5, T=T, H=2, D=128, scalar_gate=sg)
+        check(d, ALL, True, f"chunk entry point, T={T}")
