@@ -106,6 +106,27 @@ def counted_traffic(kind: str):
     return rec["read_bytes"] + rec["write_bytes"]
 
 
+def counted_workload(key: str):
+    """Counter figures of one bench workload's call (profiles/traffic.json "workloads"): HBM bytes
+    from FETCH_SIZE/WRITE_SIZE and the matrix-core / vector-ALU busy fractions, or None once the
+    prefill kernel source has changed since they were taken."""
+    import hashlib
+    try:
+        tj = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
+        rec = tj["workloads"][key]
+        want = tj["prefill"]["source_sha256"]
+    except (OSError, KeyError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in ("kda_prefill.hip", "kda_device.h", "kda_launch.h"):
+        with open(os.path.join(ROOT, "gated_delta_rule_62_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != want:
+        return None
+    return {"traffic": rec["read_bytes"] + rec["write_bytes"], "mfma_busy": rec["mfma_busy"],
+            "valu_busy": rec["valu_busy"], "kernels": rec["kernels"]}
+
+
 # floats per (chunk, head) record of the backward at d = 128: Q', K', K'', the decay exponents
 # (32 x 128 each), M, P, L (32 x 32 each), e_m, e_n (128 each), beta (32)
 Rec128 = 4 * 32 * 128 + 3 * 32 * 32 + 2 * 128 + 32
@@ -337,6 +358,11 @@ def main():
             line["cpu_baseline"] = "the headline line's (same batch)"
         elif not args.no_cpu_baseline:
             line["cpu_baseline"] = cpu_baseline_batch(torch, xw)
+        cw = counted_workload(key)
+        if cw is not None:
+            line["roofline"]["traffic"] = cw["traffic"]
+            line["roofline"]["traffic_vs_algorithmic"] = cw["traffic"] / line["roofline"]["bytes_per_call"]
+            line["counters"] = {"mfma_busy": cw["mfma_busy"], "valu_busy": cw["valu_busy"], "kernels": cw["kernels"]}
         prefill_workloads[key] = line
         del xw, ow, Sw, wsw
         torch.cuda.empty_cache()
@@ -435,7 +461,8 @@ def main():
     eu1.record(stream)
     torch.cuda.synchronize()
     unfused_ms = eu0.elapsed_time(eu1) / args.steps
-    fused = {"workload": "long_context_prefill with q/k L2 norm, sigmoid beta, logsigmoid decay and an output "
+    fused = {"counters": counted_workload("fused"),
+             "workload": "long_context_prefill with q/k L2 norm, sigmoid beta, logsigmoid decay and an output "
                          "gate inside the kernels (kda_chunk_fwd_fused)",
              "ms_per_call": fused_ms, "vs_plain_call": fused_ms / ms_step,
              "tokens_per_s": tokens / (fused_ms / 1e3),
@@ -470,7 +497,9 @@ def main():
     gdn_ms = eg0.elapsed_time(eg1) / args.steps
     # bytes: q, k, v and o (bf16 rows of d), one log_alpha and one beta per token-head, S0 and S_final
     gdn_bytes = w6.B * w6.T * w6.H * (4 * d * 2 + 2 + 2) + 2 * w6.B * w6.H * d * d * 4
-    gdn = {"workload": "long_context_prefill, scalar gate: B=1, T=65536, H=32, d=128, bf16, "
+    gdn_counters = counted_workload("gdn")
+    gdn = {"counters": gdn_counters,
+           "workload": "long_context_prefill, scalar gate: B=1, T=65536, H=32, d=128, bf16, "
                        "log_alpha [B,T,H] = logsigmoid(N(0,1)+6)/16",
            "value": w6.B * w6.T / (gdn_ms / 1e3), "unit": "tokens/s", "ms_per_call": gdn_ms,
            "roofline": {"bound": "hbm", "achieved": gdn_bytes / (gdn_ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
@@ -487,7 +516,7 @@ def main():
     tgf = timed_calls(torch, call_gdn_fused, stream, 3, args.steps)
     gdn["fused"] = {"workload": "the same with the fused prologue and an output gate (gdn_chunk_fwd_fused)",
                     "ms_per_call_median": tgf["median"], "ms_per_call_min": tgf["min"],
-                    "vs_plain_call": tgf["median"] / gdn_ms}
+                    "vs_plain_call": tgf["median"] / gdn_ms, "counters": counted_workload("gdn_fused")}
     del xg, og, Sg, gate_g
 
     # ------------------------------------------------------------------ continuation (serving shapes)
@@ -635,7 +664,10 @@ def main():
                      "mfma_frac_dense_tile": tile_tflops / BF16_PEAK_TFLOPS,
                      "flop_convention": f"algorithmic {prefill_alg_flops_per_token_head(d)} / dense-tile "
                                         f"{prefill_tile_flops_per_token_head(d)} per token-head at C={CHUNK}",
-                     "flops_per_launch": flops},
+                     "flops_per_launch": flops,
+                     # matrix-core and vector-ALU busy fractions of the call's kernels (rocprofv3
+                     # counters, profiles/kernel_counters.md), or null once the kernels changed
+                     "counters": counted_workload("long_context")},
         "cpu_baseline": cpu,
         "prefill_workloads": prefill_workloads,
         "decode": decode,

@@ -42,15 +42,19 @@ def _both(d):
     return to_host(o), to_host(Sf), to_host(o_ref), to_host(S_ref)
 
 
-@pytest.mark.parametrize("case", ["equal-length", "packed"])
+@pytest.mark.parametrize("case", ["equal-length", "packed", "packed, cut into segments"])
 def test_noalloc_matches_the_workspace_entry_point(case):
     if case == "equal-length":
         # segmented schedule (summaries and entry states in the scratch), then a smaller call
         big = inputs.make_prefill(W[2], seed=701, B=1, T=3000, H=4, s0=True)
         small = inputs.make_prefill(W[2], seed=702, B=1, T=1100, H=2, s0=True)
-    else:
+    elif case == "packed":
         big = inputs.make_prefill(W[4], seed=703, H=3, lengths=[400, 0, 1, 257, 96, 31])
         small = inputs.make_prefill(W[4], seed=704, H=2, lengths=[65, 3])
+    else:
+        # few long sequences: the segment table, summaries and entry states in the scratch
+        big = inputs.make_prefill(W[4], seed=705, H=4, lengths=[3000, 700, 40, 0])
+        small = inputs.make_prefill(W[4], seed=706, H=2, lengths=[900, 5])
     for label, d in (("first", big), ("second, smaller", small)):
         print(f"[noalloc] {case} {label}: B={d['B']} T={d['T']} H={d['H']} N={d['N']}", flush=True)
         o, Sf, o_ref, S_ref = _both(d)
