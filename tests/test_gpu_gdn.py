@@ -154,20 +154,23 @@ def test_rejects_chunk_64():
     assert e.value.status == kda.KDA_ERR_UNSUPPORTED
 
 
-def test_long_context_full_size_sampled_heads():
+def test_long_context_full_size_all_heads():
     """The scalar-gate long-context workload (B1 H32 T65536 d128) in the launch
-    configuration the benchmark times; heads 0, 17, 31 checked against the oracle."""
+    configuration the benchmark times; every head against the oracle, 8 at a time."""
     kda = _kda()
     w = W[6]
     x = inputs.device_prefill(w)
     o, Sf = kda.gdn_chunk_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"], None,
                               out_dtype=torch.float32)
     torch.cuda.synchronize()
-    heads = [0, 17, 31]
-    args = [host_bits(x[kk][:, :, heads]) for kk in KEYS]
-    args[3] = broadcast_gate(args[3], w.D)
-    o_ref, S_ref = oracle.kda_fwd(*args, S0=x["S0"][:, heads].cpu().numpy(), o_dtype=np.float64)
-    eo = o_metric(to_host(o[:, :, heads]), o_ref)
-    es = state_metric(to_host(Sf[:, heads]), S_ref)
-    print(f"[gdn] long context heads {heads}: worst o {eo:.3e} S_final {es:.3e}", flush=True)
-    assert eo <= TOL_BF16 and es <= TOL_BF16
+    worst_o = worst_s = 0.0
+    for h0 in range(0, w.H, 8):
+        heads = list(range(h0, h0 + 8))
+        args = [host_bits(x[kk][:, :, heads]) for kk in KEYS]
+        args[3] = broadcast_gate(args[3], w.D)
+        o_ref, S_ref = oracle.kda_fwd(*args, S0=x["S0"][:, heads].cpu().numpy(), o_dtype=np.float64)
+        eo = o_metric(to_host(o[:, :, heads]), o_ref)
+        es = state_metric(to_host(Sf[:, heads]), S_ref)
+        print(f"[gdn] long context heads {h0}..{h0 + 7}: worst o {eo:.3e} S_final {es:.3e}", flush=True)
+        worst_o, worst_s = max(worst_o, eo), max(worst_s, es)
+    assert worst_o <= TOL_BF16 and worst_s <= TOL_BF16

@@ -126,29 +126,26 @@ def test_bf16_output_is_rne_of_fp32_output():
 
 
 def test_continuation_workload_full_size():
-    """The continuation workload (256 sequences of 1..32 new tokens, 32 heads) in the
-    launch configuration the benchmark times; the oracle checks every head of a few
-    sequences from the same bf16 values."""
+    """The continuation workload (256 sequences of 1..32 new tokens, 32 heads) in the launch
+    configurations the benchmark times (the token-by-token kernel, and kda_chunk_fwd on the
+    packed batch); the oracle checks every (sequence, head) from the same bf16 values."""
     kda = _kda()
     w = W[5]
     x = inputs.device_prefill(w)
     cu = x["cu_host"]
     lens = np.diff(cu)
     print(f"[recurrent] continuation: {len(lens)} sequences, {int(cu[-1])} tokens", flush=True)
-    o, Sf = kda.kda_recurrent_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"], x["cu_seqlens"],
-                                  out_dtype=torch.float32)
+    args = [x[kk] for kk in KEYS]
+    o_r, Sf_r = kda.kda_recurrent_fwd(*args, x["S0"], x["cu_seqlens"], out_dtype=torch.float32)
+    o_c, Sf_c = kda.kda_chunk_fwd(*args, x["S0"], x["cu_seqlens"], out_dtype=torch.float32)
     torch.cuda.synchronize()
-    picks = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 100, 255})
-    worst_o = worst_s = 0.0
-    for n in picks:
-        tok = slice(int(cu[n]), int(cu[n + 1]))
-        args = [host_bits(x[kk][:, tok]) for kk in KEYS]
-        o_ref, S_ref = oracle.kda_fwd(*args, S0=x["S0"][n:n + 1].cpu().numpy(), o_dtype=np.float64)
-        eo = o_metric(to_host(o[:, tok]), o_ref)
-        es = state_metric(to_host(Sf[n:n + 1]), S_ref)
-        worst_o, worst_s = max(worst_o, eo), max(worst_s, es)
-    print(f"[recurrent]   sequences {picks}: worst o {worst_o:.3e} S_final {worst_s:.3e}", flush=True)
-    assert worst_o <= TOL_BF16 and worst_s <= TOL_BF16
+    o_ref, S_ref = oracle.kda_fwd(*[host_bits(t) for t in args], S0=x["S0"].cpu().numpy(), cu_seqlens=cu,
+                                  o_dtype=np.float64)
+    for label, o, Sf in (("token by token", o_r, Sf_r), ("chunked", o_c, Sf_c)):
+        eo = o_metric(to_host(o), o_ref, cu)
+        es = state_metric(to_host(Sf), S_ref)
+        print(f"[recurrent]   {label}, all sequences: worst o {eo:.3e} S_final {es:.3e}", flush=True)
+        assert eo <= TOL_BF16 and es <= TOL_BF16
 
 
 def test_rejects_bad_arguments():
