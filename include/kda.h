@@ -35,9 +35,13 @@
  *    log_alpha <= 0; beta in [0, 1].  Within one chunk, the summed log-decay of
  *    any channel must stay above -160 (the decay factors of a chunk are formed
  *    around its midpoint in fp32).
- *  - Outputs are bitwise deterministic for identical inputs (no atomics).
- *  - Library functions keep no mutable global state and are thread-safe; calls
- *    that share a workspace must be ordered (one stream, or events).
+ *  - Outputs are bitwise deterministic for identical inputs: no result is summed
+ *    with atomics (the one atomic counter, in the order of packed batches of more
+ *    than 4096 sequences, decides only which workgroup runs which sequence).
+ *  - Library functions are thread-safe and keep no mutable global state except
+ *    kda_chunk_fwd_noalloc's fixed scratch array (one per GPU) and its device
+ *    address, looked up once per GPU under a lock; calls that share a workspace
+ *    (or, for kda_chunk_fwd_noalloc, a GPU) must be ordered (one stream, or events).
  */
 #ifndef KDA_H
 #define KDA_H
