@@ -455,7 +455,7 @@ extern "C" kda_status gdn_recurrent_fwd_fused(const void* q, const void* k, cons
 extern "C" size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int num_seqs,
                                                 int has_cu_seqlens, int chunk) {
     if (B < 0 || T < 0 || H <= 0 || num_seqs < 0 || !head_ok(Dk, Dv)) return 0;
-    if (chunk != 0 && chunk != 32) return 0;
+    if (chunk != 0 && chunk != 32 && chunk != 64) return 0;   // evaluated at 32 in every case
     return kda::plan_backward(B, T, H, Dk, num_seqs, has_cu_seqlens != 0).workspace_bytes;
 }
 
@@ -470,7 +470,8 @@ kda_status chunk_bwd_impl(const void* q, const void* k, const void* v, const voi
     if (B < 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || num_seqs < 0) return KDA_ERR_INVALID_ARGUMENT;
     if (!dtype_ok(in_dtype) || !dtype_ok(grad_dtype)) return KDA_ERR_UNSUPPORTED;
     if (!head_ok(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
-    if (chunk != 0 && chunk != 32) return KDA_ERR_UNSUPPORTED;
+    // the forward's chunk length; the gradient is evaluated with 32-token chunks for all of them
+    if (chunk != 0 && chunk != 32 && chunk != 64) return KDA_ERR_UNSUPPORTED;
     if (cu_seqlens) {
         if (B != 1 || !aligned16(cu_seqlens)) return KDA_ERR_INVALID_ARGUMENT;
     } else if (num_seqs != B) {

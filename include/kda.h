@@ -317,22 +317,32 @@ kda_status gdn_recurrent_fwd_fused(const void* q, const void* k, const void* v, 
  * evaluated through the same chunkwise form: a forward pass over the chunks that
  * keeps every chunk's entry state, a reverse pass that carries the state gradient
  * from the last chunk to the first, and one parallel step per (chunk, head).
+ * Memory control (section 4's concern that training memory not grow with sequence
+ * length): when that per-chunk data would exceed 2 GiB (the KDA_BWD_WORKSPACE_LIMIT
+ * environment variable, in bytes, overrides the limit), equal-length batches run in
+ * windows of chunks, last window first, with one checkpointed entry state per window
+ * and the state gradient carried between windows; the gradients are bitwise those of
+ * the one-pass plan.  Packed batches always take the one-pass plan.
  *
  *   q, k, v, log_alpha, beta, S0, cu_seqlens, B, T, H, Dk, Dv, num_seqs, in_dtype:
  *                     the arguments of the kda_chunk_fwd call being differentiated
  *   d_o             : [B, T, H, Dv] in_dtype, gradient of the loss with respect to o
  *   dS_final        : [N, H, Dk, Dv] fp32 gradient with respect to S_final, or NULL
  *                     for zero
- *   chunk           : 0 or 32
+ *   chunk           : 0, 32 or 64 (the chunk length of the forward call); the gradient
+ *                     is evaluated with 32-token chunks in every case, since the
+ *                     layer, and so its gradient, does not depend on the chunk length
+ *                     beyond rounding
  *   dq, dk          : [B, T, H, Dk]   grad_dtype
  *   dv              : [B, T, H, Dv]   grad_dtype
  *   dlog_alpha      : [B, T, H, Dk]   grad_dtype
  *   dbeta           : [B, T, H]       grad_dtype
  *   dS0             : [N, H, Dk, Dv]  fp32 gradient with respect to S0, or NULL to skip
  *                     (written for every sequence, also when S0 is NULL)
- *   workspace       : device scratch of kda_chunk_bwd_workspace_bytes() bytes; it holds
- *                     every chunk's entry state and state gradient in fp32, about
- *                     (2 Dk Dv + 3 chunk Dk + 3 chunk^2) * 4 bytes per chunk and head
+ *   workspace       : device scratch of kda_chunk_bwd_workspace_bytes() bytes; per
+ *                     chunk and head (of all chunks, or of one window) it holds the
+ *                     chunk's record, entry state and state gradient in fp32, about
+ *                     (2 Dk Dv + 6 C Dk + 3 C^2) * 4 bytes with C = 32
  *
  * Supported: Dk == Dv in {64, 128}; in_dtype, grad_dtype in {KDA_F32, KDA_BF16}
  * (bf16 gradients are the round-to-nearest-even bf16 of the fp32 result).  All

@@ -214,7 +214,8 @@ def test_backward_workspace_query(lib):
         up(4 * (nc + 3) * 2 * 64 * 64) + up(4 * nc * 2 * 64 * 64) + 2 * up(4 * nc * 2 * 32 * 64)
     assert q(1, 1000, 2, 64, 64, 3, True) == want
     assert q(1, 64, 2, 96, 96, 1, False) == 0
-    assert q(1, 64, 2, 128, 128, 1, False, chunk=64) == 0
+    assert q(1, 64, 2, 128, 128, 1, False, chunk=64) == q(1, 64, 2, 128, 128, 1, False)
+    assert q(1, 64, 2, 128, 128, 1, False, chunk=16) == 0
 
 
 def test_backward_windowed_workspace(lib, monkeypatch):
@@ -264,7 +265,8 @@ def test_backward_argument_errors(lib):
                                  a["ws_bytes"], None)
     assert bwd(B=0, N=0, T=0) == kda.KDA_OK                                    # nothing to do, no HIP call
     assert bwd(Dk=96, Dv=96) == kda.KDA_ERR_UNSUPPORTED
-    assert bwd(chunk=64) == kda.KDA_ERR_UNSUPPORTED
+    assert bwd(chunk=16) == kda.KDA_ERR_UNSUPPORTED
+    assert bwd(chunk=64, B=0, N=0, T=0) == kda.KDA_OK   # the forward's 64-token chunks: evaluated at 32
     assert bwd(g_dt=3) == kda.KDA_ERR_UNSUPPORTED
     assert bwd(do=None) == kda.KDA_ERR_INVALID_ARGUMENT
     assert bwd(dk=None) == kda.KDA_ERR_INVALID_ARGUMENT

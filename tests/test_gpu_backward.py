@@ -309,3 +309,21 @@ def test_long_context_full_size_identities():
     for t in gr.values():
         assert torch.isfinite(t).all()
     assert e1 < 1e-4 and e2 < 1e-4
+
+
+def test_chunk_64_forward_gets_the_same_gradient():
+    """kda_chunk_bwd for a forward run with 64-token chunks: the layer, and so its gradient, does
+    not depend on the chunk length, and the backward evaluates it with 32-token chunks, so the
+    result equals the chunk-32 call bit for bit (and the oracle within the bound)."""
+    kda = _kda()
+    d = inputs.make_prefill(W[1], seed=251, B=2, T=300, H=2, s0=True)
+    g = inputs.make_output_grads(d, seed=252)
+    dev = {kk: to_dev(d[kk]) for kk in ("q", "k", "v", "log_alpha", "beta")}
+    args = (dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], to_dev(g["d_o"]), to_dev(d["S0"]), None,
+            to_dev(g["dS_final"]))
+    a = kda.kda_chunk_bwd(*args, chunk=32)
+    b = kda.kda_chunk_bwd(*args, chunk=64)
+    torch.cuda.synchronize()
+    for name in a:
+        assert torch.equal(a[name], b[name]), name
+    check(d, g, "chunk 64 forward")
