@@ -508,6 +508,18 @@ __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
         rB = rec[Rec<D>::BETA + (tid & (BC - 1))];
         rV.load(a.v, tok0 + i * BC, min(BC, L - i * BC), a.H, h, D, jt * TW);
     };
+    // R of the previous chunk, kept in registers until the next chunk's global stores
+    constexpr int RQ = BC * TW / BT;
+    static_assert(BC * TW % BT == 0 && D * TW % (4 * BT) == 0, "");
+    float rkeep[RQ];
+    auto store_r = [&](int ic) __attribute__((always_inline)) {
+        float* rout = a.rbuf + cslot(a, c0 + ic, h) * BC * D + jt * TW;
+#pragma unroll
+        for (int q = 0; q < RQ; ++q) {
+            const int e = tid + q * BT;
+            rout[(size_t)(e / TW) * D + e % TW] = rkeep[q];
+        }
+    };
     if (i1 > i0) fetch(i0);
     for (int i = i0; i < i1; ++i) {
         lds_barrier();
@@ -515,20 +527,28 @@ __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
         rKpp.store(sKpp, LD);
         rM.store(sM, LC);
         rV.store(sV, LT);
-        if (tid < D) {
-            sEm[tid] = rEm;
-            sEn[tid] = rEn;
+        sEm[tid & (D - 1)] = rEm;   // every thread: copies of one value, no divergent wait
+        sEn[tid & (D - 1)] = rEn;
+        sB[tid & (BC - 1)] = rB;
+        // this chunk's global stores (the entry state, the previous chunk's R) go out before the
+        // next chunk's loads, so waiting for those loads never waits on a store
+        if constexpr (!CKPT) {
+            float* slot = a.states + sslot(a, s0 + i, h) * DD + jt * TW;
+#pragma unroll
+            for (int q = 0; q < D * TW / (4 * BT); ++q) {
+                const int e = tid + q * BT, r = e / (TW / 4), c = 4 * (e % (TW / 4));
+                *reinterpret_cast<v4f*>(slot + (size_t)r * D + c) = *reinterpret_cast<const v4f*>(sS + r * LT + c);
+            }
+            if (i > i0) store_r(i - 1);
         }
-        if (tid < BC) sB[tid] = rB;
         if (i + 1 < i1) fetch(i + 1);
         lds_barrier();
-        // keep the entry state (not in the checkpoint sweep), then scale it to S_m
-        float* slot = a.states + sslot(a, s0 + i, h) * DD + jt * TW;
-        for (int e = tid; e < D * TW / 4; e += BT) {
-            const int r = e / (TW / 4), c = 4 * (e % (TW / 4));
+        // scale the entry state to S_m
+#pragma unroll
+        for (int q = 0; q < D * TW / (4 * BT); ++q) {
+            const int e = tid + q * BT, r = e / (TW / 4), c = 4 * (e % (TW / 4));
             const v4f x = *reinterpret_cast<const v4f*>(sS + r * LT + c);
             const float m = sEm[r];
-            if (!CKPT) *reinterpret_cast<v4f*>(slot + (size_t)r * D + c) = x;
             *reinterpret_cast<v4f*>(sS + r * LT + c) = v4f{x.x * m, x.y * m, x.z * m, x.w * m};
         }
         lds_barrier();
@@ -540,11 +560,11 @@ __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
             for (int v = 0; v < 4; ++v) sR[kh * BC * LT + (16 * rt + acc_row(v)) * LT + acc_col()] = acc[v];
         }
         lds_barrier();
-        float* rout = a.rbuf + cslot(a, c0 + i, h) * BC * D + jt * TW;
-        for (int e = tid; e < BC * TW; e += BT) {   // R = V - K' S_m (kept for the gradient step), Y = Diag(beta) R
-            const int r = e / TW, c = e % TW;
+#pragma unroll
+        for (int q = 0; q < RQ; ++q) {   // R = V - K' S_m (kept for the gradient step), Y = Diag(beta) R
+            const int e = tid + q * BT, r = e / TW, c = e % TW;
             const float rr = sV[r * LT + c] - sR[r * LT + c] - sR[BC * LT + r * LT + c];
-            if (!CKPT) rout[(size_t)r * D + c] = rr;
+            rkeep[q] = rr;
             sR[r * LT + c] = sB[r] * rr;
         }
         lds_barrier();
@@ -567,6 +587,7 @@ __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
             }
         }
     }
+    if (!CKPT && i1 > i0) store_r(i1 - 1);
     __syncthreads();
     // the exit state: the final state or the window's last slot, or in the checkpoint sweep the
     // next window's entry state (only for a sequence that goes on)
@@ -617,6 +638,18 @@ __global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
         rB = rec[Rec<D>::BETA + (tid & (BC - 1))];
         rO.load(a.dO, tok0 + i * BC, min(BC, L - i * BC), a.H, h, D, jt * TW);
     };
+    // dE of the chunk after this one, kept in registers until this chunk's global stores
+    constexpr int RQ = BC * TW / BT;
+    static_assert(BC * TW % BT == 0 && D * TW % (4 * BT) == 0, "");
+    float dkeep[RQ];
+    auto store_de = [&](int ic) __attribute__((always_inline)) {
+        float* deout = a.debuf + cslot(a, c0 + ic, h) * BC * D + jt * TW;
+#pragma unroll
+        for (int q = 0; q < RQ; ++q) {
+            const int e = tid + q * BT;
+            deout[(size_t)(e / TW) * D + e % TW] = dkeep[q];
+        }
+    };
     if (i1 > i0) fetch(i1 - 1);
     for (int i = i1 - 1; i >= i0; --i) {
         const int j = c0 + i;
@@ -627,20 +660,28 @@ __global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
         rM.store(sM, LC);
         rP.store(sP, LC);
         rO.store(sO, LT);
-        if (tid < D) {
-            sEm[tid] = rEm;
-            sEn[tid] = rEn;
+        sEm[tid & (D - 1)] = rEm;   // every thread: copies of one value, no divergent wait
+        sEn[tid & (D - 1)] = rEn;
+        sB[tid & (BC - 1)] = rB;
+        // this chunk's global stores (its dS_next, the next chunk's dE) go out before the
+        // previous chunk's loads, so waiting for those loads never waits on a store
+        {
+            float* slot = a.dstates + cslot(a, j, h) * DD + jt * TW;
+#pragma unroll
+            for (int q = 0; q < D * TW / (4 * BT); ++q) {
+                const int e = tid + q * BT, r = e / (TW / 4), c = 4 * (e % (TW / 4));
+                *reinterpret_cast<v4f*>(slot + (size_t)r * D + c) = *reinterpret_cast<const v4f*>(sS + r * LT + c);
+            }
+            if (i < i1 - 1) store_de(i + 1);
         }
-        if (tid < BC) sB[tid] = rB;
         if (i > i0) fetch(i - 1);
         lds_barrier();
-        // keep this chunk's dS_next, then scale it to dS_n
-        float* slot = a.dstates + cslot(a, j, h) * DD + jt * TW;
-        for (int e = tid; e < D * TW / 4; e += BT) {
-            const int r = e / (TW / 4), c = 4 * (e % (TW / 4));
+        // scale dS_next to dS_n
+#pragma unroll
+        for (int q = 0; q < D * TW / (4 * BT); ++q) {
+            const int e = tid + q * BT, r = e / (TW / 4), c = 4 * (e % (TW / 4));
             const v4f x = *reinterpret_cast<const v4f*>(sS + r * LT + c);
             const float m = sEn[r];
-            *reinterpret_cast<v4f*>(slot + (size_t)r * D + c) = x;
             *reinterpret_cast<v4f*>(sS + r * LT + c) = v4f{x.x * m, x.y * m, x.z * m, x.w * m};
         }
         lds_barrier();
@@ -655,12 +696,12 @@ __global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
             for (int v = 0; v < 4; ++v) part[(16 * rt + acc_row(v)) * LT + acc_col()] = acc[v];
         }
         lds_barrier();
-        float* deout = a.debuf + cslot(a, j, h) * BC * D + jt * TW;
-        for (int e = tid; e < BC * TW; e += BT) {   // dE (kept for the gradient step)
-            const int r = e / TW, c = e % TW;
+#pragma unroll
+        for (int q = 0; q < RQ; ++q) {   // dE (kept for the gradient step)
+            const int e = tid + q * BT, r = e / TW, c = e % TW;
             const float x = sR[r * LT + c] + sV[r * LT + c];
             sR[r * LT + c] = x;
-            deout[(size_t)r * D + c] = x;
+            dkeep[q] = x;
         }
         lds_barrier();
         if (w < 2) {   // -dV = -Diag(beta) M^T dE
@@ -686,6 +727,7 @@ __global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
             }
         }
     }
+    if (i1 > i0) store_de(i0);
     __syncthreads();
     // dS0 after the first window; before it, the gradient for the window before this one
     float* out = WIN && a.w0 > 0 ? a.dcarry : a.dS0;
@@ -726,19 +768,17 @@ __global__ __launch_bounds__(grad_threads<D>()) void grad_kernel(BackwardArgs a)
     const float* rec = a.prep + cslot(a, j, h) * Rec<D>::SIZE;
     const size_t slot = a.W ? state_slot<true>(a, p.n, p.i) : state_slot<false>(a, p.n, p.i);
     const float* S = a.states + sslot(a, slot, h) * DD;
-    const float* Snext = a.states + sslot(a, slot + 1, h) * DD;
     const float* dS = a.dstates + cslot(a, j, h) * DD;
     const float* Rg = a.rbuf + cslot(a, j, h) * BC * D;    // R = V - K' S_m of the state pass
     const float* dEg = a.debuf + cslot(a, j, h) * BC * D;  // dE of the reverse pass
 
-    // one column tile of S, dS_next, S_next, R, dE and dO, fetched a tile ahead
-    Stage<D, GW, GT> rS, rdS, rSn;
+    // one column tile of S, dS_next, R, dE and dO, fetched a tile ahead
+    Stage<D, GW, GT> rS, rdS;
     Stage<BC, GW, GT> rR, rdE;
     StageRows<IN, GW, GT> rO;
     auto fetch = [&](int ct) __attribute__((always_inline)) {
         rS.load(S + ct * GW, D);
         rdS.load(dS + ct * GW, D);
-        rSn.load(Snext + ct * GW, D);
         rR.load(Rg + ct * GW, D);
         rdE.load(dEg + ct * GW, D);
         rO.load(a.dO, p.t0, p.len, a.H, h, D, ct * GW);
@@ -793,16 +833,18 @@ __global__ __launch_bounds__(grad_threads<D>()) void grad_kernel(BackwardArgs a)
                 *reinterpret_cast<v4f*>(sY + r * LT + c) = v4f{x.x * b, x.y * b, x.z * b, x.w * b};
             }
         }
-        // S_m, dS_n tiles; rowsum(dS_next * S_next) for the last row's db
+        // S_m, dS_n tiles; rowsum(dS_n * S_m), the first part of the last row's db term
+        // rowsum(dS_next * S_next) = rowsum(dS_n * (S_m + K''^T E)) (the second part is taken
+        // from E dS_n^T after the column loop)
 #pragma unroll
         for (int it = 0; it < Stage<D, GW, GT>::IT; ++it) {
             constexpr int C4 = GW / 4;
             const int e = tid + it * GT, r = e / C4, c = 4 * (e % C4);
-            const v4f x = rS.x[it], y = rdS.x[it], z = rSn.x[it];
+            const v4f x = rS.x[it], y = rdS.x[it];
             const float em = sEm[r], en = sEn[r];
             *reinterpret_cast<v4f*>(sSm + r * LT + c) = v4f{x.x * em, x.y * em, x.z * em, x.w * em};
             *reinterpret_cast<v4f*>(sdSn + r * LT + c) = v4f{y.x * en, y.y * en, y.z * en, y.w * en};
-            float t = y.x * z.x + y.y * z.y + y.z * z.z + y.w * z.w;
+            float t = (y.x * x.x + y.y * x.y + y.z * x.z + y.w * x.w) * (em * en);
             // the GW / 4 v4f groups of row r sit in consecutive lanes
 #pragma unroll
             for (int off = C4 / 2; off >= 1; off >>= 1) t += __shfl_xor(t, off, 64);
@@ -845,6 +887,19 @@ __global__ __launch_bounds__(grad_threads<D>()) void grad_kernel(BackwardArgs a)
         }
     }
     lds_barrier();
+    {   // db's last-row term, second part: sum over rows t of K''(t, r) (E dS_n^T)(t, r), with
+        // E dS_n^T in dKpp before the dP and dL terms join it; channel r belongs to one wave
+        float t = 0.f;
+#pragma unroll
+        for (int q = 0; q < RTW; ++q)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                t += sKpp[(16 * (rt0 + q) + acc_row(v)) * LD + 16 * dt + acc_col()] * dKpp[q][v];
+        static_assert(RTW == 2, "one wave per channel tile holds all of the chunk's rows");
+        t += __shfl_xor(t, 16, 64);
+        t += __shfl_xor(t, 32, 64);
+        if ((tid & 63) < 16) sDbn[16 * dt + acc_col()] += t;
+    }
     // dP = Tril(dO E^T) -> sdE;  dA = -StrictTril(dY E^T) -> sdY  (both C x C, row stride LC)
     if (w < 4) {
 #pragma unroll
