@@ -30,7 +30,7 @@
 // reads instead of recomputing):
 //   seq_scan_kernel   packed batches: first chunk index of every sequence
 //   prep_kernel       per (chunk, head): Q', K', K'', M, P, L, e_m, e_n, beta, b - m -> record
-//   state_fwd_kernel  per (sequence, head, 16 value columns): every chunk's entry state
+//   state_fwd_kernel  per (sequence, head, 32 value columns): every chunk's entry state
 //                     and the final state, chunks in order
 //   state_rev_kernel  same split: every chunk's dS_next, chunks in reverse order; dS0
 //   grad_kernel       per (chunk, head): dq, dk, dv, dlog_alpha, dbeta
@@ -53,7 +53,6 @@ namespace {
 
 constexpr int BC = 32;    // chunk length
 constexpr int BT = 256;   // threads per workgroup (4 waves)
-constexpr int TW = 16;    // value columns per state-pass workgroup
 constexpr int GW = 32;    // value columns per step of the gradient kernel
 
 using f4 = __attribute__((__vector_size__(4 * sizeof(float)))) float;
@@ -174,6 +173,18 @@ __device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
     for (int p = 0; p < 4; ++p) split_pair(x[2 * p], x[2 * p + 1], h[p], l[p]);
     hi = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
     lo = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
+}
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Four fp32 values -> hi and lo bf16x4 operands.
+__device__ __forceinline__ void split4(const float* x, bf16x4& hi, bf16x4& lo) {
+    uint32_t h[2], l[2];
+    split_pair(x[0], x[1], h[0], l[0]);
+    split_pair(x[2], x[3], h[1], l[1]);
+    hi = __builtin_bit_cast(bf16x4, u32x2{h[0], h[1]});
+    lo = __builtin_bit_cast(bf16x4, u32x2{l[0], l[1]});
 }
 
 // acc (16 x 16) += A (16 x K) B (K x 16), A(i, k) = A[i*ai + k*ak], B(k, j) = B[k*bk + j*bj],
@@ -321,17 +332,6 @@ struct StageRows {
     }
 };
 
-// The D x TW column tile of a [D, D] state starting at g (or zeros when g is null) into LDS.
-template <int D>
-__device__ __forceinline__ void init_tile(float* s, int ls, const float* g) {
-    for (int e = threadIdx.x; e < D * TW / 4; e += BT) {
-        const int r = e / (TW / 4), c = 4 * (e % (TW / 4));
-        v4f x{0.f, 0.f, 0.f, 0.f};
-        if (g) x = *reinterpret_cast<const v4f*>(g + (size_t)r * D + c);
-        *reinterpret_cast<v4f*>(s + r * ls + c) = x;
-    }
-}
-
 // Maps a linear workgroup index to (unit, column tile) so that the tiles of one unit
 // land on one XCD (workgroups are dealt to the 8 XCDs round-robin) and share its L2.
 __device__ __forceinline__ void unit_tile(int b, int nwg, int ntile, int& unit, int& tile) {
@@ -471,15 +471,166 @@ __global__ __launch_bounds__(BT) void prep_kernel(BackwardArgs a) {
     if (tid < BC) rec[Rec<D>::BETA + tid] = sB[tid];
 }
 
+// ---------------------------------------------------------------- loader / compute state passes
+// A state-pass workgroup owns an SW = 32 column slice of one (sequence, head)'s state and runs
+// 12 waves.  Waves 0-7 compute: wave w holds columns 16 (w / 4) .. + 15 of the slice and rows
+// [(w % 4) D/4, (w % 4 + 1) D/4) of the state in MFMA accumulators (NT = D / 64 stacked 16 x 16
+// tiles; lane l holds rows 16 q + 4 (l / 16) + v, v = 0..3, of tile q at column l % 16).  Waves
+// 8-11 load: each chunk's operands go from the record into registers two chunks ahead and into
+// one of two LDS slots one chunk ahead, so the computing waves read only LDS and the memory
+// latency is hidden behind two chunks of work.  Two workgroup barriers per chunk order both.
+constexpr int SW = 32;               // value columns per workgroup
+constexpr int SCW = 8, SLW = 4;      // computing and loading waves
+constexpr int SLT = 64 * SLW;        // loading threads
+constexpr int STH = 64 * (SCW + SLW);
+
+// out (16 x 16) += A X, the sum over this wave's D / 4 state rows, with X the wave's state tiles
+// as MFMA B operand (the k index taken in the order the accumulators hold the rows) and
+// a[4 q + v] = A(l % 16, row 16 q + 4 (l / 16) + v of the wave).
+//  * split bf16, two tiles: one 32-deep step, k slot 8 (l / 16) + j <-> tile j / 4, row 4 (l / 16) + j % 4;
+//  * split bf16, one tile: one 16-deep step (v_mfma_f32_16x16x16_bf16);
+//  * fp32: 4 NT steps of the 4-deep fp32 product, step (q, v) taking row 16 q + 4 (l / 16) + v.
+template <int NT, bool SPLIT>
+__device__ __forceinline__ void mma_xb(f4& out, const float (&a)[4 * NT], const f4 (&x)[NT]) {
+    if constexpr (!SPLIT) {
+#pragma unroll
+        for (int q = 0; q < NT; ++q)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) out = __builtin_amdgcn_mfma_f32_16x16x4f32(a[4 * q + v], x[q][v], out, 0, 0, 0);
+    } else if constexpr (NT == 2) {
+        const float b[8] = {x[0][0], x[0][1], x[0][2], x[0][3], x[1][0], x[1][1], x[1][2], x[1][3]};
+        bf16x8 ah, al, bh, bl;
+        split8(a, ah, al);
+        split8(b, bh, bl);
+        out = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, out, 0, 0, 0);
+        out = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, out, 0, 0, 0);
+        out = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, out, 0, 0, 0);
+    } else {
+        static_assert(NT == 1, "");
+        const float b[4] = {x[0][0], x[0][1], x[0][2], x[0][3]};
+        bf16x4 ah, al, bh, bl;
+        split4(a, ah, al);
+        split4(b, bh, bl);
+        out = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, out, 0, 0, 0);
+        out = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, out, 0, 0, 0);
+        out = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, out, 0, 0, 0);
+    }
+}
+
+// out (16 x 16) += A B over a 32-deep sum, lane l supplying a[j] = A(l % 16, 8 (l / 16) + j) and
+// b[j] = B(8 (l / 16) + j, l % 16); the fp32 form takes k = 8 (l / 16) + s in its step s.
+template <bool SPLIT>
+__device__ __forceinline__ void mma8(f4& out, const float (&a)[8], const float (&b)[8]) {
+    if constexpr (SPLIT) {
+        bf16x8 ah, al, bh, bl;
+        split8(a, ah, al);
+        split8(b, bh, bl);
+        out = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, out, 0, 0, 0);
+        out = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, out, 0, 0, 0);
+        out = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, out, 0, 0, 0);
+    } else {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) out = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], out, 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void ld4(float* d, const float* p) {
+    const v4f x = *reinterpret_cast<const v4f*>(p);
+    d[0] = x.x;
+    d[1] = x.y;
+    d[2] = x.z;
+    d[3] = x.w;
+}
+
+// Eight consecutive floats (16-byte aligned).
+__device__ __forceinline__ void ld8(float (&d)[8], const float* p) {
+    ld4(d, p);
+    ld4(d + 4, p + 4);
+}
+
+// One 16-byte word of a C x SW block of bf16 or fp32 input per loading thread (8 bf16 or 4 fp32
+// values; the bf16 block needs half the threads).
+template <class IN>
+struct Raw8 {
+    static constexpr bool B16 = std::is_same<IN, BF16>::value;
+    using word = typename std::conditional<B16, u32x4, v4f>::type;
+    static constexpr int PER = B16 ? 8 : 4, WPR = SW / PER, WORDS = BC * WPR;   // values per word, words per row
+    static_assert(WORDS <= SLT, "");
+};
+
+// Widen one such word to fp32.
+template <class IN>
+__device__ __forceinline__ void widen8(const typename Raw8<IN>::word& x, float* f) {
+    if constexpr (Raw8<IN>::B16) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            f[2 * p] = __uint_as_float(x[p] << 16);
+            f[2 * p + 1] = __uint_as_float(x[p] & 0xffff0000u);
+        }
+    } else {
+        f[0] = x.x;
+        f[1] = x.y;
+        f[2] = x.z;
+        f[3] = x.w;
+    }
+}
+
+// Rows [t0, t0 + len) of a [tokens, H, D] input, this workgroup's SW columns from col0: one word
+// per loading thread (rows past len read row len - 1, threads past the block its last word).
+template <class IN>
+__device__ __forceinline__ typename Raw8<IN>::word load_rows(const void* p, int lt, int t0, int len, int H, int h, int D,
+                                                            int col0) {
+    using R8 = Raw8<IN>;
+    const int e = min(lt, R8::WORDS - 1), r = min(e / R8::WPR, len - 1), c = R8::PER * (e % R8::WPR);
+    return *reinterpret_cast<const typename R8::word*>(static_cast<const typename IN::storage*>(p) +
+                                                       ((size_t)(t0 + r) * H + h) * D + col0 + c);
+}
+
+// ... and its transpose into an LDS plane [column][token] (row stride ls), zero past len.
+template <class IN>
+__device__ __forceinline__ void put_rows_t(const typename Raw8<IN>::word& x, float* s, int ls, int lt, int len) {
+    using R8 = Raw8<IN>;
+    if (lt < R8::WORDS) {
+        const int r = lt / R8::WPR, c = R8::PER * (lt % R8::WPR);
+        float f[R8::PER];
+        widen8<IN>(x, f);
+#pragma unroll
+        for (int p = 0; p < R8::PER; ++p) s[(c + p) * ls + r] = r < len ? f[p] : 0.f;
+    }
+}
+
+// LDS slot of one chunk's operands for the forward state pass (floats).
+template <int D>
+struct FwdSlot {
+    static constexpr int LK = D + 4, LM = BC + 4, LV = BC + 4;
+    static constexpr int KP = 0, KPP = BC * LK, M = 2 * BC * LK, EM = M + BC * LM, EN = EM + D, BETA = EN + D,
+                         VT = BETA + BC, SIZE = VT + SW * LV;   // VT: V^T, [column][token]
+    static_assert(SIZE % 4 == 0, "");
+};
+
+// The loading waves' registers for one chunk: K' and K'' rows, M, e_m / e_n / beta, and V.
+template <int D, class IN>
+struct FwdLoad {
+    static constexpr int NK = BC * D / 4 / SLT;   // 16-byte words of K' (and K'') per thread
+    static_assert(BC * D / 4 % SLT == 0 && BC * BC / 4 == SLT && 2 * D / 4 + BC / 4 <= SLT, "");
+    v4f kp[NK], kpp[NK], m, small;
+    typename Raw8<IN>::word v;
+};
+
 // WM: 0 every chunk (compact layout), 1 the current window, 2 the current window's checkpoint only.
+//
+// Per chunk: (A) every computing wave scales its rows to S_m = Diag(e_m) S and forms its partial of
+// Y = K' S_m over its rows; (B) R = V - Y, and one 16 x 16 tile each of E = M Diag(beta) R on the
+// computing waves of row group 0 and 1; (C) every computing wave updates its rows,
+// S <- Diag(e_n)(S_m + K''^T E).  The loading waves fill the next chunk's slot during (B).
 template <int D, class IN, int WM>
-__global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
+__global__ __launch_bounds__(STH) void state_fwd_kernel(BackwardArgs a) {
     constexpr bool WIN = WM != 0, CKPT = WM == 2;
     constexpr bool SPLIT = std::is_same<IN, BF16>::value;   // split-bf16 products for bf16 inputs
-    constexpr int LD = D + 4, LC = BC + 4, LT = TW + 4, NTILE = D / TW;
-    __shared__ __attribute__((aligned(16))) float sKp[BC * LD], sKpp[BC * LD], sM[BC * LC];
-    __shared__ __attribute__((aligned(16))) float sS[D * LT], sR[2 * BC * LT], sE[BC * LT], sV[BC * LT];
-    __shared__ float sB[BC], sEm[D], sEn[D];
+    constexpr int NT = D / 64, NTILE = D / SW, LY = BC + 4;
+    using SL = FwdSlot<D>;
+    __shared__ __attribute__((aligned(16))) float sSlot[2 * SL::SIZE];
+    __shared__ __attribute__((aligned(16))) float sY[SCW * 16 * LY], sE[2 * 16 * LY];
     int u, jt;
     unit_tile(blockIdx.x, gridDim.x, NTILE, u, jt);
     const int n = u / a.H, h = u % a.H, tid = threadIdx.x, w = tid >> 6;
@@ -491,125 +642,207 @@ __global__ __launch_bounds__(BT) void state_fwd_kernel(BackwardArgs a) {
     // per-chunk and state slots of chunk i: c0 + i and s0 + i
     const int c0 = WIN ? n * a.W - a.w0 : chunk0(a, n);
     const size_t s0 = WIN ? (size_t)n * (a.W + 1) - a.w0 : (size_t)c0 + n;
-    const float* init = WIN && a.w0 > 0 ? a.ckpt + ((size_t)(a.wi - 1) * a.N * a.H + u) * DD : a.S0 ? a.S0 + (size_t)u * DD : nullptr;
-    init_tile<D>(sS, LT, init ? init + jt * TW : nullptr);
-    // the next chunk's operands are fetched into registers while this chunk computes
-    Stage<BC, D> rKp, rKpp;
-    Stage<BC, BC> rM;
-    StageRows<IN, TW> rV;
-    float rEm = 0.f, rEn = 0.f, rB = 0.f;
-    auto fetch = [&](int i) __attribute__((always_inline)) {
-        const float* rec = a.prep + cslot(a, c0 + i, h) * Rec<D>::SIZE;
-        rKp.load(rec + Rec<D>::KP, D);
-        rKpp.load(rec + Rec<D>::KPP, D);
-        rM.load(rec + Rec<D>::M, BC);
-        rEm = rec[Rec<D>::EM + (tid & (D - 1))];
-        rEn = rec[Rec<D>::EN + (tid & (D - 1))];
-        rB = rec[Rec<D>::BETA + (tid & (BC - 1))];
-        rV.load(a.v, tok0 + i * BC, min(BC, L - i * BC), a.H, h, D, jt * TW);
-    };
-    // R of the previous chunk, kept in registers until the next chunk's global stores
-    constexpr int RQ = BC * TW / BT;
-    static_assert(BC * TW % BT == 0 && D * TW % (4 * BT) == 0, "");
-    float rkeep[RQ];
-    auto store_r = [&](int ic) __attribute__((always_inline)) {
-        float* rout = a.rbuf + cslot(a, c0 + ic, h) * BC * D + jt * TW;
+    if (i1 <= i0) {   // nothing to do but pass the entry state through (an empty sequence)
+        const float* init = WIN && a.w0 > 0 ? a.ckpt + ((size_t)(a.wi - 1) * a.N * a.H + u) * DD : a.S0 ? a.S0 + (size_t)u * DD : nullptr;
+        if (CKPT) return;
+        float* slot = a.states + sslot(a, s0 + i1, h) * DD + jt * SW;
+        for (int e = tid; e < D * SW; e += STH)
+            slot[(size_t)(e / SW) * D + e % SW] = init ? init[(size_t)(e / SW) * D + jt * SW + e % SW] : 0.f;
+        return;
+    }
+
+    if (w >= SCW) {
+        // ------------------------------------------------ loading waves
+        const int lt = tid - 64 * SCW;
+        using LDS_ = FwdLoad<D, IN>;
+        auto load = [&](LDS_& x, int i) __attribute__((always_inline)) {
+            i = min(i, i1 - 1);   // past the end: the last chunk again (never used)
+            const float* rec = a.prep + cslot(a, c0 + i, h) * Rec<D>::SIZE;
 #pragma unroll
-        for (int q = 0; q < RQ; ++q) {
-            const int e = tid + q * BT;
-            rout[(size_t)(e / TW) * D + e % TW] = rkeep[q];
+            for (int k = 0; k < LDS_::NK; ++k) {
+                const int e = lt + k * SLT;
+                x.kp[k] = *reinterpret_cast<const v4f*>(rec + Rec<D>::KP + 4 * e);
+                x.kpp[k] = *reinterpret_cast<const v4f*>(rec + Rec<D>::KPP + 4 * e);
+            }
+            x.m = *reinterpret_cast<const v4f*>(rec + Rec<D>::M + 4 * lt);
+            // e_m, e_n and beta are contiguous in the record: D + D + C floats
+            x.small = *reinterpret_cast<const v4f*>(rec + Rec<D>::EM + 4 * min(lt, (2 * D + BC) / 4 - 1));
+            // V rows of this workgroup's columns
+            x.v = load_rows<IN>(a.v, lt, tok0 + i * BC, min(BC, L - i * BC), a.H, h, D, jt * SW);
+        };
+        auto put = [&](const LDS_& x, int i) __attribute__((always_inline)) {
+            float* sl = sSlot + (i & 1) * SL::SIZE;
+#pragma unroll
+            for (int k = 0; k < LDS_::NK; ++k) {
+                const int e = lt + k * SLT, r = e / (D / 4), c = 4 * (e % (D / 4));
+                *reinterpret_cast<v4f*>(sl + SL::KP + r * SL::LK + c) = x.kp[k];
+                *reinterpret_cast<v4f*>(sl + SL::KPP + r * SL::LK + c) = x.kpp[k];
+            }
+            *reinterpret_cast<v4f*>(sl + SL::M + (lt / (BC / 4)) * SL::LM + 4 * (lt % (BC / 4))) = x.m;
+            if (lt < (2 * D + BC) / 4) *reinterpret_cast<v4f*>(sl + SL::EM + 4 * lt) = x.small;
+            put_rows_t<IN>(x.v, sl + SL::VT, SL::LV, lt, min(BC, L - min(i, i1 - 1) * BC));
+        };
+        LDS_ xa, xb;
+        // chunk i0 into its slot now; i0 + 1 and i0 + 2 into registers
+        load(xa, i0);
+        put(xa, i0);
+        load(xb, i0 + 1);
+        load(xa, i0 + 2);
+        lds_barrier();
+        // per chunk i: during (B) the slot of chunk i + 1 is written (from the registers loaded two
+        // chunks before) and chunk i + 3 is requested into the same registers.  Chunks go in pairs
+        // with no branch inside (an odd count ends with an idle step that the computing waves
+        // match), so each wait covers exactly the older register set.
+        for (int i = i0; i < i1; i += 2) {
+            lds_barrier();                 // B1 of chunk i
+            put(xb, i + 1);
+            load(xb, i + 3);
+            lds_barrier();                 // B2 of chunk i
+            lds_barrier();                 // B1 of chunk i + 1
+            put(xa, i + 2);
+            load(xa, i + 4);
+            lds_barrier();                 // B2 of chunk i + 1
+        }
+        return;
+    }
+
+    // ---------------------------------------------------- computing waves
+    const int g = (tid & 63) >> 4, li = tid & 15, ct = w >> 2, rg = w & 3;
+    const int r0 = rg * (D / 4) + 4 * g, col = jt * SW + 16 * ct + li;   // lane's first row, its column
+    const float* init = WIN && a.w0 > 0 ? a.ckpt + ((size_t)(a.wi - 1) * a.N * a.H + u) * DD : a.S0 ? a.S0 + (size_t)u * DD : nullptr;
+    f4 S[NT];
+#pragma unroll
+    for (int q = 0; q < NT; ++q)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) S[q][v] = init ? init[(size_t)(r0 + 16 * q + v) * D + col] : 0.f;
+    float rkeep[8];   // R(8 g + j, col) of the last chunk (row group 0 stores it)
+    auto store_r = [&](int ic) __attribute__((always_inline)) {
+        if (rg == 0) {
+            float* rout = a.rbuf + cslot(a, c0 + ic, h) * BC * D + col;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) rout[(size_t)(8 * g + j) * D] = rkeep[j];
         }
     };
-    if (i1 > i0) fetch(i0);
+    lds_barrier();   // chunk i0's slot is ready
     for (int i = i0; i < i1; ++i) {
-        lds_barrier();
-        rKp.store(sKp, LD);
-        rKpp.store(sKpp, LD);
-        rM.store(sM, LC);
-        rV.store(sV, LT);
-        sEm[tid & (D - 1)] = rEm;   // every thread: copies of one value, no divergent wait
-        sEn[tid & (D - 1)] = rEn;
-        sB[tid & (BC - 1)] = rB;
-        // this chunk's global stores (the entry state, the previous chunk's R) go out before the
-        // next chunk's loads, so waiting for those loads never waits on a store
-        if constexpr (!CKPT) {
-            float* slot = a.states + sslot(a, s0 + i, h) * DD + jt * TW;
+        const float* sl = sSlot + (i & 1) * SL::SIZE;
+        if constexpr (!CKPT) {   // this chunk's entry state, the previous chunk's R
+            float* slot = a.states + sslot(a, s0 + i, h) * DD + col;
 #pragma unroll
-            for (int q = 0; q < D * TW / (4 * BT); ++q) {
-                const int e = tid + q * BT, r = e / (TW / 4), c = 4 * (e % (TW / 4));
-                *reinterpret_cast<v4f*>(slot + (size_t)r * D + c) = *reinterpret_cast<const v4f*>(sS + r * LT + c);
-            }
+            for (int q = 0; q < NT; ++q)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) slot[(size_t)(r0 + 16 * q + v) * D] = S[q][v];
             if (i > i0) store_r(i - 1);
         }
-        if (i + 1 < i1) fetch(i + 1);
-        lds_barrier();
-        // scale the entry state to S_m
+        // (A) S_m and this wave's partial of Y = K' S_m, stored transposed ([column][token])
+        f4 Sm[NT];
+        {
+            float em[4 * NT];
 #pragma unroll
-        for (int q = 0; q < D * TW / (4 * BT); ++q) {
-            const int e = tid + q * BT, r = e / (TW / 4), c = 4 * (e % (TW / 4));
-            const v4f x = *reinterpret_cast<const v4f*>(sS + r * LT + c);
-            const float m = sEm[r];
-            *reinterpret_cast<v4f*>(sS + r * LT + c) = v4f{x.x * m, x.y * m, x.z * m, x.w * m};
+            for (int q = 0; q < NT; ++q) ld4(em + 4 * q, sl + SL::EM + r0 + 16 * q);
+#pragma unroll
+            for (int q = 0; q < NT; ++q)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) Sm[q][v] = S[q][v] * em[4 * q + v];
         }
-        lds_barrier();
-        {   // K' S_m, the key-channel sum split in two halves over the waves
-            const int rt = w & 1, kh = w >> 1;
-            f4 acc = zero4();
-            mma<D / 2, SPLIT>(acc, sKp + 16 * rt * LD + kh * (D / 2), LD, 1, sS + kh * (D / 2) * LT, LT, 1);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) sR[kh * BC * LT + (16 * rt + acc_row(v)) * LT + acc_col()] = acc[v];
+        for (int tt = 0; tt < 2; ++tt) {
+            float kp[4 * NT];
+#pragma unroll
+            for (int q = 0; q < NT; ++q) ld4(kp + 4 * q, sl + SL::KP + (16 * tt + li) * SL::LK + r0 + 16 * q);
+            f4 y = zero4();
+            mma_xb<NT, SPLIT>(y, kp, Sm);
+            *reinterpret_cast<v4f*>(sY + (w * 16 + li) * LY + 16 * tt + 4 * g) = v4f{y[0], y[1], y[2], y[3]};
         }
-        lds_barrier();
+        lds_barrier();   // B1
+        // (B) R = V - Y (kept for the gradient step) and E = M Diag(beta) R; row groups 0 and 1
+        // take token tile rg of their column half
+        if (rg < 2) {
+            float yb[8], br[8], vt[8], bt[8];
+            ld8(br, sY + ((4 * ct) * 16 + li) * LY + 8 * g);
 #pragma unroll
-        for (int q = 0; q < RQ; ++q) {   // R = V - K' S_m (kept for the gradient step), Y = Diag(beta) R
-            const int e = tid + q * BT, r = e / TW, c = e % TW;
-            const float rr = sV[r * LT + c] - sR[r * LT + c] - sR[BC * LT + r * LT + c];
-            rkeep[q] = rr;
-            sR[r * LT + c] = sB[r] * rr;
-        }
-        lds_barrier();
-        if (w < 2) {   // E = M Y
-            f4 acc = zero4();
-            mma<BC, SPLIT>(acc, sM + 16 * w * LC, LC, 1, sR, LT, 1);
+            for (int p = 1; p < 4; ++p) {
+                ld8(yb, sY + ((4 * ct + p) * 16 + li) * LY + 8 * g);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) sE[(16 * w + acc_row(v)) * LT + acc_col()] = acc[v];
-        }
-        lds_barrier();
-        for (int rt = w; rt < D / 16; rt += 4) {   // S_next = Diag(e_n)(S_m + K''^T E)
-            f4 acc;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) acc[v] = sS[(16 * rt + acc_row(v)) * LT + acc_col()];
-            mma<BC, SPLIT>(acc, sKpp + 16 * rt, 1, LD, sE, LT, 1);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int r = 16 * rt + acc_row(v);
-                sS[r * LT + acc_col()] = acc[v] * sEn[r];
+                for (int j = 0; j < 8; ++j) br[j] += yb[j];
             }
+            ld8(vt, sl + SL::VT + (16 * ct + li) * SL::LV + 8 * g);
+            ld8(bt, sl + SL::BETA + 8 * g);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                rkeep[j] = vt[j] - br[j];
+                br[j] = bt[j] * rkeep[j];
+            }
+            float m[8];
+            ld8(m, sl + SL::M + (16 * rg + li) * SL::LM + 8 * g);
+            f4 e = zero4();
+            mma8<SPLIT>(e, m, br);
+            *reinterpret_cast<v4f*>(sE + (16 * ct + li) * LY + 16 * rg + 4 * g) = v4f{e[0], e[1], e[2], e[3]};
+        }
+        lds_barrier();   // B2
+        // (C) S <- Diag(e_n)(S_m + K''^T E) on this wave's rows
+        float eb[8];
+        ld8(eb, sE + (16 * ct + li) * LY + 8 * g);
+#pragma unroll
+        for (int q = 0; q < NT; ++q) {
+            float kpp[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) kpp[j] = sl[SL::KPP + (8 * g + j) * SL::LK + rg * (D / 4) + 16 * q + li];
+            f4 acc = Sm[q];
+            mma8<SPLIT>(acc, kpp, eb);
+            float en[4];
+            ld4(en, sl + SL::EN + r0 + 16 * q);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) S[q][v] = acc[v] * en[v];
         }
     }
-    if (!CKPT && i1 > i0) store_r(i1 - 1);
-    __syncthreads();
+    if ((i1 - i0) & 1) {   // the loading waves' idle step
+        lds_barrier();
+        lds_barrier();
+    }
+    if (!CKPT) store_r(i1 - 1);
     // the exit state: the final state or the window's last slot, or in the checkpoint sweep the
     // next window's entry state (only for a sequence that goes on)
-    float* slot = a.states + sslot(a, s0 + i1, h) * DD + jt * TW;
+    float* slot = a.states + sslot(a, s0 + i1, h) * DD + col;
     if (CKPT) {
         if (i1 >= nch) return;
-        slot = a.ckpt + ((size_t)a.wi * a.N * a.H + u) * DD + jt * TW;
+        slot = a.ckpt + ((size_t)a.wi * a.N * a.H + u) * DD + col;
     }
-    for (int e = tid; e < D * TW / 4; e += BT) {
-        const int r = e / (TW / 4), c = 4 * (e % (TW / 4));
-        *reinterpret_cast<v4f*>(slot + (size_t)r * D + c) = *reinterpret_cast<const v4f*>(sS + r * LT + c);
-    }
+#pragma unroll
+    for (int q = 0; q < NT; ++q)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) slot[(size_t)(r0 + 16 * q + v) * D] = S[q][v];
 }
 
+// LDS slot of one chunk's operands for the reverse state pass (floats).
+template <int D>
+struct RevSlot {
+    static constexpr int LK = D + 4, LM = BC + 4, LV = BC + 4;
+    static constexpr int QP = 0, KP = BC * LK, KPP = 2 * BC * LK, M = 3 * BC * LK, P = M + BC * LM, EM = P + BC * LM,
+                         EN = EM + D, BETA = EN + D, OT = BETA + BC, SIZE = OT + SW * LV;   // OT: dO^T
+    static_assert(SIZE % 4 == 0, "");
+};
+
+template <int D, class IN>
+struct RevLoad {
+    static constexpr int NK = BC * D / 4 / SLT;
+    static_assert(BC * D / 4 % SLT == 0 && BC * BC / 4 == SLT && 2 * D / 4 + BC / 4 <= SLT, "");
+    v4f qp[NK], kp[NK], kpp[NK], m, p, small;
+    typename Raw8<IN>::word o;
+};
+
+// Per chunk, in reverse: (A) every computing wave scales its rows of dS_next to dS_n = Diag(e_n)
+// dS_next and forms its partial of dE = K'' dS_n (+ P^T dO from row groups 0 and 1, one token
+// tile each); (B) dE, and one 16 x 16 tile each of -dV = -Diag(beta) M^T dE on row groups 0 and 1;
+// (C) every computing wave takes its rows of dS = Diag(e_m)(dS_n + Q'^T dO - K'^T dV), the
+// earlier chunk's dS_next.  The loading waves fill the earlier chunk's slot during (B).
 template <int D, class IN, bool WIN>
-__global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
+__global__ __launch_bounds__(STH) void state_rev_kernel(BackwardArgs a) {
     constexpr bool SPLIT = std::is_same<IN, BF16>::value;   // split-bf16 products for bf16 inputs
-    constexpr int LD = D + 4, LC = BC + 4, LT = TW + 4, NTILE = D / TW;
-    __shared__ __attribute__((aligned(16))) float sQp[BC * LD], sKp[BC * LD], sKpp[BC * LD];
-    __shared__ __attribute__((aligned(16))) float sM[BC * LC], sP[BC * LC];
-    __shared__ __attribute__((aligned(16))) float sS[D * LT], sO[BC * LT], sR[BC * LT], sV[BC * LT];
-    __shared__ float sB[BC], sEm[D], sEn[D];
+    constexpr int NT = D / 64, NTILE = D / SW, LY = BC + 4;
+    using SL = RevSlot<D>;
+    __shared__ __attribute__((aligned(16))) float sSlot[2 * SL::SIZE];
+    __shared__ __attribute__((aligned(16))) float sY[SCW * 16 * LY], sV[2 * 16 * LY];
     int u, jt;
     unit_tile(blockIdx.x, gridDim.x, NTILE, u, jt);
     const int n = u / a.H, h = u % a.H, tid = threadIdx.x, w = tid >> 6;
@@ -620,123 +853,181 @@ __global__ __launch_bounds__(BT) void state_rev_kernel(BackwardArgs a) {
     const int c0 = WIN ? n * a.W - a.w0 : chunk0(a, n);   // per-chunk slot of chunk i: c0 + i
     // dS_final where the sequence ends in this window, else the gradient the later window left
     const float* init = WIN && nch > a.w0 + a.W ? a.dcarry + (size_t)u * DD : a.dS_final ? a.dS_final + (size_t)u * DD : nullptr;
-    init_tile<D>(sS, LT, init ? init + jt * TW : nullptr);
-    // the previous chunk's operands are fetched into registers while this chunk computes
-    Stage<BC, D> rQp, rKp, rKpp;
-    Stage<BC, BC> rM, rP;
-    StageRows<IN, TW> rO;
-    float rEm = 0.f, rEn = 0.f, rB = 0.f;
-    auto fetch = [&](int i) __attribute__((always_inline)) {
-        const float* rec = a.prep + cslot(a, c0 + i, h) * Rec<D>::SIZE;
-        rQp.load(rec + Rec<D>::QP, D);
-        rKp.load(rec + Rec<D>::KP, D);
-        rKpp.load(rec + Rec<D>::KPP, D);
-        rM.load(rec + Rec<D>::M, BC);
-        rP.load(rec + Rec<D>::P, BC);
-        rEm = rec[Rec<D>::EM + (tid & (D - 1))];
-        rEn = rec[Rec<D>::EN + (tid & (D - 1))];
-        rB = rec[Rec<D>::BETA + (tid & (BC - 1))];
-        rO.load(a.dO, tok0 + i * BC, min(BC, L - i * BC), a.H, h, D, jt * TW);
-    };
-    // dE of the chunk after this one, kept in registers until this chunk's global stores
-    constexpr int RQ = BC * TW / BT;
-    static_assert(BC * TW % BT == 0 && D * TW % (4 * BT) == 0, "");
-    float dkeep[RQ];
-    auto store_de = [&](int ic) __attribute__((always_inline)) {
-        float* deout = a.debuf + cslot(a, c0 + ic, h) * BC * D + jt * TW;
-#pragma unroll
-        for (int q = 0; q < RQ; ++q) {
-            const int e = tid + q * BT;
-            deout[(size_t)(e / TW) * D + e % TW] = dkeep[q];
-        }
-    };
-    if (i1 > i0) fetch(i1 - 1);
-    for (int i = i1 - 1; i >= i0; --i) {
-        const int j = c0 + i;
-        lds_barrier();
-        rQp.store(sQp, LD);
-        rKp.store(sKp, LD);
-        rKpp.store(sKpp, LD);
-        rM.store(sM, LC);
-        rP.store(sP, LC);
-        rO.store(sO, LT);
-        sEm[tid & (D - 1)] = rEm;   // every thread: copies of one value, no divergent wait
-        sEn[tid & (D - 1)] = rEn;
-        sB[tid & (BC - 1)] = rB;
-        // this chunk's global stores (its dS_next, the next chunk's dE) go out before the
-        // previous chunk's loads, so waiting for those loads never waits on a store
-        {
-            float* slot = a.dstates + cslot(a, j, h) * DD + jt * TW;
-#pragma unroll
-            for (int q = 0; q < D * TW / (4 * BT); ++q) {
-                const int e = tid + q * BT, r = e / (TW / 4), c = 4 * (e % (TW / 4));
-                *reinterpret_cast<v4f*>(slot + (size_t)r * D + c) = *reinterpret_cast<const v4f*>(sS + r * LT + c);
-            }
-            if (i < i1 - 1) store_de(i + 1);
-        }
-        if (i > i0) fetch(i - 1);
-        lds_barrier();
-        // scale dS_next to dS_n
-#pragma unroll
-        for (int q = 0; q < D * TW / (4 * BT); ++q) {
-            const int e = tid + q * BT, r = e / (TW / 4), c = 4 * (e % (TW / 4));
-            const v4f x = *reinterpret_cast<const v4f*>(sS + r * LT + c);
-            const float m = sEn[r];
-            *reinterpret_cast<v4f*>(sS + r * LT + c) = v4f{x.x * m, x.y * m, x.z * m, x.w * m};
-        }
-        lds_barrier();
-        {   // dE = P^T dO + K'' dS_n, the key-channel sum split in two halves over the waves
-            // (the second half's partial goes to sV, which holds -dV only later)
-            const int rt = w & 1, kh = w >> 1;
-            f4 acc = zero4();
-            mma<D / 2, SPLIT>(acc, sKpp + 16 * rt * LD + kh * (D / 2), LD, 1, sS + kh * (D / 2) * LT, LT, 1);
-            if (kh == 0) mma<BC, SPLIT>(acc, sP + 16 * rt, 1, LC, sO, LT, 1);
-            float* part = kh == 0 ? sR : sV;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) part[(16 * rt + acc_row(v)) * LT + acc_col()] = acc[v];
-        }
-        lds_barrier();
-#pragma unroll
-        for (int q = 0; q < RQ; ++q) {   // dE (kept for the gradient step)
-            const int e = tid + q * BT, r = e / TW, c = e % TW;
-            const float x = sR[r * LT + c] + sV[r * LT + c];
-            sR[r * LT + c] = x;
-            dkeep[q] = x;
-        }
-        lds_barrier();
-        if (w < 2) {   // -dV = -Diag(beta) M^T dE
-            f4 acc = zero4();
-            mma<BC, SPLIT>(acc, sM + 16 * w, 1, LC, sR, LT, 1);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int r = 16 * w + acc_row(v);
-                sV[r * LT + acc_col()] = -sB[r] * acc[v];
-            }
-        }
-        lds_barrier();
-        for (int rt = w; rt < D / 16; rt += 4) {   // dS = Diag(e_m)(dS_n + Q'^T dO - K'^T dV)
-            f4 acc;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) acc[v] = sS[(16 * rt + acc_row(v)) * LT + acc_col()];
-            mma<BC, SPLIT>(acc, sQp + 16 * rt, 1, LD, sO, LT, 1);
-            mma<BC, SPLIT>(acc, sKp + 16 * rt, 1, LD, sV, LT, 1);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int r = 16 * rt + acc_row(v);
-                sS[r * LT + acc_col()] = acc[v] * sEm[r];
-            }
-        }
-    }
-    if (i1 > i0) store_de(i0);
-    __syncthreads();
     // dS0 after the first window; before it, the gradient for the window before this one
     float* out = WIN && a.w0 > 0 ? a.dcarry : a.dS0;
-    if (out) {
-        for (int e = tid; e < D * TW / 4; e += BT) {
-            const int r = e / (TW / 4), c = 4 * (e % (TW / 4));
-            *reinterpret_cast<v4f*>(out + (size_t)u * DD + (size_t)r * D + jt * TW + c) =
-                *reinterpret_cast<const v4f*>(sS + r * LT + c);
+    if (i1 <= i0) {   // an empty sequence: dS0 = dS_final
+        if (out)
+            for (int e = tid; e < D * SW; e += STH) {
+                const size_t x = (size_t)u * DD + (size_t)(e / SW) * D + jt * SW + e % SW;
+                out[x] = init ? init[x - (size_t)u * DD] : 0.f;
+            }
+        return;
+    }
+
+    if (w >= SCW) {
+        // ------------------------------------------------ loading waves
+        const int lt = tid - 64 * SCW;
+        using LDS_ = RevLoad<D, IN>;
+        auto load = [&](LDS_& x, int i) __attribute__((always_inline)) {
+            i = max(i, i0);   // before the start: the first chunk again (never used)
+            const float* rec = a.prep + cslot(a, c0 + i, h) * Rec<D>::SIZE;
+#pragma unroll
+            for (int k = 0; k < LDS_::NK; ++k) {
+                const int e = lt + k * SLT;
+                x.qp[k] = *reinterpret_cast<const v4f*>(rec + Rec<D>::QP + 4 * e);
+                x.kp[k] = *reinterpret_cast<const v4f*>(rec + Rec<D>::KP + 4 * e);
+                x.kpp[k] = *reinterpret_cast<const v4f*>(rec + Rec<D>::KPP + 4 * e);
+            }
+            x.m = *reinterpret_cast<const v4f*>(rec + Rec<D>::M + 4 * lt);
+            x.p = *reinterpret_cast<const v4f*>(rec + Rec<D>::P + 4 * lt);
+            x.small = *reinterpret_cast<const v4f*>(rec + Rec<D>::EM + 4 * min(lt, (2 * D + BC) / 4 - 1));
+            x.o = load_rows<IN>(a.dO, lt, tok0 + i * BC, min(BC, L - i * BC), a.H, h, D, jt * SW);
+        };
+        auto put = [&](const LDS_& x, int i) __attribute__((always_inline)) {
+            float* sl = sSlot + (i & 1) * SL::SIZE;
+#pragma unroll
+            for (int k = 0; k < LDS_::NK; ++k) {
+                const int e = lt + k * SLT, r = e / (D / 4), c = 4 * (e % (D / 4));
+                *reinterpret_cast<v4f*>(sl + SL::QP + r * SL::LK + c) = x.qp[k];
+                *reinterpret_cast<v4f*>(sl + SL::KP + r * SL::LK + c) = x.kp[k];
+                *reinterpret_cast<v4f*>(sl + SL::KPP + r * SL::LK + c) = x.kpp[k];
+            }
+            const int mr = lt / (BC / 4), mc = 4 * (lt % (BC / 4));
+            *reinterpret_cast<v4f*>(sl + SL::M + mr * SL::LM + mc) = x.m;
+            *reinterpret_cast<v4f*>(sl + SL::P + mr * SL::LM + mc) = x.p;
+            if (lt < (2 * D + BC) / 4) *reinterpret_cast<v4f*>(sl + SL::EM + 4 * lt) = x.small;
+            put_rows_t<IN>(x.o, sl + SL::OT, SL::LV, lt, min(BC, L - max(i, i0) * BC));
+        };
+        LDS_ xa, xb;
+        // chunk i1 - 1 into its slot now; i1 - 2 and i1 - 3 into registers
+        load(xa, i1 - 1);
+        put(xa, i1 - 1);
+        load(xb, i1 - 2);
+        load(xa, i1 - 3);
+        lds_barrier();
+        // per chunk i (descending): during (B) the slot of chunk i - 1 is written and chunk i - 3
+        // is requested into the same registers; pairs with no branch inside, as in the forward pass
+        for (int i = i1 - 1; i >= i0; i -= 2) {
+            lds_barrier();                 // B1 of chunk i
+            put(xb, i - 1);
+            load(xb, i - 3);
+            lds_barrier();                 // B2 of chunk i
+            lds_barrier();                 // B1 of chunk i - 1
+            put(xa, i - 2);
+            load(xa, i - 4);
+            lds_barrier();                 // B2 of chunk i - 1
         }
+        return;
+    }
+
+    // ---------------------------------------------------- computing waves
+    const int g = (tid & 63) >> 4, li = tid & 15, ct = w >> 2, rg = w & 3;
+    const int r0 = rg * (D / 4) + 4 * g, col = jt * SW + 16 * ct + li;
+    f4 dS[NT];
+#pragma unroll
+    for (int q = 0; q < NT; ++q)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) dS[q][v] = init ? init[(size_t)(r0 + 16 * q + v) * D + col] : 0.f;
+    float dkeep[8];   // dE(8 g + j, col) of the chunk after this one (row group 0 stores it)
+    auto store_de = [&](int ic) __attribute__((always_inline)) {
+        if (rg == 0) {
+            float* deout = a.debuf + cslot(a, c0 + ic, h) * BC * D + col;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) deout[(size_t)(8 * g + j) * D] = dkeep[j];
+        }
+    };
+    lds_barrier();   // chunk i1 - 1's slot is ready
+    for (int i = i1 - 1; i >= i0; --i) {
+        const float* sl = sSlot + (i & 1) * SL::SIZE;
+        {   // this chunk's dS_next, the later chunk's dE
+            float* slot = a.dstates + cslot(a, c0 + i, h) * DD + col;
+#pragma unroll
+            for (int q = 0; q < NT; ++q)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) slot[(size_t)(r0 + 16 * q + v) * D] = dS[q][v];
+            if (i < i1 - 1) store_de(i + 1);
+        }
+        float ob[8];   // dO(8 g + j, col)
+        ld8(ob, sl + SL::OT + (16 * ct + li) * SL::LV + 8 * g);
+        // (A) dS_n and this wave's partial of dE = K'' dS_n (+ P^T dO), stored transposed
+        f4 dSn[NT];
+        {
+            float en[4 * NT];
+#pragma unroll
+            for (int q = 0; q < NT; ++q) ld4(en + 4 * q, sl + SL::EN + r0 + 16 * q);
+#pragma unroll
+            for (int q = 0; q < NT; ++q)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) dSn[q][v] = dS[q][v] * en[4 * q + v];
+        }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            float kpp[4 * NT];
+#pragma unroll
+            for (int q = 0; q < NT; ++q) ld4(kpp + 4 * q, sl + SL::KPP + (16 * tt + li) * SL::LK + r0 + 16 * q);
+            f4 y = zero4();
+            mma_xb<NT, SPLIT>(y, kpp, dSn);
+            if (rg == tt) {   // P^T dO, token tile tt: A(t, s) = P(s, t)
+                float p[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) p[j] = sl[SL::P + (8 * g + j) * SL::LM + 16 * tt + li];
+                mma8<SPLIT>(y, p, ob);
+            }
+            *reinterpret_cast<v4f*>(sY + (w * 16 + li) * LY + 16 * tt + 4 * g) = v4f{y[0], y[1], y[2], y[3]};
+        }
+        lds_barrier();   // B1
+        // (B) dE (kept for the gradient step) and -dV = -Diag(beta) M^T dE; row groups 0 and 1 take
+        // token tile rg of their column half
+        if (rg < 2) {
+            float yb[8];
+            ld8(dkeep, sY + ((4 * ct) * 16 + li) * LY + 8 * g);
+#pragma unroll
+            for (int p = 1; p < 4; ++p) {
+                ld8(yb, sY + ((4 * ct + p) * 16 + li) * LY + 8 * g);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) dkeep[j] += yb[j];
+            }
+            float m[8], bt[4];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) m[j] = sl[SL::M + (8 * g + j) * SL::LM + 16 * rg + li];   // M^T(t', t) = M(t, t')
+            ld4(bt, sl + SL::BETA + 16 * rg + 4 * g);
+            f4 x = zero4();
+            mma8<SPLIT>(x, m, dkeep);
+            *reinterpret_cast<v4f*>(sV + (16 * ct + li) * LY + 16 * rg + 4 * g) =
+                v4f{-bt[0] * x[0], -bt[1] * x[1], -bt[2] * x[2], -bt[3] * x[3]};
+        }
+        lds_barrier();   // B2
+        // (C) dS = Diag(e_m)(dS_n + Q'^T dO - K'^T dV) on this wave's rows
+        float vb[8];
+        ld8(vb, sV + (16 * ct + li) * LY + 8 * g);
+#pragma unroll
+        for (int q = 0; q < NT; ++q) {
+            float qp[8], kp[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int x = (8 * g + j) * SL::LK + rg * (D / 4) + 16 * q + li;
+                qp[j] = sl[SL::QP + x];
+                kp[j] = sl[SL::KP + x];
+            }
+            f4 acc = dSn[q];
+            mma8<SPLIT>(acc, qp, ob);
+            mma8<SPLIT>(acc, kp, vb);
+            float em[4];
+            ld4(em, sl + SL::EM + r0 + 16 * q);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) dS[q][v] = acc[v] * em[v];
+        }
+    }
+    if ((i1 - i0) & 1) {   // the loading waves' idle step
+        lds_barrier();
+        lds_barrier();
+    }
+    store_de(i0);
+    if (out) {
+#pragma unroll
+        for (int q = 0; q < NT; ++q)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) out[(size_t)u * DD + (size_t)(r0 + 16 * q + v) * D + col] = dS[q][v];
     }
 }
 
@@ -997,8 +1288,8 @@ hipError_t launch_typed(BackwardArgs a, int nc_max, int n_win, hipStream_t st) {
     if (!a.W) {
         if (nc_max > 0) prep_kernel<D, IN, SG><<<nc_max * a.H, BT, 0, st>>>(a);
         if (units > 0) {
-            state_fwd_kernel<D, IN, 0><<<units * (D / TW), BT, 0, st>>>(a);
-            state_rev_kernel<D, IN, false><<<units * (D / TW), BT, 0, st>>>(a);
+            state_fwd_kernel<D, IN, 0><<<units * (D / SW), STH, 0, st>>>(a);
+            state_rev_kernel<D, IN, false><<<units * (D / SW), STH, 0, st>>>(a);
         }
         if (nc_max > 0) grad_kernel<D, IN, OB, SG><<<nc_max * a.H, grad_threads<D>(), 0, st>>>(a);
         return hipGetLastError();
@@ -1012,14 +1303,14 @@ hipError_t launch_typed(BackwardArgs a, int nc_max, int n_win, hipStream_t st) {
         a.wi = wi;
         a.w0 = wi * a.W;
         prep_kernel<D, IN, SG><<<grid, BT, 0, st>>>(a);
-        state_fwd_kernel<D, IN, 2><<<units * (D / TW), BT, 0, st>>>(a);
+        state_fwd_kernel<D, IN, 2><<<units * (D / SW), STH, 0, st>>>(a);
     }
     for (int wi = n_win - 1; wi >= 0; --wi) {
         a.wi = wi;
         a.w0 = wi * a.W;
         prep_kernel<D, IN, SG><<<grid, BT, 0, st>>>(a);
-        state_fwd_kernel<D, IN, 1><<<units * (D / TW), BT, 0, st>>>(a);
-        state_rev_kernel<D, IN, true><<<units * (D / TW), BT, 0, st>>>(a);
+        state_fwd_kernel<D, IN, 1><<<units * (D / SW), STH, 0, st>>>(a);
+        state_rev_kernel<D, IN, true><<<units * (D / SW), STH, 0, st>>>(a);
         grad_kernel<D, IN, OB, SG><<<grid, grad_threads<D>(), 0, st>>>(a);
     }
     return hipGetLastError();
