@@ -406,6 +406,24 @@ def main():
     dec_med = dec_ms[len(dec_ms) // 2]
     step_avg = sum(step_ms) / len(step_ms)
     dbytes = decode_alg_bytes(N, Hd, d)
+    # the same steps captured once as a HIP graph and replayed (no host work per step)
+    dg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(dg):
+        for i in range(args.decode_steps):
+            kda.kda_recurrent_step(*steps_in[i], S, o=od)
+    graph_ms = []
+    for rep in range(3):
+        S.copy_(S_init)
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        dg.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_ms.append(g0.elapsed_time(g1))
+    graph_ms.sort()
+    graph_med = graph_ms[len(graph_ms) // 2]
+    del dg
     decode = {
         "value": args.decode_steps / (dec_med / 1e3), "unit": "steps/s",
         "ms_per_step": dec_med / args.decode_steps,
@@ -416,6 +434,10 @@ def main():
                      "unit": "GB/s", "frac": dbytes / (step_avg / 1e3) / 1e9 / HBM_PEAK_GBS, "traffic": counted_traffic("decode"),
                      "kernel": "decode_step_kernel<128,BF16,bf16 out>", "avg_launch_us": step_avg * 1e3,
                      "bytes_per_launch": dbytes},
+        "graph": {"what": f"the {args.decode_steps} steps replayed from one captured HIP graph",
+                  "value": args.decode_steps / (graph_med / 1e3), "unit": "steps/s",
+                  "ms_per_step": graph_med / args.decode_steps,
+                  "hbm_frac": dbytes / (graph_med / args.decode_steps / 1e3) / 1e9 / HBM_PEAK_GBS},
     }
 
     # ------------------------------------------------------------------ fused prologue / epilogue
@@ -545,10 +567,27 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) / reps * 1e3
+        # the call captured once as a HIP graph (workspace allocated beforehand), replayed reps times
+        wsc = torch.empty(max(kda.kda_chunk_fwd_workspace_bytes(xc["B"], xc["T"], w.H, w.D, w.D, Nc, True), 256),
+                          dtype=torch.uint8, device="cuda")
+        cg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cg):
+            kda.kda_chunk_fwd(xc["q"], xc["k"], xc["v"], xc["log_alpha"], xc["beta"], xc["S0"], xc["cu_seqlens"],
+                              o=oc, S_final=Sc, workspace=wsc)
+        cg.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            cg.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us_graph = e0.elapsed_time(e1) / reps * 1e3
+        del cg
         cb = prefill_alg_bytes(Tc, w.H, w.D, Nc, True)
         return {"workload": label, "sequences": Nc, "tokens": Tc, "H": w.H, "d": w.D, "us_per_call": us,
                 "tokens_per_s": Tc / (us / 1e6), "bytes_per_call": cb, "hbm_gbs": cb / (us / 1e6) / 1e9,
-                "frac_hbm": cb / (us / 1e6) / 1e9 / HBM_PEAK_GBS}
+                "frac_hbm": cb / (us / 1e6) / 1e9 / HBM_PEAK_GBS,
+                "us_per_call_graph_replay": us_graph, "tokens_per_s_graph_replay": Tc / (us_graph / 1e6)}
 
     w5 = inputs.WORKLOADS[5]
     continuation = {
