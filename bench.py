@@ -643,7 +643,32 @@ def main():
                                         "(20 d^2 + 32 C d), each product as three bf16 MFMAs"},
         "workspace_bytes": wsb.numel(),
     }
-    del xb, gb, grads, wsb
+
+    # The fused layer's gradient on the same shape (kda_chunk_bwd_fused): raw q, k ~ 3 N(0,1),
+    # beta and decay logits, an output gate of N(0,1) logits; the maps' chain rule around the
+    # rule's gradient, with the ungated output recomputed for the gate's gradient.
+    gen = torch.Generator(device="cuda").manual_seed(1003)
+    rn = lambda *shape, s=1.0: (s * torch.randn(shape, device="cuda", generator=gen)).to(torch.bfloat16)
+    raw = {"q": rn(Bb, Tb, Hb, d, s=3.0), "k": rn(Bb, Tb, Hb, d, s=3.0), "la": rn(Bb, Tb, Hb, d),
+           "b": rn(Bb, Tb, Hb)}
+    gf = rn(Bb, Tb, Hb, d)
+    fgrads = dict(grads)
+    fgrads["dgate"] = torch.empty((Bb, Tb, Hb, d), dtype=torch.bfloat16, device="cuda")
+    wsf = torch.empty(kda.kda_chunk_bwd_fused_workspace_bytes(Bb, Tb, Hb, d, d, Bb, False, has_out_gate=True),
+                      dtype=torch.uint8, device="cuda")
+
+    def call_bwd_fused():
+        kda.kda_chunk_bwd_fused(raw["q"], raw["k"], xb["v"], raw["la"], raw["b"], gb["d_o"], None, None,
+                                gb["dS_final"], qk_l2norm=True, beta_logits=True, decay_logits=(6.0, 16.0),
+                                out_gate=gf, grads=fgrads, workspace=wsf, stream=stream)
+    tbf = timed_calls(torch, call_bwd_fused, stream, 3, args.steps)
+    backward["fused"] = {
+        "workload": "the same shape through kda_chunk_bwd_fused: q/k L2 norm, sigmoid beta, logsigmoid decay "
+                    "and an output gate (bf16 raw inputs and gradients)",
+        "ms_per_call_median": tbf["median"], "ms_per_call_min": tbf["min"],
+        "value": Bb * Tb / (tbf["median"] / 1e3), "unit": "tokens/s",
+        "vs_plain_call": tbf["median"] / bwd_ms, "workspace_bytes": wsf.numel()}
+    del xb, gb, grads, wsb, gf, raw, fgrads, wsf
     torch.cuda.empty_cache()
 
     # The long-context shape's backward (1 x 65,536 tokens, 32 heads): past the workspace limit

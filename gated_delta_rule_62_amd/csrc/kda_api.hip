@@ -6,6 +6,7 @@
 // synchronises.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -554,4 +555,165 @@ extern "C" kda_status gdn_chunk_bwd(const void* q, const void* k, const void* v,
     return chunk_bwd_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, dS_final, B, T, H, Dk, Dv, num_seqs,
                           chunk, in_dtype, grad_dtype, dq, dk, dv, dlog_alpha, dbeta, dS0, workspace,
                           workspace_bytes, stream, true);
+}
+
+// ---------------------------------------------------------------- gradient of the fused layer
+namespace {
+
+// Workspace of the fused gradient: a region shared by the rule's gradient and (with an output
+// gate) the forward pass that recomputes the ungated output, then fp32 planes for the mapped
+// inputs, the rule's gradients and the ungated output.
+struct FusedBwdLayout {
+    size_t core = 0;
+    size_t qh, kh, vf, la, bt, doc, rq, rk, dqh, dkh, dvf, dla, dbt, oc;
+    size_t bytes = 0;
+};
+
+FusedBwdLayout fused_bwd_layout(int B, int T, int H, int D, int N, bool varlen, bool gate, bool scalar_gate) {
+    FusedBwdLayout L;
+    auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+    L.core = kda::plan_backward(B, T, H, D, N, varlen).workspace_bytes;
+    if (gate) L.core = std::max(L.core, kda::plan_prefill(B, T, H, D, N, varlen, kda::kDefaultChunk).workspace_bytes);
+    const size_t rows = static_cast<size_t>(B) * T * H, nx = rows * D * 4, nb = rows * 4, ng = scalar_gate ? nb : nx;
+    size_t off = up(L.core);
+    auto take = [&](size_t n) { const size_t o = off; off = up(off + n); return o; };
+    L.qh = take(nx); L.kh = take(nx); L.vf = take(nx); L.la = take(ng); L.bt = take(nb); L.doc = take(nx);
+    L.rq = take(nb); L.rk = take(nb); L.dqh = take(nx); L.dkh = take(nx); L.dvf = take(nx); L.dla = take(ng);
+    L.dbt = take(nb); L.oc = gate ? take(nx) : 0;
+    L.bytes = off;
+    return L;
+}
+
+kda_status chunk_bwd_fused_impl(const void* q, const void* k, const void* v, const void* log_alpha, const void* beta,
+                                const float* S0, const int32_t* cu_seqlens, const void* d_o, const float* dS_final,
+                                int B, int T, int H, int Dk, int Dv, int num_seqs, int chunk, kda_dtype in_dtype,
+                                kda_dtype grad_dtype, void* dq, void* dk, void* dv, void* dlog_alpha, void* dbeta,
+                                float* dS0, void* dgate, void* workspace, size_t workspace_bytes,
+                                const kda_fusion* fusion, kda_stream_t stream, bool scalar_gate) {
+    if (B < 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || num_seqs < 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (!dtype_ok(in_dtype) || !dtype_ok(grad_dtype)) return KDA_ERR_UNSUPPORTED;
+    if (!head_ok(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
+    if (chunk != 0 && chunk != 32 && chunk != 64) return KDA_ERR_UNSUPPORTED;
+    if (!fusion_ok(fusion)) return KDA_ERR_INVALID_ARGUMENT;
+    if (cu_seqlens) {
+        if (B != 1 || !aligned16(cu_seqlens)) return KDA_ERR_INVALID_ARGUMENT;
+    } else if (num_seqs != B) {
+        return KDA_ERR_INVALID_ARGUMENT;
+    }
+    const void* gate = fusion ? fusion->out_gate : nullptr;
+    const size_t rows = static_cast<size_t>(B) * T * H;
+    const bool work = rows > 0 && num_seqs > 0;
+    if (work) {
+        const void* need[] = {q, k, v, log_alpha, beta, d_o, dq, dk, dv, dlog_alpha, dbeta};
+        for (const void* x : need)
+            if (!x || !aligned16(x)) return KDA_ERR_INVALID_ARGUMENT;
+        if (gate && (!dgate || !aligned16(dgate))) return KDA_ERR_INVALID_ARGUMENT;
+    }
+    if ((S0 && !aligned16(S0)) || (dS_final && !aligned16(dS_final)) || (dS0 && !aligned16(dS0)))
+        return KDA_ERR_INVALID_ARGUMENT;
+    const FusedBwdLayout L = fused_bwd_layout(B, T, H, Dk, num_seqs, cu_seqlens != nullptr, gate != nullptr, scalar_gate);
+    if (workspace_bytes < L.bytes) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    if (!workspace || !aligned16(workspace)) return KDA_ERR_INVALID_ARGUMENT;
+    // the gradients of the raw inputs are disjoint from the raw inputs, from each other and
+    // from the workspace
+    const size_t eg = elem_size(grad_dtype), ein = elem_size(in_dtype);
+    const size_t nx = rows * Dk, nb = rows, ng = scalar_gate ? nb : nx;
+    const size_t n_s = static_cast<size_t>(num_seqs) * H * Dk * Dv * sizeof(float);
+    const void* ins[7] = {q, k, v, log_alpha, beta, d_o, gate};
+    const size_t nin[7] = {nx * ein, nx * ein, nx * ein, ng * ein, nb * ein, nx * ein, gate ? nx * ein : 0};
+    void* outs[7] = {dq, dk, dv, dlog_alpha, dbeta, dgate, dS0};
+    const size_t nout[7] = {nx * eg, nx * eg, nx * eg, ng * eg, nb * eg, gate ? nx * eg : 0, dS0 ? n_s : 0};
+    for (int o = 0; o < 7; ++o) {
+        const size_t no = (o < 6 && !work) ? 0 : nout[o];
+        for (int i = 0; i < 7; ++i)
+            if (overlap(ins[i], work ? nin[i] : 0, outs[o], no)) return KDA_ERR_INVALID_ARGUMENT;
+        if (overlap(S0, n_s, outs[o], no) || overlap(dS_final, n_s, outs[o], no)) return KDA_ERR_INVALID_ARGUMENT;
+        for (int o2 = o + 1; o2 < 7; ++o2)
+            if (overlap(outs[o], no, outs[o2], (o2 < 6 && !work) ? 0 : nout[o2])) return KDA_ERR_INVALID_ARGUMENT;
+        if (overlap(workspace, L.bytes, outs[o], no)) return KDA_ERR_INVALID_ARGUMENT;
+    }
+    if (num_seqs == 0) return KDA_OK;
+    if (rows > 0x7fffffffu) return KDA_ERR_UNSUPPORTED;
+
+    char* w = static_cast<char*>(workspace);
+    kda::FusedBwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.d_o = d_o; a.gate = gate;
+    a.qh = reinterpret_cast<float*>(w + L.qh); a.kh = reinterpret_cast<float*>(w + L.kh);
+    a.vf = reinterpret_cast<float*>(w + L.vf); a.la = reinterpret_cast<float*>(w + L.la);
+    a.bt = reinterpret_cast<float*>(w + L.bt); a.doc = reinterpret_cast<float*>(w + L.doc);
+    a.rq = reinterpret_cast<float*>(w + L.rq); a.rk = reinterpret_cast<float*>(w + L.rk);
+    float* dqh = reinterpret_cast<float*>(w + L.dqh);
+    float* dkh = reinterpret_cast<float*>(w + L.dkh);
+    float* dvf = reinterpret_cast<float*>(w + L.dvf);
+    float* dla = reinterpret_cast<float*>(w + L.dla);
+    float* dbt = reinterpret_cast<float*>(w + L.dbt);
+    float* oc = gate ? reinterpret_cast<float*>(w + L.oc) : nullptr;
+    a.dqh = dqh; a.dkh = dkh; a.dvf = dvf; a.dla = dla; a.dbt = dbt; a.oc = oc;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dla_out = dlog_alpha; a.dbeta_out = dbeta; a.dgate = dgate;
+    a.rows = work ? rows : 0;
+    a.D = Dk;
+    a.flags = fusion ? fusion->flags : 0;
+    a.decay_bias = fusion ? fusion->decay_bias : 0.f;
+    a.decay_scale = fusion && (fusion->flags & KDA_FUSE_DECAY_LOGSIGMOID) ? fusion->decay_scale : 1.f;
+    a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = grad_dtype == KDA_BF16; a.scalar_gate = scalar_gate;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+
+    // 1. the maps: the rule's inputs in fp32
+    if (kda::launch_fused_bwd_pre(a, st) != hipSuccess) return KDA_ERR_HIP;
+    // 2. with a gate, the ungated output of the rule on those inputs
+    if (gate) {
+        const kda_status s = chunk_fwd_impl(a.qh, a.kh, a.vf, a.la, a.bt, S0, cu_seqlens, B, T, H, Dk, Dv, num_seqs,
+                                            kda::kDefaultChunk, KDA_F32, KDA_F32, oc, nullptr, workspace, L.core,
+                                            stream, scalar_gate);
+        if (s != KDA_OK) return s;
+    }
+    // 3. the rule's gradient on the mapped inputs (fp32 products), into the workspace
+    const kda_status s = chunk_bwd_impl(a.qh, a.kh, a.vf, a.la, a.bt, S0, cu_seqlens, a.doc, dS_final, B, T, H, Dk,
+                                        Dv, num_seqs, chunk, KDA_F32, KDA_F32, dqh, dkh, dvf, dla, dbt, dS0,
+                                        workspace, L.core, stream, scalar_gate);
+    if (s != KDA_OK) return s;
+    // 4. the chain rule back through the maps and the gate
+    return kda::launch_fused_bwd_post(a, st) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" size_t kda_chunk_bwd_fused_workspace_bytes(int B, int T, int H, int Dk, int Dv, int num_seqs,
+                                                      int has_cu_seqlens, int chunk, int has_out_gate) {
+    if (B < 0 || T < 0 || H <= 0 || num_seqs < 0 || !head_ok(Dk, Dv)) return 0;
+    if (chunk != 0 && chunk != 32 && chunk != 64) return 0;
+    return fused_bwd_layout(B, T, H, Dk, num_seqs, has_cu_seqlens != 0, has_out_gate != 0, false).bytes;
+}
+
+extern "C" size_t gdn_chunk_bwd_fused_workspace_bytes(int B, int T, int H, int Dk, int Dv, int num_seqs,
+                                                      int has_cu_seqlens, int chunk, int has_out_gate) {
+    if (B < 0 || T < 0 || H <= 0 || num_seqs < 0 || !head_ok(Dk, Dv)) return 0;
+    if (chunk != 0 && chunk != 32 && chunk != 64) return 0;
+    return fused_bwd_layout(B, T, H, Dk, num_seqs, has_cu_seqlens != 0, has_out_gate != 0, true).bytes;
+}
+
+extern "C" kda_status kda_chunk_bwd_fused(const void* q, const void* k, const void* v, const void* log_alpha,
+                                          const void* beta, const float* S0, const int32_t* cu_seqlens,
+                                          const void* d_o, const float* dS_final,
+                                          int B, int T, int H, int Dk, int Dv, int num_seqs, int chunk,
+                                          kda_dtype in_dtype, kda_dtype grad_dtype,
+                                          void* dq, void* dk, void* dv, void* dlog_alpha, void* dbeta, float* dS0,
+                                          void* dgate, void* workspace, size_t workspace_bytes,
+                                          const kda_fusion* fusion, kda_stream_t stream) {
+    return chunk_bwd_fused_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, dS_final, B, T, H, Dk, Dv,
+                                num_seqs, chunk, in_dtype, grad_dtype, dq, dk, dv, dlog_alpha, dbeta, dS0, dgate,
+                                workspace, workspace_bytes, fusion, stream, false);
+}
+
+extern "C" kda_status gdn_chunk_bwd_fused(const void* q, const void* k, const void* v, const void* log_alpha,
+                                          const void* beta, const float* S0, const int32_t* cu_seqlens,
+                                          const void* d_o, const float* dS_final,
+                                          int B, int T, int H, int Dk, int Dv, int num_seqs, int chunk,
+                                          kda_dtype in_dtype, kda_dtype grad_dtype,
+                                          void* dq, void* dk, void* dv, void* dlog_alpha, void* dbeta, float* dS0,
+                                          void* dgate, void* workspace, size_t workspace_bytes,
+                                          const kda_fusion* fusion, kda_stream_t stream) {
+    return chunk_bwd_fused_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, d_o, dS_final, B, T, H, Dk, Dv,
+                                num_seqs, chunk, in_dtype, grad_dtype, dq, dk, dv, dlog_alpha, dbeta, dS0, dgate,
+                                workspace, workspace_bytes, fusion, stream, true);
 }

@@ -90,6 +90,23 @@ hipError_t launch_decode(int D, bool in_bf16, bool out_bf16, const void* q, cons
                          float* S_out, void* o, int units, hipStream_t stream, bool scalar_gate,
                          const Fusion* fusion = nullptr);
 
+// The elementwise steps of the fused layer's gradient (kda_fused_bwd.hip): rows = tokens x
+// heads of D (= Dk = Dv) values.  Raw inputs in dtype; the mapped inputs, the rule's fp32
+// gradients and the ungated output in the workspace; the raw inputs' gradients out.
+struct FusedBwdArgs {
+    const void *q, *k, *v, *log_alpha, *beta, *d_o, *gate;    // raw inputs (gate may be null)
+    float *qh, *kh, *vf, *la, *bt, *doc, *rq, *rk;            // pre: mapped inputs, 1/|q|, 1/|k|
+    const float *dqh, *dkh, *dvf, *dla, *dbt, *oc;            // the rule's gradients, ungated o
+    void *dq, *dk, *dv, *dla_out, *dbeta_out, *dgate;         // gradients of the raw inputs
+    size_t rows = 0;
+    int D = 128;
+    int flags = 0;
+    float decay_bias = 0.f, decay_scale = 1.f;
+    bool in_bf16 = false, out_bf16 = false, scalar_gate = false;
+};
+hipError_t launch_fused_bwd_pre(const FusedBwdArgs& a, hipStream_t stream);
+hipError_t launch_fused_bwd_post(const FusedBwdArgs& a, hipStream_t stream);
+
 hipError_t launch_recurrent_fwd(int D, bool in_bf16, bool out_bf16, const void* q, const void* k,
                                 const void* v, const void* g, const void* b, const float* S0,
                                 const int32_t* cu, int T, int H, int units, void* o, float* S_final,

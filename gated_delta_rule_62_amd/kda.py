@@ -25,7 +25,9 @@ EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd
             "kda_recurrent_fwd", "gdn_chunk_fwd", "gdn_recurrent_step", "gdn_recurrent_fwd",
             "kda_chunk_fwd_fused", "kda_recurrent_step_fused", "kda_chunk_bwd_workspace_bytes",
             "kda_chunk_bwd", "gdn_chunk_bwd", "kda_chunk_fwd_noalloc", "gdn_chunk_fwd_fused",
-            "gdn_recurrent_step_fused", "kda_recurrent_fwd_fused", "gdn_recurrent_fwd_fused")
+            "gdn_recurrent_step_fused", "kda_recurrent_fwd_fused", "gdn_recurrent_fwd_fused",
+            "kda_chunk_bwd_fused_workspace_bytes", "kda_chunk_bwd_fused", "gdn_chunk_bwd_fused_workspace_bytes",
+            "gdn_chunk_bwd_fused")
 KDA_FUSE_QK_L2NORM, KDA_FUSE_BETA_SIGMOID, KDA_FUSE_DECAY_LOGSIGMOID = 1, 2, 4
 
 
@@ -82,6 +84,11 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_bwd.restype = i32
     lib.gdn_chunk_bwd.argtypes = lib.kda_chunk_bwd.argtypes
     lib.gdn_chunk_bwd.restype = i32
+    for pre in ("kda", "gdn"):
+        getattr(lib, f"{pre}_chunk_bwd_fused_workspace_bytes").argtypes = [i32] * 9
+        getattr(lib, f"{pre}_chunk_bwd_fused_workspace_bytes").restype = sz
+        getattr(lib, f"{pre}_chunk_bwd_fused").argtypes = [vp] * 9 + [i32] * 7 + [i32, i32] + [vp] * 7 + [vp, sz, fp, vp]
+        getattr(lib, f"{pre}_chunk_bwd_fused").restype = i32
     for pre in ("kda", "gdn"):
         getattr(lib, f"{pre}_chunk_fwd").argtypes = lib.kda_chunk_fwd.argtypes
         getattr(lib, f"{pre}_chunk_fwd").restype = i32
@@ -400,3 +407,65 @@ def kda_chunk_bwd(q, k, v, log_alpha, beta, d_o, S0=None, cu_seqlens=None, dS_fi
 def gdn_chunk_bwd(q, k, v, log_alpha, beta, d_o, S0=None, cu_seqlens=None, dS_final=None, **kw):
     """Gradient of gdn_chunk_fwd: log_alpha and the returned dlog_alpha are [B, T, H]."""
     return kda_chunk_bwd(q, k, v, log_alpha, beta, d_o, S0, cu_seqlens, dS_final, _fn="gdn_chunk_bwd", **kw)
+
+
+def kda_chunk_bwd_fused_workspace_bytes(B, T, H, Dk, Dv, num_seqs, has_cu_seqlens, chunk=CHUNK, has_out_gate=False,
+                                        scalar_gate=False) -> int:
+    fn = "gdn_chunk_bwd_fused_workspace_bytes" if scalar_gate else "kda_chunk_bwd_fused_workspace_bytes"
+    return int(getattr(load_library(), fn)(B, T, H, Dk, Dv, num_seqs, int(has_cu_seqlens), chunk, int(has_out_gate)))
+
+
+def kda_chunk_bwd_fused(q, k, v, log_alpha, beta, d_o, S0=None, cu_seqlens=None, dS_final=None, *,
+                        qk_l2norm=False, beta_logits=False, decay_logits=None, out_gate=None,
+                        grad_dtype=torch.float32, grads=None, want_dS0=True, workspace=None, chunk=CHUNK,
+                        stream=None, _fn="kda_chunk_bwd_fused"):
+    """Gradient of kda_chunk_fwd_fused with respect to its raw inputs (the maps and the gate
+    as in kda_chunk_fwd_fused; d_o is the gradient of the gated output).  Returns a dict dq,
+    dk, dv, dlog_alpha, dbeta, dgate (grad_dtype; dgate None without a gate) and dS0."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if d_o.dtype != q.dtype or (out_gate is not None and out_gate.dtype != q.dtype):
+        raise TypeError("d_o and out_gate must have the inputs' dtype")
+    g = dict(grads or {})
+    dev = q.device
+    own = []
+    shapes = [("dq", q.shape), ("dk", q.shape), ("dv", v.shape), ("dlog_alpha", log_alpha.shape), ("dbeta", beta.shape)]
+    if out_gate is not None:
+        shapes.append(("dgate", out_gate.shape))
+    for name, shape in shapes:
+        if g.get(name) is None:
+            g[name] = torch.empty(shape, dtype=grad_dtype, device=dev)
+            own.append(g[name])
+    if out_gate is None:
+        g["dgate"] = None
+    if g.get("dS0") is None and want_dS0:
+        g["dS0"] = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev)
+        own.append(g["dS0"])
+    _check_dev(q, k, v, log_alpha, beta, d_o, S0, cu_seqlens, dS_final, workspace, out_gate,
+               *[t for t in g.values() if t is not None])
+    sg = _fn.startswith("gdn")
+    ws_need = kda_chunk_bwd_fused_workspace_bytes(B, T, H, Dk, Dv, N, cu_seqlens is not None, chunk,
+                                                  out_gate is not None, sg)
+    if workspace is None:
+        workspace = torch.empty(max(ws_need, 256), dtype=torch.uint8, device=dev)
+        own.append(workspace)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    fz = _fusion(qk_l2norm, beta_logits, decay_logits, out_gate)
+    st = getattr(load_library(), _fn)(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(cu_seqlens),
+        _ptr(d_o), _ptr(dS_final), B, T, H, Dk, Dv, N, chunk, _dtype_code(q.dtype), _dtype_code(g["dq"].dtype),
+        _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dlog_alpha"]), _ptr(g["dbeta"]), _ptr(g.get("dS0")),
+        _ptr(g["dgate"]), _ptr(workspace), ws_bytes, ctypes.byref(fz), _stream_ptr(stream))
+    if st != KDA_OK:
+        raise KDAError(st, _fn)
+    _keep_for(stream, *own)
+    return g
+
+
+def gdn_chunk_bwd_fused(q, k, v, log_alpha, beta, d_o, S0=None, cu_seqlens=None, dS_final=None, **kw):
+    """Gradient of gdn_chunk_fwd_fused: log_alpha (decay logits) and dlog_alpha are [B, T, H]."""
+    return kda_chunk_bwd_fused(q, k, v, log_alpha, beta, d_o, S0, cu_seqlens, dS_final, _fn="gdn_chunk_bwd_fused",
+                               **kw)

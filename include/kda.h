@@ -376,6 +376,58 @@ kda_status gdn_chunk_bwd(const void* q, const void* k, const void* v, const void
                          void* dq, void* dk, void* dv, void* dlog_alpha, void* dbeta, float* dS0,
                          void* workspace, size_t workspace_bytes, kda_stream_t stream);
 
+/*
+ * kda_chunk_bwd_fused -- gradient of kda_chunk_fwd_fused: the fused layer's output
+ * o = rule(maps(q, k, beta, log_alpha), v, S0) * sigmoid(gate) (the gate when
+ * fusion->out_gate is set) and its final states, differentiated with respect to the raw
+ * inputs.  The maps are those of kda_fusion (L2 norm of q and k, sigmoid of beta logits,
+ * logsigmoid(a + decay_bias) / decay_scale of decay logits); the rule is the gated delta
+ * rule of "Decoding Hybrid Attention Architectures" section 3.4.  The chain rule runs
+ * through each map ("Decoding Hybrid Attention Architectures" section 3.2 takes the keys as
+ * normalised; the maps themselves are this library's reading):
+ *   x' = x / sqrt(sum x^2 + 1e-12):  dx = (dx' - x' (x' . dx')) / sqrt(sum x^2 + 1e-12)
+ *   beta = sigmoid(b):               db = dbeta beta (1 - beta)
+ *   log_alpha = logsigmoid(a + c)/s: da = dlog_alpha (1 - sigmoid(a + c)) / s
+ *   o * sigmoid(g):                  d(o) = d_o sigmoid(g), dg = d_o o sigmoid(g)(1 - sigmoid(g))
+ * Arguments as for kda_chunk_bwd, with d_o the gradient of the gated output, plus
+ *   dgate      : [B, T, H, Dv] grad_dtype, the gradient of the gate logits (required when
+ *                fusion->out_gate is set, else ignored)
+ *   fusion     : the same kda_fusion as the forward call (NULL = the plain gradient)
+ *   workspace  : kda_chunk_bwd_fused_workspace_bytes() bytes (has_out_gate 0 or 1): the
+ *                rule's gradient workspace, then fp32 copies of the mapped inputs, of the
+ *                rule's gradients and, with a gate, of the ungated output.
+ * The rule's gradient runs on the mapped inputs in fp32 (fp32 matrix-core products); with a
+ * gate, one forward pass first recomputes the ungated output.  dlog_alpha and dbeta hold the
+ * gradients of the decay and beta logits under those flags.  Errors as for kda_chunk_bwd.
+ */
+size_t kda_chunk_bwd_fused_workspace_bytes(int B, int T, int H, int Dk, int Dv, int num_seqs,
+                                           int has_cu_seqlens, int chunk, int has_out_gate);
+
+kda_status kda_chunk_bwd_fused(const void* q, const void* k, const void* v, const void* log_alpha,
+                               const void* beta, const float* S0, const int32_t* cu_seqlens,
+                               const void* d_o, const float* dS_final,
+                               int B, int T, int H, int Dk, int Dv, int num_seqs, int chunk,
+                               kda_dtype in_dtype, kda_dtype grad_dtype,
+                               void* dq, void* dk, void* dv, void* dlog_alpha, void* dbeta, float* dS0,
+                               void* dgate, void* workspace, size_t workspace_bytes,
+                               const kda_fusion* fusion, kda_stream_t stream);
+
+/*
+ * gdn_chunk_bwd_fused -- the same for the scalar gate (gdn_chunk_fwd_fused): log_alpha and
+ * dlog_alpha [B, T, H], the decay map applied to the one logit per token and head.
+ */
+size_t gdn_chunk_bwd_fused_workspace_bytes(int B, int T, int H, int Dk, int Dv, int num_seqs,
+                                           int has_cu_seqlens, int chunk, int has_out_gate);
+
+kda_status gdn_chunk_bwd_fused(const void* q, const void* k, const void* v, const void* log_alpha,
+                               const void* beta, const float* S0, const int32_t* cu_seqlens,
+                               const void* d_o, const float* dS_final,
+                               int B, int T, int H, int Dk, int Dv, int num_seqs, int chunk,
+                               kda_dtype in_dtype, kda_dtype grad_dtype,
+                               void* dq, void* dk, void* dv, void* dlog_alpha, void* dbeta, float* dS0,
+                               void* dgate, void* workspace, size_t workspace_bytes,
+                               const kda_fusion* fusion, kda_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
