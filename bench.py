@@ -127,9 +127,9 @@ def counted_workload(key: str):
             "valu_busy": rec["valu_busy"], "kernels": rec["kernels"]}
 
 
-# floats per (chunk, head) record of the backward at d = 128: Q', K', K'', the decay exponents
-# (32 x 128 each), M, P, L (32 x 32 each), e_m, e_n (128 each), beta (32)
-Rec128 = 4 * 32 * 128 + 3 * 32 * 32 + 2 * 128 + 32
+# floats per (chunk, head) record of the backward at d = 128: M, P, L (32 x 32 each), e_m, e_n
+# (128 each), beta (32), the decay exponents (32 x 128)
+Rec128 = 3 * 32 * 32 + 2 * 128 + 32 + 32 * 128
 
 
 def timed_calls(torch, fn, stream, warmup: int, n: int) -> dict:

@@ -29,7 +29,8 @@
 // the state passes also keep R = V - K' S_m and dE of every chunk, which the gradient step
 // reads instead of recomputing):
 //   seq_scan_kernel   packed batches: first chunk index of every sequence
-//   prep_kernel       per (chunk, head): Q', K', K'', M, P, L, e_m, e_n, beta, b - m -> record
+//   prep_kernel       per (chunk, head): M, P, L, e_m, e_n, beta, b - m -> record (Q', K', K''
+//                     are rebuilt from q, k and b - m where they are read)
 //   state_fwd_kernel  per (sequence, head, 32 value columns): every chunk's entry state
 //                     and the final state, chunks in order
 //   state_rev_kernel  same split: every chunk's dS_next, chunks in reverse order; dS0
@@ -58,12 +59,14 @@ constexpr int GW = 32;    // value columns per step of the gradient kernel
 using f4 = __attribute__((__vector_size__(4 * sizeof(float)))) float;
 
 // Offsets (in floats) inside the per-(chunk, head) record written by prep_kernel.
+// The decayed keys and queries Q' = Q e^{X}, K' = K e^{X}, K'' = K e^{-X} (X = b - m) are not
+// kept: every reader rebuilds them from q, k and X with the same fp32 operations (rebuild_qk),
+// which reproduces them bit for bit and keeps the record at 29 KB (d = 128) instead of 77 KB.
 template <int D>
 struct Rec {
-    static constexpr int QP = 0, KP = BC * D, KPP = 2 * BC * D, M = 3 * BC * D, P = M + BC * BC,
-                         L = P + BC * BC, EM = L + BC * BC, EN = EM + D, BETA = EN + D, X = BETA + BC,
-                         SIZE = X + BC * D;
-    static_assert(SIZE % 4 == 0, "records must stay 16-byte aligned");
+    static constexpr int M = 0, P = M + BC * BC, L = P + BC * BC, EM = L + BC * BC, EN = EM + D, BETA = EN + D,
+                         X = BETA + BC, SIZE = X + BC * D;
+    static_assert(SIZE % 4 == 0 && X % 4 == 0, "records must stay 16-byte aligned");
 };
 
 template <class IN>
@@ -332,6 +335,37 @@ struct StageRows {
     }
 };
 
+// Four consecutive values of one row of a [tokens, H, D] input in the input's own type (8 bytes of
+// bf16 or 16 of fp32), and their fp32 widening.
+template <class IN>
+struct In4 {
+    static constexpr bool B16 = std::is_same<IN, BF16>::value;
+    using word = typename std::conditional<B16, v2u, v4f>::type;
+    __device__ __forceinline__ static word load(const void* p, size_t idx) {
+        return *reinterpret_cast<const word*>(static_cast<const typename IN::storage*>(p) + idx);
+    }
+    __device__ __forceinline__ static v4f widen(const word& v) {
+        if constexpr (B16) {
+            return v4f{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                       __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
+        } else {
+            return v;
+        }
+    }
+};
+
+// The decayed operands of four elements of one row, from the input x (q or k) and the decay
+// exponents X = b - m: up = x e^{X} (Q' or K') and dn = x e^{-X} (K''), the same fp32 operations
+// as prep_kernel; rows past the chunk's end (ok false) are zero.
+__device__ __forceinline__ void decay4(v4f x, v4f X, bool ok, v4f& up, v4f& dn) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float u = fast_exp(X[j]), d = fast_exp(-X[j]);
+        up[j] = ok ? x[j] * u : 0.f;
+        dn[j] = ok ? x[j] * d : 0.f;
+    }
+}
+
 // Maps a linear workgroup index to (unit, column tile) so that the tiles of one unit
 // land on one XCD (workgroups are dealt to the 8 XCDs round-robin) and share its L2.
 __device__ __forceinline__ void unit_tile(int b, int nwg, int ntile, int& unit, int& tile) {
@@ -458,9 +492,6 @@ __global__ __launch_bounds__(BT) void prep_kernel(BackwardArgs a) {
 #pragma unroll
         for (int r = 0; r < BC; ++r) rec[Rec<D>::M + r * BC + tid] = col[r];
     }
-    s2g<BC, D>(rec + Rec<D>::QP, D, sQ, LD);
-    s2g<BC, D>(rec + Rec<D>::KP, D, sK, LD);
-    s2g<BC, D>(rec + Rec<D>::KPP, D, sKpp, LD);
     s2g<BC, BC>(rec + Rec<D>::P, BC, sP, LC);
     s2g<BC, BC>(rec + Rec<D>::L, BC, sL, LC);
     s2g<BC, D>(rec + Rec<D>::X, D, sG, LD);
@@ -608,12 +639,14 @@ struct FwdSlot {
     static_assert(SIZE % 4 == 0, "");
 };
 
-// The loading waves' registers for one chunk: K' and K'' rows, M, e_m / e_n / beta, and V.
+// The loading waves' registers for one chunk: K rows and the decay exponents X of the same
+// elements (K' and K'' are formed from them on the way to LDS), M, e_m / e_n / beta, and V.
 template <int D, class IN>
 struct FwdLoad {
-    static constexpr int NK = BC * D / 4 / SLT;   // 16-byte words of K' (and K'') per thread
+    static constexpr int NK = BC * D / 4 / SLT;   // groups of 4 elements of K' (and K'') per thread
     static_assert(BC * D / 4 % SLT == 0 && BC * BC / 4 == SLT && 2 * D / 4 + BC / 4 <= SLT, "");
-    v4f kp[NK], kpp[NK], m, small;
+    typename In4<IN>::word k[NK];
+    v4f x[NK], m, small;
     typename Raw8<IN>::word v;
 };
 
@@ -658,11 +691,12 @@ __global__ __launch_bounds__(STH) void state_fwd_kernel(BackwardArgs a) {
         auto load = [&](LDS_& x, int i) __attribute__((always_inline)) {
             i = min(i, i1 - 1);   // past the end: the last chunk again (never used)
             const float* rec = a.prep + cslot(a, c0 + i, h) * Rec<D>::SIZE;
+            const int len = min(BC, L - i * BC);
 #pragma unroll
             for (int k = 0; k < LDS_::NK; ++k) {
-                const int e = lt + k * SLT;
-                x.kp[k] = *reinterpret_cast<const v4f*>(rec + Rec<D>::KP + 4 * e);
-                x.kpp[k] = *reinterpret_cast<const v4f*>(rec + Rec<D>::KPP + 4 * e);
+                const int e = lt + k * SLT, r = min(e / (D / 4), len - 1), c = 4 * (e % (D / 4));
+                x.k[k] = In4<IN>::load(a.k, ((size_t)(tok0 + i * BC + r) * a.H + h) * D + c);
+                x.x[k] = *reinterpret_cast<const v4f*>(rec + Rec<D>::X + 4 * e);
             }
             x.m = *reinterpret_cast<const v4f*>(rec + Rec<D>::M + 4 * lt);
             // e_m, e_n and beta are contiguous in the record: D + D + C floats
@@ -672,15 +706,18 @@ __global__ __launch_bounds__(STH) void state_fwd_kernel(BackwardArgs a) {
         };
         auto put = [&](const LDS_& x, int i) __attribute__((always_inline)) {
             float* sl = sSlot + (i & 1) * SL::SIZE;
+            const int len = min(BC, L - min(i, i1 - 1) * BC);
 #pragma unroll
             for (int k = 0; k < LDS_::NK; ++k) {
                 const int e = lt + k * SLT, r = e / (D / 4), c = 4 * (e % (D / 4));
-                *reinterpret_cast<v4f*>(sl + SL::KP + r * SL::LK + c) = x.kp[k];
-                *reinterpret_cast<v4f*>(sl + SL::KPP + r * SL::LK + c) = x.kpp[k];
+                v4f kp, kpp;
+                decay4(In4<IN>::widen(x.k[k]), x.x[k], r < len, kp, kpp);
+                *reinterpret_cast<v4f*>(sl + SL::KP + r * SL::LK + c) = kp;
+                *reinterpret_cast<v4f*>(sl + SL::KPP + r * SL::LK + c) = kpp;
             }
             *reinterpret_cast<v4f*>(sl + SL::M + (lt / (BC / 4)) * SL::LM + 4 * (lt % (BC / 4))) = x.m;
             if (lt < (2 * D + BC) / 4) *reinterpret_cast<v4f*>(sl + SL::EM + 4 * lt) = x.small;
-            put_rows_t<IN>(x.v, sl + SL::VT, SL::LV, lt, min(BC, L - min(i, i1 - 1) * BC));
+            put_rows_t<IN>(x.v, sl + SL::VT, SL::LV, lt, len);
         };
         LDS_ xa, xb;
         // chunk i0 into its slot now; i0 + 1 and i0 + 2 into registers
@@ -827,7 +864,8 @@ template <int D, class IN>
 struct RevLoad {
     static constexpr int NK = BC * D / 4 / SLT;
     static_assert(BC * D / 4 % SLT == 0 && BC * BC / 4 == SLT && 2 * D / 4 + BC / 4 <= SLT, "");
-    v4f qp[NK], kp[NK], kpp[NK], m, p, small;
+    typename In4<IN>::word q[NK], k[NK];   // Q, K rows; Q', K', K'' are formed on the way to LDS
+    v4f x[NK], m, p, small;                 // the decay exponents X of the same elements, M, P, ...
     typename Raw8<IN>::word o;
 };
 
@@ -871,12 +909,14 @@ __global__ __launch_bounds__(STH) void state_rev_kernel(BackwardArgs a) {
         auto load = [&](LDS_& x, int i) __attribute__((always_inline)) {
             i = max(i, i0);   // before the start: the first chunk again (never used)
             const float* rec = a.prep + cslot(a, c0 + i, h) * Rec<D>::SIZE;
+            const int len = min(BC, L - i * BC);
 #pragma unroll
             for (int k = 0; k < LDS_::NK; ++k) {
-                const int e = lt + k * SLT;
-                x.qp[k] = *reinterpret_cast<const v4f*>(rec + Rec<D>::QP + 4 * e);
-                x.kp[k] = *reinterpret_cast<const v4f*>(rec + Rec<D>::KP + 4 * e);
-                x.kpp[k] = *reinterpret_cast<const v4f*>(rec + Rec<D>::KPP + 4 * e);
+                const int e = lt + k * SLT, r = min(e / (D / 4), len - 1), c = 4 * (e % (D / 4));
+                const size_t idx = ((size_t)(tok0 + i * BC + r) * a.H + h) * D + c;
+                x.q[k] = In4<IN>::load(a.q, idx);
+                x.k[k] = In4<IN>::load(a.k, idx);
+                x.x[k] = *reinterpret_cast<const v4f*>(rec + Rec<D>::X + 4 * e);
             }
             x.m = *reinterpret_cast<const v4f*>(rec + Rec<D>::M + 4 * lt);
             x.p = *reinterpret_cast<const v4f*>(rec + Rec<D>::P + 4 * lt);
@@ -885,18 +925,22 @@ __global__ __launch_bounds__(STH) void state_rev_kernel(BackwardArgs a) {
         };
         auto put = [&](const LDS_& x, int i) __attribute__((always_inline)) {
             float* sl = sSlot + (i & 1) * SL::SIZE;
+            const int len = min(BC, L - max(i, i0) * BC);
 #pragma unroll
             for (int k = 0; k < LDS_::NK; ++k) {
                 const int e = lt + k * SLT, r = e / (D / 4), c = 4 * (e % (D / 4));
-                *reinterpret_cast<v4f*>(sl + SL::QP + r * SL::LK + c) = x.qp[k];
-                *reinterpret_cast<v4f*>(sl + SL::KP + r * SL::LK + c) = x.kp[k];
-                *reinterpret_cast<v4f*>(sl + SL::KPP + r * SL::LK + c) = x.kpp[k];
+                v4f qp, kp, kpp, unused;
+                decay4(In4<IN>::widen(x.q[k]), x.x[k], r < len, qp, unused);
+                decay4(In4<IN>::widen(x.k[k]), x.x[k], r < len, kp, kpp);
+                *reinterpret_cast<v4f*>(sl + SL::QP + r * SL::LK + c) = qp;
+                *reinterpret_cast<v4f*>(sl + SL::KP + r * SL::LK + c) = kp;
+                *reinterpret_cast<v4f*>(sl + SL::KPP + r * SL::LK + c) = kpp;
             }
             const int mr = lt / (BC / 4), mc = 4 * (lt % (BC / 4));
             *reinterpret_cast<v4f*>(sl + SL::M + mr * SL::LM + mc) = x.m;
             *reinterpret_cast<v4f*>(sl + SL::P + mr * SL::LM + mc) = x.p;
             if (lt < (2 * D + BC) / 4) *reinterpret_cast<v4f*>(sl + SL::EM + 4 * lt) = x.small;
-            put_rows_t<IN>(x.o, sl + SL::OT, SL::LV, lt, min(BC, L - max(i, i0) * BC));
+            put_rows_t<IN>(x.o, sl + SL::OT, SL::LV, lt, len);
         };
         LDS_ xa, xb;
         // chunk i1 - 1 into its slot now; i1 - 2 and i1 - 3 into registers
@@ -1074,22 +1118,32 @@ __global__ __launch_bounds__(grad_threads<D>()) void grad_kernel(BackwardArgs a)
         rdE.load(dEg + ct * GW, D);
         rO.load(a.dO, p.t0, p.len, a.H, h, D, ct * GW);
     };
-    Stage<BC, D, GT> rX;   // decay exponents b - m, used after the column loop
+    Stage<BC, D, GT> rX;   // decay exponents X = b - m: Q', K', K'' now, the decay factors at the end
     {
-        Stage<BC, D, GT> r1, r2, r3;
+        using SR = StageRows<IN, D, GT>;
+        SR rq, rk;
         Stage<BC, BC, GT> r4, r6;
-        r1.load(rec + Rec<D>::QP, D);
-        r2.load(rec + Rec<D>::KP, D);
-        r3.load(rec + Rec<D>::KPP, D);
+        rq.load(a.q, p.t0, p.len, a.H, h, D, 0);
+        rk.load(a.k, p.t0, p.len, a.H, h, D, 0);
+        rX.load(rec + Rec<D>::X, D);
         r4.load(rec + Rec<D>::M, BC);
         r6.load(rec + Rec<D>::L, BC);
         const float em = rec[Rec<D>::EM + (tid & (D - 1))], en = rec[Rec<D>::EN + (tid & (D - 1))];
         const float bt = rec[Rec<D>::BETA + (tid & (BC - 1))];
         fetch(0);
-        rX.load(rec + Rec<D>::X, D);
-        r1.store(sQp, LD);
-        r2.store(sKp, LD);
-        r3.store(sKpp, LD);
+        static_assert(SR::IT == Stage<BC, D, GT>::IT && SR::C4 == Stage<BC, D, GT>::C4, "");
+#pragma unroll
+        for (int it = 0; it < SR::IT; ++it) {   // Q' = Q e^X, K' = K e^X, K'' = K e^-X
+            const int e = tid + it * GT, r = e / SR::C4, c = 4 * (e % SR::C4);
+            if (SR::live(e)) {
+                v4f qp, kp, kpp, unused;
+                decay4(SR::widen(rq.x[it]), rX.x[it], r < p.len, qp, unused);
+                decay4(SR::widen(rk.x[it]), rX.x[it], r < p.len, kp, kpp);
+                *reinterpret_cast<v4f*>(sQp + r * LD + c) = qp;
+                *reinterpret_cast<v4f*>(sKp + r * LD + c) = kp;
+                *reinterpret_cast<v4f*>(sKpp + r * LD + c) = kpp;
+            }
+        }
         r4.store(sM, LC);
         r6.store(sL, LC);
         if (tid < D) {

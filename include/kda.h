@@ -342,7 +342,7 @@ kda_status gdn_recurrent_fwd_fused(const void* q, const void* k, const void* v, 
  *   workspace       : device scratch of kda_chunk_bwd_workspace_bytes() bytes; per
  *                     chunk and head (of all chunks, or of one window) it holds the
  *                     chunk's record, entry state and state gradient in fp32, about
- *                     (2 Dk Dv + 6 C Dk + 3 C^2) * 4 bytes with C = 32
+ *                     (2 Dk Dv + 3 C Dk + 3 C^2) * 4 bytes with C = 32
  *
  * Supported: Dk == Dv in {64, 128}; in_dtype, grad_dtype in {KDA_F32, KDA_BF16}
  * (bf16 gradients are the round-to-nearest-even bf16 of the fp32 result).  All

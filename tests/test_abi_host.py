@@ -204,13 +204,13 @@ def test_fused_argument_errors(lib):
 def test_backward_workspace_query(lib):
     q = kda.kda_chunk_bwd_workspace_bytes
     up = lambda x: (x + 255) // 256 * 256
-    rec = 4 * 32 * 128 + 3 * 32 * 32 + 2 * 128 + 32          # floats per (chunk, head) record
+    rec = 3 * 32 * 32 + 2 * 128 + 32 + 32 * 128               # floats per (chunk, head) record
     nc, H, D = 4 * 128, 16, 128                                # 4 sequences of 4096 tokens
     want = up(4 * nc * H * rec) + up(4 * (nc + 4) * H * D * D) + up(4 * nc * H * D * D) + 2 * up(4 * nc * H * 32 * D)
     assert q(4, 4096, 16, 128, 128, 4, False) == want
     # packed: a chunk-start table and room for ceil(T / 32) + N chunks
     nc = 1000 // 32 + 1 + 3
-    want = up(4 * 4) + up(4 * nc * 2 * (4 * 32 * 64 + 3 * 32 * 32 + 2 * 64 + 32)) + \
+    want = up(4 * 4) + up(4 * nc * 2 * (3 * 32 * 32 + 2 * 64 + 32 + 32 * 64)) + \
         up(4 * (nc + 3) * 2 * 64 * 64) + up(4 * nc * 2 * 64 * 64) + 2 * up(4 * nc * 2 * 32 * 64)
     assert q(1, 1000, 2, 64, 64, 3, True) == want
     assert q(1, 64, 2, 96, 96, 1, False) == 0
@@ -224,28 +224,28 @@ def test_backward_windowed_workspace(lib, monkeypatch):
     window and the carried state gradient."""
     q = kda.kda_chunk_bwd_workspace_bytes
     up = lambda x: (x + 255) // 256 * 256
-    rec = 4 * 32 * 128 + 3 * 32 * 32 + 2 * 128 + 32
+    rec = 3 * 32 * 32 + 2 * 128 + 32 + 32 * 128
     per_chunk = 4 * (rec + 2 * 128 * 128 + 2 * 32 * 128)
     st = 4 * 128 * 128
 
     def windowed(units, W, n_win):
         return (up(4 * units * W * rec) + up(st * units * (W + 1)) + up(st * units * W) +
                 2 * up(4 * units * W * 32 * 128) + up(st * units * (n_win - 1)) + up(st * units))
-    # training shape: 1.99 GB, under the limit: one pass, unchanged
+    # training shape: 1.59 GB, under the limit: one pass, unchanged
     assert q(4, 4096, 16, 128, 128, 4, False) == up(4 * 512 * 16 * rec) + up(st * 516 * 16) + \
         up(st * 512 * 16) + 2 * up(4 * 512 * 16 * 32 * 128)
-    # long context (2048 chunks, 32 heads): 8 windows of 256 chunks, 2.01 GB instead of 15.9 GB
+    # long context (2048 chunks, 32 heads): 6 windows of 342 chunks, 2.13 GB instead of 12.7 GB
     lc = q(1, 65536, 32, 128, 128, 1, False)
-    assert lc == windowed(32, 256, 8) and lc <= 2 << 30
-    assert 2048 * 32 * per_chunk > 15.9e9
-    # a smaller limit (the environment override) gives smaller windows: 29 windows of 71 chunks
+    assert lc == windowed(32, 342, 6) and lc <= 2 << 30
+    assert 2048 * 32 * per_chunk > 12.6e9
+    # a smaller limit (the environment override) gives smaller windows: 23 windows of 90 chunks
     monkeypatch.setenv("KDA_BWD_WORKSPACE_LIMIT", str(600 << 20))
-    assert q(1, 65536, 32, 128, 128, 1, False) == windowed(32, 71, 29) <= 600 << 20
+    assert q(1, 65536, 32, 128, 128, 1, False) == windowed(32, 90, 23) <= 600 << 20
     assert q(2, 1000, 2, 128, 128, 2, False) == up(4 * 64 * 2 * rec) + up(st * 66 * 2) + \
         up(st * 64 * 2) + 2 * up(4 * 64 * 2 * 32 * 128)   # 2 x 32 chunks: one pass
-    # no window fits 4 MiB: the least, 11 windows of 3 chunks (6.06 MB)
+    # no window fits 4 MiB: the least, 8 windows of 4 chunks (5.46 MB)
     monkeypatch.setenv("KDA_BWD_WORKSPACE_LIMIT", str(4 << 20))
-    assert q(2, 1000, 2, 128, 128, 2, False) == windowed(4, 3, 11)
+    assert q(2, 1000, 2, 128, 128, 2, False) == windowed(4, 4, 8)
     # packed batches keep one pass
     assert q(1, 1000, 2, 64, 64, 3, True) > 0
 
