@@ -29,7 +29,7 @@
 // the state passes also keep R = V - K' S_m and dE of every chunk, which the gradient step
 // reads instead of recomputing):
 //   seq_scan_kernel   packed batches: first chunk index of every sequence
-//   prep_kernel       per (chunk, head): M, P, L, e_m, e_n, beta, b - m -> record (Q', K', K''
+//   prep_kernel       per (chunk, head): M, P, L, e_m, e_n, beta, (b - m) log2 e -> record (Q', K', K''
 //                     are rebuilt from q, k and b - m where they are read)
 //   state_fwd_kernel  per (sequence, head, 32 value columns): every chunk's entry state
 //                     and the final state, chunks in order
@@ -59,8 +59,8 @@ constexpr int GW = 32;    // value columns per step of the gradient kernel
 using f4 = __attribute__((__vector_size__(4 * sizeof(float)))) float;
 
 // Offsets (in floats) inside the per-(chunk, head) record written by prep_kernel.
-// The decayed keys and queries Q' = Q e^{X}, K' = K e^{X}, K'' = K e^{-X} (X = b - m) are not
-// kept: every reader rebuilds them from q, k and X with the same fp32 operations (rebuild_qk),
+// The decayed keys and queries Q' = Q e^{b-m}, K' = K e^{b-m}, K'' = K e^{m-b} are not kept:
+// every reader rebuilds them from q, k and X (b - m in log2 units) with the same fp32 operations,
 // which reproduces them bit for bit and keeps the record at 29 KB (d = 128) instead of 77 KB.
 template <int D>
 struct Rec {
@@ -354,15 +354,19 @@ struct In4 {
     }
 };
 
+// 2^x on the hardware exp2 unit.  The record keeps the decay exponents in log2 units,
+// X2 = (b - m) log2(e) rounded once, so 2^{X2} is fast_exp(b - m) bit for bit.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // The decayed operands of four elements of one row, from the input x (q or k) and the decay
-// exponents X = b - m: up = x e^{X} (Q' or K') and dn = x e^{-X} (K''), the same fp32 operations
-// as prep_kernel; rows past the chunk's end (ok false) are zero.
-__device__ __forceinline__ void decay4(v4f x, v4f X, bool ok, v4f& up, v4f& dn) {
+// exponents X2: up = x 2^{X2} (Q' or K') and dn = x 2^{-X2} (K''), the same fp32 operations as
+// prep_kernel; rows past the chunk's end (ok false) are zero.
+__device__ __forceinline__ void decay4(v4f x, v4f X2, bool ok, v4f& up, v4f& dn) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const float u = fast_exp(X[j]), d = fast_exp(-X[j]);
-        up[j] = ok ? x[j] * u : 0.f;
-        dn[j] = ok ? x[j] * d : 0.f;
+        const float xi = ok ? x[j] : 0.f;
+        up[j] = xi * exp2_hw(X2[j]);
+        dn[j] = xi * exp2_hw(-X2[j]);
     }
 }
 
@@ -443,9 +447,9 @@ __global__ __launch_bounds__(BT) void prep_kernel(BackwardArgs a) {
         }
         const float m = sG[(BC / 2 - 1) * LD + tid];
         for (int r = 0; r < BC; ++r) {
-            const float x = sG[r * LD + tid] - m;
-            sG[r * LD + tid] = x;
-            const float up = fast_exp(x), dn = fast_exp(-x);
+            const float x2 = (sG[r * LD + tid] - m) * 1.4426950408889634f;   // (b - m) in log2 units
+            sG[r * LD + tid] = x2;
+            const float up = exp2_hw(x2), dn = exp2_hw(-x2);
             const float kv = sK[r * LD + tid];
             sQ[r * LD + tid] *= up;
             sK[r * LD + tid] = kv * up;
@@ -1118,7 +1122,7 @@ __global__ __launch_bounds__(grad_threads<D>()) void grad_kernel(BackwardArgs a)
         rdE.load(dEg + ct * GW, D);
         rO.load(a.dO, p.t0, p.len, a.H, h, D, ct * GW);
     };
-    Stage<BC, D, GT> rX;   // decay exponents X = b - m: Q', K', K'' now, the decay factors at the end
+    Stage<BC, D, GT> rX;   // decay exponents (b - m) log2(e): Q', K', K'' now, the decay factors at the end
     {
         using SR = StageRows<IN, D, GT>;
         SR rq, rk;
@@ -1133,7 +1137,7 @@ __global__ __launch_bounds__(grad_threads<D>()) void grad_kernel(BackwardArgs a)
         fetch(0);
         static_assert(SR::IT == Stage<BC, D, GT>::IT && SR::C4 == Stage<BC, D, GT>::C4, "");
 #pragma unroll
-        for (int it = 0; it < SR::IT; ++it) {   // Q' = Q e^X, K' = K e^X, K'' = K e^-X
+        for (int it = 0; it < SR::IT; ++it) {   // Q' = Q e^{b-m}, K' = K e^{b-m}, K'' = K e^{m-b}
             const int e = tid + it * GT, r = e / SR::C4, c = 4 * (e % SR::C4);
             if (SR::live(e)) {
                 v4f qp, kp, kpp, unused;
@@ -1280,7 +1284,7 @@ __global__ __launch_bounds__(grad_threads<D>()) void grad_kernel(BackwardArgs a)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int r = 16 * rt + acc_row(v), c = 16 * dt + acc_col();
-            const float x = sX[r * LD + c], up = fast_exp(x), dn = fast_exp(-x);
+            const float x2 = sX[r * LD + c], up = exp2_hw(x2), dn = exp2_hw(-x2);
             const float gq = dQp[q][v], gk = dKp[q][v], gkk = dKpp[q][v];
             sDb[r * LD + c] = sQp[r * LD + c] * gq + sKp[r * LD + c] * gk - sKpp[r * LD + c] * gkk;
             if (r < p.len) {
