@@ -467,7 +467,7 @@ kda_status chunk_bwd_impl(const void* q, const void* k, const void* v, const voi
                           int B, int T, int H, int Dk, int Dv, int num_seqs, int chunk, kda_dtype in_dtype,
                           kda_dtype grad_dtype, void* dq, void* dk, void* dv, void* dlog_alpha, void* dbeta,
                           float* dS0, void* workspace, size_t workspace_bytes, kda_stream_t stream,
-                          bool scalar_gate) {
+                          bool scalar_gate, bool split_fp32 = false) {
     if (B < 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || num_seqs < 0) return KDA_ERR_INVALID_ARGUMENT;
     if (!dtype_ok(in_dtype) || !dtype_ok(grad_dtype)) return KDA_ERR_UNSUPPORTED;
     if (!head_ok(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
@@ -527,6 +527,7 @@ kda_status chunk_bwd_impl(const void* q, const void* k, const void* v, const voi
     a.B = B; a.T = T; a.H = H; a.D = Dk; a.N = num_seqs;
     a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = grad_dtype == KDA_BF16;
     a.scalar_gate = scalar_gate;
+    a.split_fp32 = split_fp32;
     hipError_t err = kda::launch_backward(a, plan, workspace, reinterpret_cast<hipStream_t>(stream));
     return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
@@ -667,10 +668,12 @@ kda_status chunk_bwd_fused_impl(const void* q, const void* k, const void* v, con
                                             stream, scalar_gate);
         if (s != KDA_OK) return s;
     }
-    // 3. the rule's gradient on the mapped inputs (fp32 products), into the workspace
+    // 3. the rule's gradient on the mapped inputs, into the workspace: fp32 products for fp32 raw
+    // inputs; for bf16 raw inputs, whose bound is that of bf16 inputs, split-bf16 products on the
+    // fp32 mapped inputs (fp32-accurate to about 1e-4 against that bound's 2e-3)
     const kda_status s = chunk_bwd_impl(a.qh, a.kh, a.vf, a.la, a.bt, S0, cu_seqlens, a.doc, dS_final, B, T, H, Dk,
                                         Dv, num_seqs, chunk, KDA_F32, KDA_F32, dqh, dkh, dvf, dla, dbt, dS0,
-                                        workspace, L.core, stream, scalar_gate);
+                                        workspace, L.core, stream, scalar_gate, in_dtype == KDA_BF16);
     if (s != KDA_OK) return s;
     // 4. the chain rule back through the maps and the gate
     return kda::launch_fused_bwd_post(a, st) == hipSuccess ? KDA_OK : KDA_ERR_HIP;

@@ -31,6 +31,7 @@ struct BackwardArgs {
     int B, T, H, D, N;
     bool in_bf16, out_bf16;
     bool scalar_gate = false;                // log_alpha and dlog_alpha are [B, T, H]
+    bool split_fp32 = false;                 // fp32 inputs, split-bf16 products (a bf16-input bound)
 };
 
 struct BackwardPlan {

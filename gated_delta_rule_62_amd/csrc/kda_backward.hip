@@ -58,6 +58,11 @@ constexpr int GW = 32;    // value columns per step of the gradient kernel
 
 using f4 = __attribute__((__vector_size__(4 * sizeof(float)))) float;
 
+// fp32 inputs whose products may run split bf16 (hi + lo, about 16 mantissa bits per operand): the
+// gradient of the fused layer on the fp32 mapped values of bf16 raw inputs, whose bound is that of
+// bf16 inputs.  Loads and layouts are F32's.
+struct F32S : F32 {};
+
 // Offsets (in floats) inside the per-(chunk, head) record written by prep_kernel.
 // The decayed keys and queries Q' = Q e^{b-m}, K' = K e^{b-m}, K'' = K e^{m-b} are not kept:
 // every reader rebuilds them from q, k and X (b - m in log2 units) with the same fp32 operations,
@@ -407,7 +412,7 @@ __global__ __launch_bounds__(BT) void seq_scan_kernel(const int32_t* cu, int N, 
 
 template <int D, class IN, bool SG>
 __global__ __launch_bounds__(BT) void prep_kernel(BackwardArgs a) {
-    constexpr bool SPLIT = std::is_same<IN, BF16>::value;   // split-bf16 products for bf16 inputs
+    constexpr bool SPLIT = !std::is_same<IN, F32>::value;   // split-bf16 products for BF16 and F32S
     constexpr int LD = D + 4, LC = BC + 4;
     __shared__ __attribute__((aligned(16))) float sQ[BC * LD], sK[BC * LD], sKpp[BC * LD], sG[BC * LD];
     __shared__ __attribute__((aligned(16))) float sL[BC * LC], sP[BC * LC];
@@ -663,7 +668,7 @@ struct FwdLoad {
 template <int D, class IN, int WM>
 __global__ __launch_bounds__(STH) void state_fwd_kernel(BackwardArgs a) {
     constexpr bool WIN = WM != 0, CKPT = WM == 2;
-    constexpr bool SPLIT = std::is_same<IN, BF16>::value;   // split-bf16 products for bf16 inputs
+    constexpr bool SPLIT = !std::is_same<IN, F32>::value;   // split-bf16 products for BF16 and F32S
     constexpr int NT = D / 64, NTILE = D / SW, LY = BC + 4;
     using SL = FwdSlot<D>;
     __shared__ __attribute__((aligned(16))) float sSlot[2 * SL::SIZE];
@@ -880,7 +885,7 @@ struct RevLoad {
 // earlier chunk's dS_next.  The loading waves fill the earlier chunk's slot during (B).
 template <int D, class IN, bool WIN>
 __global__ __launch_bounds__(STH) void state_rev_kernel(BackwardArgs a) {
-    constexpr bool SPLIT = std::is_same<IN, BF16>::value;   // split-bf16 products for bf16 inputs
+    constexpr bool SPLIT = !std::is_same<IN, F32>::value;   // split-bf16 products for BF16 and F32S
     constexpr int NT = D / 64, NTILE = D / SW, LY = BC + 4;
     using SL = RevSlot<D>;
     __shared__ __attribute__((aligned(16))) float sSlot[2 * SL::SIZE];
@@ -1087,7 +1092,7 @@ constexpr int grad_threads() { return 8 * D / GRAD_RTW; }
 
 template <int D, class IN, bool OB, bool SG>
 __global__ __launch_bounds__(grad_threads<D>()) void grad_kernel(BackwardArgs a) {
-    constexpr bool SPLIT = std::is_same<IN, BF16>::value;   // split-bf16 products for bf16 inputs
+    constexpr bool SPLIT = !std::is_same<IN, F32>::value;   // split-bf16 products for BF16 and F32S
     constexpr int LD = D + 4, LC = BC + 4, LT = GW + 4, NCT = D / GW;
     constexpr int RTW = GRAD_RTW, GT = grad_threads<D>(), NW = GT / 64;   // threads and waves
     static_assert(NW >= 4 && NW == (D / 16) * (2 / RTW), "");
@@ -1478,6 +1483,12 @@ hipError_t launch_backward(BackwardArgs a, const BackwardPlan& pl, void* workspa
 #define KDA_BWD_CASE(DD, IN, OB)                                                              \
     if (a.D == DD && a.in_bf16 == std::is_same<IN, BF16>::value && a.out_bf16 == OB)         \
         return a.scalar_gate ? launch_typed<DD, IN, OB, true>(a, nc, nw, st) : launch_typed<DD, IN, OB, false>(a, nc, nw, st);
+    if (a.split_fp32 && !a.in_bf16) {
+        KDA_BWD_CASE(128, F32S, false)
+        KDA_BWD_CASE(128, F32S, true)
+        KDA_BWD_CASE(64, F32S, false)
+        KDA_BWD_CASE(64, F32S, true)
+    }
     KDA_BWD_CASE(128, BF16, false)
     KDA_BWD_CASE(128, BF16, true)
     KDA_BWD_CASE(128, F32, false)

@@ -396,8 +396,10 @@ kda_status gdn_chunk_bwd(const void* q, const void* k, const void* v, const void
  *   workspace  : kda_chunk_bwd_fused_workspace_bytes() bytes (has_out_gate 0 or 1): the
  *                rule's gradient workspace, then fp32 copies of the mapped inputs, of the
  *                rule's gradients and, with a gate, of the ungated output.
- * The rule's gradient runs on the mapped inputs in fp32 (fp32 matrix-core products); with a
- * gate, one forward pass first recomputes the ungated output.  dlog_alpha and dbeta hold the
+ * The rule's gradient runs on the mapped inputs in fp32: with fp32 matrix-core products for
+ * fp32 raw inputs, and with split-bf16 products (hi + lo, fp32 accumulation) for bf16 raw
+ * inputs, whose tolerance is the bf16 one; with a gate, one forward pass first recomputes the
+ * ungated output.  dlog_alpha and dbeta hold the
  * gradients of the decay and beta logits under those flags.  Errors as for kda_chunk_bwd.
  */
 size_t kda_chunk_bwd_fused_workspace_bytes(int B, int T, int H, int Dk, int Dv, int num_seqs,
