@@ -13,9 +13,11 @@
 //                      db = dbeta s (1 - s) with s = sigmoid(b),
 //                      da = dlog_alpha (1 - sigmoid(a + bias)) / scale,
 //                      dgate = d_o o s (1 - s) with s = sigmoid(gate) and o the ungated output.
-// One wave per (token, head) row of Dk = Dv = D values, D / 64 per lane; the dot products over
-// the row are wave reductions.
+// Eight consecutive values of a (token, head) row of Dk = Dv = D values per lane (16-byte
+// accesses), D / 8 lanes per row; the dot products over the row are reductions over those lanes.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "kda_device.h"
 #include "kda_launch.h"
@@ -23,11 +25,71 @@
 namespace kda {
 namespace {
 
-constexpr int kRowsPerBlock = 4;   // one wave per row
+constexpr int kWavesPerBlock = 4;
 
-__device__ __forceinline__ float wave_sum(float x) {
+// Eight consecutive values of a row in the input's type (16 bytes of bf16 or 32 of fp32), and
+// their fp32 widening.
+template <class IN>
+struct Vec8 {
+    static constexpr bool B16 = std::is_same<IN, BF16>::value;
+    float x[8];
+    __device__ __forceinline__ void load(const void* p, size_t i) {
+        if constexpr (B16) {
+            const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + i);
+            const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+            for (int j = 0; j < 4; ++j) {
+                x[2 * j] = __uint_as_float(u[j] << 16);
+                x[2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
+            }
+        } else {
+            const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+            const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i + 4);
+            x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+            x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+        }
+    }
+};
+
+// One value of a per-row input ([tokens, H]) in fp32.
+template <class IN>
+__device__ __forceinline__ float ld_in(const void* p, size_t i, IN) {
+    return IN::to_f32(static_cast<const typename IN::storage*>(p)[i]);
+}
+
+__device__ __forceinline__ void load8(float (&x)[8], const float* p) {
+    const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+__device__ __forceinline__ void store8(float* p, const float (&x)[8]) {
+    *reinterpret_cast<float4*>(p) = float4{x[0], x[1], x[2], x[3]};
+    *reinterpret_cast<float4*>(p + 4) = float4{x[4], x[5], x[6], x[7]};
+}
+
+// Eight outputs: fp32, or the round-to-nearest-even bf16 of each (16 bytes).
+template <bool OUT_BF16>
+__device__ __forceinline__ void store_out8(void* base, size_t i, const float (&x)[8]) {
+    if constexpr (OUT_BF16) {
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const __bf16 lo = static_cast<__bf16>(x[2 * j]), hi = static_cast<__bf16>(x[2 * j + 1]);
+            w[j] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
+                   (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
+        }
+        *reinterpret_cast<uint4*>(static_cast<__bf16*>(base) + i) = uint4{w[0], w[1], w[2], w[3]};
+    } else {
+        store8(static_cast<float*>(base) + i, x);
+    }
+}
+
+// Sum over the LPR lanes of one row (an aligned group of LPR lanes of the wave).
+template <int LPR>
+__device__ __forceinline__ float row_sum(float x) {
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
     return x;
 }
 
@@ -40,125 +102,160 @@ __device__ __forceinline__ float sigm(float x) {
 // log(sigmoid(x)) = min(x, 0) - log1p(e^-|x|)
 __device__ __forceinline__ float logsigm(float x) { return fminf(x, 0.f) - log1pf(fast_exp(-fabsf(x))); }
 
+// Rows of D values, 8 consecutive values per lane: LPR = D / 8 lanes per row, 64 / LPR rows per
+// wave.  The launch covers every row; the lanes of a row past the last exit together.
+template <int D>
+struct RowMap {
+    static constexpr int LPR = D / 8, RPW = 64 / LPR, RPB = RPW * kWavesPerBlock;
+    size_t row;
+    int c, first;
+    __device__ __forceinline__ RowMap() {
+        const int t = threadIdx.x;
+        row = static_cast<size_t>(blockIdx.x) * RPB + t / LPR;
+        c = 8 * (t % LPR);
+        first = t % LPR == 0;
+    }
+};
+
 template <int D, class IN, bool SG>
-__global__ __launch_bounds__(64 * kRowsPerBlock) void fused_pre_kernel(FusedBwdArgs a) {
-    constexpr int E = D / 64;
-    const size_t row = static_cast<size_t>(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6);
-    if (row >= a.rows) return;
-    const int l = threadIdx.x & 63;
-    using S = typename IN::storage;
-    const S* q = static_cast<const S*>(a.q);
-    const S* k = static_cast<const S*>(a.k);
-    const S* v = static_cast<const S*>(a.v);
-    const S* dO = static_cast<const S*>(a.d_o);
-    const S* gate = static_cast<const S*>(a.gate);
-    const S* la = static_cast<const S*>(a.log_alpha);
-    const S* bt = static_cast<const S*>(a.beta);
-    const size_t base = row * D;
-    float qv[E], kv[E], sq = 0.f, sk = 0.f;
+__global__ __launch_bounds__(64 * kWavesPerBlock) void fused_pre_kernel(FusedBwdArgs a) {
+    using RM = RowMap<D>;
+    const RM m;
+    if (m.row >= a.rows) return;
+    const size_t i = m.row * D + m.c;
+    Vec8<IN> q, k, v, d;
+    q.load(a.q, i);
+    k.load(a.k, i);
+    v.load(a.v, i);
+    d.load(a.d_o, i);
+    float sq = 0.f, sk = 0.f;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        qv[e] = IN::to_f32(q[base + l + 64 * e]);
-        kv[e] = IN::to_f32(k[base + l + 64 * e]);
-        sq += qv[e] * qv[e];
-        sk += kv[e] * kv[e];
+    for (int j = 0; j < 8; ++j) {
+        sq += q.x[j] * q.x[j];
+        sk += k.x[j] * k.x[j];
     }
     const bool l2 = a.flags & 1;
-    const float rq = l2 ? 1.f / sqrtf(wave_sum(sq) + 1e-12f) : 1.f;
-    const float rk = l2 ? 1.f / sqrtf(wave_sum(sk) + 1e-12f) : 1.f;
+    const float rq = l2 ? 1.f / sqrtf(row_sum<RM::LPR>(sq) + 1e-12f) : 1.f;
+    const float rk = l2 ? 1.f / sqrtf(row_sum<RM::LPR>(sk) + 1e-12f) : 1.f;
+    float o[8];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const size_t i = base + l + 64 * e;
-        a.qh[i] = qv[e] * rq;
-        a.kh[i] = kv[e] * rk;
-        a.vf[i] = IN::to_f32(v[i]);
-        const float d = IN::to_f32(dO[i]);
-        a.doc[i] = gate ? d * sigm(IN::to_f32(gate[i])) : d;
-        if constexpr (!SG) {
-            const float x = IN::to_f32(la[i]);
-            a.la[i] = (a.flags & 4) ? logsigm(x + a.decay_bias) / a.decay_scale : x;
+    for (int j = 0; j < 8; ++j) o[j] = q.x[j] * rq;
+    store8(a.qh + i, o);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = k.x[j] * rk;
+    store8(a.kh + i, o);
+    store8(a.vf + i, v.x);
+    if (a.gate) {
+        Vec8<IN> g;
+        g.load(a.gate, i);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = d.x[j] * sigm(g.x[j]);
+        store8(a.doc + i, o);
+    } else {
+        store8(a.doc + i, d.x);
+    }
+    if constexpr (!SG) {
+        Vec8<IN> g;
+        g.load(a.log_alpha, i);
+        if (a.flags & 4) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[j] = logsigm(g.x[j] + a.decay_bias) / a.decay_scale;
+            store8(a.la + i, o);
+        } else {
+            store8(a.la + i, g.x);
         }
     }
-    if (l == 0) {
-        a.rq[row] = rq;
-        a.rk[row] = rk;
-        const float b = IN::to_f32(bt[row]);
-        a.bt[row] = (a.flags & 2) ? sigm(b) : b;
+    if (m.first) {
+        a.rq[m.row] = rq;
+        a.rk[m.row] = rk;
+        const float b = ld_in(a.beta, m.row, IN{});
+        a.bt[m.row] = (a.flags & 2) ? sigm(b) : b;
         if constexpr (SG) {
-            const float x = IN::to_f32(la[row]);
-            a.la[row] = (a.flags & 4) ? logsigm(x + a.decay_bias) / a.decay_scale : x;
+            const float x = ld_in(a.log_alpha, m.row, IN{});
+            a.la[m.row] = (a.flags & 4) ? logsigm(x + a.decay_bias) / a.decay_scale : x;
         }
     }
 }
 
 template <int D, class IN, bool OB, bool SG>
-__global__ __launch_bounds__(64 * kRowsPerBlock) void fused_post_kernel(FusedBwdArgs a) {
-    constexpr int E = D / 64;
-    const size_t row = static_cast<size_t>(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 6);
-    if (row >= a.rows) return;
-    const int l = threadIdx.x & 63;
-    using S = typename IN::storage;
-    const S* dO = static_cast<const S*>(a.d_o);
-    const S* gate = static_cast<const S*>(a.gate);
-    const S* la = static_cast<const S*>(a.log_alpha);
-    const S* bt = static_cast<const S*>(a.beta);
-    const size_t base = row * D;
+__global__ __launch_bounds__(64 * kWavesPerBlock) void fused_post_kernel(FusedBwdArgs a) {
+    using RM = RowMap<D>;
+    const RM m;
+    if (m.row >= a.rows) return;
+    const size_t i = m.row * D + m.c;
     const bool l2 = a.flags & 1;
-    float dq[E], dk[E], pq = 0.f, pk = 0.f;
+    float dq[8], dk[8], qh[8], kh[8], o[8];
+    load8(dq, a.dqh + i);
+    load8(dk, a.dkh + i);
+    load8(qh, a.qh + i);
+    load8(kh, a.kh + i);
+    float pq = 0.f, pk = 0.f;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const size_t i = base + l + 64 * e;
-        dq[e] = a.dqh[i];
-        dk[e] = a.dkh[i];
-        pq += a.qh[i] * dq[e];
-        pk += a.kh[i] * dk[e];
+    for (int j = 0; j < 8; ++j) {
+        pq += qh[j] * dq[j];
+        pk += kh[j] * dk[j];
     }
     if (l2) {
-        pq = wave_sum(pq);
-        pk = wave_sum(pk);
+        pq = row_sum<RM::LPR>(pq);
+        pk = row_sum<RM::LPR>(pk);
     }
-    const float rq = a.rq[row], rk = a.rk[row];
+    const float rq = a.rq[m.row], rk = a.rk[m.row];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const size_t i = base + l + 64 * e;
-        const float gq = l2 ? (dq[e] - a.qh[i] * pq) * rq : dq[e];
-        const float gk = l2 ? (dk[e] - a.kh[i] * pk) * rk : dk[e];
-        store_out<OB>(a.dq, i, gq);
-        store_out<OB>(a.dk, i, gk);
-        store_out<OB>(a.dv, i, a.dvf[i]);
-        if constexpr (!SG) {
-            const float g = a.dla[i];
-            store_out<OB>(a.dla_out, i,
-                          (a.flags & 4) ? g * sigm(-(IN::to_f32(la[i]) + a.decay_bias)) / a.decay_scale : g);
+    for (int j = 0; j < 8; ++j) o[j] = l2 ? (dq[j] - qh[j] * pq) * rq : dq[j];
+    store_out8<OB>(a.dq, i, o);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = l2 ? (dk[j] - kh[j] * pk) * rk : dk[j];
+    store_out8<OB>(a.dk, i, o);
+    load8(o, a.dvf + i);
+    store_out8<OB>(a.dv, i, o);
+    if constexpr (!SG) {
+        load8(o, a.dla + i);
+        if (a.flags & 4) {
+            Vec8<IN> x;
+            x.load(a.log_alpha, i);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[j] = o[j] * sigm(-(x.x[j] + a.decay_bias)) / a.decay_scale;
         }
-        if (gate) {
-            const float s = sigm(IN::to_f32(gate[i]));
-            store_out<OB>(a.dgate, i, IN::to_f32(dO[i]) * a.oc[i] * s * (1.f - s));
-        }
+        store_out8<OB>(a.dla_out, i, o);
     }
-    if (l == 0) {
-        const float g = a.dbt[row];
-        const float s = sigm(IN::to_f32(bt[row]));
-        store_out<OB>(a.dbeta_out, row, (a.flags & 2) ? g * s * (1.f - s) : g);
+    if (a.gate) {
+        Vec8<IN> g, d;
+        g.load(a.gate, i);
+        d.load(a.d_o, i);
+        float oc[8];
+        load8(oc, a.oc + i);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float s = sigm(g.x[j]);
+            o[j] = d.x[j] * oc[j] * s * (1.f - s);
+        }
+        store_out8<OB>(a.dgate, i, o);
+    }
+    if (m.first) {
+        const float g = a.dbt[m.row];
+        const float s = sigm(ld_in(a.beta, m.row, IN{}));
+        store_out<OB>(a.dbeta_out, m.row, (a.flags & 2) ? g * s * (1.f - s) : g);
         if constexpr (SG) {
-            const float h = a.dla[row];
-            store_out<OB>(a.dla_out, row,
-                          (a.flags & 4) ? h * sigm(-(IN::to_f32(la[row]) + a.decay_bias)) / a.decay_scale : h);
+            const float h = a.dla[m.row];
+            store_out<OB>(a.dla_out, m.row,
+                          (a.flags & 4) ? h * sigm(-(ld_in(a.log_alpha, m.row, IN{}) + a.decay_bias)) / a.decay_scale : h);
         }
     }
 }
 
 template <int D, class IN, bool SG>
 hipError_t pre_typed(const FusedBwdArgs& a, hipStream_t st) {
-    const unsigned grid = static_cast<unsigned>((a.rows + kRowsPerBlock - 1) / kRowsPerBlock);
-    fused_pre_kernel<D, IN, SG><<<grid, 64 * kRowsPerBlock, 0, st>>>(a);
+    constexpr int RPB = RowMap<D>::RPB;
+    const unsigned grid = static_cast<unsigned>((a.rows + RPB - 1) / RPB);
+    fused_pre_kernel<D, IN, SG><<<grid, 64 * kWavesPerBlock, 0, st>>>(a);
     return hipGetLastError();
 }
 
 template <int D, class IN, bool OB, bool SG>
 hipError_t post_typed(const FusedBwdArgs& a, hipStream_t st) {
-    const unsigned grid = static_cast<unsigned>((a.rows + kRowsPerBlock - 1) / kRowsPerBlock);
-    fused_post_kernel<D, IN, OB, SG><<<grid, 64 * kRowsPerBlock, 0, st>>>(a);
+    constexpr int RPB = RowMap<D>::RPB;
+    const unsigned grid = static_cast<unsigned>((a.rows + RPB - 1) / RPB);
+    fused_post_kernel<D, IN, OB, SG><<<grid, 64 * kWavesPerBlock, 0, st>>>(a);
     return hipGetLastError();
 }
 
