@@ -2101,12 +2101,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // against all others, O(N) per thread over a grid of N threads: for batches of up to
 // kOrderExactMax sequences.  Larger batches take the bucketed order below.
 __global__ __launch_bounds__(256) void order_kernel(const int32_t* __restrict__ cu, int32_t* __restrict__ order, int N) {
+    __shared__ int len[kOrderExactMax];   // every sequence's length, read once per workgroup
+    for (int m = threadIdx.x; m < N; m += blockDim.x) len[m] = cu[m + 1] - cu[m];
+    __syncthreads();
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= N) return;
-    const int li = cu[i + 1] - cu[i];
+    const int li = len[i];
     int rank = 0;
     for (int m = 0; m < N; ++m) {
-        const int lm = cu[m + 1] - cu[m];
+        const int lm = len[m];
         rank += (lm > li) || (lm == li && m < i);
     }
     order[rank] = i;
@@ -2169,22 +2172,27 @@ __global__ __launch_bounds__(256) void order_scatter_kernel(const int32_t* __res
 // Ranks are longest first (ties by index), as in the one-pass order.
 __global__ __launch_bounds__(256) void seg_plan_kernel(const int32_t* __restrict__ cu, int N, int C, int items,
                                                        int Lmin, float ratio, int32_t* __restrict__ tab) {
-    __shared__ int red[256];
+    __shared__ int red[2][4];   // per-wave partials, two sets so consecutive reductions need one barrier each
     __shared__ int more_r[256];
+    __shared__ int lens[256];
     const int i = threadIdx.x;
     const bool act = i < N;
     const int len = act ? cu[i + 1] - cu[i] : 0;
+    lens[i] = len;
     const int c = (len + C - 1) / C;
+    int parity = 0;
+    // over the 256 threads: a wave reduction, then the four waves' partials through LDS
     auto reduce = [&](int x, bool take_max) {
-        red[i] = x;
-        __syncthreads();
-        for (int o = 128; o > 0; o >>= 1) {
-            if (i < o) red[i] = take_max ? max(red[i], red[i + o]) : red[i] + red[i + o];
-            __syncthreads();
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const int y = __shfl_xor(x, o, 64);
+            x = take_max ? max(x, y) : x + y;
         }
-        const int r = red[0];
+        if ((i & 63) == 0) red[parity][i >> 6] = x;
         __syncthreads();
-        return r;
+        const int* p = red[parity];
+        parity ^= 1;
+        return take_max ? max(max(p[0], p[1]), max(p[2], p[3])) : (p[0] + p[1]) + (p[2] + p[3]);
     };
     auto more_of = [&](int L) {
         const int t = L >= 64 ? max(1, static_cast<int>(rintf(ratio * L))) : L;
@@ -2208,7 +2216,7 @@ __global__ __launch_bounds__(256) void seg_plan_kernel(const int32_t* __restrict
     if (act) {
         int rank = 0;
         for (int m = 0; m < N; ++m) {
-            const int lm = cu[m + 1] - cu[m];
+            const int lm = lens[m];
             rank += (lm > len) || (lm == len && m < i);
         }
         const int m = cut ? more_of(L) : 0;
