@@ -31,9 +31,10 @@
 //   seq_scan_kernel   packed batches: first chunk index of every sequence
 //   prep_kernel       per (chunk, head): M, P, L, e_m, e_n, beta, (b - m) log2 e -> record (Q', K', K''
 //                     are rebuilt from q, k and b - m where they are read)
-//   state_fwd_kernel  per (sequence, head, 32 value columns): every chunk's entry state
+//   state_fwd         per (sequence, head, 32 value columns): every chunk's entry state
 //                     and the final state, chunks in order
-//   state_rev_kernel  same split: every chunk's dS_next, chunks in reverse order; dS0
+//   state_rev         same split: every chunk's dS_next, chunks in reverse order; dS0 (the two
+//                     state passes are independent and run in one launch, state_pair_kernel)
 //   grad_kernel       per (chunk, head): dq, dk, dv, dlog_alpha, dbeta
 // The scalar-gated variant (one log-decay per token and head, broadcast over the key
 // channels) runs the same kernels; its dlog_alpha is the per-channel one summed over the
@@ -665,16 +666,23 @@ struct FwdLoad {
 // Y = K' S_m over its rows; (B) R = V - Y, and one 16 x 16 tile each of E = M Diag(beta) R on the
 // computing waves of row group 0 and 1; (C) every computing wave updates its rows,
 // S <- Diag(e_n)(S_m + K''^T E).  The loading waves fill the next chunk's slot during (B).
+template <int D>
+struct alignas(16) FwdShared {
+    float slot[2 * FwdSlot<D>::SIZE];
+    float y[SCW * 16 * (BC + 4)], e[2 * 16 * (BC + 4)];
+};
+
 template <int D, class IN, int WM>
-__global__ __launch_bounds__(STH) void state_fwd_kernel(BackwardArgs a) {
+__device__ __forceinline__ void state_fwd_body(const BackwardArgs& a, FwdShared<D>& sh, int block, int nblocks) {
     constexpr bool WIN = WM != 0, CKPT = WM == 2;
     constexpr bool SPLIT = !std::is_same<IN, F32>::value;   // split-bf16 products for BF16 and F32S
     constexpr int NT = D / 64, NTILE = D / SW, LY = BC + 4;
     using SL = FwdSlot<D>;
-    __shared__ __attribute__((aligned(16))) float sSlot[2 * SL::SIZE];
-    __shared__ __attribute__((aligned(16))) float sY[SCW * 16 * LY], sE[2 * 16 * LY];
+    float* const sSlot = sh.slot;
+    float* const sY = sh.y;
+    float* const sE = sh.e;
     int u, jt;
-    unit_tile(blockIdx.x, gridDim.x, NTILE, u, jt);
+    unit_tile(block, nblocks, NTILE, u, jt);
     const int n = u / a.H, h = u % a.H, tid = threadIdx.x, w = tid >> 6;
     const int L = seq_len(a, n), nch = (L + BC - 1) / BC, tok0 = seq_first_token(a, n);
     const size_t DD = (size_t)D * D;
@@ -860,6 +868,12 @@ __global__ __launch_bounds__(STH) void state_fwd_kernel(BackwardArgs a) {
         for (int v = 0; v < 4; ++v) slot[(size_t)(r0 + 16 * q + v) * D] = S[q][v];
 }
 
+template <int D, class IN, int WM>
+__global__ __launch_bounds__(STH) void state_fwd_kernel(BackwardArgs a) {
+    __shared__ FwdShared<D> sh;
+    state_fwd_body<D, IN, WM>(a, sh, blockIdx.x, gridDim.x);
+}
+
 // LDS slot of one chunk's operands for the reverse state pass (floats).
 template <int D>
 struct RevSlot {
@@ -883,15 +897,22 @@ struct RevLoad {
 // tile each); (B) dE, and one 16 x 16 tile each of -dV = -Diag(beta) M^T dE on row groups 0 and 1;
 // (C) every computing wave takes its rows of dS = Diag(e_m)(dS_n + Q'^T dO - K'^T dV), the
 // earlier chunk's dS_next.  The loading waves fill the earlier chunk's slot during (B).
+template <int D>
+struct alignas(16) RevShared {
+    float slot[2 * RevSlot<D>::SIZE];
+    float y[SCW * 16 * (BC + 4)], v[2 * 16 * (BC + 4)];
+};
+
 template <int D, class IN, bool WIN>
-__global__ __launch_bounds__(STH) void state_rev_kernel(BackwardArgs a) {
+__device__ __forceinline__ void state_rev_body(const BackwardArgs& a, RevShared<D>& sh, int block, int nblocks) {
     constexpr bool SPLIT = !std::is_same<IN, F32>::value;   // split-bf16 products for BF16 and F32S
     constexpr int NT = D / 64, NTILE = D / SW, LY = BC + 4;
     using SL = RevSlot<D>;
-    __shared__ __attribute__((aligned(16))) float sSlot[2 * SL::SIZE];
-    __shared__ __attribute__((aligned(16))) float sY[SCW * 16 * LY], sV[2 * 16 * LY];
+    float* const sSlot = sh.slot;
+    float* const sY = sh.y;
+    float* const sV = sh.v;
     int u, jt;
-    unit_tile(blockIdx.x, gridDim.x, NTILE, u, jt);
+    unit_tile(block, nblocks, NTILE, u, jt);
     const int n = u / a.H, h = u % a.H, tid = threadIdx.x, w = tid >> 6;
     const int L = seq_len(a, n), nch = (L + BC - 1) / BC, tok0 = seq_first_token(a, n);
     const size_t DD = (size_t)D * D;
@@ -1086,6 +1107,20 @@ __global__ __launch_bounds__(STH) void state_rev_kernel(BackwardArgs a) {
 
 // Each wave owns one 16-column tile of D in GRAD_RTW of the chunk's two 16-row tiles (so 8 D /
 // GRAD_RTW threads), and waves 0-3 also the four 16 x 16 tiles of the C x GW and C x C products.
+// The two state passes of the same chunks in one launch: they are independent (the reverse
+// pass reads only the records, dO and the later state gradient), so when each has fewer
+// workgroups than the chip has compute units (few sequences and heads) they run side by side.
+// Workgroups [0, nf) run the forward pass, the rest the reverse pass.
+template <int D, class IN, int WM, bool WIN>
+__global__ __launch_bounds__(STH) void state_pair_kernel(BackwardArgs a, int nf) {
+    __shared__ union {
+        FwdShared<D> f;
+        RevShared<D> r;
+    } sh;
+    if (static_cast<int>(blockIdx.x) < nf) state_fwd_body<D, IN, WM>(a, sh.f, blockIdx.x, nf);
+    else state_rev_body<D, IN, WIN>(a, sh.r, blockIdx.x - nf, gridDim.x - nf);
+}
+
 constexpr int GRAD_RTW = 2;
 template <int D>
 constexpr int grad_threads() { return 8 * D / GRAD_RTW; }
@@ -1350,10 +1385,7 @@ hipError_t launch_typed(BackwardArgs a, int nc_max, int n_win, hipStream_t st) {
     }
     if (!a.W) {
         if (nc_max > 0) prep_kernel<D, IN, SG><<<nc_max * a.H, BT, 0, st>>>(a);
-        if (units > 0) {
-            state_fwd_kernel<D, IN, 0><<<units * (D / SW), STH, 0, st>>>(a);
-            state_rev_kernel<D, IN, false><<<units * (D / SW), STH, 0, st>>>(a);
-        }
+        if (units > 0) state_pair_kernel<D, IN, 0, false><<<2 * units * (D / SW), STH, 0, st>>>(a, units * (D / SW));
         if (nc_max > 0) grad_kernel<D, IN, OB, SG><<<nc_max * a.H, grad_threads<D>(), 0, st>>>(a);
         return hipGetLastError();
     }
@@ -1372,8 +1404,7 @@ hipError_t launch_typed(BackwardArgs a, int nc_max, int n_win, hipStream_t st) {
         a.wi = wi;
         a.w0 = wi * a.W;
         prep_kernel<D, IN, SG><<<grid, BT, 0, st>>>(a);
-        state_fwd_kernel<D, IN, 1><<<units * (D / SW), STH, 0, st>>>(a);
-        state_rev_kernel<D, IN, true><<<units * (D / SW), STH, 0, st>>>(a);
+        state_pair_kernel<D, IN, 1, true><<<2 * units * (D / SW), STH, 0, st>>>(a, units * (D / SW));
         grad_kernel<D, IN, OB, SG><<<grid, grad_threads<D>(), 0, st>>>(a);
     }
     return hipGetLastError();
