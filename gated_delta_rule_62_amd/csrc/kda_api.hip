@@ -64,6 +64,10 @@ extern "C" size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int
     if (B < 0 || T < 0 || H <= 0 || num_seqs < 0 || !head_ok(Dk, Dv)) return 0;
     if (!kda::chunk_supported(chunk)) return 0;
     kda::PrefillPlan plan = kda::plan_prefill(B, T, H, Dk, num_seqs, has_cu_seqlens != 0, chunk);
+    if (chunk == 64) {   // also enough for the 32-token evaluation of the scalar gate and fused calls
+        const kda::PrefillPlan p32 = kda::plan_prefill(B, T, H, Dk, num_seqs, has_cu_seqlens != 0, 32);
+        return std::max(plan.workspace_bytes, p32.workspace_bytes);
+    }
     return plan.workspace_bytes;
 }
 
@@ -102,7 +106,9 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
     if (!kda::chunk_supported(chunk)) return KDA_ERR_UNSUPPORTED;
     if (!fusion_ok(fusion)) return KDA_ERR_INVALID_ARGUMENT;
     const bool fused = fusion && (fusion->flags || fusion->out_gate);
-    if ((scalar_gate || fused) && chunk != 0 && chunk != 32) return KDA_ERR_UNSUPPORTED;
+    // The scalar gate and the fused maps run on the pipelined 32-token kernel: a 64-token request is
+    // evaluated with 32-token chunks (the result does not depend on the chunk length beyond rounding).
+    if ((scalar_gate || fused) && chunk == 64) chunk = 32;
     if (cu_seqlens) {
         if (B != 1) return KDA_ERR_INVALID_ARGUMENT;
         if (!aligned16(cu_seqlens)) return KDA_ERR_INVALID_ARGUMENT;

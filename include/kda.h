@@ -86,7 +86,9 @@ const char* kda_status_string(kda_status s);
  * Packed batches with 32-token chunks and fewer than 256 (sequence, head) pairs
  * reserve segment summaries for 256 / H segments per head: the call cuts its
  * sequences into segments on the device, from cu_seqlens, so that one long
- * sequence still spreads over the chip.
+ * sequence still spreads over the chip.  For chunk 64 the size also covers the
+ * 32-token evaluation that the scalar-gate and fused entry points use for such a
+ * request, so one query serves every entry point that takes these arguments.
  */
 size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int num_seqs,
                                      int has_cu_seqlens, int chunk);
@@ -205,8 +207,9 @@ kda_status kda_recurrent_fwd(const void* q, const void* k, const void* v, const 
  *                             o <- o * sigmoid(gate), per value channel
  *
  * The _fused functions take the arguments of their plain counterparts plus a
- * kda_fusion (NULL or all-zero = the plain function); kda_chunk_fwd_fused supports
- * chunk 0 or 32 and uses kda_chunk_fwd_workspace_bytes().
+ * kda_fusion (NULL or all-zero = the plain function); kda_chunk_fwd_fused takes chunk 0,
+ * 32 or 64 (64 is evaluated with 32-token chunks, which change the result only by rounding)
+ * and uses kda_chunk_fwd_workspace_bytes() with the same chunk argument.
  */
 typedef enum {
     KDA_FUSE_QK_L2NORM = 1,
@@ -247,7 +250,8 @@ kda_status kda_recurrent_step_fused(const void* q, const void* k, const void* v,
  *               (gdn_recurrent_step), in_dtype; every other argument as in the
  *               kda_ function of the same suffix.
  *
- * gdn_chunk_fwd supports chunk 0 or 32 and uses kda_chunk_fwd_workspace_bytes().
+ * gdn_chunk_fwd takes chunk 0, 32 or 64 (64 is evaluated with 32-token chunks) and uses
+ * kda_chunk_fwd_workspace_bytes() with the same chunk argument.
  * With a scalar decay the chunk's decay factors leave the contractions, so with
  * bf16 inputs the keys and queries are exact MFMA operands and the prefill does
  * about a third less matrix work and almost no per-element decay work.
@@ -269,7 +273,8 @@ kda_status gdn_recurrent_step(const void* q, const void* k, const void* v, const
  * Scalar gate with the fused prologue / epilogue: gdn_chunk_fwd and gdn_recurrent_step
  * plus a kda_fusion, with the maps of kda_chunk_fwd_fused applied to the scalar-gate
  * inputs (KDA_FUSE_DECAY_LOGSIGMOID maps the one log_alpha logit per token and head).
- * gdn_chunk_fwd_fused supports chunk 0 or 32 and uses kda_chunk_fwd_workspace_bytes().
+ * gdn_chunk_fwd_fused takes chunk 0, 32 or 64 (64 is evaluated with 32-token chunks) and
+ * uses kda_chunk_fwd_workspace_bytes() with the same chunk argument.
  */
 kda_status gdn_chunk_fwd_fused(const void* q, const void* k, const void* v, const void* log_alpha,
                                const void* beta, const float* S0, const int32_t* cu_seqlens,

@@ -74,7 +74,10 @@ def test_workspace_query_plans(lib):
     # are cut into 8 segments (one workgroup per compute unit in each pass); 2048 chunks of 32
     # into 9, since segment 0's output pass runs beside the summaries of segments 1..7.
     assert q(1, 65536, 32, 128, 128, 1, False) == st + 3 * 32 * 8 * 128 * 128 * 4
-    assert q(1, 65536, 32, 128, 128, 1, False, chunk=64) == st + 3 * 32 * 7 * 128 * 128 * 4
+    # the 64-token plan needs 7 segment gaps; its query also covers the 32-token evaluation of the
+    # scalar-gate and fused calls, so it returns the larger of the two
+    assert q(1, 65536, 32, 128, 128, 1, False, chunk=64) == max(st + 3 * 32 * 7 * 128 * 128 * 4,
+                                                                st + 3 * 32 * 8 * 128 * 128 * 4)
     # training shape, 64 units: 5 segments of 32-token chunks (summaries of 1..3 beside 0)
     assert q(4, 4096, 16, 128, 128, 4, False) == st + 3 * 64 * 4 * 128 * 128 * 4
     # enough units to fill the chip: single pass, only the status block
@@ -86,7 +89,9 @@ def test_workspace_query_plans(lib):
     assert q(1, 100000, 2, 128, 128, 4096, True) == st + 4096 * 4
     assert q(1, 100000, 2, 128, 128, 5000, True) == st + 20224 + 8192
     assert q(1, 200, 32, 128, 128, 1, True) == st + 256           # 7 chunks: too short to cut
-    assert q(1, 65536, 32, 128, 128, 1, True, chunk=64) == st + 256
+    # a packed chunk-64 call needs only the order table; the query also covers the 32-token
+    # (segmented) evaluation of a scalar-gate or fused call with the same arguments
+    assert q(1, 65536, 32, 128, 128, 1, True, chunk=64) == max(st + 256, q(1, 65536, 32, 128, 128, 1, True, chunk=32))
     # fewer than 256 (sequence, head) pairs, 32-token chunks: a segment table (4 + 5N + 2 int32,
     # rounded to 256 bytes) and 3 matrices per head for each of 256 / H segment slots
     mat = 128 * 128 * 4
@@ -190,7 +195,11 @@ def test_fused_argument_errors(lib):
     assert fwd(fz(flags=kda.KDA_FUSE_DECAY_LOGSIGMOID, scale=-2.0)) == kda.KDA_ERR_INVALID_ARGUMENT
     assert fwd(fz(gate=(3 << 40) + 4)) == kda.KDA_ERR_INVALID_ARGUMENT             # misaligned gate
     assert fwd(fz(gate=(2 << 40) + 64)) == kda.KDA_ERR_INVALID_ARGUMENT            # gate overlaps o
-    assert fwd(fz(flags=kda.KDA_FUSE_QK_L2NORM), chunk=64) == kda.KDA_ERR_UNSUPPORTED
+    # a 64-token request is accepted (evaluated with 32-token chunks): here it stops at the missing workspace
+    assert fwd(fz(flags=kda.KDA_FUSE_QK_L2NORM), chunk=64) == kda.KDA_ERR_WORKSPACE_TOO_SMALL
+    q = kda.kda_chunk_fwd_workspace_bytes
+    for shape in ((1, 65536, 32, 128, 128, 1, False), (4, 4096, 16, 128, 128, 4, False), (1, 1000, 2, 64, 64, 3, True)):
+        assert q(*shape, 64) >= q(*shape, 32)   # enough for either evaluation
     assert fwd(fz(flags=kda.KDA_FUSE_QK_L2NORM), B=0, N=0, T=0) == kda.KDA_OK       # nothing to do
 
     def step(fusion):

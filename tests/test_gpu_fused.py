@@ -116,6 +116,20 @@ def test_segmented_two_pass_path():
     check(d, ALL, True, "segmented")
 
 
+@pytest.mark.parametrize("sg", [False, True])
+def test_chunk_64_is_evaluated_with_32_token_chunks(sg):
+    """The fused maps run on the 32-token kernel: a 64-token request gives the 32-token call's
+    outputs bit for bit (equal-length segmented and packed batches), and both are within the
+    parity bound of the oracle."""
+    for d, label in ((inputs.make_raw_prefill(713, B=1, T=1000, H=2, D=128, scalar_gate=sg), "segmented"),
+                     (inputs.make_raw_prefill(714, H=3, D=64, lengths=[70, 0, 1, 64, 129], scalar_gate=sg),
+                      "packed")):
+        o32, S32, _ = run(d, ALL, True, chunk=32)
+        o64, S64, _ = run(d, ALL, True, chunk=64)
+        assert np.array_equal(o32, o64) and np.array_equal(S32, S64), label
+    check(d, ALL, True, "chunk 64 packed")
+
+
 def test_varlen_and_short():
     d = inputs.make_raw_prefill(704, H=3, D=128, lengths=[70, 0, 1, 64, 129])
     check(d, ALL, True, "varlen")

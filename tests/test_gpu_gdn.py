@@ -145,13 +145,19 @@ def test_bf16_output_is_rne_and_deterministic():
     assert np.array_equal(o32, o32b) and np.array_equal(S32, S32b)
 
 
-def test_rejects_chunk_64():
+def test_chunk_64_is_evaluated_with_32_token_chunks():
+    """The scalar gate runs on the 32-token kernel: a 64-token request gives the 32-token call's
+    outputs bit for bit, with a workspace sized by the 64-token query."""
     kda = _kda()
-    d = inputs.make_prefill(W[6], seed=611, B=1, T=64, H=2)
+    d = inputs.make_prefill(W[6], seed=611, B=1, T=1000, H=2, s0=True)
     dev = {kk: to_dev(d[kk]) for kk in KEYS}
-    with pytest.raises(kda.KDAError) as e:
-        kda.gdn_chunk_fwd(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], chunk=64)
-    assert e.value.status == kda.KDA_ERR_UNSUPPORTED
+    S0 = to_dev(d["S0"])
+    ws = torch.empty(kda.kda_chunk_fwd_workspace_bytes(1, 1000, 2, 128, 128, 1, False, 64), dtype=torch.uint8,
+                     device="cuda")
+    o32, S32 = kda.gdn_chunk_fwd(*(dev[kk] for kk in KEYS), S0, chunk=32, out_dtype=torch.float32)
+    o64, S64 = kda.gdn_chunk_fwd(*(dev[kk] for kk in KEYS), S0, chunk=64, out_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o32, o64) and torch.equal(S32, S64)
 
 
 def test_long_context_full_size_all_heads():
