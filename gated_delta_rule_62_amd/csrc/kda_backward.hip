@@ -1394,7 +1394,25 @@ hipError_t launch_typed(BackwardArgs a, int nc_max, int n_win, hipStream_t st) {
     // rebuilds its chunk records and entry states, runs the reverse pass from the state gradient
     // the later window left, and takes its chunks' gradients.
     const int grid = a.N * a.W * a.H;
-    for (int wi = 0; wi + 1 < n_win; ++wi) {
+    // The checkpoints.  bf16 inputs (parity bound 2e-3): all windows' entry states at once, from
+    // the prefill's segment summaries (segments = windows) chained by its combine, in scratch that
+    // the window data takes over afterwards.  fp32 inputs, or when that scratch does not fit: a
+    // sweep over the windows, each rebuilding its records and running the forward state pass.
+    bool ckpt_done = false;
+    if constexpr (std::is_same<IN, BF16>::value) {
+        const size_t avail = static_cast<size_t>(reinterpret_cast<char*>(a.ckpt) - reinterpret_cast<char*>(a.prep));
+        if (segment_states_workspace_bytes(a.N, a.H, D, n_win) <= avail) {
+            PrefillArgs pa;
+            pa.q = a.q; pa.k = a.k; pa.v = a.v; pa.g = a.g; pa.beta = a.beta;
+            pa.S0 = a.S0; pa.cu = nullptr; pa.o = nullptr; pa.S_final = nullptr; pa.workspace = a.prep;
+            pa.B = a.B; pa.T = a.T; pa.H = a.H; pa.D = D; pa.N = a.N;
+            pa.in_bf16 = true; pa.out_bf16 = false; pa.scalar_gate = SG;
+            const hipError_t e = launch_segment_states(pa, a.W, n_win, a.ckpt, st);
+            if (e != hipSuccess) return e;
+            ckpt_done = true;
+        }
+    }
+    for (int wi = 0; !ckpt_done && wi + 1 < n_win; ++wi) {
         a.wi = wi;
         a.w0 = wi * a.W;
         prep_kernel<D, IN, SG><<<grid, BT, 0, st>>>(a);

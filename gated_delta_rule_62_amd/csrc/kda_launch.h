@@ -85,6 +85,13 @@ hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan, hipStre
 // Clears the status word of a prefill workspace (for calls that run no prefill kernel).
 hipError_t clear_prefill_status(void* workspace, const PrefillPlan& plan, hipStream_t stream);
 
+// Entry states of the segments of W chunks (32 tokens each) of an equal-length batch, without
+// outputs: the summaries of segments 0..G-2 from a zero state (S_loc and the transition Phi) and
+// the combine chaining them from S0 (nullptr: zero).  entry receives [G-1][N*H][D][D] fp32, the
+// entry state of segment s at slot s - 1.  The workspace holds a status word and the summaries.
+size_t segment_states_workspace_bytes(int N, int H, int D, int G);
+hipError_t launch_segment_states(const PrefillArgs& a, int W, int G, float* entry, hipStream_t stream);
+
 hipError_t launch_decode(int D, bool in_bf16, bool out_bf16, const void* q, const void* k,
                          const void* v, const void* g, const void* b, const float* S_in,
                          float* S_out, void* o, int units, hipStream_t stream, bool scalar_gate,

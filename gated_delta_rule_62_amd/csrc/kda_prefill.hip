@@ -2429,6 +2429,50 @@ hipError_t clear_prefill_status(void* workspace, const PrefillPlan& plan, hipStr
     return hipGetLastError();
 }
 
+namespace {
+template <int D, typename IN, bool SG>
+hipError_t segment_states_typed(const PrefillArgs& pa, int W, int G, float* entry, hipStream_t stream) {
+    KernelArgs a;
+    a.q = pa.q; a.k = pa.k; a.v = pa.v; a.g = pa.g; a.beta = pa.beta;
+    a.S0 = pa.S0; a.cu = nullptr; a.order = nullptr; a.seg = nullptr; a.o = nullptr; a.S_final = nullptr;
+    a.T = pa.T; a.H = pa.H; a.NH = pa.N * pa.H; a.G = G; a.cps = W; a.cps0 = W;
+    a.chunks = (pa.T + 31) / 32; a.seg0 = 0; a.split0 = 0;
+    a.fuse_flags = 0; a.decay_bias = 0.f; a.decay_scale = 1.f; a.out_gate = nullptr;
+    a.wait_limit = pa.wait_limit;
+    char* ws = static_cast<char*>(pa.workspace);
+    const size_t mat = align256(static_cast<size_t>(a.NH) * (G - 1) * D * D * sizeof(float));
+    a.status = reinterpret_cast<int*>(ws);
+    a.phi = reinterpret_cast<float*>(ws + kStatusBytes);
+    a.sloc = reinterpret_cast<float*>(ws + kStatusBytes + mat);
+    a.se = entry;
+    hipLaunchKernelGGL(status_clear_kernel, dim3(1), dim3(64), 0, stream, a.status);
+    hipLaunchKernelGGL((pipe_kernel<D, IN, false, 1, SG, false>), dim3(a.NH * (G - 1)), dim3(PCfg<D, 1>::NT), 0,
+                       stream, a);
+    hipLaunchKernelGGL(combine_kernel<D>, dim3(a.NH, D / 16), dim3(256), 0, stream, pa.S0, a.phi, a.sloc, entry,
+                       a.NH, G, 1, nullptr, pa.H);
+    return hipGetLastError();
+}
+}  // namespace
+
+size_t segment_states_workspace_bytes(int N, int H, int D, int G) {
+    if (G < 2) return kStatusBytes;
+    return kStatusBytes + 2 * align256(static_cast<size_t>(N) * H * (G - 1) * D * D * sizeof(float));
+}
+
+hipError_t launch_segment_states(const PrefillArgs& a, int W, int G, float* entry, hipStream_t stream) {
+    if (G < 2 || a.N * a.H == 0) return hipSuccess;
+#define KDA_SEG_CASE(DD, INT)                                                                      \
+    if (a.D == DD && a.in_bf16 == std::is_same<INT, BF16>::value)                                  \
+        return a.scalar_gate ? segment_states_typed<DD, INT, true>(a, W, G, entry, stream)        \
+                             : segment_states_typed<DD, INT, false>(a, W, G, entry, stream);
+    KDA_SEG_CASE(128, BF16)
+    KDA_SEG_CASE(128, F32)
+    KDA_SEG_CASE(64, BF16)
+    KDA_SEG_CASE(64, F32)
+#undef KDA_SEG_CASE
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& plan, hipStream_t stream) {
 #define KDA_PREFILL_CASE(DD, CC, INT, OB)                                                              \
     if (a.D == DD && plan.chunk == CC && a.in_bf16 == std::is_same<INT, BF16>::value && a.out_bf16 == OB) { \

@@ -326,8 +326,12 @@ kda_status gdn_recurrent_fwd_fused(const void* q, const void* k, const void* v, 
  * length): when that per-chunk data would exceed 2 GiB (the KDA_BWD_WORKSPACE_LIMIT
  * environment variable, in bytes, overrides the limit), equal-length batches run in
  * windows of chunks, last window first, with one checkpointed entry state per window
- * and the state gradient carried between windows; the gradients are bitwise those of
- * the one-pass plan.  Packed batches always take the one-pass plan.
+ * and the state gradient carried between windows.  fp32 inputs: the checkpoints come
+ * from a sweep of the backward's forward state pass and the gradients are bitwise
+ * those of the one-pass plan.  bf16 inputs: the checkpoints come from the prefill's
+ * segment summaries chained by its combine (windows = segments), so they differ from
+ * the one-pass plan in fp32 rounding order only.  Packed batches always take the
+ * one-pass plan.
  *
  *   q, k, v, log_alpha, beta, S0, cu_seqlens, B, T, H, Dk, Dv, num_seqs, in_dtype:
  *                     the arguments of the kda_chunk_fwd call being differentiated

@@ -217,8 +217,12 @@ WINDOW_CASES = [   # (label, make_prefill overrides, limit in bytes, expected wi
 def test_windowed_backward(label, kw, limit, win, monkeypatch):
     """Past the workspace limit an equal-length backward runs window by window (a forward sweep
     keeps each window's entry state, then the windows run from last to first, each carrying the
-    state gradient to the one before).  Every chunk's arithmetic is that of the one-pass plan, so
-    the gradients are bitwise equal to it, and within the parity bound of the oracle."""
+    state gradient to the one before).  fp32 inputs: the checkpoints come from the backward's own
+    forward state pass, so every chunk's arithmetic is that of the one-pass plan and the gradients
+    are bitwise equal to it.  bf16 inputs: where their scratch fits, the checkpoints come from
+    the prefill's segment summaries and combine, whose fp32 rounding differs; then the gradients
+    agree with the one-pass plan to 1e-4 of each tensor's largest magnitude.  Both are checked
+    against the oracle to the parity bound."""
     kda = _kda()
     kw = dict(kw)
     w = W[kw.pop("w")]
@@ -236,7 +240,12 @@ def test_windowed_backward(label, kw, limit, win, monkeypatch):
         assert (T + 31) // 32 > Wc * (n - 1)
     got = gpu_bwd(d, g)
     for name in ref_one:
-        assert np.array_equal(got[name], ref_one[name]), f"{label}: {name} differs from the one-pass plan"
+        if w.dtype == "f32":
+            assert np.array_equal(got[name], ref_one[name]), f"{label}: {name} differs from the one-pass plan"
+        else:
+            scale = max(float(np.abs(ref_one[name]).max()), 1e-30)
+            err = float(np.abs(got[name].astype(np.float64) - ref_one[name]).max()) / scale
+            assert err <= 1e-4, f"{label}: {name} differs from the one-pass plan by {err:.3g}"
     check(d, g, f"windowed {label}")
     monkeypatch.delenv("KDA_BWD_WORKSPACE_LIMIT")
 
