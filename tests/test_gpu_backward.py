@@ -208,6 +208,7 @@ WINDOW_CASES = [   # (label, make_prefill overrides, limit in bytes, expected wi
     ("bf16 d128 ragged", dict(w=1, B=2, T=1000, H=2, s0=True), 4 << 20, (4, 8)),
     ("fp32 d64 ragged", dict(w=0, B=2, T=1000, H=3, D=64, s0=True), 3 << 20, None),
     ("bf16 d128 two windows", dict(w=2, B=1, T=2000, H=2, s0=True), 20 << 20, None),
+    ("bf16 d128 no S0", dict(w=1, B=2, T=1500, H=2, s0=False), 8 << 20, None),
     ("bf16 d64 scalar gate", dict(w=1, B=2, T=700, H=2, D=64, s0=True, scalar_gate=True), 2 << 20, None),
     ("fp32 d128 scalar gate", dict(w=0, B=1, T=900, H=2, D=128, s0=True, scalar_gate=True), 6 << 20, None),
 ]
